@@ -1,0 +1,55 @@
+"""Plain, slow, fp64 CPU oracle for decode-phase attention over a KV cache.
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the product path (the C-ABI library and its
+Python binding) imports, calls or links this package; only the tests, the
+``smoke()`` check and the CPU-baseline leg of the benchmark do.  The oracle shares
+no code, tables or helpers with the HIP path.
+
+Every function is written straight from the definitions on the source pages, in
+float64, with no tiling, no splitting and no online softmax:
+
+* ``static_cache``  -- the static preallocated buffer ``[batch, heads, capacity,
+  head_dim]``, its 0/1 attention mask, append-at-write-position and masked
+  scaled-dot-product decode attention (OpenVINO NPU LLM article, Part 1
+  "Solution: preallocation + attention mask"; Part 2 KV-cache update;
+  "Attention on the NPU" -> "incremental SDPA").
+* ``paged``         -- paged KV cache addressed through block tables: host
+  validation, the ``gather_pa_kv_cache`` mapping, and paged GQA decode attention
+  (PyPTO GatherPaKvCache article, section 3 "tensor contract and data
+  semantics").
+* ``sparse``        -- top-k sparse MLA-style decode (FlashMLA on Huawei Ascend,
+  "Mathematical formulation").
+
+bf16 tensors enter the oracle as their raw 16-bit patterns (``numpy.uint16``) and
+are widened exactly to float64 (``bf16.widen``); copies (append, gather) move the
+16-bit patterns untouched, so they can be compared bit for bit.
+
+Parity status of each function (what pins it, from tests/test_oracle_*.py):
+every function here is pinned by closed forms, printed values, invariants,
+library-routine special cases or brute force; none is "parity unpinned".
+"""
+
+from .bf16 import widen, round_to_bf16_bits
+from .static_cache import kv_append, decode_static
+from .paged import (
+    PagedIndexError,
+    validate_paged,
+    gather_pa_kv_cache,
+    decode_paged,
+    decode_paged_via_gather,
+)
+from .sparse import sparse_topk_decode, validate_sparse
+
+__all__ = [
+    "widen",
+    "round_to_bf16_bits",
+    "kv_append",
+    "decode_static",
+    "PagedIndexError",
+    "validate_paged",
+    "gather_pa_kv_cache",
+    "decode_paged",
+    "decode_paged_via_gather",
+    "sparse_topk_decode",
+    "validate_sparse",
+]
