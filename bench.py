@@ -1,0 +1,282 @@
+#!/usr/bin/env python3
+"""Benchmark of decode attention over a KV cache on one MI355X.
+
+Default workload (one "step"): a LLaMA-7B-shaped decode step over the static
+preallocated buffer -- 32 layers, each with its own bf16 cache [B, 32, 4096, 128];
+per layer the new token's K/V is appended at row L_b - 1 (kv_append) and one
+fp32 query row per head attends the L_b valid rows (decode_attn_static); L_b is
+uniform on 1..4096 per sequence and the same in every layer.  Batch 8 is the
+headline; batch 1 and the paged gather (cache [8192, 128, 8, 128], 32 sequences
+of 1..4096 tokens) are reported in the same line.  Inputs are synthetic and
+resident in HBM before timing starts.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+Prints one JSON line.  value = algorithmic HBM bytes per step / seconds per step
+(GB/s); the roofline object prices the dominant kernel launch against the 8 TB/s
+HBM peak; cpu_baseline times the fp64 oracle on a bounded sample on the host.
+"""
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "decode-attn µs/step and achieved HBM GB/s (% of peak); gather GB/s"
+HBM_PEAK_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--batch", type=int, default=8)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="approximate host time spent on the oracle baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true", help="skip the batch-1 and gather legs")
+    return ap.parse_args()
+
+
+def event_pair(torch):
+    return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+
+class StaticStep:
+    """32 layers x (kv_append + decode_attn_static) with preallocated outputs."""
+
+    def __init__(self, B, torch, dakv, workloads, acc, seed=2):
+        self.torch, self.dakv = torch, dakv
+        self.model = workloads.static_llama_layers(B, device="cuda:0", seed=seed)
+        m = self.model
+        self.outs = [torch.empty((B, m.H, m.D), dtype=torch.float32, device="cuda:0")
+                     for _ in m.layers]
+        nbytes = dakv.decode_attn_static_workspace_size(B, m.H, m.cap, m.D)
+        self.ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0")
+        self.attn_bytes = acc.decode_static_bytes(B, m.H, m.D, m.lengths, q_elem=acc.FP32,
+                                                  with_mask=True, with_lse=False)
+        self.append_bytes = acc.kv_append_bytes(B, m.H, m.D, with_mask=True)
+        self.step_bytes = len(m.layers) * (self.attn_bytes + self.append_bytes)
+
+    def append(self, layer):
+        m = self.model
+        self.dakv.kv_append(layer.k_cache, layer.v_cache, layer.k_new, layer.v_new, m.write_pos,
+                            m.mask)
+
+    def attend(self, i, layer):
+        m = self.model
+        self.dakv.decode_attn_static(layer.q, layer.k_cache, layer.v_cache, mask=m.mask,
+                                     valid_len=m.valid_len, scale=m.scale, out=self.outs[i],
+                                     workspace=self.ws, want_lse=False)
+
+    def run(self):
+        for i, layer in enumerate(self.model.layers):
+            self.append(layer)
+            self.attend(i, layer)
+
+    def per_launch_ms(self, reps=2):
+        """Average duration of each decode_attn_static and kv_append call (HIP events
+        on the stream the kernels run on)."""
+        torch = self.torch
+        attn, app = [], []
+        for _ in range(reps):
+            for i, layer in enumerate(self.model.layers):
+                a0, a1 = event_pair(torch)
+                b0, b1 = event_pair(torch)
+                a0.record()
+                self.append(layer)
+                a1.record()
+                b0.record()
+                self.attend(i, layer)
+                b1.record()
+                app.append((a0, a1))
+                attn.append((b0, b1))
+        torch.cuda.synchronize()
+        avg = lambda pairs: sum(s.elapsed_time(e) for s, e in pairs) / len(pairs)
+        return avg(attn), avg(app)
+
+
+def time_steps(torch, fn, steps, warmup):
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    s, e = event_pair(torch)
+    t0 = time.perf_counter()
+    s.record()
+    for _ in range(steps):
+        fn()
+    e.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return s.elapsed_time(e) / steps, wall
+
+
+def gather_leg(torch, dakv, workloads, acc, reps=20):
+    case = workloads.gather_nd(device="cuda:0", seed=3)
+    idx = case.index
+    t = torch.from_numpy(idx.block_tables).to("cuda:0")
+    s = torch.from_numpy(idx.seq_lens).to("cuda:0")
+    o = torch.from_numpy(idx.seq_offset).to("cuda:0")
+    T = int(idx.seq_lens[-1])
+    ko = torch.empty((T, 8, 128), dtype=torch.bfloat16, device="cuda:0")
+    vo = torch.empty_like(ko)
+    dakv.validate_paged(idx.block_tables, idx.seq_lens, idx.seq_offset, 8192, 128)
+    call = lambda: dakv.gather_pa_kv_cache(case.key_cache, case.value_cache, t, s, o,
+                                           total_tokens=T, key_out=ko, value_out=vo,
+                                           validate=False)
+    for _ in range(3):
+        call()
+    torch.cuda.synchronize()
+    pairs = []
+    for _ in range(reps):
+        a, b = event_pair(torch)
+        a.record()
+        call()
+        b.record()
+        pairs.append((a, b))
+    torch.cuda.synchronize()
+    ms = sum(x.elapsed_time(y) for x, y in pairs) / len(pairs)
+    nbytes = acc.gather_bytes(idx.lengths, 8, 128, 8, 128, 128, with_offset=True)
+    del case, ko, vo
+    return {"workload": "gather_pa_kv_cache ND: cache [8192,128,8,128] bf16, 32 sequences "
+                        "of U{1..4096} tokens, block_tables [32,64], random offsets",
+            "total_tokens": T, "us_per_call": round(ms * 1e3, 2),
+            "algorithmic_bytes": nbytes, "GBps": round(nbytes / (ms * 1e-3) / 1e9, 1),
+            "frac_of_peak": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+
+
+def cpu_baseline(step, budget_s):
+    """The fp64 oracle over (layer, sequence) pairs of the same step until the budget is
+    spent; GB/s = algorithmic bytes of the pairs done / host seconds."""
+    import numpy as np
+    import oracle
+    from decode_attention_kv_amd import accounting as acc
+
+    def bits(t):
+        return t.detach().cpu().contiguous().view(step.torch.int16).numpy().view(np.uint16)
+
+    m = step.model
+    done_bytes, pairs, spent = 0, 0, 0.0
+    for layer in m.layers:
+        for b in range(m.B):
+            L = m.lengths[b]
+            q = layer.q[b:b + 1].cpu().numpy()
+            kc = bits(layer.k_cache[b:b + 1, :, :L])
+            vc = bits(layer.v_cache[b:b + 1, :, :L])
+            mask = m.mask[b:b + 1, :L].cpu().numpy().copy()
+            mask[0, L - 1] = 1
+            t0 = time.perf_counter()
+            oracle.kv_append(kc, vc, bits(layer.k_new[b:b + 1]), bits(layer.v_new[b:b + 1]),
+                             [L - 1], mask)
+            oracle.decode_static(q, kc, vc, mask, [L], m.scale)
+            spent += time.perf_counter() - t0
+            done_bytes += acc.decode_static_bytes(1, m.H, m.D, [L], q_elem=acc.FP32) + \
+                acc.kv_append_bytes(1, m.H, m.D)
+            pairs += 1
+            if spent >= budget_s:
+                break
+        if spent >= budget_s:
+            break
+    threads = None
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:
+        pass
+    cores = len(os.sched_getaffinity(0))
+    return {"value": round(done_bytes / spent / 1e9, 4), "unit": "GB/s",
+            "cores": threads if threads else cores, "host_cores_visible": cores,
+            "kind": "oracle",
+            "sample": f"{pairs} (layer, sequence) pairs of the batch-{m.B} step "
+                      f"(append + attend, fp64 NumPy), {spent:.1f} s"}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(--gpus must be 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import decode_attention_kv_amd as dakv
+    from decode_attention_kv_amd import accounting as acc
+    import workloads
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    dakv.lib()
+
+    B = args.batch
+    step = StaticStep(B, torch, dakv, workloads, acc)
+    ms, wall = time_steps(torch, step.run, args.steps, args.warmup)
+    attn_ms, app_ms = step.per_launch_ms()
+    value = step.step_bytes / (ms * 1e-3) / 1e9
+    attn_gbs = step.attn_bytes / (attn_ms * 1e-3) / 1e9
+    m = step.model
+    line = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "us_per_step": round(ms * 1e3, 1),
+        "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "kv_dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": f"static-buffer decode step, LLaMA-7B-shaped: 32 layers x (kv_append + "
+                        f"decode_attn_static), batch {B}, 32 heads x 128, capacity 4096, "
+                        f"L ~ U{{1..4096}} per sequence",
+            "global_batch": B, "seq_len": m.cap, "valid_lengths": m.lengths,
+            "parallelism": "none (one GPU)",
+            "algorithmic_bytes_per_step": step.step_bytes,
+        },
+        "roofline": {
+            "kernel": "decode_attn_static (split pass + merge), one call per layer",
+            "bound": "hbm", "achieved": round(attn_gbs, 1), "peak": HBM_PEAK_GBS,
+            "unit": "GB/s", "frac": round(attn_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+            "bytes_per_launch": step.attn_bytes, "us_per_launch": round(attn_ms * 1e3, 2),
+            "kv_append_us_per_launch": round(app_ms * 1e3, 2),
+        },
+        "wall_s_timed": round(wall, 3),
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(step, args.cpu_seconds)
+    del step
+    torch.cuda.empty_cache()
+    if not args.no_extras:
+        s1 = StaticStep(1, torch, dakv, workloads, acc, seed=12)
+        ms1, _ = time_steps(torch, s1.run, max(args.steps, 20), args.warmup)
+        a1, ap1 = s1.per_launch_ms()
+        line["batch1"] = {
+            "us_per_step": round(ms1 * 1e3, 1),
+            "GBps": round(s1.step_bytes / (ms1 * 1e-3) / 1e9, 1),
+            "valid_lengths": s1.model.lengths,
+            "attn_us_per_launch": round(a1 * 1e3, 2),
+            "attn_GBps": round(s1.attn_bytes / (a1 * 1e-3) / 1e9, 1),
+            "kv_append_us_per_launch": round(ap1 * 1e3, 2),
+        }
+        del s1
+        torch.cuda.empty_cache()
+        line["gather"] = gather_leg(torch, dakv, workloads, acc)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,38 @@
+"""Decode-phase attention over a KV cache, native to AMD MI355X (gfx950).
+
+The product is the C-ABI library ``libdakv.so`` (declared in include/dakv.h) with
+hand-written HIP kernels; ``ops`` is its thin torch-facing binding.  There is no
+CPU fallback: loading fails loudly when the library has not been built.
+"""
+
+from .ops import (
+    kv_append,
+    decode_attn_static,
+    decode_attn_static_workspace_size,
+    gather_pa_kv_cache,
+    decode_attn_paged,
+    decode_attn_paged_workspace_size,
+    sparse_topk_decode_attn,
+    sparse_topk_decode_attn_workspace_size,
+    validate_paged,
+    validate_sparse,
+    validate_range,
+)
+from ._lib import DakvError, lib, strerror
+
+__all__ = [
+    "kv_append",
+    "decode_attn_static",
+    "decode_attn_static_workspace_size",
+    "gather_pa_kv_cache",
+    "decode_attn_paged",
+    "decode_attn_paged_workspace_size",
+    "sparse_topk_decode_attn",
+    "sparse_topk_decode_attn_workspace_size",
+    "validate_paged",
+    "validate_sparse",
+    "validate_range",
+    "DakvError",
+    "lib",
+    "strerror",
+]

@@ -1,0 +1,206 @@
+// C-ABI entry points: argument checks on the host, then the gfx950 launchers.
+// Nothing here allocates, frees or synchronises.
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+
+#include "../../include/dakv.h"
+#include "launch.hpp"
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int from_hip(hipError_t e) {
+  if (e == hipErrorNotSupported) return DAKV_ENOTSUP;
+  return e == hipSuccess ? DAKV_OK : DAKV_EHIP;
+}
+
+hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+}  // namespace
+
+extern "C" {
+
+const char* dakv_strerror(int code) {
+  switch (code) {
+    case DAKV_OK: return "ok";
+    case DAKV_EINVAL: return "invalid argument (null pointer, size, alignment or workspace)";
+    case DAKV_ENOTSUP: return "unsupported shape (no kernel built for it)";
+    case DAKV_ERANGE: return "index content outside the contract";
+    case DAKV_EHIP: return "HIP runtime error at launch";
+    default: return "unknown status";
+  }
+}
+
+// ------------------------------------------------------------------ kv_append
+int dakv_kv_append(void* k_cache, void* v_cache, const void* k_new, const void* v_new,
+                   const int32_t* write_pos, int32_t* mask, int B, int H, int cap, int D,
+                   int32_t* err_flag, void* stream) {
+  if (B < 0 || H < 0 || cap < 0 || D <= 0) return DAKV_EINVAL;
+  if (B == 0 || H == 0) return DAKV_OK;
+  if (cap == 0) return DAKV_EINVAL;
+  if (!k_cache || !v_cache || !k_new || !v_new || !write_pos) return DAKV_EINVAL;
+  if ((D * 2) % 16 != 0) return DAKV_ENOTSUP;
+  if (!aligned16(k_cache) || !aligned16(v_cache) || !aligned16(k_new) || !aligned16(v_new))
+    return DAKV_EINVAL;
+  return from_hip(dakv::launch_kv_append(k_cache, v_cache, k_new, v_new, write_pos, mask, B, H,
+                                         cap, D, err_flag, as_stream(stream)));
+}
+
+// --------------------------------------------------------- decode_attn_static
+size_t dakv_decode_attn_static_workspace_size(int B, int H, int cap, int D) {
+  if (B <= 0 || H <= 0 || cap <= 0 || D <= 0) return 0;
+  return dakv::static_workspace_bytes(B, H, cap, D);
+}
+
+int dakv_decode_attn_static(const float* q, const void* k_cache, const void* v_cache,
+                            const int32_t* mask, const int32_t* valid_len, int B, int H,
+                            int cap, int D, float scale, float* out, float* lse,
+                            void* workspace, size_t workspace_bytes, int num_splits,
+                            int32_t* err_flag, void* stream) {
+  if (B < 0 || H < 0 || cap <= 0 || D <= 0 || num_splits < 0) return DAKV_EINVAL;
+  if (B == 0 || H == 0) return DAKV_OK;
+  if (D != 64 && D != 128) return DAKV_ENOTSUP;
+  if (!q || !k_cache || !v_cache || !out || !workspace) return DAKV_EINVAL;
+  if (!mask && !valid_len) return DAKV_EINVAL;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out) ||
+      !aligned16(workspace))
+    return DAKV_EINVAL;
+  if (workspace_bytes < dakv::static_workspace_bytes(B, H, cap, D)) return DAKV_EINVAL;
+  const dakv::SplitPlan plan = dakv::plan_static(B, H, cap, D, num_splits);
+  return from_hip(dakv::launch_decode_static(q, k_cache, v_cache, mask, valid_len, B, H, cap, D,
+                                             scale, out, lse, workspace, plan, err_flag,
+                                             as_stream(stream)));
+}
+
+// --------------------------------------------------------- gather_pa_kv_cache
+int dakv_gather_pa_kv_cache(const void* key_cache, const void* value_cache, int num_blocks,
+                            int block_size, int Hk, int Dk, int Hv, int Dv,
+                            const int32_t* block_tables, int Q, int table_cols,
+                            const int32_t* seq_lens, const int32_t* seq_offset,
+                            int total_tokens, void* key_out, void* value_out,
+                            int32_t* err_flag, void* stream) {
+  if (num_blocks <= 0 || block_size <= 0 || Hk <= 0 || Dk <= 0 || Hv <= 0 || Dv <= 0 ||
+      Q < 0 || table_cols < 0 || total_tokens < 0)
+    return DAKV_EINVAL;
+  if (total_tokens == 0) return DAKV_OK;
+  if (Q == 0 || table_cols == 0) return DAKV_EINVAL;
+  if (!key_cache || !value_cache || !block_tables || !seq_lens || !key_out || !value_out)
+    return DAKV_EINVAL;
+  const long long kb = 2LL * Hk * Dk, vb = 2LL * Hv * Dv;
+  if (kb % 16 != 0 || vb % 16 != 0) return DAKV_ENOTSUP;
+  if (kb > (1 << 30) || vb > (1 << 30)) return DAKV_ENOTSUP;
+  if (!aligned16(key_cache) || !aligned16(value_cache) || !aligned16(key_out) ||
+      !aligned16(value_out))
+    return DAKV_EINVAL;
+  return from_hip(dakv::launch_gather(key_cache, value_cache, num_blocks, block_size, (int)kb,
+                                      (int)vb, block_tables, Q, table_cols, seq_lens, seq_offset,
+                                      total_tokens, key_out, value_out, err_flag,
+                                      as_stream(stream)));
+}
+
+// ---------------------------------------------------------- decode_attn_paged
+size_t dakv_decode_attn_paged_workspace_size(int B, int Hq, int D, int max_seq_len,
+                                             int block_size) {
+  if (B <= 0 || Hq <= 0 || D <= 0 || max_seq_len < 0 || block_size <= 0) return 0;
+  return dakv::paged_workspace_bytes(B, Hq, D, max_seq_len, block_size);
+}
+
+int dakv_decode_attn_paged(const void* q, const void* key_cache, const void* value_cache,
+                           const int32_t* block_tables, int table_cols,
+                           const int32_t* seq_lens, const int32_t* seq_offset, int B, int Hq,
+                           int Hkv, int D, int num_blocks, int block_size, int max_seq_len,
+                           float scale, float* out, float* lse, void* workspace,
+                           size_t workspace_bytes, int num_splits, int32_t* err_flag,
+                           void* stream) {
+  if (B < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || num_blocks <= 0 || block_size <= 0 ||
+      max_seq_len < 0 || table_cols <= 0 || num_splits < 0)
+    return DAKV_EINVAL;
+  if (B == 0) return DAKV_OK;
+  if (Hq % Hkv != 0) return DAKV_EINVAL;
+  const int G = Hq / Hkv;
+  if (D != 128) return DAKV_ENOTSUP;
+  if (G != 1 && G != 2 && G != 4 && G != 8) return DAKV_ENOTSUP;
+  if (block_size != 16 && block_size != 32 && block_size != 64 && block_size != 128)
+    return DAKV_ENOTSUP;
+  if (!q || !key_cache || !value_cache || !block_tables || !seq_lens || !out || !workspace)
+    return DAKV_EINVAL;
+  if (!aligned16(q) || !aligned16(key_cache) || !aligned16(value_cache) || !aligned16(out) ||
+      !aligned16(workspace))
+    return DAKV_EINVAL;
+  if (workspace_bytes < dakv::paged_workspace_bytes(B, Hq, D, max_seq_len, block_size))
+    return DAKV_EINVAL;
+  const dakv::SplitPlan plan = dakv::plan_paged(B, Hkv, max_seq_len, block_size, num_splits);
+  return from_hip(dakv::launch_decode_paged(q, key_cache, value_cache, block_tables, table_cols,
+                                            seq_lens, seq_offset, B, Hq, Hkv, D, num_blocks,
+                                            block_size, max_seq_len, scale, out, lse, workspace,
+                                            plan, err_flag, as_stream(stream)));
+}
+
+// ---------------------------------------------------- sparse_topk_decode_attn
+size_t dakv_sparse_topk_decode_attn_workspace_size(int B, int Hq, int d_qk, int d_v,
+                                                   int topk) {
+  if (B <= 0 || Hq <= 0 || d_qk <= 0 || d_v <= 0 || topk <= 0) return 0;
+  return dakv::sparse_workspace_bytes(B, Hq, d_qk, d_v, topk);
+}
+
+int dakv_sparse_topk_decode_attn(const void* q, const void* kv, const int32_t* indices,
+                                 int B, int Hq, int s_kv, int d_qk, int d_v, int topk,
+                                 float sm_scale, float* out, float* lse, void* workspace,
+                                 size_t workspace_bytes, int32_t* err_flag, void* stream) {
+  if (B < 0 || Hq <= 0 || s_kv <= 0 || d_qk <= 0 || d_v <= 0 || topk < 0) return DAKV_EINVAL;
+  if (B == 0) return DAKV_OK;
+  if (d_qk != 576 || d_v != 512) return DAKV_ENOTSUP;
+  if (Hq % 16 != 0 || Hq > 128) return DAKV_ENOTSUP;
+  if (!q || !kv || !out || (topk > 0 && !indices)) return DAKV_EINVAL;
+  if (!aligned16(q) || !aligned16(kv) || !aligned16(out)) return DAKV_EINVAL;
+  const size_t need = dakv::sparse_workspace_bytes(B, Hq, d_qk, d_v, topk);
+  if (need > 0 && (!workspace || !aligned16(workspace) || workspace_bytes < need))
+    return DAKV_EINVAL;
+  return from_hip(dakv::launch_sparse(q, kv, indices, B, Hq, s_kv, d_qk, d_v, topk, sm_scale,
+                                      out, lse, workspace, err_flag, as_stream(stream)));
+}
+
+// ------------------------------------------------------------ host validators
+int dakv_validate_paged(const int32_t* block_tables, int Q, int table_cols,
+                        const int32_t* seq_lens, const int32_t* seq_offset, int num_blocks,
+                        int block_size) {
+  if (Q < 0 || table_cols < 0 || num_blocks < 0 || block_size <= 0) return DAKV_EINVAL;
+  if (!seq_lens) return DAKV_EINVAL;
+  if (Q > 0 && table_cols > 0 && !block_tables) return DAKV_EINVAL;
+  if (seq_lens[0] != 0) return DAKV_ERANGE;
+  for (int q = 0; q < Q; ++q) {
+    const long long len = (long long)seq_lens[q + 1] - seq_lens[q];
+    if (len < 0) return DAKV_ERANGE;
+    const int off = seq_offset ? seq_offset[q] : 0;
+    if (off < 0 || off % block_size != 0) return DAKV_ERANGE;
+    const long long first = off / block_size;
+    const long long used = (len + block_size - 1) / block_size;
+    if (used == 0) continue;
+    if (first + used > table_cols) return DAKV_ERANGE;
+    const int32_t* row = block_tables + (size_t)q * table_cols;
+    for (long long c = first; c < first + used; ++c)
+      if (row[c] < 0 || row[c] >= num_blocks) return DAKV_ERANGE;
+  }
+  return DAKV_OK;
+}
+
+int dakv_validate_sparse(const int32_t* indices, int B, int topk, int s_kv) {
+  if (B < 0 || topk < 0 || s_kv < 0) return DAKV_EINVAL;
+  if ((size_t)B * topk > 0 && !indices) return DAKV_EINVAL;
+  const size_t n = (size_t)B * topk;
+  for (size_t i = 0; i < n; ++i)
+    if (indices[i] < 0 || indices[i] >= s_kv) return DAKV_ERANGE;
+  return DAKV_OK;
+}
+
+int dakv_validate_range(const int32_t* values, int n, int lo, int hi) {
+  if (n < 0) return DAKV_EINVAL;
+  if (n > 0 && !values) return DAKV_EINVAL;
+  for (int i = 0; i < n; ++i)
+    if (values[i] < lo || values[i] > hi) return DAKV_ERANGE;
+  return DAKV_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,82 @@
+// Device helpers shared by the gfx950 kernels: bf16 unpacking, 16-lane DPP
+// reductions, the base-2 exponential, and the error-flag update.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dakv {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kNegInf = -__builtin_inff();
+
+// Two bf16 values packed in one 32-bit word (element 0 in the low half).
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Eight bf16 values of a 16-byte load as floats.
+__device__ __forceinline__ void unpack8(const uint4& v, float* f) {
+  f[0] = bf16_lo(v.x); f[1] = bf16_hi(v.x);
+  f[2] = bf16_lo(v.y); f[3] = bf16_hi(v.y);
+  f[4] = bf16_lo(v.z); f[5] = bf16_hi(v.z);
+  f[6] = bf16_lo(v.w); f[7] = bf16_hi(v.w);
+}
+
+// fp32 -> bf16 bits, round to nearest even (finite inputs).
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float x) {
+  uint32_t u = __float_as_uint(x);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
+}
+
+// v_exp_f32: 2^x, exact at 0, 0 at -inf.
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// DPP lane permutations inside a row of 16 lanes.
+//   0xB1 quad_perm [1,0,3,2]   (xor 1)
+//   0x4E quad_perm [2,3,0,1]   (xor 2)
+//   0x141 row_half_mirror      (lane i <- 7 - i within each 8)
+//   0x140 row_mirror           (lane i <- 15 - i within each 16)
+template <int kCtrl>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, 0xf, 0xf, false));
+}
+
+// Sum over aligned groups of kLanes lanes (kLanes in {4, 8, 16}); every lane of a
+// group receives the group's sum.
+template <int kLanes>
+__device__ __forceinline__ float group_sum(float v) {
+  v += dpp<0xB1>(v);
+  v += dpp<0x4E>(v);
+  if constexpr (kLanes >= 8) v += dpp<0x141>(v);
+  if constexpr (kLanes >= 16) v += dpp<0x140>(v);
+  return v;
+}
+
+template <int kLanes>
+__device__ __forceinline__ float group_max(float v) {
+  v = fmaxf(v, dpp<0xB1>(v));
+  v = fmaxf(v, dpp<0x4E>(v));
+  if constexpr (kLanes >= 8) v = fmaxf(v, dpp<0x141>(v));
+  if constexpr (kLanes >= 16) v = fmaxf(v, dpp<0x140>(v));
+  return v;
+}
+
+__device__ __forceinline__ void raise_flag(int32_t* err_flag, int32_t bit) {
+  if (err_flag) atomicOr(err_flag, bit);
+}
+
+__device__ __forceinline__ uint4 load16(const void* p) {
+  return *reinterpret_cast<const uint4*>(p);
+}
+
+__device__ __forceinline__ void store16(void* p, const uint4& v) {
+  *reinterpret_cast<uint4*>(p) = v;
+}
+
+}  // namespace dakv

@@ -1,0 +1,49 @@
+// Host-side launchers of the gfx950 kernels (internal to the library).  The
+// C-ABI entry points validate arguments and then call these; every launcher
+// enqueues on `stream` and returns hipGetLastError().
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace dakv {
+
+hipError_t launch_kv_append(void* k_cache, void* v_cache, const void* k_new, const void* v_new,
+                            const int32_t* write_pos, int32_t* mask, int B, int H, int cap,
+                            int D, int32_t* err_flag, hipStream_t stream);
+
+hipError_t launch_gather(const void* key_cache, const void* value_cache, int num_blocks,
+                         int block_size, int k_row_bytes, int v_row_bytes,
+                         const int32_t* block_tables, int Q, int table_cols,
+                         const int32_t* seq_lens, const int32_t* seq_offset, int total_tokens,
+                         void* key_out, void* value_out, int32_t* err_flag, hipStream_t stream);
+
+// Split-K plan of a decode call: rows [s*chunk, (s+1)*chunk) go to split s.
+struct SplitPlan {
+  int chunk;       // rows per split
+  int max_splits;  // splits of the longest possible sequence
+};
+
+SplitPlan plan_static(int B, int H, int cap, int D, int forced_splits);
+size_t static_workspace_bytes(int B, int H, int cap, int D);
+hipError_t launch_decode_static(const float* q, const void* k_cache, const void* v_cache,
+                                const int32_t* mask, const int32_t* valid_len, int B, int H,
+                                int cap, int D, float scale, float* out, float* lse, void* ws,
+                                const SplitPlan& plan, int32_t* err_flag, hipStream_t stream);
+
+SplitPlan plan_paged(int B, int Hkv, int max_seq_len, int block_size, int forced_splits);
+size_t paged_workspace_bytes(int B, int Hq, int D, int max_seq_len, int block_size);
+hipError_t launch_decode_paged(const void* q, const void* key_cache, const void* value_cache,
+                               const int32_t* block_tables, int table_cols,
+                               const int32_t* seq_lens, const int32_t* seq_offset, int B,
+                               int Hq, int Hkv, int D, int num_blocks, int block_size,
+                               int max_seq_len, float scale, float* out, float* lse, void* ws,
+                               const SplitPlan& plan, int32_t* err_flag, hipStream_t stream);
+
+size_t sparse_workspace_bytes(int B, int Hq, int d_qk, int d_v, int topk);
+hipError_t launch_sparse(const void* q, const void* kv, const int32_t* indices, int B, int Hq,
+                         int s_kv, int d_qk, int d_v, int topk, float sm_scale, float* out,
+                         float* lse, void* ws, int32_t* err_flag, hipStream_t stream);
+
+}  // namespace dakv

@@ -1,0 +1,295 @@
+"""Thin torch-facing binding of the C-ABI (argument marshalling only).
+
+Every function here has the name of its C entry point without the ``dakv_`` prefix.
+torch is used for device memory (outputs and workspace are allocated with it when
+the caller does not pass them) and for the current stream; all computation
+happens in the HIP kernels of libdakv.so.  Shape/dtype/device mistakes raise
+``ValueError`` before any call; a nonzero C status raises ``DakvError`` (a
+``ValueError``).
+"""
+
+import ctypes
+import math
+
+import numpy as np
+import torch
+
+from . import _lib
+from ._lib import check, lib
+
+
+def _p(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _need(t, name, dtype, shape=None):
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a torch tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    return t
+
+
+def _opt(t, name, dtype, shape=None):
+    return None if t is None else _need(t, name, dtype, shape)
+
+
+def _host_i32(x):
+    """A host int32 numpy copy of an index tensor (a device copy synchronises)."""
+    if isinstance(x, torch.Tensor):
+        x = x.detach().to("cpu")
+        return np.ascontiguousarray(x.numpy().astype(np.int32, copy=False))
+    return np.ascontiguousarray(np.asarray(x, dtype=np.int32))
+
+
+def _hp(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+# ------------------------------------------------------------------ validators
+
+
+def validate_paged(block_tables, seq_lens, seq_offset, num_blocks, block_size):
+    """Host check of paged index content (cumulative seq_lens, offsets, block ids)."""
+    t = _host_i32(block_tables)
+    if t.ndim != 2:
+        raise ValueError("block_tables must be [Q, cols]")
+    s = _host_i32(seq_lens).reshape(-1)
+    Q, cols = t.shape
+    if s.shape != (Q + 1,):
+        raise ValueError("only cumulative seq_lens of length Q + 1 is supported")
+    o = None if seq_offset is None else _host_i32(seq_offset).reshape(-1)
+    if o is not None and o.shape != (Q,):
+        raise ValueError("seq_offset must be [Q]")
+    check("validate_paged", lib().dakv_validate_paged(_hp(t), Q, cols, _hp(s), _hp(o),
+                                                      int(num_blocks), int(block_size)))
+
+
+def validate_sparse(indices, s_kv):
+    a = _host_i32(indices)
+    B, topk = a.shape if a.ndim == 2 else (1, a.size)
+    check("validate_sparse", lib().dakv_validate_sparse(_hp(a), B, topk, int(s_kv)))
+
+
+def validate_range(values, lo, hi):
+    a = _host_i32(values).reshape(-1)
+    check("validate_range", lib().dakv_validate_range(_hp(a), a.size, int(lo), int(hi)))
+
+
+# ------------------------------------------------------------------- kv_append
+
+
+def kv_append(k_cache, v_cache, k_new, v_new, write_pos, mask=None, err_flag=None):
+    """Write k_new/v_new [B, H, D] into row write_pos[b] of k_cache/v_cache [B, H, cap, D]."""
+    _need(k_cache, "k_cache", torch.bfloat16)
+    B, H, cap, D = k_cache.shape
+    _need(v_cache, "v_cache", torch.bfloat16, (B, H, cap, D))
+    _need(k_new, "k_new", torch.bfloat16, (B, H, D))
+    _need(v_new, "v_new", torch.bfloat16, (B, H, D))
+    _need(write_pos, "write_pos", torch.int32, (B,))
+    _opt(mask, "mask", torch.int32, (B, cap))
+    _opt(err_flag, "err_flag", torch.int32, (1,))
+    check("kv_append", lib().dakv_kv_append(_p(k_cache), _p(v_cache), _p(k_new), _p(v_new),
+                                            _p(write_pos), _p(mask), B, H, cap, D,
+                                            _p(err_flag), _stream()))
+
+
+# ---------------------------------------------------------- decode_attn_static
+
+
+def decode_attn_static_workspace_size(B, H, cap, D):
+    return int(lib().dakv_decode_attn_static_workspace_size(B, H, cap, D))
+
+
+def _workspace(nbytes, device, workspace):
+    if workspace is not None:
+        _need(workspace, "workspace", torch.uint8)
+        if workspace.numel() < nbytes:
+            raise ValueError(f"workspace needs {nbytes} bytes")
+        return workspace
+    return torch.empty(max(nbytes, 16), dtype=torch.uint8, device=device)
+
+
+def decode_attn_static(q, k_cache, v_cache, mask=None, valid_len=None, scale=None, out=None,
+                       lse=None, workspace=None, num_splits=0, err_flag=None, want_lse=True):
+    """Decode attention over the static buffer.  Returns ``(out, lse)``.
+
+    q fp32 [B, H, D]; k_cache/v_cache bf16 [B, H, cap, D]; mask int32 [B, cap] and/or
+    valid_len int32 [B].  ``lse`` is None when ``want_lse`` is false and no lse
+    tensor is given.
+    """
+    _need(k_cache, "k_cache", torch.bfloat16)
+    B, H, cap, D = k_cache.shape
+    _need(v_cache, "v_cache", torch.bfloat16, (B, H, cap, D))
+    _need(q, "q", torch.float32, (B, H, D))
+    _opt(mask, "mask", torch.int32, (B, cap))
+    _opt(valid_len, "valid_len", torch.int32, (B,))
+    if mask is None and valid_len is None:
+        raise ValueError("give a mask, a valid length, or both")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty((B, H, D), dtype=torch.float32, device=q.device)
+    _need(out, "out", torch.float32, (B, H, D))
+    if lse is None and want_lse:
+        lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
+    _opt(lse, "lse", torch.float32, (B, H))
+    _opt(err_flag, "err_flag", torch.int32, (1,))
+    nbytes = decode_attn_static_workspace_size(B, H, cap, D)
+    ws = _workspace(nbytes, q.device, workspace)
+    check("decode_attn_static", lib().dakv_decode_attn_static(
+        _p(q), _p(k_cache), _p(v_cache), _p(mask), _p(valid_len), B, H, cap, D, float(scale),
+        _p(out), _p(lse), _p(ws), ws.numel(), int(num_splits), _p(err_flag), _stream()))
+    return out, lse
+
+
+# ---------------------------------------------------------- gather_pa_kv_cache
+
+
+def gather_pa_kv_cache(key_cache, value_cache, block_tables, seq_lens, seq_offset=None,
+                       total_tokens=None, key_out=None, value_out=None, err_flag=None,
+                       validate=True):
+    """Collect paged K/V rows into contiguous [total_tokens, H, D] outputs (bit copy).
+
+    With ``validate`` the index tensors are copied to the host and checked first
+    (the index tensors are host-ready on the pages); ``total_tokens`` defaults to
+    seq_lens[Q] read on the host.
+    """
+    _need(key_cache, "key_cache", torch.bfloat16)
+    _need(value_cache, "value_cache", torch.bfloat16)
+    if key_cache.dim() != 4 or value_cache.dim() != 4:
+        raise ValueError("caches must be [num_blocks, block_size, heads, dim]")
+    nb, bs, Hk, Dk = key_cache.shape
+    nb2, bs2, Hv, Dv = value_cache.shape
+    if (nb, bs) != (nb2, bs2):
+        raise ValueError("key_cache and value_cache must agree on num_blocks, block_size")
+    _need(block_tables, "block_tables", torch.int32)
+    if block_tables.dim() != 2:
+        raise ValueError("block_tables must be [Q, cols]")
+    Q, cols = block_tables.shape
+    _need(seq_lens, "seq_lens", torch.int32)
+    if tuple(seq_lens.shape) != (Q + 1,):
+        raise ValueError("only cumulative seq_lens [Q + 1] is supported")
+    _opt(seq_offset, "seq_offset", torch.int32, (Q,))
+    if validate:
+        validate_paged(block_tables, seq_lens, seq_offset, nb, bs)
+    if total_tokens is None:
+        total_tokens = int(_host_i32(seq_lens)[-1])
+    T = int(total_tokens)
+    if key_out is None:
+        key_out = torch.empty((T, Hk, Dk), dtype=torch.bfloat16, device=key_cache.device)
+    if value_out is None:
+        value_out = torch.empty((T, Hv, Dv), dtype=torch.bfloat16, device=key_cache.device)
+    _need(key_out, "key_out", torch.bfloat16, (T, Hk, Dk))
+    _need(value_out, "value_out", torch.bfloat16, (T, Hv, Dv))
+    _opt(err_flag, "err_flag", torch.int32, (1,))
+    check("gather_pa_kv_cache", lib().dakv_gather_pa_kv_cache(
+        _p(key_cache), _p(value_cache), nb, bs, Hk, Dk, Hv, Dv, _p(block_tables), Q, cols,
+        _p(seq_lens), _p(seq_offset), T, _p(key_out), _p(value_out), _p(err_flag), _stream()))
+    return key_out, value_out
+
+
+# ----------------------------------------------------------- decode_attn_paged
+
+
+def decode_attn_paged_workspace_size(B, Hq, D, max_seq_len, block_size):
+    return int(lib().dakv_decode_attn_paged_workspace_size(B, Hq, D, max_seq_len, block_size))
+
+
+def decode_attn_paged(q, key_cache, value_cache, block_tables, seq_lens, seq_offset=None,
+                      max_seq_len=None, scale=None, out=None, lse=None, workspace=None,
+                      num_splits=0, err_flag=None, validate=False, want_lse=True):
+    """Paged GQA decode attention.  Returns ``(out, lse)``.
+
+    q bf16 [B, Hq, D]; caches bf16 [num_blocks, block_size, Hkv, D]; block_tables
+    int32 [B, cols]; cumulative seq_lens int32 [B + 1]; ``max_seq_len`` is a host
+    upper bound of the lengths (read from seq_lens on the host when omitted).
+    """
+    _need(q, "q", torch.bfloat16)
+    B, Hq, D = q.shape
+    _need(key_cache, "key_cache", torch.bfloat16)
+    nb, bs, Hkv, Dk = key_cache.shape
+    if Dk != D:
+        raise ValueError("key_cache head dim must equal q's")
+    _need(value_cache, "value_cache", torch.bfloat16, (nb, bs, Hkv, D))
+    _need(block_tables, "block_tables", torch.int32)
+    if block_tables.dim() != 2 or block_tables.shape[0] != B:
+        raise ValueError("block_tables must be [B, cols]")
+    cols = block_tables.shape[1]
+    _need(seq_lens, "seq_lens", torch.int32, (B + 1,))
+    _opt(seq_offset, "seq_offset", torch.int32, (B,))
+    if validate:
+        validate_paged(block_tables, seq_lens, seq_offset, nb, bs)
+    if max_seq_len is None:
+        lens = np.diff(_host_i32(seq_lens))
+        max_seq_len = int(lens.max()) if lens.size else 0
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
+    _need(out, "out", torch.float32, (B, Hq, D))
+    if lse is None and want_lse:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    _opt(lse, "lse", torch.float32, (B, Hq))
+    _opt(err_flag, "err_flag", torch.int32, (1,))
+    nbytes = decode_attn_paged_workspace_size(B, Hq, D, int(max_seq_len), bs)
+    ws = _workspace(nbytes, q.device, workspace)
+    check("decode_attn_paged", lib().dakv_decode_attn_paged(
+        _p(q), _p(key_cache), _p(value_cache), _p(block_tables), cols, _p(seq_lens),
+        _p(seq_offset), B, Hq, Hkv, D, nb, bs, int(max_seq_len), float(scale), _p(out), _p(lse),
+        _p(ws), ws.numel(), int(num_splits), _p(err_flag), _stream()))
+    return out, lse
+
+
+# ----------------------------------------------------- sparse_topk_decode_attn
+
+
+def sparse_topk_decode_attn_workspace_size(B, Hq, d_qk, d_v, topk):
+    return int(lib().dakv_sparse_topk_decode_attn_workspace_size(B, Hq, d_qk, d_v, topk))
+
+
+def sparse_topk_decode_attn(q, kv, indices, d_v=512, sm_scale=None, out=None, lse=None,
+                            workspace=None, err_flag=None, validate=False, want_lse=True):
+    """Top-k sparse MLA-style decode.  Returns ``(out, lse)``.
+
+    q bf16 [B, Hq, d_qk]; kv bf16 [B, s_kv, d_qk]; indices int32 [B, topk].
+    """
+    _need(q, "q", torch.bfloat16)
+    B, Hq, d_qk = q.shape
+    _need(kv, "kv", torch.bfloat16)
+    if kv.dim() != 3 or kv.shape[0] != B or kv.shape[2] != d_qk:
+        raise ValueError("kv must be [B, s_kv, d_qk]")
+    s_kv = kv.shape[1]
+    _need(indices, "indices", torch.int32)
+    if indices.dim() != 2 or indices.shape[0] != B:
+        raise ValueError("indices must be [B, topk]")
+    topk = indices.shape[1]
+    if validate:
+        validate_sparse(indices, s_kv)
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(d_qk)
+    if out is None:
+        out = torch.empty((B, Hq, d_v), dtype=torch.float32, device=q.device)
+    _need(out, "out", torch.float32, (B, Hq, d_v))
+    if lse is None and want_lse:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    _opt(lse, "lse", torch.float32, (B, Hq))
+    _opt(err_flag, "err_flag", torch.int32, (1,))
+    nbytes = sparse_topk_decode_attn_workspace_size(B, Hq, d_qk, d_v, topk)
+    ws = _workspace(nbytes, q.device, workspace)
+    check("sparse_topk_decode_attn", lib().dakv_sparse_topk_decode_attn(
+        _p(q), _p(kv), _p(indices), B, Hq, s_kv, d_qk, d_v, topk, float(sm_scale), _p(out),
+        _p(lse), _p(ws), ws.numel(), _p(err_flag), _stream()))
+    return out, lse

@@ -1,0 +1,239 @@
+/*
+ * dakv.h -- decode-phase attention over a KV cache on AMD MI355X (gfx950).
+ *
+ * A C-ABI library: plain pointers and sizes, no framework types.  Every tensor
+ * is caller-owned device memory, dense and row-major in the shape given; the
+ * library never allocates, frees or synchronises.  Each call enqueues its
+ * kernels on `stream` (a hipStream_t; NULL is the null stream) and returns at
+ * once.  Base pointers of tensors must be 16-byte aligned.
+ *
+ * Return value of every entry point: DAKV_OK (0) or a negative DAKV_E* code,
+ * decided on the host before anything is enqueued (DAKV_EHIP: a launch error
+ * reported by the HIP runtime).  Faults that only the device can see (index
+ * content of device tensors) never cause an out-of-bounds access: the kernel
+ * skips the offending unit and ORs a DAKV_ERR_* bit into the optional
+ * caller-owned int32 `err_flag` (pass NULL to ignore).  The host validators
+ * dakv_validate_* check index content on host copies before a call.
+ *
+ * Sources (pages on decode attention; each entry point cites the passage that
+ * defines its operation):
+ *   [NPU-LLM]  OpenVINO community article on LLM inference on the Intel NPU,
+ *              openvinohackathon.51openlab.com article 882, and its retelling
+ *              "NPU 上的 LLM 推理：KV Cache 与软件栈" (jonathanding.github.io).
+ *   [PyPTO]    "PyPTO 实现 AscendC GatherPaKvCache（Norm/ND 分支）", www.mhpn.cn.
+ *   [FlashMLA] "FlashMLA на Huawei Ascend: ядро разреженного внимания изнутри",
+ *              ai.flicky.cc.
+ */
+#ifndef DAKV_H
+#define DAKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ------------------------------------------------------- */
+#define DAKV_OK 0
+#define DAKV_EINVAL (-1)  /* null pointer, bad size, misaligned pointer, short workspace */
+#define DAKV_ENOTSUP (-2) /* a shape no kernel is built for (head_dim, block size, ...) */
+#define DAKV_ERANGE (-3)  /* a host validator found index content outside the contract */
+#define DAKV_EHIP (-4)    /* the HIP runtime reported an error at launch */
+
+/* ---- device error-flag bits (OR-ed into *err_flag) ---------------------- */
+#define DAKV_ERR_BLOCK_ID 1     /* a used block-table entry is outside [0, num_blocks) */
+#define DAKV_ERR_WRITE_POS 2    /* an append position is outside [0, cap) */
+#define DAKV_ERR_SPARSE_INDEX 4 /* a sparse index is outside [0, s_kv) */
+#define DAKV_ERR_SEQ_LENS 8     /* cumulative seq_lens decrease, or a table offset is bad */
+#define DAKV_ERR_VALID_LEN 16   /* a valid length is outside [0, cap] (clamped) */
+
+/* Text for a status code (static storage). */
+const char* dakv_strerror(int code);
+
+/* ========================================================================
+ * Static preallocated KV buffer   ([NPU-LLM] Part 1, "Solution:
+ * preallocation + attention mask"; Part 2, the generate loop)
+ *
+ * Cache layout: k_cache, v_cache bf16 [B, H, cap, D] -- one fixed buffer per
+ * layer; capacity = MAX_PROMPT_LEN + MIN_RESPONSE_LEN on the page (1024+128).
+ * Row t of sequence b is attended iff t < valid_len[b] and mask[b, t] != 0.
+ * ======================================================================== */
+
+/*
+ * kv_append -- write the new token's K and V into the next free row.
+ * [NPU-LLM] Part 2: the cache update writes only the new row (the present
+ * K/V of the new token) into the first empty slot of the past buffer and
+ * increments the stored-row counter.
+ *
+ *   k_cache, v_cache  bf16 [B, H, cap, D], updated in place at row write_pos[b]
+ *   k_new, v_new      bf16 [B, H, D]
+ *   write_pos         int32 [B] device; the row to write (rows stored so far)
+ *   mask              int32 [B, cap] or NULL; when given, mask[b, write_pos[b]] = 1
+ *   err_flag          optional; DAKV_ERR_WRITE_POS if a position is outside
+ *                     [0, cap) -- that sequence is left untouched
+ * Requires D*2 to be a multiple of 16.
+ */
+int dakv_kv_append(void* k_cache, void* v_cache, const void* k_new, const void* v_new,
+                   const int32_t* write_pos, int32_t* mask, int B, int H, int cap, int D,
+                   int32_t* err_flag, void* stream);
+
+/*
+ * Workspace bytes dakv_decode_attn_static needs (split-K partial outputs and
+ * log-sum-exps).  Depends only on the sizes, so one buffer serves every call
+ * of that size.
+ */
+size_t dakv_decode_attn_static_workspace_size(int B, int H, int cap, int D);
+
+/*
+ * decode_attn_static -- one new query row per (sequence, head) attending over
+ * the static buffer.  [NPU-LLM] "Attention on the NPU": decomposed SDPA
+ * (Q K^T, times the scale, plus the mask, softmax, times V) and "incremental
+ * SDPA" (the one-query decode case); Part 1: mask = 0 -> -inf before softmax,
+ * so those rows get weight zero.  The "Flash SDPA" passage: tiles along the
+ * sequence computed independently and merged exactly with a running maximum and
+ * sum -- here split-K over the rows, then a log-sum-exp merge.
+ *
+ *   q          fp32 [B, H, D]
+ *   k_cache    bf16 [B, H, cap, D];  v_cache likewise
+ *   mask       int32 [B, cap] (nonzero = attend) or NULL
+ *   valid_len  int32 [B] device, or NULL (= cap); at least one of mask /
+ *              valid_len.  Values outside [0, cap] are clamped and flagged.
+ *   scale      multiplier of q.k (1/sqrt(D) for standard attention)
+ *   out        fp32 [B, H, D]: sum_t softmax(scale q.K_t) V_t over attended rows;
+ *              zeros when no row is attended
+ *   lse        fp32 [B, H] or NULL: natural log of sum_t exp(scale q.K_t);
+ *              -inf when no row is attended
+ *   workspace  device scratch of at least
+ *              dakv_decode_attn_static_workspace_size(B, H, cap, D) bytes
+ *   num_splits 0 = automatic; n >= 1 forces n splits of the row axis (capped at
+ *              the workspace's maximum)
+ * Rows not attended are never read, so NaN/Inf stored there cannot reach out.
+ * Supported: D in {64, 128}.
+ */
+int dakv_decode_attn_static(const float* q, const void* k_cache, const void* v_cache,
+                            const int32_t* mask, const int32_t* valid_len, int B, int H,
+                            int cap, int D, float scale, float* out, float* lse,
+                            void* workspace, size_t workspace_bytes, int num_splits,
+                            int32_t* err_flag, void* stream);
+
+/* ========================================================================
+ * Paged KV cache   ([PyPTO] section 3, tensor contract and gather semantics)
+ *
+ * key_cache bf16 [num_blocks, block_size, Hk, Dk], value_cache bf16
+ * [num_blocks, block_size, Hv, Dv]; block_tables int32 [Q, table_cols];
+ * seq_lens int32 [Q + 1] cumulative (seq_lens[0] = 0, non-decreasing; sequence
+ * q has seq_lens[q+1] - seq_lens[q] tokens); seq_offset int32 [Q] (multiples of
+ * block_size, >= 0) or NULL (all zero).  Token t of sequence q lives in
+ * physical block block_tables[q, seq_offset[q]/block_size + t/block_size], slot
+ * t % block_size.
+ * ======================================================================== */
+
+/*
+ * gather_pa_kv_cache -- collect each sequence's paged rows into contiguous
+ * outputs.  [PyPTO] 3.2: key_out[seq_lens[q] + t] = key_cache[physical block,
+ * slot] and likewise for values; 3.3: shape constraints; 7: only cumulative
+ * seq_lens.  A bit copy: the outputs equal the source rows bit for bit.
+ *
+ *   key_out    bf16 [total_tokens, Hk, Dk];  value_out bf16 [total_tokens, Hv, Dv]
+ *   total_tokens  host copy of seq_lens[Q]
+ *   err_flag   optional; a used block id outside [0, num_blocks) leaves that
+ *              output row zero and sets DAKV_ERR_BLOCK_ID; inconsistent
+ *              seq_lens set DAKV_ERR_SEQ_LENS (rows past total_tokens are never
+ *              written)
+ * Requires Hk*Dk*2 and Hv*Dv*2 to be multiples of 16.
+ */
+int dakv_gather_pa_kv_cache(const void* key_cache, const void* value_cache, int num_blocks,
+                            int block_size, int Hk, int Dk, int Hv, int Dv,
+                            const int32_t* block_tables, int Q, int table_cols,
+                            const int32_t* seq_lens, const int32_t* seq_offset,
+                            int total_tokens, void* key_out, void* value_out,
+                            int32_t* err_flag, void* stream);
+
+/* Workspace bytes dakv_decode_attn_paged needs for sequences of at most
+ * max_seq_len tokens. */
+size_t dakv_decode_attn_paged_workspace_size(int B, int Hq, int D, int max_seq_len,
+                                             int block_size);
+
+/*
+ * decode_attn_paged -- paged GQA decode attention: the masked-softmax decode of
+ * decode_attn_static over the rows the block table yields (valid length = the
+ * sequence length).  Query head h reads KV head h / (Hq / Hkv): several query
+ * heads share one KV head ([NPU-LLM] closing part, GQA: several Q heads share
+ * the same K/V tile), and its rows are read once for the whole group.
+ *
+ *   q            bf16 [B, Hq, D]
+ *   key_cache    bf16 [num_blocks, block_size, Hkv, D]; value_cache likewise
+ *   block_tables int32 [B, table_cols]; seq_lens int32 [B + 1] cumulative;
+ *   seq_offset   int32 [B] or NULL
+ *   max_seq_len  host upper bound of every sequence length (sizes the splits)
+ *   out          fp32 [B, Hq, D];  lse fp32 [B, Hq] or NULL
+ *   err_flag     optional; a bad block id excludes that block's rows and sets
+ *                DAKV_ERR_BLOCK_ID; a sequence longer than max_seq_len or than
+ *                its table is cut there and sets DAKV_ERR_SEQ_LENS
+ * Supported: D = 128, block_size in {16, 32, 64, 128}, Hq % Hkv == 0,
+ * Hq / Hkv <= 16.
+ */
+int dakv_decode_attn_paged(const void* q, const void* key_cache, const void* value_cache,
+                           const int32_t* block_tables, int table_cols,
+                           const int32_t* seq_lens, const int32_t* seq_offset, int B, int Hq,
+                           int Hkv, int D, int num_blocks, int block_size, int max_seq_len,
+                           float scale, float* out, float* lse, void* workspace,
+                           size_t workspace_bytes, int num_splits, int32_t* err_flag,
+                           void* stream);
+
+/* ========================================================================
+ * Top-k sparse MLA-style decode   ([FlashMLA] "Mathematical formulation")
+ * ======================================================================== */
+
+/* Workspace bytes dakv_sparse_topk_decode_attn needs. */
+size_t dakv_sparse_topk_decode_attn_workspace_size(int B, int Hq, int d_qk, int d_v,
+                                                   int topk);
+
+/*
+ * sparse_topk_decode_attn -- every query head of sequence b attends the topk
+ * rows of its latent cache named by indices[b]:
+ *   G = kv[b][indices[b]]             [topk, d_qk]   (duplicates count twice)
+ *   S = softmax(sm_scale * q[b] G^T)  [Hq, topk]
+ *   out[b] = S G[:, :d_v]             [Hq, d_v]
+ * [FlashMLA] "Mathematical formulation"; "Course of computation": blocks of
+ * the index list, online softmax with running max and sum-exp, S rounded to
+ * bf16 before S.V.
+ *
+ *   q        bf16 [B, Hq, d_qk];  kv bf16 [B, s_kv, d_qk];  indices int32 [B, topk]
+ *   out      fp32 [B, Hq, d_v];   lse fp32 [B, Hq] or NULL (natural log of the
+ *            sum of exp(sm_scale * scores))
+ *   err_flag optional; an index outside [0, s_kv) is skipped and sets
+ *            DAKV_ERR_SPARSE_INDEX
+ * Supported: d_qk = 576, d_v = 512, Hq a multiple of 16 up to 128.
+ */
+int dakv_sparse_topk_decode_attn(const void* q, const void* kv, const int32_t* indices,
+                                 int B, int Hq, int s_kv, int d_qk, int d_v, int topk,
+                                 float sm_scale, float* out, float* lse, void* workspace,
+                                 size_t workspace_bytes, int32_t* err_flag, void* stream);
+
+/* ========================================================================
+ * Host validators (HOST pointers; no GPU needed).  [PyPTO] 3.3 and 5.1: the
+ * index tensors are host-ready and are checked on the host before a call.
+ * Return DAKV_OK, DAKV_EINVAL (null/size) or DAKV_ERANGE (bad content).
+ * ======================================================================== */
+
+/* Cumulative seq_lens [Q+1] from 0, non-decreasing; seq_offset (or NULL) >= 0
+ * and divisible by block_size; every used table entry inside [0, num_blocks);
+ * used columns inside the table. */
+int dakv_validate_paged(const int32_t* block_tables, int Q, int table_cols,
+                        const int32_t* seq_lens, const int32_t* seq_offset, int num_blocks,
+                        int block_size);
+
+/* Every index inside [0, s_kv). */
+int dakv_validate_sparse(const int32_t* indices, int B, int topk, int s_kv);
+
+/* Every value inside [lo, hi] (append positions: [0, cap-1]; valid lengths:
+ * [0, cap]). */
+int dakv_validate_range(const int32_t* values, int n, int lo, int hi);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DAKV_H */

@@ -1,0 +1,149 @@
+"""The C-ABI boundary on the CPU: the library loads, exports every declared entry
+point, and its host-side checks and validators reject what the contract rejects.
+No call here reaches the GPU: every one returns from a host check first."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle.paged import PagedIndexError
+
+import decode_attention_kv_amd as dakv
+from decode_attention_kv_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dakv.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dakv_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_entry_point():
+    names = declared_functions()
+    assert len(names) >= 12
+    lib = dakv.lib()
+    for name in names:
+        assert hasattr(lib, name), name
+    assert set(names) == set(_lib.SIGNATURES), "binding and header disagree"
+
+
+def test_status_texts():
+    for code in (0, -1, -2, -3, -4):
+        assert dakv.strerror(code)
+    assert dakv.strerror(0) == "ok"
+
+
+# ------------------------------------------------------------- host validators
+
+
+def _paged_cases(seed):
+    rng = np.random.default_rng(seed)
+    for _ in range(60):
+        Q = int(rng.integers(1, 6))
+        bs = int(rng.choice([1, 2, 4, 16]))
+        cols = int(rng.integers(1, 6))
+        nb = int(rng.integers(1, 40))
+        lens = rng.integers(0, bs * cols + 1, size=Q)
+        seq = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+        tables = rng.integers(-2, nb + 2, size=(Q, cols)).astype(np.int32)
+        offs = (bs * rng.integers(0, cols, size=Q)).astype(np.int32)
+        kind = rng.integers(0, 6)
+        if kind == 1:
+            offs[0] += 1                       # unaligned
+        elif kind == 2:
+            seq[1:] = seq[1:][::-1].copy()     # may decrease
+        elif kind == 3:
+            seq[0] = 1
+        elif kind == 4:
+            offs[-1] = -bs
+        yield tables, seq, (None if kind == 5 else offs), nb, bs
+
+
+def test_validate_paged_agrees_with_the_oracle():
+    n_ok = n_bad = 0
+    for tables, seq, offs, nb, bs in _paged_cases(40):
+        try:
+            oracle.validate_paged(tables, seq, offs, nb, bs)
+            expect_ok = True
+        except PagedIndexError:
+            expect_ok = False
+        if expect_ok:
+            dakv.validate_paged(tables, seq, offs, nb, bs)
+            n_ok += 1
+        else:
+            with pytest.raises(ValueError):
+                dakv.validate_paged(tables, seq, offs, nb, bs)
+            n_bad += 1
+    assert n_ok > 5 and n_bad > 5
+
+
+def test_validate_paged_rejects_non_cumulative_seq_lens():
+    with pytest.raises(ValueError, match="cumulative"):
+        dakv.validate_paged(np.zeros((2, 3), np.int32), np.array([3, 4], np.int32), None, 4, 2)
+
+
+def test_validate_sparse_and_range():
+    dakv.validate_sparse(np.array([[0, 5, 9]], np.int32), 10)
+    for bad in (-1, 10):
+        with pytest.raises(ValueError):
+            dakv.validate_sparse(np.array([[0, bad]], np.int32), 10)
+    dakv.validate_range(np.array([0, 3, 7], np.int32), 0, 7)
+    with pytest.raises(ValueError):
+        dakv.validate_range(np.array([0, 8], np.int32), 0, 7)
+
+
+# ------------------------------------------------------- argument checks (no GPU)
+
+NULL = None
+
+
+def test_entry_points_reject_bad_arguments_before_any_launch():
+    L = dakv.lib()
+    fake = ctypes.c_void_p(4096)       # aligned, never dereferenced: the checks fail first
+    odd = ctypes.c_void_p(4096 + 8)    # misaligned
+    # kv_append: null cache, negative sizes, D*2 not a multiple of 16
+    assert L.dakv_kv_append(NULL, fake, fake, fake, fake, NULL, 1, 1, 4, 8, NULL, NULL) == _lib.EINVAL
+    assert L.dakv_kv_append(fake, fake, fake, fake, fake, NULL, -1, 1, 4, 8, NULL, NULL) == _lib.EINVAL
+    assert L.dakv_kv_append(fake, fake, fake, fake, fake, NULL, 1, 1, 4, 4, NULL, NULL) == _lib.ENOTSUP
+    assert L.dakv_kv_append(odd, fake, fake, fake, fake, NULL, 1, 1, 4, 8, NULL, NULL) == _lib.EINVAL
+    # empty batch is a no-op success
+    assert L.dakv_kv_append(NULL, NULL, NULL, NULL, NULL, NULL, 0, 1, 4, 8, NULL, NULL) == _lib.OK
+    # decode_attn_static: unsupported D, neither mask nor valid_len, short workspace
+    ws = L.dakv_decode_attn_static_workspace_size(1, 4, 1152, 64)
+    assert ws > 0
+    args = lambda D, mask, vl, wsb: (fake, fake, fake, mask, vl, 1, 4, 1152, D, 0.125, fake,
+                                     NULL, fake, wsb, 0, NULL, NULL)
+    assert L.dakv_decode_attn_static(*args(96, fake, NULL, ws)) == _lib.ENOTSUP
+    assert L.dakv_decode_attn_static(*args(64, NULL, NULL, ws)) == _lib.EINVAL
+    assert L.dakv_decode_attn_static(*args(64, fake, NULL, ws - 4)) == _lib.EINVAL
+    # gather: odd row bytes, zero tables
+    assert L.dakv_gather_pa_kv_cache(fake, fake, 8, 4, 1, 3, 1, 8, fake, 1, 2, fake, NULL, 4,
+                                     fake, fake, NULL, NULL) == _lib.ENOTSUP
+    assert L.dakv_gather_pa_kv_cache(fake, fake, 8, 4, 1, 8, 1, 8, fake, 0, 2, fake, NULL, 4,
+                                     fake, fake, NULL, NULL) == _lib.EINVAL
+    assert L.dakv_gather_pa_kv_cache(fake, fake, 8, 4, 1, 8, 1, 8, fake, 1, 2, fake, NULL, 0,
+                                     fake, fake, NULL, NULL) == _lib.OK
+    # paged: heads not divisible, unsupported block size / head dim
+    wsp = L.dakv_decode_attn_paged_workspace_size(2, 8, 128, 100, 16)
+    pargs = lambda Hq, Hkv, D, bs: (fake, fake, fake, fake, 4, fake, NULL, 2, Hq, Hkv, D, 10, bs,
+                                    100, 0.1, fake, NULL, fake, wsp, 0, NULL, NULL)
+    assert L.dakv_decode_attn_paged(*pargs(8, 3, 128, 16)) == _lib.EINVAL
+    assert L.dakv_decode_attn_paged(*pargs(8, 2, 128, 12)) == _lib.ENOTSUP
+    assert L.dakv_decode_attn_paged(*pargs(8, 2, 64, 16)) == _lib.ENOTSUP
+    # sparse: unsupported dims
+    assert L.dakv_sparse_topk_decode_attn(fake, fake, fake, 1, 128, 100, 256, 128, 8, 0.1, fake,
+                                          NULL, fake, 1 << 20, NULL, NULL) == _lib.ENOTSUP
+
+
+def test_python_binding_rejects_cpu_tensors():
+    import torch
+    k = torch.zeros((1, 1, 4, 8), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU"):
+        dakv.decode_attn_static(torch.zeros((1, 1, 8)), k, k, valid_len=torch.ones(1, dtype=torch.int32))
