@@ -152,6 +152,82 @@ def gather_leg(torch, dakv, workloads, acc, reps=20):
             "frac_of_peak": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
 
 
+def time_call(torch, call, reps=20, warm=3):
+    """Average duration of one call from back-to-back HIP event pairs on the current stream."""
+    for _ in range(warm):
+        call()
+    torch.cuda.synchronize()
+    pairs = []
+    for _ in range(reps):
+        a, b = event_pair(torch)
+        a.record()
+        call()
+        b.record()
+        pairs.append((a, b))
+    torch.cuda.synchronize()
+    return sum(x.elapsed_time(y) for x, y in pairs) / len(pairs)
+
+
+def paged_leg(torch, dakv, workloads, acc):
+    case = workloads.paged_gqa(device="cuda:0", seed=4)
+    idx = case.index
+    t = torch.from_numpy(idx.block_tables).to("cuda:0")
+    s = torch.from_numpy(idx.seq_lens).to("cuda:0")
+    B = len(idx.lengths)
+    out = torch.empty((B, case.Hq, case.D), dtype=torch.float32, device="cuda:0")
+    max_len = max(idx.lengths)
+    ws = torch.empty(dakv.decode_attn_paged_workspace_size(B, case.Hq, case.D, max_len, 16),
+                     dtype=torch.uint8, device="cuda:0")
+    call = lambda: dakv.decode_attn_paged(case.q, case.key_cache, case.value_cache, t, s, None,
+                                          max_seq_len=max_len, scale=case.scale, out=out,
+                                          workspace=ws, want_lse=False)
+    ms = time_call(torch, call)
+    nbytes = acc.decode_paged_bytes(idx.lengths, case.Hq, case.Hkv, case.D, 16)
+    del case, out, ws
+    return {"workload": "paged GQA decode: batch 64, 32 query / 8 KV heads, head_dim 128, "
+                        "block 16, contexts log-uniform [512, 16384]",
+            "total_tokens": int(sum(idx.lengths)), "us_per_call": round(ms * 1e3, 2),
+            "algorithmic_bytes": nbytes, "GBps": round(nbytes / (ms * 1e-3) / 1e9, 1),
+            "frac_of_peak": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+
+
+def sparse_leg(torch, dakv, workloads, acc):
+    case = workloads.sparse_mla(device="cuda:0", seed=5)
+    B, Hq, d_qk = case.q.shape
+    topk = case.indices.shape[1]
+    out = torch.empty((B, Hq, case.d_v), dtype=torch.float32, device="cuda:0")
+    ws = torch.empty(dakv.sparse_topk_decode_attn_workspace_size(B, Hq, d_qk, case.d_v, topk),
+                     dtype=torch.uint8, device="cuda:0")
+    call = lambda: dakv.sparse_topk_decode_attn(case.q, case.kv, case.indices, d_v=case.d_v,
+                                                sm_scale=case.sm_scale, out=out, workspace=ws,
+                                                want_lse=False)
+    # the 604 MB cache exceeds the 256 MB last-level cache, but the 44 MB actually
+    # touched fits: flush it between calls by streaming a 1 GiB buffer
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda:0")
+    pairs = []
+    for r in range(23):
+        flush.fill_(r & 0xFF)
+        a, b = event_pair(torch)
+        a.record()
+        call()
+        b.record()
+        if r >= 3:
+            pairs.append((a, b))
+    torch.cuda.synchronize()
+    ms = sum(x.elapsed_time(y) for x, y in pairs) / len(pairs)
+    warm_ms = time_call(torch, call)
+    nbytes = acc.sparse_bytes(B, Hq, d_qk, case.d_v, topk)
+    flops = acc.sparse_flops(B, Hq, d_qk, case.d_v, topk)
+    del case, out, ws, flush
+    return {"workload": "top-k sparse MLA decode: batch 16, 128 heads on one latent KV, "
+                        "d_qk 576 / d_v 512, context 32768, top-2048",
+            "us_per_call": round(ms * 1e3, 2), "us_per_call_warm_cache": round(warm_ms * 1e3, 2),
+            "algorithmic_bytes": nbytes, "GBps": round(nbytes / (ms * 1e-3) / 1e9, 1),
+            "frac_of_hbm_peak": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "TFLOPs": round(flops / (ms * 1e-3) / 1e12, 1),
+            "frac_of_bf16_mfma_peak": round(flops / (ms * 1e-3) / 2.5e15, 4)}
+
+
 def cpu_baseline(step, budget_s):
     """The fp64 oracle over (layer, sequence) pairs of the same step until the budget is
     spent; GB/s = algorithmic bytes of the pairs done / host seconds."""
@@ -275,6 +351,10 @@ def main():
         del s1
         torch.cuda.empty_cache()
         line["gather"] = gather_leg(torch, dakv, workloads, acc)
+        torch.cuda.empty_cache()
+        line["paged_gqa"] = paged_leg(torch, dakv, workloads, acc)
+        torch.cuda.empty_cache()
+        line["sparse_mla"] = sparse_leg(torch, dakv, workloads, acc)
     print(json.dumps(line), flush=True)
 
 

@@ -1,0 +1,96 @@
+"""GPU parity: sparse_topk_decode_attn (MFMA) vs the fp64 oracle."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+import decode_attention_kv_amd as dakv
+from conftest import assert_attention_close, assert_lse_close, bits, npy
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def run(case, **kw):
+    out, lse = dakv.sparse_topk_decode_attn(case.q, case.kv, case.indices, d_v=case.d_v,
+                                            sm_scale=case.sm_scale, **kw)
+    torch.cuda.synchronize()
+    return npy(out), npy(lse)
+
+
+def ref(case, rows=None):
+    q, kv, idx = bits(case.q), case.kv, npy(case.indices)
+    if rows is not None:
+        q, idx = q[rows], idx[rows]
+        kv = case.kv[rows]
+    return oracle.sparse_topk_decode(q, bits(kv), idx, case.d_v, case.sm_scale)
+
+
+@pytest.mark.parametrize("B,Hq,s_kv,topk", [
+    (2, 16, 1000, 300),     # two splits, ragged last tile
+    (1, 48, 700, 33),       # one head group with an idle wave, ragged tile
+    (2, 64, 5000, 512),
+    (2, 128, 4096, 2048),   # the config's heads and top-k at a smaller context
+    (3, 32, 64, 1),         # a single index
+])
+def test_sparse_matches_oracle(B, Hq, s_kv, topk):
+    print(f"sparse B={B} Hq={Hq} s_kv={s_kv} topk={topk}", flush=True)
+    case = workloads.sparse_case(B, Hq, s_kv, topk, device=DEV, seed=80 + topk)
+    out, lse = run(case)
+    r_out, r_lse = ref(case)
+    assert_attention_close(out, r_out)
+    assert_lse_close(lse, r_lse)
+
+
+def test_sparse_full_index_is_dense_attention():
+    B, Hq, s_kv = 1, 32, 640
+    case = workloads.sparse_case(B, Hq, s_kv, s_kv, device=DEV, seed=90)
+    case.indices = torch.arange(s_kv, dtype=torch.int32, device=DEV)[None].repeat(B, 1).contiguous()
+    out, _ = run(case)
+    r_out, _ = ref(case)
+    assert_attention_close(out, r_out)
+
+
+def test_sparse_duplicates_count_twice_and_order_is_irrelevant():
+    case = workloads.sparse_case(2, 32, 300, 100, device=DEV, seed=91)
+    idx = npy(case.indices).copy()
+    idx[:, 50:60] = idx[:, 0:10]                      # duplicates
+    case.indices = torch.from_numpy(idx).to(DEV)
+    out, _ = run(case)
+    r_out, _ = ref(case)
+    assert_attention_close(out, r_out)
+    case.indices = torch.from_numpy(idx[:, ::-1].copy()).to(DEV)
+    out2, _ = run(case)
+    assert_attention_close(out2, r_out)
+
+
+def test_sparse_out_of_range_index_is_flagged_and_skipped():
+    case = workloads.sparse_case(1, 16, 200, 40, device=DEV, seed=92)
+    idx = npy(case.indices).copy()
+    good = idx.copy()
+    idx[0, 7] = 200
+    idx[0, 30] = -5
+    case.indices = torch.from_numpy(idx).to(DEV)
+    flag = torch.zeros(1, dtype=torch.int32, device=DEV)
+    out, _ = run(case, err_flag=flag)
+    assert int(flag.item()) & dakv._lib.ERR_SPARSE_INDEX
+    keep = [i for i in range(40) if i not in (7, 30)]
+    r_out, _ = oracle.sparse_topk_decode(bits(case.q), bits(case.kv), good[:, keep],
+                                         case.d_v, case.sm_scale)
+    assert_attention_close(out, r_out)
+    with pytest.raises(ValueError):
+        dakv.validate_sparse(idx, 200)
+
+
+def test_sparse_mla_full_size_sampled():
+    """Batch 16, 128 heads, d_qk 576 / d_v 512, context 32768, top-2048: every output of
+    three sequences against the oracle."""
+    print("sparse full size", flush=True)
+    case = workloads.sparse_mla(device=DEV, seed=5)
+    out, lse = run(case)
+    for b in (0, 7, 15):
+        r_out, r_lse = ref(case, rows=slice(b, b + 1))
+        assert_attention_close(out[b:b + 1], r_out)
+        assert_lse_close(lse[b:b + 1], r_lse)
