@@ -14,6 +14,7 @@
 //   * the C layout of S^T puts head (lane % 16) and 4 tokens per half-tile in each
 //     lane, which is already the A layout of P for O = P V when the 8 tokens of a
 //     lane group are taken in the order {4g..4g+3, 16+4g..16+4g+3};
+//   * P enters the matrix core as bf16 hi + lo parts (two MFMAs per block);
 //   * V (the first 512 dims of the same rows) is read from LDS as 8 rows x 16
 //     bytes per lane and transposed in registers into the B operand (8 tokens of
 //     one dim per MFMA), so no transposing LDS access is needed; output column n
@@ -172,12 +173,17 @@ sparse_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
         }
       }
       const float mu = m_ref == kNegInf ? 0.f : m_ref;
-      bf16x8_t pa;
+      // P as two bf16 parts (p = hi + lo to about 16 significant bits): rounding
+      // P to one bf16 alone can put the output off by more than 2e-3 when a few
+      // rows dominate the softmax.
+      bf16x8_t pa, pl;
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
         const float p = exp2_fast(sc[k] - mu);
         lsum += p;
-        pa[k] = (__bf16)p;
+        const __bf16 hi = (__bf16)p;
+        pa[k] = hi;
+        pl[k] = (__bf16)(p - (float)hi);
       }
       // O += P V, four blocks of 128 dims
 #pragma unroll
@@ -197,8 +203,9 @@ sparse_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
             const uint32_t hi = R[2 * k + 1][j >> 1];
             vb[k] = (j & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
           }
-          oacc[c * 8 + j] =
-              __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, as_bf16x8(vb), oacc[c * 8 + j], 0, 0, 0);
+          const bf16x8_t vbf = as_bf16x8(vb);
+          oacc[c * 8 + j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, vbf, oacc[c * 8 + j], 0, 0, 0);
+          oacc[c * 8 + j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl, vbf, oacc[c * 8 + j], 0, 0, 0);
         }
       }
     }
