@@ -59,7 +59,7 @@ class StaticStep:
         self.outs = [torch.empty((B, m.H, m.D), dtype=torch.float32, device="cuda:0")
                      for _ in m.layers]
         nbytes = dakv.decode_attn_static_workspace_size(B, m.H, m.cap, m.D)
-        self.ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0")
+        self.ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda:0")
         self.attn_bytes = acc.decode_static_bytes(B, m.H, m.D, m.lengths, q_elem=acc.FP32,
                                                   with_mask=True, with_lse=False)
         self.append_bytes = acc.kv_append_bytes(B, m.H, m.D, with_mask=True)
@@ -81,26 +81,47 @@ class StaticStep:
             self.append(layer)
             self.attend(i, layer)
 
-    def per_launch_ms(self, reps=2):
-        """Average duration of each decode_attn_static and kv_append call (HIP events
-        on the stream the kernels run on)."""
+    def capture(self, fn):
+        """fn captured once into a HIP graph (torch.cuda.CUDAGraph) after a warm-up."""
         torch = self.torch
-        attn, app = [], []
-        for _ in range(reps):
-            for i, layer in enumerate(self.model.layers):
-                a0, a1 = event_pair(torch)
-                b0, b1 = event_pair(torch)
-                a0.record()
-                self.append(layer)
-                a1.record()
-                b0.record()
-                self.attend(i, layer)
-                b1.record()
-                app.append((a0, a1))
-                attn.append((b0, b1))
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            fn()
+        torch.cuda.current_stream().wait_stream(side)
         torch.cuda.synchronize()
-        avg = lambda pairs: sum(s.elapsed_time(e) for s, e in pairs) / len(pairs)
-        return avg(attn), avg(app)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            fn()
+        torch.cuda.synchronize()
+        return graph
+
+    def attend_all(self):
+        for i, layer in enumerate(self.model.layers):
+            self.attend(i, layer)
+
+    def append_all(self):
+        for layer in self.model.layers:
+            self.append(layer)
+
+    def per_launch_ms(self, reps=10):
+        """Average duration of one decode_attn_static launch and one kv_append launch:
+        a graph of the 32 layers' calls of one kind, timed with HIP events on the
+        stream it replays on, divided by 32 (gaps between the launches included)."""
+        torch = self.torch
+        res = []
+        for fn in (self.attend_all, self.append_all):
+            g = self.capture(fn)
+            g.replay()
+            torch.cuda.synchronize()
+            s, e = event_pair(torch)
+            s.record()
+            for _ in range(reps):
+                g.replay()
+            e.record()
+            torch.cuda.synchronize()
+            res.append(s.elapsed_time(e) / reps / len(self.model.layers))
+        return res[0], res[1]
 
 
 def time_steps(torch, fn, steps, warmup):
@@ -176,7 +197,7 @@ def paged_leg(torch, dakv, workloads, acc):
     B = len(idx.lengths)
     out = torch.empty((B, case.Hq, case.D), dtype=torch.float32, device="cuda:0")
     max_len = max(idx.lengths)
-    ws = torch.empty(dakv.decode_attn_paged_workspace_size(B, case.Hq, case.D, max_len, 16),
+    ws = torch.zeros(dakv.decode_attn_paged_workspace_size(B, case.Hq, case.D, max_len, 16),
                      dtype=torch.uint8, device="cuda:0")
     call = lambda: dakv.decode_attn_paged(case.q, case.key_cache, case.value_cache, t, s, None,
                                           max_seq_len=max_len, scale=case.scale, out=out,
@@ -294,7 +315,9 @@ def main():
 
     B = args.batch
     step = StaticStep(B, torch, dakv, workloads, acc)
-    ms, wall = time_steps(torch, step.run, args.steps, args.warmup)
+    graph = step.capture(step.run)
+    ms, wall = time_steps(torch, graph.replay, args.steps, args.warmup)
+    eager_ms, _ = time_steps(torch, step.run, max(3, args.steps // 4), 1)
     attn_ms, app_ms = step.per_launch_ms()
     value = step.step_bytes / (ms * 1e-3) / 1e9
     attn_gbs = step.attn_bytes / (attn_ms * 1e-3) / 1e9
@@ -308,6 +331,7 @@ def main():
         "warmup": args.warmup,
         "ms_per_step": round(ms, 4),
         "us_per_step": round(ms * 1e3, 1),
+        "us_per_step_eager_launches": round(eager_ms * 1e3, 1),
         "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
         "higher_is_better": True,
         "scaling": "weak",
@@ -323,8 +347,11 @@ def main():
             "parallelism": "none (one GPU)",
             "algorithmic_bytes_per_step": step.step_bytes,
         },
+        "timing": "the 32-layer step is captured once as a HIP graph and replayed; "
+                  "HIP events around the replays",
         "roofline": {
-            "kernel": "decode_attn_static (split pass + merge), one call per layer",
+            "kernel": "static_decode_kernel<128> (split-K with in-kernel merge), one launch "
+                      "per layer; per-launch time from a graph of the 32 launches",
             "bound": "hbm", "achieved": round(attn_gbs, 1), "peak": HBM_PEAK_GBS,
             "unit": "GB/s", "frac": round(attn_gbs / HBM_PEAK_GBS, 4), "traffic": None,
             "bytes_per_launch": step.attn_bytes, "us_per_launch": round(attn_ms * 1e3, 2),
@@ -334,11 +361,12 @@ def main():
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(step, args.cpu_seconds)
-    del step
+    del graph, step
     torch.cuda.empty_cache()
     if not args.no_extras:
         s1 = StaticStep(1, torch, dakv, workloads, acc, seed=12)
-        ms1, _ = time_steps(torch, s1.run, max(args.steps, 20), args.warmup)
+        g1 = s1.capture(s1.run)
+        ms1, _ = time_steps(torch, g1.replay, max(args.steps, 20), args.warmup)
         a1, ap1 = s1.per_launch_ms()
         line["batch1"] = {
             "us_per_step": round(ms1 * 1e3, 1),
@@ -348,7 +376,7 @@ def main():
             "attn_GBps": round(s1.attn_bytes / (a1 * 1e-3) / 1e9, 1),
             "kv_append_us_per_launch": round(ap1 * 1e3, 2),
         }
-        del s1
+        del g1, s1
         torch.cuda.empty_cache()
         line["gather"] = gather_leg(torch, dakv, workloads, acc)
         torch.cuda.empty_cache()

@@ -124,6 +124,7 @@ int dakv_decode_attn_paged(const void* q, const void* key_cache, const void* val
   if (G != 1 && G != 2 && G != 4 && G != 8) return DAKV_ENOTSUP;
   if (block_size != 16 && block_size != 32 && block_size != 64 && block_size != 128)
     return DAKV_ENOTSUP;
+  if (!dakv::paged_supported(max_seq_len, block_size)) return DAKV_ENOTSUP;
   if (!q || !key_cache || !value_cache || !block_tables || !seq_lens || !out || !workspace)
     return DAKV_EINVAL;
   if (!aligned16(q) || !aligned16(key_cache) || !aligned16(value_cache) || !aligned16(out) ||

@@ -1,21 +1,22 @@
 // Decode attention, split-K over the row (sequence) axis, for the static buffer
-// and the paged cache, plus the log-sum-exp merge of the split partials.
+// and the paged cache, with the log-sum-exp merge of the splits folded into the
+// same kernel.
 //
-// Pass 1 -- one workgroup (4 waves) per (sequence, KV head, split).  A row of
-// D = 128 bf16 is 256 bytes = 16 lanes x 16 bytes, so one 128-bit load per lane
+// One workgroup (4 waves) per (sequence, KV head, split of `chunk` rows).  A row
+// of D = 128 bf16 is 256 bytes = 16 lanes x 16 bytes, so one 128-bit load per lane
 // covers 4 rows per wave (8 rows at D = 64).  Each 16-lane group keeps its own
 // running max m, sum l and output o (8 dims per lane) over the rows it sees
-// (online softmax, base 2: log2(e) is folded into the query), the dot product is
-// reduced across the group with DPP row operations, and rows outside the
-// attended set are never loaded.  At the end the groups of a wave merge through
-// cross-lane shuffles, the 4 waves through LDS, and the split writes its
-// normalised partial o / l and log2-sum-exp to the workspace.  For grouped-query
-// attention every loaded K/V row serves all G query heads of its KV head.
+// (online softmax in base 2: log2(e) is folded into the query), the dot product is
+// reduced across the group with DPP row operations, and rows outside the attended
+// set are never loaded.  For grouped-query attention each loaded K/V row serves
+// all G query heads of its KV head.
 //
-// Pass 2 -- one workgroup per (sequence, query head): out = sum_j w_j o_j /
-// sum_j w_j with w_j = 2^(lse_j - max lse); splits whose rows were all masked
-// carry lse = -inf and weight 0.  With a single split this is a copy, so a lone
-// attended row comes out bit-exact.
+// End of a split: the groups of a wave merge through cross-lane shuffles, the 4
+// waves through LDS.  A sequence that fits one split writes out = o / l directly.
+// Otherwise each split stores its normalised partial o / l and log2-sum-exp in the
+// workspace, bumps a per-unit counter, and the last split to arrive merges all of
+// them (weights 2^(lse_j - max)) and resets the counter to zero for the next call.
+// The counters therefore have to be zero before the first call on a workspace.
 #include "device.hpp"
 #include "launch.hpp"
 
@@ -24,6 +25,7 @@ namespace dakv {
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kMinChunk = 64;
+constexpr int kMaxSplits = 256;  // splits one unit may have (merge state lives in LDS)
 
 // Effective row count of a static-buffer sequence: valid_len[b] clamped to
 // [0, cap] (clamping is flagged), or cap without a valid_len.
@@ -56,14 +58,24 @@ __device__ __forceinline__ int paged_len(const int32_t* seq_lens, const int32_t*
   return L;
 }
 
-// Online-softmax state of one query head for one 16-lane (D/8-lane) row group.
+// Online-softmax state of G query heads for one row group (D/8 lanes).
 template <int G>
 struct HeadState {
   float m[G], l[G], o[G][8];
 };
 
-// Merge the row groups of one wave (they differ in the lane bits above the
-// group), so that every group ends with the wave's state.
+template <int G>
+__device__ __forceinline__ void init_state(HeadState<G>& st) {
+#pragma unroll
+  for (int j = 0; j < G; ++j) {
+    st.m[j] = kNegInf;
+    st.l[j] = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) st.o[j][i] = 0.f;
+  }
+}
+
+// Merge the row groups of one wave (they differ in the lane bits above the group).
 template <int LPR, int G>
 __device__ __forceinline__ void merge_groups(HeadState<G>& st) {
 #pragma unroll
@@ -87,62 +99,14 @@ __device__ __forceinline__ void merge_groups(HeadState<G>& st) {
   }
 }
 
-// Cross-wave merge through LDS and the write of this split's partials.
-// ws_o:   [unit heads][max_splits][D]  (normalised o / l)
-// ws_lse: [unit heads][max_splits]     (log2 of sum 2^s, -inf if empty)
-template <int D, int G>
-__device__ __forceinline__ void write_partials(const HeadState<G>& st, int lane, int wave,
-                                               float* __restrict__ ws_o,
-                                               float* __restrict__ ws_lse, size_t head0,
-                                               int split, int max_splits) {
-  constexpr int LPR = D / 8;
-  __shared__ float sm_o[kWaves][G][D];
-  __shared__ float sm_m[kWaves][G];
-  __shared__ float sm_l[kWaves][G];
-  if (lane < LPR) {
-#pragma unroll
-    for (int j = 0; j < G; ++j) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) sm_o[wave][j][lane * 8 + i] = st.o[j][i];
-      if (lane == 0) {
-        sm_m[wave][j] = st.m[j];
-        sm_l[wave][j] = st.l[j];
-      }
-    }
-  }
-  __syncthreads();
-  for (int idx = threadIdx.x; idx < G * D; idx += kThreads) {
-    const int j = idx / D;
-    const int d = idx - j * D;
-    float M = kNegInf;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm_m[w][j]);
-    const size_t unit = (head0 + j) * max_splits + split;
-    if (M == kNegInf) {
-      ws_o[unit * D + d] = 0.f;
-      if (d == 0) ws_lse[unit] = kNegInf;
-      continue;
-    }
-    float num = 0.f, den = 0.f;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      const float wt = exp2_fast(sm_m[w][j] - M);
-      num += wt * sm_o[w][j][d];
-      den += wt * sm_l[w][j];
-    }
-    ws_o[unit * D + d] = num / den;
-    if (d == 0) ws_lse[unit] = M + __log2f(den);
-  }
-}
-
-// The row loop shared by the static and paged kernels.  RowAt(t, ok) returns
-// the element offset of row t's piece for this lane and clears ok when the row
-// must not be read.  q is pre-scaled by scale * log2(e).
+// The row loop shared by the static and paged kernels.  RowAt(t, it_row, ok)
+// gives the element offset of row t's piece for this lane and clears ok for rows
+// that must not be read.  q is pre-scaled by scale * log2(e).
 template <int D, int G, int U, typename RowAt>
 __device__ __forceinline__ void attend_rows(const uint16_t* __restrict__ kc,
-                                            const uint16_t* __restrict__ vc, const float (&q)[G][8],
-                                            int r0, int r1, int wave, int slot, RowAt row_at,
-                                            HeadState<G>& st) {
+                                            const uint16_t* __restrict__ vc,
+                                            const float (&q)[G][8], int r0, int r1, int wave,
+                                            int slot, RowAt row_at, HeadState<G>& st) {
   constexpr int LPR = D / 8;
   constexpr int RPW = 64 / LPR;
   constexpr int kStep = kWaves * RPW * U;
@@ -151,9 +115,10 @@ __device__ __forceinline__ void attend_rows(const uint16_t* __restrict__ kc,
     bool ok[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int t = base + (u * kWaves + wave) * RPW + slot;
+      const int o = (u * kWaves + wave) * RPW + slot;  // row offset inside this step
+      const int t = base + o;
       ok[u] = t < r1;
-      const size_t off = row_at(t, ok[u]);
+      const size_t off = row_at(t, o, base, ok[u]);
       kr[u] = make_uint4(0, 0, 0, 0);
       vr[u] = make_uint4(0, 0, 0, 0);
       if (ok[u]) {
@@ -204,71 +169,216 @@ __device__ __forceinline__ void attend_rows(const uint16_t* __restrict__ kc,
   }
 }
 
-template <int G>
-__device__ __forceinline__ void init_state(HeadState<G>& st) {
-#pragma unroll
-  for (int j = 0; j < G; ++j) {
-    st.m[j] = kNegInf;
-    st.l[j] = 0.f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) st.o[j][i] = 0.f;
-  }
+// Workspace of one decode call (all fp32 except the counters):
+//   o     [units * G][max_splits][D]   normalised partial outputs
+//   lse   [units * G][max_splits]      log2-sum-exp of each partial
+//   count [units]                      splits finished (int32, zero between calls)
+struct Workspace {
+  float* o;
+  float* lse;
+  int32_t* count;
+};
+
+__host__ __device__ inline size_t ws_floats(size_t heads, int max_splits, int D) {
+  return heads * (size_t)max_splits * (size_t)(D + 1);
 }
 
-// ---------------------------------------------------------------- static pass 1
+// End of a split: combine the waves, then either write the output (single
+// split) or store a partial and let the last split of the unit merge.
+//   unit:  index of this workgroup's (sequence, KV head); heads head0 .. head0+G-1
+//   n:     number of splits of this unit (all of them run)
+template <int D, int G>
+__device__ __forceinline__ void finish_split(const HeadState<G>& st, int lane, int wave,
+                                             const Workspace& ws, int unit, size_t head0,
+                                             int split, int n, int max_splits,
+                                             float* __restrict__ out, float* __restrict__ lse) {
+  constexpr int LPR = D / 8;
+  __shared__ float sm_o[kWaves][G][D];
+  __shared__ float sm_m[kWaves][G];
+  __shared__ float sm_l[kWaves][G];
+  __shared__ float sm_lse[G][kMaxSplits];
+  __shared__ float sm_M[G], sm_den[G];
+  __shared__ float4 sm_red[kThreads];
+  __shared__ int sm_last;
+  const int tid = threadIdx.x;
+  if (lane < LPR) {
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) sm_o[wave][j][lane * 8 + i] = st.o[j][i];
+      if (lane == 0) {
+        sm_m[wave][j] = st.m[j];
+        sm_l[wave][j] = st.l[j];
+      }
+    }
+  }
+  __syncthreads();
+  for (int idx = tid; idx < G * D; idx += kThreads) {
+    const int j = idx / D;
+    const int d = idx - j * D;
+    float M = kNegInf;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm_m[w][j]);
+    float val = 0.f, lse2 = kNegInf;
+    if (M != kNegInf) {
+      float num = 0.f, den = 0.f;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const float wt = exp2_fast(sm_m[w][j] - M);
+        num += wt * sm_o[w][j][d];
+        den += wt * sm_l[w][j];
+      }
+      val = num / den;
+      lse2 = M + __log2f(den);
+    }
+    if (n == 1) {
+      out[(head0 + j) * D + d] = val;
+      if (lse && d == 0) lse[head0 + j] = lse2 * kLn2;
+    } else {
+      const size_t row = (head0 + j) * max_splits + split;
+      ws.o[row * D + d] = val;
+      if (d == 0) ws.lse[row] = lse2;
+    }
+  }
+  if (n == 1) return;
+
+  // publish the partial, count this split, and find out whether it is the last
+  __threadfence();
+  __syncthreads();
+  if (tid == 0) sm_last = atomicAdd(ws.count + unit, 1) == n - 1;
+  __syncthreads();
+  if (!sm_last) return;
+  __threadfence();
+
+  for (int idx = tid; idx < G * n; idx += kThreads) {
+    const int j = idx / n;
+    const int s = idx - j * n;
+    sm_lse[j][s] = ws.lse[(head0 + j) * max_splits + s];
+  }
+  __syncthreads();
+  if (tid < G) {
+    float M = kNegInf;
+    for (int s = 0; s < n; ++s) M = fmaxf(M, sm_lse[tid][s]);
+    float den = 0.f;
+    if (M != kNegInf)
+      for (int s = 0; s < n; ++s) den += exp2_fast(sm_lse[tid][s] - M);
+    sm_M[tid] = M;
+    sm_den[tid] = den;
+  }
+  __syncthreads();
+  // G*D/4 float4 columns; the threads split the partials into `groups` strided sets
+  constexpr int kCols = G * D / 4;
+  constexpr int kGroups = kThreads / kCols > 0 ? kThreads / kCols : 1;
+  for (int c = tid % kCols; c < kCols && tid < kCols * kGroups; c += kCols) {
+    const int grp = tid / kCols;
+    const int j = (c * 4) / D;
+    const int d = c * 4 - j * D;
+    const float M = sm_M[j];
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (M != kNegInf) {
+      const float* base = ws.o + ((head0 + j) * max_splits) * D + d;
+      for (int s = grp; s < n; s += kGroups) {
+        const float w = exp2_fast(sm_lse[j][s] - M);
+        const float4 v = *reinterpret_cast<const float4*>(base + (size_t)s * D);
+        acc.x += w * v.x; acc.y += w * v.y; acc.z += w * v.z; acc.w += w * v.w;
+      }
+    }
+    sm_red[tid] = acc;
+  }
+  __syncthreads();
+  if (tid < kCols) {
+    const int j = (tid * 4) / D;
+    const int d = tid * 4 - j * D;
+    float4 acc = sm_red[tid];
+    for (int g = 1; g < kGroups; ++g) {
+      const float4 v = sm_red[tid + g * kCols];
+      acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+    }
+    const float M = sm_M[j];
+    float4 r = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (M != kNegInf) {
+      const float inv = 1.f / sm_den[j];
+      r = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+    }
+    *reinterpret_cast<float4*>(out + (head0 + j) * D + d) = r;
+    if (lse && d == 0) lse[head0 + j] = M == kNegInf ? kNegInf : (M + __log2f(sm_den[j])) * kLn2;
+  }
+  if (tid == 0) atomicExch(ws.count + unit, 0);
+}
+
+// ---------------------------------------------------------------- static layout
 template <int D>
 __global__ void __launch_bounds__(kThreads)
-static_split_kernel(const float* __restrict__ q, const uint16_t* __restrict__ k_cache,
-                    const uint16_t* __restrict__ v_cache, const int32_t* __restrict__ mask,
-                    const int32_t* __restrict__ valid_len, int H, int cap, float scale_log2,
-                    int chunk, int max_splits, float* __restrict__ ws_o,
-                    float* __restrict__ ws_lse, int32_t* err_flag) {
+static_decode_kernel(const float* __restrict__ q, const uint16_t* __restrict__ k_cache,
+                     const uint16_t* __restrict__ v_cache, const int32_t* __restrict__ mask,
+                     const int32_t* __restrict__ valid_len, int H, int cap, float scale_log2,
+                     int chunk, int max_splits, Workspace ws, float* __restrict__ out,
+                     float* __restrict__ lse, int32_t* err_flag) {
   constexpr int LPR = D / 8;
+  constexpr int RPW = 64 / LPR;
   constexpr int U = 4;
+  constexpr int kStep = kWaves * RPW * U;   // rows per loop step: 64 (D=128), 128 (D=64)
+  constexpr int kBallots = kStep / 64;
   const int split = blockIdx.x % max_splits;
   const int bh = blockIdx.x / max_splits;
   const int b = bh / H;
-  const int L = static_len(valid_len, b, cap, err_flag, split == 0 && bh % H == 0 && threadIdx.x == 0);
+  const int L = static_len(valid_len, b, cap, err_flag,
+                           split == 0 && bh % H == 0 && threadIdx.x == 0);
+  const int n = L > 0 ? (L + chunk - 1) / chunk : 1;
+  if (split >= n) return;
   const int r0 = split * chunk;
-  if (r0 >= L) return;
   const int r1 = min(r0 + chunk, L);
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int slot = lane / LPR;
   const int sub = lane % LPR;
 
   float qr[1][8];
   {
-    const float* qp = q + (size_t)bh * D + sub * 8;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) qr[0][i] = qp[i] * scale_log2;
+    const float4* qp = reinterpret_cast<const float4*>(q + (size_t)bh * D + sub * 8);
+    const float4 a = qp[0], c = qp[1];
+    qr[0][0] = a.x * scale_log2; qr[0][1] = a.y * scale_log2;
+    qr[0][2] = a.z * scale_log2; qr[0][3] = a.w * scale_log2;
+    qr[0][4] = c.x * scale_log2; qr[0][5] = c.y * scale_log2;
+    qr[0][6] = c.z * scale_log2; qr[0][7] = c.w * scale_log2;
   }
   const size_t head_base = (size_t)bh * cap * D + (size_t)sub * 8;
   const int32_t* mrow = mask ? mask + (size_t)b * cap : nullptr;
-  auto row_at = [&](int t, bool& ok) -> size_t {
-    if (ok && mrow) ok = mrow[t] != 0;
+  // attended-row bits of the current step, one 64-row ballot per wave-wide load
+  uint64_t bits[kBallots];
+  int bits_base = -1;
+  auto row_at = [&](int t, int o, int base, bool& ok) -> size_t {
+    if (mrow) {
+      if (bits_base != base) {
+#pragma unroll
+        for (int k = 0; k < kBallots; ++k) {
+          const int tt = base + 64 * k + lane;
+          bits[k] = __ballot(tt < r1 && mrow[tt] != 0);
+        }
+        bits_base = base;
+      }
+      ok = ok && ((bits[o >> 6] >> (o & 63)) & 1ull);
+    }
     return head_base + (size_t)t * D;
   };
   HeadState<1> st;
   init_state(st);
   attend_rows<D, 1, U>(k_cache, v_cache, qr, r0, r1, wave, lane / LPR, row_at, st);
-  (void)slot;
   merge_groups<LPR, 1>(st);
-  write_partials<D, 1>(st, lane, wave, ws_o, ws_lse, (size_t)bh, split, max_splits);
+  finish_split<D, 1>(st, lane, wave, ws, bh, (size_t)bh, split, n, max_splits, out, lse);
 }
 
-// ----------------------------------------------------------------- paged pass 1
+// ------------------------------------------------------------------ paged layout
 constexpr int kMaxTableSpan = 72;  // block-table entries one split may touch
 
 template <int G>
 __global__ void __launch_bounds__(kThreads)
-paged_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ key_cache,
-                   const uint16_t* __restrict__ value_cache,
-                   const int32_t* __restrict__ block_tables, int table_cols,
-                   const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ seq_offset,
-                   int Hq, int Hkv, int num_blocks, int block_size, int bs_log2, int max_len,
-                   float scale_log2, int chunk, int max_splits, float* __restrict__ ws_o,
-                   float* __restrict__ ws_lse, int32_t* err_flag) {
+paged_decode_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ key_cache,
+                    const uint16_t* __restrict__ value_cache,
+                    const int32_t* __restrict__ block_tables, int table_cols,
+                    const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ seq_offset,
+                    int Hq, int Hkv, int num_blocks, int block_size, int bs_log2, int max_len,
+                    float scale_log2, int chunk, int max_splits, Workspace ws,
+                    float* __restrict__ out, float* __restrict__ lse, int32_t* err_flag) {
   constexpr int D = 128;
   constexpr int LPR = D / 8;
   constexpr int U = G >= 4 ? 2 : 4;
@@ -280,11 +390,12 @@ paged_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
   int toff = 0;
   const int L = paged_len(seq_lens, seq_offset, b, block_size, table_cols, max_len, &toff,
                           err_flag, split == 0 && g == 0 && threadIdx.x == 0);
+  const int n = L > 0 ? (L + chunk - 1) / chunk : 1;
+  if (split >= n) return;
   const int r0 = split * chunk;
-  if (r0 >= L) return;
   const int r1 = min(r0 + chunk, L);
   const int blk0 = r0 >> bs_log2;
-  const int nblk = ((r1 - 1) >> bs_log2) - blk0 + 1;
+  const int nblk = r1 > r0 ? ((r1 - 1) >> bs_log2) - blk0 + 1 : 0;
   for (int i = threadIdx.x; i < nblk; i += kThreads) {
     int phys = block_tables[(size_t)b * table_cols + toff + blk0 + i];
     if (phys < 0 || phys >= num_blocks) {
@@ -309,58 +420,21 @@ paged_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
   const size_t row_stride = (size_t)Hkv * D;
   const size_t head_off = (size_t)g * D + (size_t)sub * 8;
   const int bs_mask = block_size - 1;
-  auto row_at = [&](int t, bool& ok) -> size_t {
+  auto row_at = [&](int t, int, int, bool& ok) -> size_t {
     if (!ok) return 0;
     const int phys = tbl[(t >> bs_log2) - blk0];
-    if (phys < 0) { ok = false; return 0; }
+    if (phys < 0) {
+      ok = false;
+      return 0;
+    }
     return ((size_t)phys * block_size + (t & bs_mask)) * row_stride + head_off;
   };
   HeadState<G> st;
   init_state(st);
   attend_rows<D, G, U>(key_cache, value_cache, qr, r0, r1, wave, lane / LPR, row_at, st);
   merge_groups<LPR, G>(st);
-  write_partials<D, G>(st, lane, wave, ws_o, ws_lse, (size_t)b * Hq + (size_t)g * group, split,
-                       max_splits);
-}
-
-// ------------------------------------------------------------------- pass 2
-// Length modes: 0 = static with valid_len (or cap), 1 = paged.
-template <int D>
-__global__ void __launch_bounds__(D)
-merge_kernel(const float* __restrict__ ws_o, const float* __restrict__ ws_lse, int heads,
-             int chunk, int max_splits, int mode, const int32_t* __restrict__ valid_len, int cap,
-             const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ seq_offset,
-             int block_size, int table_cols, int max_len, float* __restrict__ out,
-             float* __restrict__ lse) {
-  const int bh = blockIdx.x;
-  const int b = bh / heads;
-  const int d = threadIdx.x;
-  int L;
-  if (mode == 0) {
-    L = static_len(valid_len, b, cap, nullptr, false);
-  } else {
-    int toff;
-    L = paged_len(seq_lens, seq_offset, b, block_size, table_cols, max_len, &toff, nullptr,
-                  false);
-  }
-  const int n = (L + chunk - 1) / chunk;
-  const float* lp = ws_lse + (size_t)bh * max_splits;
-  const float* op = ws_o + (size_t)bh * max_splits * D + d;
-  float M = kNegInf;
-  for (int j = 0; j < n; ++j) M = fmaxf(M, lp[j]);
-  if (M == kNegInf) {
-    out[(size_t)bh * D + d] = 0.f;
-    if (lse && d == 0) lse[bh] = kNegInf;
-    return;
-  }
-  float num = 0.f, den = 0.f;
-  for (int j = 0; j < n; ++j) {
-    const float w = exp2_fast(lp[j] - M);
-    num += w * op[(size_t)j * D];
-    den += w;
-  }
-  out[(size_t)bh * D + d] = num / den;
-  if (lse && d == 0) lse[bh] = (M + __log2f(den)) * kLn2;
+  finish_split<D, G>(st, lane, wave, ws, bg, (size_t)b * Hq + (size_t)g * group, split, n,
+                     max_splits, out, lse);
 }
 
 // ------------------------------------------------------------------- planning
@@ -369,49 +443,59 @@ static int round_up(int x, int m) { return (x + m - 1) / m * m; }
 SplitPlan plan_static(int B, int H, int cap, int D, int forced_splits) {
   (void)D;
   SplitPlan p;
+  const int least = round_up((cap + kMaxSplits - 1) / kMaxSplits, kMinChunk);
+  int c;
   if (forced_splits > 0) {
-    const int per = (cap + forced_splits - 1) / forced_splits;
-    p.chunk = per < kMinChunk ? kMinChunk : round_up(per, kMinChunk);
+    c = round_up((cap + forced_splits - 1) / forced_splits, kMinChunk);
   } else {
-    // about 2048 workgroup slots at full capacity; 64..1024 rows per split
-    long long want = ((long long)B * H * cap + 2047) / 2048;
-    int c = (int)(want > 1024 ? 1024 : want);
-    p.chunk = c < kMinChunk ? kMinChunk : round_up(c, kMinChunk);
+    // about 4096 workgroups at full capacity, at most 256 rows each
+    const long long want = ((long long)B * H * cap + 4095) / 4096;
+    c = round_up((int)(want > 256 ? 256 : want), kMinChunk);
   }
-  if (cap <= 0) p.chunk = kMinChunk;
-  p.max_splits = cap > 0 ? (cap + p.chunk - 1) / p.chunk : 1;
+  if (c < kMinChunk) c = kMinChunk;
+  if (c < least) c = least;
+  p.chunk = c;
+  p.max_splits = cap > 0 ? (cap + c - 1) / c : 1;
   return p;
 }
 
 size_t static_workspace_bytes(int B, int H, int cap, int D) {
-  const size_t splits = cap > 0 ? (size_t)(cap + kMinChunk - 1) / kMinChunk : 1;
-  return (size_t)B * H * splits * (size_t)(D + 1) * sizeof(float);
+  const int least = round_up((cap + kMaxSplits - 1) / kMaxSplits, kMinChunk);
+  const int c = least > kMinChunk ? least : kMinChunk;
+  const int splits = cap > 0 ? (cap + c - 1) / c : 1;
+  return ws_floats((size_t)B * H, splits, D) * sizeof(float) + (size_t)B * H * sizeof(int32_t);
+}
+
+static Workspace carve(void* ws, size_t heads, int max_splits, int D) {
+  Workspace w;
+  w.o = static_cast<float*>(ws);
+  w.lse = w.o + heads * (size_t)max_splits * D;
+  w.count = reinterpret_cast<int32_t*>(w.lse + heads * (size_t)max_splits);
+  return w;
 }
 
 hipError_t launch_decode_static(const float* q, const void* k_cache, const void* v_cache,
                                 const int32_t* mask, const int32_t* valid_len, int B, int H,
                                 int cap, int D, float scale, float* out, float* lse, void* ws,
                                 const SplitPlan& plan, int32_t* err_flag, hipStream_t stream) {
-  float* ws_o = static_cast<float*>(ws);
-  float* ws_lse = ws_o + (size_t)B * H * plan.max_splits * D;
+  // the counters sit after the largest o/lse area so that they do not move
+  // between plans of the same sizes
+  const SplitPlan widest = plan_static(B, H, cap, D, kMaxSplits);
+  Workspace w = carve(ws, (size_t)B * H, plan.max_splits, D);
+  w.count = reinterpret_cast<int32_t*>(static_cast<float*>(ws) +
+                                       ws_floats((size_t)B * H, widest.max_splits, D));
   const float scale_log2 = scale * kLog2e;
-  const dim3 grid1((unsigned)(B * H * plan.max_splits));
+  const dim3 grid((unsigned)(B * H * plan.max_splits));
   const auto* kc = static_cast<const uint16_t*>(k_cache);
   const auto* vc = static_cast<const uint16_t*>(v_cache);
   if (D == 128) {
-    hipLaunchKernelGGL(static_split_kernel<128>, grid1, dim3(kThreads), 0, stream, q, kc, vc,
-                       mask, valid_len, H, cap, scale_log2, plan.chunk, plan.max_splits, ws_o,
-                       ws_lse, err_flag);
-    hipLaunchKernelGGL(merge_kernel<128>, dim3(B * H), dim3(128), 0, stream, ws_o, ws_lse, H,
-                       plan.chunk, plan.max_splits, 0, valid_len, cap, nullptr, nullptr, 1, 0, 0,
-                       out, lse);
+    hipLaunchKernelGGL(static_decode_kernel<128>, grid, dim3(kThreads), 0, stream, q, kc, vc,
+                       mask, valid_len, H, cap, scale_log2, plan.chunk, plan.max_splits, w, out,
+                       lse, err_flag);
   } else {
-    hipLaunchKernelGGL(static_split_kernel<64>, grid1, dim3(kThreads), 0, stream, q, kc, vc,
-                       mask, valid_len, H, cap, scale_log2, plan.chunk, plan.max_splits, ws_o,
-                       ws_lse, err_flag);
-    hipLaunchKernelGGL(merge_kernel<64>, dim3(B * H), dim3(64), 0, stream, ws_o, ws_lse, H,
-                       plan.chunk, plan.max_splits, 0, valid_len, cap, nullptr, nullptr, 1, 0, 0,
-                       out, lse);
+    hipLaunchKernelGGL(static_decode_kernel<64>, grid, dim3(kThreads), 0, stream, q, kc, vc,
+                       mask, valid_len, H, cap, scale_log2, plan.chunk, plan.max_splits, w, out,
+                       lse, err_flag);
   }
   return hipGetLastError();
 }
@@ -419,27 +503,37 @@ hipError_t launch_decode_static(const float* q, const void* k_cache, const void*
 SplitPlan plan_paged(int B, int Hkv, int max_seq_len, int block_size, int forced_splits) {
   SplitPlan p;
   const int unit = block_size > kMinChunk ? block_size : kMinChunk;
-  // one split may touch at most kMaxTableSpan - 1 blocks
+  // one split may touch at most kMaxTableSpan - 2 blocks
   const int most = ((kMaxTableSpan - 2) * block_size) / unit * unit;
+  const int least = round_up((max_seq_len + kMaxSplits - 1) / kMaxSplits, unit);
   int c;
   if (forced_splits > 0) {
     c = round_up((max_seq_len + forced_splits - 1) / forced_splits, unit);
   } else {
-    long long want = ((long long)B * Hkv * max_seq_len + 2047) / 2048;
+    const long long want = ((long long)B * Hkv * max_seq_len + 4095) / 4096;
     c = (int)(want > 512 ? 512 : want);
     c = round_up(c < 1 ? 1 : c, unit);
   }
   if (c < unit) c = unit;
   if (c > most) c = most;
+  if (c < least) c = least;
   p.chunk = c;
   p.max_splits = max_seq_len > 0 ? (max_seq_len + c - 1) / c : 1;
   return p;
 }
 
+bool paged_supported(int max_seq_len, int block_size) {
+  const int unit = block_size > kMinChunk ? block_size : kMinChunk;
+  const int most = ((kMaxTableSpan - 2) * block_size) / unit * unit;
+  return (long long)most * kMaxSplits >= max_seq_len;
+}
+
 size_t paged_workspace_bytes(int B, int Hq, int D, int max_seq_len, int block_size) {
   const int unit = block_size > kMinChunk ? block_size : kMinChunk;
-  const size_t splits = max_seq_len > 0 ? (size_t)(max_seq_len + unit - 1) / unit : 1;
-  return (size_t)B * Hq * splits * (size_t)(D + 1) * sizeof(float);
+  const int least = round_up((max_seq_len + kMaxSplits - 1) / kMaxSplits, unit);
+  const int c = least > unit ? least : unit;
+  const int splits = max_seq_len > 0 ? (max_seq_len + c - 1) / c : 1;
+  return ws_floats((size_t)B * Hq, splits, D) * sizeof(float) + (size_t)B * Hq * sizeof(int32_t);
 }
 
 hipError_t launch_decode_paged(const void* q, const void* key_cache, const void* value_cache,
@@ -449,21 +543,26 @@ hipError_t launch_decode_paged(const void* q, const void* key_cache, const void*
                                int max_seq_len, float scale, float* out, float* lse, void* ws,
                                const SplitPlan& plan, int32_t* err_flag, hipStream_t stream) {
   (void)D;
-  float* ws_o = static_cast<float*>(ws);
-  float* ws_lse = ws_o + (size_t)B * Hq * plan.max_splits * 128;
+  const int unit = block_size > kMinChunk ? block_size : kMinChunk;
+  const int least = round_up((max_seq_len + kMaxSplits - 1) / kMaxSplits, unit);
+  const int c = least > unit ? least : unit;
+  const int widest = max_seq_len > 0 ? (max_seq_len + c - 1) / c : 1;
+  Workspace w = carve(ws, (size_t)B * Hq, plan.max_splits, 128);
+  w.count = reinterpret_cast<int32_t*>(static_cast<float*>(ws) +
+                                       ws_floats((size_t)B * Hq, widest, 128));
   const float scale_log2 = scale * kLog2e;
   int bs_log2 = 0;
   while ((1 << bs_log2) < block_size) ++bs_log2;
-  const dim3 grid1((unsigned)(B * Hkv * plan.max_splits));
+  const dim3 grid((unsigned)(B * Hkv * plan.max_splits));
   const auto* qb = static_cast<const uint16_t*>(q);
   const auto* kc = static_cast<const uint16_t*>(key_cache);
   const auto* vc = static_cast<const uint16_t*>(value_cache);
   const int G = Hq / Hkv;
 #define DAKV_PAGED(GG)                                                                        \
-  hipLaunchKernelGGL(paged_split_kernel<GG>, grid1, dim3(kThreads), 0, stream, qb, kc, vc,   \
+  hipLaunchKernelGGL(paged_decode_kernel<GG>, grid, dim3(kThreads), 0, stream, qb, kc, vc,   \
                      block_tables, table_cols, seq_lens, seq_offset, Hq, Hkv, num_blocks,    \
                      block_size, bs_log2, max_seq_len, scale_log2, plan.chunk,               \
-                     plan.max_splits, ws_o, ws_lse, err_flag)
+                     plan.max_splits, w, out, lse, err_flag)
   switch (G) {
     case 1: DAKV_PAGED(1); break;
     case 2: DAKV_PAGED(2); break;
@@ -472,9 +571,6 @@ hipError_t launch_decode_paged(const void* q, const void* key_cache, const void*
     default: return hipErrorInvalidValue;
   }
 #undef DAKV_PAGED
-  hipLaunchKernelGGL(merge_kernel<128>, dim3(B * Hq), dim3(128), 0, stream, ws_o, ws_lse, Hq,
-                     plan.chunk, plan.max_splits, 1, nullptr, 0, seq_lens, seq_offset, block_size,
-                     table_cols, max_seq_len, out, lse);
   return hipGetLastError();
 }
 

@@ -33,6 +33,8 @@ hipError_t launch_decode_static(const float* q, const void* k_cache, const void*
                                 const SplitPlan& plan, int32_t* err_flag, hipStream_t stream);
 
 SplitPlan plan_paged(int B, int Hkv, int max_seq_len, int block_size, int forced_splits);
+// Whether a sequence of max_seq_len tokens fits the split limits of the paged kernel.
+bool paged_supported(int max_seq_len, int block_size);
 size_t paged_workspace_bytes(int B, int Hq, int D, int max_seq_len, int block_size);
 hipError_t launch_decode_paged(const void* q, const void* key_cache, const void* value_cache,
                                const int32_t* block_tables, int table_cols,

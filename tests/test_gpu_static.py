@@ -238,3 +238,72 @@ def test_llama_layer_step_full_size_sampled(B):
             assert np.array_equal(bits(layer.k_cache[b, :, L - 1]), bits(layer.k_new[b]))
     del model
     torch.cuda.empty_cache()
+
+
+def test_graph_replay_of_append_and_attend_matches_eager():
+    """A 3-layer append+attend step captured as a HIP graph: every replay (with eager
+    work and synchronisation between replays) gives exactly the eager outputs."""
+    model = workloads.static_llama_layers(2, n_layers=3, H=8, D=128, cap=1024, device=DEV,
+                                          seed=31, lengths=[1000, 77])
+    ws = torch.zeros(dakv.decode_attn_static_workspace_size(2, 8, 1024, 128), dtype=torch.uint8,
+                     device=DEV)
+    outs = [torch.empty((2, 8, 128), dtype=torch.float32, device=DEV) for _ in model.layers]
+    lses = [torch.empty((2, 8), dtype=torch.float32, device=DEV) for _ in model.layers]
+
+    def step():
+        for i, layer in enumerate(model.layers):
+            dakv.kv_append(layer.k_cache, layer.v_cache, layer.k_new, layer.v_new,
+                           model.write_pos, model.mask)
+            dakv.decode_attn_static(layer.q, layer.k_cache, layer.v_cache, mask=model.mask,
+                                    valid_len=model.valid_len, scale=model.scale, out=outs[i],
+                                    lse=lses[i], workspace=ws)
+
+    step()
+    torch.cuda.synchronize()
+    eager = [(npy(o).copy(), npy(l).copy()) for o, l in zip(outs, lses)]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for r in range(4):
+        for o in outs:
+            o.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for i, (o, l) in enumerate(zip(outs, lses)):
+            assert np.array_equal(npy(o), eager[i][0]), (r, i)
+            assert np.array_equal(npy(l), eager[i][1]), (r, i)
+        dakv.decode_attn_static(model.layers[0].q, model.layers[0].k_cache,
+                                model.layers[0].v_cache, valid_len=model.valid_len,
+                                scale=model.scale, workspace=ws)
+        torch.cuda.synchronize()
+    ref, _ = oracle.decode_static(npy(model.layers[2].q), bits(model.layers[2].k_cache),
+                                  bits(model.layers[2].v_cache), npy(model.mask) * 0 + 1,
+                                  model.lengths, model.scale)
+    assert_attention_close(eager[2][0], ref)
+    del graph
+
+
+def test_many_splits_merge_and_workspace_reuse():
+    """Capacity 16384 at batch 1 gives 64-row splits (up to 256 per head): the in-kernel
+    merge of many partials, repeated on one workspace, stays at the oracle."""
+    case = workloads.static_case(1, 4, 128, 16384, [16384], device=DEV, seed=32,
+                                 garbage_std=1.0)
+    ws = torch.zeros(dakv.decode_attn_static_workspace_size(1, 4, 16384, 128),
+                     dtype=torch.uint8, device=DEV)
+    ref_out, ref_lse = oracle_static(case)
+    for n in (0, 256, 3, 0):
+        out, lse = dakv.decode_attn_static(case.q, case.k_cache, case.v_cache,
+                                           valid_len=case.valid_len, scale=case.scale,
+                                           workspace=ws, num_splits=n)
+        torch.cuda.synchronize()
+        assert_attention_close(npy(out), ref_out)
+        assert_lse_close(npy(lse), ref_lse)
+    counters = ws.view(torch.int32)[-4:]
+    assert int(counters.abs().sum()) == 0
