@@ -1,6 +1,5 @@
 // Decode attention, split-K over the row (sequence) axis, for the static buffer
-// and the paged cache, with the log-sum-exp merge of the splits folded into the
-// same kernel.
+// and the paged cache, and the log-sum-exp merge of the splits.
 //
 // One workgroup (4 waves) per (sequence, KV head, split of `chunk` rows).  A row
 // of D = 128 bf16 is 256 bytes = 16 lanes x 16 bytes, so one 128-bit load per lane
@@ -14,9 +13,10 @@
 // End of a split: the groups of a wave merge through cross-lane shuffles, the 4
 // waves through LDS.  A sequence that fits one split writes out = o / l directly.
 // Otherwise each split stores its normalised partial o / l and log2-sum-exp in the
-// workspace, bumps a per-unit counter, and the last split to arrive merges all of
-// them (weights 2^(lse_j - max)) and resets the counter to zero for the next call.
-// The counters therefore have to be zero before the first call on a workspace.
+// workspace and merge_kernel combines them (weights 2^(lse_j - max)).  (Merging in
+// the last split to finish would need device-scope fences between workgroups; on
+// this chip those write back and invalidate the L2 of the XCD, which costs far
+// more than the second launch.)
 #include "device.hpp"
 #include "launch.hpp"
 
@@ -169,38 +169,29 @@ __device__ __forceinline__ void attend_rows(const uint16_t* __restrict__ kc,
   }
 }
 
-// Workspace of one decode call (all fp32 except the counters):
-//   o     [units * G][max_splits][D]   normalised partial outputs
-//   lse   [units * G][max_splits]      log2-sum-exp of each partial
-//   count [units]                      splits finished (int32, zero between calls)
+// Workspace of one decode call (fp32):
+//   o   [units * G][max_splits][D]   normalised partial outputs o / l
+//   lse [units * G][max_splits]      log2-sum-exp of each partial (-inf if empty)
 struct Workspace {
   float* o;
   float* lse;
-  int32_t* count;
 };
 
 __host__ __device__ inline size_t ws_floats(size_t heads, int max_splits, int D) {
   return heads * (size_t)max_splits * (size_t)(D + 1);
 }
 
-// End of a split: combine the waves, then either write the output (single
-// split) or store a partial and let the last split of the unit merge.
-//   unit:  index of this workgroup's (sequence, KV head); heads head0 .. head0+G-1
-//   n:     number of splits of this unit (all of them run)
+// End of a split: combine the waves through LDS, then write the output directly
+// (a sequence that fits one split) or this split's partial for merge_kernel.
 template <int D, int G>
 __device__ __forceinline__ void finish_split(const HeadState<G>& st, int lane, int wave,
-                                             const Workspace& ws, int unit, size_t head0,
-                                             int split, int n, int max_splits,
-                                             float* __restrict__ out, float* __restrict__ lse) {
+                                             const Workspace& ws, size_t head0, int split,
+                                             int n, int max_splits, float* __restrict__ out,
+                                             float* __restrict__ lse) {
   constexpr int LPR = D / 8;
   __shared__ float sm_o[kWaves][G][D];
   __shared__ float sm_m[kWaves][G];
   __shared__ float sm_l[kWaves][G];
-  __shared__ float sm_lse[G][kMaxSplits];
-  __shared__ float sm_M[G], sm_den[G];
-  __shared__ float4 sm_red[kThreads];
-  __shared__ int sm_last;
-  const int tid = threadIdx.x;
   if (lane < LPR) {
 #pragma unroll
     for (int j = 0; j < G; ++j) {
@@ -213,7 +204,7 @@ __device__ __forceinline__ void finish_split(const HeadState<G>& st, int lane, i
     }
   }
   __syncthreads();
-  for (int idx = tid; idx < G * D; idx += kThreads) {
+  for (int idx = threadIdx.x; idx < G * D; idx += kThreads) {
     const int j = idx / D;
     const int d = idx - j * D;
     float M = kNegInf;
@@ -240,70 +231,6 @@ __device__ __forceinline__ void finish_split(const HeadState<G>& st, int lane, i
       if (d == 0) ws.lse[row] = lse2;
     }
   }
-  if (n == 1) return;
-
-  // publish the partial, count this split, and find out whether it is the last
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) sm_last = atomicAdd(ws.count + unit, 1) == n - 1;
-  __syncthreads();
-  if (!sm_last) return;
-  __threadfence();
-
-  for (int idx = tid; idx < G * n; idx += kThreads) {
-    const int j = idx / n;
-    const int s = idx - j * n;
-    sm_lse[j][s] = ws.lse[(head0 + j) * max_splits + s];
-  }
-  __syncthreads();
-  if (tid < G) {
-    float M = kNegInf;
-    for (int s = 0; s < n; ++s) M = fmaxf(M, sm_lse[tid][s]);
-    float den = 0.f;
-    if (M != kNegInf)
-      for (int s = 0; s < n; ++s) den += exp2_fast(sm_lse[tid][s] - M);
-    sm_M[tid] = M;
-    sm_den[tid] = den;
-  }
-  __syncthreads();
-  // G*D/4 float4 columns; the threads split the partials into `groups` strided sets
-  constexpr int kCols = G * D / 4;
-  constexpr int kGroups = kThreads / kCols > 0 ? kThreads / kCols : 1;
-  for (int c = tid % kCols; c < kCols && tid < kCols * kGroups; c += kCols) {
-    const int grp = tid / kCols;
-    const int j = (c * 4) / D;
-    const int d = c * 4 - j * D;
-    const float M = sm_M[j];
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (M != kNegInf) {
-      const float* base = ws.o + ((head0 + j) * max_splits) * D + d;
-      for (int s = grp; s < n; s += kGroups) {
-        const float w = exp2_fast(sm_lse[j][s] - M);
-        const float4 v = *reinterpret_cast<const float4*>(base + (size_t)s * D);
-        acc.x += w * v.x; acc.y += w * v.y; acc.z += w * v.z; acc.w += w * v.w;
-      }
-    }
-    sm_red[tid] = acc;
-  }
-  __syncthreads();
-  if (tid < kCols) {
-    const int j = (tid * 4) / D;
-    const int d = tid * 4 - j * D;
-    float4 acc = sm_red[tid];
-    for (int g = 1; g < kGroups; ++g) {
-      const float4 v = sm_red[tid + g * kCols];
-      acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
-    }
-    const float M = sm_M[j];
-    float4 r = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (M != kNegInf) {
-      const float inv = 1.f / sm_den[j];
-      r = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
-    }
-    *reinterpret_cast<float4*>(out + (head0 + j) * D + d) = r;
-    if (lse && d == 0) lse[head0 + j] = M == kNegInf ? kNegInf : (M + __log2f(sm_den[j])) * kLn2;
-  }
-  if (tid == 0) atomicExch(ws.count + unit, 0);
 }
 
 // ---------------------------------------------------------------- static layout
@@ -364,7 +291,7 @@ static_decode_kernel(const float* __restrict__ q, const uint16_t* __restrict__ k
   init_state(st);
   attend_rows<D, 1, U>(k_cache, v_cache, qr, r0, r1, wave, lane / LPR, row_at, st);
   merge_groups<LPR, 1>(st);
-  finish_split<D, 1>(st, lane, wave, ws, bh, (size_t)bh, split, n, max_splits, out, lse);
+  finish_split<D, 1>(st, lane, wave, ws, (size_t)bh, split, n, max_splits, out, lse);
 }
 
 // ------------------------------------------------------------------ paged layout
@@ -433,8 +360,91 @@ paged_decode_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
   init_state(st);
   attend_rows<D, G, U>(key_cache, value_cache, qr, r0, r1, wave, lane / LPR, row_at, st);
   merge_groups<LPR, G>(st);
-  finish_split<D, G>(st, lane, wave, ws, bg, (size_t)b * Hq + (size_t)g * group, split, n,
+  finish_split<D, G>(st, lane, wave, ws, (size_t)b * Hq + (size_t)g * group, split, n,
                      max_splits, out, lse);
+}
+
+// ------------------------------------------------------------------- merge
+// One workgroup per (sequence, query head) with more than one split.  The
+// partials' log2-sum-exps are loaded at once into LDS; then the D/4 float4
+// columns are shared among 256 / (D/4) split groups, so every thread issues its
+// few partial loads together, and the groups are summed through LDS.
+// Length modes: 0 = static (valid_len or cap), 1 = paged.
+template <int D>
+__global__ void __launch_bounds__(kThreads)
+merge_kernel(Workspace ws, int heads, int chunk, int max_splits, int mode,
+             const int32_t* __restrict__ valid_len, int cap, const int32_t* __restrict__ seq_lens,
+             const int32_t* __restrict__ seq_offset, int block_size, int table_cols, int max_len,
+             float* __restrict__ out, float* __restrict__ lse) {
+  constexpr int kCols = D / 4;
+  constexpr int kGroups = kThreads / kCols;
+  __shared__ float sm_w[kMaxSplits];
+  __shared__ float sm_part[kWaves];
+  __shared__ float4 sm_red[kThreads];
+  const int bh = blockIdx.x;
+  const int b = bh / heads;
+  const int tid = threadIdx.x;
+  int L;
+  if (mode == 0) {
+    L = static_len(valid_len, b, cap, nullptr, false);
+  } else {
+    int toff;
+    L = paged_len(seq_lens, seq_offset, b, block_size, table_cols, max_len, &toff, nullptr,
+                  false);
+  }
+  const int n = L > 0 ? (L + chunk - 1) / chunk : 1;
+  if (n == 1) return;  // the split kernel wrote this head's output
+  const float* lp = ws.lse + (size_t)bh * max_splits;
+  float v = kNegInf;
+  for (int j = tid; j < n; j += kThreads) {
+    const float x = lp[j];
+    sm_w[j] = x;
+    v = fmaxf(v, x);
+  }
+  for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
+  if ((tid & 63) == 0) sm_part[tid >> 6] = v;
+  __syncthreads();
+  const float M = fmaxf(fmaxf(sm_part[0], sm_part[1]), fmaxf(sm_part[2], sm_part[3]));
+  __syncthreads();
+  float den_part = 0.f;
+  if (M != kNegInf) {
+    for (int j = tid; j < n; j += kThreads) {
+      const float w = exp2_fast(sm_w[j] - M);
+      sm_w[j] = w;
+      den_part += w;
+    }
+  }
+  for (int off = 32; off > 0; off >>= 1) den_part += __shfl_xor(den_part, off);
+  if ((tid & 63) == 0) sm_part[tid >> 6] = den_part;
+  __syncthreads();
+  const float den = sm_part[0] + sm_part[1] + sm_part[2] + sm_part[3];
+  const int c = tid % kCols;
+  const int grp = tid / kCols;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (M != kNegInf) {
+    const float* op = ws.o + (size_t)bh * max_splits * D + c * 4;
+    for (int j = grp; j < n; j += kGroups) {
+      const float w = sm_w[j];
+      const float4 x = *reinterpret_cast<const float4*>(op + (size_t)j * D);
+      acc.x += w * x.x; acc.y += w * x.y; acc.z += w * x.z; acc.w += w * x.w;
+    }
+  }
+  sm_red[tid] = acc;
+  __syncthreads();
+  if (tid < kCols) {
+#pragma unroll
+    for (int g = 1; g < kGroups; ++g) {
+      const float4 x = sm_red[tid + g * kCols];
+      acc.x += x.x; acc.y += x.y; acc.z += x.z; acc.w += x.w;
+    }
+    float4 r = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (M != kNegInf) {
+      const float inv = 1.f / den;
+      r = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+    }
+    *reinterpret_cast<float4*>(out + (size_t)bh * D + c * 4) = r;
+    if (lse && tid == 0) lse[bh] = M == kNegInf ? kNegInf : (M + __log2f(den)) * kLn2;
+  }
 }
 
 // ------------------------------------------------------------------- planning
@@ -463,14 +473,13 @@ size_t static_workspace_bytes(int B, int H, int cap, int D) {
   const int least = round_up((cap + kMaxSplits - 1) / kMaxSplits, kMinChunk);
   const int c = least > kMinChunk ? least : kMinChunk;
   const int splits = cap > 0 ? (cap + c - 1) / c : 1;
-  return ws_floats((size_t)B * H, splits, D) * sizeof(float) + (size_t)B * H * sizeof(int32_t);
+  return ws_floats((size_t)B * H, splits, D) * sizeof(float);
 }
 
 static Workspace carve(void* ws, size_t heads, int max_splits, int D) {
   Workspace w;
   w.o = static_cast<float*>(ws);
   w.lse = w.o + heads * (size_t)max_splits * D;
-  w.count = reinterpret_cast<int32_t*>(w.lse + heads * (size_t)max_splits);
   return w;
 }
 
@@ -478,12 +487,7 @@ hipError_t launch_decode_static(const float* q, const void* k_cache, const void*
                                 const int32_t* mask, const int32_t* valid_len, int B, int H,
                                 int cap, int D, float scale, float* out, float* lse, void* ws,
                                 const SplitPlan& plan, int32_t* err_flag, hipStream_t stream) {
-  // the counters sit after the largest o/lse area so that they do not move
-  // between plans of the same sizes
-  const SplitPlan widest = plan_static(B, H, cap, D, kMaxSplits);
-  Workspace w = carve(ws, (size_t)B * H, plan.max_splits, D);
-  w.count = reinterpret_cast<int32_t*>(static_cast<float*>(ws) +
-                                       ws_floats((size_t)B * H, widest.max_splits, D));
+  const Workspace w = carve(ws, (size_t)B * H, plan.max_splits, D);
   const float scale_log2 = scale * kLog2e;
   const dim3 grid((unsigned)(B * H * plan.max_splits));
   const auto* kc = static_cast<const uint16_t*>(k_cache);
@@ -492,10 +496,18 @@ hipError_t launch_decode_static(const float* q, const void* k_cache, const void*
     hipLaunchKernelGGL(static_decode_kernel<128>, grid, dim3(kThreads), 0, stream, q, kc, vc,
                        mask, valid_len, H, cap, scale_log2, plan.chunk, plan.max_splits, w, out,
                        lse, err_flag);
+    if (plan.max_splits > 1)
+      hipLaunchKernelGGL(merge_kernel<128>, dim3(B * H), dim3(kThreads), 0, stream, w, H,
+                         plan.chunk, plan.max_splits, 0, valid_len, cap, nullptr, nullptr, 1, 0,
+                         0, out, lse);
   } else {
     hipLaunchKernelGGL(static_decode_kernel<64>, grid, dim3(kThreads), 0, stream, q, kc, vc,
                        mask, valid_len, H, cap, scale_log2, plan.chunk, plan.max_splits, w, out,
                        lse, err_flag);
+    if (plan.max_splits > 1)
+      hipLaunchKernelGGL(merge_kernel<64>, dim3(B * H), dim3(kThreads), 0, stream, w, H,
+                         plan.chunk, plan.max_splits, 0, valid_len, cap, nullptr, nullptr, 1, 0,
+                         0, out, lse);
   }
   return hipGetLastError();
 }
@@ -533,7 +545,7 @@ size_t paged_workspace_bytes(int B, int Hq, int D, int max_seq_len, int block_si
   const int least = round_up((max_seq_len + kMaxSplits - 1) / kMaxSplits, unit);
   const int c = least > unit ? least : unit;
   const int splits = max_seq_len > 0 ? (max_seq_len + c - 1) / c : 1;
-  return ws_floats((size_t)B * Hq, splits, D) * sizeof(float) + (size_t)B * Hq * sizeof(int32_t);
+  return ws_floats((size_t)B * Hq, splits, D) * sizeof(float);
 }
 
 hipError_t launch_decode_paged(const void* q, const void* key_cache, const void* value_cache,
@@ -543,13 +555,7 @@ hipError_t launch_decode_paged(const void* q, const void* key_cache, const void*
                                int max_seq_len, float scale, float* out, float* lse, void* ws,
                                const SplitPlan& plan, int32_t* err_flag, hipStream_t stream) {
   (void)D;
-  const int unit = block_size > kMinChunk ? block_size : kMinChunk;
-  const int least = round_up((max_seq_len + kMaxSplits - 1) / kMaxSplits, unit);
-  const int c = least > unit ? least : unit;
-  const int widest = max_seq_len > 0 ? (max_seq_len + c - 1) / c : 1;
-  Workspace w = carve(ws, (size_t)B * Hq, plan.max_splits, 128);
-  w.count = reinterpret_cast<int32_t*>(static_cast<float*>(ws) +
-                                       ws_floats((size_t)B * Hq, widest, 128));
+  const Workspace w = carve(ws, (size_t)B * Hq, plan.max_splits, 128);
   const float scale_log2 = scale * kLog2e;
   int bs_log2 = 0;
   while ((1 << bs_log2) < block_size) ++bs_log2;
@@ -571,6 +577,10 @@ hipError_t launch_decode_paged(const void* q, const void* key_cache, const void*
     default: return hipErrorInvalidValue;
   }
 #undef DAKV_PAGED
+  if (plan.max_splits > 1)
+    hipLaunchKernelGGL(merge_kernel<128>, dim3(B * Hq), dim3(kThreads), 0, stream, w, Hq,
+                       plan.chunk, plan.max_splits, 1, nullptr, 0, seq_lens, seq_offset,
+                       block_size, table_cols, max_seq_len, out, lse);
   return hipGetLastError();
 }
 

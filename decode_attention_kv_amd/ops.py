@@ -114,14 +114,13 @@ def decode_attn_static_workspace_size(B, H, cap, D):
 
 
 def _workspace(nbytes, device, workspace):
-    """The caller's workspace, or a new zero-filled one (the split counters inside a
-    workspace must be zero before its first use; every call leaves them zero)."""
+    """The caller's workspace, or a new one."""
     if workspace is not None:
         _need(workspace, "workspace", torch.uint8)
         if workspace.numel() < nbytes:
             raise ValueError(f"workspace needs {nbytes} bytes")
         return workspace
-    return torch.zeros(max(nbytes, 16), dtype=torch.uint8, device=device)
+    return torch.empty(max(nbytes, 16), dtype=torch.uint8, device=device)
 
 
 def decode_attn_static(q, k_cache, v_cache, mask=None, valid_len=None, scale=None, out=None,

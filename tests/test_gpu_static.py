@@ -291,8 +291,8 @@ def test_graph_replay_of_append_and_attend_matches_eager():
 
 
 def test_many_splits_merge_and_workspace_reuse():
-    """Capacity 16384 at batch 1 gives 64-row splits (up to 256 per head): the in-kernel
-    merge of many partials, repeated on one workspace, stays at the oracle."""
+    """Capacity 16384 at batch 1 gives 64-row splits (up to 256 per head): the merge of
+    many partials, repeated on one workspace, stays at the oracle."""
     case = workloads.static_case(1, 4, 128, 16384, [16384], device=DEV, seed=32,
                                  garbage_std=1.0)
     ws = torch.zeros(dakv.decode_attn_static_workspace_size(1, 4, 16384, 128),
@@ -305,5 +305,3 @@ def test_many_splits_merge_and_workspace_reuse():
         torch.cuda.synchronize()
         assert_attention_close(npy(out), ref_out)
         assert_lse_close(npy(lse), ref_lse)
-    counters = ws.view(torch.int32)[-4:]
-    assert int(counters.abs().sum()) == 0
