@@ -9,6 +9,7 @@ from .ops import (
     kv_append,
     decode_attn_static,
     decode_attn_static_workspace_size,
+    decode_step_static,
     gather_pa_kv_cache,
     decode_attn_paged,
     decode_attn_paged_workspace_size,
@@ -24,6 +25,7 @@ __all__ = [
     "kv_append",
     "decode_attn_static",
     "decode_attn_static_workspace_size",
+    "decode_step_static",
     "gather_pa_kv_cache",
     "decode_attn_paged",
     "decode_attn_paged_workspace_size",

@@ -34,6 +34,8 @@ SIGNATURES = {
     "dakv_decode_attn_static_workspace_size": (_sz, [_i, _i, _i, _i]),
     "dakv_decode_attn_static": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _vp, _vp,
                                      _vp, _sz, _i, _vp, _vp]),
+    "dakv_decode_step_static": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _f,
+                                     _vp, _vp, _vp, _sz, _i, _vp, _vp]),
     "dakv_gather_pa_kv_cache": (_i, [_vp, _vp, _i, _i, _i, _i, _i, _i, _vp, _i, _i, _vp, _vp,
                                      _i, _vp, _vp, _vp, _vp]),
     "dakv_decode_attn_paged_workspace_size": (_sz, [_i, _i, _i, _i, _i]),

@@ -62,6 +62,7 @@ int dakv_decode_attn_static(const float* q, const void* k_cache, const void* v_c
   if (B < 0 || H < 0 || cap <= 0 || D <= 0 || num_splits < 0) return DAKV_EINVAL;
   if (B == 0 || H == 0) return DAKV_OK;
   if (D != 64 && D != 128) return DAKV_ENOTSUP;
+  if (!dakv::static_supported(cap)) return DAKV_ENOTSUP;
   if (!q || !k_cache || !v_cache || !out || !workspace) return DAKV_EINVAL;
   if (!mask && !valid_len) return DAKV_EINVAL;
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out) ||
@@ -69,9 +70,32 @@ int dakv_decode_attn_static(const float* q, const void* k_cache, const void* v_c
     return DAKV_EINVAL;
   if (workspace_bytes < dakv::static_workspace_bytes(B, H, cap, D)) return DAKV_EINVAL;
   const dakv::SplitPlan plan = dakv::plan_static(B, H, cap, D, num_splits);
-  return from_hip(dakv::launch_decode_static(q, k_cache, v_cache, mask, valid_len, B, H, cap, D,
-                                             scale, out, lse, workspace, plan, err_flag,
-                                             as_stream(stream)));
+  return from_hip(dakv::launch_decode_static(
+      q, const_cast<void*>(k_cache), const_cast<void*>(v_cache), const_cast<int32_t*>(mask),
+      valid_len, nullptr, nullptr, nullptr, B, H, cap, D, scale, out, lse, workspace, plan,
+      err_flag, as_stream(stream)));
+}
+
+int dakv_decode_step_static(const float* q, void* k_cache, void* v_cache, const void* k_new,
+                            const void* v_new, const int32_t* write_pos, int32_t* mask,
+                            const int32_t* valid_len, int B, int H, int cap, int D, float scale,
+                            float* out, float* lse, void* workspace, size_t workspace_bytes,
+                            int num_splits, int32_t* err_flag, void* stream) {
+  if (B < 0 || H < 0 || cap <= 0 || D <= 0 || num_splits < 0) return DAKV_EINVAL;
+  if (B == 0 || H == 0) return DAKV_OK;
+  if (D != 64 && D != 128) return DAKV_ENOTSUP;
+  if (!dakv::static_supported(cap)) return DAKV_ENOTSUP;
+  if (!q || !k_cache || !v_cache || !k_new || !v_new || !write_pos || !out || !workspace)
+    return DAKV_EINVAL;
+  if (!mask && !valid_len) return DAKV_EINVAL;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(k_new) ||
+      !aligned16(v_new) || !aligned16(out) || !aligned16(workspace))
+    return DAKV_EINVAL;
+  if (workspace_bytes < dakv::static_workspace_bytes(B, H, cap, D)) return DAKV_EINVAL;
+  const dakv::SplitPlan plan = dakv::plan_static(B, H, cap, D, num_splits);
+  return from_hip(dakv::launch_decode_static(q, k_cache, v_cache, mask, valid_len, k_new, v_new,
+                                             write_pos, B, H, cap, D, scale, out, lse, workspace,
+                                             plan, err_flag, as_stream(stream)));
 }
 
 // --------------------------------------------------------- gather_pa_kv_cache

@@ -99,73 +99,129 @@ __device__ __forceinline__ void merge_groups(HeadState<G>& st) {
   }
 }
 
-// The row loop shared by the static and paged kernels.  RowAt(t, it_row, ok)
-// gives the element offset of row t's piece for this lane and clears ok for rows
-// that must not be read.  q is pre-scaled by scale * log2(e).
-template <int D, int G, int U, typename RowAt>
-__device__ __forceinline__ void attend_rows(const uint16_t* __restrict__ kc,
-                                            const uint16_t* __restrict__ vc,
-                                            const float (&q)[G][8], int r0, int r1, int wave,
-                                            int slot, RowAt row_at, HeadState<G>& st) {
+// Where a loop step's K/V pieces come from.  Both loaders are branch-free: a row
+// that must not be used still issues its load, but the load either touches no
+// memory (buffer load past the end of the resource returns zeros) or re-reads a
+// fixed in-bounds location, and its value is never used.
+//
+// BufferRows: one (sequence, head) region of the static cache; `off` is a byte
+// offset inside it, and kNoRow (past num_records) stands for "no row".
+struct BufferRows {
+  __amdgpu_buffer_rsrc_t k, v;
+  static constexpr uint32_t kNoRow = 0x80000000u;
+  __device__ BufferRows(const uint16_t* kbase, const uint16_t* vbase, uint32_t bytes)
+      : k(__builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(kbase), (short)0, (int)bytes,
+                                            0x00020000)),
+        v(__builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(vbase), (short)0, (int)bytes,
+                                            0x00020000)) {}
+  __device__ __forceinline__ void load(uint32_t off, uint4& kr, uint4& vr) const {
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4 a = __builtin_amdgcn_raw_buffer_load_b128(k, (int)off, 0, 0);
+    const u32x4 b = __builtin_amdgcn_raw_buffer_load_b128(v, (int)off, 0, 0);
+    kr = make_uint4(a[0], a[1], a[2], a[3]);
+    vr = make_uint4(b[0], b[1], b[2], b[3]);
+  }
+};
+
+// GlobalRows: the paged pool through 64-bit addresses; `off` is an element offset
+// from the pool base (0, an in-bounds location, for rows that are not used).
+struct GlobalRows {
+  const uint16_t* k;
+  const uint16_t* v;
+  __device__ __forceinline__ void load(size_t off, uint4& kr, uint4& vr) const {
+    kr = load16(k + off);
+    vr = load16(v + off);
+  }
+};
+
+// One loop step's loads: U rows per lane group, K and V.  RowAt(t, ok) returns
+// the loader offset of row t (or the loader's "no row" value) and clears ok for
+// rows that must not be used; Patch(t, kr, vr) may then replace a row's values.
+template <int D, int U, typename Rows, typename RowAt, typename Patch>
+__device__ __forceinline__ void issue_rows(const Rows& rows, int base, int r1, int wave,
+                                           int slot, RowAt& row_at, Patch& patch,
+                                           uint4 (&kr)[U], uint4 (&vr)[U], bool (&ok)[U]) {
+  constexpr int RPW = 64 / (D / 8);
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int t = base + (u * kWaves + wave) * RPW + slot;
+    ok[u] = t < r1;
+    rows.load(row_at(t, ok[u]), kr[u], vr[u]);
+    patch(t, kr[u], vr[u]);
+  }
+}
+
+struct NoPatch {
+  __device__ __forceinline__ void operator()(int, uint4&, uint4&) const {}
+};
+
+// One loop step's arithmetic: scores of the U rows for each of the G heads, then
+// the online-softmax update of (m, l, o).
+template <int D, int G, int U>
+__device__ __forceinline__ void consume_rows(const float (&q)[G][8], const uint4 (&kr)[U],
+                                             const uint4 (&vr)[U], const bool (&ok)[U],
+                                             HeadState<G>& st) {
   constexpr int LPR = D / 8;
-  constexpr int RPW = 64 / LPR;
-  constexpr int kStep = kWaves * RPW * U;
-  for (int base = r0; base < r1; base += kStep) {
-    uint4 kr[U], vr[U];
-    bool ok[U];
+  float s[G][U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int o = (u * kWaves + wave) * RPW + slot;  // row offset inside this step
-      const int t = base + o;
-      ok[u] = t < r1;
-      const size_t off = row_at(t, o, base, ok[u]);
-      kr[u] = make_uint4(0, 0, 0, 0);
-      vr[u] = make_uint4(0, 0, 0, 0);
-      if (ok[u]) {
-        kr[u] = load16(kc + off);
-        vr[u] = load16(vc + off);
-      }
-    }
-    float s[G][U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      float kf[8];
-      unpack8(kr[u], kf);
-#pragma unroll
-      for (int j = 0; j < G; ++j) {
-        float acc = 0.f;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) acc = fmaf(q[j][i], kf[i], acc);
-        acc = group_sum<LPR>(acc);
-        s[j][u] = ok[u] ? acc : kNegInf;
-      }
-    }
+  for (int u = 0; u < U; ++u) {
+    float kf[8];
+    unpack8(kr[u], kf);
 #pragma unroll
     for (int j = 0; j < G; ++j) {
-      float mnew = st.m[j];
+      float acc = 0.f;
 #pragma unroll
-      for (int u = 0; u < U; ++u) mnew = fmaxf(mnew, s[j][u]);
-      const float ms = mnew == kNegInf ? 0.f : mnew;
-      const float alpha = exp2_fast(st.m[j] - ms);
-      float psum = 0.f;
-      float p[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        p[u] = exp2_fast(s[j][u] - ms);
-        psum += p[u];
-      }
-      st.l[j] = st.l[j] * alpha + psum;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) st.o[j][i] *= alpha;
-      st.m[j] = mnew;
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        float vf[8];
-        unpack8(vr[u], vf);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) st.o[j][i] = fmaf(p[u], vf[i], st.o[j][i]);
-      }
+      for (int i = 0; i < 8; ++i) acc = fmaf(q[j][i], kf[i], acc);
+      acc = group_sum<LPR>(acc);
+      s[j][u] = ok[u] ? acc : kNegInf;
     }
+  }
+#pragma unroll
+  for (int j = 0; j < G; ++j) {
+    float mnew = st.m[j];
+#pragma unroll
+    for (int u = 0; u < U; ++u) mnew = fmaxf(mnew, s[j][u]);
+    const float ms = mnew == kNegInf ? 0.f : mnew;
+    const float alpha = exp2_fast(st.m[j] - ms);
+    float psum = 0.f;
+    float p[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      p[u] = exp2_fast(s[j][u] - ms);
+      psum += p[u];
+    }
+    st.l[j] = st.l[j] * alpha + psum;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) st.o[j][i] *= alpha;
+    st.m[j] = mnew;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float vf[8];
+      unpack8(vr[u], vf);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) st.o[j][i] = fmaf(p[u], vf[i], st.o[j][i]);
+    }
+  }
+}
+
+// The row loop shared by the static and paged kernels.  Each step issues all of
+// its 2U loads (U rows per lane group, K and V) before using any of them; the
+// latency between steps is hidden by the other workgroups resident on the CU
+// (splits are one or a few steps long).  Step(base) runs before each step's loads
+// (the static kernel refreshes its mask ballots there).  q is pre-scaled by
+// scale * log2(e).
+template <int D, int G, int U, typename Rows, typename RowAt, typename Patch, typename Step>
+__device__ __forceinline__ void attend_rows(const Rows& rows, const float (&q)[G][8], int r0,
+                                            int r1, int wave, int slot, RowAt row_at,
+                                            Patch patch, Step step, HeadState<G>& st) {
+  constexpr int RPW = 64 / (D / 8);
+  constexpr int kStep = kWaves * RPW * U;
+  for (int base = r0; base < r1; base += kStep) {
+    step(base);
+    uint4 kr[U], vr[U];
+    bool ok[U];
+    issue_rows<D, U>(rows, base, r1, wave, slot, row_at, patch, kr, vr, ok);
+    consume_rows<D, G, U>(q, kr, vr, ok, st);
   }
 }
 
@@ -234,62 +290,115 @@ __device__ __forceinline__ void finish_split(const HeadState<G>& st, int lane, i
 }
 
 // ---------------------------------------------------------------- static layout
-template <int D>
+constexpr int kStaticChunkMax = 256;  // rows per split of the static layout, at most
+
+// Split pass of decode_attn_static and, with kAppend, of decode_step_static (the
+// new token's K/V row is written into the cache by the split that owns its
+// position and is attended from the registers it was read into; the mask bit is
+// set once per sequence).
+template <int D, int U, bool kAppend>
 __global__ void __launch_bounds__(kThreads)
-static_decode_kernel(const float* __restrict__ q, const uint16_t* __restrict__ k_cache,
-                     const uint16_t* __restrict__ v_cache, const int32_t* __restrict__ mask,
-                     const int32_t* __restrict__ valid_len, int H, int cap, float scale_log2,
-                     int chunk, int max_splits, Workspace ws, float* __restrict__ out,
-                     float* __restrict__ lse, int32_t* err_flag) {
+static_decode_kernel(const float* __restrict__ q, uint16_t* __restrict__ k_cache,
+                     uint16_t* __restrict__ v_cache, int32_t* __restrict__ mask,
+                     const int32_t* __restrict__ valid_len, const uint16_t* __restrict__ k_new,
+                     const uint16_t* __restrict__ v_new, const int32_t* __restrict__ write_pos,
+                     int H, int cap, float scale_log2, int chunk, int max_splits, Workspace ws,
+                     float* __restrict__ out, float* __restrict__ lse, int32_t* err_flag) {
   constexpr int LPR = D / 8;
   constexpr int RPW = 64 / LPR;
-  constexpr int U = 4;
-  constexpr int kStep = kWaves * RPW * U;   // rows per loop step: 64 (D=128), 128 (D=64)
-  constexpr int kBallots = kStep / 64;
+  constexpr int kStep = kWaves * RPW * U;  // rows per step
+  constexpr int kBallots = (kStep + 63) / 64;
   const int split = blockIdx.x % max_splits;
   const int bh = blockIdx.x / max_splits;
   const int b = bh / H;
-  const int L = static_len(valid_len, b, cap, err_flag,
-                           split == 0 && bh % H == 0 && threadIdx.x == 0);
-  const int n = L > 0 ? (L + chunk - 1) / chunk : 1;
-  if (split >= n) return;
-  const int r0 = split * chunk;
-  const int r1 = min(r0 + chunk, L);
+  const int h = bh - b * H;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int sub = lane % LPR;
-
-  float qr[1][8];
-  {
-    const float4* qp = reinterpret_cast<const float4*>(q + (size_t)bh * D + sub * 8);
-    const float4 a = qp[0], c = qp[1];
-    qr[0][0] = a.x * scale_log2; qr[0][1] = a.y * scale_log2;
-    qr[0][2] = a.z * scale_log2; qr[0][3] = a.w * scale_log2;
-    qr[0][4] = c.x * scale_log2; qr[0][5] = c.y * scale_log2;
-    qr[0][6] = c.z * scale_log2; qr[0][7] = c.w * scale_log2;
-  }
-  const size_t head_base = (size_t)bh * cap * D + (size_t)sub * 8;
+  const int r0 = split * chunk;
   const int32_t* mrow = mask ? mask + (size_t)b * cap : nullptr;
-  // attended-row bits of the current step, one 64-row ballot per wave-wide load
-  uint64_t bits[kBallots];
-  int bits_base = -1;
-  auto row_at = [&](int t, int o, int base, bool& ok) -> size_t {
-    if (mrow) {
-      if (bits_base != base) {
+  // Every load this split needs before any wait: the valid length, the append
+  // position and row, the query, and the mask entries of the first step
+  // (clamped into the row, never branched).
+  const int Lraw = valid_len ? valid_len[b] : cap;
+  int p = -1;
+  uint4 kn = make_uint4(0, 0, 0, 0), vn = make_uint4(0, 0, 0, 0);
+  if constexpr (kAppend) {
+    p = write_pos[b];
+    kn = load16(k_new + (size_t)bh * D + sub * 8);
+    vn = load16(v_new + (size_t)bh * D + sub * 8);
+  }
+  const float4* qp = reinterpret_cast<const float4*>(q + (size_t)bh * D + sub * 8);
+  const float4 qa = qp[0], qc = qp[1];
+  int32_t mv[kBallots];
+  if (mrow) {
 #pragma unroll
-        for (int k = 0; k < kBallots; ++k) {
-          const int tt = base + 64 * k + lane;
-          bits[k] = __ballot(tt < r1 && mrow[tt] != 0);
-        }
-        bits_base = base;
+    for (int k = 0; k < kBallots; ++k) mv[k] = mrow[min(r0 + 64 * k + lane, cap - 1)];
+  }
+  const bool report = split == 0 && h == 0 && threadIdx.x == 0;
+  if constexpr (kAppend) {
+    if (p < 0 || p >= cap) {
+      if (report) raise_flag(err_flag, 2);
+      p = -1;
+    } else if (p / chunk == split) {
+      // this split owns the position: store the new row (and the mask bit once)
+      if (wave == 0 && lane < 2 * LPR) {
+        const size_t at = ((size_t)bh * cap + p) * D + (size_t)(lane % LPR) * 8;
+        const uint16_t* src = (lane < LPR ? k_new : v_new) + (size_t)bh * D + (lane % LPR) * 8;
+        store16((lane < LPR ? k_cache : v_cache) + at, load16(src));
       }
-      ok = ok && ((bits[o >> 6] >> (o & 63)) & 1ull);
+      if (mrow && h == 0 && threadIdx.x == 0) mask[(size_t)b * cap + p] = 1;
     }
-    return head_base + (size_t)t * D;
+  }
+  int L = Lraw;
+  if (L < 0 || L > cap) {
+    if (report) raise_flag(err_flag, 16);
+    L = L < 0 ? 0 : cap;
+  }
+  const int n = L > 0 ? (L + chunk - 1) / chunk : 1;
+  if (split >= n) return;
+  const int r1 = min(r0 + chunk, L);
+  float qr[1][8];
+  qr[0][0] = qa.x * scale_log2; qr[0][1] = qa.y * scale_log2;
+  qr[0][2] = qa.z * scale_log2; qr[0][3] = qa.w * scale_log2;
+  qr[0][4] = qc.x * scale_log2; qr[0][5] = qc.y * scale_log2;
+  qr[0][6] = qc.z * scale_log2; qr[0][7] = qc.w * scale_log2;
+  // bit (t - step base) of the ballots: row t of the current step is attended
+  uint64_t bits[kBallots];
+#pragma unroll
+  for (int k = 0; k < kBallots; ++k)
+    bits[k] = __ballot(r0 + 64 * k + lane < r1 && (!mrow || mv[k] != 0));
+  int bits_base = r0;
+  auto step = [&](int base) {
+    if (base != bits_base) {
+      bits_base = base;
+#pragma unroll
+      for (int k = 0; k < kBallots; ++k) {
+        const int t = base + 64 * k + lane;
+        bits[k] = __ballot(t < r1 && (!mrow || mrow[min(t, cap - 1)] != 0));
+      }
+    }
+  };
+  const BufferRows rows(k_cache + (size_t)bh * cap * D, v_cache + (size_t)bh * cap * D,
+                        (uint32_t)cap * D * 2);
+  const uint32_t lane_off = (uint32_t)sub * 16;
+  auto row_at = [&](int t, bool& ok) -> uint32_t {
+    const int o = t - bits_base;
+    ok = ok && (((bits[o >> 6] >> (o & 63)) & 1ull) || t == p);
+    // the appended row comes from the registers, not from memory
+    return (ok && t != p) ? (uint32_t)t * (D * 2) + lane_off : BufferRows::kNoRow;
+  };
+  auto patch = [&](int t, uint4& kr, uint4& vr) {
+    if constexpr (kAppend) {
+      if (t == p) {
+        kr = kn;
+        vr = vn;
+      }
+    }
   };
   HeadState<1> st;
   init_state(st);
-  attend_rows<D, 1, U>(k_cache, v_cache, qr, r0, r1, wave, lane / LPR, row_at, st);
+  attend_rows<D, 1, U>(rows, qr, r0, r1, wave, lane / LPR, row_at, patch, step, st);
   merge_groups<LPR, 1>(st);
   finish_split<D, 1>(st, lane, wave, ws, (size_t)bh, split, n, max_splits, out, lse);
 }
@@ -347,18 +456,16 @@ paged_decode_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
   const size_t row_stride = (size_t)Hkv * D;
   const size_t head_off = (size_t)g * D + (size_t)sub * 8;
   const int bs_mask = block_size - 1;
-  auto row_at = [&](int t, int, int, bool& ok) -> size_t {
-    if (!ok) return 0;
-    const int phys = tbl[(t >> bs_log2) - blk0];
-    if (phys < 0) {
-      ok = false;
-      return 0;
-    }
-    return ((size_t)phys * block_size + (t & bs_mask)) * row_stride + head_off;
+  const GlobalRows rows{key_cache, value_cache};
+  auto row_at = [&](int t, bool& ok) -> size_t {
+    const int phys = ok ? tbl[(t >> bs_log2) - blk0] : -1;
+    ok = phys >= 0;
+    return ok ? ((size_t)phys * block_size + (t & bs_mask)) * row_stride + head_off : 0;
   };
   HeadState<G> st;
   init_state(st);
-  attend_rows<D, G, U>(key_cache, value_cache, qr, r0, r1, wave, lane / LPR, row_at, st);
+  attend_rows<D, G, U>(rows, qr, r0, r1, wave, lane / LPR, row_at, NoPatch{},
+                       [](int) {}, st);
   merge_groups<LPR, G>(st);
   finish_split<D, G>(st, lane, wave, ws, (size_t)b * Hq + (size_t)g * group, split, n,
                      max_splits, out, lse);
@@ -453,26 +560,26 @@ static int round_up(int x, int m) { return (x + m - 1) / m * m; }
 SplitPlan plan_static(int B, int H, int cap, int D, int forced_splits) {
   (void)D;
   SplitPlan p;
-  const int least = round_up((cap + kMaxSplits - 1) / kMaxSplits, kMinChunk);
   int c;
   if (forced_splits > 0) {
     c = round_up((cap + forced_splits - 1) / forced_splits, kMinChunk);
   } else {
-    // about 4096 workgroups at full capacity, at most 256 rows each
-    const long long want = ((long long)B * H * cap + 4095) / 4096;
-    c = round_up((int)(want > 256 ? 256 : want), kMinChunk);
+    // short splits (one 64-row step at D = 128): the CU keeps many resident and
+    // hides each one's memory latency behind the others; longer only when the
+    // split count would exceed what the merge holds
+    c = round_up((cap + kMaxSplits - 1) / kMaxSplits, kMinChunk);
   }
   if (c < kMinChunk) c = kMinChunk;
-  if (c < least) c = least;
+  if (c > kStaticChunkMax) c = kStaticChunkMax;
   p.chunk = c;
   p.max_splits = cap > 0 ? (cap + c - 1) / c : 1;
   return p;
 }
 
+bool static_supported(int cap) { return cap > 0 && cap <= kStaticChunkMax * kMaxSplits; }
+
 size_t static_workspace_bytes(int B, int H, int cap, int D) {
-  const int least = round_up((cap + kMaxSplits - 1) / kMaxSplits, kMinChunk);
-  const int c = least > kMinChunk ? least : kMinChunk;
-  const int splits = cap > 0 ? (cap + c - 1) / c : 1;
+  const int splits = cap > 0 ? (cap + kMinChunk - 1) / kMinChunk : 1;
   return ws_floats((size_t)B * H, splits, D) * sizeof(float);
 }
 
@@ -483,31 +590,44 @@ static Workspace carve(void* ws, size_t heads, int max_splits, int D) {
   return w;
 }
 
-hipError_t launch_decode_static(const float* q, const void* k_cache, const void* v_cache,
-                                const int32_t* mask, const int32_t* valid_len, int B, int H,
-                                int cap, int D, float scale, float* out, float* lse, void* ws,
-                                const SplitPlan& plan, int32_t* err_flag, hipStream_t stream) {
+template <int D, bool kAppend>
+static void launch_static_d(const float* q, void* k_cache, void* v_cache, int32_t* mask,
+                            const int32_t* valid_len, const void* k_new, const void* v_new,
+                            const int32_t* write_pos, int B, int H, int cap, float scale,
+                            float* out, float* lse, void* ws, const SplitPlan& plan,
+                            int32_t* err_flag, hipStream_t stream) {
   const Workspace w = carve(ws, (size_t)B * H, plan.max_splits, D);
-  const float scale_log2 = scale * kLog2e;
-  const dim3 grid((unsigned)(B * H * plan.max_splits));
-  const auto* kc = static_cast<const uint16_t*>(k_cache);
-  const auto* vc = static_cast<const uint16_t*>(v_cache);
+  hipLaunchKernelGGL((static_decode_kernel<D, 4, kAppend>), dim3((unsigned)(B * H * plan.max_splits)),
+                     dim3(kThreads), 0, stream, q, static_cast<uint16_t*>(k_cache),
+                     static_cast<uint16_t*>(v_cache), mask, valid_len,
+                     static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new),
+                     write_pos, H, cap, scale * kLog2e, plan.chunk, plan.max_splits, w, out, lse,
+                     err_flag);
+  if (plan.max_splits > 1)
+    hipLaunchKernelGGL(merge_kernel<D>, dim3(B * H), dim3(kThreads), 0, stream, w, H, plan.chunk,
+                       plan.max_splits, 0, valid_len, cap, nullptr, nullptr, 1, 0, 0, out, lse);
+}
+
+hipError_t launch_decode_static(const float* q, void* k_cache, void* v_cache, int32_t* mask,
+                                const int32_t* valid_len, const void* k_new, const void* v_new,
+                                const int32_t* write_pos, int B, int H, int cap, int D,
+                                float scale, float* out, float* lse, void* ws,
+                                const SplitPlan& plan, int32_t* err_flag, hipStream_t stream) {
+  const bool append = write_pos != nullptr;
   if (D == 128) {
-    hipLaunchKernelGGL(static_decode_kernel<128>, grid, dim3(kThreads), 0, stream, q, kc, vc,
-                       mask, valid_len, H, cap, scale_log2, plan.chunk, plan.max_splits, w, out,
-                       lse, err_flag);
-    if (plan.max_splits > 1)
-      hipLaunchKernelGGL(merge_kernel<128>, dim3(B * H), dim3(kThreads), 0, stream, w, H,
-                         plan.chunk, plan.max_splits, 0, valid_len, cap, nullptr, nullptr, 1, 0,
-                         0, out, lse);
+    if (append)
+      launch_static_d<128, true>(q, k_cache, v_cache, mask, valid_len, k_new, v_new, write_pos,
+                                 B, H, cap, scale, out, lse, ws, plan, err_flag, stream);
+    else
+      launch_static_d<128, false>(q, k_cache, v_cache, mask, valid_len, k_new, v_new, write_pos,
+                                  B, H, cap, scale, out, lse, ws, plan, err_flag, stream);
   } else {
-    hipLaunchKernelGGL(static_decode_kernel<64>, grid, dim3(kThreads), 0, stream, q, kc, vc,
-                       mask, valid_len, H, cap, scale_log2, plan.chunk, plan.max_splits, w, out,
-                       lse, err_flag);
-    if (plan.max_splits > 1)
-      hipLaunchKernelGGL(merge_kernel<64>, dim3(B * H), dim3(kThreads), 0, stream, w, H,
-                         plan.chunk, plan.max_splits, 0, valid_len, cap, nullptr, nullptr, 1, 0,
-                         0, out, lse);
+    if (append)
+      launch_static_d<64, true>(q, k_cache, v_cache, mask, valid_len, k_new, v_new, write_pos, B,
+                                H, cap, scale, out, lse, ws, plan, err_flag, stream);
+    else
+      launch_static_d<64, false>(q, k_cache, v_cache, mask, valid_len, k_new, v_new, write_pos,
+                                 B, H, cap, scale, out, lse, ws, plan, err_flag, stream);
   }
   return hipGetLastError();
 }

@@ -26,10 +26,14 @@ struct SplitPlan {
 };
 
 SplitPlan plan_static(int B, int H, int cap, int D, int forced_splits);
+// Whether a capacity fits the split limits of the static kernel (<= 65536 rows).
+bool static_supported(int cap);
 size_t static_workspace_bytes(int B, int H, int cap, int D);
-hipError_t launch_decode_static(const float* q, const void* k_cache, const void* v_cache,
-                                const int32_t* mask, const int32_t* valid_len, int B, int H,
-                                int cap, int D, float scale, float* out, float* lse, void* ws,
+// decode_attn_static; with write_pos != nullptr also the append of decode_step_static
+hipError_t launch_decode_static(const float* q, void* k_cache, void* v_cache, int32_t* mask,
+                                const int32_t* valid_len, const void* k_new, const void* v_new,
+                                const int32_t* write_pos, int B, int H, int cap, int D,
+                                float scale, float* out, float* lse, void* ws,
                                 const SplitPlan& plan, int32_t* err_flag, hipStream_t stream);
 
 SplitPlan plan_paged(int B, int Hkv, int max_seq_len, int block_size, int forced_splits);

@@ -109,13 +109,33 @@ size_t dakv_decode_attn_static_workspace_size(int B, int H, int cap, int D);
  *   num_splits 0 = automatic; n >= 1 forces n splits of the row axis (capped at
  *              the workspace's maximum)
  * Rows not attended are never read, so NaN/Inf stored there cannot reach out.
- * Supported: D in {64, 128}.
+ * Supported: D in {64, 128}; cap <= 65536.
  */
 int dakv_decode_attn_static(const float* q, const void* k_cache, const void* v_cache,
                             const int32_t* mask, const int32_t* valid_len, int B, int H,
                             int cap, int D, float scale, float* out, float* lse,
                             void* workspace, size_t workspace_bytes, int num_splits,
                             int32_t* err_flag, void* stream);
+
+/*
+ * decode_step_static -- one decode step of a layer: kv_append of the new token's
+ * K/V at write_pos[b] (mask bit set when a mask is given), then
+ * decode_attn_static over the updated buffer, in one pass.  [NPU-LLM] Part 2:
+ * each generate step writes the new row into the next free slot, then the
+ * incremental SDPA attends the whole valid buffer; the mutable command list of
+ * the NPU runtime replays the same work every step.  The result is what
+ * dakv_kv_append followed by dakv_decode_attn_static gives, bit for bit: the split
+ * that owns position write_pos[b] stores the row and attends it from registers.
+ *
+ * Arguments as for the two calls; k_cache, v_cache and mask are updated in place.
+ * A write position outside [0, cap) sets DAKV_ERR_WRITE_POS and that sequence is
+ * attended without the new row.  Supported: D in {64, 128}.
+ */
+int dakv_decode_step_static(const float* q, void* k_cache, void* v_cache, const void* k_new,
+                            const void* v_new, const int32_t* write_pos, int32_t* mask,
+                            const int32_t* valid_len, int B, int H, int cap, int D, float scale,
+                            float* out, float* lse, void* workspace, size_t workspace_bytes,
+                            int num_splits, int32_t* err_flag, void* stream);
 
 /* ========================================================================
  * Paged KV cache   ([PyPTO] section 3, tensor contract and gather semantics)
@@ -171,8 +191,8 @@ size_t dakv_decode_attn_paged_workspace_size(int B, int Hq, int D, int max_seq_l
  *   err_flag     optional; a bad block id excludes that block's rows and sets
  *                DAKV_ERR_BLOCK_ID; a sequence longer than max_seq_len or than
  *                its table is cut there and sets DAKV_ERR_SEQ_LENS
- * Supported: D = 128, block_size in {16, 32, 64, 128}, Hq % Hkv == 0,
- * Hq / Hkv <= 16.
+ * Supported: D = 128, block_size in {16, 32, 64, 128}, Hq / Hkv in {1, 2, 4, 8},
+ * max_seq_len small enough for 256 splits (278528 tokens at block 16).
  */
 int dakv_decode_attn_paged(const void* q, const void* key_cache, const void* value_cache,
                            const int32_t* block_tables, int table_cols,

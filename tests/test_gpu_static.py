@@ -305,3 +305,56 @@ def test_many_splits_merge_and_workspace_reuse():
         torch.cuda.synchronize()
         assert_attention_close(npy(out), ref_out)
         assert_lse_close(npy(lse), ref_lse)
+
+
+# ------------------------------------------------------------ fused decode step
+
+
+@pytest.mark.parametrize("D,lengths,cap", [(128, [1, 700, 4096, 63], 4096), (64, [5, 103], 1152)])
+def test_fused_step_equals_append_then_attend_bit_for_bit(D, lengths, cap):
+    B, H = len(lengths), 4
+    case = workloads.static_case(B, H, D, cap, lengths, device=DEV, seed=33)
+    g = torch.Generator(device=DEV).manual_seed(34)
+    kn = torch.randn((B, H, D), generator=g, device=DEV).to(torch.bfloat16)
+    vn = torch.randn((B, H, D), generator=g, device=DEV).to(torch.bfloat16)
+    pos = torch.tensor([L - 1 for L in lengths], dtype=torch.int32, device=DEV)
+    mask0 = case.mask.clone()
+    mask0[torch.arange(B), pos.long()] = 0          # the append sets this bit
+    k1, v1, m1 = case.k_cache.clone(), case.v_cache.clone(), mask0.clone()
+    dakv.kv_append(k1, v1, kn, vn, pos, m1)
+    out1, lse1 = dakv.decode_attn_static(case.q, k1, v1, mask=m1, valid_len=case.valid_len,
+                                         scale=case.scale)
+    k2, v2, m2 = case.k_cache.clone(), case.v_cache.clone(), mask0.clone()
+    out2, lse2 = dakv.decode_step_static(case.q, k2, v2, kn, vn, pos, mask=m2,
+                                         valid_len=case.valid_len, scale=case.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(out1, out2) and torch.equal(lse1, lse2)
+    assert torch.equal(k1.view(torch.int16), k2.view(torch.int16))
+    assert torch.equal(v1.view(torch.int16), v2.view(torch.int16))
+    assert torch.equal(m1, m2)
+    ek, ev, em = oracle.kv_append(bits(case.k_cache), bits(case.v_cache), bits(kn), bits(vn),
+                                  npy(pos), npy(mask0))
+    ref_out, ref_lse = oracle.decode_static(npy(case.q), ek, ev, em, lengths, case.scale)
+    assert_attention_close(npy(out2), ref_out)
+    assert_lse_close(npy(lse2), ref_lse)
+
+
+def test_fused_step_position_outside_attended_rows_and_out_of_range():
+    """A write position past the valid length is stored but not attended; one outside
+    the buffer is flagged and the sequence is attended without it."""
+    B, H, D, cap = 2, 2, 128, 512
+    case = workloads.static_case(B, H, D, cap, [100, 300], device=DEV, seed=35)
+    kn = torch.ones((B, H, D), dtype=torch.bfloat16, device=DEV)
+    pos = torch.tensor([400, 512], dtype=torch.int32, device=DEV)
+    flag = torch.zeros(1, dtype=torch.int32, device=DEV)
+    k0 = bits(case.k_cache).copy()
+    out, _ = dakv.decode_step_static(case.q, case.k_cache, case.v_cache, kn, kn, pos,
+                                     mask=case.mask, valid_len=case.valid_len, scale=case.scale,
+                                     err_flag=flag)
+    torch.cuda.synchronize()
+    assert int(flag.item()) & dakv._lib.ERR_WRITE_POS
+    assert float(case.k_cache[0, :, 400].float().mean()) == 1.0 and int(case.mask[0, 400]) == 1
+    assert np.array_equal(bits(case.k_cache)[1], k0[1])
+    ref, _ = oracle.decode_static(npy(case.q), k0, bits(case.v_cache), None, [100, 300],
+                                  case.scale)
+    assert_attention_close(npy(out), ref)
