@@ -54,95 +54,98 @@ hipError_t launch_kv_append(void* k_cache, void* v_cache, const void* k_new, con
 // gather_pa_kv_cache.  A workgroup owns kGatherTok consecutive OUTPUT rows, so
 // every output byte is written exactly once with no atomics and the work is
 // balanced whatever the sequence lengths are.  Phase 1 resolves each output row
-// to its source row (binary search of the cumulative seq_lens, then the block
-// table); phase 2 streams the rows, one wave per row, 16 bytes per lane.
+// to its source row: a binary search of the cumulative seq_lens (staged in LDS
+// when they fit) and one block-table read.  Phase 2 copies the workgroup's rows
+// as one flat list of 16-byte pieces (each token's K pieces, then its V pieces):
+// every thread issues kGatherSlots loads before its first store, consecutive
+// threads touch consecutive pieces of a row, and there is no branch per piece
+// (pieces past the end repeat the last piece; rows with a bad block id are
+// written as zeros).
 // ---------------------------------------------------------------------------
 constexpr int kGatherTok = 32;
-constexpr int kGatherUnroll = 4;
+constexpr int kGatherSlots = 16;
+constexpr int kGatherLensLds = 4096;
 
-__device__ __forceinline__ void copy_rows(const uint8_t* __restrict__ ksrc,
-                                          uint8_t* __restrict__ kdst, int k_pieces,
-                                          const uint8_t* __restrict__ vsrc,
-                                          uint8_t* __restrict__ vdst, int v_pieces,
-                                          bool valid, int lane) {
-  const int pieces = k_pieces > v_pieces ? k_pieces : v_pieces;
-  for (int base = 0; base < pieces; base += 64 * kGatherUnroll) {
-    uint4 kr[kGatherUnroll], vr[kGatherUnroll];
-#pragma unroll
-    for (int u = 0; u < kGatherUnroll; ++u) {
-      const int p = base + u * 64 + lane;
-      kr[u] = make_uint4(0, 0, 0, 0);
-      vr[u] = make_uint4(0, 0, 0, 0);
-      if (valid && p < k_pieces) kr[u] = load16(ksrc + (size_t)p * 16);
-      if (valid && p < v_pieces) vr[u] = load16(vsrc + (size_t)p * 16);
-    }
-#pragma unroll
-    for (int u = 0; u < kGatherUnroll; ++u) {
-      const int p = base + u * 64 + lane;
-      if (p < k_pieces) store16(kdst + (size_t)p * 16, kr[u]);
-      if (p < v_pieces) store16(vdst + (size_t)p * 16, vr[u]);
-    }
-  }
-}
+typedef uint32_t gx_u32x4 __attribute__((ext_vector_type(4)));
 
 __global__ void __launch_bounds__(256)
 gather_kernel(const uint8_t* __restrict__ key_cache, const uint8_t* __restrict__ value_cache,
-              int num_blocks, int block_size, int k_row_bytes, int v_row_bytes,
+              int num_blocks, int block_size, int k_pieces, int v_pieces, uint32_t piece_magic,
               const int32_t* __restrict__ block_tables, int Q, int table_cols,
               const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ seq_offset,
               int total_tokens, uint8_t* __restrict__ key_out, uint8_t* __restrict__ value_out,
               int32_t* err_flag) {
   __shared__ long long src_row[kGatherTok];
+  __shared__ int lens[kGatherLensLds];
   const int tok0 = blockIdx.x * kGatherTok;
+  const int ntok = min(kGatherTok, total_tokens - tok0);
   const int tid = threadIdx.x;
-  if (tid < kGatherTok) {
+  const bool staged = Q + 1 <= kGatherLensLds;
+  if (staged) {
+    for (int i = tid; i <= Q; i += 256) lens[i] = seq_lens[i];
+    __syncthreads();
+  }
+  if (tid < ntok) {
     const int o = tok0 + tid;
     long long src = -1;
-    if (o < total_tokens) {
-      // last q with seq_lens[q] <= o
-      int lo = 0, hi = Q - 1;
-      while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (seq_lens[mid] <= o) lo = mid; else hi = mid - 1;
-      }
-      const int q = lo;
-      const int t = o - seq_lens[q];
-      const int len = seq_lens[q + 1] - seq_lens[q];
-      const int off = seq_offset ? seq_offset[q] : 0;
-      if (t < 0 || t >= len || off < 0 || off % block_size != 0) {
+    // last q with seq_lens[q] <= o
+    int lo = 0, hi = Q - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      const int v = staged ? lens[mid] : seq_lens[mid];
+      if (v <= o) lo = mid; else hi = mid - 1;
+    }
+    const int q = lo;
+    const int start = staged ? lens[q] : seq_lens[q];
+    const int end = staged ? lens[q + 1] : seq_lens[q + 1];
+    const int t = o - start;
+    const int off = seq_offset ? seq_offset[q] : 0;
+    if (t < 0 || t >= end - start || off < 0 || off % block_size != 0) {
+      raise_flag(err_flag, 8);
+    } else {
+      const int col = off / block_size + t / block_size;
+      if (col >= table_cols) {
         raise_flag(err_flag, 8);
       } else {
-        const int col = off / block_size + t / block_size;
-        if (col >= table_cols) {
-          raise_flag(err_flag, 8);
-        } else {
-          const int phys = block_tables[(size_t)q * table_cols + col];
-          if (phys < 0 || phys >= num_blocks) {
-            raise_flag(err_flag, 1);
-          } else {
-            src = (long long)phys * block_size + (t % block_size);
-          }
-        }
+        const int phys = block_tables[(size_t)q * table_cols + col];
+        if (phys < 0 || phys >= num_blocks) raise_flag(err_flag, 1);
+        else src = (long long)phys * block_size + (t % block_size);
       }
     }
     src_row[tid] = src;
   }
   __syncthreads();
-  const int wave = tid >> 6;
-  const int lane = tid & 63;
-  const int k_pieces = k_row_bytes / 16;
-  const int v_pieces = v_row_bytes / 16;
-  for (int j = wave; j < kGatherTok; j += 4) {
-    const int o = tok0 + j;
-    if (o >= total_tokens) break;
-    const long long s = src_row[j];
-    const bool valid = s >= 0;
-    const long long sr = valid ? s : 0;
-    copy_rows(key_cache + sr * k_row_bytes, key_out + (size_t)o * k_row_bytes, k_pieces,
-              value_cache + sr * v_row_bytes, value_out + (size_t)o * v_row_bytes, v_pieces,
-              valid, lane);
+  const int P = k_pieces + v_pieces;
+  const int N = ntok * P;
+  const size_t kb = (size_t)k_pieces * 16, vb = (size_t)v_pieces * 16;
+  for (int base = 0; base < N; base += 256 * kGatherSlots) {
+    gx_u32x4 r[kGatherSlots];
+    uint8_t* dst[kGatherSlots];
+#pragma unroll
+    for (int s = 0; s < kGatherSlots; ++s) {
+      const int i = min(base + s * 256 + tid, N - 1);
+      const int j = (int)__umulhi((uint32_t)i, piece_magic);  // i / P
+      const int pc = i - j * P;
+      const long long sr = src_row[j];
+      const size_t row = sr >= 0 ? (size_t)sr : 0;
+      const size_t o = (size_t)(tok0 + j);
+      const bool is_k = pc < k_pieces;
+      const uint8_t* src = is_k ? key_cache + row * kb + (size_t)pc * 16
+                                : value_cache + row * vb + (size_t)(pc - k_pieces) * 16;
+      dst[s] = is_k ? key_out + o * kb + (size_t)pc * 16
+                    : value_out + o * vb + (size_t)(pc - k_pieces) * 16;
+      const gx_u32x4 v = *reinterpret_cast<const gx_u32x4*>(src);
+      r[s] = sr >= 0 ? v : gx_u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int s = 0; s < kGatherSlots; ++s)
+      __builtin_nontemporal_store(r[s], reinterpret_cast<gx_u32x4*>(dst[s]));
   }
 }
+
+// Longest token row (K plus V, in 16-byte pieces) the kernel takes: the
+// reciprocal multiply that splits piece indices is exact up to here.
+constexpr int kGatherMaxPieces = 11584;
 
 hipError_t launch_gather(const void* key_cache, const void* value_cache, int num_blocks,
                          int block_size, int k_row_bytes, int v_row_bytes,
@@ -150,13 +153,17 @@ hipError_t launch_gather(const void* key_cache, const void* value_cache, int num
                          const int32_t* seq_lens, const int32_t* seq_offset, int total_tokens,
                          void* key_out, void* value_out, int32_t* err_flag, hipStream_t stream) {
   if (total_tokens <= 0) return hipSuccess;
+  const int kp = k_row_bytes / 16, vp = v_row_bytes / 16;
+  const int P = kp + vp;
+  if (P > kGatherMaxPieces) return hipErrorNotSupported;
+  // ceil(2^32 / P): exact i / P for every i < kGatherTok * P when P <= 11584
+  const uint32_t magic = (uint32_t)(((1ull << 32) + (uint64_t)P - 1) / (uint64_t)P);
   const int grid = (total_tokens + kGatherTok - 1) / kGatherTok;
   hipLaunchKernelGGL(gather_kernel, dim3(grid), dim3(256), 0, stream,
                      static_cast<const uint8_t*>(key_cache),
-                     static_cast<const uint8_t*>(value_cache), num_blocks, block_size,
-                     k_row_bytes, v_row_bytes, block_tables, Q, table_cols, seq_lens,
-                     seq_offset, total_tokens, static_cast<uint8_t*>(key_out),
-                     static_cast<uint8_t*>(value_out), err_flag);
+                     static_cast<const uint8_t*>(value_cache), num_blocks, block_size, kp, vp,
+                     magic, block_tables, Q, table_cols, seq_lens, seq_offset, total_tokens,
+                     static_cast<uint8_t*>(key_out), static_cast<uint8_t*>(value_out), err_flag);
   return hipGetLastError();
 }
 

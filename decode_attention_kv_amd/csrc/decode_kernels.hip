@@ -225,6 +225,28 @@ __device__ __forceinline__ void attend_rows(const Rows& rows, const float (&q)[G
   }
 }
 
+// The same loop for a split of exactly kSteps steps (rows at or past r1 are
+// cleared by RowAt), fully unrolled with two register sets used in turn: the
+// loads of step s+1 are in flight while step s is computed, and with no loop the
+// compiler can wait on exactly the loads each step needs.
+template <int D, int G, int U, int kSteps, typename Rows, typename RowAt, typename Patch>
+__device__ __forceinline__ void attend_rows_fixed(const Rows& rows, const float (&q)[G][8],
+                                                  int r0, int r1, int wave, int slot,
+                                                  RowAt row_at, Patch patch, HeadState<G>& st) {
+  constexpr int RPW = 64 / (D / 8);
+  constexpr int kStep = kWaves * RPW * U;
+  uint4 kr[2][U], vr[2][U];
+  bool ok[2][U];
+  issue_rows<D, U>(rows, r0, r1, wave, slot, row_at, patch, kr[0], vr[0], ok[0]);
+#pragma unroll
+  for (int s = 0; s < kSteps; ++s) {
+    if (s + 1 < kSteps)
+      issue_rows<D, U>(rows, r0 + (s + 1) * kStep, r1, wave, slot, row_at, patch,
+                       kr[(s + 1) & 1], vr[(s + 1) & 1], ok[(s + 1) & 1]);
+    consume_rows<D, G, U>(q, kr[s & 1], vr[s & 1], ok[s & 1], st);
+  }
+}
+
 // Workspace of one decode call (fp32):
 //   o   [units * G][max_splits][D]   normalised partial outputs o / l
 //   lse [units * G][max_splits]      log2-sum-exp of each partial (-inf if empty)
@@ -294,9 +316,9 @@ constexpr int kStaticChunkMax = 256;  // rows per split of the static layout, at
 
 // Split pass of decode_attn_static and, with kAppend, of decode_step_static (the
 // new token's K/V row is written into the cache by the split that owns its
-// position and is attended from the registers it was read into; the mask bit is
-// set once per sequence).
-template <int D, int U, bool kAppend>
+// position, which attends it from registers; the mask bit is set once per
+// sequence).  A split is kSteps steps of U rows per lane group (chunk rows).
+template <int D, int U, int kSteps, bool kAppend>
 __global__ void __launch_bounds__(kThreads)
 static_decode_kernel(const float* __restrict__ q, uint16_t* __restrict__ k_cache,
                      uint16_t* __restrict__ v_cache, int32_t* __restrict__ mask,
@@ -306,8 +328,8 @@ static_decode_kernel(const float* __restrict__ q, uint16_t* __restrict__ k_cache
                      float* __restrict__ out, float* __restrict__ lse, int32_t* err_flag) {
   constexpr int LPR = D / 8;
   constexpr int RPW = 64 / LPR;
-  constexpr int kStep = kWaves * RPW * U;  // rows per step
-  constexpr int kBallots = (kStep + 63) / 64;
+  constexpr int kStep = kWaves * RPW * U;             // rows per step
+  constexpr int kBallots = (kSteps * kStep + 63) / 64;
   const int split = blockIdx.x % max_splits;
   const int bh = blockIdx.x / max_splits;
   const int b = bh / H;
@@ -318,16 +340,10 @@ static_decode_kernel(const float* __restrict__ q, uint16_t* __restrict__ k_cache
   const int r0 = split * chunk;
   const int32_t* mrow = mask ? mask + (size_t)b * cap : nullptr;
   // Every load this split needs before any wait: the valid length, the append
-  // position and row, the query, and the mask entries of the first step
-  // (clamped into the row, never branched).
+  // position, the query, and the mask entries of the split's rows (clamped
+  // into the row, never branched).
   const int Lraw = valid_len ? valid_len[b] : cap;
-  int p = -1;
-  uint4 kn = make_uint4(0, 0, 0, 0), vn = make_uint4(0, 0, 0, 0);
-  if constexpr (kAppend) {
-    p = write_pos[b];
-    kn = load16(k_new + (size_t)bh * D + sub * 8);
-    vn = load16(v_new + (size_t)bh * D + sub * 8);
-  }
+  int p = kAppend ? write_pos[b] : -1;
   const float4* qp = reinterpret_cast<const float4*>(q + (size_t)bh * D + sub * 8);
   const float4 qa = qp[0], qc = qp[1];
   int32_t mv[kBallots];
@@ -336,18 +352,24 @@ static_decode_kernel(const float* __restrict__ q, uint16_t* __restrict__ k_cache
     for (int k = 0; k < kBallots; ++k) mv[k] = mrow[min(r0 + 64 * k + lane, cap - 1)];
   }
   const bool report = split == 0 && h == 0 && threadIdx.x == 0;
+  uint4 kn = make_uint4(0, 0, 0, 0), vn = make_uint4(0, 0, 0, 0);
   if constexpr (kAppend) {
     if (p < 0 || p >= cap) {
       if (report) raise_flag(err_flag, 2);
       p = -1;
     } else if (p / chunk == split) {
-      // this split owns the position: store the new row (and the mask bit once)
-      if (wave == 0 && lane < 2 * LPR) {
-        const size_t at = ((size_t)bh * cap + p) * D + (size_t)(lane % LPR) * 8;
-        const uint16_t* src = (lane < LPR ? k_new : v_new) + (size_t)bh * D + (lane % LPR) * 8;
-        store16((lane < LPR ? k_cache : v_cache) + at, load16(src));
+      // this split owns the position: read the new row, store it (and the mask
+      // bit, once per sequence)
+      kn = load16(k_new + (size_t)bh * D + sub * 8);
+      vn = load16(v_new + (size_t)bh * D + sub * 8);
+      if (wave == 0 && lane < LPR) {
+        const size_t at = ((size_t)bh * cap + p) * D + (size_t)lane * 8;
+        store16(k_cache + at, kn);
+        store16(v_cache + at, vn);
       }
       if (mrow && h == 0 && threadIdx.x == 0) mask[(size_t)b * cap + p] = 1;
+    } else {
+      p = -1;  // another split holds the new row
     }
   }
   int L = Lraw;
@@ -363,29 +385,18 @@ static_decode_kernel(const float* __restrict__ q, uint16_t* __restrict__ k_cache
   qr[0][2] = qa.z * scale_log2; qr[0][3] = qa.w * scale_log2;
   qr[0][4] = qc.x * scale_log2; qr[0][5] = qc.y * scale_log2;
   qr[0][6] = qc.z * scale_log2; qr[0][7] = qc.w * scale_log2;
-  // bit (t - step base) of the ballots: row t of the current step is attended
+  // bit (t - r0) of the ballots: row t of the split is attended
   uint64_t bits[kBallots];
 #pragma unroll
   for (int k = 0; k < kBallots; ++k)
     bits[k] = __ballot(r0 + 64 * k + lane < r1 && (!mrow || mv[k] != 0));
-  int bits_base = r0;
-  auto step = [&](int base) {
-    if (base != bits_base) {
-      bits_base = base;
-#pragma unroll
-      for (int k = 0; k < kBallots; ++k) {
-        const int t = base + 64 * k + lane;
-        bits[k] = __ballot(t < r1 && (!mrow || mrow[min(t, cap - 1)] != 0));
-      }
-    }
-  };
   const BufferRows rows(k_cache + (size_t)bh * cap * D, v_cache + (size_t)bh * cap * D,
                         (uint32_t)cap * D * 2);
   const uint32_t lane_off = (uint32_t)sub * 16;
   auto row_at = [&](int t, bool& ok) -> uint32_t {
-    const int o = t - bits_base;
+    const int o = t - r0;
     ok = ok && (((bits[o >> 6] >> (o & 63)) & 1ull) || t == p);
-    // the appended row comes from the registers, not from memory
+    // the appended row comes from registers, not from memory
     return (ok && t != p) ? (uint32_t)t * (D * 2) + lane_off : BufferRows::kNoRow;
   };
   auto patch = [&](int t, uint4& kr, uint4& vr) {
@@ -398,7 +409,7 @@ static_decode_kernel(const float* __restrict__ q, uint16_t* __restrict__ k_cache
   };
   HeadState<1> st;
   init_state(st);
-  attend_rows<D, 1, U>(rows, qr, r0, r1, wave, lane / LPR, row_at, patch, step, st);
+  attend_rows_fixed<D, 1, U, kSteps>(rows, qr, r0, r1, wave, lane / LPR, row_at, patch, st);
   merge_groups<LPR, 1>(st);
   finish_split<D, 1>(st, lane, wave, ws, (size_t)bh, split, n, max_splits, out, lse);
 }
@@ -558,19 +569,21 @@ merge_kernel(Workspace ws, int heads, int chunk, int max_splits, int mode,
 static int round_up(int x, int m) { return (x + m - 1) / m * m; }
 
 SplitPlan plan_static(int B, int H, int cap, int D, int forced_splits) {
+  (void)B;
+  (void)H;
   (void)D;
   SplitPlan p;
-  int c;
+  // at least ceil(cap / 256) rows so that the splits fit the merge's 256 slots
+  int want = (cap + kMaxSplits - 1) / kMaxSplits;
   if (forced_splits > 0) {
-    c = round_up((cap + forced_splits - 1) / forced_splits, kMinChunk);
-  } else {
-    // short splits (one 64-row step at D = 128): the CU keeps many resident and
-    // hides each one's memory latency behind the others; longer only when the
-    // split count would exceed what the merge holds
-    c = round_up((cap + kMaxSplits - 1) / kMaxSplits, kMinChunk);
+    const int per = (cap + forced_splits - 1) / forced_splits;
+    if (per > want) want = per;
   }
-  if (c < kMinChunk) c = kMinChunk;
-  if (c > kStaticChunkMax) c = kStaticChunkMax;
+  // split sizes are 64, 128 or 256 rows; by default the shortest the limit
+  // allows (one 64-row step at D = 128): many short splits per CU hide each
+  // one's memory latency behind the others
+  int c = kMinChunk;
+  while (c < want && c < kStaticChunkMax) c *= 2;
   p.chunk = c;
   p.max_splits = cap > 0 ? (cap + c - 1) / c : 1;
   return p;
@@ -590,6 +603,20 @@ static Workspace carve(void* ws, size_t heads, int max_splits, int D) {
   return w;
 }
 
+template <int D, int kSteps, bool kAppend>
+static void launch_static_k(const float* q, void* k_cache, void* v_cache, int32_t* mask,
+                            const int32_t* valid_len, const void* k_new, const void* v_new,
+                            const int32_t* write_pos, int B, int H, int cap, float scale,
+                            float* out, float* lse, const Workspace& w, const SplitPlan& plan,
+                            int32_t* err_flag, hipStream_t stream) {
+  hipLaunchKernelGGL((static_decode_kernel<D, 4, kSteps, kAppend>),
+                     dim3((unsigned)(B * H * plan.max_splits)), dim3(kThreads), 0, stream, q,
+                     static_cast<uint16_t*>(k_cache), static_cast<uint16_t*>(v_cache), mask,
+                     valid_len, static_cast<const uint16_t*>(k_new),
+                     static_cast<const uint16_t*>(v_new), write_pos, H, cap, scale * kLog2e,
+                     plan.chunk, plan.max_splits, w, out, lse, err_flag);
+}
+
 template <int D, bool kAppend>
 static void launch_static_d(const float* q, void* k_cache, void* v_cache, int32_t* mask,
                             const int32_t* valid_len, const void* k_new, const void* v_new,
@@ -597,12 +624,16 @@ static void launch_static_d(const float* q, void* k_cache, void* v_cache, int32_
                             float* out, float* lse, void* ws, const SplitPlan& plan,
                             int32_t* err_flag, hipStream_t stream) {
   const Workspace w = carve(ws, (size_t)B * H, plan.max_splits, D);
-  hipLaunchKernelGGL((static_decode_kernel<D, 4, kAppend>), dim3((unsigned)(B * H * plan.max_splits)),
-                     dim3(kThreads), 0, stream, q, static_cast<uint16_t*>(k_cache),
-                     static_cast<uint16_t*>(v_cache), mask, valid_len,
-                     static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new),
-                     write_pos, H, cap, scale * kLog2e, plan.chunk, plan.max_splits, w, out, lse,
-                     err_flag);
+  constexpr int kStep = kWaves * (64 / (D / 8)) * 4;  // rows per step (U = 4)
+  const int steps = (plan.chunk + kStep - 1) / kStep;
+#define DAKV_STATIC(S)                                                                      \
+  launch_static_k<D, S, kAppend>(q, k_cache, v_cache, mask, valid_len, k_new, v_new,         \
+                                 write_pos, B, H, cap, scale, out, lse, w, plan, err_flag,   \
+                                 stream)
+  if (steps <= 1) DAKV_STATIC(1);
+  else if (steps <= 2) DAKV_STATIC(2);
+  else DAKV_STATIC(4);
+#undef DAKV_STATIC
   if (plan.max_splits > 1)
     hipLaunchKernelGGL(merge_kernel<D>, dim3(B * H), dim3(kThreads), 0, stream, w, H, plan.chunk,
                        plan.max_splits, 0, valid_len, cap, nullptr, nullptr, 1, 0, 0, out, lse);

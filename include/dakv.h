@@ -161,7 +161,8 @@ int dakv_decode_step_static(const float* q, void* k_cache, void* v_cache, const 
  *              output row zero and sets DAKV_ERR_BLOCK_ID; inconsistent
  *              seq_lens set DAKV_ERR_SEQ_LENS (rows past total_tokens are never
  *              written)
- * Requires Hk*Dk*2 and Hv*Dv*2 to be multiples of 16.
+ * Requires Hk*Dk*2 and Hv*Dv*2 to be multiples of 16; ENOTSUP when a token's
+ * K plus V row exceeds 185344 bytes.
  */
 int dakv_gather_pa_kv_cache(const void* key_cache, const void* value_cache, int num_blocks,
                             int block_size, int Hk, int Dk, int Hv, int Dv,
