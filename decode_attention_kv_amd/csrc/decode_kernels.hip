@@ -417,6 +417,20 @@ static_decode_kernel(const float* __restrict__ q, uint16_t* __restrict__ k_cache
 // ------------------------------------------------------------------ paged layout
 constexpr int kMaxTableSpan = 72;  // block-table entries one split may touch
 
+// Step shape of the paged kernel per group size G: U rows per lane group per
+// step and kSteps steps per unrolled super-step (fewer rows in flight when each
+// row feeds more heads and the state takes more registers).
+template <int G> struct PagedShape;
+template <> struct PagedShape<1> { static constexpr int U = 4, kSteps = 2; };
+template <> struct PagedShape<2> { static constexpr int U = 4, kSteps = 2; };
+template <> struct PagedShape<4> { static constexpr int U = 2, kSteps = 4; };
+template <> struct PagedShape<8> { static constexpr int U = 2, kSteps = 2; };
+
+template <int G>
+constexpr int paged_super_rows() {
+  return kWaves * 4 * PagedShape<G>::U * PagedShape<G>::kSteps;  // D = 128: 4 rows per wave
+}
+
 template <int G>
 __global__ void __launch_bounds__(kThreads)
 paged_decode_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ key_cache,
@@ -428,12 +442,23 @@ paged_decode_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
                     float* __restrict__ out, float* __restrict__ lse, int32_t* err_flag) {
   constexpr int D = 128;
   constexpr int LPR = D / 8;
-  constexpr int U = G >= 4 ? 2 : 4;
+  constexpr int U = PagedShape<G>::U;
+  constexpr int kSteps = PagedShape<G>::kSteps;
+  constexpr int kSuper = paged_super_rows<G>();
   __shared__ int tbl[kMaxTableSpan];
   const int split = blockIdx.x % max_splits;
   const int bg = blockIdx.x / max_splits;
   const int b = bg / Hkv;
   const int g = bg - b * Hkv;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int sub = lane % LPR;
+  const int group = Hq / Hkv;  // == G
+  // the query first (independent of everything else), then the lengths
+  uint4 qraw[G];
+#pragma unroll
+  for (int j = 0; j < G; ++j)
+    qraw[j] = load16(q + ((size_t)b * Hq + (size_t)g * group + j) * D + sub * 8);
   int toff = 0;
   const int L = paged_len(seq_lens, seq_offset, b, block_size, table_cols, max_len, &toff,
                           err_flag, split == 0 && g == 0 && threadIdx.x == 0);
@@ -451,19 +476,14 @@ paged_decode_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     }
     tbl[i] = phys;
   }
-  __syncthreads();
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int sub = lane % LPR;
-  const int group = Hq / Hkv;  // == G
   float qr[G][8];
 #pragma unroll
   for (int j = 0; j < G; ++j) {
-    const uint4 raw = load16(q + ((size_t)b * Hq + (size_t)g * group + j) * D + sub * 8);
-    unpack8(raw, qr[j]);
+    unpack8(qraw[j], qr[j]);
 #pragma unroll
     for (int i = 0; i < 8; ++i) qr[j][i] *= scale_log2;
   }
+  __syncthreads();
   const size_t row_stride = (size_t)Hkv * D;
   const size_t head_off = (size_t)g * D + (size_t)sub * 8;
   const int bs_mask = block_size - 1;
@@ -475,8 +495,9 @@ paged_decode_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
   };
   HeadState<G> st;
   init_state(st);
-  attend_rows<D, G, U>(rows, qr, r0, r1, wave, lane / LPR, row_at, NoPatch{},
-                       [](int) {}, st);
+  for (int base = r0; base < r1; base += kSuper)
+    attend_rows_fixed<D, G, U, kSteps>(rows, qr, base, r1, wave, lane / LPR, row_at, NoPatch{},
+                                       st);
   merge_groups<LPR, G>(st);
   finish_split<D, G>(st, lane, wave, ws, (size_t)b * Hq + (size_t)g * group, split, n,
                      max_splits, out, lse);
@@ -663,9 +684,21 @@ hipError_t launch_decode_static(const float* q, void* k_cache, void* v_cache, in
   return hipGetLastError();
 }
 
-SplitPlan plan_paged(int B, int Hkv, int max_seq_len, int block_size, int forced_splits) {
+static int paged_super(int G) {
+  switch (G) {
+    case 1: return paged_super_rows<1>();
+    case 2: return paged_super_rows<2>();
+    case 4: return paged_super_rows<4>();
+    default: return paged_super_rows<8>();
+  }
+}
+
+SplitPlan plan_paged(int B, int Hkv, int G, int max_seq_len, int block_size,
+                     int forced_splits) {
   SplitPlan p;
-  const int unit = block_size > kMinChunk ? block_size : kMinChunk;
+  int unit = block_size > kMinChunk ? block_size : kMinChunk;
+  const int sup = paged_super(G);
+  if (sup > unit) unit = sup;
   // one split may touch at most kMaxTableSpan - 2 blocks
   const int most = ((kMaxTableSpan - 2) * block_size) / unit * unit;
   const int least = round_up((max_seq_len + kMaxSplits - 1) / kMaxSplits, unit);
@@ -686,7 +719,9 @@ SplitPlan plan_paged(int B, int Hkv, int max_seq_len, int block_size, int forced
 }
 
 bool paged_supported(int max_seq_len, int block_size) {
-  const int unit = block_size > kMinChunk ? block_size : kMinChunk;
+  // the widest super-step (128 rows) bounds the unit from below
+  int unit = block_size > kMinChunk ? block_size : kMinChunk;
+  if (unit < 128) unit = 128;
   const int most = ((kMaxTableSpan - 2) * block_size) / unit * unit;
   return (long long)most * kMaxSplits >= max_seq_len;
 }

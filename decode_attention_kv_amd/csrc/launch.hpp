@@ -36,7 +36,8 @@ hipError_t launch_decode_static(const float* q, void* k_cache, void* v_cache, in
                                 float scale, float* out, float* lse, void* ws,
                                 const SplitPlan& plan, int32_t* err_flag, hipStream_t stream);
 
-SplitPlan plan_paged(int B, int Hkv, int max_seq_len, int block_size, int forced_splits);
+SplitPlan plan_paged(int B, int Hkv, int G, int max_seq_len, int block_size,
+                     int forced_splits);
 // Whether a sequence of max_seq_len tokens fits the split limits of the paged kernel.
 bool paged_supported(int max_seq_len, int block_size);
 size_t paged_workspace_bytes(int B, int Hq, int D, int max_seq_len, int block_size);
