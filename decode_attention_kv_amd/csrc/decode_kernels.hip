@@ -204,31 +204,12 @@ __device__ __forceinline__ void consume_rows(const float (&q)[G][8], const uint4
   }
 }
 
-// The row loop shared by the static and paged kernels.  Each step issues all of
-// its 2U loads (U rows per lane group, K and V) before using any of them; the
-// latency between steps is hidden by the other workgroups resident on the CU
-// (splits are one or a few steps long).  Step(base) runs before each step's loads
-// (the static kernel refreshes its mask ballots there).  q is pre-scaled by
-// scale * log2(e).
-template <int D, int G, int U, typename Rows, typename RowAt, typename Patch, typename Step>
-__device__ __forceinline__ void attend_rows(const Rows& rows, const float (&q)[G][8], int r0,
-                                            int r1, int wave, int slot, RowAt row_at,
-                                            Patch patch, Step step, HeadState<G>& st) {
-  constexpr int RPW = 64 / (D / 8);
-  constexpr int kStep = kWaves * RPW * U;
-  for (int base = r0; base < r1; base += kStep) {
-    step(base);
-    uint4 kr[U], vr[U];
-    bool ok[U];
-    issue_rows<D, U>(rows, base, r1, wave, slot, row_at, patch, kr, vr, ok);
-    consume_rows<D, G, U>(q, kr, vr, ok, st);
-  }
-}
-
-// The same loop for a split of exactly kSteps steps (rows at or past r1 are
-// cleared by RowAt), fully unrolled with two register sets used in turn: the
-// loads of step s+1 are in flight while step s is computed, and with no loop the
-// compiler can wait on exactly the loads each step needs.
+// The row loop shared by the static and paged kernels, for exactly kSteps steps
+// (rows at or past r1 are cleared by RowAt).  Each step issues all of its 2U loads
+// (U rows per lane group, K and V) before using any; the steps are fully unrolled
+// with two register sets used in turn, so the loads of step s+1 are in flight
+// while step s is computed and, with no loop, the compiler waits on exactly the
+// loads each step needs.  q is pre-scaled by scale * log2(e).
 template <int D, int G, int U, int kSteps, typename Rows, typename RowAt, typename Patch>
 __device__ __forceinline__ void attend_rows_fixed(const Rows& rows, const float (&q)[G][8],
                                                   int r0, int r1, int wave, int slot,
@@ -259,8 +240,78 @@ __host__ __device__ inline size_t ws_floats(size_t heads, int max_splits, int D)
   return heads * (size_t)max_splits * (size_t)(D + 1);
 }
 
+// Log-sum-exp merge of one head's n partials by the whole workgroup.  The
+// partials' log2-sum-exps go to LDS at once; then the D/4 float4 columns are
+// shared among kThreads / (D/4) split groups, so every thread issues its few
+// partial loads together, and the groups are summed through LDS.
+template <int D>
+__device__ __forceinline__ void merge_head(const float* __restrict__ lp,
+                                           const float* __restrict__ op, int n,
+                                           float* __restrict__ outp, float* __restrict__ lsep) {
+  constexpr int kCols = D / 4;
+  constexpr int kGroups = kThreads / kCols;
+  __shared__ float sm_w[kMaxSplits];
+  __shared__ float sm_part[kWaves];
+  __shared__ float4 sm_red[kThreads];
+  const int tid = threadIdx.x;
+  float v = kNegInf;
+  for (int j = tid; j < n; j += kThreads) {
+    const float x = lp[j];
+    sm_w[j] = x;
+    v = fmaxf(v, x);
+  }
+  for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
+  if ((tid & 63) == 0) sm_part[tid >> 6] = v;
+  __syncthreads();
+  const float M = fmaxf(fmaxf(sm_part[0], sm_part[1]), fmaxf(sm_part[2], sm_part[3]));
+  __syncthreads();
+  float den_part = 0.f;
+  if (M != kNegInf) {
+    for (int j = tid; j < n; j += kThreads) {
+      const float w = exp2_fast(sm_w[j] - M);
+      sm_w[j] = w;
+      den_part += w;
+    }
+  }
+  for (int off = 32; off > 0; off >>= 1) den_part += __shfl_xor(den_part, off);
+  if ((tid & 63) == 0) sm_part[tid >> 6] = den_part;
+  __syncthreads();
+  const float den = sm_part[0] + sm_part[1] + sm_part[2] + sm_part[3];
+  const int c = tid % kCols;
+  const int grp = tid / kCols;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (M != kNegInf) {
+    const float* cp = op + c * 4;
+    for (int j = grp; j < n; j += kGroups) {
+      const float w = sm_w[j];
+      const float4 x = *reinterpret_cast<const float4*>(cp + (size_t)j * D);
+      acc.x += w * x.x; acc.y += w * x.y; acc.z += w * x.z; acc.w += w * x.w;
+    }
+  }
+  sm_red[tid] = acc;
+  __syncthreads();
+  if (tid < kCols) {
+#pragma unroll
+    for (int g = 1; g < kGroups; ++g) {
+      const float4 x = sm_red[tid + g * kCols];
+      acc.x += x.x; acc.y += x.y; acc.z += x.z; acc.w += x.w;
+    }
+    float4 r = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (M != kNegInf) {
+      const float inv = 1.f / den;
+      r = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+    }
+    *reinterpret_cast<float4*>(outp + c * 4) = r;
+    if (lsep && tid == 0) *lsep = M == kNegInf ? kNegInf : (M + __log2f(den)) * kLn2;
+  }
+  __syncthreads();
+}
+
 // End of a split: combine the waves through LDS, then write the output directly
 // (a sequence that fits one split) or this split's partial for merge_kernel.
+// (The splits are not merged in the last one to finish: publishing the partials
+// to another XCD takes a device-scope release that writes back the L2, or
+// device-coherent atomics; both measured far slower than a second launch.)
 template <int D, int G>
 __device__ __forceinline__ void finish_split(const HeadState<G>& st, int lane, int wave,
                                              const Workspace& ws, size_t head0, int split,
@@ -314,29 +365,36 @@ __device__ __forceinline__ void finish_split(const HeadState<G>& st, int lane, i
 // ---------------------------------------------------------------- static layout
 constexpr int kStaticChunkMax = 256;  // rows per split of the static layout, at most
 
-// Split pass of decode_attn_static and, with kAppend, of decode_step_static (the
-// new token's K/V row is written into the cache by the split that owns its
-// position, which attends it from registers; the mask bit is set once per
-// sequence).  A split is kSteps steps of U rows per lane group (chunk rows).
+// Split pass of decode_attn_static and, with kAppend, of decode_step_static.
+// A split is kSteps steps of U rows per lane group (chunk rows).  Workgroups are
+// numbered split-major (all units' first splits, then all second splits, ...).
+//
+// Appending: the split that owns position p = write_pos[b] stores the new K/V row
+// with exactly the lanes that later load that row's pieces, so the ordinary load
+// returns the stored values (a lane's load after its own store to the same
+// address); p is attended whatever its mask entry says (the append sets it), and
+// the mask bit is written once per sequence.
 template <int D, int U, int kSteps, bool kAppend>
 __global__ void __launch_bounds__(kThreads)
 static_decode_kernel(const float* __restrict__ q, uint16_t* __restrict__ k_cache,
                      uint16_t* __restrict__ v_cache, int32_t* __restrict__ mask,
                      const int32_t* __restrict__ valid_len, const uint16_t* __restrict__ k_new,
                      const uint16_t* __restrict__ v_new, const int32_t* __restrict__ write_pos,
-                     int H, int cap, float scale_log2, int chunk, int max_splits, Workspace ws,
+                     int H, int cap, float scale_log2, int chunk, int units, Workspace ws,
                      float* __restrict__ out, float* __restrict__ lse, int32_t* err_flag) {
   constexpr int LPR = D / 8;
   constexpr int RPW = 64 / LPR;
   constexpr int kStep = kWaves * RPW * U;             // rows per step
   constexpr int kBallots = (kSteps * kStep + 63) / 64;
-  const int split = blockIdx.x % max_splits;
-  const int bh = blockIdx.x / max_splits;
+  const int split = blockIdx.x / units;
+  const int bh = blockIdx.x - split * units;
+  const int max_splits = gridDim.x / units;
   const int b = bh / H;
   const int h = bh - b * H;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int sub = lane % LPR;
+  const int slot = lane / LPR;
   const int r0 = split * chunk;
   const int32_t* mrow = mask ? mask + (size_t)b * cap : nullptr;
   // Every load this split needs before any wait: the valid length, the append
@@ -352,20 +410,16 @@ static_decode_kernel(const float* __restrict__ q, uint16_t* __restrict__ k_cache
     for (int k = 0; k < kBallots; ++k) mv[k] = mrow[min(r0 + 64 * k + lane, cap - 1)];
   }
   const bool report = split == 0 && h == 0 && threadIdx.x == 0;
-  uint4 kn = make_uint4(0, 0, 0, 0), vn = make_uint4(0, 0, 0, 0);
   if constexpr (kAppend) {
     if (p < 0 || p >= cap) {
       if (report) raise_flag(err_flag, 2);
       p = -1;
     } else if (p / chunk == split) {
-      // this split owns the position: read the new row, store it (and the mask
-      // bit, once per sequence)
-      kn = load16(k_new + (size_t)bh * D + sub * 8);
-      vn = load16(v_new + (size_t)bh * D + sub * 8);
-      if (wave == 0 && lane < LPR) {
-        const size_t at = ((size_t)bh * cap + p) * D + (size_t)lane * 8;
-        store16(k_cache + at, kn);
-        store16(v_cache + at, vn);
+      const int o = p - r0;  // the lanes of (wave, slot) below load row p in the loop
+      if (wave == (o / RPW) % kWaves && slot == o % RPW) {
+        const size_t at = ((size_t)bh * cap + p) * D + (size_t)sub * 8;
+        store16(k_cache + at, load16(k_new + (size_t)bh * D + sub * 8));
+        store16(v_cache + at, load16(v_new + (size_t)bh * D + sub * 8));
       }
       if (mrow && h == 0 && threadIdx.x == 0) mask[(size_t)b * cap + p] = 1;
     } else {
@@ -396,20 +450,11 @@ static_decode_kernel(const float* __restrict__ q, uint16_t* __restrict__ k_cache
   auto row_at = [&](int t, bool& ok) -> uint32_t {
     const int o = t - r0;
     ok = ok && (((bits[o >> 6] >> (o & 63)) & 1ull) || t == p);
-    // the appended row comes from registers, not from memory
-    return (ok && t != p) ? (uint32_t)t * (D * 2) + lane_off : BufferRows::kNoRow;
-  };
-  auto patch = [&](int t, uint4& kr, uint4& vr) {
-    if constexpr (kAppend) {
-      if (t == p) {
-        kr = kn;
-        vr = vn;
-      }
-    }
+    return ok ? (uint32_t)t * (D * 2) + lane_off : BufferRows::kNoRow;
   };
   HeadState<1> st;
   init_state(st);
-  attend_rows_fixed<D, 1, U, kSteps>(rows, qr, r0, r1, wave, lane / LPR, row_at, patch, st);
+  attend_rows_fixed<D, 1, U, kSteps>(rows, qr, r0, r1, wave, slot, row_at, NoPatch{}, st);
   merge_groups<LPR, 1>(st);
   finish_split<D, 1>(st, lane, wave, ws, (size_t)bh, split, n, max_splits, out, lse);
 }
@@ -515,14 +560,8 @@ merge_kernel(Workspace ws, int heads, int chunk, int max_splits, int mode,
              const int32_t* __restrict__ valid_len, int cap, const int32_t* __restrict__ seq_lens,
              const int32_t* __restrict__ seq_offset, int block_size, int table_cols, int max_len,
              float* __restrict__ out, float* __restrict__ lse) {
-  constexpr int kCols = D / 4;
-  constexpr int kGroups = kThreads / kCols;
-  __shared__ float sm_w[kMaxSplits];
-  __shared__ float sm_part[kWaves];
-  __shared__ float4 sm_red[kThreads];
   const int bh = blockIdx.x;
   const int b = bh / heads;
-  const int tid = threadIdx.x;
   int L;
   if (mode == 0) {
     L = static_len(valid_len, b, cap, nullptr, false);
@@ -533,57 +572,8 @@ merge_kernel(Workspace ws, int heads, int chunk, int max_splits, int mode,
   }
   const int n = L > 0 ? (L + chunk - 1) / chunk : 1;
   if (n == 1) return;  // the split kernel wrote this head's output
-  const float* lp = ws.lse + (size_t)bh * max_splits;
-  float v = kNegInf;
-  for (int j = tid; j < n; j += kThreads) {
-    const float x = lp[j];
-    sm_w[j] = x;
-    v = fmaxf(v, x);
-  }
-  for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
-  if ((tid & 63) == 0) sm_part[tid >> 6] = v;
-  __syncthreads();
-  const float M = fmaxf(fmaxf(sm_part[0], sm_part[1]), fmaxf(sm_part[2], sm_part[3]));
-  __syncthreads();
-  float den_part = 0.f;
-  if (M != kNegInf) {
-    for (int j = tid; j < n; j += kThreads) {
-      const float w = exp2_fast(sm_w[j] - M);
-      sm_w[j] = w;
-      den_part += w;
-    }
-  }
-  for (int off = 32; off > 0; off >>= 1) den_part += __shfl_xor(den_part, off);
-  if ((tid & 63) == 0) sm_part[tid >> 6] = den_part;
-  __syncthreads();
-  const float den = sm_part[0] + sm_part[1] + sm_part[2] + sm_part[3];
-  const int c = tid % kCols;
-  const int grp = tid / kCols;
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  if (M != kNegInf) {
-    const float* op = ws.o + (size_t)bh * max_splits * D + c * 4;
-    for (int j = grp; j < n; j += kGroups) {
-      const float w = sm_w[j];
-      const float4 x = *reinterpret_cast<const float4*>(op + (size_t)j * D);
-      acc.x += w * x.x; acc.y += w * x.y; acc.z += w * x.z; acc.w += w * x.w;
-    }
-  }
-  sm_red[tid] = acc;
-  __syncthreads();
-  if (tid < kCols) {
-#pragma unroll
-    for (int g = 1; g < kGroups; ++g) {
-      const float4 x = sm_red[tid + g * kCols];
-      acc.x += x.x; acc.y += x.y; acc.z += x.z; acc.w += x.w;
-    }
-    float4 r = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (M != kNegInf) {
-      const float inv = 1.f / den;
-      r = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
-    }
-    *reinterpret_cast<float4*>(out + (size_t)bh * D + c * 4) = r;
-    if (lse && tid == 0) lse[bh] = M == kNegInf ? kNegInf : (M + __log2f(den)) * kLn2;
-  }
+  merge_head<D>(ws.lse + (size_t)bh * max_splits, ws.o + (size_t)bh * max_splits * D, n,
+                       out + (size_t)bh * D, lse ? lse + bh : nullptr);
 }
 
 // ------------------------------------------------------------------- planning
@@ -635,7 +625,7 @@ static void launch_static_k(const float* q, void* k_cache, void* v_cache, int32_
                      static_cast<uint16_t*>(k_cache), static_cast<uint16_t*>(v_cache), mask,
                      valid_len, static_cast<const uint16_t*>(k_new),
                      static_cast<const uint16_t*>(v_new), write_pos, H, cap, scale * kLog2e,
-                     plan.chunk, plan.max_splits, w, out, lse, err_flag);
+                     plan.chunk, B * H, w, out, lse, err_flag);
 }
 
 template <int D, bool kAppend>
