@@ -580,8 +580,6 @@ merge_kernel(Workspace ws, int heads, int chunk, int max_splits, int mode,
 static int round_up(int x, int m) { return (x + m - 1) / m * m; }
 
 SplitPlan plan_static(int B, int H, int cap, int D, int forced_splits) {
-  (void)B;
-  (void)H;
   (void)D;
   SplitPlan p;
   // at least ceil(cap / 256) rows so that the splits fit the merge's 256 slots
@@ -590,9 +588,12 @@ SplitPlan plan_static(int B, int H, int cap, int D, int forced_splits) {
     const int per = (cap + forced_splits - 1) / forced_splits;
     if (per > want) want = per;
   }
-  // split sizes are 64, 128 or 256 rows; by default the shortest the limit
-  // allows (one 64-row step at D = 128): many short splits per CU hide each
-  // one's memory latency behind the others
+  // split sizes are 64, 128 or 256 rows.  Short splits (one 64-row step at
+  // D = 128) let the CU hide each one's memory latency behind the others; once
+  // the call has some 4096 or more 128-row splits, 128 rows measure better
+  // (fewer partials to merge, fewer workgroups to launch).
+  if (forced_splits <= 0 && (long long)B * H * ((cap + 127) / 128) >= 4096 && want < 128)
+    want = 128;
   int c = kMinChunk;
   while (c < want && c < kStaticChunkMax) c *= 2;
   p.chunk = c;
