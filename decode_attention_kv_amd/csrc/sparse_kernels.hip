@@ -10,7 +10,8 @@
 //   * the rows are fetched from HBM (16-byte loads, issued one tile ahead) into
 //     an LDS buffer (row pitch 1168 bytes to spread banks), double-buffered;
 //   * S^T[token, head] = G Q^T with v_mfma_f32_16x16x32_bf16: A = 16 rows x 32
-//     dims read from LDS, B = Q^T kept in registers for the whole split;
+//     dims and B = Q^T (the group's Q rows, staged in LDS once per split) both
+//     read from LDS, six k-steps of operands ahead of their MFMAs;
 //   * the C layout of S^T puts head (lane % 16) and 4 tokens per half-tile in each
 //     lane, which is already the A layout of P for O = P V when the 8 tokens of a
 //     lane group are taken in the order {4g..4g+3, 16+4g..16+4g+3};
@@ -43,6 +44,7 @@ constexpr int kKSteps = kDqk / 32;                      // 18
 constexpr int kVBlocks = kDv / 128;                     // 4
 // The page's rescale threshold is 6 in natural-log units; scores here are in log2.
 constexpr float kRescale = 6.0f * kLog2e;
+constexpr uint32_t kNoRow = 0x80000000u;  // a buffer offset past any sequence: loads 0
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(const u32x4_t& v) {
   return __builtin_bit_cast(bf16x8_t, v);
@@ -54,7 +56,8 @@ sparse_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
                     float scale_log2, int n_hg, int n_splits, int per_hg,
                     float* __restrict__ ws_o, float* __restrict__ ws_lse, int32_t* err_flag) {
   __shared__ __attribute__((aligned(16))) uint8_t tile[2][kTile * kPitch];
-  __shared__ int rows[kSplit];
+  __shared__ __attribute__((aligned(16))) uint8_t qs[kHeadsPerWG * kPitch];  // this group's Q rows
+  __shared__ uint32_t rows[kSplit];  // byte offset of each index's row in kv[b], or kNoRow
   // blockIdx -> (head group, unit); units of the same (b, split) in different head
   // groups are per_hg (a multiple of 8) apart, so they land on the same XCD.
   const int hg = blockIdx.x / per_hg;
@@ -70,30 +73,34 @@ sparse_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
   const int t0 = split * kSplit;
   const int ntok = min(kSplit, topk - t0);
   for (int i = tid; i < kSplit; i += 256) {
-    int r = -1;
+    uint32_t r = kNoRow;
     if (i < ntok) {
       const int idx = indices[(size_t)b * topk + t0 + i];
-      if (idx >= 0 && idx < s_kv) r = idx;
+      if (idx >= 0 && idx < s_kv) r = (uint32_t)idx * kRowBytes;
       else raise_flag(err_flag, 4);
     }
     rows[i] = r;
   }
   __syncthreads();
-  const uint8_t* kvb = reinterpret_cast<const uint8_t*>(kv) + (size_t)b * s_kv * kRowBytes;
+  // the sequence's latent rows as a buffer: an absent row reads as zeros
+  const __amdgpu_buffer_rsrc_t kvr = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(kv) + (size_t)b * s_kv * kDqk, (short)0, (int)(s_kv * kRowBytes),
+      0x00020000);
   const int ntiles = (ntok + kTile - 1) / kTile;
 
   u32x4_t stage[kLoads];
   auto load_tile = [&](int ti) {
+    uint32_t off[kLoads];
 #pragma unroll
     for (int k = 0; k < kLoads; ++k) {
       const int c = tid + 256 * k;
       const int r = c / kChunksPerRow;
-      const int col = c - r * kChunksPerRow;
-      const int row = rows[ti * kTile + r];
-      u32x4_t v = {0u, 0u, 0u, 0u};
-      if (row >= 0) v = *reinterpret_cast<const u32x4_t*>(kvb + (size_t)row * kRowBytes + col * 16);
-      stage[k] = v;
+      const uint32_t o = rows[ti * kTile + r];
+      off[k] = o == kNoRow ? kNoRow : o + (uint32_t)(c - r * kChunksPerRow) * 16;
     }
+#pragma unroll
+    for (int k = 0; k < kLoads; ++k)
+      stage[k] = __builtin_amdgcn_raw_buffer_load_b128(kvr, (int)off[k], 0, 0);
   };
   auto store_tile = [&](int buf) {
 #pragma unroll
@@ -107,15 +114,25 @@ sparse_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
 
   const int head0 = hg * kHeadsPerWG + wave * kHeadsPerWave;
   const bool active = head0 < Hq;
-  // Q^T as the B operand: lane -> head head0 + col16, dims 8*grp + 32*s .. +8
-  bf16x8_t qb[kKSteps];
+  // This group's 64 query rows go to LDS (rows past Hq read as zeros); a wave
+  // reads the B operand Q^T of its 16 heads from there: lane -> head head0 +
+  // col16, dims 8*grp + 32*s .. +8.
   {
-    const int h = active ? head0 + col16 : 0;
-    const uint8_t* qp = reinterpret_cast<const uint8_t*>(q) +
-                        (((size_t)b * Hq + h) * kDqk + grp * 8) * 2;
+    const __amdgpu_buffer_rsrc_t qr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(q) + (size_t)b * Hq * kDqk, (short)0, Hq * kRowBytes, 0x00020000);
+    constexpr int kQLoads = kHeadsPerWG * kChunksPerRow / 256;  // 18
+    const int hbase = hg * kHeadsPerWG;
 #pragma unroll
-    for (int s = 0; s < kKSteps; ++s) qb[s] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(qp + s * 64));
+    for (int k = 0; k < kQLoads; ++k) {
+      const int c = tid + 256 * k;
+      const int r = c / kChunksPerRow;
+      const int col = c - r * kChunksPerRow;
+      const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(
+          qr, (int)((uint32_t)(hbase + r) * kRowBytes + col * 16), 0, 0);
+      *reinterpret_cast<u32x4_t*>(&qs[r * kPitch + col * 16]) = v;
+    }
   }
+  const uint8_t* qrow = qs + (wave * kHeadsPerWave + col16) * kPitch + grp * 16;
   f32x4_t oacc[kVBlocks * 8];
 #pragma unroll
   for (int j = 0; j < kVBlocks * 8; ++j) oacc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -132,15 +149,25 @@ sparse_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     if (it + 1 < ntiles) load_tile(it + 1);
     if (active) {
       const uint8_t* T = tile[buf];
-      f32x4_t st[2];
+      // S^T = G Q^T: the A operands of 6 k-steps of both halves are read from LDS
+      // together, then their 12 MFMAs run
+      f32x4_t st[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
+      const uint8_t* arow0 = T + col16 * kPitch + grp * 16;
+      const uint8_t* arow1 = arow0 + 16 * kPitch;
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        st[h] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        const uint8_t* arow = T + (16 * h + col16) * kPitch + grp * 16;
+      for (int s0 = 0; s0 < kKSteps; s0 += 6) {
+        u32x4_t a0[6], a1[6], qv[6];
 #pragma unroll
-        for (int s = 0; s < kKSteps; ++s) {
-          const bf16x8_t a = as_bf16x8(*reinterpret_cast<const u32x4_t*>(arow + s * 64));
-          st[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qb[s], st[h], 0, 0, 0);
+        for (int k = 0; k < 6; ++k) {
+          a0[k] = *reinterpret_cast<const u32x4_t*>(arow0 + (s0 + k) * 64);
+          a1[k] = *reinterpret_cast<const u32x4_t*>(arow1 + (s0 + k) * 64);
+          qv[k] = *reinterpret_cast<const u32x4_t*>(qrow + (s0 + k) * 64);
+        }
+#pragma unroll
+        for (int k = 0; k < 6; ++k) {
+          const bf16x8_t qk = as_bf16x8(qv[k]);
+          st[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a0[k]), qk, st[0], 0, 0, 0);
+          st[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a1[k]), qk, st[1], 0, 0, 0);
         }
       }
       // st[h][i] = score of token 16h + 4*grp + i (of this tile) for head col16
@@ -151,7 +178,7 @@ sparse_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int tok = it * kTile + 16 * h + 4 * grp + i;
-          const float v = rows[tok] >= 0 ? st[h][i] * scale_log2 : kNegInf;
+          const float v = rows[tok] != kNoRow ? st[h][i] * scale_log2 : kNegInf;
           sc[4 * h + i] = v;
           tmax = fmaxf(tmax, v);
         }
@@ -185,22 +212,28 @@ sparse_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
         pa[k] = hi;
         pl[k] = (__bf16)(p - (float)hi);
       }
-      // O += P V, four blocks of 128 dims
-#pragma unroll
-      for (int c = 0; c < kVBlocks; ++c) {
-        u32x4_t R[8];
+      // O += P V, four blocks of 128 dims; block c+1's rows are read from LDS
+      // before block c's MFMAs
+      u32x4_t R[2][8];
+      auto read_block = [&](int c, u32x4_t (&dst)[8]) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           const int trow = (i < 4) ? (4 * grp + i) : (16 + 4 * grp + (i - 4));
-          R[i] = *reinterpret_cast<const u32x4_t*>(T + trow * kPitch + (c * 128 + col16 * 8) * 2);
+          dst[i] = *reinterpret_cast<const u32x4_t*>(T + trow * kPitch + (c * 128 + col16 * 8) * 2);
         }
+      };
+      read_block(0, R[0]);
+#pragma unroll
+      for (int c = 0; c < kVBlocks; ++c) {
+        if (c + 1 < kVBlocks) read_block(c + 1, R[(c + 1) & 1]);
+        const u32x4_t (&Rc)[8] = R[c & 1];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           u32x4_t vb;
 #pragma unroll
           for (int k = 0; k < 4; ++k) {
-            const uint32_t lo = R[2 * k][j >> 1];
-            const uint32_t hi = R[2 * k + 1][j >> 1];
+            const uint32_t lo = Rc[2 * k][j >> 1];
+            const uint32_t hi = Rc[2 * k + 1][j >> 1];
             vb[k] = (j & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
           }
           const bf16x8_t vbf = as_bf16x8(vb);
