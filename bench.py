@@ -32,6 +32,40 @@ METRIC = "decode-attn µs/step and achieved HBM GB/s (% of peak); gather GB/s"
 HBM_PEAK_GBS = 8000.0
 
 
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "static_decode_step_b8_traffic.md")
+STATIC_SOURCES = ("decode_kernels.hip", "device.hpp", "launch.hpp")
+
+
+def static_sources_sha256():
+    import hashlib
+    h = hashlib.sha256()
+    for name in STATIC_SOURCES:
+        with open(os.path.join(ROOT, "decode_attention_kv_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def recorded_traffic():
+    """HBM bytes per fused step call from the committed counter summary, or None
+    when it is missing or was taken on other kernel sources than these."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            text = f.read()
+    except OSError:
+        return None
+    fields = {}
+    for raw in text.splitlines():
+        if ":" in raw and raw.strip().startswith(("kernel_sources_sha256", "traffic_bytes_per_call")):
+            k, v = raw.strip().strip("`").split(":", 1)
+            fields[k.strip()] = v.strip().strip("`")
+    if fields.get("kernel_sources_sha256") != static_sources_sha256():
+        return None
+    try:
+        return int(fields["traffic_bytes_per_call"])
+    except (KeyError, ValueError):
+        return None
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -42,6 +76,10 @@ def parse():
                     help="approximate host time spent on the oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="skip the batch-1 and gather legs")
+    ap.add_argument("--counter-pass", action="store_true",
+                    help="no timing: a 1 GiB device copy (counter calibration), then a few "
+                         "eager calls of every kernel on the benchmark inputs, for "
+                         "rocprofv3 --pmc runs")
     return ap.parse_args()
 
 
@@ -156,7 +194,7 @@ def time_steps(torch, fn, steps, warmup):
     return s.elapsed_time(e) / steps, wall
 
 
-def gather_leg(torch, dakv, workloads, acc, reps=20):
+def gather_leg(torch, dakv, workloads, acc, reps=20, counter_pass=False):
     case = workloads.gather_nd(device="cuda:0", seed=3)
     idx = case.index
     t = torch.from_numpy(idx.block_tables).to("cuda:0")
@@ -169,25 +207,43 @@ def gather_leg(torch, dakv, workloads, acc, reps=20):
     call = lambda: dakv.gather_pa_kv_cache(case.key_cache, case.value_cache, t, s, o,
                                            total_tokens=T, key_out=ko, value_out=vo,
                                            validate=False)
-    for _ in range(3):
+    if counter_pass:
         call()
-    torch.cuda.synchronize()
-    pairs = []
-    for _ in range(reps):
-        a, b = event_pair(torch)
-        a.record()
-        call()
-        b.record()
-        pairs.append((a, b))
-    torch.cuda.synchronize()
-    ms = sum(x.elapsed_time(y) for x, y in pairs) / len(pairs)
+        torch.cuda.synchronize()
+        return acc.gather_bytes(idx.lengths, 8, 128, 8, 128, 128, with_offset=True)
+    # the 247 MB read and 247 MB written fit the 256 MB last-level cache together
+    # only in part; flush it between calls so that every call reads from HBM
+    ms = time_cold(torch, call, reps)
+    warm_ms = time_call(torch, call)
     nbytes = acc.gather_bytes(idx.lengths, 8, 128, 8, 128, 128, with_offset=True)
     del case, ko, vo
     return {"workload": "gather_pa_kv_cache ND: cache [8192,128,8,128] bf16, 32 sequences "
                         "of U{1..4096} tokens, block_tables [32,64], random offsets",
             "total_tokens": T, "us_per_call": round(ms * 1e3, 2),
+            "us_per_call_back_to_back": round(warm_ms * 1e3, 2),
             "algorithmic_bytes": nbytes, "GBps": round(nbytes / (ms * 1e-3) / 1e9, 1),
             "frac_of_peak": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+
+
+def time_cold(torch, call, reps=20, warm=3):
+    """Average duration of one call with the last-level cache flushed before each:
+    a 1 GiB buffer is read (summed) in between, which leaves only clean lines of
+    that buffer in the cache, so the call neither hits its own data nor pays for
+    writing back someone else's (HIP events on the current stream)."""
+    flush = torch.zeros(1 << 28, dtype=torch.float32, device="cuda:0")
+    sink = torch.zeros((), dtype=torch.float32, device="cuda:0")
+    pairs = []
+    for r in range(warm + reps):
+        torch.sum(flush, dim=0, out=sink)
+        a, b = event_pair(torch)
+        a.record()
+        call()
+        b.record()
+        if r >= warm:
+            pairs.append((a, b))
+    torch.cuda.synchronize()
+    del flush, sink
+    return sum(x.elapsed_time(y) for x, y in pairs) / len(pairs)
 
 
 def time_call(torch, call, reps=20, warm=3):
@@ -206,7 +262,7 @@ def time_call(torch, call, reps=20, warm=3):
     return sum(x.elapsed_time(y) for x, y in pairs) / len(pairs)
 
 
-def paged_leg(torch, dakv, workloads, acc):
+def paged_leg(torch, dakv, workloads, acc, counter_pass=False):
     case = workloads.paged_gqa(device="cuda:0", seed=4)
     idx = case.index
     t = torch.from_numpy(idx.block_tables).to("cuda:0")
@@ -219,7 +275,11 @@ def paged_leg(torch, dakv, workloads, acc):
     call = lambda: dakv.decode_attn_paged(case.q, case.key_cache, case.value_cache, t, s, None,
                                           max_seq_len=max_len, scale=case.scale, out=out,
                                           workspace=ws, want_lse=False)
-    ms = time_call(torch, call)
+    if counter_pass:
+        call()
+        torch.cuda.synchronize()
+        return acc.decode_paged_bytes(idx.lengths, case.Hq, case.Hkv, case.D, 16)
+    ms = time_cold(torch, call)
     nbytes = acc.decode_paged_bytes(idx.lengths, case.Hq, case.Hkv, case.D, 16)
     del case, out, ws
     return {"workload": "paged GQA decode: batch 64, 32 query / 8 KV heads, head_dim 128, "
@@ -229,7 +289,7 @@ def paged_leg(torch, dakv, workloads, acc):
             "frac_of_peak": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
 
 
-def sparse_leg(torch, dakv, workloads, acc):
+def sparse_leg(torch, dakv, workloads, acc, counter_pass=False):
     case = workloads.sparse_mla(device="cuda:0", seed=5)
     B, Hq, d_qk = case.q.shape
     topk = case.indices.shape[1]
@@ -239,24 +299,17 @@ def sparse_leg(torch, dakv, workloads, acc):
     call = lambda: dakv.sparse_topk_decode_attn(case.q, case.kv, case.indices, d_v=case.d_v,
                                                 sm_scale=case.sm_scale, out=out, workspace=ws,
                                                 want_lse=False)
-    # the 604 MB cache exceeds the 256 MB last-level cache, but the 44 MB actually
-    # touched fits: flush it between calls by streaming a 1 GiB buffer
-    flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda:0")
-    pairs = []
-    for r in range(23):
-        flush.fill_(r & 0xFF)
-        a, b = event_pair(torch)
-        a.record()
+    if counter_pass:
         call()
-        b.record()
-        if r >= 3:
-            pairs.append((a, b))
-    torch.cuda.synchronize()
-    ms = sum(x.elapsed_time(y) for x, y in pairs) / len(pairs)
+        torch.cuda.synchronize()
+        return acc.sparse_bytes(B, Hq, d_qk, case.d_v, topk)
+    # the 604 MB cache exceeds the 256 MB last-level cache, but the 44 MB actually
+    # touched fits: flush it between calls
+    ms = time_cold(torch, call)
     warm_ms = time_call(torch, call)
     nbytes = acc.sparse_bytes(B, Hq, d_qk, case.d_v, topk)
     flops = acc.sparse_flops(B, Hq, d_qk, case.d_v, topk)
-    del case, out, ws, flush
+    del case, out, ws
     return {"workload": "top-k sparse MLA decode: batch 16, 128 heads on one latent KV, "
                         "d_qk 576 / d_v 512, context 32768, top-2048",
             "us_per_call": round(ms * 1e3, 2), "us_per_call_warm_cache": round(warm_ms * 1e3, 2),
@@ -312,6 +365,34 @@ def cpu_baseline(step, budget_s):
                       f"(append + attend, fp64 NumPy), {spent:.1f} s"}
 
 
+def counter_pass(torch, dakv, workloads, acc, B, calls=3):
+    """Launches for hardware-counter runs: a plain 1 GiB copy first (its FETCH_SIZE
+    and WRITE_SIZE give the counters' scale), then `calls` eager fused steps of the
+    batch-B benchmark step and one call of each other leg.  Prints the algorithmic
+    bytes of each launch kind."""
+    a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda:0")
+    b = torch.empty_like(a)
+    a.fill_(1)
+    torch.cuda.synchronize()
+    b.copy_(a)
+    torch.cuda.synchronize()
+    del a, b
+    torch.cuda.empty_cache()
+    step = StaticStep(B, torch, dakv, workloads, acc)
+    for _ in range(calls):
+        step.run()
+    torch.cuda.synchronize()
+    info = {"copy_bytes_each_way": 1 << 30, "static_step_call_bytes": step.attn_bytes +
+            step.append_bytes, "static_step_calls": calls * len(step.model.layers),
+            "static_grid_batch": B}
+    del step
+    torch.cuda.empty_cache()
+    for name, leg in (("gather", gather_leg), ("paged_gqa", paged_leg), ("sparse_mla", sparse_leg)):
+        info[name + "_call_bytes"] = leg(torch, dakv, workloads, acc, counter_pass=True)
+        torch.cuda.empty_cache()
+    print(json.dumps(info), flush=True)
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -331,6 +412,9 @@ def main():
     dakv.lib()
 
     B = args.batch
+    if args.counter_pass:
+        counter_pass(torch, dakv, workloads, acc, B)
+        return
     step = StaticStep(B, torch, dakv, workloads, acc)
     graph = step.capture(step.run)
     ms, wall = time_steps(torch, graph.replay, args.steps, args.warmup)
@@ -376,7 +460,8 @@ def main():
                       "merge_kernel<128>, one call per layer; per-call time from a graph of "
                       "the 32 calls (HIP events), so the merge and launch gaps are included",
             "bound": "hbm", "achieved": round(fused_gbs, 1), "peak": HBM_PEAK_GBS,
-            "unit": "GB/s", "frac": round(fused_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+            "unit": "GB/s", "frac": round(fused_gbs / HBM_PEAK_GBS, 4),
+            "traffic": recorded_traffic() if B == 8 else None,
             "bytes_per_launch": fused_bytes, "us_per_launch": round(fused_ms * 1e3, 2),
             "decode_attn_static_us_per_call": round(attn_ms * 1e3, 2),
             "kv_append_us_per_call": round(app_ms * 1e3, 2),

@@ -60,13 +60,14 @@ hipError_t launch_kv_append(void* k_cache, void* v_cache, const void* k_new, con
 // every thread issues kGatherSlots loads before its first store, consecutive
 // threads touch consecutive pieces of a row, and there is no branch per piece
 // (pieces past the end repeat the last piece; rows with a bad block id are
-// written as zeros).
+// written as zeros).  Loads and stores are non-temporal: each byte moves once.
 // ---------------------------------------------------------------------------
 constexpr int kGatherTok = 32;
 constexpr int kGatherSlots = 16;
 constexpr int kGatherLensLds = 4096;
 
 typedef uint32_t gx_u32x4 __attribute__((ext_vector_type(4)));
+
 
 __global__ void __launch_bounds__(256)
 gather_kernel(const uint8_t* __restrict__ key_cache, const uint8_t* __restrict__ value_cache,
@@ -134,7 +135,7 @@ gather_kernel(const uint8_t* __restrict__ key_cache, const uint8_t* __restrict__
                                 : value_cache + row * vb + (size_t)(pc - k_pieces) * 16;
       dst[s] = is_k ? key_out + o * kb + (size_t)pc * 16
                     : value_out + o * vb + (size_t)(pc - k_pieces) * 16;
-      const gx_u32x4 v = *reinterpret_cast<const gx_u32x4*>(src);
+      const gx_u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const gx_u32x4*>(src));
       r[s] = sr >= 0 ? v : gx_u32x4{0u, 0u, 0u, 0u};
     }
 #pragma unroll

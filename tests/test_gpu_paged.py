@@ -138,6 +138,20 @@ def test_paged_gqa_groups_match_oracle(G):
     assert_lse_close(lse, ref_lse)
 
 
+@pytest.mark.parametrize("Hq,Hkv", [(8, 8), (32, 8), (64, 8), (16, 16), (32, 16), (16, 4),
+                                     (6, 3), (24, 3), (32, 32)])
+def test_paged_head_layouts_match_oracle(Hq, Hkv):
+    """KV head counts that divide 16 (one workgroup reads whole token rows of all
+    heads) and ones that do not (one workgroup per KV head)."""
+    lengths = [1, 15, 16, 17, 100, 513, 0, 700]
+    case = workloads.paged_case(lengths, Hq=Hq, Hkv=Hkv, D=128, block_size=16, device=DEV,
+                                seed=80 + Hq + Hkv)
+    out, lse = run_paged(case)
+    ref_out, ref_lse = oracle_paged(case)
+    assert_attention_close(out, ref_out)
+    assert_lse_close(lse, ref_lse)
+
+
 @pytest.mark.parametrize("bs", [32, 64, 128])
 def test_paged_block_sizes_with_offsets(bs):
     lengths = [3 * bs + 5, bs, 1, 700]
