@@ -42,20 +42,29 @@ __device__ __forceinline__ int static_len(const int32_t* valid_len, int b, int c
   return L;
 }
 
-// Effective row count of a paged sequence: its cumulative-length difference,
-// cut at max_len and at the table's last column; inconsistencies are flagged.
+// Effective row count of a paged sequence from its cumulative lengths [start,
+// end) and table offset: the difference, cut at max_len and at the table's last
+// column (toff = the offset in blocks); *bad tells whether anything was cut.
+__device__ __forceinline__ int paged_len_of(int start, int end, int off, int block_size,
+                                            int table_cols, int max_len, int* toff, bool* bad) {
+  int L = end - start;
+  *bad = false;
+  if (L < 0) { L = 0; *bad = true; }
+  if (off < 0 || off % block_size != 0) { L = 0; *bad = true; *toff = 0; }
+  else *toff = off / block_size;
+  const int room = (table_cols - *toff) * block_size;
+  if (L > room) { L = room > 0 ? room : 0; *bad = true; }
+  if (L > max_len) { L = max_len; *bad = true; }
+  return L;
+}
+
+// The same, loading the sequence's entries; inconsistencies are flagged.
 __device__ __forceinline__ int paged_len(const int32_t* seq_lens, const int32_t* seq_offset,
                                          int b, int block_size, int table_cols, int max_len,
                                          int* toff, int32_t* err_flag, bool report) {
-  int L = seq_lens[b + 1] - seq_lens[b];
-  const int off = seq_offset ? seq_offset[b] : 0;
-  bool bad = false;
-  if (L < 0) { L = 0; bad = true; }
-  if (off < 0 || off % block_size != 0) { L = 0; bad = true; *toff = 0; }
-  else *toff = off / block_size;
-  const int room = (table_cols - *toff) * block_size;
-  if (L > room) { L = room > 0 ? room : 0; bad = true; }
-  if (L > max_len) { L = max_len; bad = true; }
+  bool bad;
+  const int L = paged_len_of(seq_lens[b], seq_lens[b + 1], seq_offset ? seq_offset[b] : 0,
+                             block_size, table_cols, max_len, toff, &bad);
   if (bad && report) raise_flag(err_flag, 8);
   return L;
 }
@@ -731,11 +740,8 @@ paged_rows_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k
 }
 
 // ------------------------------------------------------------------- merge
-// One workgroup per (sequence, query head) with more than one split.  The
-// partials' log2-sum-exps are loaded at once into LDS; then the D/4 float4
-// columns are shared among 256 / (D/4) split groups, so every thread issues its
-// few partial loads together, and the groups are summed through LDS.
-// Length modes: 0 = static (valid_len or cap), 1 = paged.
+// One workgroup per (sequence, query head); heads that fit one split return at
+// once.  Length modes: 0 = static (valid_len or cap), 1 = paged.
 template <int D>
 __global__ void __launch_bounds__(kThreads)
 merge_kernel(Workspace ws, int heads, int chunk, int max_splits, int mode,
@@ -744,18 +750,19 @@ merge_kernel(Workspace ws, int heads, int chunk, int max_splits, int mode,
              float* __restrict__ out, float* __restrict__ lse) {
   const int bh = blockIdx.x;
   const int b = bh / heads;
-  int L;
+  int L, toff;
+  bool bad;
   if (mode == 0) {
-    L = static_len(valid_len, b, cap, nullptr, false);
+    L = valid_len ? valid_len[b] : cap;
+    L = L < 0 ? 0 : (L > cap ? cap : L);
   } else {
-    int toff;
-    L = paged_len(seq_lens, seq_offset, b, block_size, table_cols, max_len, &toff, nullptr,
-                  false);
+    L = paged_len_of(seq_lens[b], seq_lens[b + 1], seq_offset ? seq_offset[b] : 0, block_size,
+                     table_cols, max_len, &toff, &bad);
   }
   const int n = L > 0 ? (L + chunk - 1) / chunk : 1;
   if (n == 1) return;  // the split kernel wrote this head's output
   merge_head<D>(ws.lse + (size_t)bh * max_splits, ws.o + (size_t)bh * max_splits * D, n,
-                       out + (size_t)bh * D, lse ? lse + bh : nullptr);
+                out + (size_t)bh * D, lse ? lse + bh : nullptr);
 }
 
 // ------------------------------------------------------------------- planning
