@@ -5,22 +5,26 @@
 // with a running max that is only moved when it grows by more than a threshold
 // ("skip scale").
 //
-// Work split: one workgroup (4 waves) per (sequence, 64 query heads, 256 indices).
-// Each wave owns 16 heads.  Per tile of 32 gathered rows:
-//   * the rows are fetched from HBM (16-byte loads, issued one tile ahead) into
-//     an LDS buffer (row pitch 1168 bytes to spread banks), double-buffered;
+// Work split: one workgroup (4 waves) per (sequence, 32 query heads, 512
+// indices); the head groups of one (sequence, index split) sit a multiple of 8
+// workgroups apart, so they run on one XCD and share its L2.  Wave w owns 16
+// heads (head block w & 1) and one half of every 64-row tile (rows 32 (w >> 1)
+// .. +32).  Per tile:
+//   * the 64 gathered rows are fetched from HBM (16-byte loads into registers,
+//     one tile ahead, in two halves) and stored to an LDS buffer (row pitch 1168
+//     bytes to spread banks), double-buffered; both head blocks read a row there;
 //   * S^T[token, head] = G Q^T with v_mfma_f32_16x16x32_bf16: A = 16 rows x 32
-//     dims and B = Q^T (the group's Q rows, staged in LDS once per split) both
-//     read from LDS, six k-steps of operands ahead of their MFMAs;
-//   * the C layout of S^T puts head (lane % 16) and 4 tokens per half-tile in each
-//     lane, which is already the A layout of P for O = P V when the 8 tokens of a
-//     lane group are taken in the order {4g..4g+3, 16+4g..16+4g+3};
+//     dims from LDS, B = Q^T of the wave's 16 heads, held in registers for the
+//     whole split (18 k-steps x 16 bytes per lane);
+//   * the C layout of S^T puts head (lane % 16) and 4 tokens per 16-row half in
+//     each lane, which is already the A layout of P for O = P V when the 8 tokens
+//     of a lane group are taken in the order {4g..4g+3, 16+4g..16+4g+3};
 //   * P enters the matrix core as bf16 hi + lo parts (two MFMAs per block);
 //   * V (the first 512 dims of the same rows) is read from LDS as 8 rows x 16
 //     bytes per lane and transposed in registers into the B operand (8 tokens of
-//     one dim per MFMA), so no transposing LDS access is needed; output column n
-//     of MFMA j is dim 8n + j of the 128-dim block.
-// Each split writes o / l and the log2-sum-exp; a merge kernel combines splits.
+//     one dim per MFMA); output column n of MFMA j is dim 8n + j of a 128-dim block.
+// At the end the two row-half waves of a head block merge through LDS, and the
+// split writes o / l and the log2-sum-exp; a merge kernel combines the splits.
 #include "device.hpp"
 #include "launch.hpp"
 
@@ -34,17 +38,22 @@ constexpr int kDqk = 576;
 constexpr int kDv = 512;
 constexpr int kRowBytes = kDqk * 2;                     // 1152
 constexpr int kPitch = kRowBytes + 16;                  // LDS row pitch
-constexpr int kTile = 32;                               // gathered rows per tile
-constexpr int kSplit = 256;                             // indices per workgroup
+constexpr int kTile = 64;                               // gathered rows per tile
+constexpr int kHalf = kTile / 2;                        // rows of a tile one wave takes
+constexpr int kSplit = 512;                             // indices per workgroup
+constexpr int kTiles = kSplit / kTile;                  // 8
 constexpr int kHeadsPerWave = 16;
-constexpr int kHeadsPerWG = 64;
+constexpr int kHeadsPerWG = 32;
 constexpr int kChunksPerRow = kRowBytes / 16;           // 72
-constexpr int kLoads = kTile * kChunksPerRow / 256;     // 9 per thread per tile
+constexpr int kLoads = kTile * kChunksPerRow / 256;     // 18 per thread per tile
+static_assert(kTile * 4 == 256 && kLoads * 4 == kChunksPerRow, "4 threads per tile row");
 constexpr int kKSteps = kDqk / 32;                      // 18
 constexpr int kVBlocks = kDv / 128;                     // 4
 // The page's rescale threshold is 6 in natural-log units; scores here are in log2.
 constexpr float kRescale = 6.0f * kLog2e;
 constexpr uint32_t kNoRow = 0x80000000u;  // a buffer offset past any sequence: loads 0
+static_assert(kTile * kChunksPerRow % 256 == 0, "whole loads per thread");
+static_assert(kSplit % kTile == 0, "whole tiles per split");
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(const u32x4_t& v) {
   return __builtin_bit_cast(bf16x8_t, v);
@@ -56,10 +65,7 @@ sparse_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
                     float scale_log2, int n_hg, int n_splits, int per_hg,
                     float* __restrict__ ws_o, float* __restrict__ ws_lse, int32_t* err_flag) {
   __shared__ __attribute__((aligned(16))) uint8_t tile[2][kTile * kPitch];
-  __shared__ __attribute__((aligned(16))) uint8_t qs[kHeadsPerWG * kPitch];  // this group's Q rows
   __shared__ uint32_t rows[kSplit];  // byte offset of each index's row in kv[b], or kNoRow
-  // blockIdx -> (head group, unit); units of the same (b, split) in different head
-  // groups are per_hg (a multiple of 8) apart, so they land on the same XCD.
   const int hg = blockIdx.x / per_hg;
   const int u = blockIdx.x - hg * per_hg;
   if (u >= B * n_splits) return;
@@ -68,10 +74,25 @@ sparse_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
+  const int hb = wave & 1;     // head block of the group
+  const int th = wave >> 1;    // row half of every tile
   const int grp = lane >> 4;   // lane group 0..3
   const int col16 = lane & 15;
+  const int head0 = hg * kHeadsPerWG + hb * kHeadsPerWave;
+  const bool active = head0 < Hq;
   const int t0 = split * kSplit;
   const int ntok = min(kSplit, topk - t0);
+  // Q^T of the wave's heads as B operands: lane -> head head0 + col16, dims
+  // 32 s + 8 grp .. +8 (heads past Hq read as zeros).
+  u32x4_t qreg[kKSteps];
+  {
+    const __amdgpu_buffer_rsrc_t qr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(q) + (size_t)b * Hq * kDqk, (short)0, Hq * kRowBytes, 0x00020000);
+    const uint32_t base = (uint32_t)(head0 + col16) * kRowBytes + grp * 16;
+#pragma unroll
+    for (int s = 0; s < kKSteps; ++s)
+      qreg[s] = __builtin_amdgcn_raw_buffer_load_b128(qr, (int)(base + s * 64), 0, 0);
+  }
   for (int i = tid; i < kSplit; i += 256) {
     uint32_t r = kNoRow;
     if (i < ntok) {
@@ -88,96 +109,86 @@ sparse_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
       0x00020000);
   const int ntiles = (ntok + kTile - 1) / kTile;
 
-  u32x4_t stage[kLoads];
-  auto load_tile = [&](int ti) {
-    uint32_t off[kLoads];
+  // Register staging of the gathered rows, in two halves of kLoads / 2 loads per
+  // thread: while tile it is computed from one LDS buffer, the first half of tile
+  // it + 1 is in flight during the scores and goes to the other buffer after them,
+  // and the second half is in flight during O += P V and goes there after it.  The
+  // tile loop is fully unrolled (straight-line code), so each LDS store waits for
+  // exactly its own loads; tiles past the split's end load kNoRow offsets (zeros,
+  // no memory traffic).
+  // Thread t copies row t / 4 of a tile: 16-byte pieces (t % 4) + 4 k, k < 18,
+  // i.e. 64 contiguous bytes per row per load instruction across 4 lanes.
+  constexpr int kHalfLoads = kLoads / 2;
+  const int my_row = tid >> 2;
+  const uint32_t my_piece = (uint32_t)(tid & 3) * 16;
+  uint8_t* const lds_dst = &tile[0][my_row * kPitch + my_piece];
+  constexpr int kBufBytes = kTile * kPitch;
+  u32x4_t stage[kHalfLoads];
+  auto load_half = [&](int ti, int part) {
+    const uint32_t o = rows[ti * kTile + my_row];
+    const uint32_t base = o == kNoRow ? kNoRow : o + my_piece;
 #pragma unroll
-    for (int k = 0; k < kLoads; ++k) {
-      const int c = tid + 256 * k;
-      const int r = c / kChunksPerRow;
-      const uint32_t o = rows[ti * kTile + r];
-      off[k] = o == kNoRow ? kNoRow : o + (uint32_t)(c - r * kChunksPerRow) * 16;
+    for (int k = 0; k < kHalfLoads; ++k) {
+      const int kk = part * kHalfLoads + k;
+      // past the resource (kNoRow) the load returns zeros with no memory traffic
+      stage[k] = __builtin_amdgcn_raw_buffer_load_b128(kvr, (int)(base + (o == kNoRow ? 0u : kk * 64u)), 0, 0);
     }
-#pragma unroll
-    for (int k = 0; k < kLoads; ++k)
-      stage[k] = __builtin_amdgcn_raw_buffer_load_b128(kvr, (int)off[k], 0, 0);
   };
-  auto store_tile = [&](int buf) {
+  auto store_half = [&](int buf, int part) {
 #pragma unroll
-    for (int k = 0; k < kLoads; ++k) {
-      const int c = tid + 256 * k;
-      const int r = c / kChunksPerRow;
-      const int col = c - r * kChunksPerRow;
-      *reinterpret_cast<u32x4_t*>(&tile[buf][r * kPitch + col * 16]) = stage[k];
+    for (int k = 0; k < kHalfLoads; ++k) {
+      const int kk = part * kHalfLoads + k;
+      *reinterpret_cast<u32x4_t*>(lds_dst + buf * kBufBytes + kk * 64) = stage[k];
     }
   };
 
-  const int head0 = hg * kHeadsPerWG + wave * kHeadsPerWave;
-  const bool active = head0 < Hq;
-  // This group's 64 query rows go to LDS (rows past Hq read as zeros); a wave
-  // reads the B operand Q^T of its 16 heads from there: lane -> head head0 +
-  // col16, dims 8*grp + 32*s .. +8.
-  {
-    const __amdgpu_buffer_rsrc_t qr = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t*>(q) + (size_t)b * Hq * kDqk, (short)0, Hq * kRowBytes, 0x00020000);
-    constexpr int kQLoads = kHeadsPerWG * kChunksPerRow / 256;  // 18
-    const int hbase = hg * kHeadsPerWG;
-#pragma unroll
-    for (int k = 0; k < kQLoads; ++k) {
-      const int c = tid + 256 * k;
-      const int r = c / kChunksPerRow;
-      const int col = c - r * kChunksPerRow;
-      const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(
-          qr, (int)((uint32_t)(hbase + r) * kRowBytes + col * 16), 0, 0);
-      *reinterpret_cast<u32x4_t*>(&qs[r * kPitch + col * 16]) = v;
-    }
-  }
-  const uint8_t* qrow = qs + (wave * kHeadsPerWave + col16) * kPitch + grp * 16;
   f32x4_t oacc[kVBlocks * 8];
 #pragma unroll
   for (int j = 0; j < kVBlocks * 8; ++j) oacc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   float m_ref = kNegInf;  // running max used for the exponentials, head head0 + col16
   float lsum = 0.f;       // this lane's share of the sum of exponentials
 
-  if (ntiles > 0) {
-    load_tile(0);
-    store_tile(0);
-  }
+  load_half(0, 0);
+  store_half(0, 0);
+  load_half(0, 1);
+  store_half(0, 1);
   __syncthreads();
-  for (int it = 0; it < ntiles; ++it) {
+#pragma unroll
+  for (int it = 0; it < kTiles; ++it) {
     const int buf = it & 1;
-    if (it + 1 < ntiles) load_tile(it + 1);
-    if (active) {
-      const uint8_t* T = tile[buf];
-      // S^T = G Q^T: the A operands of 6 k-steps of both halves are read from LDS
-      // together, then their 12 MFMAs run
+    const bool next = it + 1 < kTiles;
+    if (next) load_half(it + 1, 0);
+    if (active && it < ntiles) {
+      const uint8_t* T = tile[buf] + th * kHalf * kPitch;
+      // S^T = G Q^T: the A operands of kBatch k-steps of both 16-row halves are
+      // read from LDS together, then their 2 kBatch MFMAs run
+      constexpr int kBatch = 3;
       f32x4_t st[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
       const uint8_t* arow0 = T + col16 * kPitch + grp * 16;
       const uint8_t* arow1 = arow0 + 16 * kPitch;
 #pragma unroll
-      for (int s0 = 0; s0 < kKSteps; s0 += 6) {
-        u32x4_t a0[6], a1[6], qv[6];
+      for (int s0 = 0; s0 < kKSteps; s0 += kBatch) {
+        u32x4_t a0[kBatch], a1[kBatch];
 #pragma unroll
-        for (int k = 0; k < 6; ++k) {
+        for (int k = 0; k < kBatch; ++k) {
           a0[k] = *reinterpret_cast<const u32x4_t*>(arow0 + (s0 + k) * 64);
           a1[k] = *reinterpret_cast<const u32x4_t*>(arow1 + (s0 + k) * 64);
-          qv[k] = *reinterpret_cast<const u32x4_t*>(qrow + (s0 + k) * 64);
         }
 #pragma unroll
-        for (int k = 0; k < 6; ++k) {
-          const bf16x8_t qk = as_bf16x8(qv[k]);
+        for (int k = 0; k < kBatch; ++k) {
+          const bf16x8_t qk = as_bf16x8(qreg[s0 + k]);
           st[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a0[k]), qk, st[0], 0, 0, 0);
           st[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a1[k]), qk, st[1], 0, 0, 0);
         }
       }
-      // st[h][i] = score of token 16h + 4*grp + i (of this tile) for head col16
+      // st[h][i] = score of row 16h + 4*grp + i (of this wave's half) for head col16
       float sc[8];
       float tmax = kNegInf;
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int tok = it * kTile + 16 * h + 4 * grp + i;
+          const int tok = it * kTile + th * kHalf + 16 * h + 4 * grp + i;
           const float v = rows[tok] != kNoRow ? st[h][i] * scale_log2 : kNegInf;
           sc[4 * h + i] = v;
           tmax = fmaxf(tmax, v);
@@ -200,6 +211,10 @@ sparse_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
         }
       }
       const float mu = m_ref == kNegInf ? 0.f : m_ref;
+      if (next) {
+        store_half(buf ^ 1, 0);
+        load_half(it + 1, 1);
+      }
       // P as two bf16 parts (p = hi + lo to about 16 significant bits): rounding
       // P to one bf16 alone can put the output off by more than 2e-3 when a few
       // rows dominate the softmax.
@@ -212,21 +227,15 @@ sparse_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
         pa[k] = hi;
         pl[k] = (__bf16)(p - (float)hi);
       }
-      // O += P V, four blocks of 128 dims; block c+1's rows are read from LDS
-      // before block c's MFMAs
-      u32x4_t R[2][8];
-      auto read_block = [&](int c, u32x4_t (&dst)[8]) {
+      // O += P V, four blocks of 128 dims
+#pragma unroll
+      for (int c = 0; c < kVBlocks; ++c) {
+        u32x4_t Rc[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           const int trow = (i < 4) ? (4 * grp + i) : (16 + 4 * grp + (i - 4));
-          dst[i] = *reinterpret_cast<const u32x4_t*>(T + trow * kPitch + (c * 128 + col16 * 8) * 2);
+          Rc[i] = *reinterpret_cast<const u32x4_t*>(T + trow * kPitch + (c * 128 + col16 * 8) * 2);
         }
-      };
-      read_block(0, R[0]);
-#pragma unroll
-      for (int c = 0; c < kVBlocks; ++c) {
-        if (c + 1 < kVBlocks) read_block(c + 1, R[(c + 1) & 1]);
-        const u32x4_t (&Rc)[8] = R[c & 1];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           u32x4_t vb;
@@ -241,12 +250,18 @@ sparse_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
           oacc[c * 8 + j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl, vbf, oacc[c * 8 + j], 0, 0, 0);
         }
       }
+    } else if (next) {
+      store_half(buf ^ 1, 0);
+      load_half(it + 1, 1);
     }
-    if (it + 1 < ntiles) store_tile(buf ^ 1);
-    __syncthreads();
+    if (next) {
+      store_half(buf ^ 1, 1);
+      __syncthreads();
+    }
   }
 
-  // Epilogue: per head, total of the exponentials over the 4 lane groups.
+  // Epilogue.  Per head (lane group g holds heads 4g + i of the block): the
+  // wave's max and total of the exponentials.
   lsum += __shfl_xor(lsum, 16);
   lsum += __shfl_xor(lsum, 32);
   float lh[4], mh[4];
@@ -255,58 +270,105 @@ sparse_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     lh[i] = __shfl(lsum, 4 * grp + i);
     mh[i] = __shfl(m_ref, 4 * grp + i);
   }
-  if (!active) return;
+  // The row-half-1 wave of each head block hands its state to the row-half-0
+  // wave through LDS (tile buffer 0, free once every wave is past the last tile).
+  constexpr int kXfer = kVBlocks * 8 * 64 * 4 + 64 * 8;  // floats per head block
+  static_assert(2 * kXfer * 4 <= kTile * kPitch, "hand-over fits one tile buffer");
+  float* xf = reinterpret_cast<float*>(tile[0]) + hb * kXfer;
+  __syncthreads();
+  if (th == 1) {
+#pragma unroll
+    for (int j = 0; j < kVBlocks * 8; ++j)
+      *reinterpret_cast<f32x4_t*>(xf + (j * 64 + lane) * 4) = oacc[j];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      xf[kVBlocks * 8 * 256 + lane * 8 + i] = mh[i];
+      xf[kVBlocks * 8 * 256 + lane * 8 + 4 + i] = lh[i];
+    }
+  }
+  __syncthreads();
+  if (th == 1 || !active) return;
+  float wa[4], wb[4], inv[4], lse2[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float mb = xf[kVBlocks * 8 * 256 + lane * 8 + i];
+    const float lb = xf[kVBlocks * 8 * 256 + lane * 8 + 4 + i];
+    const float M = fmaxf(mh[i], mb);
+    if (M == kNegInf) {
+      wa[i] = wb[i] = inv[i] = 0.f;
+      lse2[i] = kNegInf;
+    } else {
+      wa[i] = exp2_fast(mh[i] - M);
+      wb[i] = exp2_fast(mb - M);
+      const float l = lh[i] * wa[i] + lb * wb[i];
+      inv[i] = 1.f / l;
+      lse2[i] = M + __log2f(l);
+    }
+  }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int head = head0 + 4 * grp + i;
     const size_t unit = ((size_t)b * Hq + head) * n_splits + split;
     float* dst = ws_o + unit * kDv + col16 * 8;
-    const bool empty = mh[i] == kNegInf;
-    const float inv = empty ? 0.f : 1.f / lh[i];
+    float o[kVBlocks * 8];
+#pragma unroll
+    for (int j = 0; j < kVBlocks * 8; ++j)
+      o[j] = (oacc[j][i] * wa[i] + xf[(j * 64 + lane) * 4 + i] * wb[i]) * inv[i];
 #pragma unroll
     for (int c = 0; c < kVBlocks; ++c) {
-      float4 lo4, hi4;
-      lo4.x = oacc[c * 8 + 0][i] * inv; lo4.y = oacc[c * 8 + 1][i] * inv;
-      lo4.z = oacc[c * 8 + 2][i] * inv; lo4.w = oacc[c * 8 + 3][i] * inv;
-      hi4.x = oacc[c * 8 + 4][i] * inv; hi4.y = oacc[c * 8 + 5][i] * inv;
-      hi4.z = oacc[c * 8 + 6][i] * inv; hi4.w = oacc[c * 8 + 7][i] * inv;
-      *reinterpret_cast<float4*>(dst + c * 128) = lo4;
-      *reinterpret_cast<float4*>(dst + c * 128 + 4) = hi4;
+      *reinterpret_cast<float4*>(dst + c * 128) =
+          make_float4(o[c * 8 + 0], o[c * 8 + 1], o[c * 8 + 2], o[c * 8 + 3]);
+      *reinterpret_cast<float4*>(dst + c * 128 + 4) =
+          make_float4(o[c * 8 + 4], o[c * 8 + 5], o[c * 8 + 6], o[c * 8 + 7]);
     }
-    if (col16 == 0) ws_lse[unit] = empty ? kNegInf : mh[i] + __log2f(lh[i]);
+    if (col16 == 0) ws_lse[unit] = lse2[i];
   }
 }
 
-// Combine the splits of one (sequence, head): weights 2^(lse_j - max).
+// Combine the splits of one (sequence, head): weights 2^(lse_j - max).  Splits
+// are taken 8 at a time with all 8 loads of a thread issued before their use.
+constexpr int kMergeBatch = 8;
+static_assert(kDv == 2 * 256, "two columns per thread");
+
 __global__ void __launch_bounds__(256)
 sparse_merge_kernel(const float* __restrict__ ws_o, const float* __restrict__ ws_lse,
                     int n_splits, float* __restrict__ out, float* __restrict__ lse) {
   const int bh = blockIdx.x;
   const float* lp = ws_lse + (size_t)bh * n_splits;
+  const float* op = ws_o + (size_t)bh * n_splits * kDv;
   float M = kNegInf;
-  for (int j = 0; j < n_splits; ++j) M = fmaxf(M, lp[j]);
-  for (int d = threadIdx.x; d < kDv; d += 256) {
-    if (M == kNegInf) {
-      out[(size_t)bh * kDv + d] = 0.f;
-      continue;
-    }
-    float num = 0.f, den = 0.f;
-    for (int j = 0; j < n_splits; ++j) {
-      const float w = exp2_fast(lp[j] - M);
-      num += w * ws_o[((size_t)bh * n_splits + j) * kDv + d];
-      den += w;
-    }
-    out[(size_t)bh * kDv + d] = num / den;
+  for (int j0 = 0; j0 < n_splits; j0 += kMergeBatch) {
+    float x[kMergeBatch];
+#pragma unroll
+    for (int k = 0; k < kMergeBatch; ++k) x[k] = j0 + k < n_splits ? lp[j0 + k] : kNegInf;
+#pragma unroll
+    for (int k = 0; k < kMergeBatch; ++k) M = fmaxf(M, x[k]);
   }
-  if (lse && threadIdx.x == 0) {
-    if (M == kNegInf) {
-      lse[bh] = kNegInf;
-    } else {
-      float den = 0.f;
-      for (int j = 0; j < n_splits; ++j) den += exp2_fast(lp[j] - M);
-      lse[bh] = (M + __log2f(den)) * kLn2;
+  const int d0 = threadIdx.x * 2;  // two adjacent columns per thread
+  float num0 = 0.f, num1 = 0.f, den = 0.f;
+  if (M != kNegInf) {
+    for (int j0 = 0; j0 < n_splits; j0 += kMergeBatch) {
+      float w[kMergeBatch];
+      float2 v[kMergeBatch];
+#pragma unroll
+      for (int k = 0; k < kMergeBatch; ++k) {
+        const bool in = j0 + k < n_splits;
+        w[k] = in ? lp[j0 + k] : kNegInf;
+        v[k] = in ? *reinterpret_cast<const float2*>(op + (size_t)(j0 + k) * kDv + d0)
+                  : make_float2(0.f, 0.f);
+      }
+#pragma unroll
+      for (int k = 0; k < kMergeBatch; ++k) {
+        const float wk = exp2_fast(w[k] - M);
+        num0 += wk * v[k].x;
+        num1 += wk * v[k].y;
+        den += wk;
+      }
     }
   }
+  const float inv = M == kNegInf ? 0.f : 1.f / den;
+  *reinterpret_cast<float2*>(out + (size_t)bh * kDv + d0) = make_float2(num0 * inv, num1 * inv);
+  if (lse && threadIdx.x == 0) lse[bh] = M == kNegInf ? kNegInf : (M + __log2f(den)) * kLn2;
 }
 
 static int sparse_splits(int topk) { return (topk + kSplit - 1) / kSplit; }
