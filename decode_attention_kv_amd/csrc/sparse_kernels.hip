@@ -8,21 +8,25 @@
 // Work split: one workgroup (4 waves) per (sequence, 32 query heads, 512
 // indices); the head groups of one (sequence, index split) sit a multiple of 8
 // workgroups apart, so they run on one XCD and share its L2.  Wave w owns 16
-// heads (head block w & 1) and one half of every 64-row tile (rows 32 (w >> 1)
-// .. +32).  Per tile:
-//   * the 64 gathered rows are fetched from HBM (16-byte loads into registers,
-//     one tile ahead, in two halves) and stored to an LDS buffer (row pitch 1168
-//     bytes to spread banks), double-buffered; both head blocks read a row there;
+// heads (head block w & 1) and one 32-row half (w >> 1) of every 64-row tile.
+//   * Rows are gathered by direct-to-LDS buffer loads (16 bytes per lane, no
+//     registers) into two tile buffers: tile it + 1 is in flight while tile it is
+//     computed; one barrier per tile.  A tile is 64 unpadded 1152-byte rows; the
+//     16-byte pieces of row r are stored in a permuted order (XOR of the piece's
+//     low 3 bits with a function of r) so that both LDS read patterns below hit
+//     16 distinct bank groups.
 //   * S^T[token, head] = G Q^T with v_mfma_f32_16x16x32_bf16: A = 16 rows x 32
-//     dims from LDS, B = Q^T of the wave's 16 heads, held in registers for the
-//     whole split (18 k-steps x 16 bytes per lane);
-//   * the C layout of S^T puts head (lane % 16) and 4 tokens per 16-row half in
-//     each lane, which is already the A layout of P for O = P V when the 8 tokens
-//     of a lane group are taken in the order {4g..4g+3, 16+4g..16+4g+3};
-//   * P enters the matrix core as bf16 hi + lo parts (two MFMAs per block);
-//   * V (the first 512 dims of the same rows) is read from LDS as 8 rows x 16
-//     bytes per lane and transposed in registers into the B operand (8 tokens of
-//     one dim per MFMA); output column n of MFMA j is dim 8n + j of a 128-dim block.
+//     dims from LDS (read a batch of k-steps ahead), B = Q^T of the wave's 16
+//     heads, held in registers for the whole split (18 k-steps x 16 bytes per
+//     lane); four accumulation chains (two 16-row halves x even/odd k-steps).
+//   * The C layout of S^T (lane: head lane % 16, tokens 4 (lane / 16) + i of
+//     each half) is the A layout of P for O = P V when the 8 tokens of a lane
+//     group are taken in the order {4g..4g+3, 16+4g..16+4g+3}; P enters the
+//     matrix core as bf16 hi + lo parts (two MFMAs per block).
+//   * The B operand of P V (8 rows of one dim per lane) comes straight from LDS
+//     with two transposing reads ds_read_b64_tr_b16: lane j of a 16-lane group
+//     points at row 4 (group) + j / 4 (+16), dims 4 (j % 4) .. +3 of a 16-dim
+//     block, and lane i receives dim i of that block for the 4 rows.
 // At the end the two row-half waves of a head block merge through LDS, and the
 // split writes o / l and the log2-sum-exp; a merge kernel combines the splits.
 #include "device.hpp"
@@ -31,31 +35,48 @@
 namespace dakv {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4;
 
 constexpr int kDqk = 576;
 constexpr int kDv = 512;
 constexpr int kRowBytes = kDqk * 2;                     // 1152
-constexpr int kPitch = kRowBytes + 16;                  // LDS row pitch
+constexpr int kPieces = kRowBytes / 16;                 // 72 pieces of 16 bytes
 constexpr int kTile = 64;                               // gathered rows per tile
 constexpr int kHalf = kTile / 2;                        // rows of a tile one wave takes
+constexpr int kTileBytes = kTile * kRowBytes;           // 73728
 constexpr int kSplit = 512;                             // indices per workgroup
 constexpr int kTiles = kSplit / kTile;                  // 8
 constexpr int kHeadsPerWave = 16;
 constexpr int kHeadsPerWG = 32;
-constexpr int kChunksPerRow = kRowBytes / 16;           // 72
-constexpr int kLoads = kTile * kChunksPerRow / 256;     // 18 per thread per tile
-static_assert(kTile * 4 == 256 && kLoads * 4 == kChunksPerRow, "4 threads per tile row");
+constexpr int kDmaPerWave = kTileBytes / 1024 / 4;      // 18 wave loads of 1 KiB per tile
 constexpr int kKSteps = kDqk / 32;                      // 18
-constexpr int kVBlocks = kDv / 128;                     // 4
+constexpr int kDimBlocks = kDv / 16;                    // 32 output blocks of 16 dims
 // The page's rescale threshold is 6 in natural-log units; scores here are in log2.
 constexpr float kRescale = 6.0f * kLog2e;
 constexpr uint32_t kNoRow = 0x80000000u;  // a buffer offset past any sequence: loads 0
-static_assert(kTile * kChunksPerRow % 256 == 0, "whole loads per thread");
+static_assert(kTileBytes % 4096 == 0, "whole 1 KiB wave loads per wave");
+static_assert(kPieces % 8 == 0, "pieces permute within groups of 8");
 static_assert(kSplit % kTile == 0, "whole tiles per split");
 
+// Position of piece p of row r inside the row (an involution: it also maps a
+// position back to its piece).
+__device__ __forceinline__ int piece_slot(int p, int r) {
+  const int k = (r >> 1) & 7;
+  const int x = ((k << 1) & 7) | (k >> 2);
+  return (p & ~7) | ((p & 7) ^ x);
+}
+
 __device__ __forceinline__ bf16x8_t as_bf16x8(const u32x4_t& v) {
+  return __builtin_bit_cast(bf16x8_t, v);
+}
+
+__device__ __forceinline__ bf16x8_t join_bf16x4(const i16x4_t& lo, const i16x4_t& hi) {
+  typedef short i16x8_t __attribute__((ext_vector_type(8)));
+  const i16x8_t v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   return __builtin_bit_cast(bf16x8_t, v);
 }
 
@@ -64,8 +85,10 @@ sparse_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
                     const int32_t* __restrict__ indices, int B, int Hq, int s_kv, int topk,
                     float scale_log2, int n_hg, int n_splits, int per_hg,
                     float* __restrict__ ws_o, float* __restrict__ ws_lse, int32_t* err_flag) {
-  __shared__ __attribute__((aligned(16))) uint8_t tile[2][kTile * kPitch];
+  __shared__ __attribute__((aligned(1024))) uint8_t buf0[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t buf1[kTileBytes];
   __shared__ uint32_t rows[kSplit];  // byte offset of each index's row in kv[b], or kNoRow
+  uint8_t* const ring[2] = {buf0, buf1};
   const int hg = blockIdx.x / per_hg;
   const int u = blockIdx.x - hg * per_hg;
   if (u >= B * n_splits) return;
@@ -109,79 +132,90 @@ sparse_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
       0x00020000);
   const int ntiles = (ntok + kTile - 1) / kTile;
 
-  // Register staging of the gathered rows, in two halves of kLoads / 2 loads per
-  // thread: while tile it is computed from one LDS buffer, the first half of tile
-  // it + 1 is in flight during the scores and goes to the other buffer after them,
-  // and the second half is in flight during O += P V and goes there after it.  The
-  // tile loop is fully unrolled (straight-line code), so each LDS store waits for
-  // exactly its own loads; tiles past the split's end load kNoRow offsets (zeros,
-  // no memory traffic).
-  // Thread t copies row t / 4 of a tile: 16-byte pieces (t % 4) + 4 k, k < 18,
-  // i.e. 64 contiguous bytes per row per load instruction across 4 lanes.
-  constexpr int kHalfLoads = kLoads / 2;
-  const int my_row = tid >> 2;
-  const uint32_t my_piece = (uint32_t)(tid & 3) * 16;
-  uint8_t* const lds_dst = &tile[0][my_row * kPitch + my_piece];
-  constexpr int kBufBytes = kTile * kPitch;
-  u32x4_t stage[kHalfLoads];
-  auto load_half = [&](int ti, int part) {
-    const uint32_t o = rows[ti * kTile + my_row];
-    const uint32_t base = o == kNoRow ? kNoRow : o + my_piece;
+  // Tile ti into a buffer: wave load I (this wave's I = 18 wave + k) fills bytes
+  // [1024 I, 1024 I + 1024) of the tile, lane L the 16 bytes at 1024 I + 16 L,
+  // i.e. position c = 64 I + L = 72 r + s of row r, which holds piece
+  // piece_slot(s, r).  Tiles past the split's end load kNoRow offsets (zeros).
+  auto fetch_tile = [&](int ti, uint8_t* dst) {
+    uint32_t off[kDmaPerWave];
 #pragma unroll
-    for (int k = 0; k < kHalfLoads; ++k) {
-      const int kk = part * kHalfLoads + k;
-      // past the resource (kNoRow) the load returns zeros with no memory traffic
-      stage[k] = __builtin_amdgcn_raw_buffer_load_b128(kvr, (int)(base + (o == kNoRow ? 0u : kk * 64u)), 0, 0);
+    for (int k = 0; k < kDmaPerWave; ++k) {
+      const int I = wave * kDmaPerWave + k;
+      const int c = I * 64 + lane;
+      const int r = c / kPieces;
+      const int p = piece_slot(c - r * kPieces, r);
+      const uint32_t o = rows[ti * kTile + r];
+      off[k] = o == kNoRow ? kNoRow : o + (uint32_t)p * 16;
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int k = 0; k < kDmaPerWave; ++k) {
+      const int I = wave * kDmaPerWave + k;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(kvr, (lds_void*)(dst + I * 1024), 16, (int)off[k],
+                                               0, 0, 0);
     }
   };
-  auto store_half = [&](int buf, int part) {
-#pragma unroll
-    for (int k = 0; k < kHalfLoads; ++k) {
-      const int kk = part * kHalfLoads + k;
-      *reinterpret_cast<u32x4_t*>(lds_dst + buf * kBufBytes + kk * 64) = stage[k];
-    }
-  };
+  fetch_tile(0, buf0);
 
-  f32x4_t oacc[kVBlocks * 8];
+  f32x4_t oacc[kDimBlocks];
 #pragma unroll
-  for (int j = 0; j < kVBlocks * 8; ++j) oacc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < kDimBlocks; ++j) oacc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   float m_ref = kNegInf;  // running max used for the exponentials, head head0 + col16
   float lsum = 0.f;       // this lane's share of the sum of exponentials
 
-  load_half(0, 0);
-  store_half(0, 0);
-  load_half(0, 1);
-  store_half(0, 1);
-  __syncthreads();
+  // A operand of k-step s, half h: row 32 th + 16 h + col16, piece 4 s + grp.
+  const int arow0 = th * kHalf + col16;
+  const int arow1 = arow0 + 16;
+  // transposing reads of 16-dim block jb: rows 32 th + 4 grp + col16 / 4 (+16),
+  // dims 16 jb + 4 (col16 % 4) .. +3: piece 2 jb + (col16 % 4) / 2, byte
+  // 8 (col16 & 1) of it.
+  const int vrow0 = th * kHalf + 4 * grp + (col16 >> 2);
+  const int vrow1 = vrow0 + 16;
+  const int vsub = (col16 & 3) >> 1;
+  const int vhalf = (col16 & 1) * 8;
+
 #pragma unroll
   for (int it = 0; it < kTiles; ++it) {
-    const int buf = it & 1;
-    const bool next = it + 1 < kTiles;
-    if (next) load_half(it + 1, 0);
+    // this wave's loads of tile it are complete (none later is in flight yet);
+    // the barrier makes every wave's part visible and ends every wave's reads of
+    // tile it - 1, whose buffer the next fetch refills
+    __builtin_amdgcn_s_waitcnt((0 & 15) | (7 << 4) | (15 << 8));  // vmcnt(0) only
+    __builtin_amdgcn_s_barrier();
+    if (it + 1 < kTiles) fetch_tile(it + 1, ring[(it + 1) & 1]);
     if (active && it < ntiles) {
-      const uint8_t* T = tile[buf] + th * kHalf * kPitch;
-      // S^T = G Q^T: the A operands of kBatch k-steps of both 16-row halves are
-      // read from LDS together, then their 2 kBatch MFMAs run
-      constexpr int kBatch = 3;
-      f32x4_t st[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
-      const uint8_t* arow0 = T + col16 * kPitch + grp * 16;
-      const uint8_t* arow1 = arow0 + 16 * kPitch;
+      const uint8_t* T = ring[it & 1];
+      // S^T = G Q^T over 18 k-steps: chains (half, k-step parity); A operands
+      // read from LDS a batch of 3 k-steps ahead (scheduling barriers keep it so)
+      f32x4_t st[2][2];
 #pragma unroll
-      for (int s0 = 0; s0 < kKSteps; s0 += kBatch) {
-        u32x4_t a0[kBatch], a1[kBatch];
+      for (int h = 0; h < 2; ++h) st[h][0] = st[h][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      const uint8_t* ap0 = T + arow0 * kRowBytes;
+      const uint8_t* ap1 = T + arow1 * kRowBytes;
+      constexpr int kBatch = 3;
+      u32x4_t a[2][kBatch][2];
+      auto read_a = [&](int s0, u32x4_t (&dst)[kBatch][2]) {
 #pragma unroll
         for (int k = 0; k < kBatch; ++k) {
-          a0[k] = *reinterpret_cast<const u32x4_t*>(arow0 + (s0 + k) * 64);
-          a1[k] = *reinterpret_cast<const u32x4_t*>(arow1 + (s0 + k) * 64);
+          dst[k][0] = *reinterpret_cast<const u32x4_t*>(ap0 + piece_slot(4 * (s0 + k) + grp, arow0) * 16);
+          dst[k][1] = *reinterpret_cast<const u32x4_t*>(ap1 + piece_slot(4 * (s0 + k) + grp, arow1) * 16);
         }
+      };
+      read_a(0, a[0]);
+#pragma unroll
+      for (int s0 = 0; s0 < kKSteps; s0 += kBatch) {
+        const int cur = (s0 / kBatch) & 1;
+        if (s0 + kBatch < kKSteps) read_a(s0 + kBatch, a[cur ^ 1]);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int k = 0; k < kBatch; ++k) {
           const bf16x8_t qk = as_bf16x8(qreg[s0 + k]);
-          st[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a0[k]), qk, st[0], 0, 0, 0);
-          st[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a1[k]), qk, st[1], 0, 0, 0);
+          const int par = (s0 + k) & 1;
+          st[0][par] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[cur][k][0]), qk, st[0][par], 0, 0, 0);
+          st[1][par] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[cur][k][1]), qk, st[1][par], 0, 0, 0);
         }
+        __builtin_amdgcn_sched_barrier(0);
       }
-      // st[h][i] = score of row 16h + 4*grp + i (of this wave's half) for head col16
+      // score of row 32 th + 16 h + 4 grp + i of the tile for head col16
       float sc[8];
       float tmax = kNegInf;
 #pragma unroll
@@ -189,7 +223,7 @@ sparse_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int tok = it * kTile + th * kHalf + 16 * h + 4 * grp + i;
-          const float v = rows[tok] != kNoRow ? st[h][i] * scale_log2 : kNegInf;
+          const float v = rows[tok] != kNoRow ? (st[h][0][i] + st[h][1][i]) * scale_log2 : kNegInf;
           sc[4 * h + i] = v;
           tmax = fmaxf(tmax, v);
         }
@@ -205,16 +239,12 @@ sparse_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
 #pragma unroll
         for (int i = 0; i < 4; ++i) a4[i] = __shfl(alpha, 4 * grp + i);
 #pragma unroll
-        for (int j = 0; j < kVBlocks * 8; ++j) {
+        for (int j = 0; j < kDimBlocks; ++j) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) oacc[j][i] *= a4[i];
         }
       }
       const float mu = m_ref == kNegInf ? 0.f : m_ref;
-      if (next) {
-        store_half(buf ^ 1, 0);
-        load_half(it + 1, 1);
-      }
       // P as two bf16 parts (p = hi + lo to about 16 significant bits): rounding
       // P to one bf16 alone can put the output off by more than 2e-3 when a few
       // rows dominate the softmax.
@@ -227,36 +257,40 @@ sparse_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
         pa[k] = hi;
         pl[k] = (__bf16)(p - (float)hi);
       }
-      // O += P V, four blocks of 128 dims
+      // O += P V, 32 blocks of 16 dims; the B operands (two transposing reads
+      // each) in batches of 4 blocks, the next batch read before this one's MFMAs
+      const uint8_t* vp0 = T + vrow0 * kRowBytes + vhalf;
+      const uint8_t* vp1 = T + vrow1 * kRowBytes + vhalf;
+      constexpr int kVB = 4;
+      i16x4_t vb[2][kVB][2];
+      auto read_v = [&](int j0, i16x4_t (&dst)[kVB][2]) {
 #pragma unroll
-      for (int c = 0; c < kVBlocks; ++c) {
-        u32x4_t Rc[8];
+        for (int k = 0; k < kVB; ++k) {
+          const int piece = 2 * (j0 + k) + vsub;
+          dst[k][0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_i16x4*)(vp0 + piece_slot(piece, vrow0) * 16));
+          dst[k][1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_i16x4*)(vp1 + piece_slot(piece, vrow1) * 16));
+        }
+      };
+      read_v(0, vb[0]);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const int trow = (i < 4) ? (4 * grp + i) : (16 + 4 * grp + (i - 4));
-          Rc[i] = *reinterpret_cast<const u32x4_t*>(T + trow * kPitch + (c * 128 + col16 * 8) * 2);
+      for (int j0 = 0; j0 < kDimBlocks; j0 += kVB) {
+        const int cur = (j0 / kVB) & 1;
+        if (j0 + kVB < kDimBlocks) read_v(j0 + kVB, vb[cur ^ 1]);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int k = 0; k < kVB; ++k) {
+          const bf16x8_t v = join_bf16x4(vb[cur][k][0], vb[cur][k][1]);
+          oacc[j0 + k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, v, oacc[j0 + k], 0, 0, 0);
         }
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          u32x4_t vb;
-#pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            const uint32_t lo = Rc[2 * k][j >> 1];
-            const uint32_t hi = Rc[2 * k + 1][j >> 1];
-            vb[k] = (j & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
-          }
-          const bf16x8_t vbf = as_bf16x8(vb);
-          oacc[c * 8 + j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, vbf, oacc[c * 8 + j], 0, 0, 0);
-          oacc[c * 8 + j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl, vbf, oacc[c * 8 + j], 0, 0, 0);
+        for (int k = 0; k < kVB; ++k) {
+          const bf16x8_t v = join_bf16x4(vb[cur][k][0], vb[cur][k][1]);
+          oacc[j0 + k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl, v, oacc[j0 + k], 0, 0, 0);
         }
+        __builtin_amdgcn_sched_barrier(0);
       }
-    } else if (next) {
-      store_half(buf ^ 1, 0);
-      load_half(it + 1, 1);
-    }
-    if (next) {
-      store_half(buf ^ 1, 1);
-      __syncthreads();
     }
   }
 
@@ -271,19 +305,20 @@ sparse_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     mh[i] = __shfl(m_ref, 4 * grp + i);
   }
   // The row-half-1 wave of each head block hands its state to the row-half-0
-  // wave through LDS (tile buffer 0, free once every wave is past the last tile).
-  constexpr int kXfer = kVBlocks * 8 * 64 * 4 + 64 * 8;  // floats per head block
-  static_assert(2 * kXfer * 4 <= kTile * kPitch, "hand-over fits one tile buffer");
-  float* xf = reinterpret_cast<float*>(tile[0]) + hb * kXfer;
+  // wave through LDS (buffer hb of the ring, free once every wave is past the
+  // last tile).
+  constexpr int kXfer = kDimBlocks * 64 * 4 + 64 * 8;  // floats per head block
+  static_assert(kXfer * 4 <= kTileBytes, "hand-over fits one tile buffer");
+  float* xf = reinterpret_cast<float*>(hb ? buf1 : buf0);
   __syncthreads();
   if (th == 1) {
 #pragma unroll
-    for (int j = 0; j < kVBlocks * 8; ++j)
+    for (int j = 0; j < kDimBlocks; ++j)
       *reinterpret_cast<f32x4_t*>(xf + (j * 64 + lane) * 4) = oacc[j];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      xf[kVBlocks * 8 * 256 + lane * 8 + i] = mh[i];
-      xf[kVBlocks * 8 * 256 + lane * 8 + 4 + i] = lh[i];
+      xf[kDimBlocks * 256 + lane * 8 + i] = mh[i];
+      xf[kDimBlocks * 256 + lane * 8 + 4 + i] = lh[i];
     }
   }
   __syncthreads();
@@ -291,8 +326,8 @@ sparse_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
   float wa[4], wb[4], inv[4], lse2[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const float mb = xf[kVBlocks * 8 * 256 + lane * 8 + i];
-    const float lb = xf[kVBlocks * 8 * 256 + lane * 8 + 4 + i];
+    const float mb = xf[kDimBlocks * 256 + lane * 8 + i];
+    const float lb = xf[kDimBlocks * 256 + lane * 8 + 4 + i];
     const float M = fmaxf(mh[i], mb);
     if (M == kNegInf) {
       wa[i] = wb[i] = inv[i] = 0.f;
@@ -309,18 +344,10 @@ sparse_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
   for (int i = 0; i < 4; ++i) {
     const int head = head0 + 4 * grp + i;
     const size_t unit = ((size_t)b * Hq + head) * n_splits + split;
-    float* dst = ws_o + unit * kDv + col16 * 8;
-    float o[kVBlocks * 8];
+    float* dst = ws_o + unit * kDv + col16;
 #pragma unroll
-    for (int j = 0; j < kVBlocks * 8; ++j)
-      o[j] = (oacc[j][i] * wa[i] + xf[(j * 64 + lane) * 4 + i] * wb[i]) * inv[i];
-#pragma unroll
-    for (int c = 0; c < kVBlocks; ++c) {
-      *reinterpret_cast<float4*>(dst + c * 128) =
-          make_float4(o[c * 8 + 0], o[c * 8 + 1], o[c * 8 + 2], o[c * 8 + 3]);
-      *reinterpret_cast<float4*>(dst + c * 128 + 4) =
-          make_float4(o[c * 8 + 4], o[c * 8 + 5], o[c * 8 + 6], o[c * 8 + 7]);
-    }
+    for (int j = 0; j < kDimBlocks; ++j)
+      dst[j * 16] = (oacc[j][i] * wa[i] + xf[(j * 64 + lane) * 4 + i] * wb[i]) * inv[i];
     if (col16 == 0) ws_lse[unit] = lse2[i];
   }
 }
