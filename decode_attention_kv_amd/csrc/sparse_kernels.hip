@@ -105,17 +105,6 @@ sparse_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
   const bool active = head0 < Hq;
   const int t0 = split * kSplit;
   const int ntok = min(kSplit, topk - t0);
-  // Q^T of the wave's heads as B operands: lane -> head head0 + col16, dims
-  // 32 s + 8 grp .. +8 (heads past Hq read as zeros).
-  u32x4_t qreg[kKSteps];
-  {
-    const __amdgpu_buffer_rsrc_t qr = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t*>(q) + (size_t)b * Hq * kDqk, (short)0, Hq * kRowBytes, 0x00020000);
-    const uint32_t base = (uint32_t)(head0 + col16) * kRowBytes + grp * 16;
-#pragma unroll
-    for (int s = 0; s < kKSteps; ++s)
-      qreg[s] = __builtin_amdgcn_raw_buffer_load_b128(qr, (int)(base + s * 64), 0, 0);
-  }
   for (int i = tid; i < kSplit; i += 256) {
     uint32_t r = kNoRow;
     if (i < ntok) {
@@ -156,6 +145,18 @@ sparse_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     }
   };
   fetch_tile(0, buf0);
+  // Q^T of the wave's heads as B operands, loaded while tile 0 is in flight:
+  // lane -> head head0 + col16, dims 32 s + 8 grp .. +8 (heads past Hq read as
+  // zeros).
+  u32x4_t qreg[kKSteps];
+  {
+    const __amdgpu_buffer_rsrc_t qr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(q) + (size_t)b * Hq * kDqk, (short)0, Hq * kRowBytes, 0x00020000);
+    const uint32_t base = (uint32_t)(head0 + col16) * kRowBytes + grp * 16;
+#pragma unroll
+    for (int s = 0; s < kKSteps; ++s)
+      qreg[s] = __builtin_amdgcn_raw_buffer_load_b128(qr, (int)(base + s * 64), 0, 0);
+  }
 
   f32x4_t oacc[kDimBlocks];
 #pragma unroll
@@ -173,6 +174,20 @@ sparse_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
   const int vrow1 = vrow0 + 16;
   const int vsub = (col16 & 3) >> 1;
   const int vhalf = (col16 & 1) * 8;
+  // Byte offsets within a row of the pieces these lanes read: the permutation
+  // only moves a piece inside its group of 8 (128 bytes), so k-step s reads at
+  // 128 (s / 2) + aoff[h][s % 2] and dim block jb at 128 (jb / 4) + voff[r][jb % 4].
+  int aoff[2][2], voff[2][4];
+#pragma unroll
+  for (int par = 0; par < 2; ++par) {
+    aoff[0][par] = piece_slot(4 * par + grp, arow0) * 16;
+    aoff[1][par] = piece_slot(4 * par + grp, arow1) * 16;
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    voff[0][j] = piece_slot(2 * j + vsub, vrow0) * 16 + vhalf;
+    voff[1][j] = piece_slot(2 * j + vsub, vrow1) * 16 + vhalf;
+  }
 
 #pragma unroll
   for (int it = 0; it < kTiles; ++it) {
@@ -189,6 +204,7 @@ sparse_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
       f32x4_t st[2][2];
 #pragma unroll
       for (int h = 0; h < 2; ++h) st[h][0] = st[h][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      // piece 4 s + grp of a row sits at 128 (s / 2) + aoff[h][s % 2]
       const uint8_t* ap0 = T + arow0 * kRowBytes;
       const uint8_t* ap1 = T + arow1 * kRowBytes;
       constexpr int kBatch = 3;
@@ -196,8 +212,9 @@ sparse_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
       auto read_a = [&](int s0, u32x4_t (&dst)[kBatch][2]) {
 #pragma unroll
         for (int k = 0; k < kBatch; ++k) {
-          dst[k][0] = *reinterpret_cast<const u32x4_t*>(ap0 + piece_slot(4 * (s0 + k) + grp, arow0) * 16);
-          dst[k][1] = *reinterpret_cast<const u32x4_t*>(ap1 + piece_slot(4 * (s0 + k) + grp, arow1) * 16);
+          const int s = s0 + k;
+          dst[k][0] = *reinterpret_cast<const u32x4_t*>(ap0 + aoff[0][s & 1] + 128 * (s >> 1));
+          dst[k][1] = *reinterpret_cast<const u32x4_t*>(ap1 + aoff[1][s & 1] + 128 * (s >> 1));
         }
       };
       read_a(0, a[0]);
@@ -238,10 +255,13 @@ sparse_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
         float a4[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) a4[i] = __shfl(alpha, 4 * grp + i);
+        // a few accumulators at a time (they live in AGPRs; the barriers keep the
+        // scheduler from moving them all to VGPRs at once)
 #pragma unroll
         for (int j = 0; j < kDimBlocks; ++j) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) oacc[j][i] *= a4[i];
+          if ((j & 3) == 3) __builtin_amdgcn_sched_barrier(0);
         }
       }
       const float mu = m_ref == kNegInf ? 0.f : m_ref;
@@ -259,18 +279,19 @@ sparse_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
       }
       // O += P V, 32 blocks of 16 dims; the B operands (two transposing reads
       // each) in batches of 4 blocks, the next batch read before this one's MFMAs
-      const uint8_t* vp0 = T + vrow0 * kRowBytes + vhalf;
-      const uint8_t* vp1 = T + vrow1 * kRowBytes + vhalf;
+      // piece 2 jb + vsub of a row sits at 128 (jb / 4) + voff[r][jb % 4]
+      const uint8_t* vp0 = T + vrow0 * kRowBytes;
+      const uint8_t* vp1 = T + vrow1 * kRowBytes;
       constexpr int kVB = 4;
       i16x4_t vb[2][kVB][2];
       auto read_v = [&](int j0, i16x4_t (&dst)[kVB][2]) {
 #pragma unroll
         for (int k = 0; k < kVB; ++k) {
-          const int piece = 2 * (j0 + k) + vsub;
+          const int jb = j0 + k;
           dst[k][0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_i16x4*)(vp0 + piece_slot(piece, vrow0) * 16));
+              (lds_i16x4*)(vp0 + voff[0][jb & 3] + 128 * (jb >> 2)));
           dst[k][1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_i16x4*)(vp1 + piece_slot(piece, vrow1) * 16));
+              (lds_i16x4*)(vp1 + voff[1][jb & 3] + 128 * (jb >> 2)));
         }
       };
       read_v(0, vb[0]);
