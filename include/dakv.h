@@ -218,8 +218,9 @@ size_t dakv_sparse_topk_decode_attn_workspace_size(int B, int Hq, int d_qk, int 
  *   S = softmax(sm_scale * q[b] G^T)  [Hq, topk]
  *   out[b] = S G[:, :d_v]             [Hq, d_v]
  * [FlashMLA] "Mathematical formulation"; "Course of computation": blocks of
- * the index list, online softmax with running max and sum-exp, S rounded to
- * bf16 before S.V.
+ * the index list, online softmax with running max and sum-exp (the page rounds
+ * S to bf16 before S.V; here S enters as a bf16 high part plus a bf16 low part,
+ * which keeps the result within the stated tolerance).
  *
  *   q        bf16 [B, Hq, d_qk];  kv bf16 [B, s_kv, d_qk];  indices int32 [B, topk]
  *   out      fp32 [B, Hq, d_v];   lse fp32 [B, Hq] or NULL (natural log of the

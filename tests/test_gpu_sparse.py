@@ -34,6 +34,8 @@ def ref(case, rows=None):
     (2, 64, 5000, 512),
     (2, 128, 4096, 2048),   # the config's heads and top-k at a smaller context
     (3, 32, 64, 1),         # a single index
+    (2, 32, 3000, 1000),    # two index splits, the second ragged
+    (2, 16, 100, 0),        # no index: zero output, lse -inf
 ])
 def test_sparse_matches_oracle(B, Hq, s_kv, topk):
     print(f"sparse B={B} Hq={Hq} s_kv={s_kv} topk={topk}", flush=True)
