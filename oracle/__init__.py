@@ -12,7 +12,9 @@ float64, with no tiling, no splitting and no online softmax:
   head_dim]``, its 0/1 attention mask, append-at-write-position and masked
   scaled-dot-product decode attention (OpenVINO NPU LLM article, Part 1
   "Solution: preallocation + attention mask"; Part 2 KV-cache update;
-  "Attention on the NPU" -> "incremental SDPA").
+  "Attention on the NPU" -> "incremental SDPA"), and the prefill -> generate
+  copy of the cache and its roll-back (Part 2 generate flow; deployment features
+  and "Current limitations").
 * ``paged``         -- paged KV cache addressed through block tables: host
   validation, the ``gather_pa_kv_cache`` mapping, and paged GQA decode attention
   (PyPTO GatherPaKvCache article, section 3 "tensor contract and data
@@ -30,7 +32,7 @@ library-routine special cases or brute force; none is "parity unpinned".
 """
 
 from .bf16 import widen, round_to_bf16_bits
-from .static_cache import kv_append, decode_static
+from .static_cache import kv_append, decode_static, copy_kvcache, trim_kvcache
 from .paged import (
     PagedIndexError,
     validate_paged,
@@ -45,6 +47,8 @@ __all__ = [
     "round_to_bf16_bits",
     "kv_append",
     "decode_static",
+    "copy_kvcache",
+    "trim_kvcache",
     "PagedIndexError",
     "validate_paged",
     "gather_pa_kv_cache",

@@ -129,3 +129,71 @@ def decode_static(q, k_cache, v_cache, mask=None, valid_len=None, scale=None):
             s = scale * (K @ q[b, h])
             out[b, h], lse[b, h] = softmax_weighted_sum(s, V)
     return out, lse
+
+
+def copy_kvcache(src, dst, lengths, mask=None):
+    """Prefill -> generate hand-over of the KV cache.
+
+    The prefill model's present K/V tensors have capacity S_src (the page: 1024),
+    the generate model's past tensors capacity S_dst (1152); for every layer's K and
+    V, the valid rows [0, len_b) of sequence b are copied from present to past at the
+    same rows (Part 2, step 3 of the generate flow: a slice per tensor, 32 layers x 2
+    tensors copied in parallel; "Current limitations": the copy is 512 MB at 7B with
+    1024 rows).  Rows of past at and after len_b keep their contents.
+
+    src, dst : lists of equal length; src[i] uint16 bits ``[B, H, S_src, D]``,
+               dst[i] uint16 bits ``[B, H, S_dst, D]``
+    lengths  : ints ``[B]`` in ``[0, min(S_src, S_dst)]``
+    mask     : int ``[B, S_dst]`` or None; when given it becomes 1 for the copied
+               rows and 0 for the rest (the stored-row count is len_b)
+
+    Returns ``(new dst list, new mask)``; inputs are not modified.
+    """
+    if len(src) != len(dst):
+        raise ValueError("src and dst must list the same number of tensors")
+    lengths = np.asarray(lengths).reshape(-1)
+    out = []
+    for s, d in zip(src, dst):
+        s = np.asarray(s)
+        d = np.array(d, copy=True)
+        B, H, S_src, D = s.shape
+        if d.shape[:2] != (B, H) or d.shape[3] != D:
+            raise ValueError("src and dst differ in batch, heads or head_dim")
+        S_dst = d.shape[2]
+        if lengths.shape != (B,):
+            raise ValueError("lengths must be [B]")
+        for b in range(B):
+            n = int(lengths[b])
+            if n < 0 or n > min(S_src, S_dst):
+                raise ValueError(f"length {n} outside [0, {min(S_src, S_dst)}]")
+            d[b, :, :n, :] = s[b, :, :n, :]
+        out.append(d)
+    if mask is not None:
+        mask = np.array(mask, copy=True)
+        if mask.shape[0] != lengths.shape[0]:
+            raise ValueError("mask must be [B, S_dst]")
+        for b in range(mask.shape[0]):
+            mask[b, :] = 0
+            mask[b, :int(lengths[b])] = 1
+    return out, mask
+
+
+def trim_kvcache(mask, new_len):
+    """Roll the stored rows of each sequence back to ``new_len[b]``.
+
+    The page's speculative-decoding support cuts the cache back to the last accepted
+    position (``trim_kvcache_for_speculative_decoding``, NPUW deployment features);
+    with the 0/1 mask that means rows at and after new_len[b] stop counting.  Earlier
+    entries are unchanged and the row contents are left as they are (the mask hides
+    them).  new_len[b] must lie in [0, S].
+    """
+    mask = np.array(mask, copy=True)
+    new_len = np.asarray(new_len).reshape(-1)
+    if new_len.shape != (mask.shape[0],):
+        raise ValueError("new_len must be [B]")
+    for b in range(mask.shape[0]):
+        n = int(new_len[b])
+        if n < 0 or n > mask.shape[1]:
+            raise ValueError(f"length {n} outside [0, {mask.shape[1]}]")
+        mask[b, n:] = 0
+    return mask

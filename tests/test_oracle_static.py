@@ -277,3 +277,101 @@ def test_valid_length_outside_capacity_is_rejected():
         oracle.decode_static(np.zeros((1, 1, 2)), K, K, valid_len=[5])
     with pytest.raises(ValueError):
         oracle.decode_static(np.zeros((1, 1, 2)), K, K)
+
+
+# ------------------------------------------- prefill -> generate copy and trim
+
+
+def _prefill_generate(rng, B, H, D, S_src, S_dst, lengths, n_tensors=2):
+    src = [random_bf16(rng, (B, H, S_src, D)) for _ in range(n_tensors)]
+    # the generate buffers start with garbage, NaN and Inf in every row
+    dst = [random_bf16(rng, (B, H, S_dst, D), std=100.0) for _ in range(n_tensors)]
+    for d in dst:
+        d[:, :, ::7] = 0x7FC0   # NaN
+        d[:, :, 3::11] = 0x7F80  # +Inf
+    return src, dst
+
+
+def test_copy_then_masked_attention_equals_attention_over_the_prompt(golden_dir):
+    """The page's hand-over: prefill capacity 1024, generate capacity 1152, a prompt of
+    4 tokens copied to rows [0:4]; the generate model then attends exactly the
+    prompt rows (mask with 4 ones), whatever its buffer held before."""
+    g = json.load(open(os.path.join(golden_dir, "mask_progression.json")))
+    S_dst = g["capacity"]
+    S_src = g["max_prompt_len"]
+    rng = np.random.default_rng(30)
+    B, H, D = 2, 2, 8
+    lengths = [g["prompt_tokens"], 37]
+    src, dst = _prefill_generate(rng, B, H, D, S_src, S_dst, lengths)
+    mask0 = np.ones((B, S_dst), dtype=np.int32)
+    new_dst, mask = oracle.copy_kvcache(src, dst, lengths, mask0)
+    assert mask.sum(axis=1).tolist() == lengths
+    q = rng.standard_normal((B, H, D))
+    got, got_lse = oracle.decode_static(q, new_dst[0], new_dst[1], mask=mask)
+    want, want_lse = oracle.decode_static(q, src[0], src[1], valid_len=lengths)
+    assert np.array_equal(got, want) and np.array_equal(got_lse, want_lse)
+    # rows at and after the length keep what the generate buffer held
+    for d_old, d_new in zip(dst, new_dst):
+        for b, n in enumerate(lengths):
+            assert np.array_equal(d_new[b, :, n:], d_old[b, :, n:])
+
+
+def test_copy_pairs_tensors_in_order_and_zero_length_copies_nothing():
+    rng = np.random.default_rng(31)
+    src, dst = _prefill_generate(rng, 1, 1, 8, 16, 20, [16], n_tensors=3)
+    new_dst, _ = oracle.copy_kvcache(src, dst, [16])
+    q = rng.standard_normal((1, 1, 8))
+    for i in range(3):
+        # tensor i of the generate model now answers like tensor i of the prefill model
+        a, _ = oracle.decode_static(q, new_dst[i], new_dst[(i + 1) % 3], valid_len=[16])
+        b, _ = oracle.decode_static(q, src[i], src[(i + 1) % 3], valid_len=[16])
+        assert np.array_equal(a, b)
+    same, _ = oracle.copy_kvcache(src, dst, [0])
+    assert all(np.array_equal(x, y) for x, y in zip(same, dst))
+
+
+def test_copy_then_generate_continues_the_printed_progression(golden_dir):
+    """After the copy of a 4-token prompt, appends give 5, 6, ... valid rows (the page's
+    4 -> 5 -> ... progression continues from the copied state)."""
+    g = json.load(open(os.path.join(golden_dir, "mask_progression.json")))
+    S_dst, S_src, P = g["capacity"], g["max_prompt_len"], g["prompt_tokens"]
+    rng = np.random.default_rng(32)
+    H, D = 1, 4
+    src, dst = _prefill_generate(rng, 1, H, D, S_src, S_dst, [P])
+    (K, V), mask = oracle.copy_kvcache(src, dst, [P], np.zeros((1, S_dst), dtype=np.int32))
+    printed = {p["generated_token"]: p["valid_rows"] for p in g["points"]}
+    for n in range(2, 12):
+        K, V, mask = oracle.kv_append(K, V, random_bf16(rng, (1, H, D)),
+                                      random_bf16(rng, (1, H, D)), [int(mask.sum())], mask)
+        if n in printed:
+            assert int(mask.sum()) == printed[n]
+        assert int(mask.sum()) == n + 3
+
+
+def test_trim_equals_attention_over_the_kept_rows():
+    rng = np.random.default_rng(33)
+    B, H, D, S = 2, 2, 8, 40
+    K = random_bf16(rng, (B, H, S, D))
+    V = random_bf16(rng, (B, H, S, D))
+    mask = np.zeros((B, S), dtype=np.int32)
+    mask[0, :30] = 1
+    mask[1, :12] = 1
+    trimmed = oracle.trim_kvcache(mask, [25, 12])
+    q = rng.standard_normal((B, H, D))
+    got, _ = oracle.decode_static(q, K, V, mask=trimmed)
+    want, _ = oracle.decode_static(q, K, V, valid_len=[25, 12])
+    assert np.array_equal(got, want)
+    empty = oracle.trim_kvcache(mask, [0, 0])
+    out, lse = oracle.decode_static(q, K, V, mask=empty)
+    assert np.all(out == 0) and np.all(np.isneginf(lse))
+
+
+def test_copy_and_trim_reject_lengths_outside_the_buffers():
+    rng = np.random.default_rng(34)
+    src, dst = _prefill_generate(rng, 1, 1, 8, 16, 20, [16])
+    with pytest.raises(ValueError):
+        oracle.copy_kvcache(src, dst, [17])
+    with pytest.raises(ValueError):
+        oracle.copy_kvcache(src, dst, [-1])
+    with pytest.raises(ValueError):
+        oracle.trim_kvcache(np.ones((1, 20), dtype=np.int32), [21])
