@@ -225,6 +225,34 @@ def gather_leg(torch, dakv, workloads, acc, reps=20, counter_pass=False):
             "frac_of_peak": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
 
 
+def copy_leg(torch, dakv, acc, counter_pass=False):
+    """The page's 7B prefill -> generate hand-over: 32 layers x K and V = 64 tensors
+    [1, 32, 1024] copied into [1, 32, 1152] buffers, 1024 rows each (512 MiB)."""
+    g = torch.Generator(device="cuda:0")
+    g.manual_seed(8)
+    src = [torch.randn((1, 32, 1024, 128), generator=g, device="cuda:0").to(torch.bfloat16)
+           for _ in range(64)]
+    dst = [torch.zeros((1, 32, 1152, 128), dtype=torch.bfloat16, device="cuda:0")
+           for _ in range(64)]
+    lens = torch.tensor([1024], dtype=torch.int32, device="cuda:0")
+    mask = torch.zeros((1, 1152), dtype=torch.int32, device="cuda:0")
+    call = lambda: dakv.copy_kvcache(src, dst, lens, mask=mask)
+    moved = acc.copy_kvcache_bytes(32, 32, 1024, 128)
+    nbytes = 2 * moved + 4 + 1152 * 4
+    if counter_pass:
+        call()
+        torch.cuda.synchronize()
+        del src, dst
+        return nbytes
+    ms = time_cold(torch, call)
+    del src, dst
+    return {"workload": "copy_kvcache: 64 tensors [1, 32, 1024 -> 1152, 128] bf16, 1024 rows "
+                        "(512 MiB read, 512 MiB written) + mask",
+            "us_per_call": round(ms * 1e3, 2), "algorithmic_bytes": nbytes,
+            "GBps": round(nbytes / (ms * 1e-3) / 1e9, 1),
+            "frac_of_peak": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+
+
 def time_cold(torch, call, reps=20, warm=3):
     """Average duration of one call with the last-level cache flushed before each:
     a 1 GiB buffer is read (summed) in between, which leaves only clean lines of
@@ -390,6 +418,7 @@ def counter_pass(torch, dakv, workloads, acc, B, calls=3):
     for name, leg in (("gather", gather_leg), ("paged_gqa", paged_leg), ("sparse_mla", sparse_leg)):
         info[name + "_call_bytes"] = leg(torch, dakv, workloads, acc, counter_pass=True)
         torch.cuda.empty_cache()
+    info["copy_kvcache_call_bytes"] = copy_leg(torch, dakv, acc, counter_pass=True)
     print(json.dumps(info), flush=True)
 
 
@@ -492,6 +521,8 @@ def main():
         line["paged_gqa"] = paged_leg(torch, dakv, workloads, acc)
         torch.cuda.empty_cache()
         line["sparse_mla"] = sparse_leg(torch, dakv, workloads, acc)
+        torch.cuda.empty_cache()
+        line["copy_kvcache"] = copy_leg(torch, dakv, acc)
     print(json.dumps(line), flush=True)
 
 

@@ -7,6 +7,8 @@ CPU fallback: loading fails loudly when the library has not been built.
 
 from .ops import (
     kv_append,
+    copy_kvcache,
+    trim_kvcache,
     decode_attn_static,
     decode_attn_static_workspace_size,
     decode_step_static,
@@ -23,6 +25,8 @@ from ._lib import DakvError, lib, strerror
 
 __all__ = [
     "kv_append",
+    "copy_kvcache",
+    "trim_kvcache",
     "decode_attn_static",
     "decode_attn_static_workspace_size",
     "decode_step_static",

@@ -21,6 +21,8 @@ ERR_WRITE_POS = 2
 ERR_SPARSE_INDEX = 4
 ERR_SEQ_LENS = 8
 ERR_VALID_LEN = 16
+ERR_COPY_LEN = 32
+COPY_MAX_TENSORS = 128
 
 _vp = ctypes.c_void_p
 _i = ctypes.c_int
@@ -31,6 +33,8 @@ _sz = ctypes.c_size_t
 SIGNATURES = {
     "dakv_strerror": (ctypes.c_char_p, [_i]),
     "dakv_kv_append": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp, _vp]),
+    "dakv_copy_kvcache": (_i, [_vp, _vp, _i, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp]),
+    "dakv_trim_kvcache": (_i, [_vp, _vp, _i, _i, _vp, _vp]),
     "dakv_decode_attn_static_workspace_size": (_sz, [_i, _i, _i, _i]),
     "dakv_decode_attn_static": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _vp, _vp,
                                      _vp, _sz, _i, _vp, _vp]),

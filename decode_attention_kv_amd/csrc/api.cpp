@@ -48,6 +48,32 @@ int dakv_kv_append(void* k_cache, void* v_cache, const void* k_new, const void* 
                                          cap, D, err_flag, as_stream(stream)));
 }
 
+// --------------------------------------------------------------- copy_kvcache
+int dakv_copy_kvcache(const void* const* src, void* const* dst, int n, int B, int H,
+                      int src_cap, int dst_cap, int D, const int32_t* lengths, int32_t* mask,
+                      int32_t* err_flag, void* stream) {
+  static_assert(dakv::kCopyMaxTensors == DAKV_COPY_MAX_TENSORS, "header and library agree");
+  if (n < 1 || n > DAKV_COPY_MAX_TENSORS || B < 0 || H < 0 || src_cap <= 0 || dst_cap <= 0 ||
+      D <= 0)
+    return DAKV_EINVAL;
+  if (B == 0) return DAKV_OK;
+  if ((D * 2) % 16 != 0) return DAKV_ENOTSUP;
+  if (!src || !dst || !lengths) return DAKV_EINVAL;
+  for (int i = 0; i < n; ++i)
+    if (!src[i] || !dst[i] || !aligned16(src[i]) || !aligned16(dst[i])) return DAKV_EINVAL;
+  if (H == 0 && !mask) return DAKV_OK;
+  return from_hip(dakv::launch_copy_kvcache(src, dst, n, B, H, src_cap, dst_cap, D, lengths, mask,
+                                            err_flag, as_stream(stream)));
+}
+
+int dakv_trim_kvcache(int32_t* mask, const int32_t* new_len, int B, int cap, int32_t* err_flag,
+                      void* stream) {
+  if (B < 0 || cap <= 0) return DAKV_EINVAL;
+  if (B == 0) return DAKV_OK;
+  if (!mask || !new_len) return DAKV_EINVAL;
+  return from_hip(dakv::launch_trim_kvcache(mask, new_len, B, cap, err_flag, as_stream(stream)));
+}
+
 // --------------------------------------------------------- decode_attn_static
 size_t dakv_decode_attn_static_workspace_size(int B, int H, int cap, int D) {
   if (B <= 0 || H <= 0 || cap <= 0 || D <= 0) return 0;

@@ -7,6 +7,8 @@
 
 namespace dakv {
 
+typedef uint32_t gx_u32x4 __attribute__((ext_vector_type(4)));
+
 // ---------------------------------------------------------------------------
 // kv_append: the new token's K and V rows go to row write_pos[b] of every head
 // (the NPU runtime's cache update writes just this row and bumps the counter).
@@ -51,6 +53,114 @@ hipError_t launch_kv_append(void* k_cache, void* v_cache, const void* k_new, con
 }
 
 // ---------------------------------------------------------------------------
+// copy_kvcache: the prefill model's valid rows [0, len_b) of every (tensor,
+// sequence, head) go to the same rows of the generate model's buffer.  For one
+// (tensor, sequence, head) those rows are len_b * row_bytes contiguous bytes in
+// both buffers (only the capacity strides differ), so the work is a batch of
+// contiguous copies; a workgroup moves one kCopyBytes chunk of one of them with
+// all of its loads issued before the first store (non-temporal both ways).
+// Grid: n * B * H * chunks, chunk fastest; chunks past the copied length exit.
+// ---------------------------------------------------------------------------
+constexpr int kCopyLoads = 8;                        // 16-byte loads per thread
+constexpr int kCopyBytes = 256 * kCopyLoads * 16;    // 32 KiB per workgroup
+
+struct CopyTable {
+  const uint8_t* src[kCopyMaxTensors];
+  uint8_t* dst[kCopyMaxTensors];
+};
+
+__device__ __forceinline__ int copy_len(const int32_t* lengths, int b, int lim, int32_t* err_flag,
+                                        bool report) {
+  int L = lengths[b];
+  if (L < 0 || L > lim) {
+    if (report) raise_flag(err_flag, 32);
+    L = L < 0 ? 0 : lim;
+  }
+  return L;
+}
+
+__global__ void __launch_bounds__(256)
+copy_kvcache_kernel(CopyTable t, int BH, int H, int src_cap, int dst_cap, int row_bytes,
+                    int chunks, const int32_t* __restrict__ lengths, int32_t* err_flag) {
+  const int c = blockIdx.x % chunks;
+  const int rest = blockIdx.x / chunks;
+  const int bh = rest % BH;
+  const int i = rest / BH;
+  const int b = bh / H;
+  const int lim = min(src_cap, dst_cap);
+  const int L = copy_len(lengths, b, lim, err_flag,
+                         i == 0 && bh - b * H == 0 && c == 0 && threadIdx.x == 0);
+  const size_t bytes = (size_t)L * row_bytes;
+  const size_t start = (size_t)c * kCopyBytes;
+  if (start >= bytes) return;
+  const int n16 = (int)(min((size_t)kCopyBytes, bytes - start) / 16);
+  const uint8_t* src = t.src[i] + (size_t)bh * src_cap * row_bytes + start;
+  uint8_t* dst = t.dst[i] + (size_t)bh * dst_cap * row_bytes + start;
+  gx_u32x4 v[kCopyLoads];
+#pragma unroll
+  for (int k = 0; k < kCopyLoads; ++k) {
+    const int j = min((int)threadIdx.x + 256 * k, n16 - 1);
+    v[k] = __builtin_nontemporal_load(reinterpret_cast<const gx_u32x4*>(src) + j);
+  }
+#pragma unroll
+  for (int k = 0; k < kCopyLoads; ++k) {
+    const int j = (int)threadIdx.x + 256 * k;
+    if (j < n16) __builtin_nontemporal_store(v[k], reinterpret_cast<gx_u32x4*>(dst) + j);
+  }
+}
+
+// The generate model's mask after the copy: 1 for the copied rows, 0 after.
+__global__ void __launch_bounds__(256)
+copy_mask_kernel(int32_t* __restrict__ mask, const int32_t* __restrict__ lengths, int cap,
+                 int lim) {
+  const int b = blockIdx.y;
+  const int r = blockIdx.x * 256 + threadIdx.x;
+  if (r >= cap) return;
+  const int L = copy_len(lengths, b, lim, nullptr, false);
+  mask[(size_t)b * cap + r] = r < L ? 1 : 0;
+}
+
+// Roll-back: rows at and after new_len[b] stop counting.
+__global__ void __launch_bounds__(256)
+trim_kernel(int32_t* __restrict__ mask, const int32_t* __restrict__ new_len, int cap,
+            int32_t* err_flag) {
+  const int b = blockIdx.y;
+  const int r = blockIdx.x * 256 + threadIdx.x;
+  const int L = copy_len(new_len, b, cap, err_flag, blockIdx.x == 0 && threadIdx.x == 0);
+  if (r < cap && r >= L) mask[(size_t)b * cap + r] = 0;
+}
+
+hipError_t launch_copy_kvcache(const void* const* src, void* const* dst, int n, int B, int H,
+                               int src_cap, int dst_cap, int D, const int32_t* lengths,
+                               int32_t* mask, int32_t* err_flag, hipStream_t stream) {
+  CopyTable t;
+  for (int i = 0; i < n; ++i) {
+    t.src[i] = static_cast<const uint8_t*>(src[i]);
+    t.dst[i] = static_cast<uint8_t*>(dst[i]);
+  }
+  const int row_bytes = D * 2;
+  const int lim = src_cap < dst_cap ? src_cap : dst_cap;
+  const long long span = (long long)lim * row_bytes;
+  const int chunks = (int)((span + kCopyBytes - 1) / kCopyBytes);
+  const long long grid = (long long)n * B * H * chunks;
+  if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
+  if (grid > 0)
+    hipLaunchKernelGGL(copy_kvcache_kernel, dim3((unsigned)grid), dim3(256), 0, stream, t, B * H,
+                       H, src_cap, dst_cap, row_bytes, chunks, lengths, err_flag);
+  if (mask)
+    hipLaunchKernelGGL(copy_mask_kernel, dim3((dst_cap + 255) / 256, B), dim3(256), 0, stream,
+                       mask, lengths, dst_cap, lim);
+  return hipGetLastError();
+}
+
+hipError_t launch_trim_kvcache(int32_t* mask, const int32_t* new_len, int B, int cap,
+                               int32_t* err_flag, hipStream_t stream) {
+  hipLaunchKernelGGL(trim_kernel, dim3((cap + 255) / 256, B), dim3(256), 0, stream, mask, new_len,
+                     cap, err_flag);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 // gather_pa_kv_cache.  A workgroup owns kGatherTok consecutive OUTPUT rows, so
 // every output byte is written exactly once with no atomics and the work is
 // balanced whatever the sequence lengths are.  Phase 1 resolves each output row
@@ -66,7 +176,6 @@ constexpr int kGatherTok = 32;
 constexpr int kGatherSlots = 16;
 constexpr int kGatherLensLds = 4096;
 
-typedef uint32_t gx_u32x4 __attribute__((ext_vector_type(4)));
 
 
 __global__ void __launch_bounds__(256)

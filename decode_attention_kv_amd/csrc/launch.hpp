@@ -9,6 +9,12 @@
 
 namespace dakv {
 
+constexpr int kCopyMaxTensors = 128;  // tensor pairs per copy_kvcache call
+hipError_t launch_copy_kvcache(const void* const* src, void* const* dst, int n, int B, int H,
+                               int src_cap, int dst_cap, int D, const int32_t* lengths,
+                               int32_t* mask, int32_t* err_flag, hipStream_t stream);
+hipError_t launch_trim_kvcache(int32_t* mask, const int32_t* new_len, int B, int cap,
+                               int32_t* err_flag, hipStream_t stream);
 hipError_t launch_kv_append(void* k_cache, void* v_cache, const void* k_new, const void* v_new,
                             const int32_t* write_pos, int32_t* mask, int B, int H, int cap,
                             int D, int32_t* err_flag, hipStream_t stream);

@@ -15,7 +15,7 @@ import numpy as np
 import torch
 
 from . import _lib
-from ._lib import check, lib
+from ._lib import COPY_MAX_TENSORS, check, lib
 
 
 def _p(t):
@@ -104,6 +104,51 @@ def kv_append(k_cache, v_cache, k_new, v_new, write_pos, mask=None, err_flag=Non
     check("kv_append", lib().dakv_kv_append(_p(k_cache), _p(v_cache), _p(k_new), _p(v_new),
                                             _p(write_pos), _p(mask), B, H, cap, D,
                                             _p(err_flag), _stream()))
+
+
+# ------------------------------------------------------ copy_kvcache / trim
+
+
+def copy_kvcache(src, dst, lengths, mask=None, err_flag=None):
+    """Copy rows [0, lengths[b]) of every src[i] [B, H, S_src, D] into dst[i]
+    [B, H, S_dst, D] (the prefill -> generate hand-over); other dst rows are kept.
+    When ``mask`` [B, S_dst] is given it becomes 1 for the copied rows, 0 after."""
+    src, dst = list(src), list(dst)
+    if not src or len(src) != len(dst):
+        raise ValueError("src and dst must be equally long, non-empty lists")
+    if len(src) > COPY_MAX_TENSORS:
+        raise ValueError(f"at most {COPY_MAX_TENSORS} tensor pairs per call")
+    if src[0].dim() != 4:
+        raise ValueError("tensors must be [B, H, S, D]")
+    B, H, S_src, D = src[0].shape
+    S_dst = dst[0].shape[2] if dst[0].dim() == 4 else -1
+    dtype = src[0].dtype
+    if dtype not in (torch.bfloat16, torch.float16):
+        raise ValueError("tensors must be bf16 or fp16")
+    for i, (s_t, d_t) in enumerate(zip(src, dst)):
+        _need(s_t, f"src[{i}]", dtype, (B, H, S_src, D))
+        _need(d_t, f"dst[{i}]", dtype, (B, H, S_dst, D))
+    _need(lengths, "lengths", torch.int32, (B,))
+    _opt(mask, "mask", torch.int32, (B, S_dst))
+    _opt(err_flag, "err_flag", torch.int32, (1,))
+    n = len(src)
+    src_arr = (ctypes.c_void_p * n)(*[t.data_ptr() for t in src])
+    dst_arr = (ctypes.c_void_p * n)(*[t.data_ptr() for t in dst])
+    check("copy_kvcache", lib().dakv_copy_kvcache(
+        ctypes.cast(src_arr, ctypes.c_void_p), ctypes.cast(dst_arr, ctypes.c_void_p), n, B, H,
+        S_src, S_dst, D, _p(lengths), _p(mask), _p(err_flag), _stream()))
+
+
+def trim_kvcache(mask, new_len, err_flag=None):
+    """Rows at and after new_len[b] of mask [B, cap] stop counting (set to 0)."""
+    _need(mask, "mask", torch.int32)
+    if mask.dim() != 2:
+        raise ValueError("mask must be [B, cap]")
+    B, cap = mask.shape
+    _need(new_len, "new_len", torch.int32, (B,))
+    _opt(err_flag, "err_flag", torch.int32, (1,))
+    check("trim_kvcache", lib().dakv_trim_kvcache(_p(mask), _p(new_len), B, cap, _p(err_flag),
+                                                  _stream()))
 
 
 # ---------------------------------------------------------- decode_attn_static

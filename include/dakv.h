@@ -47,6 +47,8 @@ extern "C" {
 #define DAKV_ERR_SPARSE_INDEX 4 /* a sparse index is outside [0, s_kv) */
 #define DAKV_ERR_SEQ_LENS 8     /* cumulative seq_lens decrease, or a table offset is bad */
 #define DAKV_ERR_VALID_LEN 16   /* a valid length is outside [0, cap] (clamped) */
+#define DAKV_ERR_COPY_LEN 32    /* a copy or trim length is outside its buffers (clamped) */
+#define DAKV_COPY_MAX_TENSORS 128 /* tensor pairs one dakv_copy_kvcache call takes */
 
 /* Text for a status code (static storage). */
 const char* dakv_strerror(int code);
@@ -77,6 +79,46 @@ const char* dakv_strerror(int code);
 int dakv_kv_append(void* k_cache, void* v_cache, const void* k_new, const void* v_new,
                    const int32_t* write_pos, int32_t* mask, int B, int H, int cap, int D,
                    int32_t* err_flag, void* stream);
+
+/*
+ * copy_kvcache -- hand the prefill model's KV cache to the generate model.
+ * [NPU-LLM] Part 2, step 3 of the generate flow: the prefill model's present
+ * tensors (capacity 1024 there) and the generate model's past tensors (1152)
+ * differ in capacity, so the valid rows [0, len) of every layer's K and V are
+ * copied as a slice, all 2 x layers tensors in parallel; "Current
+ * limitations": 512 MB at 7B with 1024 rows.
+ *
+ *   src       HOST array of n DEVICE pointers, each [B, H, src_cap, D] of 2-byte
+ *             elements (bf16 or fp16: the copy moves bits)
+ *   dst       HOST array of n DEVICE pointers, each [B, H, dst_cap, D]; rows
+ *             [0, lengths[b]) of sequence b are overwritten, the others kept
+ *   n         1 .. DAKV_COPY_MAX_TENSORS tensor pairs (pair i: src[i] -> dst[i])
+ *   lengths   int32 [B] device; rows to copy per sequence, in
+ *             [0, min(src_cap, dst_cap)]
+ *   mask      int32 [B, dst_cap] or NULL; when given it becomes 1 for the
+ *             copied rows and 0 for the rest (the stored-row count is lengths[b])
+ *   err_flag  optional; a length outside the buffers is clamped into them and
+ *             sets DAKV_ERR_COPY_LEN
+ * Pointers 16-byte aligned; D*2 a multiple of 16.  The pointer arrays are read
+ * during the call (they may be reused once it returns).
+ */
+int dakv_copy_kvcache(const void* const* src, void* const* dst, int n, int B, int H,
+                      int src_cap, int dst_cap, int D, const int32_t* lengths,
+                      int32_t* mask, int32_t* err_flag, void* stream);
+
+/*
+ * trim_kvcache -- roll each sequence's stored rows back to new_len[b].
+ * [NPU-LLM] deployment features: speculative decoding cuts the cache back to
+ * the last accepted position.  With the 0/1 mask, rows at and after new_len[b]
+ * stop counting (mask = 0); earlier entries and the row contents are left as
+ * they are.  A length of 0 resets the sequence.
+ *
+ *   mask      int32 [B, cap] device, updated in place
+ *   new_len   int32 [B] device, in [0, cap]; outside it is clamped and sets
+ *             DAKV_ERR_COPY_LEN in the optional err_flag
+ */
+int dakv_trim_kvcache(int32_t* mask, const int32_t* new_len, int B, int cap, int32_t* err_flag,
+                      void* stream);
 
 /*
  * Workspace bytes dakv_decode_attn_static needs (split-K partial outputs and

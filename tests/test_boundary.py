@@ -137,6 +137,19 @@ def test_entry_points_reject_bad_arguments_before_any_launch():
     assert L.dakv_decode_attn_paged(*pargs(8, 3, 128, 16)) == _lib.EINVAL
     assert L.dakv_decode_attn_paged(*pargs(8, 2, 128, 12)) == _lib.ENOTSUP
     assert L.dakv_decode_attn_paged(*pargs(8, 2, 64, 16)) == _lib.ENOTSUP
+    # copy_kvcache: no tensors, too many, a null or misaligned tensor pointer, odd rows
+    ptrs = lambda *p: ctypes.cast((ctypes.c_void_p * len(p))(*p), ctypes.c_void_p)
+    two = ptrs(4096, 8192)
+    cargs = lambda src, dst, n, D: (src, dst, n, 1, 2, 16, 20, D, fake, NULL, NULL, NULL)
+    assert L.dakv_copy_kvcache(*cargs(two, two, 0, 8)) == _lib.EINVAL
+    assert L.dakv_copy_kvcache(*cargs(two, two, _lib.COPY_MAX_TENSORS + 1, 8)) == _lib.EINVAL
+    assert L.dakv_copy_kvcache(*cargs(ptrs(4096, 0), two, 2, 8)) == _lib.EINVAL
+    assert L.dakv_copy_kvcache(*cargs(two, ptrs(4096, 8200), 2, 8)) == _lib.EINVAL
+    assert L.dakv_copy_kvcache(*cargs(two, two, 2, 4)) == _lib.ENOTSUP
+    assert L.dakv_copy_kvcache(NULL, NULL, 1, 0, 2, 16, 20, 8, NULL, NULL, NULL, NULL) == _lib.OK
+    # trim_kvcache: null mask, bad capacity
+    assert L.dakv_trim_kvcache(NULL, fake, 1, 8, NULL, NULL) == _lib.EINVAL
+    assert L.dakv_trim_kvcache(fake, fake, 1, 0, NULL, NULL) == _lib.EINVAL
     # sparse: unsupported dims
     assert L.dakv_sparse_topk_decode_attn(fake, fake, fake, 1, 128, 100, 256, 128, 8, 0.1, fake,
                                           NULL, fake, 1 << 20, NULL, NULL) == _lib.ENOTSUP
