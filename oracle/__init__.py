@@ -21,6 +21,10 @@ float64, with no tiling, no splitting and no online softmax:
   semantics").
 * ``sparse``        -- top-k sparse MLA-style decode (FlashMLA on Huawei Ascend,
   "Mathematical formulation").
+* ``fp8``           -- the FP8 KV cache for decode: E4M3 codes with a power-of-two
+  scale per cached row, its quantisation and the decode attention over it
+  (FlashMLA on Huawei Ascend: FP8 KV read and dequantised at decode time; a
+  token's values and scale kept together).
 
 bf16 tensors enter the oracle as their raw 16-bit patterns (``numpy.uint16``) and
 are widened exactly to float64 (``bf16.widen``); copies (append, gather) move the
@@ -41,6 +45,14 @@ from .paged import (
     decode_paged_via_gather,
 )
 from .sparse import sparse_topk_decode, validate_sparse
+from .fp8 import (
+    e4m3_decode,
+    e4m3_encode,
+    scale_exponent,
+    quantize_rows,
+    kv_append_fp8,
+    decode_static_fp8,
+)
 
 __all__ = [
     "widen",
@@ -56,4 +68,10 @@ __all__ = [
     "decode_paged_via_gather",
     "sparse_topk_decode",
     "validate_sparse",
+    "e4m3_decode",
+    "e4m3_encode",
+    "scale_exponent",
+    "quantize_rows",
+    "kv_append_fp8",
+    "decode_static_fp8",
 ]
