@@ -7,6 +7,8 @@ CPU fallback: loading fails loudly when the library has not been built.
 
 from .ops import (
     kv_append,
+    kv_append_fp8,
+    decode_attn_static_fp8,
     copy_kvcache,
     trim_kvcache,
     decode_attn_static,
@@ -25,6 +27,8 @@ from ._lib import DakvError, lib, strerror
 
 __all__ = [
     "kv_append",
+    "kv_append_fp8",
+    "decode_attn_static_fp8",
     "copy_kvcache",
     "trim_kvcache",
     "decode_attn_static",

@@ -33,6 +33,11 @@ _sz = ctypes.c_size_t
 SIGNATURES = {
     "dakv_strerror": (ctypes.c_char_p, [_i]),
     "dakv_kv_append": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp, _vp]),
+    "dakv_kv_append_fp8": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp,
+                                _vp]),
+    "dakv_decode_attn_static_fp8_workspace_size": (_sz, [_i, _i, _i, _i]),
+    "dakv_decode_attn_static_fp8": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _f,
+                                         _vp, _vp, _vp, _sz, _i, _vp, _vp]),
     "dakv_copy_kvcache": (_i, [_vp, _vp, _i, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp]),
     "dakv_trim_kvcache": (_i, [_vp, _vp, _i, _i, _vp, _vp]),
     "dakv_decode_attn_static_workspace_size": (_sz, [_i, _i, _i, _i]),

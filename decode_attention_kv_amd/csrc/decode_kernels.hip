@@ -484,6 +484,159 @@ static_decode_kernel(const float* __restrict__ q, uint16_t* __restrict__ k_cache
   finish_split<D, 1>(st, lane, wave, ws, (size_t)bh, split, n, max_splits, out, lse);
 }
 
+// ---------------------------------------------------------- static layout, FP8
+// Split pass of decode_attn_static_fp8: the cache holds E4M3 codes (one byte per
+// element, [B, H, cap, D]) and one power-of-two fp32 scale per row for K and for V
+// ([B, H, cap]).  A lane covers 8 elements of a row as in the bf16 kernel (D / 8
+// lanes per row), now 8 bytes: K and V codes arrive by 8-byte buffer loads and
+// are widened by the E4M3 conversion instruction (two codes per instruction).
+// The row scales are read like the mask, one per lane for each 64-row block of the
+// split, and a row's scale is taken from the lane that holds it: the K scale
+// multiplies the row's score, the V scale its weight in O (the sum of weights
+// uses the unscaled weight).
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ void unpack8_fp8(const u32x2_t& w, float (&f)[8]) {
+  typedef float f2_t __attribute__((ext_vector_type(2)));
+  const f2_t a = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[0], false);
+  const f2_t b = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[0], true);
+  const f2_t c = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[1], false);
+  const f2_t d = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[1], true);
+  f[0] = a[0]; f[1] = a[1]; f[2] = b[0]; f[3] = b[1];
+  f[4] = c[0]; f[5] = c[1]; f[6] = d[0]; f[7] = d[1];
+}
+
+template <int D, int U, int kSteps>
+__global__ void __launch_bounds__(kThreads)
+static_decode_fp8_kernel(const float* __restrict__ q, const uint8_t* __restrict__ k_codes,
+                         const uint8_t* __restrict__ v_codes, const float* __restrict__ k_scale,
+                         const float* __restrict__ v_scale, const int32_t* __restrict__ mask,
+                         const int32_t* __restrict__ valid_len, int H, int cap, float scale_log2,
+                         int chunk, int units, Workspace ws, float* __restrict__ out,
+                         float* __restrict__ lse, int32_t* err_flag) {
+  constexpr int LPR = D / 8;
+  constexpr int RPW = 64 / LPR;
+  constexpr int kStep = kWaves * RPW * U;             // rows per step
+  constexpr int kBallots = (kSteps * kStep + 63) / 64;
+  // the rows a wave loads at once (kWaves * RPW per u) tile 64-row words, so a
+  // lane group's row never leaves the word (s kStep + u kWaves RPW) / 64
+  static_assert(64 % (kWaves * RPW) == 0, "row words");
+  const int split = blockIdx.x / units;
+  const int bh = blockIdx.x - split * units;
+  const int max_splits = gridDim.x / units;
+  const int b = bh / H;
+  const int h = bh - b * H;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int sub = lane % LPR;
+  const int slot = lane / LPR;
+  const int r0 = split * chunk;
+  const int32_t* mrow = mask ? mask + (size_t)b * cap : nullptr;
+  const float* ksrow = k_scale + (size_t)bh * cap;
+  const float* vsrow = v_scale + (size_t)bh * cap;
+  // every load before any wait: valid length, query, and per 64-row block of the
+  // split the mask entry and both scales of row r0 + 64 k + lane (clamped)
+  const int Lraw = valid_len ? valid_len[b] : cap;
+  const float4* qp = reinterpret_cast<const float4*>(q + (size_t)bh * D + sub * 8);
+  const float4 qa = qp[0], qc = qp[1];
+  int32_t mv[kBallots];
+  float ksv[kBallots], vsv[kBallots];
+#pragma unroll
+  for (int k = 0; k < kBallots; ++k) {
+    const int r = min(r0 + 64 * k + lane, cap - 1);
+    mv[k] = mrow ? mrow[r] : 1;
+    ksv[k] = ksrow[r];
+    vsv[k] = vsrow[r];
+  }
+  int L = Lraw;
+  if (L < 0 || L > cap) {
+    if (split == 0 && h == 0 && threadIdx.x == 0) raise_flag(err_flag, 16);
+    L = L < 0 ? 0 : cap;
+  }
+  const int n = L > 0 ? (L + chunk - 1) / chunk : 1;
+  if (split >= n) return;
+  const int r1 = min(r0 + chunk, L);
+  float qr[8];
+  qr[0] = qa.x * scale_log2; qr[1] = qa.y * scale_log2;
+  qr[2] = qa.z * scale_log2; qr[3] = qa.w * scale_log2;
+  qr[4] = qc.x * scale_log2; qr[5] = qc.y * scale_log2;
+  qr[6] = qc.z * scale_log2; qr[7] = qc.w * scale_log2;
+  uint64_t bits[kBallots];
+#pragma unroll
+  for (int k = 0; k < kBallots; ++k) bits[k] = __ballot(r0 + 64 * k + lane < r1 && mv[k] != 0);
+  const __amdgpu_buffer_rsrc_t kr_rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(k_codes) + (size_t)bh * cap * D, (short)0, cap * D, 0x00020000);
+  const __amdgpu_buffer_rsrc_t vr_rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(v_codes) + (size_t)bh * cap * D, (short)0, cap * D, 0x00020000);
+  const uint32_t lane_off = (uint32_t)sub * 8;
+  float m = kNegInf, l = 0.f, o[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) o[i] = 0.f;
+  // rows of step s for this lane group: t = r0 + s kStep + (u kWaves + wave) RPW + slot
+  auto issue = [&](int s, u32x2_t (&kw)[U], u32x2_t (&vw)[U], bool (&ok)[U]) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int o_row = s * kStep + (u * kWaves + wave) * RPW + slot;  // row - r0
+      const int word = (s * kStep + u * kWaves * RPW) >> 6;            // == o_row >> 6
+      ok[u] = r0 + o_row < r1 && ((bits[word] >> (o_row - 64 * word)) & 1ull);
+      const uint32_t off = ok[u] ? (uint32_t)(r0 + o_row) * D + lane_off : BufferRows::kNoRow;
+      kw[u] = __builtin_amdgcn_raw_buffer_load_b64(kr_rs, (int)off, 0, kLoadNonTemporal);
+      vw[u] = __builtin_amdgcn_raw_buffer_load_b64(vr_rs, (int)off, 0, kLoadNonTemporal);
+    }
+  };
+  auto consume = [&](int s, const u32x2_t (&kw)[U], const u32x2_t (&vw)[U], const bool (&ok)[U]) {
+    float sc[U], ws_v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int o_row = s * kStep + (u * kWaves + wave) * RPW + slot;
+      float kf[8];
+      unpack8_fp8(kw[u], kf);
+      float acc = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc = fmaf(qr[i], kf[i], acc);
+      acc = group_sum<LPR>(acc);
+      const int word = (s * kStep + u * kWaves * RPW) >> 6;            // == o_row >> 6
+      const float ks = __shfl(ksv[word], o_row - 64 * word);
+      ws_v[u] = __shfl(vsv[word], o_row - 64 * word);
+      sc[u] = ok[u] ? acc * ks : kNegInf;
+    }
+    float mnew = m;
+#pragma unroll
+    for (int u = 0; u < U; ++u) mnew = fmaxf(mnew, sc[u]);
+    const float ms = mnew == kNegInf ? 0.f : mnew;
+    const float alpha = exp2_fast(m - ms);
+    l *= alpha;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o[i] *= alpha;
+    m = mnew;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const float p = exp2_fast(sc[u] - ms);
+      l += p;
+      const float pv = p * ws_v[u];
+      float vf[8];
+      unpack8_fp8(vw[u], vf);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) o[i] = fmaf(pv, vf[i], o[i]);
+    }
+  };
+  u32x2_t kw[2][U], vw[2][U];
+  bool ok[2][U];
+  issue(0, kw[0], vw[0], ok[0]);
+#pragma unroll
+  for (int s = 0; s < kSteps; ++s) {
+    if (s + 1 < kSteps) issue(s + 1, kw[(s + 1) & 1], vw[(s + 1) & 1], ok[(s + 1) & 1]);
+    consume(s, kw[s & 1], vw[s & 1], ok[s & 1]);
+  }
+  HeadState<1> st;
+  st.m[0] = m;
+  st.l[0] = l;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) st.o[0][i] = o[i];
+  merge_groups<LPR, 1>(st);
+  finish_split<D, 1>(st, lane, wave, ws, (size_t)bh, split, n, max_splits, out, lse);
+}
+
 // ------------------------------------------------------------------ paged layout
 constexpr int kMaxTableSpan = 72;  // block-table entries one split may touch
 
@@ -861,6 +1014,49 @@ hipError_t launch_decode_static(const float* q, void* k_cache, void* v_cache, in
       launch_static_d<64, false>(q, k_cache, v_cache, mask, valid_len, k_new, v_new, write_pos,
                                  B, H, cap, scale, out, lse, ws, plan, err_flag, stream);
   }
+  return hipGetLastError();
+}
+
+template <int D, int kSteps>
+static void launch_static_fp8_k(const float* q, const void* k_codes, const void* v_codes,
+                                const float* k_scale, const float* v_scale, const int32_t* mask,
+                                const int32_t* valid_len, int B, int H, int cap, float scale,
+                                float* out, float* lse, const Workspace& w, const SplitPlan& plan,
+                                int32_t* err_flag, hipStream_t stream) {
+  hipLaunchKernelGGL((static_decode_fp8_kernel<D, 4, kSteps>),
+                     dim3((unsigned)(B * H * plan.max_splits)), dim3(kThreads), 0, stream, q,
+                     static_cast<const uint8_t*>(k_codes), static_cast<const uint8_t*>(v_codes),
+                     k_scale, v_scale, mask, valid_len, H, cap, scale * kLog2e, plan.chunk, B * H,
+                     w, out, lse, err_flag);
+}
+
+hipError_t launch_decode_static_fp8(const float* q, const void* k_codes, const void* v_codes,
+                                    const float* k_scale, const float* v_scale,
+                                    const int32_t* mask, const int32_t* valid_len, int B, int H,
+                                    int cap, int D, float scale, float* out, float* lse, void* ws,
+                                    const SplitPlan& plan, int32_t* err_flag, hipStream_t stream) {
+  const Workspace w = carve(ws, (size_t)B * H, plan.max_splits, D);
+#define DAKV_FP8(DD)                                                                          \
+  do {                                                                                        \
+    constexpr int kStep = kWaves * (64 / (DD / 8)) * 4;                                       \
+    const int steps = (plan.chunk + kStep - 1) / kStep;                                       \
+    if (steps <= 1)                                                                           \
+      launch_static_fp8_k<DD, 1>(q, k_codes, v_codes, k_scale, v_scale, mask, valid_len, B, H, \
+                                 cap, scale, out, lse, w, plan, err_flag, stream);            \
+    else if (steps <= 2)                                                                      \
+      launch_static_fp8_k<DD, 2>(q, k_codes, v_codes, k_scale, v_scale, mask, valid_len, B, H, \
+                                 cap, scale, out, lse, w, plan, err_flag, stream);            \
+    else                                                                                      \
+      launch_static_fp8_k<DD, 4>(q, k_codes, v_codes, k_scale, v_scale, mask, valid_len, B, H, \
+                                 cap, scale, out, lse, w, plan, err_flag, stream);            \
+    if (plan.max_splits > 1)                                                                  \
+      hipLaunchKernelGGL(merge_kernel<DD>, dim3(B * H), dim3(kThreads), 0, stream, w, H,      \
+                         plan.chunk, plan.max_splits, 0, valid_len, cap, nullptr, nullptr, 1, \
+                         0, 0, out, lse);                                                     \
+  } while (0)
+  if (D == 128) DAKV_FP8(128);
+  else DAKV_FP8(64);
+#undef DAKV_FP8
   return hipGetLastError();
 }
 

@@ -81,6 +81,46 @@ int dakv_kv_append(void* k_cache, void* v_cache, const void* k_new, const void* 
                    int32_t* err_flag, void* stream);
 
 /*
+ * FP8 KV cache ([FlashMLA] section on VECTOR cores per CUBE core, item 2: at
+ * decode time the kernel reads the KV cache in FP8 and dequantises it; section on
+ * the decoding KV-cache layout: a token's values and scale go together).  Codes
+ * are OCP E4M3 (bias 7, largest finite 448), one byte per element, [B, H, cap, D];
+ * every cached row has one power-of-two fp32 scale, for K in k_scale and for V in
+ * v_scale, [B, H, cap]: s = 2^e, e the smallest integer with max|x| <= 448 * 2^e
+ * (e = 0 for a zero row), code = x / s rounded to the nearest E4M3 value, ties to
+ * the even code (zero results are the +0 code).  The cached value is
+ * decode(code) * s.  (The scales live in their own arrays rather than inside the
+ * row: on the GPU they are one coalesced 4-byte stream and the rows stay 16-byte
+ * aligned.)
+ *
+ * kv_append_fp8 -- quantise the new token's K and V rows (bf16 [B, H, D], finite
+ * values) and store codes and scales at row write_pos[b]; mask as kv_append.  A
+ * position outside [0, cap) sets DAKV_ERR_WRITE_POS and skips that sequence.
+ * D in 16 .. 256, a multiple of 16.
+ */
+int dakv_kv_append_fp8(void* k_codes, void* v_codes, float* k_scale, float* v_scale,
+                       const void* k_new, const void* v_new, const int32_t* write_pos,
+                       int32_t* mask, int B, int H, int cap, int D, int32_t* err_flag,
+                       void* stream);
+
+/* Workspace bytes dakv_decode_attn_static_fp8 needs (the same as the bf16 call's). */
+size_t dakv_decode_attn_static_fp8_workspace_size(int B, int H, int cap, int D);
+
+/*
+ * decode_attn_static_fp8 -- decode_attn_static over an FP8 cache: the same query,
+ * mask, valid length, scale, outputs, workspace and split rules, with row t of
+ * (b, h) taken as decode(code) * scale[b, h, t] for K and for V.
+ *   k_codes, v_codes  uint8 E4M3 [B, H, cap, D];  k_scale, v_scale fp32 [B, H, cap]
+ * Supported: D in {64, 128}, cap <= 65536.
+ */
+int dakv_decode_attn_static_fp8(const float* q, const void* k_codes, const void* v_codes,
+                                const float* k_scale, const float* v_scale, const int32_t* mask,
+                                const int32_t* valid_len, int B, int H, int cap, int D,
+                                float scale, float* out, float* lse, void* workspace,
+                                size_t workspace_bytes, int num_splits, int32_t* err_flag,
+                                void* stream);
+
+/*
  * copy_kvcache -- hand the prefill model's KV cache to the generate model.
  * [NPU-LLM] Part 2, step 3 of the generate flow: the prefill model's present
  * tensors (capacity 1024 there) and the generate model's past tensors (1152)

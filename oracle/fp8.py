@@ -83,6 +83,8 @@ def scale_exponent(amax):
 def quantize_rows(x_bits):
     """bf16 bit patterns ``[..., D]`` -> (codes uint8 ``[..., D]``, scale float64 ``[...]``)."""
     x = widen(x_bits)
+    if not np.all(np.isfinite(x)):
+        raise ValueError("a row with NaN or Inf has no E4M3 encoding")
     lead = x.shape[:-1]
     flat = x.reshape(-1, x.shape[-1])
     codes = np.empty(flat.shape, dtype=np.uint8)

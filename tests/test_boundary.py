@@ -147,6 +147,17 @@ def test_entry_points_reject_bad_arguments_before_any_launch():
     assert L.dakv_copy_kvcache(*cargs(two, ptrs(4096, 8200), 2, 8)) == _lib.EINVAL
     assert L.dakv_copy_kvcache(*cargs(two, two, 2, 4)) == _lib.ENOTSUP
     assert L.dakv_copy_kvcache(NULL, NULL, 1, 0, 2, 16, 20, 8, NULL, NULL, NULL, NULL) == _lib.OK
+    # fp8: unsupported head dims, missing scales
+    assert L.dakv_kv_append_fp8(fake, fake, fake, fake, fake, fake, fake, NULL, 1, 1, 4, 24,
+                                NULL, NULL) == _lib.ENOTSUP
+    assert L.dakv_kv_append_fp8(fake, fake, NULL, fake, fake, fake, fake, NULL, 1, 1, 4, 64,
+                                NULL, NULL) == _lib.EINVAL
+    wsf = L.dakv_decode_attn_static_fp8_workspace_size(1, 4, 1152, 64)
+    assert wsf == L.dakv_decode_attn_static_workspace_size(1, 4, 1152, 64)
+    fargs = lambda D, ksc: (fake, fake, fake, ksc, fake, fake, NULL, 1, 4, 1152, D, 0.125, fake,
+                            NULL, fake, wsf, 0, NULL, NULL)
+    assert L.dakv_decode_attn_static_fp8(*fargs(96, fake)) == _lib.ENOTSUP
+    assert L.dakv_decode_attn_static_fp8(*fargs(64, NULL)) == _lib.EINVAL
     # trim_kvcache: null mask, bad capacity
     assert L.dakv_trim_kvcache(NULL, fake, 1, 8, NULL, NULL) == _lib.EINVAL
     assert L.dakv_trim_kvcache(fake, fake, 1, 0, NULL, NULL) == _lib.EINVAL
