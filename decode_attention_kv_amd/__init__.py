@@ -9,6 +9,7 @@ from .ops import (
     kv_append,
     kv_append_fp8,
     decode_attn_static_fp8,
+    decode_step_static_fp8,
     copy_kvcache,
     trim_kvcache,
     decode_attn_static,
@@ -29,6 +30,7 @@ __all__ = [
     "kv_append",
     "kv_append_fp8",
     "decode_attn_static_fp8",
+    "decode_step_static_fp8",
     "copy_kvcache",
     "trim_kvcache",
     "decode_attn_static",

@@ -61,32 +61,6 @@ hipError_t launch_kv_append(void* k_cache, void* v_cache, const void* k_new, con
 // value x * 2^-e (exact) is rounded to the nearest E4M3 value, ties to the even
 // code, zero results as the +0 code.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ int e4m3_exponent_for(float amax) {
-  if (!(amax > 0.f)) return 0;
-  int E;
-  const float f = frexpf(amax, &E);        // amax = f 2^E, f in [0.5, 1); 448 = 0.875 2^9
-  return f <= 0.875f ? E - 9 : E - 8;
-}
-
-__device__ __forceinline__ uint32_t e4m3_code(float y) {  // |y| <= 448
-  const float a = fabsf(y);
-  uint32_t code;
-  if (a < 0.015625f) {                     // below 2^-6: multiples of 2^-9
-    code = (uint32_t)rintf(a * 512.f);     // 8 -> 2^-6, the smallest normal code
-  } else {
-    int F;
-    const float f = frexpf(a, &F);         // a = (2f) 2^(F-1), 2f in [1, 2)
-    uint32_t m = (uint32_t)rintf((2.f * f - 1.f) * 8.f);
-    int E = F - 1;
-    if (m == 8) {
-      m = 0;
-      ++E;
-    }
-    code = ((uint32_t)(E + 7) << 3) | m;
-  }
-  return (code != 0 && y < 0.f) ? (code | 0x80u) : code;
-}
-
 __global__ void __launch_bounds__(256)
 kv_append_fp8_kernel(uint8_t* __restrict__ k_codes, uint8_t* __restrict__ v_codes,
                      float* __restrict__ k_scale, float* __restrict__ v_scale,

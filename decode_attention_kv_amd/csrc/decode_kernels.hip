@@ -506,14 +506,20 @@ __device__ __forceinline__ void unpack8_fp8(const u32x2_t& w, float (&f)[8]) {
   f[4] = c[0]; f[5] = c[1]; f[6] = d[0]; f[7] = d[1];
 }
 
-template <int D, int U, int kSteps>
+//
+// With kAppend (decode_step_static_fp8) the split that owns p = write_pos[b]
+// first quantises the new token's K and V rows (as kv_append_fp8 does) in the
+// lanes that later consume row p; they store codes and scales and keep both in
+// registers for that row, and p is attended whatever its mask entry says.
+template <int D, int U, int kSteps, bool kAppend>
 __global__ void __launch_bounds__(kThreads)
-static_decode_fp8_kernel(const float* __restrict__ q, const uint8_t* __restrict__ k_codes,
-                         const uint8_t* __restrict__ v_codes, const float* __restrict__ k_scale,
-                         const float* __restrict__ v_scale, const int32_t* __restrict__ mask,
-                         const int32_t* __restrict__ valid_len, int H, int cap, float scale_log2,
-                         int chunk, int units, Workspace ws, float* __restrict__ out,
-                         float* __restrict__ lse, int32_t* err_flag) {
+static_decode_fp8_kernel(const float* __restrict__ q, uint8_t* __restrict__ k_codes,
+                         uint8_t* __restrict__ v_codes, float* __restrict__ k_scale,
+                         float* __restrict__ v_scale, int32_t* __restrict__ mask,
+                         const int32_t* __restrict__ valid_len, const uint16_t* __restrict__ k_new,
+                         const uint16_t* __restrict__ v_new, const int32_t* __restrict__ write_pos,
+                         int H, int cap, float scale_log2, int chunk, int units, Workspace ws,
+                         float* __restrict__ out, float* __restrict__ lse, int32_t* err_flag) {
   constexpr int LPR = D / 8;
   constexpr int RPW = 64 / LPR;
   constexpr int kStep = kWaves * RPW * U;             // rows per step
@@ -537,6 +543,7 @@ static_decode_fp8_kernel(const float* __restrict__ q, const uint8_t* __restrict_
   // every load before any wait: valid length, query, and per 64-row block of the
   // split the mask entry and both scales of row r0 + 64 k + lane (clamped)
   const int Lraw = valid_len ? valid_len[b] : cap;
+  int p = kAppend ? write_pos[b] : -1;
   const float4* qp = reinterpret_cast<const float4*>(q + (size_t)bh * D + sub * 8);
   const float4 qa = qp[0], qc = qp[1];
   int32_t mv[kBallots];
@@ -548,9 +555,57 @@ static_decode_fp8_kernel(const float* __restrict__ q, const uint8_t* __restrict_
     ksv[k] = ksrow[r];
     vsv[k] = vsrow[r];
   }
+  const bool report = split == 0 && h == 0 && threadIdx.x == 0;
+  // the appended row's codes and scales, in the lanes that own it
+  float new_ks = 0.f, new_vs = 0.f;
+  u32x2_t new_kw = {0u, 0u}, new_vw = {0u, 0u};
+  if constexpr (kAppend) {
+    if (p < 0 || p >= cap) {
+      if (report) raise_flag(err_flag, 2);
+      p = -1;
+    } else if (p / chunk == split) {
+      const int o = p - r0;
+      if (wave == (o / RPW) % kWaves && slot == o % RPW) {
+        const uint4 kn = load16(k_new + (size_t)bh * D + sub * 8);
+        const uint4 vn = load16(v_new + (size_t)bh * D + sub * 8);
+        float kx[8], vx[8];
+        unpack8(kn, kx);
+        unpack8(vn, vx);
+        float ka = 0.f, va = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          ka = fmaxf(ka, fabsf(kx[i]));
+          va = fmaxf(va, fabsf(vx[i]));
+        }
+        ka = group_max<LPR>(ka);
+        va = group_max<LPR>(va);
+        const int ke = e4m3_exponent_for(ka), ve = e4m3_exponent_for(va);
+        u32x2_t kw = {0u, 0u}, vw = {0u, 0u};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          kw[i >> 2] |= e4m3_code(ldexpf(kx[i], -ke)) << (8 * (i & 3));
+          vw[i >> 2] |= e4m3_code(ldexpf(vx[i], -ve)) << (8 * (i & 3));
+        }
+        const size_t at = ((size_t)bh * cap + p) * D + (size_t)sub * 8;
+        *reinterpret_cast<u32x2_t*>(k_codes + at) = kw;
+        *reinterpret_cast<u32x2_t*>(v_codes + at) = vw;
+        new_kw = kw;
+        new_vw = vw;
+        new_ks = ldexpf(1.f, ke);
+        new_vs = ldexpf(1.f, ve);
+        if (sub == 0) {
+          k_scale[(size_t)bh * cap + p] = new_ks;
+          v_scale[(size_t)bh * cap + p] = new_vs;
+        }
+      }
+      if (mask && h == 0 && threadIdx.x == 0) mask[(size_t)b * cap + p] = 1;
+    } else {
+      p = -1;  // another split holds the new row
+    }
+  }
   int L = Lraw;
   if (L < 0 || L > cap) {
-    if (split == 0 && h == 0 && threadIdx.x == 0) raise_flag(err_flag, 16);
+    if (report) raise_flag(err_flag, 16);
     L = L < 0 ? 0 : cap;
   }
   const int n = L > 0 ? (L + chunk - 1) / chunk : 1;
@@ -578,7 +633,8 @@ static_decode_fp8_kernel(const float* __restrict__ q, const uint8_t* __restrict_
     for (int u = 0; u < U; ++u) {
       const int o_row = s * kStep + (u * kWaves + wave) * RPW + slot;  // row - r0
       const int word = (s * kStep + u * kWaves * RPW) >> 6;            // == o_row >> 6
-      ok[u] = r0 + o_row < r1 && ((bits[word] >> (o_row - 64 * word)) & 1ull);
+      ok[u] = r0 + o_row < r1 &&
+              (((bits[word] >> (o_row - 64 * word)) & 1ull) || r0 + o_row == p);
       const uint32_t off = ok[u] ? (uint32_t)(r0 + o_row) * D + lane_off : BufferRows::kNoRow;
       kw[u] = __builtin_amdgcn_raw_buffer_load_b64(kr_rs, (int)off, 0, kLoadNonTemporal);
       vw[u] = __builtin_amdgcn_raw_buffer_load_b64(vr_rs, (int)off, 0, kLoadNonTemporal);
@@ -586,18 +642,26 @@ static_decode_fp8_kernel(const float* __restrict__ q, const uint8_t* __restrict_
   };
   auto consume = [&](int s, const u32x2_t (&kw)[U], const u32x2_t (&vw)[U], const bool (&ok)[U]) {
     float sc[U], ws_v[U];
+    bool fresh[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int o_row = s * kStep + (u * kWaves + wave) * RPW + slot;
+      // the appended row comes from registers, never from a load that follows
+      // this lane's own store
+      fresh[u] = kAppend && r0 + o_row == p;
       float kf[8];
-      unpack8_fp8(kw[u], kf);
+      unpack8_fp8(fresh[u] ? new_kw : kw[u], kf);
       float acc = 0.f;
 #pragma unroll
       for (int i = 0; i < 8; ++i) acc = fmaf(qr[i], kf[i], acc);
       acc = group_sum<LPR>(acc);
       const int word = (s * kStep + u * kWaves * RPW) >> 6;            // == o_row >> 6
-      const float ks = __shfl(ksv[word], o_row - 64 * word);
-      ws_v[u] = __shfl(vsv[word], o_row - 64 * word);
+      // both shuffles run in every lane (a lane reads another lane's scale, so
+      // none may sit out), then the appended row takes its own
+      const float ksh = __shfl(ksv[word], o_row - 64 * word);
+      const float vsh = __shfl(vsv[word], o_row - 64 * word);
+      const float ks = fresh[u] ? new_ks : ksh;
+      ws_v[u] = fresh[u] ? new_vs : vsh;
       sc[u] = ok[u] ? acc * ks : kNegInf;
     }
     float mnew = m;
@@ -615,7 +679,7 @@ static_decode_fp8_kernel(const float* __restrict__ q, const uint8_t* __restrict_
       l += p;
       const float pv = p * ws_v[u];
       float vf[8];
-      unpack8_fp8(vw[u], vf);
+      unpack8_fp8(fresh[u] ? new_vw : vw[u], vf);
 #pragma unroll
       for (int i = 0; i < 8; ++i) o[i] = fmaf(pv, vf[i], o[i]);
     }
@@ -1018,22 +1082,32 @@ hipError_t launch_decode_static(const float* q, void* k_cache, void* v_cache, in
 }
 
 template <int D, int kSteps>
-static void launch_static_fp8_k(const float* q, const void* k_codes, const void* v_codes,
-                                const float* k_scale, const float* v_scale, const int32_t* mask,
-                                const int32_t* valid_len, int B, int H, int cap, float scale,
-                                float* out, float* lse, const Workspace& w, const SplitPlan& plan,
-                                int32_t* err_flag, hipStream_t stream) {
-  hipLaunchKernelGGL((static_decode_fp8_kernel<D, 4, kSteps>),
-                     dim3((unsigned)(B * H * plan.max_splits)), dim3(kThreads), 0, stream, q,
-                     static_cast<const uint8_t*>(k_codes), static_cast<const uint8_t*>(v_codes),
-                     k_scale, v_scale, mask, valid_len, H, cap, scale * kLog2e, plan.chunk, B * H,
-                     w, out, lse, err_flag);
+static void launch_static_fp8_k(const float* q, void* k_codes, void* v_codes, float* k_scale,
+                                float* v_scale, int32_t* mask, const int32_t* valid_len,
+                                const void* k_new, const void* v_new, const int32_t* write_pos,
+                                int B, int H, int cap, float scale, float* out, float* lse,
+                                const Workspace& w, const SplitPlan& plan, int32_t* err_flag,
+                                hipStream_t stream) {
+  const dim3 grid((unsigned)(B * H * plan.max_splits));
+  auto* kc = static_cast<uint8_t*>(k_codes);
+  auto* vc = static_cast<uint8_t*>(v_codes);
+  auto* kn = static_cast<const uint16_t*>(k_new);
+  auto* vn = static_cast<const uint16_t*>(v_new);
+  if (write_pos)
+    hipLaunchKernelGGL((static_decode_fp8_kernel<D, 4, kSteps, true>), grid, dim3(kThreads), 0,
+                       stream, q, kc, vc, k_scale, v_scale, mask, valid_len, kn, vn, write_pos, H,
+                       cap, scale * kLog2e, plan.chunk, B * H, w, out, lse, err_flag);
+  else
+    hipLaunchKernelGGL((static_decode_fp8_kernel<D, 4, kSteps, false>), grid, dim3(kThreads), 0,
+                       stream, q, kc, vc, k_scale, v_scale, mask, valid_len, kn, vn, write_pos, H,
+                       cap, scale * kLog2e, plan.chunk, B * H, w, out, lse, err_flag);
 }
 
-hipError_t launch_decode_static_fp8(const float* q, const void* k_codes, const void* v_codes,
-                                    const float* k_scale, const float* v_scale,
-                                    const int32_t* mask, const int32_t* valid_len, int B, int H,
-                                    int cap, int D, float scale, float* out, float* lse, void* ws,
+hipError_t launch_decode_static_fp8(const float* q, void* k_codes, void* v_codes, float* k_scale,
+                                    float* v_scale, int32_t* mask, const int32_t* valid_len,
+                                    const void* k_new, const void* v_new,
+                                    const int32_t* write_pos, int B, int H, int cap, int D,
+                                    float scale, float* out, float* lse, void* ws,
                                     const SplitPlan& plan, int32_t* err_flag, hipStream_t stream) {
   const Workspace w = carve(ws, (size_t)B * H, plan.max_splits, D);
 #define DAKV_FP8(DD)                                                                          \
@@ -1041,14 +1115,17 @@ hipError_t launch_decode_static_fp8(const float* q, const void* k_codes, const v
     constexpr int kStep = kWaves * (64 / (DD / 8)) * 4;                                       \
     const int steps = (plan.chunk + kStep - 1) / kStep;                                       \
     if (steps <= 1)                                                                           \
-      launch_static_fp8_k<DD, 1>(q, k_codes, v_codes, k_scale, v_scale, mask, valid_len, B, H, \
-                                 cap, scale, out, lse, w, plan, err_flag, stream);            \
+      launch_static_fp8_k<DD, 1>(q, k_codes, v_codes, k_scale, v_scale, mask, valid_len, k_new, \
+                                 v_new, write_pos, B, H, cap, scale, out, lse, w, plan,       \
+                                 err_flag, stream);                                           \
     else if (steps <= 2)                                                                      \
-      launch_static_fp8_k<DD, 2>(q, k_codes, v_codes, k_scale, v_scale, mask, valid_len, B, H, \
-                                 cap, scale, out, lse, w, plan, err_flag, stream);            \
+      launch_static_fp8_k<DD, 2>(q, k_codes, v_codes, k_scale, v_scale, mask, valid_len, k_new, \
+                                 v_new, write_pos, B, H, cap, scale, out, lse, w, plan,       \
+                                 err_flag, stream);                                           \
     else                                                                                      \
-      launch_static_fp8_k<DD, 4>(q, k_codes, v_codes, k_scale, v_scale, mask, valid_len, B, H, \
-                                 cap, scale, out, lse, w, plan, err_flag, stream);            \
+      launch_static_fp8_k<DD, 4>(q, k_codes, v_codes, k_scale, v_scale, mask, valid_len, k_new, \
+                                 v_new, write_pos, B, H, cap, scale, out, lse, w, plan,       \
+                                 err_flag, stream);                                           \
     if (plan.max_splits > 1)                                                                  \
       hipLaunchKernelGGL(merge_kernel<DD>, dim3(B * H), dim3(kThreads), 0, stream, w, H,      \
                          plan.chunk, plan.max_splits, 0, valid_len, cap, nullptr, nullptr, 1, \

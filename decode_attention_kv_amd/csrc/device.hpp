@@ -79,4 +79,34 @@ __device__ __forceinline__ void store16(void* p, const uint4& v) {
   *reinterpret_cast<uint4*>(p) = v;
 }
 
+// E4M3 quantisation of a row with a power-of-two scale 2^e: e is the smallest
+// integer with amax <= 448 * 2^e (0 for amax = 0), from amax's exponent and
+// fraction, exactly; a value y = x * 2^-e (|y| <= 448) gets the code of the
+// nearest E4M3 value, ties to the even code, zero results as the +0 code.
+__device__ __forceinline__ int e4m3_exponent_for(float amax) {
+  if (!(amax > 0.f)) return 0;
+  int E;
+  const float f = frexpf(amax, &E);        // amax = f 2^E, f in [0.5, 1); 448 = 0.875 2^9
+  return f <= 0.875f ? E - 9 : E - 8;
+}
+
+__device__ __forceinline__ uint32_t e4m3_code(float y) {  // |y| <= 448
+  const float a = fabsf(y);
+  uint32_t code;
+  if (a < 0.015625f) {                     // below 2^-6: multiples of 2^-9
+    code = (uint32_t)rintf(a * 512.f);     // 8 -> 2^-6, the smallest normal code
+  } else {
+    int F;
+    const float f = frexpf(a, &F);         // a = (2f) 2^(F-1), 2f in [1, 2)
+    uint32_t m = (uint32_t)rintf((2.f * f - 1.f) * 8.f);
+    int E = F - 1;
+    if (m == 8) {
+      m = 0;
+      ++E;
+    }
+    code = ((uint32_t)(E + 7) << 3) | m;
+  }
+  return (code != 0 && y < 0.f) ? (code | 0x80u) : code;
+}
+
 }  // namespace dakv

@@ -35,10 +35,12 @@ SplitPlan plan_static(int B, int H, int cap, int D, int forced_splits);
 // Whether a capacity fits the split limits of the static kernel (<= 65536 rows).
 bool static_supported(int cap);
 size_t static_workspace_bytes(int B, int H, int cap, int D);
-hipError_t launch_decode_static_fp8(const float* q, const void* k_codes, const void* v_codes,
-                                    const float* k_scale, const float* v_scale,
-                                    const int32_t* mask, const int32_t* valid_len, int B, int H,
-                                    int cap, int D, float scale, float* out, float* lse, void* ws,
+// write_pos != NULL: append k_new / v_new (bf16 [B, H, D]) first (decode_step_static_fp8)
+hipError_t launch_decode_static_fp8(const float* q, void* k_codes, void* v_codes, float* k_scale,
+                                    float* v_scale, int32_t* mask, const int32_t* valid_len,
+                                    const void* k_new, const void* v_new,
+                                    const int32_t* write_pos, int B, int H, int cap, int D,
+                                    float scale, float* out, float* lse, void* ws,
                                     const SplitPlan& plan, int32_t* err_flag, hipStream_t stream);
 hipError_t launch_kv_append_fp8(void* k_codes, void* v_codes, float* k_scale, float* v_scale,
                                 const void* k_new, const void* v_new, const int32_t* write_pos,

@@ -121,6 +121,20 @@ int dakv_decode_attn_static_fp8(const float* q, const void* k_codes, const void*
                                 void* stream);
 
 /*
+ * decode_step_static_fp8 -- kv_append_fp8 followed by decode_attn_static_fp8, in
+ * one split pass: the split that owns write_pos[b] quantises and stores the new
+ * row before attending (same results as the two calls; the new row is attended
+ * whatever its mask entry says, and the mask entry is set).  Arguments as the two
+ * calls; k_new, v_new bf16 [B, H, D] (finite values), write_pos int32 [B].
+ */
+int dakv_decode_step_static_fp8(const float* q, void* k_codes, void* v_codes, float* k_scale,
+                                float* v_scale, const void* k_new, const void* v_new,
+                                const int32_t* write_pos, int32_t* mask, const int32_t* valid_len,
+                                int B, int H, int cap, int D, float scale, float* out, float* lse,
+                                void* workspace, size_t workspace_bytes, int num_splits,
+                                int32_t* err_flag, void* stream);
+
+/*
  * copy_kvcache -- hand the prefill model's KV cache to the generate model.
  * [NPU-LLM] Part 2, step 3 of the generate flow: the prefill model's present
  * tensors (capacity 1024 there) and the generate model's past tensors (1152)
