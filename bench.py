@@ -33,7 +33,7 @@ HBM_PEAK_GBS = 8000.0
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "static_decode_step_b8_traffic.md")
-STATIC_SOURCES = ("decode_kernels.hip", "device.hpp", "launch.hpp")
+STATIC_SOURCES = ("decode_kernels.hip", "split_common.hpp", "device.hpp")
 
 
 def static_sources_sha256():

@@ -53,65 +53,6 @@ hipError_t launch_kv_append(void* k_cache, void* v_cache, const void* k_new, con
 }
 
 // ---------------------------------------------------------------------------
-// kv_append_fp8: the new token's K and V rows are quantised to E4M3 codes with a
-// power-of-two scale per row and stored at row write_pos[b].  One wave per
-// (sequence, head, K or V): the row's largest magnitude comes from a wave
-// reduction; the scale is 2^e with e the smallest integer for which
-// max|x| <= 448 * 2^e (from the exponent and fraction of max|x|, exactly); each
-// value x * 2^-e (exact) is rounded to the nearest E4M3 value, ties to the even
-// code, zero results as the +0 code.
-// ---------------------------------------------------------------------------
-__global__ void __launch_bounds__(256)
-kv_append_fp8_kernel(uint8_t* __restrict__ k_codes, uint8_t* __restrict__ v_codes,
-                     float* __restrict__ k_scale, float* __restrict__ v_scale,
-                     const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new,
-                     const int32_t* __restrict__ write_pos, int32_t* __restrict__ mask, int H,
-                     int cap, int D, int32_t* err_flag) {
-  const int b = blockIdx.y;
-  const int unit = blockIdx.x * 4 + (threadIdx.x >> 6);  // (head, K or V)
-  const int lane = threadIdx.x & 63;
-  if (unit >= 2 * H) return;
-  const int h = unit >> 1;
-  const bool is_v = unit & 1;
-  const int pos = write_pos[b];
-  if (pos < 0 || pos >= cap) {
-    if (unit == 0 && lane == 0) raise_flag(err_flag, 2);
-    return;
-  }
-  const uint16_t* src = (is_v ? v_new : k_new) + ((size_t)b * H + h) * D;
-  const size_t row = ((size_t)b * H + h) * cap + pos;
-  uint8_t* dst = (is_v ? v_codes : k_codes) + row * D;
-  float x[4];
-  float amax = 0.f;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {            // D <= 256: at most 4 values per lane
-    const int d = lane + 64 * i;
-    x[i] = d < D ? __uint_as_float((uint32_t)src[d] << 16) : 0.f;
-    amax = fmaxf(amax, fabsf(x[i]));
-  }
-  for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
-  const int e = e4m3_exponent_for(amax);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int d = lane + 64 * i;
-    if (d < D) dst[d] = (uint8_t)e4m3_code(ldexpf(x[i], -e));
-  }
-  if (lane == 0) (is_v ? v_scale : k_scale)[row] = ldexpf(1.f, e);
-  if (mask && unit == 0 && lane == 0) mask[(size_t)b * cap + pos] = 1;
-}
-
-hipError_t launch_kv_append_fp8(void* k_codes, void* v_codes, float* k_scale, float* v_scale,
-                                const void* k_new, const void* v_new, const int32_t* write_pos,
-                                int32_t* mask, int B, int H, int cap, int D, int32_t* err_flag,
-                                hipStream_t stream) {
-  hipLaunchKernelGGL(kv_append_fp8_kernel, dim3((2 * H + 3) / 4, B), dim3(256), 0, stream,
-                     static_cast<uint8_t*>(k_codes), static_cast<uint8_t*>(v_codes), k_scale,
-                     v_scale, static_cast<const uint16_t*>(k_new),
-                     static_cast<const uint16_t*>(v_new), write_pos, mask, H, cap, D, err_flag);
-  return hipGetLastError();
-}
-
-// ---------------------------------------------------------------------------
 // copy_kvcache: the prefill model's valid rows [0, len_b) of every (tensor,
 // sequence, head) go to the same rows of the generate model's buffer.  For one
 // (tensor, sequence, head) those rows are len_b * row_bytes contiguous bytes in

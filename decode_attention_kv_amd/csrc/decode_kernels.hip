@@ -19,376 +19,11 @@
 // the last split to finish would need device-scope fences between workgroups; on
 // this chip those write back and invalidate the L2 of the XCD, which costs far
 // more than the second launch.)
-#include "device.hpp"
-#include "launch.hpp"
+#include "split_common.hpp"
 
 namespace dakv {
 
-constexpr int kWaves = 4;
-constexpr int kThreads = 64 * kWaves;
-constexpr int kMinChunk = 64;
-constexpr int kMaxSplits = 256;  // splits one unit may have (merge state lives in LDS)
-
-// Effective row count of a static-buffer sequence: valid_len[b] clamped to
-// [0, cap] (clamping is flagged), or cap without a valid_len.
-__device__ __forceinline__ int static_len(const int32_t* valid_len, int b, int cap,
-                                          int32_t* err_flag, bool report) {
-  if (!valid_len) return cap;
-  int L = valid_len[b];
-  if (L < 0 || L > cap) {
-    if (report) raise_flag(err_flag, 16);
-    L = L < 0 ? 0 : cap;
-  }
-  return L;
-}
-
-// Effective row count of a paged sequence from its cumulative lengths [start,
-// end) and table offset: the difference, cut at max_len and at the table's last
-// column (toff = the offset in blocks); *bad tells whether anything was cut.
-__device__ __forceinline__ int paged_len_of(int start, int end, int off, int block_size,
-                                            int table_cols, int max_len, int* toff, bool* bad) {
-  int L = end - start;
-  *bad = false;
-  if (L < 0) { L = 0; *bad = true; }
-  if (off < 0 || off % block_size != 0) { L = 0; *bad = true; *toff = 0; }
-  else *toff = off / block_size;
-  const int room = (table_cols - *toff) * block_size;
-  if (L > room) { L = room > 0 ? room : 0; *bad = true; }
-  if (L > max_len) { L = max_len; *bad = true; }
-  return L;
-}
-
-// The same, loading the sequence's entries; inconsistencies are flagged.
-__device__ __forceinline__ int paged_len(const int32_t* seq_lens, const int32_t* seq_offset,
-                                         int b, int block_size, int table_cols, int max_len,
-                                         int* toff, int32_t* err_flag, bool report) {
-  bool bad;
-  const int L = paged_len_of(seq_lens[b], seq_lens[b + 1], seq_offset ? seq_offset[b] : 0,
-                             block_size, table_cols, max_len, toff, &bad);
-  if (bad && report) raise_flag(err_flag, 8);
-  return L;
-}
-
-// Online-softmax state of G query heads for one row group (D/8 lanes).
-template <int G>
-struct HeadState {
-  float m[G], l[G], o[G][8];
-};
-
-template <int G>
-__device__ __forceinline__ void init_state(HeadState<G>& st) {
-#pragma unroll
-  for (int j = 0; j < G; ++j) {
-    st.m[j] = kNegInf;
-    st.l[j] = 0.f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) st.o[j][i] = 0.f;
-  }
-}
-
-// Merge the row groups of one wave (they differ in the lane bits above the group).
-template <int LPR, int G>
-__device__ __forceinline__ void merge_groups(HeadState<G>& st) {
-#pragma unroll
-  for (int off = LPR; off < 64; off <<= 1) {
-#pragma unroll
-    for (int j = 0; j < G; ++j) {
-      const float mo = __shfl_xor(st.m[j], off);
-      const float lo = __shfl_xor(st.l[j], off);
-      const float M = fmaxf(st.m[j], mo);
-      const float Ms = M == kNegInf ? 0.f : M;
-      const float ws = exp2_fast(st.m[j] - Ms);
-      const float wo = exp2_fast(mo - Ms);
-      st.l[j] = st.l[j] * ws + lo * wo;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float oo = __shfl_xor(st.o[j][i], off);
-        st.o[j][i] = st.o[j][i] * ws + oo * wo;
-      }
-      st.m[j] = M;
-    }
-  }
-}
-
-// Where a loop step's K/V pieces come from.  Both loaders are branch-free: a row
-// that must not be used still issues its load, but the load either touches no
-// memory (buffer load past the end of the resource returns zeros) or re-reads a
-// fixed in-bounds location, and its value is never used.
-//
-// BufferRows: one (sequence, head) region of the static cache; `off` is a byte
-// offset inside it, and kNoRow (past num_records) stands for "no row".
-// Cache policy of the K/V row loads: every row is read once, so the loads are
-// non-temporal (bit 1 of the buffer instruction's cache-policy operand; the
-// paged loads below use the non-temporal global form).  Measured: the static
-// fused step call drops from 48.8 to 41.9 us at batch 8.
-constexpr int kLoadNonTemporal = 2;
-
-struct BufferRows {
-  __amdgpu_buffer_rsrc_t k, v;
-  static constexpr uint32_t kNoRow = 0x80000000u;
-  __device__ BufferRows(const uint16_t* kbase, const uint16_t* vbase, uint32_t bytes)
-      : k(__builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(kbase), (short)0, (int)bytes,
-                                            0x00020000)),
-        v(__builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(vbase), (short)0, (int)bytes,
-                                            0x00020000)) {}
-  __device__ __forceinline__ void load(uint32_t off, uint4& kr, uint4& vr) const {
-    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-    const u32x4 a = __builtin_amdgcn_raw_buffer_load_b128(k, (int)off, 0, kLoadNonTemporal);
-    const u32x4 b = __builtin_amdgcn_raw_buffer_load_b128(v, (int)off, 0, kLoadNonTemporal);
-    kr = make_uint4(a[0], a[1], a[2], a[3]);
-    vr = make_uint4(b[0], b[1], b[2], b[3]);
-  }
-};
-
-// GlobalRows: the paged pool through 64-bit addresses; `off` is an element offset
-// from the pool base (0, an in-bounds location, for rows that are not used).
-struct GlobalRows {
-  const uint16_t* k;
-  const uint16_t* v;
-  __device__ __forceinline__ void load(size_t off, uint4& kr, uint4& vr) const {
-    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-    const u32x4 a = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(k + off));
-    const u32x4 b = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(v + off));
-    kr = make_uint4(a[0], a[1], a[2], a[3]);
-    vr = make_uint4(b[0], b[1], b[2], b[3]);
-  }
-};
-
-// One loop step's loads: U rows per lane group, K and V.  RowAt(t, ok) returns
-// the loader offset of row t (or the loader's "no row" value) and clears ok for
-// rows that must not be used; Patch(t, kr, vr) may then replace a row's values.
-template <int D, int U, typename Rows, typename RowAt, typename Patch>
-__device__ __forceinline__ void issue_rows(const Rows& rows, int base, int r1, int wave,
-                                           int slot, RowAt& row_at, Patch& patch,
-                                           uint4 (&kr)[U], uint4 (&vr)[U], bool (&ok)[U]) {
-  constexpr int RPW = 64 / (D / 8);
-#pragma unroll
-  for (int u = 0; u < U; ++u) {
-    const int t = base + (u * kWaves + wave) * RPW + slot;
-    ok[u] = t < r1;
-    rows.load(row_at(t, ok[u]), kr[u], vr[u]);
-    patch(t, kr[u], vr[u]);
-  }
-}
-
-struct NoPatch {
-  __device__ __forceinline__ void operator()(int, uint4&, uint4&) const {}
-};
-
-// One loop step's arithmetic: scores of the U rows for each of the G heads, then
-// the online-softmax update of (m, l, o).
-template <int D, int G, int U>
-__device__ __forceinline__ void consume_rows(const float (&q)[G][8], const uint4 (&kr)[U],
-                                             const uint4 (&vr)[U], const bool (&ok)[U],
-                                             HeadState<G>& st) {
-  constexpr int LPR = D / 8;
-  float s[G][U];
-#pragma unroll
-  for (int u = 0; u < U; ++u) {
-    float kf[8];
-    unpack8(kr[u], kf);
-#pragma unroll
-    for (int j = 0; j < G; ++j) {
-      float acc = 0.f;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) acc = fmaf(q[j][i], kf[i], acc);
-      acc = group_sum<LPR>(acc);
-      s[j][u] = ok[u] ? acc : kNegInf;
-    }
-  }
-#pragma unroll
-  for (int j = 0; j < G; ++j) {
-    float mnew = st.m[j];
-#pragma unroll
-    for (int u = 0; u < U; ++u) mnew = fmaxf(mnew, s[j][u]);
-    const float ms = mnew == kNegInf ? 0.f : mnew;
-    const float alpha = exp2_fast(st.m[j] - ms);
-    float psum = 0.f;
-    float p[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      p[u] = exp2_fast(s[j][u] - ms);
-      psum += p[u];
-    }
-    st.l[j] = st.l[j] * alpha + psum;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) st.o[j][i] *= alpha;
-    st.m[j] = mnew;
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      float vf[8];
-      unpack8(vr[u], vf);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) st.o[j][i] = fmaf(p[u], vf[i], st.o[j][i]);
-    }
-  }
-}
-
-// The row loop shared by the static and paged kernels, for exactly kSteps steps
-// (rows at or past r1 are cleared by RowAt).  Each step issues all of its 2U loads
-// (U rows per lane group, K and V) before using any; the steps are fully unrolled
-// with two register sets used in turn, so the loads of step s+1 are in flight
-// while step s is computed and, with no loop, the compiler waits on exactly the
-// loads each step needs.  q is pre-scaled by scale * log2(e).
-template <int D, int G, int U, int kSteps, typename Rows, typename RowAt, typename Patch>
-__device__ __forceinline__ void attend_rows_fixed(const Rows& rows, const float (&q)[G][8],
-                                                  int r0, int r1, int wave, int slot,
-                                                  RowAt row_at, Patch patch, HeadState<G>& st) {
-  constexpr int RPW = 64 / (D / 8);
-  constexpr int kStep = kWaves * RPW * U;
-  uint4 kr[2][U], vr[2][U];
-  bool ok[2][U];
-  issue_rows<D, U>(rows, r0, r1, wave, slot, row_at, patch, kr[0], vr[0], ok[0]);
-#pragma unroll
-  for (int s = 0; s < kSteps; ++s) {
-    if (s + 1 < kSteps)
-      issue_rows<D, U>(rows, r0 + (s + 1) * kStep, r1, wave, slot, row_at, patch,
-                       kr[(s + 1) & 1], vr[(s + 1) & 1], ok[(s + 1) & 1]);
-    consume_rows<D, G, U>(q, kr[s & 1], vr[s & 1], ok[s & 1], st);
-  }
-}
-
-// Workspace of one decode call (fp32):
-//   o   [units * G][max_splits][D]   normalised partial outputs o / l
-//   lse [units * G][max_splits]      log2-sum-exp of each partial (-inf if empty)
-struct Workspace {
-  float* o;
-  float* lse;
-};
-
-__host__ __device__ inline size_t ws_floats(size_t heads, int max_splits, int D) {
-  return heads * (size_t)max_splits * (size_t)(D + 1);
-}
-
-// Log-sum-exp merge of one head's n <= kMaxSplits partials by the whole
-// workgroup, in one memory round trip: every thread issues its log2-sum-exp load
-// (thread j holds split j) together with its first kMergePre partial loads (the
-// D/4 float4 columns are shared among kThreads / (D/4) split groups); the max and
-// the weights 2^(lse_j - max) go through LDS, and the groups are summed there.
-constexpr int kMergePre = 4;
-
-template <int D>
-__device__ __forceinline__ void merge_head(const float* __restrict__ lp,
-                                           const float* __restrict__ op, int n,
-                                           float* __restrict__ outp, float* __restrict__ lsep) {
-  static_assert(kMaxSplits <= kThreads, "one split per thread");
-  constexpr int kCols = D / 4;
-  constexpr int kGroups = kThreads / kCols;
-  __shared__ float sm_w[kMaxSplits];
-  __shared__ float sm_part[2][kWaves];
-  __shared__ float4 sm_red[kThreads];
-  const int tid = threadIdx.x;
-  const int c = tid % kCols;
-  const int grp = tid / kCols;
-  const float* cp = op + c * 4;
-  const float x = tid < n ? lp[tid] : kNegInf;
-  float4 pre[kMergePre];
-#pragma unroll
-  for (int k = 0; k < kMergePre; ++k) {
-    const int j = grp + k * kGroups;
-    pre[k] = j < n ? *reinterpret_cast<const float4*>(cp + (size_t)j * D)
-                   : make_float4(0.f, 0.f, 0.f, 0.f);
-  }
-  float v = x;
-  for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
-  if ((tid & 63) == 0) sm_part[0][tid >> 6] = v;
-  __syncthreads();
-  const float M = fmaxf(fmaxf(sm_part[0][0], sm_part[0][1]), fmaxf(sm_part[0][2], sm_part[0][3]));
-  const float w = (tid < n && M != kNegInf) ? exp2_fast(x - M) : 0.f;
-  if (tid < kMaxSplits) sm_w[tid] = w;
-  float den_part = w;
-  for (int off = 32; off > 0; off >>= 1) den_part += __shfl_xor(den_part, off);
-  if ((tid & 63) == 0) sm_part[1][tid >> 6] = den_part;
-  __syncthreads();
-  const float den = sm_part[1][0] + sm_part[1][1] + sm_part[1][2] + sm_part[1][3];
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
-  for (int k = 0; k < kMergePre; ++k) {
-    const int j = grp + k * kGroups;
-    const float wj = j < n ? sm_w[j] : 0.f;
-    acc.x += wj * pre[k].x; acc.y += wj * pre[k].y; acc.z += wj * pre[k].z; acc.w += wj * pre[k].w;
-  }
-  for (int j = grp + kMergePre * kGroups; j < n; j += kGroups) {
-    const float wj = sm_w[j];
-    const float4 y = *reinterpret_cast<const float4*>(cp + (size_t)j * D);
-    acc.x += wj * y.x; acc.y += wj * y.y; acc.z += wj * y.z; acc.w += wj * y.w;
-  }
-  sm_red[tid] = acc;
-  __syncthreads();
-  if (tid < kCols) {
-#pragma unroll
-    for (int g = 1; g < kGroups; ++g) {
-      const float4 y = sm_red[tid + g * kCols];
-      acc.x += y.x; acc.y += y.y; acc.z += y.z; acc.w += y.w;
-    }
-    float4 r = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (M != kNegInf) {
-      const float inv = 1.f / den;
-      r = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
-    }
-    *reinterpret_cast<float4*>(outp + c * 4) = r;
-    if (lsep && tid == 0) *lsep = M == kNegInf ? kNegInf : (M + __log2f(den)) * kLn2;
-  }
-  __syncthreads();
-}
-
-// End of a split: combine the waves through LDS, then write the output directly
-// (a sequence that fits one split) or this split's partial for merge_kernel.
-// (The splits are not merged in the last one to finish: publishing the partials
-// to another XCD takes a device-scope release that writes back the L2, or
-// device-coherent atomics; both measured far slower than a second launch.)
-template <int D, int G>
-__device__ __forceinline__ void finish_split(const HeadState<G>& st, int lane, int wave,
-                                             const Workspace& ws, size_t head0, int split,
-                                             int n, int max_splits, float* __restrict__ out,
-                                             float* __restrict__ lse) {
-  constexpr int LPR = D / 8;
-  __shared__ float sm_o[kWaves][G][D];
-  __shared__ float sm_m[kWaves][G];
-  __shared__ float sm_l[kWaves][G];
-  if (lane < LPR) {
-#pragma unroll
-    for (int j = 0; j < G; ++j) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) sm_o[wave][j][lane * 8 + i] = st.o[j][i];
-      if (lane == 0) {
-        sm_m[wave][j] = st.m[j];
-        sm_l[wave][j] = st.l[j];
-      }
-    }
-  }
-  __syncthreads();
-  for (int idx = threadIdx.x; idx < G * D; idx += kThreads) {
-    const int j = idx / D;
-    const int d = idx - j * D;
-    float M = kNegInf;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm_m[w][j]);
-    float val = 0.f, lse2 = kNegInf;
-    if (M != kNegInf) {
-      float num = 0.f, den = 0.f;
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
-        const float wt = exp2_fast(sm_m[w][j] - M);
-        num += wt * sm_o[w][j][d];
-        den += wt * sm_l[w][j];
-      }
-      val = num / den;
-      lse2 = M + __log2f(den);
-    }
-    if (n == 1) {
-      out[(head0 + j) * D + d] = val;
-      if (lse && d == 0) lse[head0 + j] = lse2 * kLn2;
-    } else {
-      const size_t row = (head0 + j) * max_splits + split;
-      ws.o[row * D + d] = val;
-      if (d == 0) ws.lse[row] = lse2;
-    }
-  }
-}
-
 // ---------------------------------------------------------------- static layout
-constexpr int kStaticChunkMax = 256;  // rows per split of the static layout, at most
 
 // Split pass of decode_attn_static and, with kAppend, of decode_step_static.
 // A split is kSteps steps of U rows per lane group (chunk rows).  Workgroups are
@@ -480,223 +115,6 @@ static_decode_kernel(const float* __restrict__ q, uint16_t* __restrict__ k_cache
   HeadState<1> st;
   init_state(st);
   attend_rows_fixed<D, 1, U, kSteps>(rows, qr, r0, r1, wave, slot, row_at, NoPatch{}, st);
-  merge_groups<LPR, 1>(st);
-  finish_split<D, 1>(st, lane, wave, ws, (size_t)bh, split, n, max_splits, out, lse);
-}
-
-// ---------------------------------------------------------- static layout, FP8
-// Split pass of decode_attn_static_fp8: the cache holds E4M3 codes (one byte per
-// element, [B, H, cap, D]) and one power-of-two fp32 scale per row for K and for V
-// ([B, H, cap]).  A lane covers 8 elements of a row as in the bf16 kernel (D / 8
-// lanes per row), now 8 bytes: K and V codes arrive by 8-byte buffer loads and
-// are widened by the E4M3 conversion instruction (two codes per instruction).
-// The row scales are read like the mask, one per lane for each 64-row block of the
-// split, and a row's scale is taken from the lane that holds it: the K scale
-// multiplies the row's score, the V scale its weight in O (the sum of weights
-// uses the unscaled weight).
-typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ void unpack8_fp8(const u32x2_t& w, float (&f)[8]) {
-  typedef float f2_t __attribute__((ext_vector_type(2)));
-  const f2_t a = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[0], false);
-  const f2_t b = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[0], true);
-  const f2_t c = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[1], false);
-  const f2_t d = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[1], true);
-  f[0] = a[0]; f[1] = a[1]; f[2] = b[0]; f[3] = b[1];
-  f[4] = c[0]; f[5] = c[1]; f[6] = d[0]; f[7] = d[1];
-}
-
-//
-// With kAppend (decode_step_static_fp8) the split that owns p = write_pos[b]
-// first quantises the new token's K and V rows (as kv_append_fp8 does) in the
-// lanes that later consume row p; they store codes and scales and keep both in
-// registers for that row, and p is attended whatever its mask entry says.
-template <int D, int U, int kSteps, bool kAppend>
-__global__ void __launch_bounds__(kThreads)
-static_decode_fp8_kernel(const float* __restrict__ q, uint8_t* __restrict__ k_codes,
-                         uint8_t* __restrict__ v_codes, float* __restrict__ k_scale,
-                         float* __restrict__ v_scale, int32_t* __restrict__ mask,
-                         const int32_t* __restrict__ valid_len, const uint16_t* __restrict__ k_new,
-                         const uint16_t* __restrict__ v_new, const int32_t* __restrict__ write_pos,
-                         int H, int cap, float scale_log2, int chunk, int units, Workspace ws,
-                         float* __restrict__ out, float* __restrict__ lse, int32_t* err_flag) {
-  constexpr int LPR = D / 8;
-  constexpr int RPW = 64 / LPR;
-  constexpr int kStep = kWaves * RPW * U;             // rows per step
-  constexpr int kBallots = (kSteps * kStep + 63) / 64;
-  // the rows a wave loads at once (kWaves * RPW per u) tile 64-row words, so a
-  // lane group's row never leaves the word (s kStep + u kWaves RPW) / 64
-  static_assert(64 % (kWaves * RPW) == 0, "row words");
-  const int split = blockIdx.x / units;
-  const int bh = blockIdx.x - split * units;
-  const int max_splits = gridDim.x / units;
-  const int b = bh / H;
-  const int h = bh - b * H;
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int sub = lane % LPR;
-  const int slot = lane / LPR;
-  const int r0 = split * chunk;
-  const int32_t* mrow = mask ? mask + (size_t)b * cap : nullptr;
-  const float* ksrow = k_scale + (size_t)bh * cap;
-  const float* vsrow = v_scale + (size_t)bh * cap;
-  // every load before any wait: valid length, query, and per 64-row block of the
-  // split the mask entry and both scales of row r0 + 64 k + lane (clamped)
-  const int Lraw = valid_len ? valid_len[b] : cap;
-  int p = kAppend ? write_pos[b] : -1;
-  const float4* qp = reinterpret_cast<const float4*>(q + (size_t)bh * D + sub * 8);
-  const float4 qa = qp[0], qc = qp[1];
-  int32_t mv[kBallots];
-  float ksv[kBallots], vsv[kBallots];
-#pragma unroll
-  for (int k = 0; k < kBallots; ++k) {
-    const int r = min(r0 + 64 * k + lane, cap - 1);
-    mv[k] = mrow ? mrow[r] : 1;
-    ksv[k] = ksrow[r];
-    vsv[k] = vsrow[r];
-  }
-  const bool report = split == 0 && h == 0 && threadIdx.x == 0;
-  // the appended row's codes and scales, in the lanes that own it
-  float new_ks = 0.f, new_vs = 0.f;
-  u32x2_t new_kw = {0u, 0u}, new_vw = {0u, 0u};
-  if constexpr (kAppend) {
-    if (p < 0 || p >= cap) {
-      if (report) raise_flag(err_flag, 2);
-      p = -1;
-    } else if (p / chunk == split) {
-      const int o = p - r0;
-      if (wave == (o / RPW) % kWaves && slot == o % RPW) {
-        const uint4 kn = load16(k_new + (size_t)bh * D + sub * 8);
-        const uint4 vn = load16(v_new + (size_t)bh * D + sub * 8);
-        float kx[8], vx[8];
-        unpack8(kn, kx);
-        unpack8(vn, vx);
-        float ka = 0.f, va = 0.f;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          ka = fmaxf(ka, fabsf(kx[i]));
-          va = fmaxf(va, fabsf(vx[i]));
-        }
-        ka = group_max<LPR>(ka);
-        va = group_max<LPR>(va);
-        const int ke = e4m3_exponent_for(ka), ve = e4m3_exponent_for(va);
-        u32x2_t kw = {0u, 0u}, vw = {0u, 0u};
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          kw[i >> 2] |= e4m3_code(ldexpf(kx[i], -ke)) << (8 * (i & 3));
-          vw[i >> 2] |= e4m3_code(ldexpf(vx[i], -ve)) << (8 * (i & 3));
-        }
-        const size_t at = ((size_t)bh * cap + p) * D + (size_t)sub * 8;
-        *reinterpret_cast<u32x2_t*>(k_codes + at) = kw;
-        *reinterpret_cast<u32x2_t*>(v_codes + at) = vw;
-        new_kw = kw;
-        new_vw = vw;
-        new_ks = ldexpf(1.f, ke);
-        new_vs = ldexpf(1.f, ve);
-        if (sub == 0) {
-          k_scale[(size_t)bh * cap + p] = new_ks;
-          v_scale[(size_t)bh * cap + p] = new_vs;
-        }
-      }
-      if (mask && h == 0 && threadIdx.x == 0) mask[(size_t)b * cap + p] = 1;
-    } else {
-      p = -1;  // another split holds the new row
-    }
-  }
-  int L = Lraw;
-  if (L < 0 || L > cap) {
-    if (report) raise_flag(err_flag, 16);
-    L = L < 0 ? 0 : cap;
-  }
-  const int n = L > 0 ? (L + chunk - 1) / chunk : 1;
-  if (split >= n) return;
-  const int r1 = min(r0 + chunk, L);
-  float qr[8];
-  qr[0] = qa.x * scale_log2; qr[1] = qa.y * scale_log2;
-  qr[2] = qa.z * scale_log2; qr[3] = qa.w * scale_log2;
-  qr[4] = qc.x * scale_log2; qr[5] = qc.y * scale_log2;
-  qr[6] = qc.z * scale_log2; qr[7] = qc.w * scale_log2;
-  uint64_t bits[kBallots];
-#pragma unroll
-  for (int k = 0; k < kBallots; ++k) bits[k] = __ballot(r0 + 64 * k + lane < r1 && mv[k] != 0);
-  const __amdgpu_buffer_rsrc_t kr_rs = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint8_t*>(k_codes) + (size_t)bh * cap * D, (short)0, cap * D, 0x00020000);
-  const __amdgpu_buffer_rsrc_t vr_rs = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint8_t*>(v_codes) + (size_t)bh * cap * D, (short)0, cap * D, 0x00020000);
-  const uint32_t lane_off = (uint32_t)sub * 8;
-  float m = kNegInf, l = 0.f, o[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) o[i] = 0.f;
-  // rows of step s for this lane group: t = r0 + s kStep + (u kWaves + wave) RPW + slot
-  auto issue = [&](int s, u32x2_t (&kw)[U], u32x2_t (&vw)[U], bool (&ok)[U]) {
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int o_row = s * kStep + (u * kWaves + wave) * RPW + slot;  // row - r0
-      const int word = (s * kStep + u * kWaves * RPW) >> 6;            // == o_row >> 6
-      ok[u] = r0 + o_row < r1 &&
-              (((bits[word] >> (o_row - 64 * word)) & 1ull) || r0 + o_row == p);
-      const uint32_t off = ok[u] ? (uint32_t)(r0 + o_row) * D + lane_off : BufferRows::kNoRow;
-      kw[u] = __builtin_amdgcn_raw_buffer_load_b64(kr_rs, (int)off, 0, kLoadNonTemporal);
-      vw[u] = __builtin_amdgcn_raw_buffer_load_b64(vr_rs, (int)off, 0, kLoadNonTemporal);
-    }
-  };
-  auto consume = [&](int s, const u32x2_t (&kw)[U], const u32x2_t (&vw)[U], const bool (&ok)[U]) {
-    float sc[U], ws_v[U];
-    bool fresh[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int o_row = s * kStep + (u * kWaves + wave) * RPW + slot;
-      // the appended row comes from registers, never from a load that follows
-      // this lane's own store
-      fresh[u] = kAppend && r0 + o_row == p;
-      float kf[8];
-      unpack8_fp8(fresh[u] ? new_kw : kw[u], kf);
-      float acc = 0.f;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) acc = fmaf(qr[i], kf[i], acc);
-      acc = group_sum<LPR>(acc);
-      const int word = (s * kStep + u * kWaves * RPW) >> 6;            // == o_row >> 6
-      // both shuffles run in every lane (a lane reads another lane's scale, so
-      // none may sit out), then the appended row takes its own
-      const float ksh = __shfl(ksv[word], o_row - 64 * word);
-      const float vsh = __shfl(vsv[word], o_row - 64 * word);
-      const float ks = fresh[u] ? new_ks : ksh;
-      ws_v[u] = fresh[u] ? new_vs : vsh;
-      sc[u] = ok[u] ? acc * ks : kNegInf;
-    }
-    float mnew = m;
-#pragma unroll
-    for (int u = 0; u < U; ++u) mnew = fmaxf(mnew, sc[u]);
-    const float ms = mnew == kNegInf ? 0.f : mnew;
-    const float alpha = exp2_fast(m - ms);
-    l *= alpha;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) o[i] *= alpha;
-    m = mnew;
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const float p = exp2_fast(sc[u] - ms);
-      l += p;
-      const float pv = p * ws_v[u];
-      float vf[8];
-      unpack8_fp8(fresh[u] ? new_vw : vw[u], vf);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) o[i] = fmaf(pv, vf[i], o[i]);
-    }
-  };
-  u32x2_t kw[2][U], vw[2][U];
-  bool ok[2][U];
-  issue(0, kw[0], vw[0], ok[0]);
-#pragma unroll
-  for (int s = 0; s < kSteps; ++s) {
-    if (s + 1 < kSteps) issue(s + 1, kw[(s + 1) & 1], vw[(s + 1) & 1], ok[(s + 1) & 1]);
-    consume(s, kw[s & 1], vw[s & 1], ok[s & 1]);
-  }
-  HeadState<1> st;
-  st.m[0] = m;
-  st.l[0] = l;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) st.o[0][i] = o[i];
   merge_groups<LPR, 1>(st);
   finish_split<D, 1>(st, lane, wave, ws, (size_t)bh, split, n, max_splits, out, lse);
 }
@@ -982,6 +400,18 @@ merge_kernel(Workspace ws, int heads, int chunk, int max_splits, int mode,
                 out + (size_t)bh * D, lse ? lse + bh : nullptr);
 }
 
+hipError_t launch_static_merge(const Workspace& w, int B, int H, int D, int chunk,
+                               int max_splits, const int32_t* valid_len, int cap, float* out,
+                               float* lse, hipStream_t stream) {
+  if (D == 128)
+    hipLaunchKernelGGL(merge_kernel<128>, dim3(B * H), dim3(kThreads), 0, stream, w, H, chunk,
+                       max_splits, 0, valid_len, cap, nullptr, nullptr, 1, 0, 0, out, lse);
+  else
+    hipLaunchKernelGGL(merge_kernel<64>, dim3(B * H), dim3(kThreads), 0, stream, w, H, chunk,
+                       max_splits, 0, valid_len, cap, nullptr, nullptr, 1, 0, 0, out, lse);
+  return hipGetLastError();
+}
+
 // ------------------------------------------------------------------- planning
 static int round_up(int x, int m) { return (x + m - 1) / m * m; }
 
@@ -1014,12 +444,6 @@ size_t static_workspace_bytes(int B, int H, int cap, int D) {
   return ws_floats((size_t)B * H, splits, D) * sizeof(float);
 }
 
-static Workspace carve(void* ws, size_t heads, int max_splits, int D) {
-  Workspace w;
-  w.o = static_cast<float*>(ws);
-  w.lse = w.o + heads * (size_t)max_splits * D;
-  return w;
-}
 
 template <int D, int kSteps, bool kAppend>
 static void launch_static_k(const float* q, void* k_cache, void* v_cache, int32_t* mask,
@@ -1078,62 +502,6 @@ hipError_t launch_decode_static(const float* q, void* k_cache, void* v_cache, in
       launch_static_d<64, false>(q, k_cache, v_cache, mask, valid_len, k_new, v_new, write_pos,
                                  B, H, cap, scale, out, lse, ws, plan, err_flag, stream);
   }
-  return hipGetLastError();
-}
-
-template <int D, int kSteps>
-static void launch_static_fp8_k(const float* q, void* k_codes, void* v_codes, float* k_scale,
-                                float* v_scale, int32_t* mask, const int32_t* valid_len,
-                                const void* k_new, const void* v_new, const int32_t* write_pos,
-                                int B, int H, int cap, float scale, float* out, float* lse,
-                                const Workspace& w, const SplitPlan& plan, int32_t* err_flag,
-                                hipStream_t stream) {
-  const dim3 grid((unsigned)(B * H * plan.max_splits));
-  auto* kc = static_cast<uint8_t*>(k_codes);
-  auto* vc = static_cast<uint8_t*>(v_codes);
-  auto* kn = static_cast<const uint16_t*>(k_new);
-  auto* vn = static_cast<const uint16_t*>(v_new);
-  if (write_pos)
-    hipLaunchKernelGGL((static_decode_fp8_kernel<D, 4, kSteps, true>), grid, dim3(kThreads), 0,
-                       stream, q, kc, vc, k_scale, v_scale, mask, valid_len, kn, vn, write_pos, H,
-                       cap, scale * kLog2e, plan.chunk, B * H, w, out, lse, err_flag);
-  else
-    hipLaunchKernelGGL((static_decode_fp8_kernel<D, 4, kSteps, false>), grid, dim3(kThreads), 0,
-                       stream, q, kc, vc, k_scale, v_scale, mask, valid_len, kn, vn, write_pos, H,
-                       cap, scale * kLog2e, plan.chunk, B * H, w, out, lse, err_flag);
-}
-
-hipError_t launch_decode_static_fp8(const float* q, void* k_codes, void* v_codes, float* k_scale,
-                                    float* v_scale, int32_t* mask, const int32_t* valid_len,
-                                    const void* k_new, const void* v_new,
-                                    const int32_t* write_pos, int B, int H, int cap, int D,
-                                    float scale, float* out, float* lse, void* ws,
-                                    const SplitPlan& plan, int32_t* err_flag, hipStream_t stream) {
-  const Workspace w = carve(ws, (size_t)B * H, plan.max_splits, D);
-#define DAKV_FP8(DD)                                                                          \
-  do {                                                                                        \
-    constexpr int kStep = kWaves * (64 / (DD / 8)) * 4;                                       \
-    const int steps = (plan.chunk + kStep - 1) / kStep;                                       \
-    if (steps <= 1)                                                                           \
-      launch_static_fp8_k<DD, 1>(q, k_codes, v_codes, k_scale, v_scale, mask, valid_len, k_new, \
-                                 v_new, write_pos, B, H, cap, scale, out, lse, w, plan,       \
-                                 err_flag, stream);                                           \
-    else if (steps <= 2)                                                                      \
-      launch_static_fp8_k<DD, 2>(q, k_codes, v_codes, k_scale, v_scale, mask, valid_len, k_new, \
-                                 v_new, write_pos, B, H, cap, scale, out, lse, w, plan,       \
-                                 err_flag, stream);                                           \
-    else                                                                                      \
-      launch_static_fp8_k<DD, 4>(q, k_codes, v_codes, k_scale, v_scale, mask, valid_len, k_new, \
-                                 v_new, write_pos, B, H, cap, scale, out, lse, w, plan,       \
-                                 err_flag, stream);                                           \
-    if (plan.max_splits > 1)                                                                  \
-      hipLaunchKernelGGL(merge_kernel<DD>, dim3(B * H), dim3(kThreads), 0, stream, w, H,      \
-                         plan.chunk, plan.max_splits, 0, valid_len, cap, nullptr, nullptr, 1, \
-                         0, 0, out, lse);                                                     \
-  } while (0)
-  if (D == 128) DAKV_FP8(128);
-  else DAKV_FP8(64);
-#undef DAKV_FP8
   return hipGetLastError();
 }
 

@@ -1,0 +1,340 @@
+// The FP8 KV cache of the static layout: E4M3 codes (one byte per element) with a
+// power-of-two fp32 scale per cached row, for K and for V.  kv_append_fp8
+// quantises a new token's rows; the split pass reads codes and scales and feeds
+// the same split-K machinery (workspace, merge) as the bf16 cache.
+#include "split_common.hpp"
+
+namespace dakv {
+
+// ---------------------------------------------------------------------------
+// kv_append_fp8: the new token's K and V rows are quantised to E4M3 codes with a
+// power-of-two scale per row and stored at row write_pos[b].  One wave per
+// (sequence, head, K or V): the row's largest magnitude comes from a wave
+// reduction; the scale is 2^e with e the smallest integer for which
+// max|x| <= 448 * 2^e (from the exponent and fraction of max|x|, exactly); each
+// value x * 2^-e (exact) is rounded to the nearest E4M3 value, ties to the even
+// code, zero results as the +0 code.
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256)
+kv_append_fp8_kernel(uint8_t* __restrict__ k_codes, uint8_t* __restrict__ v_codes,
+                     float* __restrict__ k_scale, float* __restrict__ v_scale,
+                     const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new,
+                     const int32_t* __restrict__ write_pos, int32_t* __restrict__ mask, int H,
+                     int cap, int D, int32_t* err_flag) {
+  const int b = blockIdx.y;
+  const int unit = blockIdx.x * 4 + (threadIdx.x >> 6);  // (head, K or V)
+  const int lane = threadIdx.x & 63;
+  if (unit >= 2 * H) return;
+  const int h = unit >> 1;
+  const bool is_v = unit & 1;
+  const int pos = write_pos[b];
+  if (pos < 0 || pos >= cap) {
+    if (unit == 0 && lane == 0) raise_flag(err_flag, 2);
+    return;
+  }
+  const uint16_t* src = (is_v ? v_new : k_new) + ((size_t)b * H + h) * D;
+  const size_t row = ((size_t)b * H + h) * cap + pos;
+  uint8_t* dst = (is_v ? v_codes : k_codes) + row * D;
+  float x[4];
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {            // D <= 256: at most 4 values per lane
+    const int d = lane + 64 * i;
+    x[i] = d < D ? __uint_as_float((uint32_t)src[d] << 16) : 0.f;
+    amax = fmaxf(amax, fabsf(x[i]));
+  }
+  for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+  const int e = e4m3_exponent_for(amax);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int d = lane + 64 * i;
+    if (d < D) dst[d] = (uint8_t)e4m3_code(ldexpf(x[i], -e));
+  }
+  if (lane == 0) (is_v ? v_scale : k_scale)[row] = ldexpf(1.f, e);
+  if (mask && unit == 0 && lane == 0) mask[(size_t)b * cap + pos] = 1;
+}
+
+hipError_t launch_kv_append_fp8(void* k_codes, void* v_codes, float* k_scale, float* v_scale,
+                                const void* k_new, const void* v_new, const int32_t* write_pos,
+                                int32_t* mask, int B, int H, int cap, int D, int32_t* err_flag,
+                                hipStream_t stream) {
+  hipLaunchKernelGGL(kv_append_fp8_kernel, dim3((2 * H + 3) / 4, B), dim3(256), 0, stream,
+                     static_cast<uint8_t*>(k_codes), static_cast<uint8_t*>(v_codes), k_scale,
+                     v_scale, static_cast<const uint16_t*>(k_new),
+                     static_cast<const uint16_t*>(v_new), write_pos, mask, H, cap, D, err_flag);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------- static layout, FP8
+// Split pass of decode_attn_static_fp8: the cache holds E4M3 codes (one byte per
+// element, [B, H, cap, D]) and one power-of-two fp32 scale per row for K and for V
+// ([B, H, cap]).  A lane covers 8 elements of a row as in the bf16 kernel (D / 8
+// lanes per row), now 8 bytes: K and V codes arrive by 8-byte buffer loads and
+// are widened by the E4M3 conversion instruction (two codes per instruction).
+// The row scales are read like the mask, one per lane for each 64-row block of the
+// split, and a row's scale is taken from the lane that holds it: the K scale
+// multiplies the row's score, the V scale its weight in O (the sum of weights
+// uses the unscaled weight).
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ void unpack8_fp8(const u32x2_t& w, float (&f)[8]) {
+  typedef float f2_t __attribute__((ext_vector_type(2)));
+  const f2_t a = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[0], false);
+  const f2_t b = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[0], true);
+  const f2_t c = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[1], false);
+  const f2_t d = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[1], true);
+  f[0] = a[0]; f[1] = a[1]; f[2] = b[0]; f[3] = b[1];
+  f[4] = c[0]; f[5] = c[1]; f[6] = d[0]; f[7] = d[1];
+}
+
+//
+// With kAppend (decode_step_static_fp8) the split that owns p = write_pos[b]
+// first quantises the new token's K and V rows (as kv_append_fp8 does) in the
+// lanes that later consume row p; they store codes and scales and keep both in
+// registers for that row, and p is attended whatever its mask entry says.
+template <int D, int U, int kSteps, bool kAppend>
+__global__ void __launch_bounds__(kThreads)
+static_decode_fp8_kernel(const float* __restrict__ q, uint8_t* __restrict__ k_codes,
+                         uint8_t* __restrict__ v_codes, float* __restrict__ k_scale,
+                         float* __restrict__ v_scale, int32_t* __restrict__ mask,
+                         const int32_t* __restrict__ valid_len, const uint16_t* __restrict__ k_new,
+                         const uint16_t* __restrict__ v_new, const int32_t* __restrict__ write_pos,
+                         int H, int cap, float scale_log2, int chunk, int units, Workspace ws,
+                         float* __restrict__ out, float* __restrict__ lse, int32_t* err_flag) {
+  constexpr int LPR = D / 8;
+  constexpr int RPW = 64 / LPR;
+  constexpr int kStep = kWaves * RPW * U;             // rows per step
+  constexpr int kBallots = (kSteps * kStep + 63) / 64;
+  // the rows a wave loads at once (kWaves * RPW per u) tile 64-row words, so a
+  // lane group's row never leaves the word (s kStep + u kWaves RPW) / 64
+  static_assert(64 % (kWaves * RPW) == 0, "row words");
+  const int split = blockIdx.x / units;
+  const int bh = blockIdx.x - split * units;
+  const int max_splits = gridDim.x / units;
+  const int b = bh / H;
+  const int h = bh - b * H;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int sub = lane % LPR;
+  const int slot = lane / LPR;
+  const int r0 = split * chunk;
+  const int32_t* mrow = mask ? mask + (size_t)b * cap : nullptr;
+  const float* ksrow = k_scale + (size_t)bh * cap;
+  const float* vsrow = v_scale + (size_t)bh * cap;
+  // every load before any wait: valid length, query, and per 64-row block of the
+  // split the mask entry and both scales of row r0 + 64 k + lane (clamped)
+  const int Lraw = valid_len ? valid_len[b] : cap;
+  int p = kAppend ? write_pos[b] : -1;
+  const float4* qp = reinterpret_cast<const float4*>(q + (size_t)bh * D + sub * 8);
+  const float4 qa = qp[0], qc = qp[1];
+  int32_t mv[kBallots];
+  float ksv[kBallots], vsv[kBallots];
+#pragma unroll
+  for (int k = 0; k < kBallots; ++k) {
+    const int r = min(r0 + 64 * k + lane, cap - 1);
+    mv[k] = mrow ? mrow[r] : 1;
+    ksv[k] = ksrow[r];
+    vsv[k] = vsrow[r];
+  }
+  const bool report = split == 0 && h == 0 && threadIdx.x == 0;
+  // the appended row's codes and scales, in the lanes that own it
+  float new_ks = 0.f, new_vs = 0.f;
+  u32x2_t new_kw = {0u, 0u}, new_vw = {0u, 0u};
+  if constexpr (kAppend) {
+    if (p < 0 || p >= cap) {
+      if (report) raise_flag(err_flag, 2);
+      p = -1;
+    } else if (p / chunk == split) {
+      const int o = p - r0;
+      if (wave == (o / RPW) % kWaves && slot == o % RPW) {
+        const uint4 kn = load16(k_new + (size_t)bh * D + sub * 8);
+        const uint4 vn = load16(v_new + (size_t)bh * D + sub * 8);
+        float kx[8], vx[8];
+        unpack8(kn, kx);
+        unpack8(vn, vx);
+        float ka = 0.f, va = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          ka = fmaxf(ka, fabsf(kx[i]));
+          va = fmaxf(va, fabsf(vx[i]));
+        }
+        ka = group_max<LPR>(ka);
+        va = group_max<LPR>(va);
+        const int ke = e4m3_exponent_for(ka), ve = e4m3_exponent_for(va);
+        u32x2_t kw = {0u, 0u}, vw = {0u, 0u};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          kw[i >> 2] |= e4m3_code(ldexpf(kx[i], -ke)) << (8 * (i & 3));
+          vw[i >> 2] |= e4m3_code(ldexpf(vx[i], -ve)) << (8 * (i & 3));
+        }
+        const size_t at = ((size_t)bh * cap + p) * D + (size_t)sub * 8;
+        *reinterpret_cast<u32x2_t*>(k_codes + at) = kw;
+        *reinterpret_cast<u32x2_t*>(v_codes + at) = vw;
+        new_kw = kw;
+        new_vw = vw;
+        new_ks = ldexpf(1.f, ke);
+        new_vs = ldexpf(1.f, ve);
+        if (sub == 0) {
+          k_scale[(size_t)bh * cap + p] = new_ks;
+          v_scale[(size_t)bh * cap + p] = new_vs;
+        }
+      }
+      if (mask && h == 0 && threadIdx.x == 0) mask[(size_t)b * cap + p] = 1;
+    } else {
+      p = -1;  // another split holds the new row
+    }
+  }
+  int L = Lraw;
+  if (L < 0 || L > cap) {
+    if (report) raise_flag(err_flag, 16);
+    L = L < 0 ? 0 : cap;
+  }
+  const int n = L > 0 ? (L + chunk - 1) / chunk : 1;
+  if (split >= n) return;
+  const int r1 = min(r0 + chunk, L);
+  float qr[8];
+  qr[0] = qa.x * scale_log2; qr[1] = qa.y * scale_log2;
+  qr[2] = qa.z * scale_log2; qr[3] = qa.w * scale_log2;
+  qr[4] = qc.x * scale_log2; qr[5] = qc.y * scale_log2;
+  qr[6] = qc.z * scale_log2; qr[7] = qc.w * scale_log2;
+  uint64_t bits[kBallots];
+#pragma unroll
+  for (int k = 0; k < kBallots; ++k) bits[k] = __ballot(r0 + 64 * k + lane < r1 && mv[k] != 0);
+  const __amdgpu_buffer_rsrc_t kr_rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(k_codes) + (size_t)bh * cap * D, (short)0, cap * D, 0x00020000);
+  const __amdgpu_buffer_rsrc_t vr_rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(v_codes) + (size_t)bh * cap * D, (short)0, cap * D, 0x00020000);
+  const uint32_t lane_off = (uint32_t)sub * 8;
+  float m = kNegInf, l = 0.f, o[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) o[i] = 0.f;
+  // rows of step s for this lane group: t = r0 + s kStep + (u kWaves + wave) RPW + slot
+  auto issue = [&](int s, u32x2_t (&kw)[U], u32x2_t (&vw)[U], bool (&ok)[U]) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int o_row = s * kStep + (u * kWaves + wave) * RPW + slot;  // row - r0
+      const int word = (s * kStep + u * kWaves * RPW) >> 6;            // == o_row >> 6
+      ok[u] = r0 + o_row < r1 &&
+              (((bits[word] >> (o_row - 64 * word)) & 1ull) || r0 + o_row == p);
+      const uint32_t off = ok[u] ? (uint32_t)(r0 + o_row) * D + lane_off : BufferRows::kNoRow;
+      kw[u] = __builtin_amdgcn_raw_buffer_load_b64(kr_rs, (int)off, 0, kLoadNonTemporal);
+      vw[u] = __builtin_amdgcn_raw_buffer_load_b64(vr_rs, (int)off, 0, kLoadNonTemporal);
+    }
+  };
+  auto consume = [&](int s, const u32x2_t (&kw)[U], const u32x2_t (&vw)[U], const bool (&ok)[U]) {
+    float sc[U], ws_v[U];
+    bool fresh[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int o_row = s * kStep + (u * kWaves + wave) * RPW + slot;
+      // the appended row comes from registers, never from a load that follows
+      // this lane's own store
+      fresh[u] = kAppend && r0 + o_row == p;
+      float kf[8];
+      unpack8_fp8(fresh[u] ? new_kw : kw[u], kf);
+      float acc = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc = fmaf(qr[i], kf[i], acc);
+      acc = group_sum<LPR>(acc);
+      const int word = (s * kStep + u * kWaves * RPW) >> 6;            // == o_row >> 6
+      // both shuffles run in every lane (a lane reads another lane's scale, so
+      // none may sit out), then the appended row takes its own
+      const float ksh = __shfl(ksv[word], o_row - 64 * word);
+      const float vsh = __shfl(vsv[word], o_row - 64 * word);
+      const float ks = fresh[u] ? new_ks : ksh;
+      ws_v[u] = fresh[u] ? new_vs : vsh;
+      sc[u] = ok[u] ? acc * ks : kNegInf;
+    }
+    float mnew = m;
+#pragma unroll
+    for (int u = 0; u < U; ++u) mnew = fmaxf(mnew, sc[u]);
+    const float ms = mnew == kNegInf ? 0.f : mnew;
+    const float alpha = exp2_fast(m - ms);
+    l *= alpha;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o[i] *= alpha;
+    m = mnew;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const float p = exp2_fast(sc[u] - ms);
+      l += p;
+      const float pv = p * ws_v[u];
+      float vf[8];
+      unpack8_fp8(fresh[u] ? new_vw : vw[u], vf);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) o[i] = fmaf(pv, vf[i], o[i]);
+    }
+  };
+  u32x2_t kw[2][U], vw[2][U];
+  bool ok[2][U];
+  issue(0, kw[0], vw[0], ok[0]);
+#pragma unroll
+  for (int s = 0; s < kSteps; ++s) {
+    if (s + 1 < kSteps) issue(s + 1, kw[(s + 1) & 1], vw[(s + 1) & 1], ok[(s + 1) & 1]);
+    consume(s, kw[s & 1], vw[s & 1], ok[s & 1]);
+  }
+  HeadState<1> st;
+  st.m[0] = m;
+  st.l[0] = l;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) st.o[0][i] = o[i];
+  merge_groups<LPR, 1>(st);
+  finish_split<D, 1>(st, lane, wave, ws, (size_t)bh, split, n, max_splits, out, lse);
+}
+
+template <int D, int kSteps>
+static void launch_static_fp8_k(const float* q, void* k_codes, void* v_codes, float* k_scale,
+                                float* v_scale, int32_t* mask, const int32_t* valid_len,
+                                const void* k_new, const void* v_new, const int32_t* write_pos,
+                                int B, int H, int cap, float scale, float* out, float* lse,
+                                const Workspace& w, const SplitPlan& plan, int32_t* err_flag,
+                                hipStream_t stream) {
+  const dim3 grid((unsigned)(B * H * plan.max_splits));
+  auto* kc = static_cast<uint8_t*>(k_codes);
+  auto* vc = static_cast<uint8_t*>(v_codes);
+  auto* kn = static_cast<const uint16_t*>(k_new);
+  auto* vn = static_cast<const uint16_t*>(v_new);
+  if (write_pos)
+    hipLaunchKernelGGL((static_decode_fp8_kernel<D, 4, kSteps, true>), grid, dim3(kThreads), 0,
+                       stream, q, kc, vc, k_scale, v_scale, mask, valid_len, kn, vn, write_pos, H,
+                       cap, scale * kLog2e, plan.chunk, B * H, w, out, lse, err_flag);
+  else
+    hipLaunchKernelGGL((static_decode_fp8_kernel<D, 4, kSteps, false>), grid, dim3(kThreads), 0,
+                       stream, q, kc, vc, k_scale, v_scale, mask, valid_len, kn, vn, write_pos, H,
+                       cap, scale * kLog2e, plan.chunk, B * H, w, out, lse, err_flag);
+}
+
+hipError_t launch_decode_static_fp8(const float* q, void* k_codes, void* v_codes, float* k_scale,
+                                    float* v_scale, int32_t* mask, const int32_t* valid_len,
+                                    const void* k_new, const void* v_new,
+                                    const int32_t* write_pos, int B, int H, int cap, int D,
+                                    float scale, float* out, float* lse, void* ws,
+                                    const SplitPlan& plan, int32_t* err_flag, hipStream_t stream) {
+  const Workspace w = carve(ws, (size_t)B * H, plan.max_splits, D);
+#define DAKV_FP8(DD)                                                                          \
+  do {                                                                                        \
+    constexpr int kStep = kWaves * (64 / (DD / 8)) * 4;                                       \
+    const int steps = (plan.chunk + kStep - 1) / kStep;                                       \
+    if (steps <= 1)                                                                           \
+      launch_static_fp8_k<DD, 1>(q, k_codes, v_codes, k_scale, v_scale, mask, valid_len, k_new, \
+                                 v_new, write_pos, B, H, cap, scale, out, lse, w, plan,       \
+                                 err_flag, stream);                                           \
+    else if (steps <= 2)                                                                      \
+      launch_static_fp8_k<DD, 2>(q, k_codes, v_codes, k_scale, v_scale, mask, valid_len, k_new, \
+                                 v_new, write_pos, B, H, cap, scale, out, lse, w, plan,       \
+                                 err_flag, stream);                                           \
+    else                                                                                      \
+      launch_static_fp8_k<DD, 4>(q, k_codes, v_codes, k_scale, v_scale, mask, valid_len, k_new, \
+                                 v_new, write_pos, B, H, cap, scale, out, lse, w, plan,       \
+                                 err_flag, stream);                                           \
+  } while (0)
+  if (D == 128) DAKV_FP8(128);
+  else DAKV_FP8(64);
+#undef DAKV_FP8
+  const hipError_t err = hipGetLastError();
+  if (err != hipSuccess || plan.max_splits <= 1) return err;
+  return launch_static_merge(w, B, H, D, plan.chunk, plan.max_splits, valid_len, cap, out, lse,
+                             stream);
+}
+
+}  // namespace dakv
