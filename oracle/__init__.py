@@ -44,7 +44,7 @@ from .paged import (
     decode_paged,
     decode_paged_via_gather,
 )
-from .sparse import sparse_topk_decode, validate_sparse
+from .sparse import sparse_topk_attn, sparse_topk_decode, validate_sparse
 from .fp8 import (
     e4m3_decode,
     e4m3_encode,
@@ -66,6 +66,7 @@ __all__ = [
     "gather_pa_kv_cache",
     "decode_paged",
     "decode_paged_via_gather",
+    "sparse_topk_attn",
     "sparse_topk_decode",
     "validate_sparse",
     "e4m3_decode",

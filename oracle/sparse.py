@@ -64,3 +64,27 @@ def sparse_topk_decode(q, kv, indices, d_v, sm_scale):
         for h in range(h_q):
             out[b, h], lse[b, h] = softmax_weighted_sum(P[h] * sm_scale, values)
     return out, lse
+
+
+def sparse_topk_attn(q, kv, indices, d_v, sm_scale):
+    """The page's kernel in general form (FlashMLA on Huawei Ascend, "Reminder of the
+    algorithm" and "Mathematical formulation"): a sequence has several q-tokens, each
+    with its own index list into the sequence's one latent cache, and the q-tokens are
+    computed separately -- each one is exactly ``sparse_topk_decode`` of that token.
+
+    q       : ``[B, s_q, h_q, d_qk]`` (uint16 bf16 bits, or float)
+    kv      : uint16 bf16 bits ``[B, s_kv, d_qk]``
+    indices : ints ``[B, s_q, topk]``
+    Returns ``out [B, s_q, h_q, d_v]`` and ``lse [B, s_q, h_q]`` (float64).
+    """
+    q = np.asarray(q)
+    indices = np.asarray(indices)
+    if q.ndim != 4 or indices.ndim != 3 or indices.shape[:2] != q.shape[:2]:
+        raise ValueError("q must be [B, s_q, h_q, d_qk] and indices [B, s_q, topk]")
+    B, s_q, h_q, _ = q.shape
+    out = np.zeros((B, s_q, h_q, d_v))
+    lse = np.full((B, s_q, h_q), -np.inf)
+    for t in range(s_q):
+        out[:, t], lse[:, t] = sparse_topk_decode(q[:, t], kv, indices[:, t], d_v, sm_scale)
+    return out, lse
+

@@ -87,3 +87,55 @@ def test_out_of_range_index_is_an_error(bad):
     kv = np.zeros((1, 50, 4), dtype=np.uint16)
     with pytest.raises(ValueError):
         oracle.sparse_topk_decode(np.zeros((1, 1, 4)), kv, np.array([[0, bad]]), 2, 1.0)
+
+
+# ------------------------------------------------------- several q-tokens per sequence
+
+
+def test_tokens_attend_through_their_own_indices_brute_force():
+    """Two q-tokens of one sequence, each with its own index list over the one latent
+    cache: every (token, head) output is the softmax-weighted mean written out with
+    math.exp over that token's gathered rows (no array library in the check)."""
+    rng = np.random.default_rng(71)
+    B, s_q, h_q, d_qk, d_v, s_kv = 2, 2, 2, 6, 4, 9
+    kv = random_bits(rng, (B, s_kv, d_qk))
+    q = random_bits(rng, (B, s_q, h_q, d_qk))
+    idx = np.stack([np.stack([rng.choice(s_kv, 4, replace=False) for _ in range(s_q)])
+                    for _ in range(B)])
+    out, lse = oracle.sparse_topk_attn(q, kv, idx, d_v, 0.5)
+    kvf, qf = widen(kv), widen(q)
+    for b in range(B):
+        for t in range(s_q):
+            for h in range(h_q):
+                rows = [kvf[b, i] for i in idx[b, t]]
+                s = [0.5 * sum(float(qf[b, t, h, d]) * float(r[d]) for d in range(d_qk))
+                     for r in rows]
+                m = max(s)
+                w = [math.exp(x - m) for x in s]
+                tot = sum(w)
+                for d in range(d_v):
+                    ref = sum(wi * float(r[d]) for wi, r in zip(w, rows)) / tot
+                    assert abs(out[b, t, h, d] - ref) < 1e-12
+                assert abs(lse[b, t, h] - (m + math.log(tot))) < 1e-12
+
+
+def test_one_token_per_sequence_is_the_decode_case():
+    rng = np.random.default_rng(72)
+    kv = random_bits(rng, (3, 20, 8))
+    q = random_bits(rng, (3, 4, 8))
+    idx = np.stack([rng.choice(20, 7, replace=False) for _ in range(3)])
+    o1, l1 = oracle.sparse_topk_attn(q[:, None], kv, idx[:, None], 5, 0.3)
+    o2, l2 = oracle.sparse_topk_decode(q, kv, idx, 5, 0.3)
+    assert np.array_equal(o1[:, 0], o2) and np.array_equal(l1[:, 0], l2)
+
+
+def test_tokens_are_independent():
+    """Swapping two tokens' queries and index lists swaps their outputs."""
+    rng = np.random.default_rng(73)
+    kv = random_bits(rng, (1, 30, 8))
+    q = random_bits(rng, (1, 3, 2, 8))
+    idx = np.stack([np.stack([rng.choice(30, 5, replace=False) for _ in range(3)])])
+    out, lse = oracle.sparse_topk_attn(q, kv, idx, 8, 0.4)
+    perm = [2, 0, 1]
+    out_p, lse_p = oracle.sparse_topk_attn(q[:, perm], kv, idx[:, perm], 8, 0.4)
+    assert np.array_equal(out_p, out[:, perm]) and np.array_equal(lse_p, lse[:, perm])
