@@ -421,6 +421,32 @@ def sparse_leg(torch, dakv, workloads, acc, counter_pass=False):
             "frac_of_bf16_mfma_peak": round(flops / (ms * 1e-3) / 2.5e15, 4)}
 
 
+def sparse_tokens_leg(torch, dakv, workloads, acc, s_q=2):
+    """The sparse MLA config with s_q q-tokens per sequence (each its own top-2048
+    list over the sequence's one latent cache), e.g. a draft token verified with the
+    next one."""
+    case = workloads.sparse_tokens_case(16, s_q, 128, 32768, 2048, device="cuda:0", seed=7)
+    B, _, Hq, d_qk = case.q.shape
+    topk = case.indices.shape[2]
+    out = torch.empty((B, s_q, Hq, case.d_v), dtype=torch.float32, device="cuda:0")
+    ws = torch.empty(dakv.sparse_topk_decode_attn_workspace_size(B * s_q, Hq, d_qk, case.d_v,
+                                                                 topk),
+                     dtype=torch.uint8, device="cuda:0")
+    call = lambda: dakv.sparse_topk_attn(case.q, case.kv, case.indices, d_v=case.d_v,
+                                         sm_scale=case.sm_scale, out=out, workspace=ws,
+                                         want_lse=False)
+    ms = time_cold(torch, call)
+    nbytes = acc.sparse_bytes(B * s_q, Hq, d_qk, case.d_v, topk)
+    flops = acc.sparse_flops(B * s_q, Hq, d_qk, case.d_v, topk)
+    del case, out, ws
+    return {"workload": f"top-k sparse MLA, {s_q} q-tokens per sequence: batch 16, 128 heads, "
+                        f"d_qk 576 / d_v 512, context 32768, top-2048 per token",
+            "us_per_call": round(ms * 1e3, 2), "algorithmic_bytes": nbytes,
+            "GBps": round(nbytes / (ms * 1e-3) / 1e9, 1),
+            "TFLOPs": round(flops / (ms * 1e-3) / 1e12, 1),
+            "frac_of_bf16_mfma_peak": round(flops / (ms * 1e-3) / 2.5e15, 4)}
+
+
 def cpu_baseline(step, budget_s):
     """The fp64 oracle over (layer, sequence) pairs of the same step until the budget is
     spent; GB/s = algorithmic bytes of the pairs done / host seconds."""
@@ -595,6 +621,7 @@ def main():
         line["paged_gqa"] = paged_leg(torch, dakv, workloads, acc)
         torch.cuda.empty_cache()
         line["sparse_mla"] = sparse_leg(torch, dakv, workloads, acc)
+        line["sparse_mla_2_tokens"] = sparse_tokens_leg(torch, dakv, workloads, acc)
         torch.cuda.empty_cache()
         line["copy_kvcache"] = copy_leg(torch, dakv, acc)
         torch.cuda.empty_cache()

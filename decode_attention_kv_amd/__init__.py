@@ -18,6 +18,7 @@ from .ops import (
     gather_pa_kv_cache,
     decode_attn_paged,
     decode_attn_paged_workspace_size,
+    sparse_topk_attn,
     sparse_topk_decode_attn,
     sparse_topk_decode_attn_workspace_size,
     validate_paged,
@@ -39,6 +40,7 @@ __all__ = [
     "gather_pa_kv_cache",
     "decode_attn_paged",
     "decode_attn_paged_workspace_size",
+    "sparse_topk_attn",
     "sparse_topk_decode_attn",
     "sparse_topk_decode_attn_workspace_size",
     "validate_paged",

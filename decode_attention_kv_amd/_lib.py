@@ -55,6 +55,8 @@ SIGNATURES = {
     "dakv_sparse_topk_decode_attn_workspace_size": (_sz, [_i, _i, _i, _i, _i]),
     "dakv_sparse_topk_decode_attn": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _vp, _vp,
                                           _vp, _sz, _vp, _vp]),
+    "dakv_sparse_topk_attn": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f, _vp, _vp,
+                                   _vp, _sz, _vp, _vp]),
     "dakv_validate_paged": (_i, [_vp, _i, _i, _vp, _vp, _i, _i]),
     "dakv_validate_sparse": (_i, [_vp, _i, _i, _i]),
     "dakv_validate_range": (_i, [_vp, _i, _i, _i]),

@@ -66,8 +66,10 @@ hipError_t launch_decode_paged(const void* q, const void* key_cache, const void*
                                const SplitPlan& plan, int32_t* err_flag, hipStream_t stream);
 
 size_t sparse_workspace_bytes(int B, int Hq, int d_qk, int d_v, int topk);
-hipError_t launch_sparse(const void* q, const void* kv, const int32_t* indices, int B, int Hq,
-                         int s_kv, int d_qk, int d_v, int topk, float sm_scale, float* out,
-                         float* lse, void* ws, int32_t* err_flag, hipStream_t stream);
+// B = (sequence, q-token) pairs; the s_q tokens of sequence b / s_q share its kv rows
+hipError_t launch_sparse(const void* q, const void* kv, const int32_t* indices, int B, int s_q,
+                         int Hq, int s_kv, int d_qk, int d_v, int topk, float sm_scale,
+                         float* out, float* lse, void* ws, int32_t* err_flag,
+                         hipStream_t stream);
 
 }  // namespace dakv

@@ -82,8 +82,8 @@ __device__ __forceinline__ bf16x8_t join_bf16x4(const i16x4_t& lo, const i16x4_t
 
 __global__ void __launch_bounds__(256)
 sparse_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
-                    const int32_t* __restrict__ indices, int B, int Hq, int s_kv, int topk,
-                    float scale_log2, int n_hg, int n_splits, int per_hg,
+                    const int32_t* __restrict__ indices, int B, int s_q, int Hq, int s_kv,
+                    int topk, float scale_log2, int n_hg, int n_splits, int per_hg,
                     float* __restrict__ ws_o, float* __restrict__ ws_lse, int32_t* err_flag) {
   __shared__ __attribute__((aligned(1024))) uint8_t buf0[kTileBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t buf1[kTileBytes];
@@ -115,10 +115,11 @@ sparse_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     rows[i] = r;
   }
   __syncthreads();
-  // the sequence's latent rows as a buffer: an absent row reads as zeros
+  // the sequence's latent rows as a buffer (the q-tokens of one sequence, b / s_q,
+  // share them): an absent row reads as zeros
   const __amdgpu_buffer_rsrc_t kvr = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t*>(kv) + (size_t)b * s_kv * kDqk, (short)0, (int)(s_kv * kRowBytes),
-      0x00020000);
+      const_cast<uint16_t*>(kv) + (size_t)(b / s_q) * s_kv * kDqk, (short)0,
+      (int)(s_kv * kRowBytes), 0x00020000);
   const int ntiles = (ntok + kTile - 1) / kTile;
 
   // Tile ti into a buffer: wave load I (this wave's I = 18 wave + k) fills bytes
@@ -426,9 +427,10 @@ size_t sparse_workspace_bytes(int B, int Hq, int d_qk, int d_v, int topk) {
   return (size_t)B * Hq * sparse_splits(topk) * (size_t)(d_v + 1) * sizeof(float);
 }
 
-hipError_t launch_sparse(const void* q, const void* kv, const int32_t* indices, int B, int Hq,
-                         int s_kv, int d_qk, int d_v, int topk, float sm_scale, float* out,
-                         float* lse, void* ws, int32_t* err_flag, hipStream_t stream) {
+hipError_t launch_sparse(const void* q, const void* kv, const int32_t* indices, int B, int s_q,
+                         int Hq, int s_kv, int d_qk, int d_v, int topk, float sm_scale,
+                         float* out, float* lse, void* ws, int32_t* err_flag,
+                         hipStream_t stream) {
   (void)d_qk;
   (void)d_v;
   const int n_splits = sparse_splits(topk);
@@ -439,8 +441,8 @@ hipError_t launch_sparse(const void* q, const void* kv, const int32_t* indices, 
     const int per_hg = (B * n_splits + 7) / 8 * 8;
     hipLaunchKernelGGL(sparse_split_kernel, dim3(n_hg * per_hg), dim3(256), 0, stream,
                        static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kv),
-                       indices, B, Hq, s_kv, topk, sm_scale * kLog2e, n_hg, n_splits, per_hg,
-                       ws_o, ws_lse, err_flag);
+                       indices, B, s_q, Hq, s_kv, topk, sm_scale * kLog2e, n_hg, n_splits,
+                       per_hg, ws_o, ws_lse, err_flag);
   }
   hipLaunchKernelGGL(sparse_merge_kernel, dim3(B * Hq), dim3(256), 0, stream, ws_o, ws_lse,
                      n_splits, out, lse);

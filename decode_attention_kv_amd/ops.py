@@ -464,3 +464,42 @@ def sparse_topk_decode_attn(q, kv, indices, d_v=512, sm_scale=None, out=None, ls
         _p(q), _p(kv), _p(indices), B, Hq, s_kv, d_qk, d_v, topk, float(sm_scale), _p(out),
         _p(lse), _p(ws), ws.numel(), _p(err_flag), _stream()))
     return out, lse
+
+
+def sparse_topk_attn(q, kv, indices, d_v=512, sm_scale=None, out=None, lse=None,
+                     workspace=None, err_flag=None, validate=False, want_lse=True):
+    """Top-k sparse MLA-style attention with several q-tokens per sequence, each with
+    its own index list into the sequence's latent cache.  Returns ``(out, lse)``.
+
+    q bf16 [B, s_q, Hq, d_qk]; kv bf16 [B, s_kv, d_qk]; indices int32 [B, s_q, topk];
+    out fp32 [B, s_q, Hq, d_v]; lse fp32 [B, s_q, Hq].
+    """
+    _need(q, "q", torch.bfloat16)
+    if q.dim() != 4:
+        raise ValueError("q must be [B, s_q, Hq, d_qk]")
+    B, s_q, Hq, d_qk = q.shape
+    _need(kv, "kv", torch.bfloat16)
+    if kv.dim() != 3 or kv.shape[0] != B or kv.shape[2] != d_qk:
+        raise ValueError("kv must be [B, s_kv, d_qk]")
+    s_kv = kv.shape[1]
+    _need(indices, "indices", torch.int32)
+    if indices.dim() != 3 or tuple(indices.shape[:2]) != (B, s_q):
+        raise ValueError("indices must be [B, s_q, topk]")
+    topk = indices.shape[2]
+    if validate:
+        validate_sparse(indices.reshape(B * s_q, topk), s_kv)
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(d_qk)
+    if out is None:
+        out = torch.empty((B, s_q, Hq, d_v), dtype=torch.float32, device=q.device)
+    _need(out, "out", torch.float32, (B, s_q, Hq, d_v))
+    if lse is None and want_lse:
+        lse = torch.empty((B, s_q, Hq), dtype=torch.float32, device=q.device)
+    _opt(lse, "lse", torch.float32, (B, s_q, Hq))
+    _opt(err_flag, "err_flag", torch.int32, (1,))
+    nbytes = sparse_topk_decode_attn_workspace_size(B * s_q, Hq, d_qk, d_v, topk)
+    ws = _workspace(nbytes, q.device, workspace)
+    check("sparse_topk_attn", lib().dakv_sparse_topk_attn(
+        _p(q), _p(kv), _p(indices), B, s_q, Hq, s_kv, d_qk, d_v, topk, float(sm_scale),
+        _p(out), _p(lse), _p(ws), ws.numel(), _p(err_flag), _stream()))
+    return out, lse

@@ -330,6 +330,26 @@ int dakv_sparse_topk_decode_attn(const void* q, const void* kv, const int32_t* i
                                  float sm_scale, float* out, float* lse, void* workspace,
                                  size_t workspace_bytes, int32_t* err_flag, void* stream);
 
+/*
+ * sparse_topk_attn -- the same kernel for several q-tokens per sequence, each
+ * with its own index list into the sequence's one latent cache; q-tokens are
+ * computed separately ([FlashMLA] "Reminder of the algorithm": the kernel takes
+ * some q-tokens and kv-tokens and an index table; "Mathematical formulation":
+ * different q-tokens are always processed separately).  Token t of sequence b:
+ *   out[b, t] = sparse_topk_decode_attn of q[b, t] over kv[b] with indices[b, t]
+ *
+ *   q        bf16 [B, s_q, Hq, d_qk];  kv bf16 [B, s_kv, d_qk];
+ *   indices  int32 [B, s_q, topk]
+ *   out      fp32 [B, s_q, Hq, d_v];   lse fp32 [B, s_q, Hq] or NULL
+ *   workspace as dakv_sparse_topk_decode_attn_workspace_size(B * s_q, ...)
+ * Supported as dakv_sparse_topk_decode_attn, and B * s_q <= 2^24.  s_q = 1 is
+ * dakv_sparse_topk_decode_attn.
+ */
+int dakv_sparse_topk_attn(const void* q, const void* kv, const int32_t* indices, int B,
+                          int s_q, int Hq, int s_kv, int d_qk, int d_v, int topk,
+                          float sm_scale, float* out, float* lse, void* workspace,
+                          size_t workspace_bytes, int32_t* err_flag, void* stream);
+
 /* ========================================================================
  * Host validators (HOST pointers; no GPU needed).  [PyPTO] 3.3 and 5.1: the
  * index tensors are host-ready and are checked on the host before a call.

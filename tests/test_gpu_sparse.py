@@ -96,3 +96,51 @@ def test_sparse_mla_full_size_sampled():
         r_out, r_lse = ref(case, rows=slice(b, b + 1))
         assert_attention_close(out[b:b + 1], r_out)
         assert_lse_close(lse[b:b + 1], r_lse)
+
+
+# ------------------------------------------------------- several q-tokens per sequence
+
+
+@pytest.mark.parametrize("B,s_q,Hq,s_kv,topk", [
+    (2, 2, 16, 1000, 300),    # two tokens per sequence, two splits, ragged tile
+    (1, 3, 32, 700, 65),      # three tokens, a ragged second tile
+    (3, 2, 128, 4096, 2048),  # the config's heads and top-k, two tokens
+    (2, 4, 16, 64, 1),        # a single index per token
+])
+def test_sparse_tokens_match_oracle(B, s_q, Hq, s_kv, topk):
+    print(f"sparse tokens B={B} s_q={s_q} Hq={Hq} s_kv={s_kv} topk={topk}", flush=True)
+    case = workloads.sparse_tokens_case(B, s_q, Hq, s_kv, topk, device=DEV, seed=60 + topk)
+    out, lse = dakv.sparse_topk_attn(case.q, case.kv, case.indices, d_v=case.d_v,
+                                     sm_scale=case.sm_scale)
+    torch.cuda.synchronize()
+    r_out, r_lse = oracle.sparse_topk_attn(bits(case.q), bits(case.kv), npy(case.indices),
+                                           case.d_v, case.sm_scale)
+    assert_attention_close(npy(out), r_out)
+    assert_lse_close(npy(lse), r_lse)
+
+
+def test_sparse_tokens_one_token_is_the_decode_call_and_bad_index_is_flagged():
+    case = workloads.sparse_tokens_case(2, 1, 32, 500, 200, device=DEV, seed=67)
+    o1, l1 = dakv.sparse_topk_attn(case.q, case.kv, case.indices, d_v=case.d_v,
+                                   sm_scale=case.sm_scale)
+    o2, l2 = dakv.sparse_topk_decode_attn(case.q[:, 0].contiguous(), case.kv,
+                                          case.indices[:, 0].contiguous(), d_v=case.d_v,
+                                          sm_scale=case.sm_scale)
+    torch.cuda.synchronize()
+    assert torch.equal(o1[:, 0], o2) and torch.equal(l1[:, 0], l2)
+    case = workloads.sparse_tokens_case(1, 2, 16, 200, 40, device=DEV, seed=68)
+    idx = npy(case.indices).copy()
+    good = idx.copy()
+    idx[0, 1, 5] = 200                                 # token 1 only
+    flag = torch.zeros(1, dtype=torch.int32, device=DEV)
+    out, _ = dakv.sparse_topk_attn(case.q, case.kv, torch.from_numpy(idx).to(DEV),
+                                   d_v=case.d_v, sm_scale=case.sm_scale, err_flag=flag)
+    torch.cuda.synchronize()
+    assert int(flag.item()) & dakv._lib.ERR_SPARSE_INDEX
+    r0, _ = oracle.sparse_topk_attn(bits(case.q)[:, :1], bits(case.kv), good[:, :1],
+                                    case.d_v, case.sm_scale)
+    keep = [i for i in range(40) if i != 5]
+    r1, _ = oracle.sparse_topk_attn(bits(case.q)[:, 1:], bits(case.kv), good[:, 1:, keep],
+                                    case.d_v, case.sm_scale)
+    assert_attention_close(npy(out)[:, :1], r0)
+    assert_attention_close(npy(out)[:, 1:], r1)

@@ -301,6 +301,22 @@ def sparse_case(B, Hq, s_kv, topk, *, d_qk=576, d_v=512, device="cpu", seed=5,
     return SparseCase(q, kv, torch.from_numpy(idx).to(device), d_v, float(sm_scale))
 
 
+def sparse_tokens_case(B, s_q, Hq, s_kv, topk, *, d_qk=576, d_v=512, device="cpu", seed=6,
+                       sm_scale=None):
+    """Several q-tokens per sequence: q [B, s_q, Hq, d_qk], one latent cache
+    kv [B, s_kv, d_qk] per sequence, indices [B, s_q, topk] distinct within a token
+    (each token draws its own list without replacement)."""
+    rng = np.random.default_rng(seed)
+    idx = np.stack([np.stack([rng.choice(s_kv, topk, replace=False) for _ in range(s_q)])
+                    for _ in range(B)]).astype(np.int32).reshape(B, s_q, topk)
+    g = _gen(device, seed)
+    kv = _randn_bf16((B, s_kv, d_qk), g, device)
+    q = _randn_bf16((B, s_q, Hq, d_qk), g, device)
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(d_qk)
+    return SparseCase(q, kv, torch.from_numpy(idx).to(device), d_v, float(sm_scale))
+
+
 def sparse_mla(*, device="cpu", seed=5):
     """Batch 16, 128 heads, d_qk 576 / d_v 512, context 32768, top-2048."""
     return sparse_case(16, 128, 32768, 2048, device=device, seed=seed)
