@@ -52,6 +52,8 @@ from .fp8 import (
     quantize_rows,
     kv_append_fp8,
     decode_static_fp8,
+    decode_paged_fp8,
+    paged_append_fp8,
 )
 
 __all__ = [
@@ -75,4 +77,6 @@ __all__ = [
     "quantize_rows",
     "kv_append_fp8",
     "decode_static_fp8",
+    "decode_paged_fp8",
+    "paged_append_fp8",
 ]

@@ -18,8 +18,13 @@ readings taken here are:
 * the code of x is x / s rounded to the nearest E4M3 value, ties to the even code
   (x / s is exact because s is a power of two, and never exceeds 448);
 * the cached value is decode(code) * s, which is exactly representable in bf16
-  (3 mantissa bits, an exponent shift), so attention over the FP8 cache is the
-  attention of the static layout over those values.
+  (3 mantissa bits, an exponent shift) unless it falls below bf16's smallest
+  subnormal, so attention over the FP8 cache is the attention of the static layout
+  over those values;
+* the paged pool holds codes ``[num_blocks, block_size, Hkv, D]`` and one scale per
+  (block, slot, KV head) ``[num_blocks, block_size, Hkv]`` for K and for V, and the
+  new token of sequence b is its last token (position len_b - 1, len_b counting
+  it), placed through the block table as every other token.
 """
 
 import math
@@ -27,6 +32,7 @@ import math
 import numpy as np
 
 from .bf16 import widen
+from .paged import _offsets, token_rows, validate_paged
 from .static_cache import attended_rows, softmax_weighted_sum
 
 E4M3_MAX = 448.0
@@ -145,3 +151,64 @@ def decode_static_fp8(q, k_codes, v_codes, k_scale, v_scale, mask=None, valid_le
             V = dequantize(v_codes[b, h, rows], v_scale[b, h, rows])
             out[b, h], lse[b, h] = softmax_weighted_sum(scale * (K @ q[b, h]), V)
     return out, lse
+
+
+def decode_paged_fp8(q, k_codes, v_codes, k_scale, v_scale, block_tables, seq_lens,
+                     seq_offset=None, scale=None):
+    """Paged GQA decode over an FP8 pool: the attention of decode_paged over the
+    dequantised rows.  q ``[B, Hq, D]`` (bf16 bits or float); codes uint8
+    ``[num_blocks, block_size, Hkv, D]``; scales ``[num_blocks, block_size, Hkv]``.
+    Returns ``out [B, Hq, D]`` and ``lse [B, Hq]`` (float64)."""
+    q = np.asarray(q)
+    qf = widen(q) if q.dtype == np.uint16 else q.astype(np.float64)
+    B, Hq, D = qf.shape
+    num_blocks, block_size, Hkv, Dk = np.shape(k_codes)
+    if Dk != D or np.shape(v_codes) != np.shape(k_codes):
+        raise ValueError("codes must be [num_blocks, block_size, Hkv, D]")
+    if np.shape(k_scale) != (num_blocks, block_size, Hkv) or np.shape(v_scale) != np.shape(k_scale):
+        raise ValueError("scales must be [num_blocks, block_size, Hkv]")
+    if Hq % Hkv != 0:
+        raise ValueError("query heads must be a multiple of KV heads")
+    group = Hq // Hkv
+    validate_paged(block_tables, seq_lens, seq_offset, num_blocks, block_size)
+    seq_lens = np.asarray(seq_lens, dtype=np.int64).reshape(-1)
+    offsets = _offsets(seq_offset, B)
+    if scale is None:
+        scale = 1.0 / np.sqrt(D)
+    out = np.zeros((B, Hq, D))
+    lse = np.full((B, Hq), -np.inf)
+    for b in range(B):
+        phys, slot = token_rows(b, block_tables, seq_lens, offsets, block_size)
+        K = dequantize(np.asarray(k_codes)[phys, slot], np.asarray(k_scale)[phys, slot])
+        V = dequantize(np.asarray(v_codes)[phys, slot], np.asarray(v_scale)[phys, slot])
+        for h in range(Hq):
+            g = h // group
+            out[b, h], lse[b, h] = softmax_weighted_sum(scale * (K[:, g, :] @ qf[b, h]),
+                                                        V[:, g, :])
+    return out, lse
+
+
+def paged_append_fp8(k_codes, v_codes, k_scale, v_scale, k_new, v_new, block_tables, seq_lens,
+                     seq_offset=None):
+    """Quantise the new token's K and V rows (bf16 bits ``[B, Hkv, D]``) and store them
+    as token len_b - 1 of each sequence, at its place in the pool (block table, then
+    slot), as kv_append_fp8 does in the static buffer.  Returns updated copies of the
+    four arrays; a sequence of length 0 has no place for the token and is an error."""
+    k_codes, v_codes = np.array(k_codes, copy=True), np.array(v_codes, copy=True)
+    k_scale, v_scale = np.array(k_scale, copy=True), np.array(v_scale, copy=True)
+    num_blocks, block_size = k_codes.shape[:2]
+    validate_paged(block_tables, seq_lens, seq_offset, num_blocks, block_size)
+    seq_lens = np.asarray(seq_lens, dtype=np.int64).reshape(-1)
+    B = seq_lens.shape[0] - 1
+    offsets = _offsets(seq_offset, B)
+    kq, ks = quantize_rows(k_new)
+    vq, vs = quantize_rows(v_new)
+    for b in range(B):
+        phys, slot = token_rows(b, block_tables, seq_lens, offsets, block_size)
+        if phys.shape[0] == 0:
+            raise ValueError(f"sequence {b} has length 0: no place for its new token")
+        p, sl = phys[-1], slot[-1]
+        k_codes[p, sl], v_codes[p, sl] = kq[b], vq[b]
+        k_scale[p, sl], v_scale[p, sl] = ks[b], vs[b]
+    return k_codes, v_codes, k_scale, v_scale
+
