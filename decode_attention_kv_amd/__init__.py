@@ -10,6 +10,8 @@ from .ops import (
     kv_append_fp8,
     decode_attn_static_fp8,
     decode_step_static_fp8,
+    paged_append_fp8,
+    decode_attn_paged_fp8,
     copy_kvcache,
     trim_kvcache,
     decode_attn_static,
@@ -32,6 +34,8 @@ __all__ = [
     "kv_append_fp8",
     "decode_attn_static_fp8",
     "decode_step_static_fp8",
+    "paged_append_fp8",
+    "decode_attn_paged_fp8",
     "copy_kvcache",
     "trim_kvcache",
     "decode_attn_static",

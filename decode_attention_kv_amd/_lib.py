@@ -57,6 +57,11 @@ SIGNATURES = {
                                           _vp, _sz, _vp, _vp]),
     "dakv_sparse_topk_attn": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f, _vp, _vp,
                                    _vp, _sz, _vp, _vp]),
+    "dakv_paged_append_fp8": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _vp, _vp, _i, _i, _i,
+                                   _i, _i, _vp, _vp]),
+    "dakv_decode_attn_paged_fp8": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _vp, _vp, _i, _i,
+                                        _i, _i, _i, _i, _i, _f, _vp, _vp, _vp, _sz, _i, _vp,
+                                        _vp]),
     "dakv_validate_paged": (_i, [_vp, _i, _i, _vp, _vp, _i, _i]),
     "dakv_validate_sparse": (_i, [_vp, _i, _i, _i]),
     "dakv_validate_range": (_i, [_vp, _i, _i, _i]),

@@ -80,6 +80,18 @@ def decode_paged_bytes(lengths, Hq, Hkv, D, block_size, q_elem=BF16, with_lse=Fa
     return kv + q + out + table + (B + 1) * INT32
 
 
+def decode_paged_fp8_bytes(lengths, Hq, Hkv, D, block_size, q_elem=BF16, with_lse=False):
+    """Paged GQA decode over the FP8 pool: each KV head's valid rows once (D code bytes
+    plus a 4-byte scale, for K and for V), q once, out once, table and lengths."""
+    T = sum(int(x) for x in lengths)
+    B = len(lengths)
+    kv = T * Hkv * (D + FP32) * 2
+    q = B * Hq * D * q_elem
+    out = B * Hq * D * FP32 + (B * Hq * FP32 if with_lse else 0)
+    table = sum(-(-int(x) // block_size) for x in lengths) * INT32
+    return kv + q + out + table + (B + 1) * INT32
+
+
 def decode_flops(rows, heads_per_row, d_qk, d_v):
     """Multiply-add flops of scores plus the weighted sum (2 per MAC)."""
     return 2 * rows * heads_per_row * (d_qk + d_v)

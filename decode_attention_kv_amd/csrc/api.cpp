@@ -257,6 +257,63 @@ int dakv_decode_attn_paged(const void* q, const void* key_cache, const void* val
                                             plan, err_flag, as_stream(stream)));
 }
 
+// ------------------------------------------------------------- paged, FP8 pool
+static bool paged_fp8_shape(int Hq, int Hkv, int D, int block_size) {
+  if (Hkv <= 0 || Hq % Hkv != 0 || 16 % Hkv != 0) return false;
+  const int G = Hq / Hkv;
+  return D == 128 && (G == 1 || G == 2 || G == 4 || G == 8) &&
+         (block_size == 16 || block_size == 32 || block_size == 64 || block_size == 128);
+}
+
+int dakv_paged_append_fp8(void* k_codes, void* v_codes, float* k_scale, float* v_scale,
+                          const void* k_new, const void* v_new, const int32_t* block_tables,
+                          int table_cols, const int32_t* seq_lens, const int32_t* seq_offset,
+                          int B, int Hkv, int D, int num_blocks, int block_size,
+                          int32_t* err_flag, void* stream) {
+  if (B < 0 || Hkv <= 0 || D <= 0 || num_blocks <= 0 || block_size <= 0 || table_cols <= 0)
+    return DAKV_EINVAL;
+  if (B == 0) return DAKV_OK;
+  if (D > 256) return DAKV_ENOTSUP;
+  if (!k_codes || !v_codes || !k_scale || !v_scale || !k_new || !v_new || !block_tables ||
+      !seq_lens)
+    return DAKV_EINVAL;
+  return from_hip(dakv::launch_paged_append_fp8(k_codes, v_codes, k_scale, v_scale, k_new,
+                                                v_new, block_tables, table_cols, seq_lens,
+                                                seq_offset, B, Hkv, D, num_blocks, block_size,
+                                                err_flag, as_stream(stream)));
+}
+
+int dakv_decode_attn_paged_fp8(const void* q, const void* k_codes, const void* v_codes,
+                               const float* k_scale, const float* v_scale,
+                               const int32_t* block_tables, int table_cols,
+                               const int32_t* seq_lens, const int32_t* seq_offset, int B,
+                               int Hq, int Hkv, int D, int num_blocks, int block_size,
+                               int max_seq_len, float scale, float* out, float* lse,
+                               void* workspace, size_t workspace_bytes, int num_splits,
+                               int32_t* err_flag, void* stream) {
+  if (B < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || num_blocks <= 0 || block_size <= 0 ||
+      max_seq_len < 0 || table_cols <= 0 || num_splits < 0)
+    return DAKV_EINVAL;
+  if (B == 0) return DAKV_OK;
+  if (Hq % Hkv != 0) return DAKV_EINVAL;
+  if (!paged_fp8_shape(Hq, Hkv, D, block_size)) return DAKV_ENOTSUP;
+  if (!dakv::paged_supported(max_seq_len, block_size)) return DAKV_ENOTSUP;
+  if (!q || !k_codes || !v_codes || !k_scale || !v_scale || !block_tables || !seq_lens ||
+      !out || !workspace)
+    return DAKV_EINVAL;
+  if (!aligned16(q) || !aligned16(k_codes) || !aligned16(v_codes) || !aligned16(out) ||
+      !aligned16(workspace))
+    return DAKV_EINVAL;
+  if (workspace_bytes < dakv::paged_workspace_bytes(B, Hq, D, max_seq_len, block_size))
+    return DAKV_EINVAL;
+  const dakv::SplitPlan plan =
+      dakv::plan_paged(B, Hkv, Hq / Hkv, max_seq_len, block_size, num_splits);
+  return from_hip(dakv::launch_decode_paged_fp8(
+      q, k_codes, v_codes, k_scale, v_scale, block_tables, table_cols, seq_lens, seq_offset, B,
+      Hq, Hkv, num_blocks, block_size, max_seq_len, scale, out, lse, workspace, plan, err_flag,
+      as_stream(stream)));
+}
+
 // ---------------------------------------------------- sparse_topk_decode_attn
 size_t dakv_sparse_topk_decode_attn_workspace_size(int B, int Hq, int d_qk, int d_v,
                                                    int topk) {

@@ -120,17 +120,6 @@ static_decode_kernel(const float* __restrict__ q, uint16_t* __restrict__ k_cache
 }
 
 // ------------------------------------------------------------------ paged layout
-constexpr int kMaxTableSpan = 72;  // block-table entries one split may touch
-
-// Step shape of the paged kernel per group size G: U rows per lane group per
-// step and kSteps steps per unrolled super-step (fewer rows in flight when each
-// row feeds more heads and the state takes more registers).
-template <int G> struct PagedShape;
-template <> struct PagedShape<1> { static constexpr int U = 4, kSteps = 2; };
-template <> struct PagedShape<2> { static constexpr int U = 4, kSteps = 2; };
-template <> struct PagedShape<4> { static constexpr int U = 2, kSteps = 4; };
-template <> struct PagedShape<8> { static constexpr int U = 2, kSteps = 2; };
-
 template <int G>
 constexpr int paged_super_rows() {
   return kWaves * 4 * PagedShape<G>::U * PagedShape<G>::kSteps;  // D = 128: 4 rows per wave
@@ -247,63 +236,6 @@ __device__ __forceinline__ void attend_slots_fixed(const GlobalRows& rows, const
   }
 }
 
-constexpr int kRowGroups = 16;  // lane groups of 16 lanes in a workgroup (D = 128)
-constexpr int kPagedRowsTarget = 4096;  // workgroups of a call, if all were full length
-
-// End of an all-heads split: every group's state goes to LDS, then each output
-// element combines the TS groups of its KV head and is written out directly
-// (one split) or as this split's partial.
-template <int G>
-__device__ __forceinline__ void finish_split_rows(const HeadState<G>& st, int gi, int sub, int Hkv,
-                                                  int ts, const Workspace& ws, size_t head0,
-                                                  int split, int n, int max_splits,
-                                                  float* __restrict__ out,
-                                                  float* __restrict__ lse) {
-  constexpr int D = 128;
-  __shared__ float sm_o[kRowGroups][G][D];
-  __shared__ float sm_m[kRowGroups][G];
-  __shared__ float sm_l[kRowGroups][G];
-#pragma unroll
-  for (int j = 0; j < G; ++j) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) sm_o[gi][j][sub * 8 + i] = st.o[j][i];
-    if (sub == 0) {
-      sm_m[gi][j] = st.m[j];
-      sm_l[gi][j] = st.l[j];
-    }
-  }
-  __syncthreads();
-  const int total = Hkv * G * D;
-  for (int idx = threadIdx.x; idx < total; idx += kThreads) {
-    const int hj = idx / D;  // query head within the sequence: h * G + j
-    const int d = idx - hj * D;
-    const int h = hj / G;
-    const int j = hj - h * G;
-    float M = kNegInf;
-    for (int s = 0; s < ts; ++s) M = fmaxf(M, sm_m[h + s * Hkv][j]);
-    float val = 0.f, lse2 = kNegInf;
-    if (M != kNegInf) {
-      float num = 0.f, den = 0.f;
-      for (int s = 0; s < ts; ++s) {
-        const int g2 = h + s * Hkv;
-        const float wt = exp2_fast(sm_m[g2][j] - M);
-        num += wt * sm_o[g2][j][d];
-        den += wt * sm_l[g2][j];
-      }
-      val = num / den;
-      lse2 = M + __log2f(den);
-    }
-    if (n == 1) {
-      out[(head0 + hj) * D + d] = val;
-      if (lse && d == 0) lse[head0 + hj] = lse2 * kLn2;
-    } else {
-      const size_t row = (head0 + hj) * max_splits + split;
-      ws.o[row * D + d] = val;
-      if (d == 0) ws.lse[row] = lse2;
-    }
-  }
-}
-
 template <int G>
 __global__ void __launch_bounds__(kThreads)
 paged_rows_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ key_cache,
@@ -409,6 +341,16 @@ hipError_t launch_static_merge(const Workspace& w, int B, int H, int D, int chun
   else
     hipLaunchKernelGGL(merge_kernel<64>, dim3(B * H), dim3(kThreads), 0, stream, w, H, chunk,
                        max_splits, 0, valid_len, cap, nullptr, nullptr, 1, 0, 0, out, lse);
+  return hipGetLastError();
+}
+
+hipError_t launch_paged_merge(const Workspace& w, int B, int Hq, int chunk, int max_splits,
+                              const int32_t* seq_lens, const int32_t* seq_offset,
+                              int block_size, int table_cols, int max_seq_len, float* out,
+                              float* lse, hipStream_t stream) {
+  hipLaunchKernelGGL(merge_kernel<128>, dim3(B * Hq), dim3(kThreads), 0, stream, w, Hq, chunk,
+                     max_splits, 1, nullptr, 0, seq_lens, seq_offset, block_size, table_cols,
+                     max_seq_len, out, lse);
   return hipGetLastError();
 }
 
@@ -620,11 +562,10 @@ hipError_t launch_decode_paged(const void* q, const void* key_cache, const void*
     }
 #undef DAKV_PAGED
   }
-  if (plan.max_splits > 1)
-    hipLaunchKernelGGL(merge_kernel<128>, dim3(B * Hq), dim3(kThreads), 0, stream, w, Hq,
-                       plan.chunk, plan.max_splits, 1, nullptr, 0, seq_lens, seq_offset,
-                       block_size, table_cols, max_seq_len, out, lse);
-  return hipGetLastError();
+  const hipError_t err = hipGetLastError();
+  if (err != hipSuccess || plan.max_splits <= 1) return err;
+  return launch_paged_merge(w, B, Hq, plan.chunk, plan.max_splits, seq_lens, seq_offset,
+                            block_size, table_cols, max_seq_len, out, lse, stream);
 }
 
 }  // namespace dakv

@@ -1,7 +1,9 @@
-// The FP8 KV cache of the static layout: E4M3 codes (one byte per element) with a
-// power-of-two fp32 scale per cached row, for K and for V.  kv_append_fp8
-// quantises a new token's rows; the split pass reads codes and scales and feeds
-// the same split-K machinery (workspace, merge) as the bf16 cache.
+// The FP8 KV cache: E4M3 codes (one byte per element) with a power-of-two fp32
+// scale per cached row, for K and for V, in the static layout ([B, H, cap, D]
+// codes, [B, H, cap] scales) and in the paged pool ([num_blocks, block_size, Hkv,
+// D] codes, [num_blocks, block_size, Hkv] scales).  The appends quantise a new
+// token's rows; the split passes read codes and scales and feed the same split-K
+// machinery (workspace, merge) as the bf16 caches.
 #include "split_common.hpp"
 
 namespace dakv {
@@ -15,6 +17,28 @@ namespace dakv {
 // value x * 2^-e (exact) is rounded to the nearest E4M3 value, ties to the even
 // code, zero results as the +0 code.
 // ---------------------------------------------------------------------------
+// One wave quantises one row of D <= 256 bf16 values: codes to dst, scale to *dst_scale.
+__device__ __forceinline__ void quantise_row_wave(const uint16_t* __restrict__ src, int D,
+                                                  uint8_t* __restrict__ dst,
+                                                  float* __restrict__ dst_scale, int lane) {
+  float x[4];
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {            // D <= 256: at most 4 values per lane
+    const int d = lane + 64 * i;
+    x[i] = d < D ? __uint_as_float((uint32_t)src[d] << 16) : 0.f;
+    amax = fmaxf(amax, fabsf(x[i]));
+  }
+  for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+  const int e = e4m3_exponent_for(amax);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int d = lane + 64 * i;
+    if (d < D) dst[d] = (uint8_t)e4m3_code(ldexpf(x[i], -e));
+  }
+  if (lane == 0) *dst_scale = ldexpf(1.f, e);
+}
+
 __global__ void __launch_bounds__(256)
 kv_append_fp8_kernel(uint8_t* __restrict__ k_codes, uint8_t* __restrict__ v_codes,
                      float* __restrict__ k_scale, float* __restrict__ v_scale,
@@ -34,23 +58,8 @@ kv_append_fp8_kernel(uint8_t* __restrict__ k_codes, uint8_t* __restrict__ v_code
   }
   const uint16_t* src = (is_v ? v_new : k_new) + ((size_t)b * H + h) * D;
   const size_t row = ((size_t)b * H + h) * cap + pos;
-  uint8_t* dst = (is_v ? v_codes : k_codes) + row * D;
-  float x[4];
-  float amax = 0.f;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {            // D <= 256: at most 4 values per lane
-    const int d = lane + 64 * i;
-    x[i] = d < D ? __uint_as_float((uint32_t)src[d] << 16) : 0.f;
-    amax = fmaxf(amax, fabsf(x[i]));
-  }
-  for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
-  const int e = e4m3_exponent_for(amax);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int d = lane + 64 * i;
-    if (d < D) dst[d] = (uint8_t)e4m3_code(ldexpf(x[i], -e));
-  }
-  if (lane == 0) (is_v ? v_scale : k_scale)[row] = ldexpf(1.f, e);
+  quantise_row_wave(src, D, (is_v ? v_codes : k_codes) + row * D,
+                    (is_v ? v_scale : k_scale) + row, lane);
   if (mask && unit == 0 && lane == 0) mask[(size_t)b * cap + pos] = 1;
 }
 
@@ -335,6 +344,248 @@ hipError_t launch_decode_static_fp8(const float* q, void* k_codes, void* v_codes
   if (err != hipSuccess || plan.max_splits <= 1) return err;
   return launch_static_merge(w, B, H, D, plan.chunk, plan.max_splits, valid_len, cap, out, lse,
                              stream);
+}
+
+// ---------------------------------------------------------------------------
+// paged_append_fp8: the new token of sequence b is its last token (position
+// len_b - 1, len_b = seq_lens[b+1] - seq_lens[b] counting it), placed through the
+// block table like every other token: block block_tables[b][seq_offset[b] / bs +
+// t / bs], slot t % bs.  One wave per (sequence, KV head, K or V), as
+// kv_append_fp8.  A sequence of length 0 or a bad table entry sets an error bit
+// (DAKV_ERR_SEQ_LENS, DAKV_ERR_BLOCK_ID) and writes nothing.
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256)
+paged_append_fp8_kernel(uint8_t* __restrict__ k_codes, uint8_t* __restrict__ v_codes,
+                        float* __restrict__ k_scale, float* __restrict__ v_scale,
+                        const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new,
+                        const int32_t* __restrict__ block_tables, int table_cols,
+                        const int32_t* __restrict__ seq_lens,
+                        const int32_t* __restrict__ seq_offset, int Hkv, int D, int num_blocks,
+                        int block_size, int32_t* err_flag) {
+  const int b = blockIdx.y;
+  const int unit = blockIdx.x * 4 + (threadIdx.x >> 6);  // (head, K or V)
+  const int lane = threadIdx.x & 63;
+  if (unit >= 2 * Hkv) return;
+  const int h = unit >> 1;
+  const bool is_v = unit & 1;
+  const bool report = unit == 0 && lane == 0;
+  const int len = seq_lens[b + 1] - seq_lens[b];
+  const int off = seq_offset ? seq_offset[b] : 0;
+  if (len <= 0 || off < 0 || off % block_size != 0) {
+    if (report) raise_flag(err_flag, 8);
+    return;
+  }
+  const int t = len - 1;
+  const int col = off / block_size + t / block_size;
+  if (col >= table_cols) {
+    if (report) raise_flag(err_flag, 8);
+    return;
+  }
+  const int phys = block_tables[(size_t)b * table_cols + col];
+  if (phys < 0 || phys >= num_blocks) {
+    if (report) raise_flag(err_flag, 1);
+    return;
+  }
+  const size_t row = ((size_t)phys * block_size + t % block_size) * Hkv + h;
+  quantise_row_wave((is_v ? v_new : k_new) + ((size_t)b * Hkv + h) * D, D,
+                    (is_v ? v_codes : k_codes) + row * D, (is_v ? v_scale : k_scale) + row,
+                    lane);
+}
+
+hipError_t launch_paged_append_fp8(void* k_codes, void* v_codes, float* k_scale,
+                                   float* v_scale, const void* k_new, const void* v_new,
+                                   const int32_t* block_tables, int table_cols,
+                                   const int32_t* seq_lens, const int32_t* seq_offset, int B,
+                                   int Hkv, int D, int num_blocks, int block_size,
+                                   int32_t* err_flag, hipStream_t stream) {
+  hipLaunchKernelGGL(paged_append_fp8_kernel, dim3((2 * Hkv + 3) / 4, B), dim3(256), 0, stream,
+                     static_cast<uint8_t*>(k_codes), static_cast<uint8_t*>(v_codes), k_scale,
+                     v_scale, static_cast<const uint16_t*>(k_new),
+                     static_cast<const uint16_t*>(v_new), block_tables, table_cols, seq_lens,
+                     seq_offset, Hkv, D, num_blocks, block_size, err_flag);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Paged GQA decode over the FP8 pool: paged_rows_kernel's work split (one
+// workgroup per (sequence, split) over all KV heads; lane group gi serves KV head
+// gi % Hkv at token slot gi / Hkv) with 8 codes (8 bytes) per lane and a row's K
+// and V scales read by its lane group (one 4-byte address for the 16 lanes).  The
+// K scale multiplies the row's scores, the V scale its weight in O.
+// ---------------------------------------------------------------------------
+template <int G>
+__global__ void __launch_bounds__(kThreads)
+paged_rows_fp8_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ k_codes,
+                      const uint8_t* __restrict__ v_codes, const float* __restrict__ k_scale,
+                      const float* __restrict__ v_scale, const int32_t* __restrict__ block_tables,
+                      int table_cols, const int32_t* __restrict__ seq_lens,
+                      const int32_t* __restrict__ seq_offset, int Hkv, int num_blocks,
+                      int block_size, int bs_log2, int max_len, float scale_log2, int chunk,
+                      int max_splits, Workspace ws, float* __restrict__ out,
+                      float* __restrict__ lse, int32_t* err_flag) {
+  constexpr int D = 128;
+  constexpr int LPR = D / 8;
+  constexpr int U = PagedShape<G>::U;
+  constexpr int kSteps = PagedShape<G>::kSteps;
+  __shared__ int tbl[kMaxTableSpan];
+  const int split = blockIdx.x % max_splits;
+  const int b = blockIdx.x / max_splits;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int sub = lane % LPR;
+  const int gi = wave * 4 + lane / LPR;
+  const int ts = kRowGroups / Hkv;
+  const int h = gi % Hkv;
+  const int slot = gi / Hkv;
+  const int Hq = Hkv * G;
+  uint4 qraw[G];
+#pragma unroll
+  for (int j = 0; j < G; ++j)
+    qraw[j] = load16(q + ((size_t)b * Hq + (size_t)h * G + j) * D + sub * 8);
+  int toff = 0;
+  const int L = paged_len(seq_lens, seq_offset, b, block_size, table_cols, max_len, &toff,
+                          err_flag, split == 0 && threadIdx.x == 0);
+  const int n = L > 0 ? (L + chunk - 1) / chunk : 1;
+  if (split >= n) return;
+  const int r0 = split * chunk;
+  const int r1 = min(r0 + chunk, L);
+  const int blk0 = r0 >> bs_log2;
+  const int nblk = r1 > r0 ? ((r1 - 1) >> bs_log2) - blk0 + 1 : 0;
+  for (int i = threadIdx.x; i < nblk; i += kThreads) {
+    int phys = block_tables[(size_t)b * table_cols + toff + blk0 + i];
+    if (phys < 0 || phys >= num_blocks) {
+      raise_flag(err_flag, 1);
+      phys = -1;
+    }
+    tbl[i] = phys;
+  }
+  float qr[G][8];
+#pragma unroll
+  for (int j = 0; j < G; ++j) {
+    unpack8(qraw[j], qr[j]);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) qr[j][i] *= scale_log2;
+  }
+  __syncthreads();
+  const int bs_mask = block_size - 1;
+  const size_t code_off = (size_t)h * D + (size_t)sub * 8;
+  // the pool row (block, slot) of token t, or 0 with ok cleared (an in-bounds dummy)
+  auto row_at = [&](int t, bool& ok) -> size_t {
+    const int phys = ok ? tbl[(t >> bs_log2) - blk0] : -1;
+    ok = phys >= 0;
+    return ok ? (size_t)phys * block_size + (t & bs_mask) : 0;
+  };
+  auto issue = [&](int t0, u32x2_t (&kw)[U], u32x2_t (&vw)[U], float (&ksc)[U],
+                   float (&vsc)[U], bool (&ok)[U]) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int t = t0 + u * ts;
+      ok[u] = t < r1;
+      const size_t row = row_at(t, ok[u]);
+      const size_t c = row * Hkv * D + code_off;
+      kw[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(k_codes + c));
+      vw[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(v_codes + c));
+      ksc[u] = k_scale[row * Hkv + h];
+      vsc[u] = v_scale[row * Hkv + h];
+    }
+  };
+  HeadState<G> st;
+  init_state(st);
+  auto consume = [&](const u32x2_t (&kw)[U], const u32x2_t (&vw)[U], const float (&ksc)[U],
+                     const float (&vsc)[U], const bool (&ok)[U]) {
+    float s[G][U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float kf[8];
+      unpack8_fp8(kw[u], kf);
+#pragma unroll
+      for (int j = 0; j < G; ++j) {
+        float acc = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc = fmaf(qr[j][i], kf[i], acc);
+        acc = group_sum<LPR>(acc);
+        s[j][u] = ok[u] ? acc * ksc[u] : kNegInf;
+      }
+    }
+    float vf[U][8];
+#pragma unroll
+    for (int u = 0; u < U; ++u) unpack8_fp8(vw[u], vf[u]);
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+      float mnew = st.m[j];
+#pragma unroll
+      for (int u = 0; u < U; ++u) mnew = fmaxf(mnew, s[j][u]);
+      const float ms = mnew == kNegInf ? 0.f : mnew;
+      const float alpha = exp2_fast(st.m[j] - ms);
+      float psum = 0.f;
+      float pw[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const float p = exp2_fast(s[j][u] - ms);
+        psum += p;
+        pw[u] = p * vsc[u];
+      }
+      st.l[j] = fmaf(st.l[j], alpha, psum);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) st.o[j][i] *= alpha;
+      st.m[j] = mnew;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) st.o[j][i] = fmaf(pw[u], vf[u][i], st.o[j][i]);
+      }
+    }
+  };
+  const int step = U * ts;
+  const int super = step * kSteps;
+  for (int base = r0; base < r1; base += super) {
+    u32x2_t kw[2][U], vw[2][U];
+    float ksc[2][U], vsc[2][U];
+    bool ok[2][U];
+    issue(base + slot, kw[0], vw[0], ksc[0], vsc[0], ok[0]);
+#pragma unroll
+    for (int s = 0; s < kSteps; ++s) {
+      if (s + 1 < kSteps)
+        issue(base + slot + (s + 1) * step, kw[(s + 1) & 1], vw[(s + 1) & 1], ksc[(s + 1) & 1],
+              vsc[(s + 1) & 1], ok[(s + 1) & 1]);
+      consume(kw[s & 1], vw[s & 1], ksc[s & 1], vsc[s & 1], ok[s & 1]);
+    }
+  }
+  finish_split_rows<G>(st, gi, sub, Hkv, ts, ws, (size_t)b * Hq, split, n, max_splits, out, lse);
+}
+
+hipError_t launch_decode_paged_fp8(const void* q, const void* k_codes, const void* v_codes,
+                                   const float* k_scale, const float* v_scale,
+                                   const int32_t* block_tables, int table_cols,
+                                   const int32_t* seq_lens, const int32_t* seq_offset, int B,
+                                   int Hq, int Hkv, int num_blocks, int block_size,
+                                   int max_seq_len, float scale, float* out, float* lse,
+                                   void* ws, const SplitPlan& plan, int32_t* err_flag,
+                                   hipStream_t stream) {
+  const Workspace w = carve(ws, (size_t)B * Hq, plan.max_splits, 128);
+  int bs_log2 = 0;
+  while ((1 << bs_log2) < block_size) ++bs_log2;
+  const auto* qb = static_cast<const uint16_t*>(q);
+  const auto* kc = static_cast<const uint8_t*>(k_codes);
+  const auto* vc = static_cast<const uint8_t*>(v_codes);
+  const dim3 grid((unsigned)(B * plan.max_splits));
+#define DAKV_PAGED_FP8(GG)                                                                    \
+  hipLaunchKernelGGL(paged_rows_fp8_kernel<GG>, grid, dim3(kThreads), 0, stream, qb, kc, vc, \
+                     k_scale, v_scale, block_tables, table_cols, seq_lens, seq_offset, Hkv,  \
+                     num_blocks, block_size, bs_log2, max_seq_len, scale * kLog2e,           \
+                     plan.chunk, plan.max_splits, w, out, lse, err_flag)
+  switch (Hq / Hkv) {
+    case 1: DAKV_PAGED_FP8(1); break;
+    case 2: DAKV_PAGED_FP8(2); break;
+    case 4: DAKV_PAGED_FP8(4); break;
+    case 8: DAKV_PAGED_FP8(8); break;
+    default: return hipErrorInvalidValue;
+  }
+#undef DAKV_PAGED_FP8
+  const hipError_t err = hipGetLastError();
+  if (err != hipSuccess || plan.max_splits <= 1) return err;
+  return launch_paged_merge(w, B, Hq, plan.chunk, plan.max_splits, seq_lens, seq_offset,
+                            block_size, table_cols, max_seq_len, out, lse, stream);
 }
 
 }  // namespace dakv

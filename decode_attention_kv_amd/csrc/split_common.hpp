@@ -374,6 +374,75 @@ __device__ __forceinline__ void finish_split(const HeadState<G, E>& st, int lane
   }
 }
 
+// ------------------------------------------------------------------ paged layout
+constexpr int kMaxTableSpan = 72;  // block-table entries one split may touch
+
+// Step shape of the paged kernel per group size G: U rows per lane group per
+// step and kSteps steps per unrolled super-step (fewer rows in flight when each
+// row feeds more heads and the state takes more registers).
+template <int G> struct PagedShape;
+template <> struct PagedShape<1> { static constexpr int U = 4, kSteps = 2; };
+template <> struct PagedShape<2> { static constexpr int U = 4, kSteps = 2; };
+template <> struct PagedShape<4> { static constexpr int U = 2, kSteps = 4; };
+template <> struct PagedShape<8> { static constexpr int U = 2, kSteps = 2; };
+
+constexpr int kRowGroups = 16;  // lane groups of 16 lanes in a workgroup (D = 128)
+constexpr int kPagedRowsTarget = 4096;  // workgroups of a call, if all were full length
+
+// End of an all-heads split: every group's state goes to LDS, then each output
+// element combines the TS groups of its KV head and is written out directly
+// (one split) or as this split's partial.
+template <int G>
+__device__ __forceinline__ void finish_split_rows(const HeadState<G>& st, int gi, int sub, int Hkv,
+                                                  int ts, const Workspace& ws, size_t head0,
+                                                  int split, int n, int max_splits,
+                                                  float* __restrict__ out,
+                                                  float* __restrict__ lse) {
+  constexpr int D = 128;
+  __shared__ float sm_o[kRowGroups][G][D];
+  __shared__ float sm_m[kRowGroups][G];
+  __shared__ float sm_l[kRowGroups][G];
+#pragma unroll
+  for (int j = 0; j < G; ++j) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) sm_o[gi][j][sub * 8 + i] = st.o[j][i];
+    if (sub == 0) {
+      sm_m[gi][j] = st.m[j];
+      sm_l[gi][j] = st.l[j];
+    }
+  }
+  __syncthreads();
+  const int total = Hkv * G * D;
+  for (int idx = threadIdx.x; idx < total; idx += kThreads) {
+    const int hj = idx / D;  // query head within the sequence: h * G + j
+    const int d = idx - hj * D;
+    const int h = hj / G;
+    const int j = hj - h * G;
+    float M = kNegInf;
+    for (int s = 0; s < ts; ++s) M = fmaxf(M, sm_m[h + s * Hkv][j]);
+    float val = 0.f, lse2 = kNegInf;
+    if (M != kNegInf) {
+      float num = 0.f, den = 0.f;
+      for (int s = 0; s < ts; ++s) {
+        const int g2 = h + s * Hkv;
+        const float wt = exp2_fast(sm_m[g2][j] - M);
+        num += wt * sm_o[g2][j][d];
+        den += wt * sm_l[g2][j];
+      }
+      val = num / den;
+      lse2 = M + __log2f(den);
+    }
+    if (n == 1) {
+      out[(head0 + hj) * D + d] = val;
+      if (lse && d == 0) lse[head0 + hj] = lse2 * kLn2;
+    } else {
+      const size_t row = (head0 + hj) * max_splits + split;
+      ws.o[row * D + d] = val;
+      if (d == 0) ws.lse[row] = lse2;
+    }
+  }
+}
+
 constexpr int kStaticChunkMax = 256;  // rows per split of the static layout, at most
 
 __host__ inline Workspace carve(void* ws, size_t heads, int max_splits, int D) {
@@ -382,6 +451,12 @@ __host__ inline Workspace carve(void* ws, size_t heads, int max_splits, int D) {
   w.lse = w.o + heads * (size_t)max_splits * D;
   return w;
 }
+
+// merge_kernel over the splits of a paged call (D = 128, lengths from seq_lens).
+hipError_t launch_paged_merge(const Workspace& w, int B, int Hq, int chunk, int max_splits,
+                              const int32_t* seq_lens, const int32_t* seq_offset,
+                              int block_size, int table_cols, int max_seq_len, float* out,
+                              float* lse, hipStream_t stream);
 
 // merge_kernel over the splits of a static-layout call (one launch, B * H heads).
 hipError_t launch_static_merge(const Workspace& w, int B, int H, int D, int chunk,

@@ -424,6 +424,75 @@ def decode_attn_paged(q, key_cache, value_cache, block_tables, seq_lens, seq_off
     return out, lse
 
 
+def paged_append_fp8(k_codes, v_codes, k_scale, v_scale, k_new, v_new, block_tables,
+                     seq_lens, seq_offset=None, err_flag=None):
+    """Quantise each sequence's new token (bf16 [B, Hkv, D]) into its last position
+    len_b - 1 of the FP8 pool (codes uint8 [num_blocks, block_size, Hkv, D], scales
+    fp32 [num_blocks, block_size, Hkv]), placed through the block table."""
+    _need(k_codes, "k_codes", torch.uint8)
+    nb, bs, Hkv, D = k_codes.shape
+    _need(v_codes, "v_codes", torch.uint8, (nb, bs, Hkv, D))
+    _need(k_scale, "k_scale", torch.float32, (nb, bs, Hkv))
+    _need(v_scale, "v_scale", torch.float32, (nb, bs, Hkv))
+    _need(k_new, "k_new", torch.bfloat16)
+    B = k_new.shape[0]
+    _need(k_new, "k_new", torch.bfloat16, (B, Hkv, D))
+    _need(v_new, "v_new", torch.bfloat16, (B, Hkv, D))
+    _need(block_tables, "block_tables", torch.int32)
+    if block_tables.dim() != 2 or block_tables.shape[0] != B:
+        raise ValueError("block_tables must be [B, cols]")
+    _need(seq_lens, "seq_lens", torch.int32, (B + 1,))
+    _opt(seq_offset, "seq_offset", torch.int32, (B,))
+    _opt(err_flag, "err_flag", torch.int32, (1,))
+    check("paged_append_fp8", lib().dakv_paged_append_fp8(
+        _p(k_codes), _p(v_codes), _p(k_scale), _p(v_scale), _p(k_new), _p(v_new),
+        _p(block_tables), block_tables.shape[1], _p(seq_lens), _p(seq_offset), B, Hkv, D, nb,
+        bs, _p(err_flag), _stream()))
+
+
+def decode_attn_paged_fp8(q, k_codes, v_codes, k_scale, v_scale, block_tables, seq_lens,
+                          seq_offset=None, max_seq_len=None, scale=None, out=None, lse=None,
+                          workspace=None, num_splits=0, err_flag=None, validate=False,
+                          want_lse=True):
+    """decode_attn_paged over the FP8 pool.  Returns ``(out, lse)``."""
+    _need(q, "q", torch.bfloat16)
+    B, Hq, D = q.shape
+    _need(k_codes, "k_codes", torch.uint8)
+    nb, bs, Hkv, Dk = k_codes.shape
+    if Dk != D:
+        raise ValueError("the pool's head dim must equal q's")
+    _need(v_codes, "v_codes", torch.uint8, (nb, bs, Hkv, D))
+    _need(k_scale, "k_scale", torch.float32, (nb, bs, Hkv))
+    _need(v_scale, "v_scale", torch.float32, (nb, bs, Hkv))
+    _need(block_tables, "block_tables", torch.int32)
+    if block_tables.dim() != 2 or block_tables.shape[0] != B:
+        raise ValueError("block_tables must be [B, cols]")
+    cols = block_tables.shape[1]
+    _need(seq_lens, "seq_lens", torch.int32, (B + 1,))
+    _opt(seq_offset, "seq_offset", torch.int32, (B,))
+    if validate:
+        validate_paged(block_tables, seq_lens, seq_offset, nb, bs)
+    if max_seq_len is None:
+        lens = np.diff(_host_i32(seq_lens))
+        max_seq_len = int(lens.max()) if lens.size else 0
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
+    _need(out, "out", torch.float32, (B, Hq, D))
+    if lse is None and want_lse:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    _opt(lse, "lse", torch.float32, (B, Hq))
+    _opt(err_flag, "err_flag", torch.int32, (1,))
+    nbytes = decode_attn_paged_workspace_size(B, Hq, D, int(max_seq_len), bs)
+    ws = _workspace(nbytes, q.device, workspace)
+    check("decode_attn_paged_fp8", lib().dakv_decode_attn_paged_fp8(
+        _p(q), _p(k_codes), _p(v_codes), _p(k_scale), _p(v_scale), _p(block_tables), cols,
+        _p(seq_lens), _p(seq_offset), B, Hq, Hkv, D, nb, bs, int(max_seq_len), float(scale),
+        _p(out), _p(lse), _p(ws), ws.numel(), int(num_splits), _p(err_flag), _stream()))
+    return out, lse
+
+
 # ----------------------------------------------------- sparse_topk_decode_attn
 
 

@@ -299,6 +299,43 @@ int dakv_decode_attn_paged(const void* q, const void* key_cache, const void* val
                            size_t workspace_bytes, int num_splits, int32_t* err_flag,
                            void* stream);
 
+/*
+ * FP8 paged pool (the FP8 cache above in the paged layout): codes uint8
+ * [num_blocks, block_size, Hkv, D] and one fp32 power-of-two scale per (block,
+ * slot, KV head) [num_blocks, block_size, Hkv] for K and for V; values decode to
+ * code * scale.
+ *
+ * paged_append_fp8 -- quantise each sequence's new token (k_new, v_new bf16
+ * [B, Hkv, D], finite) into its last position t = len_b - 1 (len_b =
+ * seq_lens[b+1] - seq_lens[b], counting the new token), at block
+ * block_tables[b][seq_offset[b] / block_size + t / block_size], slot
+ * t % block_size: the paged address resolution of decode_attn_paged and the
+ * append-at-write-position of kv_append ([NPU-LLM] Part 1; [PyPTO] 3.2).  A
+ * sequence of length 0 or an entry past its table sets DAKV_ERR_SEQ_LENS, a bad
+ * block id DAKV_ERR_BLOCK_ID; that sequence is skipped.  D <= 256.
+ */
+int dakv_paged_append_fp8(void* k_codes, void* v_codes, float* k_scale, float* v_scale,
+                          const void* k_new, const void* v_new, const int32_t* block_tables,
+                          int table_cols, const int32_t* seq_lens, const int32_t* seq_offset,
+                          int B, int Hkv, int D, int num_blocks, int block_size,
+                          int32_t* err_flag, void* stream);
+
+/*
+ * decode_attn_paged_fp8 -- decode_attn_paged over the FP8 pool: each row's K
+ * scale multiplies its scores, its V scale its weight in the output.  Arguments
+ * and workspace (dakv_decode_attn_paged_workspace_size) as decode_attn_paged.
+ * Supported: D = 128, Hkv dividing 16, Hq / Hkv in {1, 2, 4, 8}, block_size in
+ * {16, 32, 64, 128}.
+ */
+int dakv_decode_attn_paged_fp8(const void* q, const void* k_codes, const void* v_codes,
+                               const float* k_scale, const float* v_scale,
+                               const int32_t* block_tables, int table_cols,
+                               const int32_t* seq_lens, const int32_t* seq_offset, int B,
+                               int Hq, int Hkv, int D, int num_blocks, int block_size,
+                               int max_seq_len, float scale, float* out, float* lse,
+                               void* workspace, size_t workspace_bytes, int num_splits,
+                               int32_t* err_flag, void* stream);
+
 /* ========================================================================
  * Top-k sparse MLA-style decode   ([FlashMLA] "Mathematical formulation")
  * ======================================================================== */
