@@ -101,8 +101,12 @@ __device__ __forceinline__ void unpack8_fp8(const u32x2_t& w, float (&f)[8]) {
 // first quantises the new token's K and V rows (as kv_append_fp8 does) in the
 // lanes that later consume row p; they store codes and scales and keep both in
 // registers for that row, and p is attended whatever its mask entry says.
+// Occupancy: at one or two steps the kernel fits 7 waves per SIMD (<= 72 VGPRs);
+// left to itself the append variant takes 73 and drops to 6 (the fused batch-8
+// call measured 32.8 us at 6 waves, 31.4 us at 7).
 template <int D, int U, int kSteps, bool kAppend>
 __global__ void __launch_bounds__(kThreads)
+__attribute__((amdgpu_waves_per_eu(kSteps <= 2 ? 7 : 3)))
 static_decode_fp8_kernel(const float* __restrict__ q, uint8_t* __restrict__ k_codes,
                          uint8_t* __restrict__ v_codes, float* __restrict__ k_scale,
                          float* __restrict__ v_scale, int32_t* __restrict__ mask,
@@ -413,6 +417,13 @@ hipError_t launch_paged_append_fp8(void* k_codes, void* v_codes, float* k_scale,
 // and V scales read by its lane group (one 4-byte address for the 16 lanes).  The
 // K scale multiplies the row's scores, the V scale its weight in O.
 // ---------------------------------------------------------------------------
+// Step shape over the FP8 pool (rows per lane group per step, steps per unrolled
+// super-step).  Measured at G = 4 (batch 64, block 16): U = 4 in one step 262 us,
+// the bf16 kernel's 2 x 4 steps 318 us (178 VGPRs: 2 waves per SIMD), 2 x 2
+// 291 us, 8 x 1 290 us; the other group sizes keep the bf16 shape.
+template <int G> struct PagedShapeFp8 : PagedShape<G> {};
+template <> struct PagedShapeFp8<4> { static constexpr int U = 4, kSteps = 1; };
+
 template <int G>
 __global__ void __launch_bounds__(kThreads)
 paged_rows_fp8_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ k_codes,
@@ -425,8 +436,8 @@ paged_rows_fp8_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict_
                       float* __restrict__ lse, int32_t* err_flag) {
   constexpr int D = 128;
   constexpr int LPR = D / 8;
-  constexpr int U = PagedShape<G>::U;
-  constexpr int kSteps = PagedShape<G>::kSteps;
+  constexpr int U = PagedShapeFp8<G>::U;
+  constexpr int kSteps = PagedShapeFp8<G>::kSteps;
   __shared__ int tbl[kMaxTableSpan];
   const int split = blockIdx.x % max_splits;
   const int b = blockIdx.x / max_splits;
