@@ -240,3 +240,19 @@ def test_paged_gqa_full_size_sampled():
                                                case.scale)
         assert_attention_close(out[b:b + 1], ref_out)
         assert_lse_close(lse[b:b + 1], ref_lse)
+
+
+def test_paged_longest_supported_sequence():
+    """Block 16: 256 splits of 1024 tokens = 262144 tokens is the longest sequence the
+    paged kernel takes; one token more is refused on the host."""
+    print("paged 262144 tokens", flush=True)
+    case = workloads.paged_case([262144, 3], Hq=4, Hkv=1, D=128, block_size=16, device=DEV,
+                                seed=77)
+    out, lse = run_paged(case)
+    ref_out, ref_lse = oracle_paged(case)
+    assert_attention_close(out, ref_out)
+    assert_lse_close(lse, ref_lse)
+    t, s, o = to_dev(case.index)
+    with pytest.raises(ValueError):
+        dakv.decode_attn_paged(case.q, case.key_cache, case.value_cache, t, s, o,
+                               max_seq_len=262145)

@@ -358,3 +358,19 @@ def test_fused_step_position_outside_attended_rows_and_out_of_range():
     ref, _ = oracle.decode_static(npy(case.q), k0, bits(case.v_cache), None, [100, 300],
                                   case.scale)
     assert_attention_close(npy(out), ref)
+
+
+def test_largest_capacity_uses_all_256_splits():
+    """Capacity 65536 (the static kernel's limit: 256 splits of 256 rows), full and
+    ragged lengths; one more row than the limit is refused on the host."""
+    print("static cap 65536", flush=True)
+    case = workloads.static_case(2, 2, 64, 65536, [65536, 40000], device=DEV, seed=36,
+                                 garbage_std=1.0)
+    out, lse = run_static(case)
+    ref_out, ref_lse = oracle_static(case)
+    assert_attention_close(out, ref_out)
+    assert_lse_close(lse, ref_lse)
+    big = torch.zeros((1, 1, 65537, 64), dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(ValueError):
+        dakv.decode_attn_static(torch.zeros((1, 1, 64), device=DEV), big, big,
+                                valid_len=torch.tensor([1], dtype=torch.int32, device=DEV))
