@@ -1,0 +1,154 @@
+"""FP4 KV cache for decode: E2M1 codes with a power-of-two scale per row (fp64 oracle).
+
+Test infrastructure only.
+
+Source: "FlashMLA on Huawei Ascend", the section on how many VECTOR cores serve one
+CUBE core (item 2): at decode time the kernel reads the KV cache in FP8 or FP4 and
+dequantises it to bfloat16.  The page fixes neither the FP4 variant nor the scale;
+the readings taken here follow the FP8 cache's (one power-of-two scale per cached
+row, for K and for V, kept in its own array):
+
+* the FP4 format is E2M1 of the OCP microscaling specification: sign, 2-bit exponent
+  with bias 1, 1-bit mantissa, one subnormal (0.5), no infinities or NaN; the
+  magnitudes are 0, 0.5, 1, 1.5, 2, 3, 4, 6;
+* the scale of a row is s = 2^e with e the smallest integer for which
+  max|x| <= 6 * 2^e (a row of zeros gets e = 0); the code of x is x / s (exact)
+  rounded to the nearest E2M1 value, ties to the even code, zero results as +0;
+* two codes share a byte, element 2i in the low four bits and 2i + 1 in the high
+  four bits (the microscaling specification's packing);
+* the cached value is decode(code) * s, exactly representable in bf16, so the
+  attention over the FP4 cache is the attention of the static layout over those
+  values.
+"""
+
+import math
+
+import numpy as np
+
+from .bf16 import widen
+from .static_cache import attended_rows, softmax_weighted_sum
+
+E2M1_MAX = 6.0
+_MAGS = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+
+
+def e2m1_decode(nibbles):
+    """4-bit codes (any integer array, values 0..15) -> float64 values."""
+    c = np.asarray(nibbles).astype(np.int64) & 0xF
+    mag = _MAGS[c & 7]
+    return np.where(c & 8, -mag, mag)
+
+
+def e2m1_encode(x):
+    """Values with |x| <= 6 -> the nearest E2M1 code (ties to the even code; a
+    result of zero is the +0 code)."""
+    x = np.asarray(x, dtype=np.float64)
+    a = np.abs(x)
+    if np.any(a > E2M1_MAX):
+        raise ValueError("E2M1 input outside [-6, 6]")
+    hi = np.clip(np.searchsorted(_MAGS, a, side="left"), 0, 7)   # first magnitude >= a
+    lo = np.maximum(hi - 1, 0)
+    d_lo = a - _MAGS[lo]
+    d_hi = _MAGS[hi] - a
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0) & (hi != lo))
+    code = np.where(pick_hi, hi, lo)
+    code = np.where(a == _MAGS[hi], hi, code).astype(np.uint8)
+    neg = np.signbit(x) & (code != 0)
+    return np.where(neg, code | 8, code).astype(np.uint8)
+
+
+def scale_exponent(amax):
+    """Smallest integer e with amax <= 6 * 2^e (0 for amax == 0)."""
+    amax = float(amax)
+    if amax == 0.0:
+        return 0
+    _, e = math.frexp(amax / E2M1_MAX)
+    while amax <= E2M1_MAX * 2.0 ** (e - 1):
+        e -= 1
+    while amax > E2M1_MAX * 2.0 ** e:
+        e += 1
+    return e
+
+
+def pack(codes):
+    """4-bit codes ``[..., D]`` (D even) -> bytes ``[..., D/2]``, element 2i low."""
+    codes = np.asarray(codes, dtype=np.uint8)
+    return (codes[..., 0::2] | (codes[..., 1::2] << 4)).astype(np.uint8)
+
+
+def unpack(packed):
+    """Bytes ``[..., D/2]`` -> 4-bit codes ``[..., D]``."""
+    packed = np.asarray(packed, dtype=np.uint8)
+    out = np.empty(packed.shape[:-1] + (2 * packed.shape[-1],), dtype=np.uint8)
+    out[..., 0::2] = packed & 0xF
+    out[..., 1::2] = packed >> 4
+    return out
+
+
+def quantize_rows(x_bits):
+    """bf16 bit patterns ``[..., D]`` -> (packed codes uint8 ``[..., D/2]``, scale
+    float64 ``[...]``)."""
+    x = widen(x_bits)
+    if not np.all(np.isfinite(x)):
+        raise ValueError("a row with NaN or Inf has no E2M1 encoding")
+    if x.shape[-1] % 2:
+        raise ValueError("the row length must be even")
+    lead = x.shape[:-1]
+    flat = x.reshape(-1, x.shape[-1])
+    codes = np.empty(flat.shape, dtype=np.uint8)
+    scale = np.empty(flat.shape[0])
+    for r in range(flat.shape[0]):
+        e = scale_exponent(np.max(np.abs(flat[r])))
+        scale[r] = 2.0 ** e
+        codes[r] = e2m1_encode(flat[r] / scale[r])
+    return pack(codes.reshape(x.shape)), scale.reshape(lead)
+
+
+def dequantize(packed, scale):
+    return e2m1_decode(unpack(packed)) * np.asarray(scale, dtype=np.float64)[..., None]
+
+
+def kv_append_fp4(k_codes, v_codes, k_scale, v_scale, k_new, v_new, write_pos, mask=None):
+    """Quantise the new token's K and V rows (bf16 bits ``[B, H, D]``) and store the
+    packed codes and scales at row write_pos[b] (codes ``[B, H, cap, D/2]`` uint8,
+    scales ``[B, H, cap]``).  Returns updated copies ``(k_codes, v_codes, k_scale,
+    v_scale, mask)``; a position outside ``[0, cap)`` is an error."""
+    k_codes, v_codes = np.array(k_codes, copy=True), np.array(v_codes, copy=True)
+    k_scale, v_scale = np.array(k_scale, copy=True), np.array(v_scale, copy=True)
+    B, H, cap, _ = k_codes.shape
+    kq, ks = quantize_rows(k_new)
+    vq, vs = quantize_rows(v_new)
+    if mask is not None:
+        mask = np.array(mask, copy=True)
+    for b in range(B):
+        pos = int(np.asarray(write_pos).reshape(-1)[b])
+        if pos < 0 or pos >= cap:
+            raise ValueError(f"write position {pos} outside [0, {cap})")
+        k_codes[b, :, pos], v_codes[b, :, pos] = kq[b], vq[b]
+        k_scale[b, :, pos], v_scale[b, :, pos] = ks[b], vs[b]
+        if mask is not None:
+            mask[b, pos] = 1
+    return k_codes, v_codes, k_scale, v_scale, mask
+
+
+def decode_static_fp4(q, k_codes, v_codes, k_scale, v_scale, mask=None, valid_len=None,
+                      scale=None):
+    """Masked decode attention over the FP4 cache: the attention of the static layout
+    over the dequantised rows decode(code) * s (same attended-row rule)."""
+    if mask is None and valid_len is None:
+        raise ValueError("give a mask, a valid length, or both")
+    q = np.asarray(q, dtype=np.float64)
+    B, H, cap, half = np.shape(k_codes)
+    D = 2 * half
+    if scale is None:
+        scale = 1.0 / np.sqrt(D)
+    out = np.zeros((B, H, D))
+    lse = np.full((B, H), -np.inf)
+    for b in range(B):
+        rows = attended_rows(cap, None if mask is None else mask[b],
+                             None if valid_len is None else valid_len[b])
+        for h in range(H):
+            K = dequantize(k_codes[b, h, rows], k_scale[b, h, rows])
+            V = dequantize(v_codes[b, h, rows], v_scale[b, h, rows])
+            out[b, h], lse[b, h] = softmax_weighted_sum(scale * (K @ q[b, h]), V)
+    return out, lse

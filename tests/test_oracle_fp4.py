@@ -1,0 +1,98 @@
+"""Pins of the FP4 (E2M1) KV cache oracle -- CPU only."""
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import fp4, round_to_bf16_bits
+
+
+def e2m1_value(code):
+    """The format's definition: sign bit 3, exponent bits 2..1 with bias 1, mantissa
+    bit 0; exponent field 0 is the subnormal m * 2^0 * 0.5."""
+    s, e, m = (code >> 3) & 1, (code >> 1) & 3, code & 1
+    mag = m * 0.5 if e == 0 else (1.0 + 0.5 * m) * 2.0 ** (e - 1)
+    return -mag if s else mag
+
+
+def test_every_code_decodes_by_the_format_definition():
+    codes = np.arange(16)
+    assert np.array_equal(fp4.e2m1_decode(codes), [e2m1_value(int(c)) for c in codes])
+    assert sorted(set(np.abs(fp4.e2m1_decode(codes)))) == [0, 0.5, 1, 1.5, 2, 3, 4, 6]
+
+
+def test_encoding_is_the_nearest_value_ties_to_even_by_brute_force():
+    vals = np.array([e2m1_value(c) for c in range(16)])
+    grid = np.unique(np.concatenate([np.linspace(-6, 6, 2401), (vals[:-1] + vals[1:]) / 2,
+                                     vals, [0.25, -0.25, 0.75, 5.0, -5.0]]))
+    grid = grid[np.abs(grid) <= 6]
+    got = fp4.e2m1_encode(grid)
+    for x, c in zip(grid, got):
+        d = np.abs(vals - x)
+        best = [k for k in range(16) if d[k] == d.min()]
+        if vals[best[0]] == 0 and 0 in best:
+            assert c == 0, x                   # nearest value (or a tie with) zero: +0
+            continue
+        assert c in best, (x, c, best)
+        if len(best) > 1:
+            assert c % 2 == 0, (x, c, best)    # a tie goes to the even code
+
+
+def test_scale_is_the_smallest_power_of_two_that_fits():
+    for amax in [6.0, 6.0001, 3.0, 3.0001, 1e-30, 1e30, 0.7, 12.0]:
+        e = fp4.scale_exponent(amax)
+        assert amax <= 6.0 * 2.0 ** e and amax > 6.0 * 2.0 ** (e - 1)
+    assert fp4.scale_exponent(0.0) == 0
+
+
+def test_packing_puts_the_even_element_in_the_low_four_bits():
+    codes = np.array([[1, 2, 7, 8, 15, 0]], np.uint8)
+    packed = fp4.pack(codes)
+    assert packed.tolist() == [[0x21, 0x87, 0x0F]]
+    assert np.array_equal(fp4.unpack(packed), codes)
+
+
+def test_quantisation_error_is_at_most_half_a_step_of_the_scaled_grid():
+    rng = np.random.default_rng(50)
+    x = rng.standard_normal((32, 64)) * np.exp(rng.uniform(-6, 6, (32, 1)))
+    bits = round_to_bf16_bits(x)
+    packed, scale = fp4.quantize_rows(bits)
+    xs = oracle.widen(bits) / scale[:, None]
+    assert np.all(np.abs(xs) <= 6.0) and np.all(np.max(np.abs(xs), axis=1) > 3.0)
+    deq = fp4.e2m1_decode(fp4.unpack(packed))
+    mags = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6])
+    a = np.abs(xs)
+    hi = np.minimum(np.searchsorted(mags, a), 7)
+    lo = np.maximum(hi - 1, 0)
+    assert np.all(np.abs(np.abs(deq) - a) <= (mags[hi] - mags[lo]) / 2 + 1e-300)
+
+
+def test_attention_over_fp4_cache_equals_bf16_layout_of_the_same_values():
+    rng = np.random.default_rng(51)
+    B, H, cap, D = 2, 3, 40, 16
+    kc, ks = fp4.quantize_rows(round_to_bf16_bits(rng.standard_normal((B, H, cap, D)) * 2))
+    vc, vs = fp4.quantize_rows(round_to_bf16_bits(rng.standard_normal((B, H, cap, D))))
+    k_deq = round_to_bf16_bits(fp4.dequantize(kc, ks))
+    v_deq = round_to_bf16_bits(fp4.dequantize(vc, vs))
+    assert np.array_equal(oracle.widen(k_deq), fp4.dequantize(kc, ks))
+    mask = (rng.uniform(size=(B, cap)) < 0.6).astype(np.int32)
+    q = rng.standard_normal((B, H, D))
+    a, la = oracle.decode_static_fp4(q, kc, vc, ks, vs, mask=mask, valid_len=[33, 40])
+    b, lb = oracle.decode_static(q, k_deq, v_deq, mask=mask, valid_len=[33, 40])
+    assert np.array_equal(a, b) and np.array_equal(la, lb)
+
+
+def test_append_quantises_the_new_row_and_rejects_positions_outside():
+    rng = np.random.default_rng(52)
+    B, H, cap, D = 2, 2, 6, 8
+    kc = np.zeros((B, H, cap, D // 2), np.uint8)
+    ks = np.ones((B, H, cap))
+    kn = round_to_bf16_bits(rng.standard_normal((B, H, D)))
+    vn = round_to_bf16_bits(rng.standard_normal((B, H, D)))
+    mask = np.zeros((B, cap), np.int32)
+    out = oracle.kv_append_fp4(kc, kc, ks, ks, kn, vn, [0, 5], mask)
+    qk, sk = fp4.quantize_rows(kn)
+    assert np.array_equal(out[0][0, :, 0], qk[0]) and np.array_equal(out[2][1, :, 5], sk[1])
+    assert out[4][0].tolist() == [1, 0, 0, 0, 0, 0] and out[4][1, 5] == 1
+    with pytest.raises(ValueError):
+        oracle.kv_append_fp4(kc, kc, ks, ks, kn, vn, [6, 0])
