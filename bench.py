@@ -299,6 +299,66 @@ def fp8_leg(torch, dakv, acc, B=8, steps=10):
             "bf16_equivalent_GBps": round(bf16_bytes / (ms * 1e-3) / 1e9, 1)}
 
 
+def fp4_leg(torch, dakv, acc, B=8, steps=10):
+    """The batch-B LLaMA-7B-shaped step over an FP4 cache: 32 layers x (kv_append_fp4 +
+    decode_attn_static_fp4), same lengths as the bf16 step, captured as a HIP graph.
+    Codes are random bytes (two E2M1 codes each), scales random powers of two."""
+    import workloads
+    lengths = workloads.uniform_lengths(B, 1, 4096, 2)
+    H, D, cap, n_layers = 32, 128, 4096, 32
+    g = torch.Generator(device="cuda:0")
+    g.manual_seed(13)
+    layers = []
+    for _ in range(n_layers):
+        kc = torch.randint(0, 256, (B, H, cap, D // 2), generator=g, device="cuda:0",
+                           dtype=torch.uint8)
+        vc = torch.randint(0, 256, (B, H, cap, D // 2), generator=g, device="cuda:0",
+                           dtype=torch.uint8)
+        ks = torch.exp2(torch.randint(-3, 1, (B, H, cap), generator=g, device="cuda:0").float())
+        vs = torch.exp2(torch.randint(-3, 1, (B, H, cap), generator=g, device="cuda:0").float())
+        q = torch.randn((B, H, D), generator=g, device="cuda:0") * 0.1
+        kn = torch.randn((B, H, D), generator=g, device="cuda:0").to(torch.bfloat16)
+        vn = torch.randn((B, H, D), generator=g, device="cuda:0").to(torch.bfloat16)
+        layers.append((q, kc, vc, ks, vs, kn, vn, torch.empty((B, H, D), device="cuda:0")))
+    mask = torch.zeros((B, cap), dtype=torch.int32, device="cuda:0")
+    for b, L in enumerate(lengths):
+        mask[b, :L - 1] = 1
+    wpos = torch.tensor([L - 1 for L in lengths], dtype=torch.int32, device="cuda:0")
+    vlen = torch.tensor(lengths, dtype=torch.int32, device="cuda:0")
+    ws = torch.zeros(dakv.decode_attn_static_workspace_size(B, H, cap, D), dtype=torch.uint8,
+                     device="cuda:0")
+
+    def run():
+        for q, kc, vc, ks, vs, kn, vn, out in layers:
+            dakv.kv_append_fp4(kc, vc, ks, vs, kn, vn, wpos, mask)
+            dakv.decode_attn_static_fp4(q, kc, vc, ks, vs, mask=mask, valid_len=vlen,
+                                        out=out, workspace=ws, want_lse=False)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run()
+    ms, _ = time_steps(torch, graph.replay, steps, 3)
+    del graph
+    step_bytes = n_layers * (acc.decode_static_fp4_bytes(B, H, D, lengths) +
+                             acc.kv_append_fp4_bytes(B, H, D))
+    bf16_bytes = n_layers * (acc.decode_static_bytes(B, H, D, lengths) +
+                             acc.kv_append_bytes(B, H, D))
+    del layers
+    return {"workload": f"static decode step over an FP4 (E2M1 + row scale) cache: 32 layers x "
+                        f"(kv_append_fp4 + decode_attn_static_fp4), batch {B}, 32 heads x 128, "
+                        f"capacity 4096, same lengths as the bf16 step",
+            "us_per_step": round(ms * 1e3, 1), "algorithmic_bytes_per_step": step_bytes,
+            "GBps": round(step_bytes / (ms * 1e-3) / 1e9, 1),
+            "frac_of_peak": round(step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "bf16_equivalent_GBps": round(bf16_bytes / (ms * 1e-3) / 1e9, 1)}
+
+
 def copy_leg(torch, dakv, acc, counter_pass=False):
     """The page's 7B prefill -> generate hand-over: 32 layers x K and V = 64 tensors
     [1, 32, 1024] copied into [1, 32, 1152] buffers, 1024 rows each (512 MiB)."""
@@ -669,6 +729,8 @@ def main():
         line["copy_kvcache"] = copy_leg(torch, dakv, acc)
         torch.cuda.empty_cache()
         line["static_fp8"] = fp8_leg(torch, dakv, acc)
+        torch.cuda.empty_cache()
+        line["static_fp4"] = fp4_leg(torch, dakv, acc)
     print(json.dumps(line), flush=True)
 
 

@@ -10,6 +10,8 @@ from .ops import (
     kv_append_fp8,
     decode_attn_static_fp8,
     decode_step_static_fp8,
+    kv_append_fp4,
+    decode_attn_static_fp4,
     paged_append_fp8,
     decode_attn_paged_fp8,
     copy_kvcache,
@@ -34,6 +36,8 @@ __all__ = [
     "kv_append_fp8",
     "decode_attn_static_fp8",
     "decode_step_static_fp8",
+    "kv_append_fp4",
+    "decode_attn_static_fp4",
     "paged_append_fp8",
     "decode_attn_paged_fp8",
     "copy_kvcache",

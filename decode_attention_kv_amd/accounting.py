@@ -60,6 +60,23 @@ def kv_append_fp8_bytes(B, H, D, with_mask=True):
         (B * INT32 if with_mask else 0)
 
 
+def decode_static_fp4_bytes(B, H, D, attended, q_elem=FP32, with_mask=True, with_lse=False):
+    """One static decode call over the FP4 cache: half a byte per K and V element plus
+    one fp32 scale per attended row for K and for V."""
+    rows = sum(int(x) for x in attended)
+    kv = rows * H * (D // 2 + FP32) * 2
+    q = B * H * D * q_elem
+    out = B * H * D * FP32 + (B * H * FP32 if with_lse else 0)
+    mask = rows * INT32 if with_mask else 0
+    return kv + q + out + mask + B * INT32
+
+
+def kv_append_fp4_bytes(B, H, D, with_mask=True):
+    """Read the new bf16 rows and the positions; write packed codes and scales (+mask)."""
+    return 2 * B * H * D * BF16 + B * INT32 + 2 * B * H * (D // 2 + FP32) + \
+        (B * INT32 if with_mask else 0)
+
+
 def gather_bytes(lengths, Hk, Dk, Hv, Dv, block_size, with_offset=True):
     """gather_pa_kv_cache: read and write every valid token row of K and V."""
     T = sum(int(x) for x in lengths)

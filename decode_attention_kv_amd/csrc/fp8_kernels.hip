@@ -74,6 +74,81 @@ hipError_t launch_kv_append_fp8(void* k_codes, void* v_codes, float* k_scale, fl
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// kv_append_fp4: as kv_append_fp8 with E2M1 codes (magnitudes 0, 0.5, 1, 1.5, 2, 3,
+// 4, 6; scale 2^e with e the smallest integer for which max|x| <= 6 * 2^e), two
+// codes per byte, element 2i in the low four bits.  One wave per (sequence, head,
+// K or V); lane l quantises elements 2l and 2l + 1 (and 2l + 128, 2l + 129).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int e2m1_exponent_for(float amax) {
+  if (!(amax > 0.f)) return 0;
+  int E;
+  const float f = frexpf(amax, &E);        // amax = f 2^E, f in [0.5, 1); 6 = 0.75 2^3
+  return f <= 0.75f ? E - 3 : E - 2;
+}
+
+// |y| <= 6: the nearest E2M1 magnitude, counted by the midpoints it passes; a
+// midpoint between codes goes to the even one (<= below an even code, < above).
+__device__ __forceinline__ uint32_t e2m1_code(float y) {
+  const float a = fabsf(y);
+  const uint32_t code = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) +
+                        (uint32_t)(a > 1.25f) + (uint32_t)(a >= 1.75f) +
+                        (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) + (uint32_t)(a > 5.f);
+  return (code != 0 && y < 0.f) ? (code | 8u) : code;
+}
+
+__global__ void __launch_bounds__(256)
+kv_append_fp4_kernel(uint8_t* __restrict__ k_codes, uint8_t* __restrict__ v_codes,
+                     float* __restrict__ k_scale, float* __restrict__ v_scale,
+                     const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new,
+                     const int32_t* __restrict__ write_pos, int32_t* __restrict__ mask, int H,
+                     int cap, int D, int32_t* err_flag) {
+  const int b = blockIdx.y;
+  const int unit = blockIdx.x * 4 + (threadIdx.x >> 6);  // (head, K or V)
+  const int lane = threadIdx.x & 63;
+  if (unit >= 2 * H) return;
+  const int h = unit >> 1;
+  const bool is_v = unit & 1;
+  const int pos = write_pos[b];
+  if (pos < 0 || pos >= cap) {
+    if (unit == 0 && lane == 0) raise_flag(err_flag, 2);
+    return;
+  }
+  const uint16_t* src = (is_v ? v_new : k_new) + ((size_t)b * H + h) * D;
+  const size_t row = ((size_t)b * H + h) * cap + pos;
+  uint8_t* dst = (is_v ? v_codes : k_codes) + row * (D / 2);
+  float x[4];
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {            // D <= 256: pairs (2l, 2l+1) and (2l+128, 2l+129)
+    const int d = 2 * lane + 128 * (i >> 1) + (i & 1);
+    x[i] = d < D ? __uint_as_float((uint32_t)src[d] << 16) : 0.f;
+    amax = fmaxf(amax, fabsf(x[i]));
+  }
+  for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+  const int e = e2m1_exponent_for(amax);
+#pragma unroll
+  for (int pr = 0; pr < 2; ++pr) {
+    const int d = 2 * lane + 128 * pr;
+    if (d < D)
+      dst[d / 2] = (uint8_t)(e2m1_code(ldexpf(x[2 * pr], -e)) |
+                             (e2m1_code(ldexpf(x[2 * pr + 1], -e)) << 4));
+  }
+  if (lane == 0) (is_v ? v_scale : k_scale)[row] = ldexpf(1.f, e);
+  if (mask && unit == 0 && lane == 0) mask[(size_t)b * cap + pos] = 1;
+}
+
+hipError_t launch_kv_append_fp4(void* k_codes, void* v_codes, float* k_scale, float* v_scale,
+                                const void* k_new, const void* v_new, const int32_t* write_pos,
+                                int32_t* mask, int B, int H, int cap, int D, int32_t* err_flag,
+                                hipStream_t stream) {
+  hipLaunchKernelGGL(kv_append_fp4_kernel, dim3((2 * H + 3) / 4, B), dim3(256), 0, stream,
+                     static_cast<uint8_t*>(k_codes), static_cast<uint8_t*>(v_codes), k_scale,
+                     v_scale, static_cast<const uint16_t*>(k_new),
+                     static_cast<const uint16_t*>(v_new), write_pos, mask, H, cap, D, err_flag);
+  return hipGetLastError();
+}
+
 // ---------------------------------------------------------- static layout, FP8
 // Split pass of decode_attn_static_fp8: the cache holds E4M3 codes (one byte per
 // element, [B, H, cap, D]) and one power-of-two fp32 scale per row for K and for V
@@ -96,7 +171,37 @@ __device__ __forceinline__ void unpack8_fp8(const u32x2_t& w, float (&f)[8]) {
   f[4] = c[0]; f[5] = c[1]; f[6] = d[0]; f[7] = d[1];
 }
 
+// Code formats of the static split pass: the word one lane loads for its 8
+// elements of a row, how a row's bytes shrink (row bytes = D / kRowDiv), and the
+// widening to fp32.
+struct E4M3Rows {                          // one byte per element
+  typedef u32x2_t Word;
+  static constexpr int kRowDiv = 1;
+  __device__ static Word load(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, kLoadNonTemporal);
+  }
+  __device__ static void unpack(const Word& w, float (&f)[8]) { unpack8_fp8(w, f); }
+};
+
+struct E2M1Rows {                          // half a byte per element, element 2i low
+  typedef uint32_t Word;
+  static constexpr int kRowDiv = 2;
+  __device__ static Word load(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, kLoadNonTemporal);
+  }
+  __device__ static void unpack(const Word& w, float (&f)[8]) {
+    typedef float f2_t __attribute__((ext_vector_type(2)));
+    const f2_t a = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.f, 0);
+    const f2_t b = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.f, 1);
+    const f2_t c = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.f, 2);
+    const f2_t d = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.f, 3);
+    f[0] = a[0]; f[1] = a[1]; f[2] = b[0]; f[3] = b[1];
+    f[4] = c[0]; f[5] = c[1]; f[6] = d[0]; f[7] = d[1];
+  }
+};
+
 //
+// The same pass serves the FP4 cache (Fmt = E2M1Rows, 4-byte loads; no append).
 // With kAppend (decode_step_static_fp8) the split that owns p = write_pos[b]
 // first quantises the new token's K and V rows (as kv_append_fp8 does) in the
 // lanes that later consume row p; they store codes and scales and keep both in
@@ -104,7 +209,7 @@ __device__ __forceinline__ void unpack8_fp8(const u32x2_t& w, float (&f)[8]) {
 // Occupancy: at one or two steps the kernel fits 7 waves per SIMD (<= 72 VGPRs);
 // left to itself the append variant takes 73 and drops to 6 (the fused batch-8
 // call measured 32.8 us at 6 waves, 31.4 us at 7).
-template <int D, int U, int kSteps, bool kAppend>
+template <typename Fmt, int D, int U, int kSteps, bool kAppend>
 __global__ void __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(kSteps <= 2 ? 7 : 3)))
 static_decode_fp8_kernel(const float* __restrict__ q, uint8_t* __restrict__ k_codes,
@@ -121,6 +226,9 @@ static_decode_fp8_kernel(const float* __restrict__ q, uint8_t* __restrict__ k_co
   // the rows a wave loads at once (kWaves * RPW per u) tile 64-row words, so a
   // lane group's row never leaves the word (s kStep + u kWaves RPW) / 64
   static_assert(64 % (kWaves * RPW) == 0, "row words");
+  static_assert(!kAppend || Fmt::kRowDiv == 1, "the fused append writes E4M3 codes");
+  constexpr int kRowBytes = D / Fmt::kRowDiv;
+  typedef typename Fmt::Word Word;
   const int split = blockIdx.x / units;
   const int bh = blockIdx.x - split * units;
   const int max_splits = gridDim.x / units;
@@ -214,27 +322,30 @@ static_decode_fp8_kernel(const float* __restrict__ q, uint8_t* __restrict__ k_co
 #pragma unroll
   for (int k = 0; k < kBallots; ++k) bits[k] = __ballot(r0 + 64 * k + lane < r1 && mv[k] != 0);
   const __amdgpu_buffer_rsrc_t kr_rs = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint8_t*>(k_codes) + (size_t)bh * cap * D, (short)0, cap * D, 0x00020000);
+      const_cast<uint8_t*>(k_codes) + (size_t)bh * cap * kRowBytes, (short)0, cap * kRowBytes,
+      0x00020000);
   const __amdgpu_buffer_rsrc_t vr_rs = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint8_t*>(v_codes) + (size_t)bh * cap * D, (short)0, cap * D, 0x00020000);
-  const uint32_t lane_off = (uint32_t)sub * 8;
+      const_cast<uint8_t*>(v_codes) + (size_t)bh * cap * kRowBytes, (short)0, cap * kRowBytes,
+      0x00020000);
+  const uint32_t lane_off = (uint32_t)sub * (8 / Fmt::kRowDiv);
   float m = kNegInf, l = 0.f, o[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) o[i] = 0.f;
   // rows of step s for this lane group: t = r0 + s kStep + (u kWaves + wave) RPW + slot
-  auto issue = [&](int s, u32x2_t (&kw)[U], u32x2_t (&vw)[U], bool (&ok)[U]) {
+  auto issue = [&](int s, Word (&kw)[U], Word (&vw)[U], bool (&ok)[U]) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int o_row = s * kStep + (u * kWaves + wave) * RPW + slot;  // row - r0
       const int word = (s * kStep + u * kWaves * RPW) >> 6;            // == o_row >> 6
       ok[u] = r0 + o_row < r1 &&
               (((bits[word] >> (o_row - 64 * word)) & 1ull) || r0 + o_row == p);
-      const uint32_t off = ok[u] ? (uint32_t)(r0 + o_row) * D + lane_off : BufferRows::kNoRow;
-      kw[u] = __builtin_amdgcn_raw_buffer_load_b64(kr_rs, (int)off, 0, kLoadNonTemporal);
-      vw[u] = __builtin_amdgcn_raw_buffer_load_b64(vr_rs, (int)off, 0, kLoadNonTemporal);
+      const uint32_t off =
+          ok[u] ? (uint32_t)(r0 + o_row) * kRowBytes + lane_off : BufferRows::kNoRow;
+      kw[u] = Fmt::load(kr_rs, off);
+      vw[u] = Fmt::load(vr_rs, off);
     }
   };
-  auto consume = [&](int s, const u32x2_t (&kw)[U], const u32x2_t (&vw)[U], const bool (&ok)[U]) {
+  auto consume = [&](int s, const Word (&kw)[U], const Word (&vw)[U], const bool (&ok)[U]) {
     float sc[U], ws_v[U];
     bool fresh[U];
 #pragma unroll
@@ -244,7 +355,9 @@ static_decode_fp8_kernel(const float* __restrict__ q, uint8_t* __restrict__ k_co
       // this lane's own store
       fresh[u] = kAppend && r0 + o_row == p;
       float kf[8];
-      unpack8_fp8(fresh[u] ? new_kw : kw[u], kf);
+      Word kcur = kw[u];
+      if constexpr (kAppend) kcur = fresh[u] ? new_kw : kcur;
+      Fmt::unpack(kcur, kf);
       float acc = 0.f;
 #pragma unroll
       for (int i = 0; i < 8; ++i) acc = fmaf(qr[i], kf[i], acc);
@@ -273,12 +386,14 @@ static_decode_fp8_kernel(const float* __restrict__ q, uint8_t* __restrict__ k_co
       l += p;
       const float pv = p * ws_v[u];
       float vf[8];
-      unpack8_fp8(fresh[u] ? new_vw : vw[u], vf);
+      Word vcur = vw[u];
+      if constexpr (kAppend) vcur = fresh[u] ? new_vw : vcur;
+      Fmt::unpack(vcur, vf);
 #pragma unroll
       for (int i = 0; i < 8; ++i) o[i] = fmaf(pv, vf[i], o[i]);
     }
   };
-  u32x2_t kw[2][U], vw[2][U];
+  Word kw[2][U], vw[2][U];
   bool ok[2][U];
   issue(0, kw[0], vw[0], ok[0]);
 #pragma unroll
@@ -295,7 +410,7 @@ static_decode_fp8_kernel(const float* __restrict__ q, uint8_t* __restrict__ k_co
   finish_split<D, 1>(st, lane, wave, ws, (size_t)bh, split, n, max_splits, out, lse);
 }
 
-template <int D, int kSteps>
+template <typename Fmt, int D, int kSteps>
 static void launch_static_fp8_k(const float* q, void* k_codes, void* v_codes, float* k_scale,
                                 float* v_scale, int32_t* mask, const int32_t* valid_len,
                                 const void* k_new, const void* v_new, const int32_t* write_pos,
@@ -307,14 +422,54 @@ static void launch_static_fp8_k(const float* q, void* k_codes, void* v_codes, fl
   auto* vc = static_cast<uint8_t*>(v_codes);
   auto* kn = static_cast<const uint16_t*>(k_new);
   auto* vn = static_cast<const uint16_t*>(v_new);
-  if (write_pos)
-    hipLaunchKernelGGL((static_decode_fp8_kernel<D, 4, kSteps, true>), grid, dim3(kThreads), 0,
-                       stream, q, kc, vc, k_scale, v_scale, mask, valid_len, kn, vn, write_pos, H,
-                       cap, scale * kLog2e, plan.chunk, B * H, w, out, lse, err_flag);
-  else
-    hipLaunchKernelGGL((static_decode_fp8_kernel<D, 4, kSteps, false>), grid, dim3(kThreads), 0,
-                       stream, q, kc, vc, k_scale, v_scale, mask, valid_len, kn, vn, write_pos, H,
-                       cap, scale * kLog2e, plan.chunk, B * H, w, out, lse, err_flag);
+  if constexpr (Fmt::kRowDiv == 1) {
+    if (write_pos) {
+      hipLaunchKernelGGL((static_decode_fp8_kernel<Fmt, D, 4, kSteps, true>), grid,
+                         dim3(kThreads), 0, stream, q, kc, vc, k_scale, v_scale, mask, valid_len,
+                         kn, vn, write_pos, H, cap, scale * kLog2e, plan.chunk, B * H, w, out,
+                         lse, err_flag);
+      return;
+    }
+  }
+  hipLaunchKernelGGL((static_decode_fp8_kernel<Fmt, D, 4, kSteps, false>), grid,
+                     dim3(kThreads), 0, stream, q, kc, vc, k_scale, v_scale, mask, valid_len, kn,
+                     vn, write_pos, H, cap, scale * kLog2e, plan.chunk, B * H, w, out, lse,
+                     err_flag);
+}
+
+template <typename Fmt>
+static hipError_t launch_static_lowbit(const float* q, void* k_codes, void* v_codes,
+                                       float* k_scale, float* v_scale, int32_t* mask,
+                                       const int32_t* valid_len, const void* k_new,
+                                       const void* v_new, const int32_t* write_pos, int B, int H,
+                                       int cap, int D, float scale, float* out, float* lse,
+                                       void* ws, const SplitPlan& plan, int32_t* err_flag,
+                                       hipStream_t stream) {
+  const Workspace w = carve(ws, (size_t)B * H, plan.max_splits, D);
+#define DAKV_LOWBIT(DD)                                                                       \
+  do {                                                                                        \
+    constexpr int kStep = kWaves * (64 / (DD / 8)) * 4;                                       \
+    const int steps = (plan.chunk + kStep - 1) / kStep;                                       \
+    if (steps <= 1)                                                                           \
+      launch_static_fp8_k<Fmt, DD, 1>(q, k_codes, v_codes, k_scale, v_scale, mask, valid_len, \
+                                      k_new, v_new, write_pos, B, H, cap, scale, out, lse, w, \
+                                      plan, err_flag, stream);                                \
+    else if (steps <= 2)                                                                      \
+      launch_static_fp8_k<Fmt, DD, 2>(q, k_codes, v_codes, k_scale, v_scale, mask, valid_len, \
+                                      k_new, v_new, write_pos, B, H, cap, scale, out, lse, w, \
+                                      plan, err_flag, stream);                                \
+    else                                                                                      \
+      launch_static_fp8_k<Fmt, DD, 4>(q, k_codes, v_codes, k_scale, v_scale, mask, valid_len, \
+                                      k_new, v_new, write_pos, B, H, cap, scale, out, lse, w, \
+                                      plan, err_flag, stream);                                \
+  } while (0)
+  if (D == 128) DAKV_LOWBIT(128);
+  else DAKV_LOWBIT(64);
+#undef DAKV_LOWBIT
+  const hipError_t err = hipGetLastError();
+  if (err != hipSuccess || plan.max_splits <= 1) return err;
+  return launch_static_merge(w, B, H, D, plan.chunk, plan.max_splits, valid_len, cap, out, lse,
+                             stream);
 }
 
 hipError_t launch_decode_static_fp8(const float* q, void* k_codes, void* v_codes, float* k_scale,
@@ -323,31 +478,20 @@ hipError_t launch_decode_static_fp8(const float* q, void* k_codes, void* v_codes
                                     const int32_t* write_pos, int B, int H, int cap, int D,
                                     float scale, float* out, float* lse, void* ws,
                                     const SplitPlan& plan, int32_t* err_flag, hipStream_t stream) {
-  const Workspace w = carve(ws, (size_t)B * H, plan.max_splits, D);
-#define DAKV_FP8(DD)                                                                          \
-  do {                                                                                        \
-    constexpr int kStep = kWaves * (64 / (DD / 8)) * 4;                                       \
-    const int steps = (plan.chunk + kStep - 1) / kStep;                                       \
-    if (steps <= 1)                                                                           \
-      launch_static_fp8_k<DD, 1>(q, k_codes, v_codes, k_scale, v_scale, mask, valid_len, k_new, \
-                                 v_new, write_pos, B, H, cap, scale, out, lse, w, plan,       \
-                                 err_flag, stream);                                           \
-    else if (steps <= 2)                                                                      \
-      launch_static_fp8_k<DD, 2>(q, k_codes, v_codes, k_scale, v_scale, mask, valid_len, k_new, \
-                                 v_new, write_pos, B, H, cap, scale, out, lse, w, plan,       \
-                                 err_flag, stream);                                           \
-    else                                                                                      \
-      launch_static_fp8_k<DD, 4>(q, k_codes, v_codes, k_scale, v_scale, mask, valid_len, k_new, \
-                                 v_new, write_pos, B, H, cap, scale, out, lse, w, plan,       \
-                                 err_flag, stream);                                           \
-  } while (0)
-  if (D == 128) DAKV_FP8(128);
-  else DAKV_FP8(64);
-#undef DAKV_FP8
-  const hipError_t err = hipGetLastError();
-  if (err != hipSuccess || plan.max_splits <= 1) return err;
-  return launch_static_merge(w, B, H, D, plan.chunk, plan.max_splits, valid_len, cap, out, lse,
-                             stream);
+  return launch_static_lowbit<E4M3Rows>(q, k_codes, v_codes, k_scale, v_scale, mask, valid_len,
+                                        k_new, v_new, write_pos, B, H, cap, D, scale, out, lse,
+                                        ws, plan, err_flag, stream);
+}
+
+hipError_t launch_decode_static_fp4(const float* q, const void* k_codes, const void* v_codes,
+                                    const float* k_scale, const float* v_scale,
+                                    const int32_t* mask, const int32_t* valid_len, int B, int H,
+                                    int cap, int D, float scale, float* out, float* lse, void* ws,
+                                    const SplitPlan& plan, int32_t* err_flag, hipStream_t stream) {
+  return launch_static_lowbit<E2M1Rows>(
+      q, const_cast<void*>(k_codes), const_cast<void*>(v_codes), const_cast<float*>(k_scale),
+      const_cast<float*>(v_scale), const_cast<int32_t*>(mask), valid_len, nullptr, nullptr,
+      nullptr, B, H, cap, D, scale, out, lse, ws, plan, err_flag, stream);
 }
 
 // ---------------------------------------------------------------------------

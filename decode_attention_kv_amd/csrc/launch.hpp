@@ -53,6 +53,17 @@ hipError_t launch_decode_static(const float* q, void* k_cache, void* v_cache, in
                                 float scale, float* out, float* lse, void* ws,
                                 const SplitPlan& plan, int32_t* err_flag, hipStream_t stream);
 
+// FP4 cache (static layout): E2M1 codes uint8 [B, H, cap, D / 2] (two per byte),
+// scales fp32 [B, H, cap]
+hipError_t launch_kv_append_fp4(void* k_codes, void* v_codes, float* k_scale, float* v_scale,
+                                const void* k_new, const void* v_new, const int32_t* write_pos,
+                                int32_t* mask, int B, int H, int cap, int D, int32_t* err_flag,
+                                hipStream_t stream);
+hipError_t launch_decode_static_fp4(const float* q, const void* k_codes, const void* v_codes,
+                                    const float* k_scale, const float* v_scale,
+                                    const int32_t* mask, const int32_t* valid_len, int B, int H,
+                                    int cap, int D, float scale, float* out, float* lse, void* ws,
+                                    const SplitPlan& plan, int32_t* err_flag, hipStream_t stream);
 // FP8 paged pool: codes uint8 [num_blocks, block_size, Hkv, D], scales fp32
 // [num_blocks, block_size, Hkv]; D = 128, Hkv dividing 16 (the all-heads kernel).
 hipError_t launch_paged_append_fp8(void* k_codes, void* v_codes, float* k_scale,

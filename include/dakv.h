@@ -300,6 +300,30 @@ int dakv_decode_attn_paged(const void* q, const void* key_cache, const void* val
                            void* stream);
 
 /*
+ * FP4 KV cache (static layout): the FP8 cache's scheme with E2M1 codes (OCP
+ * microscaling FP4: sign, 2 exponent bits with bias 1, 1 mantissa bit;
+ * magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6), two per byte with element 2i in the low
+ * four bits: codes uint8 [B, H, cap, D / 2], scales fp32 [B, H, cap] per K and V;
+ * a row's scale is 2^e with e the smallest integer for which max|x| <= 6 * 2^e,
+ * codes round x / 2^e to the nearest value, ties to the even code, zeros to +0
+ * ([FlashMLA], the decode kernel reads FP8 or FP4 and dequantises it).
+ *
+ * kv_append_fp4 -- as kv_append_fp8 (new rows finite; D a multiple of 16, <= 256).
+ * decode_attn_static_fp4 -- as decode_attn_static_fp8 over the FP4 cache (same
+ * workspace; D in {64, 128}).
+ */
+int dakv_kv_append_fp4(void* k_codes, void* v_codes, float* k_scale, float* v_scale,
+                       const void* k_new, const void* v_new, const int32_t* write_pos,
+                       int32_t* mask, int B, int H, int cap, int D, int32_t* err_flag,
+                       void* stream);
+int dakv_decode_attn_static_fp4(const float* q, const void* k_codes, const void* v_codes,
+                                const float* k_scale, const float* v_scale, const int32_t* mask,
+                                const int32_t* valid_len, int B, int H, int cap, int D,
+                                float scale, float* out, float* lse, void* workspace,
+                                size_t workspace_bytes, int num_splits, int32_t* err_flag,
+                                void* stream);
+
+/*
  * FP8 paged pool (the FP8 cache above in the paged layout): codes uint8
  * [num_blocks, block_size, Hkv, D] and one fp32 power-of-two scale per (block,
  * slot, KV head) [num_blocks, block_size, Hkv] for K and for V; values decode to
