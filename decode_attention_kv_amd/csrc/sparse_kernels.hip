@@ -5,30 +5,39 @@
 // with a running max that is only moved when it grows by more than a threshold
 // ("skip scale").
 //
-// Work split: one workgroup (4 waves) per (sequence, 32 query heads, 512
+// Work split: one workgroup (8 waves) per (sequence, 32 query heads, 512
 // indices); the head groups of one (sequence, index split) sit a multiple of 8
-// workgroups apart, so they run on one XCD and share its L2.  Wave w owns 16
-// heads (head block w & 1) and one 32-row half (w >> 1) of every 64-row tile.
+// workgroups apart, so they run on one XCD and share its L2.  The 32 heads are
+// two blocks of 16 (hb = wave / 4); within a head block, wave rb = wave % 4
+// scores rows 16 rb .. 16 rb + 15 of every 64-row tile and accumulates output
+// dims 128 rb .. 128 rb + 127 over all 64 rows, so the accumulators of a wave
+// are 16 heads x 128 dims and two waves fit each SIMD.
 //   * Rows are gathered by direct-to-LDS buffer loads (16 bytes per lane, no
 //     registers) into two tile buffers: tile it + 1 is in flight while tile it is
-//     computed; one barrier per tile.  A tile is 64 unpadded 1152-byte rows; the
-//     16-byte pieces of row r are stored in a permuted order (XOR of the piece's
-//     low 3 bits with a function of r) so that both LDS read patterns below hit
-//     16 distinct bank groups.
-//   * S^T[token, head] = G Q^T with v_mfma_f32_16x16x32_bf16: A = 16 rows x 32
-//     dims from LDS (read a batch of k-steps ahead), B = Q^T of the wave's 16
-//     heads, held in registers for the whole split (18 k-steps x 16 bytes per
-//     lane); four accumulation chains (two 16-row halves x even/odd k-steps).
-//   * The C layout of S^T (lane: head lane % 16, tokens 4 (lane / 16) + i of
-//     each half) is the A layout of P for O = P V when the 8 tokens of a lane
-//     group are taken in the order {4g..4g+3, 16+4g..16+4g+3}; P enters the
+//     computed.  A tile is 64 unpadded 1152-byte rows; the 16-byte pieces of row
+//     r are stored in a permuted order (the piece's low 3 bits XOR (r / 2) % 8).
+//     On this chip's LDS, which serves 32 lanes of a 16-byte read per pass from
+//     512-byte bank rows (measured), that puts the 32 pieces each pass reads
+//     (16 rows x an aligned pair of pieces, for both read patterns below) in
+//     distinct banks.
+//   * S^T[token, head] = G Q^T with v_mfma_f32_16x16x32_bf16: A = the wave's 16
+//     rows x 32 dims from LDS (read a batch of k-steps ahead), B = Q^T of the
+//     wave's 16 heads, held in registers for the whole split (18 k-steps x 16
+//     bytes per lane); three accumulation chains.
+//   * Each wave publishes its scores through LDS (one barrier per tile); every
+//     wave of the head block then reads all 64 rows' scores, so the four keep
+//     the same running max and sums and take the same rescale decisions.
+//   * The C layout of S^T (lane: head lane % 16, tokens 4 (lane / 16) + i of a
+//     row block) is the A layout of P for O = P V when the 8 tokens of a lane
+//     group in k-step kk are tokens {4g..4g+3} of row blocks 2 kk and 2 kk + 1,
+//     so each lane forms its P operands from the scores it read.  P enters the
 //     matrix core as bf16 hi + lo parts (two MFMAs per block).
 //   * The B operand of P V (8 rows of one dim per lane) comes straight from LDS
 //     with two transposing reads ds_read_b64_tr_b16: lane j of a 16-lane group
 //     points at row 4 (group) + j / 4 (+16), dims 4 (j % 4) .. +3 of a 16-dim
 //     block, and lane i receives dim i of that block for the 4 rows.
-// At the end the two row-half waves of a head block merge through LDS, and the
-// split writes o / l and the log2-sum-exp; a merge kernel combines the splits.
+// At the end each wave writes its dims of o / l (and one wave the log2-sum-exp);
+// a merge kernel combines the splits.
 #include "device.hpp"
 #include "launch.hpp"
 
@@ -46,28 +55,46 @@ constexpr int kDv = 512;
 constexpr int kRowBytes = kDqk * 2;                     // 1152
 constexpr int kPieces = kRowBytes / 16;                 // 72 pieces of 16 bytes
 constexpr int kTile = 64;                               // gathered rows per tile
-constexpr int kHalf = kTile / 2;                        // rows of a tile one wave takes
 constexpr int kTileBytes = kTile * kRowBytes;           // 73728
 constexpr int kSplit = 512;                             // indices per workgroup
-constexpr int kTiles = kSplit / kTile;                  // 8
+constexpr int kSpWaves = 8;
+constexpr int kSpThreads = kSpWaves * 64;
 constexpr int kHeadsPerWave = 16;
 constexpr int kHeadsPerWG = 32;
-constexpr int kDmaPerWave = kTileBytes / 1024 / 4;      // 18 wave loads of 1 KiB per tile
+constexpr int kRowBlock = 16;                           // tile rows one wave scores
+constexpr int kRowBlocks = kTile / kRowBlock;           // 4 waves per head block
+constexpr int kDmaPerWave = kTileBytes / 1024 / kSpWaves;  // 9 wave loads of 1 KiB per tile
 constexpr int kKSteps = kDqk / 32;                      // 18
-constexpr int kDimBlocks = kDv / 16;                    // 32 output blocks of 16 dims
+constexpr int kDimsPerWave = kDv / kRowBlocks;          // 128 output dims per wave
+constexpr int kWaveDimBlocks = kDimsPerWave / 16;       // 8 blocks of 16 dims
+// s_waitcnt immediates (vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
+constexpr int kWaitVm0 = (0 & 15) | (7 << 4) | (15 << 8);    // vmcnt(0) only
+constexpr int kWaitLgkm0 = 15 | (7 << 4) | (0 << 8) | (3 << 14);  // lgkmcnt(0) only
 // The page's rescale threshold is 6 in natural-log units; scores here are in log2.
 constexpr float kRescale = 6.0f * kLog2e;
 constexpr uint32_t kNoRow = 0x80000000u;  // a buffer offset past any sequence: loads 0
-static_assert(kTileBytes % 4096 == 0, "whole 1 KiB wave loads per wave");
+static_assert(kTileBytes % (1024 * kSpWaves) == 0, "whole 1 KiB wave loads per wave");
+static_assert(2 * kHeadsPerWave == kHeadsPerWG && kRowBlocks * 2 == kSpWaves,
+              "two head blocks of four waves");
 static_assert(kPieces % 8 == 0, "pieces permute within groups of 8");
 static_assert(kSplit % kTile == 0, "whole tiles per split");
 
 // Position of piece p of row r inside the row (an involution: it also maps a
 // position back to its piece).
 __device__ __forceinline__ int piece_slot(int p, int r) {
-  const int k = (r >> 1) & 7;
-  const int x = ((k << 1) & 7) | (k >> 2);
-  return (p & ~7) | ((p & 7) ^ x);
+  return (p & ~7) | ((p & 7) ^ ((r >> 1) & 7));
+}
+
+// Barrier for values exchanged through LDS by ordinary stores: waits for this
+// wave's LDS accesses but not for its buffer loads, so the next tile's gather
+// stays in flight (an LDS release fence would also wait for those, since they
+// write LDS).  The empty asm statements keep the compiler from moving memory
+// accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 }
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(const u32x4_t& v) {
@@ -80,7 +107,7 @@ __device__ __forceinline__ bf16x8_t join_bf16x4(const i16x4_t& lo, const i16x4_t
   return __builtin_bit_cast(bf16x8_t, v);
 }
 
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(kSpThreads)
 sparse_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
                     const int32_t* __restrict__ indices, int B, int s_q, int Hq, int s_kv,
                     int topk, float scale_log2, int n_hg, int n_splits, int per_hg,
@@ -88,7 +115,7 @@ sparse_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
   __shared__ __attribute__((aligned(1024))) uint8_t buf0[kTileBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t buf1[kTileBytes];
   __shared__ uint32_t rows[kSplit];  // byte offset of each index's row in kv[b], or kNoRow
-  uint8_t* const ring[2] = {buf0, buf1};
+  __shared__ f32x4_t sm_s[2][kRowBlocks][64];            // scores of each row block
   const int hg = blockIdx.x / per_hg;
   const int u = blockIdx.x - hg * per_hg;
   if (u >= B * n_splits) return;
@@ -97,22 +124,22 @@ sparse_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int hb = wave & 1;     // head block of the group
-  const int th = wave >> 1;    // row half of every tile
+  const int hb = wave >> 2;    // head block of the group
+  const int rb = wave & 3;     // row block of every tile (scores), dim quarter (P V)
   const int grp = lane >> 4;   // lane group 0..3
   const int col16 = lane & 15;
   const int head0 = hg * kHeadsPerWG + hb * kHeadsPerWave;
-  const bool active = head0 < Hq;
   const int t0 = split * kSplit;
   const int ntok = min(kSplit, topk - t0);
-  for (int i = tid; i < kSplit; i += 256) {
+  {
+    static_assert(kSplit == kSpThreads, "one index per thread");
     uint32_t r = kNoRow;
-    if (i < ntok) {
-      const int idx = indices[(size_t)b * topk + t0 + i];
+    if (tid < ntok) {
+      const int idx = indices[(size_t)b * topk + t0 + tid];
       if (idx >= 0 && idx < s_kv) r = (uint32_t)idx * kRowBytes;
       else raise_flag(err_flag, 4);
     }
-    rows[i] = r;
+    rows[tid] = r;
   }
   __syncthreads();
   // the sequence's latent rows as a buffer (the q-tokens of one sequence, b / s_q,
@@ -122,10 +149,10 @@ sparse_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
       (int)(s_kv * kRowBytes), 0x00020000);
   const int ntiles = (ntok + kTile - 1) / kTile;
 
-  // Tile ti into a buffer: wave load I (this wave's I = 18 wave + k) fills bytes
+  // Tile ti into a buffer: wave load I (this wave's I = 9 wave + k) fills bytes
   // [1024 I, 1024 I + 1024) of the tile, lane L the 16 bytes at 1024 I + 16 L,
   // i.e. position c = 64 I + L = 72 r + s of row r, which holds piece
-  // piece_slot(s, r).  Tiles past the split's end load kNoRow offsets (zeros).
+  // piece_slot(s, r).  Rows past the split's end load kNoRow offsets (zeros).
   auto fetch_tile = [&](int ti, uint8_t* dst) {
     uint32_t off[kDmaPerWave];
 #pragma unroll
@@ -159,63 +186,66 @@ sparse_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
       qreg[s] = __builtin_amdgcn_raw_buffer_load_b128(qr, (int)(base + s * 64), 0, 0);
   }
 
-  f32x4_t oacc[kDimBlocks];
+  // O of the wave's 16 heads and its 128 output dims (C layout: lane -> dim
+  // 16 j + col16 of dim block 8 rb + j, heads 4 grp + i)
+  f32x4_t oacc[kWaveDimBlocks];
 #pragma unroll
-  for (int j = 0; j < kDimBlocks; ++j) oacc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  float m_ref = kNegInf;  // running max used for the exponentials, head head0 + col16
-  float lsum = 0.f;       // this lane's share of the sum of exponentials
+  for (int j = 0; j < kWaveDimBlocks; ++j) oacc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  // running max used for the exponentials (head head0 + col16; the same in the
+  // four waves of a head block) and this lane's share of the sum of exponentials
+  float m_ref = kNegInf;
+  float lsum = 0.f;
 
-  // A operand of k-step s, half h: row 32 th + 16 h + col16, piece 4 s + grp.
-  const int arow0 = th * kHalf + col16;
-  const int arow1 = arow0 + 16;
-  // transposing reads of 16-dim block jb: rows 32 th + 4 grp + col16 / 4 (+16),
-  // dims 16 jb + 4 (col16 % 4) .. +3: piece 2 jb + (col16 % 4) / 2, byte
-  // 8 (col16 & 1) of it.
-  const int vrow0 = th * kHalf + 4 * grp + (col16 >> 2);
-  const int vrow1 = vrow0 + 16;
+  // A operand of k-step s: row 16 rb + col16, piece 4 s + grp, which sits at
+  // byte 128 (s / 2) + aoff[s % 2] of the row (the permutation only moves a piece
+  // inside its group of 8).
+  const int arow = rb * kRowBlock + col16;
+  int aoff[2];
+#pragma unroll
+  for (int par = 0; par < 2; ++par) aoff[par] = piece_slot(4 * par + grp, arow) * 16;
+  // Transposing reads for k-step kk of P V, half r: rows 32 kk + 16 r + 4 grp +
+  // col16 / 4, dims 16 jb + 4 (col16 % 4) .. +3 of dim block jb: piece 2 jb +
+  // (col16 % 4) / 2, byte 8 (col16 & 1) of it.
   const int vsub = (col16 & 3) >> 1;
   const int vhalf = (col16 & 1) * 8;
-  // Byte offsets within a row of the pieces these lanes read: the permutation
-  // only moves a piece inside its group of 8 (128 bytes), so k-step s reads at
-  // 128 (s / 2) + aoff[h][s % 2] and dim block jb at 128 (jb / 4) + voff[r][jb % 4].
-  int aoff[2][2], voff[2][4];
+  int vbase[2][2];
+  int voff[2][2][4];
 #pragma unroll
-  for (int par = 0; par < 2; ++par) {
-    aoff[0][par] = piece_slot(4 * par + grp, arow0) * 16;
-    aoff[1][par] = piece_slot(4 * par + grp, arow1) * 16;
-  }
+  for (int kk = 0; kk < 2; ++kk) {
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    voff[0][j] = piece_slot(2 * j + vsub, vrow0) * 16 + vhalf;
-    voff[1][j] = piece_slot(2 * j + vsub, vrow1) * 16 + vhalf;
+    for (int r = 0; r < 2; ++r) {
+      const int vrow = 32 * kk + 16 * r + 4 * grp + (col16 >> 2);
+      vbase[kk][r] = vrow * kRowBytes + 256 * rb;  // dim block 8 rb starts piece group 2 rb
+#pragma unroll
+      for (int j = 0; j < 4; ++j) voff[kk][r][j] = piece_slot(2 * j + vsub, vrow) * 16 + vhalf;
+    }
   }
 
-#pragma unroll
-  for (int it = 0; it < kTiles; ++it) {
+  // One tile: T holds it, N receives the next.  (Called with the two buffers
+  // named at compile time, so the compiler sees that reads of T do not touch the
+  // gather in flight into N and does not wait for it.)
+  auto tile = [&](int it, const uint8_t* T, uint8_t* N) {
     // this wave's loads of tile it are complete (none later is in flight yet);
     // the barrier makes every wave's part visible and ends every wave's reads of
     // tile it - 1, whose buffer the next fetch refills
-    __builtin_amdgcn_s_waitcnt((0 & 15) | (7 << 4) | (15 << 8));  // vmcnt(0) only
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
     __builtin_amdgcn_s_barrier();
-    if (it + 1 < kTiles) fetch_tile(it + 1, ring[(it + 1) & 1]);
-    if (active && it < ntiles) {
-      const uint8_t* T = ring[it & 1];
-      // S^T = G Q^T over 18 k-steps: chains (half, k-step parity); A operands
-      // read from LDS a batch of 3 k-steps ahead (scheduling barriers keep it so)
-      f32x4_t st[2][2];
+    if (it + 1 < ntiles) fetch_tile(it + 1, N);
+
+    // S^T = G Q^T for the wave's 16 rows over 18 k-steps in three chains; A
+    // operands read from LDS a batch of 3 k-steps ahead
+    f32x4_t st[3];
 #pragma unroll
-      for (int h = 0; h < 2; ++h) st[h][0] = st[h][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      // piece 4 s + grp of a row sits at 128 (s / 2) + aoff[h][s % 2]
-      const uint8_t* ap0 = T + arow0 * kRowBytes;
-      const uint8_t* ap1 = T + arow1 * kRowBytes;
+    for (int c = 0; c < 3; ++c) st[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    {
+      const uint8_t* ap = T + arow * kRowBytes;
       constexpr int kBatch = 3;
-      u32x4_t a[2][kBatch][2];
-      auto read_a = [&](int s0, u32x4_t (&dst)[kBatch][2]) {
+      u32x4_t a[2][kBatch];
+      auto read_a = [&](int s0, u32x4_t (&dst)[kBatch]) {
 #pragma unroll
         for (int k = 0; k < kBatch; ++k) {
           const int s = s0 + k;
-          dst[k][0] = *reinterpret_cast<const u32x4_t*>(ap0 + aoff[0][s & 1] + 128 * (s >> 1));
-          dst[k][1] = *reinterpret_cast<const u32x4_t*>(ap1 + aoff[1][s & 1] + 128 * (s >> 1));
+          dst[k] = *reinterpret_cast<const u32x4_t*>(ap + aoff[s & 1] + 128 * (s >> 1));
         }
       };
       read_a(0, a[0]);
@@ -225,152 +255,118 @@ sparse_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
         if (s0 + kBatch < kKSteps) read_a(s0 + kBatch, a[cur ^ 1]);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int k = 0; k < kBatch; ++k) {
-          const bf16x8_t qk = as_bf16x8(qreg[s0 + k]);
-          const int par = (s0 + k) & 1;
-          st[0][par] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[cur][k][0]), qk, st[0][par], 0, 0, 0);
-          st[1][par] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[cur][k][1]), qk, st[1][par], 0, 0, 0);
-        }
+        for (int k = 0; k < kBatch; ++k)
+          st[k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[cur][k]),
+                                                          as_bf16x8(qreg[s0 + k]), st[k], 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
       }
-      // score of row 32 th + 16 h + 4 grp + i of the tile for head col16
-      float sc[8];
-      float tmax = kNegInf;
+    }
+    // scores of tile rows 16 rb + 4 grp + i for head col16 (-inf for rows past
+    // the index list), published to the head block's other three waves
+    {
+      f32x4_t sc;
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int tok = it * kTile + th * kHalf + 16 * h + 4 * grp + i;
-          const float v = rows[tok] != kNoRow ? (st[h][0][i] + st[h][1][i]) * scale_log2 : kNegInf;
-          sc[4 * h + i] = v;
-          tmax = fmaxf(tmax, v);
-        }
+      for (int i = 0; i < 4; ++i) {
+        const int tok = it * kTile + rb * kRowBlock + 4 * grp + i;
+        sc[i] = rows[tok] != kNoRow ? (st[0][i] + st[1][i] + st[2][i]) * scale_log2 : kNegInf;
       }
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-      const float mnew = fmaxf(m_ref, tmax);
-      if (__any(mnew > m_ref + kRescale)) {
-        const float alpha = mnew == kNegInf ? 1.f : exp2_fast(m_ref - mnew);
-        lsum *= alpha;
-        m_ref = mnew;
-        float a4[4];
+      sm_s[hb][rb][lane] = sc;
+    }
+    lds_barrier();
+    // every wave of the head block now holds all 64 rows' scores in the same
+    // layout (row block b: tokens 16 b + 4 grp + i) and takes the same decisions
+    f32x4_t y[kRowBlocks];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) a4[i] = __shfl(alpha, 4 * grp + i);
-        // a few accumulators at a time (they live in AGPRs; the barriers keep the
-        // scheduler from moving them all to VGPRs at once)
+    for (int b4 = 0; b4 < kRowBlocks; ++b4) y[b4] = sm_s[hb][b4][lane];
+    float tmax = kNegInf;
 #pragma unroll
-        for (int j = 0; j < kDimBlocks; ++j) {
+    for (int b4 = 0; b4 < kRowBlocks; ++b4)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) oacc[j][i] *= a4[i];
-          if ((j & 3) == 3) __builtin_amdgcn_sched_barrier(0);
-        }
+      for (int i = 0; i < 4; ++i) tmax = fmaxf(tmax, y[b4][i]);
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+    const float mnew = fmaxf(m_ref, tmax);
+    if (__any(mnew > m_ref + kRescale)) {
+      const float alpha = mnew == kNegInf ? 1.f : exp2_fast(m_ref - mnew);
+      lsum *= alpha;
+      m_ref = mnew;
+      float a4[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a4[i] = __shfl(alpha, 4 * grp + i);
+#pragma unroll
+      for (int j = 0; j < kWaveDimBlocks; ++j) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) oacc[j][i] *= a4[i];
       }
-      const float mu = m_ref == kNegInf ? 0.f : m_ref;
-      // P as two bf16 parts (p = hi + lo to about 16 significant bits): rounding
-      // P to one bf16 alone can put the output off by more than 2e-3 when a few
-      // rows dominate the softmax.
+    }
+    const float mu = m_ref == kNegInf ? 0.f : m_ref;
+
+    // O += P V over the tile's 64 rows for dim blocks 8 rb .. 8 rb + 7.  k-step
+    // kk: lane group g holds tokens {4g..4g+3} of row blocks 2 kk and 2 kk + 1
+    // (the C layout of those blocks' scores), and the transposing reads return V
+    // rows in the same order.  P as two bf16 parts (p = hi + lo to about 16
+    // significant bits): rounding P to one bf16 alone can put the output off by
+    // more than 2e-3 when a few rows dominate the softmax.
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
       bf16x8_t pa, pl;
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
-        const float p = exp2_fast(sc[k] - mu);
+        const float p = exp2_fast(y[2 * kk + (k >> 2)][k & 3] - mu);
         lsum += p;
         const __bf16 hi = (__bf16)p;
         pa[k] = hi;
         pl[k] = (__bf16)(p - (float)hi);
       }
-      // O += P V, 32 blocks of 16 dims; the B operands (two transposing reads
-      // each) in batches of 4 blocks, the next batch read before this one's MFMAs
-      // piece 2 jb + vsub of a row sits at 128 (jb / 4) + voff[r][jb % 4]
-      const uint8_t* vp0 = T + vrow0 * kRowBytes;
-      const uint8_t* vp1 = T + vrow1 * kRowBytes;
-      constexpr int kVB = 4;
-      i16x4_t vb[2][kVB][2];
-      auto read_v = [&](int j0, i16x4_t (&dst)[kVB][2]) {
+      const uint8_t* vp0 = T + vbase[kk][0];
+      const uint8_t* vp1 = T + vbase[kk][1];
+      i16x4_t vb[kWaveDimBlocks][2];
 #pragma unroll
-        for (int k = 0; k < kVB; ++k) {
-          const int jb = j0 + k;
-          dst[k][0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_i16x4*)(vp0 + voff[0][jb & 3] + 128 * (jb >> 2)));
-          dst[k][1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_i16x4*)(vp1 + voff[1][jb & 3] + 128 * (jb >> 2)));
-        }
-      };
-      read_v(0, vb[0]);
+      for (int j = 0; j < kWaveDimBlocks; ++j) {
+        vb[j][0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_i16x4*)(vp0 + voff[kk][0][j & 3] + 128 * (j >> 2)));
+        vb[j][1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_i16x4*)(vp1 + voff[kk][1][j & 3] + 128 * (j >> 2)));
+      }
 #pragma unroll
-      for (int j0 = 0; j0 < kDimBlocks; j0 += kVB) {
-        const int cur = (j0 / kVB) & 1;
-        if (j0 + kVB < kDimBlocks) read_v(j0 + kVB, vb[cur ^ 1]);
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int k = 0; k < kVB; ++k) {
-          const bf16x8_t v = join_bf16x4(vb[cur][k][0], vb[cur][k][1]);
-          oacc[j0 + k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, v, oacc[j0 + k], 0, 0, 0);
-        }
-#pragma unroll
-        for (int k = 0; k < kVB; ++k) {
-          const bf16x8_t v = join_bf16x4(vb[cur][k][0], vb[cur][k][1]);
-          oacc[j0 + k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl, v, oacc[j0 + k], 0, 0, 0);
-        }
-        __builtin_amdgcn_sched_barrier(0);
+      for (int j = 0; j < kWaveDimBlocks; ++j) {
+        const bf16x8_t v = join_bf16x4(vb[j][0], vb[j][1]);
+        oacc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, v, oacc[j], 0, 0, 0);
+        oacc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl, v, oacc[j], 0, 0, 0);
       }
     }
+  };
+  for (int it = 0; it < ntiles; it += 2) {
+    tile(it, buf0, buf1);
+    if (it + 1 < ntiles) tile(it + 1, buf1, buf0);
   }
 
-  // Epilogue.  Per head (lane group g holds heads 4g + i of the block): the
-  // wave's max and total of the exponentials.
+  // Epilogue.  The sum of exponentials per head (the four waves of a head block
+  // hold the same sums and the same running max).
   lsum += __shfl_xor(lsum, 16);
   lsum += __shfl_xor(lsum, 32);
-  float lh[4], mh[4];
+  float inv[4], lse2[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    lh[i] = __shfl(lsum, 4 * grp + i);
-    mh[i] = __shfl(m_ref, 4 * grp + i);
-  }
-  // The row-half-1 wave of each head block hands its state to the row-half-0
-  // wave through LDS (buffer hb of the ring, free once every wave is past the
-  // last tile).
-  constexpr int kXfer = kDimBlocks * 64 * 4 + 64 * 8;  // floats per head block
-  static_assert(kXfer * 4 <= kTileBytes, "hand-over fits one tile buffer");
-  float* xf = reinterpret_cast<float*>(hb ? buf1 : buf0);
-  __syncthreads();
-  if (th == 1) {
-#pragma unroll
-    for (int j = 0; j < kDimBlocks; ++j)
-      *reinterpret_cast<f32x4_t*>(xf + (j * 64 + lane) * 4) = oacc[j];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      xf[kDimBlocks * 256 + lane * 8 + i] = mh[i];
-      xf[kDimBlocks * 256 + lane * 8 + 4 + i] = lh[i];
-    }
-  }
-  __syncthreads();
-  if (th == 1 || !active) return;
-  float wa[4], wb[4], inv[4], lse2[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const float mb = xf[kDimBlocks * 256 + lane * 8 + i];
-    const float lb = xf[kDimBlocks * 256 + lane * 8 + 4 + i];
-    const float M = fmaxf(mh[i], mb);
+    const float l = __shfl(lsum, 4 * grp + i);
+    const float M = __shfl(m_ref, 4 * grp + i);
     if (M == kNegInf) {
-      wa[i] = wb[i] = inv[i] = 0.f;
+      inv[i] = 0.f;
       lse2[i] = kNegInf;
     } else {
-      wa[i] = exp2_fast(mh[i] - M);
-      wb[i] = exp2_fast(mb - M);
-      const float l = lh[i] * wa[i] + lb * wb[i];
       inv[i] = 1.f / l;
       lse2[i] = M + __log2f(l);
     }
   }
+  if (head0 >= Hq) return;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int head = head0 + 4 * grp + i;
     const size_t unit = ((size_t)b * Hq + head) * n_splits + split;
-    float* dst = ws_o + unit * kDv + col16;
+    float* dst = ws_o + unit * kDv + rb * kDimsPerWave + col16;
 #pragma unroll
-    for (int j = 0; j < kDimBlocks; ++j)
-      dst[j * 16] = (oacc[j][i] * wa[i] + xf[(j * 64 + lane) * 4 + i] * wb[i]) * inv[i];
-    if (col16 == 0) ws_lse[unit] = lse2[i];
+    for (int j = 0; j < kWaveDimBlocks; ++j) dst[j * 16] = oacc[j][i] * inv[i];
+    if (rb == 0 && col16 == 0) ws_lse[unit] = lse2[i];
   }
 }
 
@@ -439,7 +435,7 @@ hipError_t launch_sparse(const void* q, const void* kv, const int32_t* indices, 
   if (n_splits > 0) {
     const int n_hg = (Hq + kHeadsPerWG - 1) / kHeadsPerWG;
     const int per_hg = (B * n_splits + 7) / 8 * 8;
-    hipLaunchKernelGGL(sparse_split_kernel, dim3(n_hg * per_hg), dim3(256), 0, stream,
+    hipLaunchKernelGGL(sparse_split_kernel, dim3(n_hg * per_hg), dim3(kSpThreads), 0, stream,
                        static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kv),
                        indices, B, s_q, Hq, s_kv, topk, sm_scale * kLog2e, n_hg, n_splits,
                        per_hg, ws_o, ws_lse, err_flag);
