@@ -24,7 +24,8 @@ float64, with no tiling, no splitting and no online softmax:
 * ``fp8``           -- the FP8 KV cache for decode: E4M3 codes with a power-of-two
   scale per cached row, its quantisation and the decode attention over it
   (FlashMLA on Huawei Ascend: FP8 KV read and dequantised at decode time; a
-  token's values and scale kept together); also the FP8 paged pool.
+  token's values and scale kept together); also the FP8 paged pool and the FP8
+  latent cache of the sparse kernel.
 * ``fp4``           -- the FP4 KV cache for decode: E2M1 codes, two per byte, with
   a power-of-two scale per cached row, its quantisation and the decode attention
   over it (same page: the decode kernel reads FP8 or FP4 and dequantises it).
@@ -57,6 +58,8 @@ from .fp8 import (
     decode_static_fp8,
     decode_paged_fp8,
     paged_append_fp8,
+    latent_append_fp8,
+    sparse_topk_attn_fp8,
 )
 from . import fp4
 from .fp4 import kv_append_fp4, decode_static_fp4
@@ -87,4 +90,6 @@ __all__ = [
     "fp4",
     "kv_append_fp4",
     "decode_static_fp4",
+    "latent_append_fp8",
+    "sparse_topk_attn_fp8",
 ]

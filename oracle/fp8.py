@@ -24,7 +24,12 @@ readings taken here are:
 * the paged pool holds codes ``[num_blocks, block_size, Hkv, D]`` and one scale per
   (block, slot, KV head) ``[num_blocks, block_size, Hkv]`` for K and for V, and the
   new token of sequence b is its last token (position len_b - 1, len_b counting
-  it), placed through the block table as every other token.
+  it), placed through the block table as every other token;
+* the sparse kernel's latent cache (the page's own kernel) holds codes
+  ``[B, s_kv, d_qk]`` and one scale per latent row ``[B, s_kv]``: the whole row
+  (value and rotary columns alike) shares its scale; a new latent row is quantised
+  into position write_pos[b] of its sequence, and the sparse attention runs over
+  the dequantised gathered rows.
 """
 
 import math
@@ -33,6 +38,7 @@ import numpy as np
 
 from .bf16 import widen
 from .paged import _offsets, token_rows, validate_paged
+from .sparse import sparse_topk_decode, validate_sparse
 from .static_cache import attended_rows, softmax_weighted_sum
 
 E4M3_MAX = 448.0
@@ -212,3 +218,55 @@ def paged_append_fp8(k_codes, v_codes, k_scale, v_scale, k_new, v_new, block_tab
         k_scale[p, sl], v_scale[p, sl] = ks[b], vs[b]
     return k_codes, v_codes, k_scale, v_scale
 
+
+
+def latent_append_fp8(codes, scale, new_rows, write_pos):
+    """Quantise each sequence's new latent row (bf16 bits ``[B, d_qk]``) and store its
+    codes and scale at row write_pos[b] of that sequence's cache (codes ``[B, s_kv,
+    d_qk]`` uint8, scales ``[B, s_kv]``).  Returns updated copies ``(codes, scale)``; a
+    position outside ``[0, s_kv)`` is an error."""
+    codes, scale = np.array(codes, copy=True), np.array(scale, copy=True)
+    B, s_kv, _ = codes.shape
+    rq, rs = quantize_rows(new_rows)
+    for b in range(B):
+        pos = int(np.asarray(write_pos).reshape(-1)[b])
+        if pos < 0 or pos >= s_kv:
+            raise ValueError(f"write position {pos} outside [0, {s_kv})")
+        codes[b, pos] = rq[b]
+        scale[b, pos] = rs[b]
+    return codes, scale
+
+
+def sparse_topk_attn_fp8(q, codes, scale, indices, d_v, sm_scale):
+    """Sparse top-k attention over the FP8 latent cache (FlashMLA on Huawei Ascend: the
+    decode kernel reads the cache as FP8, dequantises it to bfloat16 and computes as
+    before): for each q-token, the rows its indices select are dequantised (code value
+    times the row's scale, exact in bf16) and attended exactly as ``sparse_topk_attn``
+    attends bf16 rows.
+
+    q       : ``[B, s_q, h_q, d_qk]`` (uint16 bf16 bits, or float)
+    codes   : uint8 ``[B, s_kv, d_qk]``;  scale : ``[B, s_kv]``
+    indices : ints ``[B, s_q, topk]``
+    Returns ``out [B, s_q, h_q, d_v]`` and ``lse [B, s_q, h_q]`` (float64).
+    """
+    q = np.asarray(q)
+    codes = np.asarray(codes)
+    scale = np.asarray(scale, dtype=np.float64)
+    indices = np.asarray(indices)
+    if q.ndim != 4 or indices.ndim != 3 or indices.shape[:2] != q.shape[:2]:
+        raise ValueError("q must be [B, s_q, h_q, d_qk] and indices [B, s_q, topk]")
+    B, s_q, h_q, _ = q.shape
+    if codes.ndim != 3 or codes.shape[0] != B or scale.shape != codes.shape[:2]:
+        raise ValueError("codes must be [B, s_kv, d_qk] and scale [B, s_kv]")
+    validate_sparse(indices, codes.shape[1])
+    topk = indices.shape[2]
+    out = np.zeros((B, s_q, h_q, d_v))
+    lse = np.full((B, s_q, h_q), -np.inf)
+    for b in range(B):
+        for t in range(s_q):
+            idx = indices[b, t]
+            rows = dequantize(codes[b][idx], scale[b][idx])        # [topk, d_qk]
+            o, l = sparse_topk_decode(q[b, t][None], rows[None], np.arange(topk)[None],
+                                      d_v, sm_scale)
+            out[b, t], lse[b, t] = o[0], l[0]
+    return out, lse

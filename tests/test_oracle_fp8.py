@@ -187,3 +187,94 @@ def test_paged_append_places_the_new_token_at_the_last_position():
     with pytest.raises(ValueError):
         oracle.paged_append_fp8(kc, vc, ks, vs, kn, vn, tables,
                                 np.array([0, 1, 1, 17], np.int32))   # a length-0 sequence
+
+
+# ------------------------------------------------- the sparse kernel's FP8 latent cache
+
+
+def representable_latent_rows(rng, B, n, d):
+    """Latent rows whose values are E4M3 values times a power of two, with one code of
+    magnitude above 224 per row: quantising them must give back exactly these codes
+    and scales (the scale rule picks that exponent; no -0 codes)."""
+    codes = rng.integers(0, 256, size=(B, n, d)).astype(np.uint8)
+    codes[(codes & 0x7F) == 0x7F] = 0x7E          # no NaN codes
+    codes[codes == 0x80] = 0x00                   # zeros as +0
+    codes[..., 0] = 0x7A | (codes[..., 0] & 0x80)  # 0x7A = 320 > 224
+    scale = np.exp2(rng.integers(-10, -4, size=(B, n))).astype(np.float64)
+    return codes, scale
+
+
+def test_latent_append_round_trips_576_wide_rows_and_rejects_positions_outside():
+    rng = np.random.default_rng(46)
+    B, s_kv, d = 3, 7, 576
+    codes0 = rng.integers(0, 0x70, size=(B, s_kv, d)).astype(np.uint8)
+    scale0 = np.full((B, s_kv), 0.25)
+    new_codes, new_scale = representable_latent_rows(rng, B, 1, d)
+    rows = round_to_bf16_bits(oracle.e4m3_decode(new_codes[:, 0]) * new_scale[:, :1])
+    pos = np.array([0, 6, 3])
+    codes, scale = oracle.latent_append_fp8(codes0, scale0, rows, pos)
+    for b in range(B):
+        assert np.array_equal(codes[b, pos[b]], new_codes[b, 0])
+        assert scale[b, pos[b]] == new_scale[b, 0]
+        others = np.arange(s_kv) != pos[b]
+        assert np.array_equal(codes[b, others], codes0[b, others])
+        assert np.array_equal(scale[b, others], scale0[b, others])
+    with pytest.raises(ValueError):
+        oracle.latent_append_fp8(codes0, scale0, rows, np.array([0, 7, 1]))
+    with pytest.raises(ValueError):
+        oracle.latent_append_fp8(codes0, scale0, rows, np.array([-1, 0, 1]))
+
+
+def test_sparse_fp8_equals_bf16_sparse_over_the_dequantised_rows():
+    rng = np.random.default_rng(47)
+    B, s_q, h_q, s_kv, d, d_v, topk = 2, 2, 4, 40, 24, 16, 13
+    codes, scale = representable_latent_rows(rng, B, s_kv, d)
+    kv_bits = round_to_bf16_bits(oracle.e4m3_decode(codes) * scale[..., None])
+    assert np.array_equal(oracle.widen(kv_bits), oracle.e4m3_decode(codes) * scale[..., None])
+    q = rng.standard_normal((B, s_q, h_q, d))
+    idx = rng.integers(0, s_kv, size=(B, s_q, topk))
+    a, la = oracle.sparse_topk_attn_fp8(q, codes, scale, idx, d_v, 0.3)
+    b, lb = oracle.sparse_topk_attn(q, kv_bits, idx, d_v, 0.3)
+    assert np.array_equal(a, b) and np.array_equal(la, lb)
+
+
+def test_sparse_fp8_over_equal_rows_is_that_row():
+    """Every gathered row the same: every head's output is the dequantised row's first
+    d_v values and its log-sum-exp the common score plus ln(topk)."""
+    rng = np.random.default_rng(48)
+    B, s_kv, d, d_v, h_q, topk = 1, 9, 32, 20, 3, 6
+    row_codes, row_scale = representable_latent_rows(rng, 1, 1, d)
+    codes = np.broadcast_to(row_codes, (B, s_kv, d)).copy()
+    scale = np.full((B, s_kv), row_scale[0, 0])
+    q = rng.standard_normal((B, 1, h_q, d))
+    idx = rng.integers(0, s_kv, size=(B, 1, topk))
+    out, lse = oracle.sparse_topk_attn_fp8(q, codes, scale, idx, d_v, 0.5)
+    row = oracle.e4m3_decode(row_codes[0, 0]) * row_scale[0, 0]
+    for h in range(h_q):
+        assert np.allclose(out[0, 0, h], row[:d_v], rtol=0, atol=1e-12)
+        assert np.isclose(lse[0, 0, h], 0.5 * q[0, 0, h] @ row + np.log(topk), rtol=0,
+                          atol=1e-12)
+
+
+def test_sparse_fp8_scale_acts_on_whole_rows():
+    """Doubling every row scale while halving q leaves the scores unchanged, so the
+    output doubles (the value columns double) and the log-sum-exp is unchanged: a
+    scale applied to part of a row, or not at all, breaks this."""
+    rng = np.random.default_rng(49)
+    B, s_kv, d, d_v, h_q, topk = 2, 30, 40, 32, 5, 11
+    codes, scale = representable_latent_rows(rng, B, s_kv, d)
+    q = rng.standard_normal((B, 1, h_q, d))
+    idx = rng.integers(0, s_kv, size=(B, 1, topk))
+    o1, l1 = oracle.sparse_topk_attn_fp8(q, codes, scale, idx, d_v, 0.2)
+    o2, l2 = oracle.sparse_topk_attn_fp8(q / 2, codes, scale * 2, idx, d_v, 0.2)
+    assert np.allclose(o2, 2 * o1, rtol=1e-12, atol=0)
+    assert np.allclose(l2, l1, rtol=1e-12, atol=1e-12)
+
+
+def test_sparse_fp8_rejects_out_of_range_indices():
+    codes = np.zeros((1, 5, 8), dtype=np.uint8)
+    scale = np.ones((1, 5))
+    q = np.ones((1, 1, 2, 8))
+    for bad in (5, -1):
+        with pytest.raises(ValueError):
+            oracle.sparse_topk_attn_fp8(q, codes, scale, np.array([[[0, bad]]]), 4, 1.0)
