@@ -23,6 +23,8 @@ from .ops import (
     decode_attn_paged,
     decode_attn_paged_workspace_size,
     sparse_topk_attn,
+    latent_append_fp8,
+    sparse_topk_attn_fp8,
     sparse_topk_decode_attn,
     sparse_topk_decode_attn_workspace_size,
     validate_paged,
@@ -49,6 +51,8 @@ __all__ = [
     "decode_attn_paged",
     "decode_attn_paged_workspace_size",
     "sparse_topk_attn",
+    "latent_append_fp8",
+    "sparse_topk_attn_fp8",
     "sparse_topk_decode_attn",
     "sparse_topk_decode_attn_workspace_size",
     "validate_paged",

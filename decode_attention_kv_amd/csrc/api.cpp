@@ -359,25 +359,59 @@ size_t dakv_sparse_topk_decode_attn_workspace_size(int B, int Hq, int d_qk, int 
   return dakv::sparse_workspace_bytes(B, Hq, d_qk, d_v, topk);
 }
 
-int dakv_sparse_topk_attn(const void* q, const void* kv, const int32_t* indices, int B,
-                          int s_q, int Hq, int s_kv, int d_qk, int d_v, int topk,
-                          float sm_scale, float* out, float* lse, void* workspace,
-                          size_t workspace_bytes, int32_t* err_flag, void* stream) {
+// Shared by the bf16 and the FP8 latent cache (kv_scale != nullptr).
+static int sparse_attn(const void* q, const void* kv, const float* kv_scale,
+                       const int32_t* indices, int B, int s_q, int Hq, int s_kv, int d_qk,
+                       int d_v, int topk, float sm_scale, float* out, float* lse,
+                       void* workspace, size_t workspace_bytes, int32_t* err_flag,
+                       void* stream) {
   if (B < 0 || s_q < 0 || Hq <= 0 || s_kv <= 0 || d_qk <= 0 || d_v <= 0 || topk < 0)
     return DAKV_EINVAL;
   if (B == 0 || s_q == 0) return DAKV_OK;
   if ((long long)B * s_q > (1 << 24)) return DAKV_EINVAL;
   if (d_qk != 576 || d_v != 512) return DAKV_ENOTSUP;
   if (Hq % 16 != 0 || Hq > 128) return DAKV_ENOTSUP;
+  // a sequence's latent rows are addressed with 32-bit byte offsets
+  if ((long long)s_kv * d_qk * 2 > 0x7fffffffLL) return DAKV_ENOTSUP;
   if (!q || !kv || !out || (topk > 0 && !indices)) return DAKV_EINVAL;
   if (!aligned16(q) || !aligned16(kv) || !aligned16(out)) return DAKV_EINVAL;
   const int pairs = B * s_q;
   const size_t need = dakv::sparse_workspace_bytes(pairs, Hq, d_qk, d_v, topk);
   if (need > 0 && (!workspace || !aligned16(workspace) || workspace_bytes < need))
     return DAKV_EINVAL;
-  return from_hip(dakv::launch_sparse(q, kv, indices, pairs, s_q, Hq, s_kv, d_qk, d_v, topk,
-                                      sm_scale, out, lse, workspace, err_flag,
+  return from_hip(dakv::launch_sparse(q, kv, kv_scale, indices, pairs, s_q, Hq, s_kv, d_qk, d_v,
+                                      topk, sm_scale, out, lse, workspace, err_flag,
                                       as_stream(stream)));
+}
+
+int dakv_sparse_topk_attn(const void* q, const void* kv, const int32_t* indices, int B,
+                          int s_q, int Hq, int s_kv, int d_qk, int d_v, int topk,
+                          float sm_scale, float* out, float* lse, void* workspace,
+                          size_t workspace_bytes, int32_t* err_flag, void* stream) {
+  return sparse_attn(q, kv, nullptr, indices, B, s_q, Hq, s_kv, d_qk, d_v, topk, sm_scale, out,
+                     lse, workspace, workspace_bytes, err_flag, stream);
+}
+
+int dakv_sparse_topk_attn_fp8(const void* q, const void* codes, const float* scale,
+                              const int32_t* indices, int B, int s_q, int Hq, int s_kv, int d_qk,
+                              int d_v, int topk, float sm_scale, float* out, float* lse,
+                              void* workspace, size_t workspace_bytes, int32_t* err_flag,
+                              void* stream) {
+  if (!scale && B > 0 && s_q > 0) return DAKV_EINVAL;
+  return sparse_attn(q, codes, scale, indices, B, s_q, Hq, s_kv, d_qk, d_v, topk, sm_scale, out,
+                     lse, workspace, workspace_bytes, err_flag, stream);
+}
+
+int dakv_latent_append_fp8(void* codes, float* scale, const void* new_rows,
+                           const int32_t* write_pos, int B, int s_kv, int d_qk,
+                           int32_t* err_flag, void* stream) {
+  if (B < 0 || s_kv <= 0 || d_qk <= 0) return DAKV_EINVAL;
+  if (B == 0) return DAKV_OK;
+  if (d_qk > 576) return DAKV_ENOTSUP;
+  if ((long long)B * s_kv * d_qk > 0x7fffffffffffLL) return DAKV_EINVAL;
+  if (!codes || !scale || !new_rows || !write_pos) return DAKV_EINVAL;
+  return from_hip(dakv::launch_latent_append_fp8(codes, scale, new_rows, write_pos, B, s_kv,
+                                                 d_qk, err_flag, as_stream(stream)));
 }
 
 int dakv_sparse_topk_decode_attn(const void* q, const void* kv, const int32_t* indices,

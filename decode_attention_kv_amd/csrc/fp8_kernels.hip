@@ -17,14 +17,16 @@ namespace dakv {
 // value x * 2^-e (exact) is rounded to the nearest E4M3 value, ties to the even
 // code, zero results as the +0 code.
 // ---------------------------------------------------------------------------
-// One wave quantises one row of D <= 256 bf16 values: codes to dst, scale to *dst_scale.
+// One wave quantises one row of D <= 64 kPer bf16 values: codes to dst, scale to
+// *dst_scale.
+template <int kPer>
 __device__ __forceinline__ void quantise_row_wave(const uint16_t* __restrict__ src, int D,
                                                   uint8_t* __restrict__ dst,
                                                   float* __restrict__ dst_scale, int lane) {
-  float x[4];
+  float x[kPer];
   float amax = 0.f;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {            // D <= 256: at most 4 values per lane
+  for (int i = 0; i < kPer; ++i) {         // at most kPer values per lane
     const int d = lane + 64 * i;
     x[i] = d < D ? __uint_as_float((uint32_t)src[d] << 16) : 0.f;
     amax = fmaxf(amax, fabsf(x[i]));
@@ -32,7 +34,7 @@ __device__ __forceinline__ void quantise_row_wave(const uint16_t* __restrict__ s
   for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
   const int e = e4m3_exponent_for(amax);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < kPer; ++i) {
     const int d = lane + 64 * i;
     if (d < D) dst[d] = (uint8_t)e4m3_code(ldexpf(x[i], -e));
   }
@@ -58,7 +60,7 @@ kv_append_fp8_kernel(uint8_t* __restrict__ k_codes, uint8_t* __restrict__ v_code
   }
   const uint16_t* src = (is_v ? v_new : k_new) + ((size_t)b * H + h) * D;
   const size_t row = ((size_t)b * H + h) * cap + pos;
-  quantise_row_wave(src, D, (is_v ? v_codes : k_codes) + row * D,
+  quantise_row_wave<4>(src, D, (is_v ? v_codes : k_codes) + row * D,
                     (is_v ? v_scale : k_scale) + row, lane);
   if (mask && unit == 0 && lane == 0) mask[(size_t)b * cap + pos] = 1;
 }
@@ -71,6 +73,38 @@ hipError_t launch_kv_append_fp8(void* k_codes, void* v_codes, float* k_scale, fl
                      static_cast<uint8_t*>(k_codes), static_cast<uint8_t*>(v_codes), k_scale,
                      v_scale, static_cast<const uint16_t*>(k_new),
                      static_cast<const uint16_t*>(v_new), write_pos, mask, H, cap, D, err_flag);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// latent_append_fp8: each sequence's new latent row (bf16, d <= 576 values) is
+// quantised as kv_append_fp8 quantises a K or V row and stored at row
+// write_pos[b] of that sequence's latent cache (codes [B, s_kv, d], scales
+// [B, s_kv]).  One wave per sequence.
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256)
+latent_append_fp8_kernel(uint8_t* __restrict__ codes, float* __restrict__ scale,
+                         const uint16_t* __restrict__ new_rows,
+                         const int32_t* __restrict__ write_pos, int B, int s_kv, int d,
+                         int32_t* err_flag) {
+  const int b = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (b >= B) return;
+  const int pos = write_pos[b];
+  if (pos < 0 || pos >= s_kv) {
+    if (lane == 0) raise_flag(err_flag, 2);
+    return;
+  }
+  const size_t row = (size_t)b * s_kv + pos;
+  quantise_row_wave<9>(new_rows + (size_t)b * d, d, codes + row * d, scale + row, lane);
+}
+
+hipError_t launch_latent_append_fp8(void* codes, float* scale, const void* new_rows,
+                                    const int32_t* write_pos, int B, int s_kv, int d,
+                                    int32_t* err_flag, hipStream_t stream) {
+  hipLaunchKernelGGL(latent_append_fp8_kernel, dim3((B + 3) / 4), dim3(256), 0, stream,
+                     static_cast<uint8_t*>(codes), scale, static_cast<const uint16_t*>(new_rows),
+                     write_pos, B, s_kv, d, err_flag);
   return hipGetLastError();
 }
 
@@ -535,7 +569,7 @@ paged_append_fp8_kernel(uint8_t* __restrict__ k_codes, uint8_t* __restrict__ v_c
     return;
   }
   const size_t row = ((size_t)phys * block_size + t % block_size) * Hkv + h;
-  quantise_row_wave((is_v ? v_new : k_new) + ((size_t)b * Hkv + h) * D, D,
+  quantise_row_wave<4>((is_v ? v_new : k_new) + ((size_t)b * Hkv + h) * D, D,
                     (is_v ? v_codes : k_codes) + row * D, (is_v ? v_scale : k_scale) + row,
                     lane);
 }

@@ -411,6 +411,36 @@ int dakv_sparse_topk_attn(const void* q, const void* kv, const int32_t* indices,
                           float sm_scale, float* out, float* lse, void* workspace,
                           size_t workspace_bytes, int32_t* err_flag, void* stream);
 
+/*
+ * FP8 latent cache of the sparse kernel ([FlashMLA] section on VECTOR cores per
+ * CUBE core, item 2: the decode kernel reads the KV cache in FP8 and dequantises
+ * it to bfloat16 for the matrix unit; section on the decoding KV-cache layout: a
+ * token's values and its scale go together).  Codes uint8 [B, s_kv, d_qk] in the
+ * E4M3 format and scale rule of the FP8 KV cache above, one fp32 scale per latent
+ * row (all d_qk columns, value and rotary alike) in scale [B, s_kv].
+ *
+ * latent_append_fp8 -- quantise each sequence's new latent row (bf16 [B, d_qk],
+ * finite values) and store codes and scale at row write_pos[b] (int32 [B]
+ * device).  A position outside [0, s_kv) sets DAKV_ERR_WRITE_POS and skips that
+ * sequence.  d_qk up to 576.
+ */
+int dakv_latent_append_fp8(void* codes, float* scale, const void* new_rows,
+                           const int32_t* write_pos, int B, int s_kv, int d_qk,
+                           int32_t* err_flag, void* stream);
+
+/*
+ * sparse_topk_attn_fp8 -- dakv_sparse_topk_attn over the FP8 latent cache: the
+ * rows named by the indices are dequantised (code value times row scale, exact in
+ * bf16) and attended as bf16 rows are.  Arguments as dakv_sparse_topk_attn with
+ * kv replaced by codes (uint8 [B, s_kv, d_qk], 16-byte aligned) and scale (fp32
+ * [B, s_kv]); same workspace size, supported shapes and error behaviour.
+ */
+int dakv_sparse_topk_attn_fp8(const void* q, const void* codes, const float* scale,
+                              const int32_t* indices, int B, int s_q, int Hq, int s_kv, int d_qk,
+                              int d_v, int topk, float sm_scale, float* out, float* lse,
+                              void* workspace, size_t workspace_bytes, int32_t* err_flag,
+                              void* stream);
+
 /* ========================================================================
  * Host validators (HOST pointers; no GPU needed).  [PyPTO] 3.3 and 5.1: the
  * index tensors are host-ready and are checked on the host before a call.

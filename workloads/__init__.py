@@ -317,6 +317,38 @@ def sparse_tokens_case(B, s_q, Hq, s_kv, topk, *, d_qk=576, d_v=512, device="cpu
     return SparseCase(q, kv, torch.from_numpy(idx).to(device), d_v, float(sm_scale))
 
 
+@dataclass
+class SparseFp8Case:
+    q: torch.Tensor        # bf16 [B, s_q, Hq, d_qk]
+    codes: torch.Tensor    # uint8 [B, s_kv, d_qk], E4M3 codes (no NaN code)
+    scale: torch.Tensor    # fp32 [B, s_kv], powers of two
+    indices: torch.Tensor  # int32 [B, s_q, topk]
+    d_v: int
+    sm_scale: float
+
+
+def sparse_fp8_case(B, s_q, Hq, s_kv, topk, *, d_qk=576, d_v=512, device="cpu", seed=7,
+                    sm_scale=None):
+    """An FP8 latent cache as stored bytes: uniformly drawn finite E4M3 codes (the two
+    NaN codes are replaced by 0x7E) and row scales 2^-12 .. 2^-6, so the cached values
+    reach about 7 in magnitude, as those of quantised O(1) rows do; q bf16 N(0,1);
+    indices distinct within a token."""
+    rng = np.random.default_rng(seed)
+    idx = np.stack([np.stack([rng.choice(s_kv, topk, replace=False) for _ in range(s_q)])
+                    for _ in range(B)]).astype(np.int32).reshape(B, s_q, topk)
+    g = _gen(device, seed)
+    codes = torch.randint(0, 256, (B, s_kv, d_qk), generator=g, device=device,
+                          dtype=torch.uint8)
+    codes[(codes & 0x7F) == 0x7F] = 0x7E
+    e = torch.randint(-12, -5, (B, s_kv), generator=g, device=device, dtype=torch.int32)
+    scale = torch.exp2(e.to(torch.float32))
+    q = _randn_bf16((B, s_q, Hq, d_qk), g, device)
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(d_qk)
+    return SparseFp8Case(q, codes, scale, torch.from_numpy(idx).to(device), d_v,
+                         float(sm_scale))
+
+
 def sparse_mla(*, device="cpu", seed=5):
     """Batch 16, 128 heads, d_qk 576 / d_v 512, context 32768, top-2048."""
     return sparse_case(16, 128, 32768, 2048, device=device, seed=seed)
