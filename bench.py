@@ -570,6 +570,31 @@ def sparse_tokens_leg(torch, dakv, workloads, acc, s_q=2):
             "frac_of_bf16_mfma_peak": round(flops / (ms * 1e-3) / 2.5e15, 4)}
 
 
+def sparse_fp8_leg(torch, dakv, workloads, acc):
+    """The sparse MLA config over an FP8 latent cache (E4M3 codes with one power-of-two
+    scale per latent row)."""
+    case = workloads.sparse_fp8_case(16, 1, 128, 32768, 2048, device="cuda:0", seed=5)
+    B, s_q, Hq, d_qk = case.q.shape
+    topk = case.indices.shape[2]
+    out = torch.empty((B, s_q, Hq, case.d_v), dtype=torch.float32, device="cuda:0")
+    ws = torch.empty(dakv.sparse_topk_decode_attn_workspace_size(B, Hq, d_qk, case.d_v, topk),
+                     dtype=torch.uint8, device="cuda:0")
+    call = lambda: dakv.sparse_topk_attn_fp8(case.q, case.codes, case.scale, case.indices,
+                                             d_v=case.d_v, sm_scale=case.sm_scale, out=out,
+                                             workspace=ws, want_lse=False)
+    ms = time_cold(torch, call)
+    nbytes = acc.sparse_fp8_bytes(B, Hq, d_qk, case.d_v, topk)
+    flops = acc.sparse_flops(B, Hq, d_qk, case.d_v, topk)
+    del case, out, ws
+    return {"workload": "top-k sparse MLA decode over an FP8 latent cache (E4M3 + row scale): "
+                        "batch 16, 128 heads, d_qk 576 / d_v 512, context 32768, top-2048",
+            "us_per_call": round(ms * 1e3, 2), "algorithmic_bytes": nbytes,
+            "GBps": round(nbytes / (ms * 1e-3) / 1e9, 1),
+            "frac_of_hbm_peak": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "TFLOPs": round(flops / (ms * 1e-3) / 1e12, 1),
+            "frac_of_bf16_mfma_peak": round(flops / (ms * 1e-3) / 2.5e15, 4)}
+
+
 def cpu_baseline(step, budget_s):
     """The fp64 oracle over (layer, sequence) pairs of the same step until the budget is
     spent; GB/s = algorithmic bytes of the pairs done / host seconds."""
@@ -747,6 +772,8 @@ def main():
         torch.cuda.empty_cache()
         line["sparse_mla"] = sparse_leg(torch, dakv, workloads, acc)
         line["sparse_mla_2_tokens"] = sparse_tokens_leg(torch, dakv, workloads, acc)
+        torch.cuda.empty_cache()
+        line["sparse_mla_fp8"] = sparse_fp8_leg(torch, dakv, workloads, acc)
         torch.cuda.empty_cache()
         line["copy_kvcache"] = copy_leg(torch, dakv, acc)
         torch.cuda.empty_cache()

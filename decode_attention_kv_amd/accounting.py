@@ -122,6 +122,15 @@ def sparse_bytes(B, Hq, d_qk, d_v, topk, q_elem=BF16, with_lse=False):
     return gathered + q + out + B * topk * INT32
 
 
+def sparse_fp8_bytes(B, Hq, d_qk, d_v, topk, with_lse=False):
+    """Sparse MLA decode over the FP8 latent cache: the gathered rows' codes (one byte
+    per value) and row scales once per sequence, q, out, indices."""
+    gathered = B * topk * (d_qk + FP32)
+    q = B * Hq * d_qk * BF16
+    out = B * Hq * d_v * FP32 + (B * Hq * FP32 if with_lse else 0)
+    return gathered + q + out + B * topk * INT32
+
+
 def sparse_macs(B, Hq, d_qk, d_v, topk):
     """Multiply-accumulates of P = Q G^T and O = S G[:, :d_v]."""
     return B * Hq * topk * (d_qk + d_v)

@@ -52,3 +52,11 @@ def test_gather_bytes_count_read_and_write_of_valid_rows():
     b = acc.gather_bytes([3, 0, 130], 8, 128, 8, 128, 128, with_offset=True)
     rows = 133 * 2 * 8 * 128 * 2
     assert b == 2 * rows + (1 + 0 + 2) * 4 + 4 * 4 + 3 * 4
+
+
+def test_sparse_fp8_bytes_halve_the_gathered_rows():
+    # one byte per latent value plus a 4-byte scale per gathered row
+    b = acc.sparse_fp8_bytes(16, 128, 576, 512, 2048)
+    assert b == 16 * 2048 * (576 + 4) + 16 * 128 * 576 * 2 + 16 * 128 * 512 * 4 + 16 * 2048 * 4
+    full = acc.sparse_bytes(16, 128, 576, 512, 2048)
+    assert full - b == 16 * 2048 * (576 * 2 - 576 - 4)
