@@ -28,7 +28,8 @@ float64, with no tiling, no splitting and no online softmax:
   latent cache of the sparse kernel.
 * ``fp4``           -- the FP4 KV cache for decode: E2M1 codes, two per byte, with
   a power-of-two scale per cached row, its quantisation and the decode attention
-  over it (same page: the decode kernel reads FP8 or FP4 and dequantises it).
+  over it (same page: the decode kernel reads FP8 or FP4 and dequantises it);
+  also the FP4 latent cache of the sparse kernel.
 
 bf16 tensors enter the oracle as their raw 16-bit patterns (``numpy.uint16``) and
 are widened exactly to float64 (``bf16.widen``); copies (append, gather) move the
@@ -62,7 +63,7 @@ from .fp8 import (
     sparse_topk_attn_fp8,
 )
 from . import fp4
-from .fp4 import kv_append_fp4, decode_static_fp4
+from .fp4 import kv_append_fp4, decode_static_fp4, latent_append_fp4, sparse_topk_attn_fp4
 
 __all__ = [
     "widen",
@@ -92,4 +93,6 @@ __all__ = [
     "decode_static_fp4",
     "latent_append_fp8",
     "sparse_topk_attn_fp8",
+    "latent_append_fp4",
+    "sparse_topk_attn_fp4",
 ]

@@ -18,7 +18,10 @@ row, for K and for V, kept in its own array):
   four bits (the microscaling specification's packing);
 * the cached value is decode(code) * s, exactly representable in bf16, so the
   attention over the FP4 cache is the attention of the static layout over those
-  values.
+  values;
+* the sparse kernel's latent cache in FP4 holds packed codes ``[B, s_kv, d_qk/2]``
+  and one scale per latent row ``[B, s_kv]`` for all its columns, as the FP8
+  latent cache does; the sparse attention runs over the dequantised gathered rows.
 """
 
 import math
@@ -26,6 +29,7 @@ import math
 import numpy as np
 
 from .bf16 import widen
+from .sparse import sparse_topk_decode, validate_sparse
 from .static_cache import attended_rows, softmax_weighted_sum
 
 E2M1_MAX = 6.0
@@ -151,4 +155,57 @@ def decode_static_fp4(q, k_codes, v_codes, k_scale, v_scale, mask=None, valid_le
             K = dequantize(k_codes[b, h, rows], k_scale[b, h, rows])
             V = dequantize(v_codes[b, h, rows], v_scale[b, h, rows])
             out[b, h], lse[b, h] = softmax_weighted_sum(scale * (K @ q[b, h]), V)
+    return out, lse
+
+
+def latent_append_fp4(codes, scale, new_rows, write_pos):
+    """Quantise each sequence's new latent row (bf16 bits ``[B, d_qk]``) and store its
+    packed codes and scale at row write_pos[b] of that sequence's cache (codes
+    ``[B, s_kv, d_qk/2]`` uint8, scales ``[B, s_kv]``).  Returns updated copies
+    ``(codes, scale)``; a position outside ``[0, s_kv)`` is an error."""
+    codes, scale = np.array(codes, copy=True), np.array(scale, copy=True)
+    B, s_kv, _ = codes.shape
+    rq, rs = quantize_rows(new_rows)
+    for b in range(B):
+        pos = int(np.asarray(write_pos).reshape(-1)[b])
+        if pos < 0 or pos >= s_kv:
+            raise ValueError(f"write position {pos} outside [0, {s_kv})")
+        codes[b, pos] = rq[b]
+        scale[b, pos] = rs[b]
+    return codes, scale
+
+
+def sparse_topk_attn_fp4(q, codes, scale, indices, d_v, sm_scale):
+    """Sparse top-k attention over the FP4 latent cache (FlashMLA on Huawei Ascend: the
+    decode kernel reads the cache as FP8 or FP4 and dequantises it to bfloat16): for
+    each q-token, the rows its indices select are dequantised (code value times the
+    row's scale, exact in bf16) and attended exactly as ``sparse_topk_attn`` attends
+    bf16 rows.
+
+    q       : ``[B, s_q, h_q, d_qk]`` (uint16 bf16 bits, or float)
+    codes   : uint8 ``[B, s_kv, d_qk/2]`` (element 2i in the low four bits);
+    scale   : ``[B, s_kv]``;  indices : ints ``[B, s_q, topk]``
+    Returns ``out [B, s_q, h_q, d_v]`` and ``lse [B, s_q, h_q]`` (float64).
+    """
+    q = np.asarray(q)
+    codes = np.asarray(codes)
+    scale = np.asarray(scale, dtype=np.float64)
+    indices = np.asarray(indices)
+    if q.ndim != 4 or indices.ndim != 3 or indices.shape[:2] != q.shape[:2]:
+        raise ValueError("q must be [B, s_q, h_q, d_qk] and indices [B, s_q, topk]")
+    B, s_q, h_q, d_qk = q.shape
+    if (codes.ndim != 3 or codes.shape[0] != B or 2 * codes.shape[2] != d_qk
+            or scale.shape != codes.shape[:2]):
+        raise ValueError("codes must be [B, s_kv, d_qk/2] and scale [B, s_kv]")
+    validate_sparse(indices, codes.shape[1])
+    topk = indices.shape[2]
+    out = np.zeros((B, s_q, h_q, d_v))
+    lse = np.full((B, s_q, h_q), -np.inf)
+    for b in range(B):
+        for t in range(s_q):
+            idx = indices[b, t]
+            rows = dequantize(codes[b][idx], scale[b][idx])        # [topk, d_qk]
+            o, l = sparse_topk_decode(q[b, t][None], rows[None], np.arange(topk)[None],
+                                      d_v, sm_scale)
+            out[b, t], lse[b, t] = o[0], l[0]
     return out, lse

@@ -96,3 +96,88 @@ def test_append_quantises_the_new_row_and_rejects_positions_outside():
     assert out[4][0].tolist() == [1, 0, 0, 0, 0, 0] and out[4][1, 5] == 1
     with pytest.raises(ValueError):
         oracle.kv_append_fp4(kc, kc, ks, ks, kn, vn, [6, 0])
+
+
+# ------------------------------------------------- the sparse kernel's FP4 latent cache
+
+
+def representable_latent_rows(rng, B, n, d):
+    """Packed latent rows whose values are E2M1 values times a power of two, with a
+    code of magnitude 6 in each row: quantising them gives back exactly these codes
+    and scales (no -0 codes: zeros are stored as +0)."""
+    nib = rng.integers(0, 16, size=(B, n, d)).astype(np.uint8)
+    nib[nib == 8] = 0                              # -0 -> +0
+    nib[..., 0] = 7 | (nib[..., 0] & 8)            # magnitude 6
+    scale = np.exp2(rng.integers(-8, -2, size=(B, n))).astype(np.float64)
+    return fp4.pack(nib), scale
+
+
+def test_latent_append_fp4_round_trips_576_wide_rows_and_rejects_positions_outside():
+    rng = np.random.default_rng(56)
+    B, s_kv, d = 3, 7, 576
+    codes0 = rng.integers(0, 256, size=(B, s_kv, d // 2)).astype(np.uint8)
+    scale0 = np.full((B, s_kv), 0.5)
+    new_codes, new_scale = representable_latent_rows(rng, B, 1, d)
+    rows = round_to_bf16_bits(fp4.dequantize(new_codes[:, 0], new_scale[:, 0]))
+    pos = np.array([6, 0, 2])
+    codes, scale = oracle.latent_append_fp4(codes0, scale0, rows, pos)
+    for b in range(B):
+        assert np.array_equal(codes[b, pos[b]], new_codes[b, 0])
+        assert scale[b, pos[b]] == new_scale[b, 0]
+        others = np.arange(s_kv) != pos[b]
+        assert np.array_equal(codes[b, others], codes0[b, others])
+        assert np.array_equal(scale[b, others], scale0[b, others])
+    for bad in ([0, 7, 1], [-1, 0, 1]):
+        with pytest.raises(ValueError):
+            oracle.latent_append_fp4(codes0, scale0, rows, np.array(bad))
+
+
+def test_sparse_fp4_equals_bf16_sparse_over_the_dequantised_rows():
+    rng = np.random.default_rng(57)
+    B, s_q, h_q, s_kv, d, d_v, topk = 2, 2, 4, 40, 24, 16, 13
+    codes, scale = representable_latent_rows(rng, B, s_kv, d)
+    deq = fp4.dequantize(codes, scale)
+    kv_bits = round_to_bf16_bits(deq)
+    assert np.array_equal(oracle.widen(kv_bits), deq)
+    q = rng.standard_normal((B, s_q, h_q, d))
+    idx = rng.integers(0, s_kv, size=(B, s_q, topk))
+    a, la = oracle.sparse_topk_attn_fp4(q, codes, scale, idx, d_v, 0.3)
+    b, lb = oracle.sparse_topk_attn(q, kv_bits, idx, d_v, 0.3)
+    assert np.array_equal(a, b) and np.array_equal(la, lb)
+
+
+def test_sparse_fp4_over_equal_rows_is_that_row():
+    rng = np.random.default_rng(58)
+    B, s_kv, d, d_v, h_q, topk = 1, 9, 32, 20, 3, 6
+    row_codes, row_scale = representable_latent_rows(rng, 1, 1, d)
+    codes = np.broadcast_to(row_codes, (B, s_kv, d // 2)).copy()
+    scale = np.full((B, s_kv), row_scale[0, 0])
+    q = rng.standard_normal((B, 1, h_q, d))
+    idx = rng.integers(0, s_kv, size=(B, 1, topk))
+    out, lse = oracle.sparse_topk_attn_fp4(q, codes, scale, idx, d_v, 0.5)
+    row = fp4.dequantize(row_codes[0, 0], row_scale[0, 0])
+    for h in range(h_q):
+        assert np.allclose(out[0, 0, h], row[:d_v], rtol=0, atol=1e-12)
+        assert np.isclose(lse[0, 0, h], 0.5 * q[0, 0, h] @ row + np.log(topk), rtol=0,
+                          atol=1e-12)
+
+
+def test_sparse_fp4_scale_acts_on_whole_rows():
+    rng = np.random.default_rng(59)
+    B, s_kv, d, d_v, h_q, topk = 2, 30, 40, 32, 5, 11
+    codes, scale = representable_latent_rows(rng, B, s_kv, d)
+    q = rng.standard_normal((B, 1, h_q, d))
+    idx = rng.integers(0, s_kv, size=(B, 1, topk))
+    o1, l1 = oracle.sparse_topk_attn_fp4(q, codes, scale, idx, d_v, 0.2)
+    o2, l2 = oracle.sparse_topk_attn_fp4(q / 2, codes, scale * 2, idx, d_v, 0.2)
+    assert np.allclose(o2, 2 * o1, rtol=1e-12, atol=0)
+    assert np.allclose(l2, l1, rtol=1e-12, atol=1e-12)
+
+
+def test_sparse_fp4_rejects_out_of_range_indices():
+    codes = np.zeros((1, 5, 4), dtype=np.uint8)
+    scale = np.ones((1, 5))
+    q = np.ones((1, 1, 2, 8))
+    for bad in (5, -1):
+        with pytest.raises(ValueError):
+            oracle.sparse_topk_attn_fp4(q, codes, scale, np.array([[[0, bad]]]), 4, 1.0)
