@@ -570,23 +570,26 @@ def sparse_tokens_leg(torch, dakv, workloads, acc, s_q=2):
             "frac_of_bf16_mfma_peak": round(flops / (ms * 1e-3) / 2.5e15, 4)}
 
 
-def sparse_fp8_leg(torch, dakv, workloads, acc):
-    """The sparse MLA config over an FP8 latent cache (E4M3 codes with one power-of-two
-    scale per latent row)."""
-    case = workloads.sparse_fp8_case(16, 1, 128, 32768, 2048, device="cuda:0", seed=5)
+def sparse_lowbit_leg(torch, dakv, workloads, acc, fmt="fp8"):
+    """The sparse MLA config over a low-bit latent cache: E4M3 (fmt "fp8") or E2M1 two
+    per byte ("fp4") codes with one power-of-two scale per latent row."""
+    make = workloads.sparse_fp8_case if fmt == "fp8" else workloads.sparse_fp4_case
+    fn = dakv.sparse_topk_attn_fp8 if fmt == "fp8" else dakv.sparse_topk_attn_fp4
+    nbytes_of = acc.sparse_fp8_bytes if fmt == "fp8" else acc.sparse_fp4_bytes
+    case = make(16, 1, 128, 32768, 2048, device="cuda:0", seed=5)
     B, s_q, Hq, d_qk = case.q.shape
     topk = case.indices.shape[2]
     out = torch.empty((B, s_q, Hq, case.d_v), dtype=torch.float32, device="cuda:0")
     ws = torch.empty(dakv.sparse_topk_decode_attn_workspace_size(B, Hq, d_qk, case.d_v, topk),
                      dtype=torch.uint8, device="cuda:0")
-    call = lambda: dakv.sparse_topk_attn_fp8(case.q, case.codes, case.scale, case.indices,
-                                             d_v=case.d_v, sm_scale=case.sm_scale, out=out,
-                                             workspace=ws, want_lse=False)
+    call = lambda: fn(case.q, case.codes, case.scale, case.indices, d_v=case.d_v,
+                      sm_scale=case.sm_scale, out=out, workspace=ws, want_lse=False)
     ms = time_cold(torch, call)
-    nbytes = acc.sparse_fp8_bytes(B, Hq, d_qk, case.d_v, topk)
+    nbytes = nbytes_of(B, Hq, d_qk, case.d_v, topk)
     flops = acc.sparse_flops(B, Hq, d_qk, case.d_v, topk)
     del case, out, ws
-    return {"workload": "top-k sparse MLA decode over an FP8 latent cache (E4M3 + row scale): "
+    name = "FP8 (E4M3" if fmt == "fp8" else "FP4 (E2M1, two per byte"
+    return {"workload": f"top-k sparse MLA decode over an {name} + row scale) latent cache: "
                         "batch 16, 128 heads, d_qk 576 / d_v 512, context 32768, top-2048",
             "us_per_call": round(ms * 1e3, 2), "algorithmic_bytes": nbytes,
             "GBps": round(nbytes / (ms * 1e-3) / 1e9, 1),
@@ -773,7 +776,9 @@ def main():
         line["sparse_mla"] = sparse_leg(torch, dakv, workloads, acc)
         line["sparse_mla_2_tokens"] = sparse_tokens_leg(torch, dakv, workloads, acc)
         torch.cuda.empty_cache()
-        line["sparse_mla_fp8"] = sparse_fp8_leg(torch, dakv, workloads, acc)
+        line["sparse_mla_fp8"] = sparse_lowbit_leg(torch, dakv, workloads, acc, "fp8")
+        torch.cuda.empty_cache()
+        line["sparse_mla_fp4"] = sparse_lowbit_leg(torch, dakv, workloads, acc, "fp4")
         torch.cuda.empty_cache()
         line["copy_kvcache"] = copy_leg(torch, dakv, acc)
         torch.cuda.empty_cache()

@@ -25,6 +25,8 @@ from .ops import (
     sparse_topk_attn,
     latent_append_fp8,
     sparse_topk_attn_fp8,
+    latent_append_fp4,
+    sparse_topk_attn_fp4,
     sparse_topk_decode_attn,
     sparse_topk_decode_attn_workspace_size,
     validate_paged,
@@ -53,6 +55,8 @@ __all__ = [
     "sparse_topk_attn",
     "latent_append_fp8",
     "sparse_topk_attn_fp8",
+    "latent_append_fp4",
+    "sparse_topk_attn_fp4",
     "sparse_topk_decode_attn",
     "sparse_topk_decode_attn_workspace_size",
     "validate_paged",

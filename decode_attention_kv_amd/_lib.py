@@ -64,6 +64,9 @@ SIGNATURES = {
     "dakv_latent_append_fp8": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _vp, _vp]),
     "dakv_sparse_topk_attn_fp8": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f, _vp,
                                        _vp, _vp, _sz, _vp, _vp]),
+    "dakv_latent_append_fp4": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _vp, _vp]),
+    "dakv_sparse_topk_attn_fp4": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f, _vp,
+                                       _vp, _vp, _sz, _vp, _vp]),
     "dakv_paged_append_fp8": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _vp, _vp, _i, _i, _i,
                                    _i, _i, _vp, _vp]),
     "dakv_decode_attn_paged_fp8": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _vp, _vp, _i, _i,

@@ -122,6 +122,12 @@ def sparse_bytes(B, Hq, d_qk, d_v, topk, q_elem=BF16, with_lse=False):
     return gathered + q + out + B * topk * INT32
 
 
+def sparse_fp4_bytes(B, Hq, d_qk, d_v, topk, with_lse=False):
+    """Sparse MLA decode over the FP4 latent cache: as sparse_fp8_bytes with half a
+    byte per value."""
+    return sparse_fp8_bytes(B, Hq, d_qk, d_v, topk, with_lse) - B * topk * d_qk // 2
+
+
 def sparse_fp8_bytes(B, Hq, d_qk, d_v, topk, with_lse=False):
     """Sparse MLA decode over the FP8 latent cache: the gathered rows' codes (one byte
     per value) and row scales once per sequence, q, out, indices."""

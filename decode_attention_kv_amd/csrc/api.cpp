@@ -359,8 +359,8 @@ size_t dakv_sparse_topk_decode_attn_workspace_size(int B, int Hq, int d_qk, int 
   return dakv::sparse_workspace_bytes(B, Hq, d_qk, d_v, topk);
 }
 
-// Shared by the bf16 and the FP8 latent cache (kv_scale != nullptr).
-static int sparse_attn(const void* q, const void* kv, const float* kv_scale,
+// Shared by the bf16, FP8 and FP4 latent caches (format 0, 1, 2).
+static int sparse_attn(const void* q, const void* kv, const float* kv_scale, int format,
                        const int32_t* indices, int B, int s_q, int Hq, int s_kv, int d_qk,
                        int d_v, int topk, float sm_scale, float* out, float* lse,
                        void* workspace, size_t workspace_bytes, int32_t* err_flag,
@@ -379,8 +379,8 @@ static int sparse_attn(const void* q, const void* kv, const float* kv_scale,
   const size_t need = dakv::sparse_workspace_bytes(pairs, Hq, d_qk, d_v, topk);
   if (need > 0 && (!workspace || !aligned16(workspace) || workspace_bytes < need))
     return DAKV_EINVAL;
-  return from_hip(dakv::launch_sparse(q, kv, kv_scale, indices, pairs, s_q, Hq, s_kv, d_qk, d_v,
-                                      topk, sm_scale, out, lse, workspace, err_flag,
+  return from_hip(dakv::launch_sparse(q, kv, kv_scale, format, indices, pairs, s_q, Hq, s_kv,
+                                      d_qk, d_v, topk, sm_scale, out, lse, workspace, err_flag,
                                       as_stream(stream)));
 }
 
@@ -388,8 +388,8 @@ int dakv_sparse_topk_attn(const void* q, const void* kv, const int32_t* indices,
                           int s_q, int Hq, int s_kv, int d_qk, int d_v, int topk,
                           float sm_scale, float* out, float* lse, void* workspace,
                           size_t workspace_bytes, int32_t* err_flag, void* stream) {
-  return sparse_attn(q, kv, nullptr, indices, B, s_q, Hq, s_kv, d_qk, d_v, topk, sm_scale, out,
-                     lse, workspace, workspace_bytes, err_flag, stream);
+  return sparse_attn(q, kv, nullptr, 0, indices, B, s_q, Hq, s_kv, d_qk, d_v, topk, sm_scale,
+                     out, lse, workspace, workspace_bytes, err_flag, stream);
 }
 
 int dakv_sparse_topk_attn_fp8(const void* q, const void* codes, const float* scale,
@@ -398,8 +398,29 @@ int dakv_sparse_topk_attn_fp8(const void* q, const void* codes, const float* sca
                               void* workspace, size_t workspace_bytes, int32_t* err_flag,
                               void* stream) {
   if (!scale && B > 0 && s_q > 0) return DAKV_EINVAL;
-  return sparse_attn(q, codes, scale, indices, B, s_q, Hq, s_kv, d_qk, d_v, topk, sm_scale, out,
-                     lse, workspace, workspace_bytes, err_flag, stream);
+  return sparse_attn(q, codes, scale, 1, indices, B, s_q, Hq, s_kv, d_qk, d_v, topk, sm_scale,
+                     out, lse, workspace, workspace_bytes, err_flag, stream);
+}
+
+int dakv_sparse_topk_attn_fp4(const void* q, const void* codes, const float* scale,
+                              const int32_t* indices, int B, int s_q, int Hq, int s_kv, int d_qk,
+                              int d_v, int topk, float sm_scale, float* out, float* lse,
+                              void* workspace, size_t workspace_bytes, int32_t* err_flag,
+                              void* stream) {
+  if (!scale && B > 0 && s_q > 0) return DAKV_EINVAL;
+  return sparse_attn(q, codes, scale, 2, indices, B, s_q, Hq, s_kv, d_qk, d_v, topk, sm_scale,
+                     out, lse, workspace, workspace_bytes, err_flag, stream);
+}
+
+int dakv_latent_append_fp4(void* codes, float* scale, const void* new_rows,
+                           const int32_t* write_pos, int B, int s_kv, int d_qk,
+                           int32_t* err_flag, void* stream) {
+  if (B < 0 || s_kv <= 0 || d_qk <= 0) return DAKV_EINVAL;
+  if (B == 0) return DAKV_OK;
+  if (d_qk > 576 || d_qk % 2 != 0) return DAKV_ENOTSUP;
+  if (!codes || !scale || !new_rows || !write_pos) return DAKV_EINVAL;
+  return from_hip(dakv::launch_latent_append_fp4(codes, scale, new_rows, write_pos, B, s_kv,
+                                                 d_qk, err_flag, as_stream(stream)));
 }
 
 int dakv_latent_append_fp8(void* codes, float* scale, const void* new_rows,
@@ -408,7 +429,6 @@ int dakv_latent_append_fp8(void* codes, float* scale, const void* new_rows,
   if (B < 0 || s_kv <= 0 || d_qk <= 0) return DAKV_EINVAL;
   if (B == 0) return DAKV_OK;
   if (d_qk > 576) return DAKV_ENOTSUP;
-  if ((long long)B * s_kv * d_qk > 0x7fffffffffffLL) return DAKV_EINVAL;
   if (!codes || !scale || !new_rows || !write_pos) return DAKV_EINVAL;
   return from_hip(dakv::launch_latent_append_fp8(codes, scale, new_rows, write_pos, B, s_kv,
                                                  d_qk, err_flag, as_stream(stream)));

@@ -183,6 +183,57 @@ hipError_t launch_kv_append_fp4(void* k_codes, void* v_codes, float* k_scale, fl
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// latent_append_fp4: as latent_append_fp8 with E2M1 codes (the scale and rounding
+// of kv_append_fp4), two codes per byte.  One wave per sequence; lane l quantises
+// the value pairs (2p, 2p + 1) for p = l + 64 k.
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256)
+latent_append_fp4_kernel(uint8_t* __restrict__ codes, float* __restrict__ scale,
+                         const uint16_t* __restrict__ new_rows,
+                         const int32_t* __restrict__ write_pos, int B, int s_kv, int d,
+                         int32_t* err_flag) {
+  constexpr int kPairs = 5;                  // d <= 640
+  const int b = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (b >= B) return;
+  const int pos = write_pos[b];
+  if (pos < 0 || pos >= s_kv) {
+    if (lane == 0) raise_flag(err_flag, 2);
+    return;
+  }
+  const uint16_t* src = new_rows + (size_t)b * d;
+  float x[2 * kPairs];
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 2 * kPairs; ++i) {
+    const int v = 2 * (lane + 64 * (i >> 1)) + (i & 1);
+    x[i] = v < d ? __uint_as_float((uint32_t)src[v] << 16) : 0.f;
+    amax = fmaxf(amax, fabsf(x[i]));
+  }
+  for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+  const int e = e2m1_exponent_for(amax);
+  const size_t row = (size_t)b * s_kv + pos;
+  uint8_t* dst = codes + row * (d / 2);
+#pragma unroll
+  for (int k = 0; k < kPairs; ++k) {
+    const int p = lane + 64 * k;
+    if (2 * p < d)
+      dst[p] = (uint8_t)(e2m1_code(ldexpf(x[2 * k], -e)) |
+                         (e2m1_code(ldexpf(x[2 * k + 1], -e)) << 4));
+  }
+  if (lane == 0) scale[row] = ldexpf(1.f, e);
+}
+
+hipError_t launch_latent_append_fp4(void* codes, float* scale, const void* new_rows,
+                                    const int32_t* write_pos, int B, int s_kv, int d,
+                                    int32_t* err_flag, hipStream_t stream) {
+  hipLaunchKernelGGL(latent_append_fp4_kernel, dim3((B + 3) / 4), dim3(256), 0, stream,
+                     static_cast<uint8_t*>(codes), scale, static_cast<const uint16_t*>(new_rows),
+                     write_pos, B, s_kv, d, err_flag);
+  return hipGetLastError();
+}
+
 // ---------------------------------------------------------- static layout, FP8
 // Split pass of decode_attn_static_fp8: the cache holds E4M3 codes (one byte per
 // element, [B, H, cap, D]) and one power-of-two fp32 scale per row for K and for V

@@ -95,13 +95,18 @@ hipError_t launch_decode_paged(const void* q, const void* key_cache, const void*
 
 size_t sparse_workspace_bytes(int B, int Hq, int d_qk, int d_v, int topk);
 // B = (sequence, q-token) pairs; the s_q tokens of sequence b / s_q share its kv rows.
-// kv_scale == nullptr: bf16 latent rows; otherwise E4M3 codes with one scale per row.
-hipError_t launch_sparse(const void* q, const void* kv, const float* kv_scale,
+// format 0: bf16 latent rows; 1: E4M3 codes, 2: E2M1 codes (two a byte), each with one
+// fp32 scale per row in kv_scale.
+hipError_t launch_sparse(const void* q, const void* kv, const float* kv_scale, int format,
                          const int32_t* indices, int B, int s_q, int Hq, int s_kv, int d_qk,
                          int d_v, int topk, float sm_scale, float* out, float* lse, void* ws,
                          int32_t* err_flag, hipStream_t stream);
 // quantising append of one latent row (d <= 576) per sequence into [B, s_kv, d] codes
 hipError_t launch_latent_append_fp8(void* codes, float* scale, const void* new_rows,
+                                    const int32_t* write_pos, int B, int s_kv, int d,
+                                    int32_t* err_flag, hipStream_t stream);
+// the same in E2M1 (d even, d <= 640): packed codes [B, s_kv, d / 2]
+hipError_t launch_latent_append_fp4(void* codes, float* scale, const void* new_rows,
                                     const int32_t* write_pos, int B, int s_kv, int d,
                                     int32_t* err_flag, hipStream_t stream);
 

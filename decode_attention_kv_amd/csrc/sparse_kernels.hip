@@ -108,23 +108,28 @@ __device__ __forceinline__ bf16x8_t join_bf16x4(const i16x4_t& lo, const i16x4_t
   return __builtin_bit_cast(bf16x8_t, v);
 }
 
-// kFp8: the latent cache holds E4M3 codes (576 bytes a row) and one fp32 scale per
-// row.  The tile buffers keep the bf16 layout of the bf16 cache: each thread loads
-// its code pieces of the next tile into registers while the current tile is
+// Latent cache formats: bf16 rows, or codes with one fp32 scale per row -- E4M3
+// (one byte a value) or E2M1 (two values a byte, element 2i in the low four bits).
+// For codes, the tile buffers keep the bf16 layout of the bf16 cache: each thread
+// loads its code pieces of the next tile into registers while the current tile is
 // computed, then stores them as code value times row scale (exact in bf16, the
 // scale being a power of two) at the permuted piece positions.
-template <bool kFp8>
+enum LatentFormat : int { kLatentBf16 = 0, kLatentFp8 = 1, kLatentFp4 = 2 };
+
+template <int kFmt>
 __global__ void __launch_bounds__(kSpThreads)
 sparse_split_kernel(const uint16_t* __restrict__ q, const void* __restrict__ kv,
                     const float* __restrict__ kv_scale, const int32_t* __restrict__ indices,
                     int B, int s_q, int Hq, int s_kv, int topk, float scale_log2, int n_hg,
                     int n_splits, int per_hg, float* __restrict__ ws_o,
                     float* __restrict__ ws_lse, int32_t* err_flag) {
-  constexpr int kSrcRowBytes = kFp8 ? kDqk : kRowBytes;  // a latent row in the cache
+  constexpr bool kCodes = kFmt != kLatentBf16;
+  constexpr int kSrcRowBytes = kFmt == kLatentBf16 ? kRowBytes     // a latent row in the cache
+                               : kFmt == kLatentFp8 ? kDqk : kDqk / 2;
   __shared__ __attribute__((aligned(1024))) uint8_t buf0[kTileBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t buf1[kTileBytes];
   __shared__ uint32_t rows[kSplit];  // byte offset of each index's row in kv[b], or kNoRow
-  __shared__ float row_scale[kFp8 ? kSplit : 1];         // FP8: each index's row scale
+  __shared__ float row_scale[kCodes ? kSplit : 1];       // codes: each index's row scale
   __shared__ f32x4_t sm_s[2][kRowBlocks][64];            // scores of each row block
   const int hg = blockIdx.x / per_hg;
   const int u = blockIdx.x - hg * per_hg;
@@ -149,13 +154,13 @@ sparse_split_kernel(const uint16_t* __restrict__ q, const void* __restrict__ kv,
       const int idx = indices[(size_t)b * topk + t0 + tid];
       if (idx >= 0 && idx < s_kv) {
         r = (uint32_t)idx * kSrcRowBytes;
-        if constexpr (kFp8) sc = kv_scale[(size_t)(b / s_q) * s_kv + idx];
+        if constexpr (kCodes) sc = kv_scale[(size_t)(b / s_q) * s_kv + idx];
       } else {
         raise_flag(err_flag, 4);
       }
     }
     rows[tid] = r;
-    if constexpr (kFp8) row_scale[tid] = sc;
+    if constexpr (kCodes) row_scale[tid] = sc;
   }
   __syncthreads();
   // the sequence's latent rows as a buffer (the q-tokens of one sequence, b / s_q,
@@ -189,19 +194,21 @@ sparse_split_kernel(const uint16_t* __restrict__ q, const void* __restrict__ kv,
                                                0, 0, 0);
     }
   };
-  // FP8: thread t holds code pieces c = t + 512 k of a tile (row c / 36, codes
-  // 16 (c % 36) .. +15), loaded by load_codes and stored converted by store_codes
-  // as bf16 pieces 2 (c % 36) and 2 (c % 36) + 1 of that row.
-  constexpr int kCodePieces = kTile * (kDqk / 16);                         // 2304
-  constexpr int kCodesPerThread = (kCodePieces + kSpThreads - 1) / kSpThreads;  // 5
-  u32x4_t creg[kFp8 ? kCodesPerThread : 1];
+  // Codes: thread t holds the 16-byte code pieces c = t + 512 k of a tile (row
+  // c / P, P pieces a row: 36 of 16 E4M3 values or 18 of 32 E2M1 values), loaded by
+  // load_codes and stored converted by store_codes as the 2 (E4M3) or 4 (E2M1)
+  // bf16 pieces of those values.
+  constexpr int kCodePiecesRow = kSrcRowBytes / 16;
+  constexpr int kCodePieces = kTile * kCodePiecesRow;            // 2304 or 1152
+  constexpr int kCodesPerThread = (kCodePieces + kSpThreads - 1) / kSpThreads;  // 5 or 3
+  u32x4_t creg[kCodes ? kCodesPerThread : 1];
   auto load_codes = [&](int ti) {
 #pragma unroll
     for (int k = 0; k < kCodesPerThread; ++k) {
       const int c = tid + kSpThreads * k;
-      const int r = c / (kDqk / 16);
+      const int r = c / kCodePiecesRow;
       const uint32_t o = c < kCodePieces ? rows[ti * kTile + r] : kNoRow;
-      const uint32_t off = o == kNoRow ? kNoRow : o + (uint32_t)(c - r * (kDqk / 16)) * 16;
+      const uint32_t off = o == kNoRow ? kNoRow : o + (uint32_t)(c - r * kCodePiecesRow) * 16;
       creg[k] = __builtin_amdgcn_raw_buffer_load_b128(kvr, (int)off, 0, 0);
     }
   };
@@ -210,24 +217,39 @@ sparse_split_kernel(const uint16_t* __restrict__ q, const void* __restrict__ kv,
     for (int k = 0; k < kCodesPerThread; ++k) {
       const int c = tid + kSpThreads * k;
       if (c < kCodePieces) {
-        const int r = c / (kDqk / 16);
-        const int pp = c - r * (kDqk / 16);
+        const int r = c / kCodePiecesRow;
+        const int pp = c - r * kCodePiecesRow;
         const float sc = row_scale[ti * kTile + r];
-        u32x4_t h[2];
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const bf16x2_t lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(creg[k][w], sc, false);
-          const bf16x2_t hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(creg[k][w], sc, true);
-          h[w >> 1][2 * (w & 1)] = __builtin_bit_cast(uint32_t, lo);
-          h[w >> 1][2 * (w & 1) + 1] = __builtin_bit_cast(uint32_t, hi);
-        }
         uint8_t* row = dst + r * kRowBytes;
-        *reinterpret_cast<u32x4_t*>(row + piece_slot(2 * pp, r) * 16) = h[0];
-        *reinterpret_cast<u32x4_t*>(row + piece_slot(2 * pp + 1, r) * 16) = h[1];
+        if constexpr (kFmt == kLatentFp8) {
+          // word w: values 4 w .. 4 w + 3 of the piece (bytes in memory order)
+          u32x4_t h[2];
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            const bf16x2_t lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(creg[k][w], sc, false);
+            const bf16x2_t hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(creg[k][w], sc, true);
+            h[w >> 1][2 * (w & 1)] = __builtin_bit_cast(uint32_t, lo);
+            h[w >> 1][2 * (w & 1) + 1] = __builtin_bit_cast(uint32_t, hi);
+          }
+          *reinterpret_cast<u32x4_t*>(row + piece_slot(2 * pp, r) * 16) = h[0];
+          *reinterpret_cast<u32x4_t*>(row + piece_slot(2 * pp + 1, r) * 16) = h[1];
+        } else {
+          // word w: values 8 w .. 8 w + 7 of the piece, byte j holding 8 w + 2 j (low
+          // four bits) and 8 w + 2 j + 1 -- one bf16 piece
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            const u32x4_t h = {
+                __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(creg[k][w], sc, 0)),
+                __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(creg[k][w], sc, 1)),
+                __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(creg[k][w], sc, 2)),
+                __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(creg[k][w], sc, 3))};
+            *reinterpret_cast<u32x4_t*>(row + piece_slot(4 * pp + w, r) * 16) = h;
+          }
+        }
       }
     }
   };
-  if constexpr (kFp8) load_codes(0);
+  if constexpr (kCodes) load_codes(0);
   else fetch_tile(0, buf0);
   // Q^T of the wave's heads as B operands, loaded while tile 0 is in flight:
   // lane -> head head0 + col16, dims 32 s + 8 grp .. +8 (heads past Hq read as
@@ -241,7 +263,7 @@ sparse_split_kernel(const uint16_t* __restrict__ q, const void* __restrict__ kv,
     for (int s = 0; s < kKSteps; ++s)
       qreg[s] = __builtin_amdgcn_raw_buffer_load_b128(qr, (int)(base + s * 64), 0, 0);
   }
-  if constexpr (kFp8) {
+  if constexpr (kCodes) {
     __builtin_amdgcn_s_waitcnt(kWaitVm0);
     store_codes(0, buf0);
   }
@@ -288,14 +310,14 @@ sparse_split_kernel(const uint16_t* __restrict__ q, const void* __restrict__ kv,
     // this wave's loads of tile it are complete (none later is in flight yet);
     // the barrier makes every wave's part visible and ends every wave's reads of
     // tile it - 1, whose buffer the next fetch refills
-    // (FP8: this wave's converted stores of tile it are complete.)
-    if constexpr (kFp8) __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+    // (codes: this wave's converted stores of tile it are complete.)
+    if constexpr (kCodes) __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
     else __builtin_amdgcn_s_waitcnt(kWaitVm0);
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     if (it + 1 < ntiles) {
-      if constexpr (kFp8) load_codes(it + 1);
+      if constexpr (kCodes) load_codes(it + 1);
       else fetch_tile(it + 1, N);
     }
 
@@ -402,7 +424,7 @@ sparse_split_kernel(const uint16_t* __restrict__ q, const void* __restrict__ kv,
         oacc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl, v, oacc[j], 0, 0, 0);
       }
     }
-    if constexpr (kFp8) {
+    if constexpr (kCodes) {
       if (it + 1 < ntiles) {
         __builtin_amdgcn_s_waitcnt(kWaitVm0);
         store_codes(it + 1, N);
@@ -496,7 +518,7 @@ size_t sparse_workspace_bytes(int B, int Hq, int d_qk, int d_v, int topk) {
   return (size_t)B * Hq * sparse_splits(topk) * (size_t)(d_v + 1) * sizeof(float);
 }
 
-hipError_t launch_sparse(const void* q, const void* kv, const float* kv_scale,
+hipError_t launch_sparse(const void* q, const void* kv, const float* kv_scale, int format,
                          const int32_t* indices, int B, int s_q, int Hq, int s_kv, int d_qk,
                          int d_v, int topk, float sm_scale, float* out, float* lse, void* ws,
                          int32_t* err_flag, hipStream_t stream) {
@@ -508,16 +530,21 @@ hipError_t launch_sparse(const void* q, const void* kv, const float* kv_scale,
   if (n_splits > 0) {
     const int n_hg = (Hq + kHeadsPerWG - 1) / kHeadsPerWG;
     const int per_hg = (B * n_splits + 7) / 8 * 8;
-    if (kv_scale)
-      hipLaunchKernelGGL(sparse_split_kernel<true>, dim3(n_hg * per_hg), dim3(kSpThreads), 0,
-                         stream, static_cast<const uint16_t*>(q), kv, kv_scale, indices, B, s_q,
-                         Hq, s_kv, topk, sm_scale * kLog2e, n_hg, n_splits, per_hg, ws_o, ws_lse,
-                         err_flag);
+    const dim3 grid(n_hg * per_hg), block(kSpThreads);
+    const float sl = sm_scale * kLog2e;
+    const uint16_t* q16 = static_cast<const uint16_t*>(q);
+    if (format == kLatentFp8)
+      hipLaunchKernelGGL(sparse_split_kernel<kLatentFp8>, grid, block, 0, stream, q16, kv,
+                         kv_scale, indices, B, s_q, Hq, s_kv, topk, sl, n_hg, n_splits, per_hg,
+                         ws_o, ws_lse, err_flag);
+    else if (format == kLatentFp4)
+      hipLaunchKernelGGL(sparse_split_kernel<kLatentFp4>, grid, block, 0, stream, q16, kv,
+                         kv_scale, indices, B, s_q, Hq, s_kv, topk, sl, n_hg, n_splits, per_hg,
+                         ws_o, ws_lse, err_flag);
     else
-      hipLaunchKernelGGL(sparse_split_kernel<false>, dim3(n_hg * per_hg), dim3(kSpThreads), 0,
-                         stream, static_cast<const uint16_t*>(q), kv, nullptr, indices, B, s_q,
-                         Hq, s_kv, topk, sm_scale * kLog2e, n_hg, n_splits, per_hg, ws_o, ws_lse,
-                         err_flag);
+      hipLaunchKernelGGL(sparse_split_kernel<kLatentBf16>, grid, block, 0, stream, q16, kv,
+                         nullptr, indices, B, s_q, Hq, s_kv, topk, sl, n_hg, n_splits, per_hg,
+                         ws_o, ws_lse, err_flag);
   }
   hipLaunchKernelGGL(sparse_merge_kernel, dim3(B * Hq), dim3(256), 0, stream, ws_o, ws_lse,
                      n_splits, out, lse);

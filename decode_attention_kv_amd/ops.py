@@ -682,3 +682,58 @@ def sparse_topk_attn_fp8(q, codes, scale, indices, d_v=512, sm_scale=None, out=N
         _p(q), _p(codes), _p(scale), _p(indices), B, s_q, Hq, s_kv, d_qk, d_v, topk,
         float(sm_scale), _p(out), _p(lse), _p(ws), ws.numel(), _p(err_flag), _stream()))
     return out, lse
+
+
+def latent_append_fp4(codes, scale, new_rows, write_pos, err_flag=None):
+    """Quantise each sequence's new latent row (bf16 [B, d_qk]) to E2M1 codes (two per
+    byte, element 2i in the low four bits) with a power-of-two scale and store them at
+    row write_pos[b] of codes uint8 [B, s_kv, d_qk / 2] and scale fp32 [B, s_kv]."""
+    _need(codes, "codes", torch.uint8)
+    if codes.dim() != 3:
+        raise ValueError("codes must be [B, s_kv, d_qk / 2]")
+    B, s_kv, half = codes.shape
+    d_qk = 2 * half
+    _need(scale, "scale", torch.float32, (B, s_kv))
+    _need(new_rows, "new_rows", torch.bfloat16, (B, d_qk))
+    _need(write_pos, "write_pos", torch.int32, (B,))
+    _opt(err_flag, "err_flag", torch.int32, (1,))
+    check("latent_append_fp4", lib().dakv_latent_append_fp4(
+        _p(codes), _p(scale), _p(new_rows), _p(write_pos), B, s_kv, d_qk, _p(err_flag),
+        _stream()))
+
+
+def sparse_topk_attn_fp4(q, codes, scale, indices, d_v=512, sm_scale=None, out=None, lse=None,
+                         workspace=None, err_flag=None, validate=False, want_lse=True):
+    """sparse_topk_attn over the FP4 latent cache (codes uint8 [B, s_kv, d_qk / 2],
+    scale fp32 [B, s_kv]).  q bf16 [B, s_q, Hq, d_qk]; indices int32 [B, s_q, topk].
+    Returns ``(out, lse)``."""
+    _need(q, "q", torch.bfloat16)
+    if q.dim() != 4:
+        raise ValueError("q must be [B, s_q, Hq, d_qk]")
+    B, s_q, Hq, d_qk = q.shape
+    _need(codes, "codes", torch.uint8)
+    if codes.dim() != 3 or codes.shape[0] != B or 2 * codes.shape[2] != d_qk:
+        raise ValueError("codes must be [B, s_kv, d_qk / 2]")
+    s_kv = codes.shape[1]
+    _need(scale, "scale", torch.float32, (B, s_kv))
+    _need(indices, "indices", torch.int32)
+    if indices.dim() != 3 or tuple(indices.shape[:2]) != (B, s_q):
+        raise ValueError("indices must be [B, s_q, topk]")
+    topk = indices.shape[2]
+    if validate:
+        validate_sparse(indices.reshape(B * s_q, topk), s_kv)
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(d_qk)
+    if out is None:
+        out = torch.empty((B, s_q, Hq, d_v), dtype=torch.float32, device=q.device)
+    _need(out, "out", torch.float32, (B, s_q, Hq, d_v))
+    if lse is None and want_lse:
+        lse = torch.empty((B, s_q, Hq), dtype=torch.float32, device=q.device)
+    _opt(lse, "lse", torch.float32, (B, s_q, Hq))
+    _opt(err_flag, "err_flag", torch.int32, (1,))
+    nbytes = sparse_topk_decode_attn_workspace_size(B * s_q, Hq, d_qk, d_v, topk)
+    ws = _workspace(nbytes, q.device, workspace)
+    check("sparse_topk_attn_fp4", lib().dakv_sparse_topk_attn_fp4(
+        _p(q), _p(codes), _p(scale), _p(indices), B, s_q, Hq, s_kv, d_qk, d_v, topk,
+        float(sm_scale), _p(out), _p(lse), _p(ws), ws.numel(), _p(err_flag), _stream()))
+    return out, lse

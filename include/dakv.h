@@ -441,6 +441,25 @@ int dakv_sparse_topk_attn_fp8(const void* q, const void* codes, const float* sca
                               void* workspace, size_t workspace_bytes, int32_t* err_flag,
                               void* stream);
 
+/*
+ * FP4 latent cache of the sparse kernel (same passages: the decode kernel reads
+ * the KV cache in FP8 or FP4).  Codes uint8 [B, s_kv, d_qk / 2] in the E2M1
+ * format, packing and scale rule of the FP4 KV cache above (element 2i in the low
+ * four bits), one fp32 scale per latent row in scale [B, s_kv].
+ *
+ * latent_append_fp4 -- as latent_append_fp8 in E2M1; d_qk even, up to 576.
+ * sparse_topk_attn_fp4 -- as sparse_topk_attn_fp8 over the E2M1 codes (uint8
+ * [B, s_kv, d_qk / 2], 16-byte aligned).
+ */
+int dakv_latent_append_fp4(void* codes, float* scale, const void* new_rows,
+                           const int32_t* write_pos, int B, int s_kv, int d_qk,
+                           int32_t* err_flag, void* stream);
+int dakv_sparse_topk_attn_fp4(const void* q, const void* codes, const float* scale,
+                              const int32_t* indices, int B, int s_q, int Hq, int s_kv, int d_qk,
+                              int d_v, int topk, float sm_scale, float* out, float* lse,
+                              void* workspace, size_t workspace_bytes, int32_t* err_flag,
+                              void* stream);
+
 /* ========================================================================
  * Host validators (HOST pointers; no GPU needed).  [PyPTO] 3.3 and 5.1: the
  * index tensors are host-ready and are checked on the host before a call.

@@ -60,3 +60,10 @@ def test_sparse_fp8_bytes_halve_the_gathered_rows():
     assert b == 16 * 2048 * (576 + 4) + 16 * 128 * 576 * 2 + 16 * 128 * 512 * 4 + 16 * 2048 * 4
     full = acc.sparse_bytes(16, 128, 576, 512, 2048)
     assert full - b == 16 * 2048 * (576 * 2 - 576 - 4)
+
+
+def test_sparse_fp4_bytes_are_half_a_byte_per_value():
+    b4 = acc.sparse_fp4_bytes(16, 128, 576, 512, 2048)
+    b8 = acc.sparse_fp8_bytes(16, 128, 576, 512, 2048)
+    assert b8 - b4 == 16 * 2048 * 576 // 2
+    assert b4 == 16 * 2048 * (288 + 4) + 16 * 128 * 576 * 2 + 16 * 128 * 512 * 4 + 16 * 2048 * 4

@@ -349,6 +349,27 @@ def sparse_fp8_case(B, s_q, Hq, s_kv, topk, *, d_qk=576, d_v=512, device="cpu", 
                          float(sm_scale))
 
 
+def sparse_fp4_case(B, s_q, Hq, s_kv, topk, *, d_qk=576, d_v=512, device="cpu", seed=8,
+                    sm_scale=None):
+    """An FP4 latent cache as stored bytes: uniformly drawn bytes (two E2M1 codes each,
+    every code finite) ``[B, s_kv, d_qk / 2]`` and row scales 2^-3 .. 2^0, so the cached
+    values reach 6 in magnitude; q bf16 N(0,1); indices distinct within a token.
+    Returned in a SparseFp8Case (codes packed)."""
+    rng = np.random.default_rng(seed)
+    idx = np.stack([np.stack([rng.choice(s_kv, topk, replace=False) for _ in range(s_q)])
+                    for _ in range(B)]).astype(np.int32).reshape(B, s_q, topk)
+    g = _gen(device, seed)
+    codes = torch.randint(0, 256, (B, s_kv, d_qk // 2), generator=g, device=device,
+                          dtype=torch.uint8)
+    e = torch.randint(-3, 1, (B, s_kv), generator=g, device=device, dtype=torch.int32)
+    scale = torch.exp2(e.to(torch.float32))
+    q = _randn_bf16((B, s_q, Hq, d_qk), g, device)
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(d_qk)
+    return SparseFp8Case(q, codes, scale, torch.from_numpy(idx).to(device), d_v,
+                         float(sm_scale))
+
+
 def sparse_mla(*, device="cpu", seed=5):
     """Batch 16, 128 heads, d_qk 576 / d_v 512, context 32768, top-2048."""
     return sparse_case(16, 128, 32768, 2048, device=device, seed=seed)
