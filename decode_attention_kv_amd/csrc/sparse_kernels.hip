@@ -466,7 +466,9 @@ sparse_split_kernel(const uint16_t* __restrict__ q, const void* __restrict__ kv,
 }
 
 // Combine the splits of one (sequence, head): weights 2^(lse_j - max).  Splits
-// are taken 8 at a time with all 8 loads of a thread issued before their use.
+// are taken 8 at a time; each thread issues its log-sum-exp and partial loads of
+// a batch together, so a head of up to 8 splits takes one memory round trip
+// (running max and sums rescaled from batch to batch).
 constexpr int kMergeBatch = 8;
 static_assert(kDv == 2 * 256, "two columns per thread");
 
@@ -476,35 +478,34 @@ sparse_merge_kernel(const float* __restrict__ ws_o, const float* __restrict__ ws
   const int bh = blockIdx.x;
   const float* lp = ws_lse + (size_t)bh * n_splits;
   const float* op = ws_o + (size_t)bh * n_splits * kDv;
-  float M = kNegInf;
+  const int d0 = threadIdx.x * 2;  // two adjacent columns per thread
+  float M = kNegInf, num0 = 0.f, num1 = 0.f, den = 0.f;
   for (int j0 = 0; j0 < n_splits; j0 += kMergeBatch) {
     float x[kMergeBatch];
+    float2 v[kMergeBatch];
 #pragma unroll
-    for (int k = 0; k < kMergeBatch; ++k) x[k] = j0 + k < n_splits ? lp[j0 + k] : kNegInf;
-#pragma unroll
-    for (int k = 0; k < kMergeBatch; ++k) M = fmaxf(M, x[k]);
-  }
-  const int d0 = threadIdx.x * 2;  // two adjacent columns per thread
-  float num0 = 0.f, num1 = 0.f, den = 0.f;
-  if (M != kNegInf) {
-    for (int j0 = 0; j0 < n_splits; j0 += kMergeBatch) {
-      float w[kMergeBatch];
-      float2 v[kMergeBatch];
-#pragma unroll
-      for (int k = 0; k < kMergeBatch; ++k) {
-        const bool in = j0 + k < n_splits;
-        w[k] = in ? lp[j0 + k] : kNegInf;
-        v[k] = in ? *reinterpret_cast<const float2*>(op + (size_t)(j0 + k) * kDv + d0)
-                  : make_float2(0.f, 0.f);
-      }
-#pragma unroll
-      for (int k = 0; k < kMergeBatch; ++k) {
-        const float wk = exp2_fast(w[k] - M);
-        num0 += wk * v[k].x;
-        num1 += wk * v[k].y;
-        den += wk;
-      }
+    for (int k = 0; k < kMergeBatch; ++k) {
+      const bool in = j0 + k < n_splits;
+      x[k] = in ? lp[j0 + k] : kNegInf;
+      v[k] = in ? *reinterpret_cast<const float2*>(op + (size_t)(j0 + k) * kDv + d0)
+                : make_float2(0.f, 0.f);
     }
+    float m = M;
+#pragma unroll
+    for (int k = 0; k < kMergeBatch; ++k) m = fmaxf(m, x[k]);
+    if (m == kNegInf) continue;  // nothing attended yet
+    const float r = exp2_fast(M - m);  // 0 while M is -inf
+    num0 *= r;
+    num1 *= r;
+    den *= r;
+#pragma unroll
+    for (int k = 0; k < kMergeBatch; ++k) {
+      const float wk = exp2_fast(x[k] - m);
+      num0 += wk * v[k].x;
+      num1 += wk * v[k].y;
+      den += wk;
+    }
+    M = m;
   }
   const float inv = M == kNegInf ? 0.f : 1.f / den;
   *reinterpret_cast<float2*>(out + (size_t)bh * kDv + d0) = make_float2(num0 * inv, num1 * inv);

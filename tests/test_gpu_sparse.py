@@ -36,6 +36,7 @@ def ref(case, rows=None):
     (3, 32, 64, 1),         # a single index
     (2, 32, 3000, 1000),    # two index splits, the second ragged
     (2, 16, 100, 0),        # no index: zero output, lse -inf
+    (1, 16, 8000, 5000),    # ten index splits: the merge takes them in two batches
 ])
 def test_sparse_matches_oracle(B, Hq, s_kv, topk):
     print(f"sparse B={B} Hq={Hq} s_kv={s_kv} topk={topk}", flush=True)
