@@ -29,7 +29,7 @@ float64, with no tiling, no splitting and no online softmax:
 * ``fp4``           -- the FP4 KV cache for decode: E2M1 codes, two per byte, with
   a power-of-two scale per cached row, its quantisation and the decode attention
   over it (same page: the decode kernel reads FP8 or FP4 and dequantises it);
-  also the FP4 latent cache of the sparse kernel.
+  also the FP4 paged pool and the FP4 latent cache of the sparse kernel.
 
 bf16 tensors enter the oracle as their raw 16-bit patterns (``numpy.uint16``) and
 are widened exactly to float64 (``bf16.widen``); copies (append, gather) move the
@@ -63,7 +63,14 @@ from .fp8 import (
     sparse_topk_attn_fp8,
 )
 from . import fp4
-from .fp4 import kv_append_fp4, decode_static_fp4, latent_append_fp4, sparse_topk_attn_fp4
+from .fp4 import (
+    kv_append_fp4,
+    decode_static_fp4,
+    latent_append_fp4,
+    sparse_topk_attn_fp4,
+    decode_paged_fp4,
+    paged_append_fp4,
+)
 
 __all__ = [
     "widen",
@@ -95,4 +102,6 @@ __all__ = [
     "sparse_topk_attn_fp8",
     "latent_append_fp4",
     "sparse_topk_attn_fp4",
+    "decode_paged_fp4",
+    "paged_append_fp4",
 ]

@@ -19,6 +19,9 @@ row, for K and for V, kept in its own array):
 * the cached value is decode(code) * s, exactly representable in bf16, so the
   attention over the FP4 cache is the attention of the static layout over those
   values;
+* the paged pool in FP4 holds packed codes ``[num_blocks, block_size, Hkv, D/2]`` and
+  one scale per (block, slot, KV head) for K and for V, with the new token of a
+  sequence placed as in the FP8 pool (its last position, through the table);
 * the sparse kernel's latent cache in FP4 holds packed codes ``[B, s_kv, d_qk/2]``
   and one scale per latent row ``[B, s_kv]`` for all its columns, as the FP8
   latent cache does; the sparse attention runs over the dequantised gathered rows.
@@ -29,6 +32,7 @@ import math
 import numpy as np
 
 from .bf16 import widen
+from .paged import _offsets, token_rows, validate_paged
 from .sparse import sparse_topk_decode, validate_sparse
 from .static_cache import attended_rows, softmax_weighted_sum
 
@@ -209,3 +213,63 @@ def sparse_topk_attn_fp4(q, codes, scale, indices, d_v, sm_scale):
                                       d_v, sm_scale)
             out[b, t], lse[b, t] = o[0], l[0]
     return out, lse
+
+
+def decode_paged_fp4(q, k_codes, v_codes, k_scale, v_scale, block_tables, seq_lens,
+                     seq_offset=None, scale=None):
+    """Paged GQA decode over an FP4 pool: the attention of decode_paged over the
+    dequantised rows.  q ``[B, Hq, D]`` (bf16 bits or float); packed codes uint8
+    ``[num_blocks, block_size, Hkv, D/2]``; scales ``[num_blocks, block_size, Hkv]``.
+    Returns ``out [B, Hq, D]`` and ``lse [B, Hq]`` (float64)."""
+    q = np.asarray(q)
+    qf = widen(q) if q.dtype == np.uint16 else q.astype(np.float64)
+    B, Hq, D = qf.shape
+    num_blocks, block_size, Hkv, half = np.shape(k_codes)
+    if 2 * half != D or np.shape(v_codes) != np.shape(k_codes):
+        raise ValueError("codes must be [num_blocks, block_size, Hkv, D/2]")
+    if np.shape(k_scale) != (num_blocks, block_size, Hkv) or np.shape(v_scale) != np.shape(k_scale):
+        raise ValueError("scales must be [num_blocks, block_size, Hkv]")
+    if Hq % Hkv != 0:
+        raise ValueError("query heads must be a multiple of KV heads")
+    group = Hq // Hkv
+    validate_paged(block_tables, seq_lens, seq_offset, num_blocks, block_size)
+    seq_lens = np.asarray(seq_lens, dtype=np.int64).reshape(-1)
+    offsets = _offsets(seq_offset, B)
+    if scale is None:
+        scale = 1.0 / np.sqrt(D)
+    out = np.zeros((B, Hq, D))
+    lse = np.full((B, Hq), -np.inf)
+    for b in range(B):
+        phys, slot = token_rows(b, block_tables, seq_lens, offsets, block_size)
+        K = dequantize(np.asarray(k_codes)[phys, slot], np.asarray(k_scale)[phys, slot])
+        V = dequantize(np.asarray(v_codes)[phys, slot], np.asarray(v_scale)[phys, slot])
+        for h in range(Hq):
+            g = h // group
+            out[b, h], lse[b, h] = softmax_weighted_sum(scale * (K[:, g, :] @ qf[b, h]),
+                                                        V[:, g, :])
+    return out, lse
+
+
+def paged_append_fp4(k_codes, v_codes, k_scale, v_scale, k_new, v_new, block_tables, seq_lens,
+                     seq_offset=None):
+    """Quantise the new token's K and V rows (bf16 bits ``[B, Hkv, D]``) to E2M1 and
+    store them as token len_b - 1 of each sequence, at its place in the pool (block
+    table, then slot).  Returns updated copies of the four arrays; a sequence of
+    length 0 has no place for the token and is an error."""
+    k_codes, v_codes = np.array(k_codes, copy=True), np.array(v_codes, copy=True)
+    k_scale, v_scale = np.array(k_scale, copy=True), np.array(v_scale, copy=True)
+    num_blocks, block_size = k_codes.shape[:2]
+    validate_paged(block_tables, seq_lens, seq_offset, num_blocks, block_size)
+    seq_lens = np.asarray(seq_lens, dtype=np.int64).reshape(-1)
+    B = seq_lens.shape[0] - 1
+    offsets = _offsets(seq_offset, B)
+    kq, ks = quantize_rows(k_new)
+    vq, vs = quantize_rows(v_new)
+    for b in range(B):
+        phys, slot = token_rows(b, block_tables, seq_lens, offsets, block_size)
+        if phys.shape[0] == 0:
+            raise ValueError(f"sequence {b} has length 0: no place for its new token")
+        p, sl = phys[-1], slot[-1]
+        k_codes[p, sl], v_codes[p, sl] = kq[b], vq[b]
+        k_scale[p, sl], v_scale[p, sl] = ks[b], vs[b]
+    return k_codes, v_codes, k_scale, v_scale

@@ -181,3 +181,80 @@ def test_sparse_fp4_rejects_out_of_range_indices():
     for bad in (5, -1):
         with pytest.raises(ValueError):
             oracle.sparse_topk_attn_fp4(q, codes, scale, np.array([[[0, bad]]]), 4, 1.0)
+
+
+# ------------------------------------------------------------------ paged FP4 pool
+
+
+def _small_pool_fp4(rng, lengths, bs, Hkv, D):
+    """A pool holding the E2M1-quantised rows of random bf16 K/V, its table and offsets."""
+    need = [-(-L // bs) for L in lengths]
+    nb = sum(need) + 3
+    perm = rng.permutation(nb).astype(np.int32)
+    tables = np.full((len(lengths), max(need)), -1, np.int32)
+    at = 0
+    for q, n in enumerate(need):
+        tables[q, :n] = perm[at:at + n]
+        at += n
+    seq_lens = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    kc, ks = fp4.quantize_rows(round_to_bf16_bits(rng.standard_normal((nb, bs, Hkv, D)) * 2))
+    vc, vs = fp4.quantize_rows(round_to_bf16_bits(rng.standard_normal((nb, bs, Hkv, D))))
+    return kc, vc, ks, vs, tables, seq_lens
+
+
+def test_paged_fp4_decode_equals_bf16_paged_decode_of_the_same_values():
+    rng = np.random.default_rng(61)
+    lengths, bs, Hkv, D, Hq = [5, 16, 33], 8, 2, 16, 4
+    kc, vc, ks, vs, tables, seq_lens = _small_pool_fp4(rng, lengths, bs, Hkv, D)
+    k_deq = round_to_bf16_bits(fp4.dequantize(kc, ks))
+    v_deq = round_to_bf16_bits(fp4.dequantize(vc, vs))
+    assert np.array_equal(oracle.widen(v_deq), fp4.dequantize(vc, vs))
+    q = round_to_bf16_bits(rng.standard_normal((3, Hq, D)))
+    a, la = oracle.decode_paged_fp4(q, kc, vc, ks, vs, tables, seq_lens)
+    b, lb = oracle.decode_paged(q, k_deq, v_deq, tables, seq_lens)
+    assert np.array_equal(a, b) and np.array_equal(la, lb)
+
+
+def test_paged_fp4_decode_equals_static_fp4_decode_of_the_same_rows():
+    rng = np.random.default_rng(62)
+    lengths, bs, Hkv, D, group = [7, 12], 4, 2, 8, 2
+    kc, vc, ks, vs, tables, seq_lens = _small_pool_fp4(rng, lengths, bs, Hkv, D)
+    q = rng.standard_normal((2, Hkv * group, D))
+    out, lse = oracle.decode_paged_fp4(q, kc, vc, ks, vs, tables, seq_lens)
+    cap = max(lengths)
+    for b, L in enumerate(lengths):
+        t = np.arange(L)
+        phys, slot = tables[b, t // bs], t % bs
+        skc = np.zeros((1, Hkv * group, cap, D // 2), np.uint8)
+        svc = np.zeros_like(skc)
+        sks = np.ones((1, Hkv * group, cap))
+        svs = np.ones_like(sks)
+        for h in range(Hkv * group):
+            skc[0, h, :L] = kc[phys, slot, h // group]
+            svc[0, h, :L] = vc[phys, slot, h // group]
+            sks[0, h, :L] = ks[phys, slot, h // group]
+            svs[0, h, :L] = vs[phys, slot, h // group]
+        o2, l2 = oracle.decode_static_fp4(q[b:b + 1], skc, svc, sks, svs, valid_len=[L])
+        assert np.allclose(out[b], o2[0], rtol=0, atol=1e-13)
+        assert np.allclose(lse[b], l2[0], rtol=0, atol=1e-13)
+
+
+def test_paged_append_fp4_places_the_new_token_at_the_last_position():
+    rng = np.random.default_rng(63)
+    lengths, bs, Hkv, D = [1, 9, 16], 8, 2, 16
+    kc, vc, ks, vs, tables, seq_lens = _small_pool_fp4(rng, lengths, bs, Hkv, D)
+    kn = round_to_bf16_bits(rng.standard_normal((3, Hkv, D)) * 5)
+    vn = round_to_bf16_bits(rng.standard_normal((3, Hkv, D)))
+    kc2, vc2, ks2, vs2 = oracle.paged_append_fp4(kc, vc, ks, vs, kn, vn, tables, seq_lens)
+    qk, sk = fp4.quantize_rows(kn)
+    qv, sv = fp4.quantize_rows(vn)
+    changed = np.zeros(kc.shape[:2], bool)
+    for b, L in enumerate(lengths):
+        p, s = tables[b, (L - 1) // bs], (L - 1) % bs
+        assert np.array_equal(kc2[p, s], qk[b]) and np.array_equal(vc2[p, s], qv[b])
+        assert np.array_equal(ks2[p, s], sk[b]) and np.array_equal(vs2[p, s], sv[b])
+        changed[p, s] = True
+    assert np.array_equal(kc2[~changed], kc[~changed]) and np.array_equal(vs2[~changed], vs[~changed])
+    with pytest.raises(ValueError):
+        oracle.paged_append_fp4(kc, vc, ks, vs, kn, vn, tables,
+                                np.array([0, 1, 1, 17], np.int32))
