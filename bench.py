@@ -473,22 +473,26 @@ def paged_leg(torch, dakv, workloads, acc, counter_pass=False):
             "frac_of_peak": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
 
 
-def paged_fp8_leg(torch, dakv, workloads, acc):
-    """The paged GQA config over an FP8 pool (same lengths, table and pool size):
-    random finite E4M3 codes, row scales random powers of two."""
+def paged_lowbit_leg(torch, dakv, workloads, acc, fmt="fp8"):
+    """The paged GQA config over a low-bit pool (same lengths, table and pool size):
+    random finite E4M3 codes (fmt "fp8") or random bytes of two E2M1 codes ("fp4"),
+    row scales random powers of two."""
     case = workloads.paged_gqa(device="cuda:0", seed=4)
     idx = case.index
     nb, bs, Hkv, D = case.key_cache.shape
     del case.key_cache, case.value_cache
+    fp4 = fmt == "fp4"
     g = torch.Generator(device="cuda:0")
-    g.manual_seed(12)
+    g.manual_seed(13 if fp4 else 12)
     codes = []
     for _ in range(2):
-        c = torch.randint(0, 256, (nb, bs, Hkv, D), generator=g, device="cuda:0",
-                          dtype=torch.uint8)
-        c[(c & 0x7F) == 0x7F] = 0x7E
+        c = torch.randint(0, 256, (nb, bs, Hkv, D // 2 if fp4 else D), generator=g,
+                          device="cuda:0", dtype=torch.uint8)
+        if not fp4:
+            c[(c & 0x7F) == 0x7F] = 0x7E
         codes.append(c)
-    scales = [torch.exp2(torch.randint(-12, -5, (nb, bs, Hkv), generator=g,
+    lo, hi = (-3, 1) if fp4 else (-12, -5)
+    scales = [torch.exp2(torch.randint(lo, hi, (nb, bs, Hkv), generator=g,
                                        device="cuda:0").float()) for _ in range(2)]
     t = torch.from_numpy(idx.block_tables).to("cuda:0")
     s = torch.from_numpy(idx.seq_lens).to("cuda:0")
@@ -497,15 +501,17 @@ def paged_fp8_leg(torch, dakv, workloads, acc):
     max_len = max(idx.lengths)
     ws = torch.zeros(dakv.decode_attn_paged_workspace_size(B, case.Hq, D, max_len, bs),
                      dtype=torch.uint8, device="cuda:0")
-    call = lambda: dakv.decode_attn_paged_fp8(case.q, codes[0], codes[1], scales[0], scales[1],
-                                              t, s, None, max_seq_len=max_len,
-                                              scale=case.scale, out=out, workspace=ws,
-                                              want_lse=False)
+    fn = dakv.decode_attn_paged_fp4 if fp4 else dakv.decode_attn_paged_fp8
+    call = lambda: fn(case.q, codes[0], codes[1], scales[0], scales[1], t, s, None,
+                      max_seq_len=max_len, scale=case.scale, out=out, workspace=ws,
+                      want_lse=False)
     ms = time_cold(torch, call)
-    nbytes = acc.decode_paged_fp8_bytes(idx.lengths, case.Hq, Hkv, D, bs)
+    nbytes = (acc.decode_paged_fp4_bytes if fp4 else acc.decode_paged_fp8_bytes)(
+        idx.lengths, case.Hq, Hkv, D, bs)
     bf16_bytes = acc.decode_paged_bytes(idx.lengths, case.Hq, Hkv, D, bs)
     del case, codes, scales, out, ws
-    return {"workload": "paged GQA decode over an FP8 pool (E4M3 + row scale): batch 64, "
+    name = "an FP4 pool (E2M1 two per byte" if fp4 else "an FP8 pool (E4M3"
+    return {"workload": f"paged GQA decode over {name} + row scale): batch 64, "
                         "32 query / 8 KV heads, head_dim 128, block 16, contexts log-uniform "
                         "[512, 16384]",
             "us_per_call": round(ms * 1e3, 2), "algorithmic_bytes": nbytes,
@@ -771,7 +777,9 @@ def main():
         torch.cuda.empty_cache()
         line["paged_gqa"] = paged_leg(torch, dakv, workloads, acc)
         torch.cuda.empty_cache()
-        line["paged_gqa_fp8"] = paged_fp8_leg(torch, dakv, workloads, acc)
+        line["paged_gqa_fp8"] = paged_lowbit_leg(torch, dakv, workloads, acc, "fp8")
+        torch.cuda.empty_cache()
+        line["paged_gqa_fp4"] = paged_lowbit_leg(torch, dakv, workloads, acc, "fp4")
         torch.cuda.empty_cache()
         line["sparse_mla"] = sparse_leg(torch, dakv, workloads, acc)
         line["sparse_mla_2_tokens"] = sparse_tokens_leg(torch, dakv, workloads, acc)

@@ -72,6 +72,11 @@ SIGNATURES = {
     "dakv_decode_attn_paged_fp8": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _vp, _vp, _i, _i,
                                         _i, _i, _i, _i, _i, _f, _vp, _vp, _vp, _sz, _i, _vp,
                                         _vp]),
+    "dakv_paged_append_fp4": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _vp, _vp, _i, _i, _i,
+                                   _i, _i, _vp, _vp]),
+    "dakv_decode_attn_paged_fp4": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _vp, _vp, _i, _i,
+                                        _i, _i, _i, _i, _i, _f, _vp, _vp, _vp, _sz, _i, _vp,
+                                        _vp]),
     "dakv_validate_paged": (_i, [_vp, _i, _i, _vp, _vp, _i, _i]),
     "dakv_validate_sparse": (_i, [_vp, _i, _i, _i]),
     "dakv_validate_range": (_i, [_vp, _i, _i, _i]),

@@ -109,6 +109,14 @@ def decode_paged_fp8_bytes(lengths, Hq, Hkv, D, block_size, q_elem=BF16, with_ls
     return kv + q + out + table + (B + 1) * INT32
 
 
+def decode_paged_fp4_bytes(lengths, Hq, Hkv, D, block_size, q_elem=BF16, with_lse=False):
+    """Paged GQA decode over the FP4 pool: as decode_paged_fp8_bytes with D / 2 code
+    bytes per row."""
+    T = sum(int(x) for x in lengths)
+    return decode_paged_fp8_bytes(lengths, Hq, Hkv, D, block_size, q_elem, with_lse) - \
+        T * Hkv * (D // 2) * 2
+
+
 def decode_flops(rows, heads_per_row, d_qk, d_v):
     """Multiply-add flops of scores plus the weighted sum (2 per MAC)."""
     return 2 * rows * heads_per_row * (d_qk + d_v)

@@ -303,32 +303,34 @@ static bool paged_fp8_shape(int Hq, int Hkv, int D, int block_size) {
          (block_size == 16 || block_size == 32 || block_size == 64 || block_size == 128);
 }
 
-int dakv_paged_append_fp8(void* k_codes, void* v_codes, float* k_scale, float* v_scale,
-                          const void* k_new, const void* v_new, const int32_t* block_tables,
-                          int table_cols, const int32_t* seq_lens, const int32_t* seq_offset,
-                          int B, int Hkv, int D, int num_blocks, int block_size,
-                          int32_t* err_flag, void* stream) {
+// Shared by the FP8 and FP4 pools (codes one byte or half a byte per element).
+static int paged_append_lowbit(bool fp4, void* k_codes, void* v_codes, float* k_scale,
+                               float* v_scale, const void* k_new, const void* v_new,
+                               const int32_t* block_tables, int table_cols,
+                               const int32_t* seq_lens, const int32_t* seq_offset, int B,
+                               int Hkv, int D, int num_blocks, int block_size, int32_t* err_flag,
+                               void* stream) {
   if (B < 0 || Hkv <= 0 || D <= 0 || num_blocks <= 0 || block_size <= 0 || table_cols <= 0)
     return DAKV_EINVAL;
   if (B == 0) return DAKV_OK;
-  if (D > 256) return DAKV_ENOTSUP;
+  if (D > 256 || (fp4 && D % 16 != 0)) return DAKV_ENOTSUP;
   if (!k_codes || !v_codes || !k_scale || !v_scale || !k_new || !v_new || !block_tables ||
       !seq_lens)
     return DAKV_EINVAL;
-  return from_hip(dakv::launch_paged_append_fp8(k_codes, v_codes, k_scale, v_scale, k_new,
-                                                v_new, block_tables, table_cols, seq_lens,
-                                                seq_offset, B, Hkv, D, num_blocks, block_size,
-                                                err_flag, as_stream(stream)));
+  const auto launch = fp4 ? dakv::launch_paged_append_fp4 : dakv::launch_paged_append_fp8;
+  return from_hip(launch(k_codes, v_codes, k_scale, v_scale, k_new, v_new, block_tables,
+                         table_cols, seq_lens, seq_offset, B, Hkv, D, num_blocks, block_size,
+                         err_flag, as_stream(stream)));
 }
 
-int dakv_decode_attn_paged_fp8(const void* q, const void* k_codes, const void* v_codes,
-                               const float* k_scale, const float* v_scale,
+static int decode_paged_lowbit(bool fp4, const void* q, const void* k_codes,
+                               const void* v_codes, const float* k_scale, const float* v_scale,
                                const int32_t* block_tables, int table_cols,
-                               const int32_t* seq_lens, const int32_t* seq_offset, int B,
-                               int Hq, int Hkv, int D, int num_blocks, int block_size,
-                               int max_seq_len, float scale, float* out, float* lse,
-                               void* workspace, size_t workspace_bytes, int num_splits,
-                               int32_t* err_flag, void* stream) {
+                               const int32_t* seq_lens, const int32_t* seq_offset, int B, int Hq,
+                               int Hkv, int D, int num_blocks, int block_size, int max_seq_len,
+                               float scale, float* out, float* lse, void* workspace,
+                               size_t workspace_bytes, int num_splits, int32_t* err_flag,
+                               void* stream) {
   if (B < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || num_blocks <= 0 || block_size <= 0 ||
       max_seq_len < 0 || table_cols <= 0 || num_splits < 0)
     return DAKV_EINVAL;
@@ -346,10 +348,58 @@ int dakv_decode_attn_paged_fp8(const void* q, const void* k_codes, const void* v
     return DAKV_EINVAL;
   const dakv::SplitPlan plan =
       dakv::plan_paged(B, Hkv, Hq / Hkv, max_seq_len, block_size, num_splits);
-  return from_hip(dakv::launch_decode_paged_fp8(
-      q, k_codes, v_codes, k_scale, v_scale, block_tables, table_cols, seq_lens, seq_offset, B,
-      Hq, Hkv, num_blocks, block_size, max_seq_len, scale, out, lse, workspace, plan, err_flag,
-      as_stream(stream)));
+  const auto launch = fp4 ? dakv::launch_decode_paged_fp4 : dakv::launch_decode_paged_fp8;
+  return from_hip(launch(q, k_codes, v_codes, k_scale, v_scale, block_tables, table_cols,
+                         seq_lens, seq_offset, B, Hq, Hkv, num_blocks, block_size, max_seq_len,
+                         scale, out, lse, workspace, plan, err_flag, as_stream(stream)));
+}
+
+int dakv_paged_append_fp8(void* k_codes, void* v_codes, float* k_scale, float* v_scale,
+                          const void* k_new, const void* v_new, const int32_t* block_tables,
+                          int table_cols, const int32_t* seq_lens, const int32_t* seq_offset,
+                          int B, int Hkv, int D, int num_blocks, int block_size,
+                          int32_t* err_flag, void* stream) {
+  return paged_append_lowbit(false, k_codes, v_codes, k_scale, v_scale, k_new, v_new,
+                             block_tables, table_cols, seq_lens, seq_offset, B, Hkv, D,
+                             num_blocks, block_size, err_flag, stream);
+}
+
+int dakv_paged_append_fp4(void* k_codes, void* v_codes, float* k_scale, float* v_scale,
+                          const void* k_new, const void* v_new, const int32_t* block_tables,
+                          int table_cols, const int32_t* seq_lens, const int32_t* seq_offset,
+                          int B, int Hkv, int D, int num_blocks, int block_size,
+                          int32_t* err_flag, void* stream) {
+  return paged_append_lowbit(true, k_codes, v_codes, k_scale, v_scale, k_new, v_new,
+                             block_tables, table_cols, seq_lens, seq_offset, B, Hkv, D,
+                             num_blocks, block_size, err_flag, stream);
+}
+
+int dakv_decode_attn_paged_fp8(const void* q, const void* k_codes, const void* v_codes,
+                               const float* k_scale, const float* v_scale,
+                               const int32_t* block_tables, int table_cols,
+                               const int32_t* seq_lens, const int32_t* seq_offset, int B,
+                               int Hq, int Hkv, int D, int num_blocks, int block_size,
+                               int max_seq_len, float scale, float* out, float* lse,
+                               void* workspace, size_t workspace_bytes, int num_splits,
+                               int32_t* err_flag, void* stream) {
+  return decode_paged_lowbit(false, q, k_codes, v_codes, k_scale, v_scale, block_tables,
+                             table_cols, seq_lens, seq_offset, B, Hq, Hkv, D, num_blocks,
+                             block_size, max_seq_len, scale, out, lse, workspace,
+                             workspace_bytes, num_splits, err_flag, stream);
+}
+
+int dakv_decode_attn_paged_fp4(const void* q, const void* k_codes, const void* v_codes,
+                               const float* k_scale, const float* v_scale,
+                               const int32_t* block_tables, int table_cols,
+                               const int32_t* seq_lens, const int32_t* seq_offset, int B,
+                               int Hq, int Hkv, int D, int num_blocks, int block_size,
+                               int max_seq_len, float scale, float* out, float* lse,
+                               void* workspace, size_t workspace_bytes, int num_splits,
+                               int32_t* err_flag, void* stream) {
+  return decode_paged_lowbit(true, q, k_codes, v_codes, k_scale, v_scale, block_tables,
+                             table_cols, seq_lens, seq_offset, B, Hq, Hkv, D, num_blocks,
+                             block_size, max_seq_len, scale, out, lse, workspace,
+                             workspace_bytes, num_splits, err_flag, stream);
 }
 
 // ---------------------------------------------------- sparse_topk_decode_attn

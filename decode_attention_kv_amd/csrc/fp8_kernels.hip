@@ -131,6 +131,32 @@ __device__ __forceinline__ uint32_t e2m1_code(float y) {
   return (code != 0 && y < 0.f) ? (code | 8u) : code;
 }
 
+// One wave quantises one row of D <= 128 kPairs bf16 values to E2M1: lane l takes
+// the value pairs (2p, 2p + 1) for p = l + 64 k and writes their byte p.
+template <int kPairs>
+__device__ __forceinline__ void quantise_row_wave_fp4(const uint16_t* __restrict__ src, int D,
+                                                      uint8_t* __restrict__ dst,
+                                                      float* __restrict__ dst_scale, int lane) {
+  float x[2 * kPairs];
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 2 * kPairs; ++i) {
+    const int v = 2 * (lane + 64 * (i >> 1)) + (i & 1);
+    x[i] = v < D ? __uint_as_float((uint32_t)src[v] << 16) : 0.f;
+    amax = fmaxf(amax, fabsf(x[i]));
+  }
+  for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+  const int e = e2m1_exponent_for(amax);
+#pragma unroll
+  for (int k = 0; k < kPairs; ++k) {
+    const int p = lane + 64 * k;
+    if (2 * p < D)
+      dst[p] = (uint8_t)(e2m1_code(ldexpf(x[2 * k], -e)) |
+                         (e2m1_code(ldexpf(x[2 * k + 1], -e)) << 4));
+  }
+  if (lane == 0) *dst_scale = ldexpf(1.f, e);
+}
+
 __global__ void __launch_bounds__(256)
 kv_append_fp4_kernel(uint8_t* __restrict__ k_codes, uint8_t* __restrict__ v_codes,
                      float* __restrict__ k_scale, float* __restrict__ v_scale,
@@ -148,27 +174,10 @@ kv_append_fp4_kernel(uint8_t* __restrict__ k_codes, uint8_t* __restrict__ v_code
     if (unit == 0 && lane == 0) raise_flag(err_flag, 2);
     return;
   }
-  const uint16_t* src = (is_v ? v_new : k_new) + ((size_t)b * H + h) * D;
   const size_t row = ((size_t)b * H + h) * cap + pos;
-  uint8_t* dst = (is_v ? v_codes : k_codes) + row * (D / 2);
-  float x[4];
-  float amax = 0.f;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {            // D <= 256: pairs (2l, 2l+1) and (2l+128, 2l+129)
-    const int d = 2 * lane + 128 * (i >> 1) + (i & 1);
-    x[i] = d < D ? __uint_as_float((uint32_t)src[d] << 16) : 0.f;
-    amax = fmaxf(amax, fabsf(x[i]));
-  }
-  for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
-  const int e = e2m1_exponent_for(amax);
-#pragma unroll
-  for (int pr = 0; pr < 2; ++pr) {
-    const int d = 2 * lane + 128 * pr;
-    if (d < D)
-      dst[d / 2] = (uint8_t)(e2m1_code(ldexpf(x[2 * pr], -e)) |
-                             (e2m1_code(ldexpf(x[2 * pr + 1], -e)) << 4));
-  }
-  if (lane == 0) (is_v ? v_scale : k_scale)[row] = ldexpf(1.f, e);
+  quantise_row_wave_fp4<2>((is_v ? v_new : k_new) + ((size_t)b * H + h) * D, D,
+                           (is_v ? v_codes : k_codes) + row * (D / 2),
+                           (is_v ? v_scale : k_scale) + row, lane);  // D <= 256
   if (mask && unit == 0 && lane == 0) mask[(size_t)b * cap + pos] = 1;
 }
 
@@ -193,7 +202,6 @@ latent_append_fp4_kernel(uint8_t* __restrict__ codes, float* __restrict__ scale,
                          const uint16_t* __restrict__ new_rows,
                          const int32_t* __restrict__ write_pos, int B, int s_kv, int d,
                          int32_t* err_flag) {
-  constexpr int kPairs = 5;                  // d <= 640
   const int b = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (b >= B) return;
@@ -202,27 +210,9 @@ latent_append_fp4_kernel(uint8_t* __restrict__ codes, float* __restrict__ scale,
     if (lane == 0) raise_flag(err_flag, 2);
     return;
   }
-  const uint16_t* src = new_rows + (size_t)b * d;
-  float x[2 * kPairs];
-  float amax = 0.f;
-#pragma unroll
-  for (int i = 0; i < 2 * kPairs; ++i) {
-    const int v = 2 * (lane + 64 * (i >> 1)) + (i & 1);
-    x[i] = v < d ? __uint_as_float((uint32_t)src[v] << 16) : 0.f;
-    amax = fmaxf(amax, fabsf(x[i]));
-  }
-  for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
-  const int e = e2m1_exponent_for(amax);
   const size_t row = (size_t)b * s_kv + pos;
-  uint8_t* dst = codes + row * (d / 2);
-#pragma unroll
-  for (int k = 0; k < kPairs; ++k) {
-    const int p = lane + 64 * k;
-    if (2 * p < d)
-      dst[p] = (uint8_t)(e2m1_code(ldexpf(x[2 * k], -e)) |
-                         (e2m1_code(ldexpf(x[2 * k + 1], -e)) << 4));
-  }
-  if (lane == 0) scale[row] = ldexpf(1.f, e);
+  quantise_row_wave_fp4<5>(new_rows + (size_t)b * d, d, codes + row * (d / 2), scale + row,
+                           lane);  // d <= 640
 }
 
 hipError_t launch_latent_append_fp4(void* codes, float* scale, const void* new_rows,
@@ -297,7 +287,7 @@ struct E2M1Rows {                          // half a byte per element, element 2
 template <typename Fmt, int D, int U, int kSteps, bool kAppend>
 __global__ void __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(kSteps <= 2 ? 7 : 3)))
-static_decode_fp8_kernel(const float* __restrict__ q, uint8_t* __restrict__ k_codes,
+static_decode_lowbit_kernel(const float* __restrict__ q, uint8_t* __restrict__ k_codes,
                          uint8_t* __restrict__ v_codes, float* __restrict__ k_scale,
                          float* __restrict__ v_scale, int32_t* __restrict__ mask,
                          const int32_t* __restrict__ valid_len, const uint16_t* __restrict__ k_new,
@@ -509,14 +499,14 @@ static void launch_static_fp8_k(const float* q, void* k_codes, void* v_codes, fl
   auto* vn = static_cast<const uint16_t*>(v_new);
   if constexpr (Fmt::kRowDiv == 1) {
     if (write_pos) {
-      hipLaunchKernelGGL((static_decode_fp8_kernel<Fmt, D, 4, kSteps, true>), grid,
+      hipLaunchKernelGGL((static_decode_lowbit_kernel<Fmt, D, 4, kSteps, true>), grid,
                          dim3(kThreads), 0, stream, q, kc, vc, k_scale, v_scale, mask, valid_len,
                          kn, vn, write_pos, H, cap, scale * kLog2e, plan.chunk, B * H, w, out,
                          lse, err_flag);
       return;
     }
   }
-  hipLaunchKernelGGL((static_decode_fp8_kernel<Fmt, D, 4, kSteps, false>), grid,
+  hipLaunchKernelGGL((static_decode_lowbit_kernel<Fmt, D, 4, kSteps, false>), grid,
                      dim3(kThreads), 0, stream, q, kc, vc, k_scale, v_scale, mask, valid_len, kn,
                      vn, write_pos, H, cap, scale * kLog2e, plan.chunk, B * H, w, out, lse,
                      err_flag);
@@ -580,15 +570,17 @@ hipError_t launch_decode_static_fp4(const float* q, const void* k_codes, const v
 }
 
 // ---------------------------------------------------------------------------
-// paged_append_fp8: the new token of sequence b is its last token (position
-// len_b - 1, len_b = seq_lens[b+1] - seq_lens[b] counting it), placed through the
-// block table like every other token: block block_tables[b][seq_offset[b] / bs +
-// t / bs], slot t % bs.  One wave per (sequence, KV head, K or V), as
-// kv_append_fp8.  A sequence of length 0 or a bad table entry sets an error bit
-// (DAKV_ERR_SEQ_LENS, DAKV_ERR_BLOCK_ID) and writes nothing.
+// paged_append_fp8 / paged_append_fp4: the new token of sequence b is its last
+// token (position len_b - 1, len_b = seq_lens[b+1] - seq_lens[b] counting it),
+// placed through the block table like every other token: block
+// block_tables[b][seq_offset[b] / bs + t / bs], slot t % bs.  One wave per
+// (sequence, KV head, K or V), as kv_append_fp8 / kv_append_fp4.  A sequence of
+// length 0 or a bad table entry sets an error bit (DAKV_ERR_SEQ_LENS,
+// DAKV_ERR_BLOCK_ID) and writes nothing.
 // ---------------------------------------------------------------------------
+template <bool kFp4>
 __global__ void __launch_bounds__(256)
-paged_append_fp8_kernel(uint8_t* __restrict__ k_codes, uint8_t* __restrict__ v_codes,
+paged_append_lowbit_kernel(uint8_t* __restrict__ k_codes, uint8_t* __restrict__ v_codes,
                         float* __restrict__ k_scale, float* __restrict__ v_scale,
                         const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new,
                         const int32_t* __restrict__ block_tables, int table_cols,
@@ -620,9 +612,12 @@ paged_append_fp8_kernel(uint8_t* __restrict__ k_codes, uint8_t* __restrict__ v_c
     return;
   }
   const size_t row = ((size_t)phys * block_size + t % block_size) * Hkv + h;
-  quantise_row_wave<4>((is_v ? v_new : k_new) + ((size_t)b * Hkv + h) * D, D,
-                    (is_v ? v_codes : k_codes) + row * D, (is_v ? v_scale : k_scale) + row,
-                    lane);
+  const uint16_t* src = (is_v ? v_new : k_new) + ((size_t)b * Hkv + h) * D;
+  float* dscale = (is_v ? v_scale : k_scale) + row;
+  if constexpr (kFp4)
+    quantise_row_wave_fp4<2>(src, D, (is_v ? v_codes : k_codes) + row * (D / 2), dscale, lane);
+  else
+    quantise_row_wave<4>(src, D, (is_v ? v_codes : k_codes) + row * D, dscale, lane);
 }
 
 hipError_t launch_paged_append_fp8(void* k_codes, void* v_codes, float* k_scale,
@@ -631,20 +626,35 @@ hipError_t launch_paged_append_fp8(void* k_codes, void* v_codes, float* k_scale,
                                    const int32_t* seq_lens, const int32_t* seq_offset, int B,
                                    int Hkv, int D, int num_blocks, int block_size,
                                    int32_t* err_flag, hipStream_t stream) {
-  hipLaunchKernelGGL(paged_append_fp8_kernel, dim3((2 * Hkv + 3) / 4, B), dim3(256), 0, stream,
-                     static_cast<uint8_t*>(k_codes), static_cast<uint8_t*>(v_codes), k_scale,
-                     v_scale, static_cast<const uint16_t*>(k_new),
+  hipLaunchKernelGGL(paged_append_lowbit_kernel<false>, dim3((2 * Hkv + 3) / 4, B), dim3(256), 0,
+                     stream, static_cast<uint8_t*>(k_codes), static_cast<uint8_t*>(v_codes),
+                     k_scale, v_scale, static_cast<const uint16_t*>(k_new),
+                     static_cast<const uint16_t*>(v_new), block_tables, table_cols, seq_lens,
+                     seq_offset, Hkv, D, num_blocks, block_size, err_flag);
+  return hipGetLastError();
+}
+
+hipError_t launch_paged_append_fp4(void* k_codes, void* v_codes, float* k_scale,
+                                   float* v_scale, const void* k_new, const void* v_new,
+                                   const int32_t* block_tables, int table_cols,
+                                   const int32_t* seq_lens, const int32_t* seq_offset, int B,
+                                   int Hkv, int D, int num_blocks, int block_size,
+                                   int32_t* err_flag, hipStream_t stream) {
+  hipLaunchKernelGGL(paged_append_lowbit_kernel<true>, dim3((2 * Hkv + 3) / 4, B), dim3(256), 0,
+                     stream, static_cast<uint8_t*>(k_codes), static_cast<uint8_t*>(v_codes),
+                     k_scale, v_scale, static_cast<const uint16_t*>(k_new),
                      static_cast<const uint16_t*>(v_new), block_tables, table_cols, seq_lens,
                      seq_offset, Hkv, D, num_blocks, block_size, err_flag);
   return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
-// Paged GQA decode over the FP8 pool: paged_rows_kernel's work split (one
+// Paged GQA decode over the FP8 or FP4 pool: paged_rows_kernel's work split (one
 // workgroup per (sequence, split) over all KV heads; lane group gi serves KV head
-// gi % Hkv at token slot gi / Hkv) with 8 codes (8 bytes) per lane and a row's K
-// and V scales read by its lane group (one 4-byte address for the 16 lanes).  The
-// K scale multiplies the row's scores, the V scale its weight in O.
+// gi % Hkv at token slot gi / Hkv) with 8 codes per lane (8 bytes of E4M3 or 4
+// bytes of E2M1) and a row's K and V scales read by its lane group (one 4-byte
+// address for the 16 lanes).  The K scale multiplies the row's scores, the V scale
+// its weight in O.
 // ---------------------------------------------------------------------------
 // Step shape over the FP8 pool (rows per lane group per step, steps per unrolled
 // super-step).  Measured at G = 4 (batch 64, block 16): U = 4 in one step 262 us,
@@ -653,9 +663,9 @@ hipError_t launch_paged_append_fp8(void* k_codes, void* v_codes, float* k_scale,
 template <int G> struct PagedShapeFp8 : PagedShape<G> {};
 template <> struct PagedShapeFp8<4> { static constexpr int U = 4, kSteps = 1; };
 
-template <int G>
+template <typename Fmt, int G>
 __global__ void __launch_bounds__(kThreads)
-paged_rows_fp8_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ k_codes,
+paged_rows_lowbit_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ k_codes,
                       const uint8_t* __restrict__ v_codes, const float* __restrict__ k_scale,
                       const float* __restrict__ v_scale, const int32_t* __restrict__ block_tables,
                       int table_cols, const int32_t* __restrict__ seq_lens,
@@ -708,36 +718,37 @@ paged_rows_fp8_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict_
   }
   __syncthreads();
   const int bs_mask = block_size - 1;
-  const size_t code_off = (size_t)h * D + (size_t)sub * 8;
+  const size_t code_off = ((size_t)h * D + (size_t)sub * 8) / Fmt::kRowDiv;
   // the pool row (block, slot) of token t, or 0 with ok cleared (an in-bounds dummy)
   auto row_at = [&](int t, bool& ok) -> size_t {
     const int phys = ok ? tbl[(t >> bs_log2) - blk0] : -1;
     ok = phys >= 0;
     return ok ? (size_t)phys * block_size + (t & bs_mask) : 0;
   };
-  auto issue = [&](int t0, u32x2_t (&kw)[U], u32x2_t (&vw)[U], float (&ksc)[U],
+  typedef typename Fmt::Word Word;
+  auto issue = [&](int t0, Word (&kw)[U], Word (&vw)[U], float (&ksc)[U],
                    float (&vsc)[U], bool (&ok)[U]) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int t = t0 + u * ts;
       ok[u] = t < r1;
       const size_t row = row_at(t, ok[u]);
-      const size_t c = row * Hkv * D + code_off;
-      kw[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(k_codes + c));
-      vw[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(v_codes + c));
+      const size_t c = row * Hkv * (D / Fmt::kRowDiv) + code_off;
+      kw[u] = __builtin_nontemporal_load(reinterpret_cast<const Word*>(k_codes + c));
+      vw[u] = __builtin_nontemporal_load(reinterpret_cast<const Word*>(v_codes + c));
       ksc[u] = k_scale[row * Hkv + h];
       vsc[u] = v_scale[row * Hkv + h];
     }
   };
   HeadState<G> st;
   init_state(st);
-  auto consume = [&](const u32x2_t (&kw)[U], const u32x2_t (&vw)[U], const float (&ksc)[U],
+  auto consume = [&](const Word (&kw)[U], const Word (&vw)[U], const float (&ksc)[U],
                      const float (&vsc)[U], const bool (&ok)[U]) {
     float s[G][U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       float kf[8];
-      unpack8_fp8(kw[u], kf);
+      Fmt::unpack(kw[u], kf);
 #pragma unroll
       for (int j = 0; j < G; ++j) {
         float acc = 0.f;
@@ -749,7 +760,7 @@ paged_rows_fp8_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict_
     }
     float vf[U][8];
 #pragma unroll
-    for (int u = 0; u < U; ++u) unpack8_fp8(vw[u], vf[u]);
+    for (int u = 0; u < U; ++u) Fmt::unpack(vw[u], vf[u]);
 #pragma unroll
     for (int j = 0; j < G; ++j) {
       float mnew = st.m[j];
@@ -779,7 +790,7 @@ paged_rows_fp8_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict_
   const int step = U * ts;
   const int super = step * kSteps;
   for (int base = r0; base < r1; base += super) {
-    u32x2_t kw[2][U], vw[2][U];
+    Word kw[2][U], vw[2][U];
     float ksc[2][U], vsc[2][U];
     bool ok[2][U];
     issue(base + slot, kw[0], vw[0], ksc[0], vsc[0], ok[0]);
@@ -794,14 +805,15 @@ paged_rows_fp8_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict_
   finish_split_rows<G>(st, gi, sub, Hkv, ts, ws, (size_t)b * Hq, split, n, max_splits, out, lse);
 }
 
-hipError_t launch_decode_paged_fp8(const void* q, const void* k_codes, const void* v_codes,
-                                   const float* k_scale, const float* v_scale,
-                                   const int32_t* block_tables, int table_cols,
-                                   const int32_t* seq_lens, const int32_t* seq_offset, int B,
-                                   int Hq, int Hkv, int num_blocks, int block_size,
-                                   int max_seq_len, float scale, float* out, float* lse,
-                                   void* ws, const SplitPlan& plan, int32_t* err_flag,
-                                   hipStream_t stream) {
+template <typename Fmt>
+static hipError_t launch_paged_lowbit(const void* q, const void* k_codes, const void* v_codes,
+                                      const float* k_scale, const float* v_scale,
+                                      const int32_t* block_tables, int table_cols,
+                                      const int32_t* seq_lens, const int32_t* seq_offset, int B,
+                                      int Hq, int Hkv, int num_blocks, int block_size,
+                                      int max_seq_len, float scale, float* out, float* lse,
+                                      void* ws, const SplitPlan& plan, int32_t* err_flag,
+                                      hipStream_t stream) {
   const Workspace w = carve(ws, (size_t)B * Hq, plan.max_splits, 128);
   int bs_log2 = 0;
   while ((1 << bs_log2) < block_size) ++bs_log2;
@@ -810,7 +822,7 @@ hipError_t launch_decode_paged_fp8(const void* q, const void* k_codes, const voi
   const auto* vc = static_cast<const uint8_t*>(v_codes);
   const dim3 grid((unsigned)(B * plan.max_splits));
 #define DAKV_PAGED_FP8(GG)                                                                    \
-  hipLaunchKernelGGL(paged_rows_fp8_kernel<GG>, grid, dim3(kThreads), 0, stream, qb, kc, vc, \
+  hipLaunchKernelGGL((paged_rows_lowbit_kernel<Fmt, GG>), grid, dim3(kThreads), 0, stream, qb, kc, vc, \
                      k_scale, v_scale, block_tables, table_cols, seq_lens, seq_offset, Hkv,  \
                      num_blocks, block_size, bs_log2, max_seq_len, scale * kLog2e,           \
                      plan.chunk, plan.max_splits, w, out, lse, err_flag)
@@ -826,6 +838,34 @@ hipError_t launch_decode_paged_fp8(const void* q, const void* k_codes, const voi
   if (err != hipSuccess || plan.max_splits <= 1) return err;
   return launch_paged_merge(w, B, Hq, plan.chunk, plan.max_splits, seq_lens, seq_offset,
                             block_size, table_cols, max_seq_len, out, lse, stream);
+}
+
+hipError_t launch_decode_paged_fp8(const void* q, const void* k_codes, const void* v_codes,
+                                   const float* k_scale, const float* v_scale,
+                                   const int32_t* block_tables, int table_cols,
+                                   const int32_t* seq_lens, const int32_t* seq_offset, int B,
+                                   int Hq, int Hkv, int num_blocks, int block_size,
+                                   int max_seq_len, float scale, float* out, float* lse,
+                                   void* ws, const SplitPlan& plan, int32_t* err_flag,
+                                   hipStream_t stream) {
+  return launch_paged_lowbit<E4M3Rows>(q, k_codes, v_codes, k_scale, v_scale, block_tables,
+                                       table_cols, seq_lens, seq_offset, B, Hq, Hkv, num_blocks,
+                                       block_size, max_seq_len, scale, out, lse, ws, plan,
+                                       err_flag, stream);
+}
+
+hipError_t launch_decode_paged_fp4(const void* q, const void* k_codes, const void* v_codes,
+                                   const float* k_scale, const float* v_scale,
+                                   const int32_t* block_tables, int table_cols,
+                                   const int32_t* seq_lens, const int32_t* seq_offset, int B,
+                                   int Hq, int Hkv, int num_blocks, int block_size,
+                                   int max_seq_len, float scale, float* out, float* lse,
+                                   void* ws, const SplitPlan& plan, int32_t* err_flag,
+                                   hipStream_t stream) {
+  return launch_paged_lowbit<E2M1Rows>(q, k_codes, v_codes, k_scale, v_scale, block_tables,
+                                       table_cols, seq_lens, seq_offset, B, Hq, Hkv, num_blocks,
+                                       block_size, max_seq_len, scale, out, lse, ws, plan,
+                                       err_flag, stream);
 }
 
 }  // namespace dakv

@@ -80,6 +80,21 @@ hipError_t launch_decode_paged_fp8(const void* q, const void* k_codes, const voi
                                    int max_seq_len, float scale, float* out, float* lse,
                                    void* ws, const SplitPlan& plan, int32_t* err_flag,
                                    hipStream_t stream);
+// FP4 paged pool: packed codes uint8 [num_blocks, block_size, Hkv, D / 2], same scales.
+hipError_t launch_paged_append_fp4(void* k_codes, void* v_codes, float* k_scale,
+                                   float* v_scale, const void* k_new, const void* v_new,
+                                   const int32_t* block_tables, int table_cols,
+                                   const int32_t* seq_lens, const int32_t* seq_offset, int B,
+                                   int Hkv, int D, int num_blocks, int block_size,
+                                   int32_t* err_flag, hipStream_t stream);
+hipError_t launch_decode_paged_fp4(const void* q, const void* k_codes, const void* v_codes,
+                                   const float* k_scale, const float* v_scale,
+                                   const int32_t* block_tables, int table_cols,
+                                   const int32_t* seq_lens, const int32_t* seq_offset, int B,
+                                   int Hq, int Hkv, int num_blocks, int block_size,
+                                   int max_seq_len, float scale, float* out, float* lse,
+                                   void* ws, const SplitPlan& plan, int32_t* err_flag,
+                                   hipStream_t stream);
 
 SplitPlan plan_paged(int B, int Hkv, int G, int max_seq_len, int block_size,
                      int forced_splits);

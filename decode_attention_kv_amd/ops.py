@@ -480,14 +480,13 @@ def decode_attn_paged(q, key_cache, value_cache, block_tables, seq_lens, seq_off
     return out, lse
 
 
-def paged_append_fp8(k_codes, v_codes, k_scale, v_scale, k_new, v_new, block_tables,
-                     seq_lens, seq_offset=None, err_flag=None):
-    """Quantise each sequence's new token (bf16 [B, Hkv, D]) into its last position
-    len_b - 1 of the FP8 pool (codes uint8 [num_blocks, block_size, Hkv, D], scales
-    fp32 [num_blocks, block_size, Hkv]), placed through the block table."""
+def _paged_append_lowbit(fmt, k_codes, v_codes, k_scale, v_scale, k_new, v_new,
+                         block_tables, seq_lens, seq_offset, err_flag):
+    per = 2 if fmt == "fp4" else 1          # values per code byte
     _need(k_codes, "k_codes", torch.uint8)
-    nb, bs, Hkv, D = k_codes.shape
-    _need(v_codes, "v_codes", torch.uint8, (nb, bs, Hkv, D))
+    nb, bs, Hkv, Dc = k_codes.shape
+    D = Dc * per
+    _need(v_codes, "v_codes", torch.uint8, (nb, bs, Hkv, Dc))
     _need(k_scale, "k_scale", torch.float32, (nb, bs, Hkv))
     _need(v_scale, "v_scale", torch.float32, (nb, bs, Hkv))
     _need(k_new, "k_new", torch.bfloat16)
@@ -500,24 +499,41 @@ def paged_append_fp8(k_codes, v_codes, k_scale, v_scale, k_new, v_new, block_tab
     _need(seq_lens, "seq_lens", torch.int32, (B + 1,))
     _opt(seq_offset, "seq_offset", torch.int32, (B,))
     _opt(err_flag, "err_flag", torch.int32, (1,))
-    check("paged_append_fp8", lib().dakv_paged_append_fp8(
+    name = "paged_append_" + fmt
+    check(name, getattr(lib(), "dakv_" + name)(
         _p(k_codes), _p(v_codes), _p(k_scale), _p(v_scale), _p(k_new), _p(v_new),
         _p(block_tables), block_tables.shape[1], _p(seq_lens), _p(seq_offset), B, Hkv, D, nb,
         bs, _p(err_flag), _stream()))
 
 
-def decode_attn_paged_fp8(q, k_codes, v_codes, k_scale, v_scale, block_tables, seq_lens,
-                          seq_offset=None, max_seq_len=None, scale=None, out=None, lse=None,
-                          workspace=None, num_splits=0, err_flag=None, validate=False,
-                          want_lse=True):
-    """decode_attn_paged over the FP8 pool.  Returns ``(out, lse)``."""
+def paged_append_fp8(k_codes, v_codes, k_scale, v_scale, k_new, v_new, block_tables,
+                     seq_lens, seq_offset=None, err_flag=None):
+    """Quantise each sequence's new token (bf16 [B, Hkv, D]) into its last position
+    len_b - 1 of the FP8 pool (codes uint8 [num_blocks, block_size, Hkv, D], scales
+    fp32 [num_blocks, block_size, Hkv]), placed through the block table."""
+    _paged_append_lowbit("fp8", k_codes, v_codes, k_scale, v_scale, k_new, v_new,
+                         block_tables, seq_lens, seq_offset, err_flag)
+
+
+def paged_append_fp4(k_codes, v_codes, k_scale, v_scale, k_new, v_new, block_tables,
+                     seq_lens, seq_offset=None, err_flag=None):
+    """As paged_append_fp8 into the FP4 pool (E2M1 codes two per byte, element 2i in
+    the low four bits: uint8 [num_blocks, block_size, Hkv, D / 2])."""
+    _paged_append_lowbit("fp4", k_codes, v_codes, k_scale, v_scale, k_new, v_new,
+                         block_tables, seq_lens, seq_offset, err_flag)
+
+
+def _decode_attn_paged_lowbit(fmt, q, k_codes, v_codes, k_scale, v_scale, block_tables,
+                              seq_lens, seq_offset, max_seq_len, scale, out, lse, workspace,
+                              num_splits, err_flag, validate, want_lse):
+    per = 2 if fmt == "fp4" else 1          # values per code byte
     _need(q, "q", torch.bfloat16)
     B, Hq, D = q.shape
     _need(k_codes, "k_codes", torch.uint8)
-    nb, bs, Hkv, Dk = k_codes.shape
-    if Dk != D:
+    nb, bs, Hkv, Dc = k_codes.shape
+    if Dc * per != D:
         raise ValueError("the pool's head dim must equal q's")
-    _need(v_codes, "v_codes", torch.uint8, (nb, bs, Hkv, D))
+    _need(v_codes, "v_codes", torch.uint8, (nb, bs, Hkv, Dc))
     _need(k_scale, "k_scale", torch.float32, (nb, bs, Hkv))
     _need(v_scale, "v_scale", torch.float32, (nb, bs, Hkv))
     _need(block_tables, "block_tables", torch.int32)
@@ -542,11 +558,35 @@ def decode_attn_paged_fp8(q, k_codes, v_codes, k_scale, v_scale, block_tables, s
     _opt(err_flag, "err_flag", torch.int32, (1,))
     nbytes = decode_attn_paged_workspace_size(B, Hq, D, int(max_seq_len), bs)
     ws = _workspace(nbytes, q.device, workspace)
-    check("decode_attn_paged_fp8", lib().dakv_decode_attn_paged_fp8(
+    name = "decode_attn_paged_" + fmt
+    check(name, getattr(lib(), "dakv_" + name)(
         _p(q), _p(k_codes), _p(v_codes), _p(k_scale), _p(v_scale), _p(block_tables), cols,
         _p(seq_lens), _p(seq_offset), B, Hq, Hkv, D, nb, bs, int(max_seq_len), float(scale),
         _p(out), _p(lse), _p(ws), ws.numel(), int(num_splits), _p(err_flag), _stream()))
     return out, lse
+
+
+def decode_attn_paged_fp8(q, k_codes, v_codes, k_scale, v_scale, block_tables, seq_lens,
+                          seq_offset=None, max_seq_len=None, scale=None, out=None, lse=None,
+                          workspace=None, num_splits=0, err_flag=None, validate=False,
+                          want_lse=True):
+    """decode_attn_paged over the FP8 pool.  Returns ``(out, lse)``."""
+    return _decode_attn_paged_lowbit("fp8", q, k_codes, v_codes, k_scale, v_scale,
+                                     block_tables, seq_lens, seq_offset, max_seq_len, scale,
+                                     out, lse, workspace, num_splits, err_flag, validate,
+                                     want_lse)
+
+
+def decode_attn_paged_fp4(q, k_codes, v_codes, k_scale, v_scale, block_tables, seq_lens,
+                          seq_offset=None, max_seq_len=None, scale=None, out=None, lse=None,
+                          workspace=None, num_splits=0, err_flag=None, validate=False,
+                          want_lse=True):
+    """decode_attn_paged over the FP4 pool (packed codes uint8 [num_blocks,
+    block_size, Hkv, D / 2]).  Returns ``(out, lse)``."""
+    return _decode_attn_paged_lowbit("fp4", q, k_codes, v_codes, k_scale, v_scale,
+                                     block_tables, seq_lens, seq_offset, max_seq_len, scale,
+                                     out, lse, workspace, num_splits, err_flag, validate,
+                                     want_lse)
 
 
 # ----------------------------------------------------- sparse_topk_decode_attn

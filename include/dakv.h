@@ -360,6 +360,30 @@ int dakv_decode_attn_paged_fp8(const void* q, const void* k_codes, const void* v
                                void* workspace, size_t workspace_bytes, int num_splits,
                                int32_t* err_flag, void* stream);
 
+/*
+ * FP4 paged pool (the FP4 cache above in the paged layout): packed E2M1 codes
+ * uint8 [num_blocks, block_size, Hkv, D / 2] (element 2i in the low four bits)
+ * and the scales of the FP8 pool.
+ *
+ * paged_append_fp4 -- as paged_append_fp8 with E2M1 codes; D a multiple of 16,
+ * up to 256.
+ * decode_attn_paged_fp4 -- as decode_attn_paged_fp8 over the E2M1 codes; same
+ * arguments, workspace and supported shapes.
+ */
+int dakv_paged_append_fp4(void* k_codes, void* v_codes, float* k_scale, float* v_scale,
+                          const void* k_new, const void* v_new, const int32_t* block_tables,
+                          int table_cols, const int32_t* seq_lens, const int32_t* seq_offset,
+                          int B, int Hkv, int D, int num_blocks, int block_size,
+                          int32_t* err_flag, void* stream);
+int dakv_decode_attn_paged_fp4(const void* q, const void* k_codes, const void* v_codes,
+                               const float* k_scale, const float* v_scale,
+                               const int32_t* block_tables, int table_cols,
+                               const int32_t* seq_lens, const int32_t* seq_offset, int B,
+                               int Hq, int Hkv, int D, int num_blocks, int block_size,
+                               int max_seq_len, float scale, float* out, float* lse,
+                               void* workspace, size_t workspace_bytes, int num_splits,
+                               int32_t* err_flag, void* stream);
+
 /* ========================================================================
  * Top-k sparse MLA-style decode   ([FlashMLA] "Mathematical formulation")
  * ======================================================================== */

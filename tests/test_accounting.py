@@ -67,3 +67,10 @@ def test_sparse_fp4_bytes_are_half_a_byte_per_value():
     b8 = acc.sparse_fp8_bytes(16, 128, 576, 512, 2048)
     assert b8 - b4 == 16 * 2048 * 576 // 2
     assert b4 == 16 * 2048 * (288 + 4) + 16 * 128 * 576 * 2 + 16 * 128 * 512 * 4 + 16 * 2048 * 4
+
+
+def test_paged_fp4_bytes_are_half_a_byte_per_value():
+    lengths = [5, 300, 17]
+    b4 = acc.decode_paged_fp4_bytes(lengths, 32, 8, 128, 16)
+    b8 = acc.decode_paged_fp8_bytes(lengths, 32, 8, 128, 16)
+    assert b8 - b4 == sum(lengths) * 8 * 64 * 2
