@@ -408,7 +408,9 @@ size_t dakv_sparse_topk_decode_attn_workspace_size(int B, int Hq, int d_qk, int 
  *            sum of exp(sm_scale * scores))
  *   err_flag optional; an index outside [0, s_kv) is skipped and sets
  *            DAKV_ERR_SPARSE_INDEX
- * Supported: d_qk = 576, d_v = 512, Hq a multiple of 16 up to 128.
+ * Supported: d_qk = 576, d_v = 512, Hq a multiple of 16 up to 128, and s_kv with
+ * s_kv * d_qk * 2 below 2^31 (a sequence's rows are addressed with 32-bit byte
+ * offsets); otherwise DAKV_ENOTSUP.
  */
 int dakv_sparse_topk_decode_attn(const void* q, const void* kv, const int32_t* indices,
                                  int B, int Hq, int s_kv, int d_qk, int d_v, int topk,
