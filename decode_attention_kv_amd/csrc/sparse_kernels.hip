@@ -146,15 +146,43 @@ sparse_split_kernel(const uint16_t* __restrict__ q, const void* __restrict__ kv,
   const int head0 = hg * kHeadsPerWG + hb * kHeadsPerWave;
   const int t0 = split * kSplit;
   const int ntok = min(kSplit, topk - t0);
+  // Q of the workgroup's 32 heads (36 KiB, contiguous in q) is gathered once into
+  // buf1, which is free until tile 1, in the tile layout (head r of the group as
+  // row r, its pieces permuted by piece_slot); every wave then reads its Q^T
+  // operands from there.  (Loading them straight from memory had each Q value
+  // fetched by the 4 waves of a head block and the 4 index splits of a sequence.)
+  // Positions past the 32 heads, and heads past Hq, are filled with zeros.  The
+  // offsets are computed first, this thread's index load is issued next, and the
+  // gather after it, so that waiting for the index does not wait for the gather.
+  constexpr int kQPieces = kHeadsPerWG * kPieces;                         // 2304
+  constexpr int kQLoads = (kQPieces + kSpThreads - 1) / kSpThreads;       // 5 per wave
+  static_assert(kQLoads * kSpThreads * 16 <= kTileBytes, "Q fits one tile buffer");
+  static_assert(kSplit == kSpThreads, "one index per thread");
+  uint32_t qoff[kQLoads];
+#pragma unroll
+  for (int k = 0; k < kQLoads; ++k) {
+    const uint32_t c = (uint32_t)((k * kSpWaves + wave) * 64 + lane);
+    const uint32_t r = c / kPieces;
+    const int p = piece_slot((int)(c - r * kPieces), (int)r);
+    qoff[k] = r < kHeadsPerWG ? (hg * kHeadsPerWG + r) * kRowBytes + (uint32_t)p * 16 : kNoRow;
+    asm volatile("" : "+v"(qoff[k]));  // computed here, before the index load
+  }
+  const int my_idx = tid < ntok ? indices[(size_t)b * topk + t0 + tid] : -1;
   {
-    static_assert(kSplit == kSpThreads, "one index per thread");
+    const __amdgpu_buffer_rsrc_t qr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(q) + (size_t)b * Hq * kDqk, (short)0, Hq * kRowBytes, 0x00020000);
+#pragma unroll
+    for (int k = 0; k < kQLoads; ++k)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          qr, (lds_void*)(buf1 + (k * kSpWaves + wave) * 1024), 16, (int)qoff[k], 0, 0, 0);
+  }
+  {
     uint32_t r = kNoRow;
     float sc = 0.f;
     if (tid < ntok) {
-      const int idx = indices[(size_t)b * topk + t0 + tid];
-      if (idx >= 0 && idx < s_kv) {
-        r = (uint32_t)idx * kSrcRowBytes;
-        if constexpr (kCodes) sc = kv_scale[(size_t)(b / s_q) * s_kv + idx];
+      if (my_idx >= 0 && my_idx < s_kv) {
+        r = (uint32_t)my_idx * kSrcRowBytes;
+        if constexpr (kCodes) sc = kv_scale[(size_t)(b / s_q) * s_kv + my_idx];
       } else {
         raise_flag(err_flag, 4);
       }
@@ -162,7 +190,7 @@ sparse_split_kernel(const uint16_t* __restrict__ q, const void* __restrict__ kv,
     rows[tid] = r;
     if constexpr (kCodes) row_scale[tid] = sc;
   }
-  __syncthreads();
+  lds_barrier();
   // the sequence's latent rows as a buffer (the q-tokens of one sequence, b / s_q,
   // share them): an absent row reads as zeros
   const __amdgpu_buffer_rsrc_t kvr = __builtin_amdgcn_make_buffer_rsrc(
@@ -251,22 +279,24 @@ sparse_split_kernel(const uint16_t* __restrict__ q, const void* __restrict__ kv,
   };
   if constexpr (kCodes) load_codes(0);
   else fetch_tile(0, buf0);
-  // Q^T of the wave's heads as B operands, loaded while tile 0 is in flight:
-  // lane -> head head0 + col16, dims 32 s + 8 grp .. +8 (heads past Hq read as
-  // zeros).
+  // Q^T of the wave's heads as B operands, read from buf1 once its gather is
+  // complete: lane -> head head0 + col16 (row hb * 16 + col16 of buf1), dims
+  // 32 s + 8 grp .. +8.  All reads are done before tile 1's gather refills buf1.
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
   u32x4_t qreg[kKSteps];
   {
-    const __amdgpu_buffer_rsrc_t qr = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t*>(q) + (size_t)b * Hq * kDqk, (short)0, Hq * kRowBytes, 0x00020000);
-    const uint32_t base = (uint32_t)(head0 + col16) * kRowBytes + grp * 16;
+    const int qrow = hb * kHeadsPerWave + col16;
+    const uint8_t* qp = buf1 + qrow * kRowBytes;
+    const int q0 = piece_slot(grp, qrow) * 16, q1 = piece_slot(4 + grp, qrow) * 16;
 #pragma unroll
     for (int s = 0; s < kKSteps; ++s)
-      qreg[s] = __builtin_amdgcn_raw_buffer_load_b128(qr, (int)(base + s * 64), 0, 0);
+      qreg[s] = *reinterpret_cast<const u32x4_t*>(qp + ((s & 1) ? q1 : q0) + 128 * (s >> 1));
   }
-  if constexpr (kCodes) {
-    __builtin_amdgcn_s_waitcnt(kWaitVm0);
-    store_codes(0, buf0);
-  }
+  __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+  if constexpr (kCodes) store_codes(0, buf0);
 
   // O of the wave's 16 heads and its 128 output dims (C layout: lane -> dim
   // 16 j + col16 of dim block 8 rb + j, heads 4 grp + i)
