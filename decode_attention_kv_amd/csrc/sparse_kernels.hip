@@ -98,6 +98,29 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
+// Max and sum over the 4 lane groups (lanes l, l ^ 16, l ^ 32, l ^ 48) with the
+// row-swap instructions, without an LDS round trip: after a swap of x with itself a
+// lane holds {x[l], x[l ^ 16]} (v_permlane16_swap) or {x[l], x[l ^ 32]}
+// (v_permlane32_swap), in an order that does not matter here (checked on the
+// device).
+__device__ __forceinline__ float group4_max(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+__device__ __forceinline__ float group4_sum(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 __device__ __forceinline__ bf16x8_t as_bf16x8(const u32x4_t& v) {
   return __builtin_bit_cast(bf16x8_t, v);
 }
@@ -402,8 +425,7 @@ sparse_split_kernel(const uint16_t* __restrict__ q, const void* __restrict__ kv,
     for (int b4 = 0; b4 < kRowBlocks; ++b4)
 #pragma unroll
       for (int i = 0; i < 4; ++i) tmax = fmaxf(tmax, y[b4][i]);
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+    tmax = group4_max(tmax);
     const float mnew = fmaxf(m_ref, tmax);
     if (__any(mnew > m_ref + kRescale)) {
       const float alpha = mnew == kNegInf ? 1.f : exp2_fast(m_ref - mnew);
@@ -468,8 +490,7 @@ sparse_split_kernel(const uint16_t* __restrict__ q, const void* __restrict__ kv,
 
   // Epilogue.  The sum of exponentials per head (the four waves of a head block
   // hold the same sums and the same running max).
-  lsum += __shfl_xor(lsum, 16);
-  lsum += __shfl_xor(lsum, 32);
+  lsum = group4_sum(lsum);
   float inv[4], lse2[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
