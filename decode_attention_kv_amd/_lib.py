@@ -44,6 +44,8 @@ SIGNATURES = {
                                          _vp, _vp, _vp, _sz, _i, _vp, _vp]),
     "dakv_decode_step_static_fp8": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i,
                                          _i, _i, _i, _f, _vp, _vp, _vp, _sz, _i, _vp, _vp]),
+    "dakv_decode_step_static_fp4": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i,
+                                         _i, _i, _i, _f, _vp, _vp, _vp, _sz, _i, _vp, _vp]),
     "dakv_copy_kvcache": (_i, [_vp, _vp, _i, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp]),
     "dakv_trim_kvcache": (_i, [_vp, _vp, _i, _i, _vp, _vp]),
     "dakv_decode_attn_static_workspace_size": (_sz, [_i, _i, _i, _i]),

@@ -154,6 +154,31 @@ int dakv_decode_step_static_fp8(const float* q, void* k_codes, void* v_codes, fl
                                                  as_stream(stream)));
 }
 
+int dakv_decode_step_static_fp4(const float* q, void* k_codes, void* v_codes, float* k_scale,
+                                float* v_scale, const void* k_new, const void* v_new,
+                                const int32_t* write_pos, int32_t* mask, const int32_t* valid_len,
+                                int B, int H, int cap, int D, float scale, float* out, float* lse,
+                                void* workspace, size_t workspace_bytes, int num_splits,
+                                int32_t* err_flag, void* stream) {
+  if (B < 0 || H < 0 || cap <= 0 || D <= 0 || num_splits < 0) return DAKV_EINVAL;
+  if (B == 0 || H == 0) return DAKV_OK;
+  if (D != 64 && D != 128) return DAKV_ENOTSUP;
+  if (!dakv::static_supported(cap)) return DAKV_ENOTSUP;
+  if (!q || !k_codes || !v_codes || !k_scale || !v_scale || !k_new || !v_new || !write_pos ||
+      !out || !workspace)
+    return DAKV_EINVAL;
+  if (!mask && !valid_len) return DAKV_EINVAL;
+  if (!aligned16(q) || !aligned16(k_codes) || !aligned16(v_codes) || !aligned16(k_new) ||
+      !aligned16(v_new) || !aligned16(out) || !aligned16(workspace))
+    return DAKV_EINVAL;
+  if (workspace_bytes < dakv::static_workspace_bytes(B, H, cap, D)) return DAKV_EINVAL;
+  const dakv::SplitPlan plan = dakv::plan_static(B, H, cap, D, num_splits);
+  return from_hip(dakv::launch_decode_step_static_fp4(q, k_codes, v_codes, k_scale, v_scale,
+                                                      mask, valid_len, k_new, v_new, write_pos,
+                                                      B, H, cap, D, scale, out, lse, workspace,
+                                                      plan, err_flag, as_stream(stream)));
+}
+
 // --------------------------------------------------------------- copy_kvcache
 int dakv_copy_kvcache(const void* const* src, void* const* dst, int n, int B, int H,
                       int src_cap, int dst_cap, int D, const int32_t* lengths, int32_t* mask,

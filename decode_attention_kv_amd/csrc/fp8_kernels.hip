@@ -256,6 +256,14 @@ struct E4M3Rows {                          // one byte per element
     return __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, kLoadNonTemporal);
   }
   __device__ static void unpack(const Word& w, float (&f)[8]) { unpack8_fp8(w, f); }
+  // the scale exponent of a row with largest magnitude amax, and 8 values' codes
+  __device__ static int exponent_for(float amax) { return e4m3_exponent_for(amax); }
+  __device__ static Word quantise8(const float (&x)[8], int e) {
+    Word w = {0u, 0u};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) w[i >> 2] |= e4m3_code(ldexpf(x[i], -e)) << (8 * (i & 3));
+    return w;
+  }
 };
 
 struct E2M1Rows {                          // half a byte per element, element 2i low
@@ -273,14 +281,21 @@ struct E2M1Rows {                          // half a byte per element, element 2
     f[0] = a[0]; f[1] = a[1]; f[2] = b[0]; f[3] = b[1];
     f[4] = c[0]; f[5] = c[1]; f[6] = d[0]; f[7] = d[1];
   }
+  __device__ static int exponent_for(float amax) { return e2m1_exponent_for(amax); }
+  __device__ static Word quantise8(const float (&x)[8], int e) {
+    Word w = 0u;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) w |= e2m1_code(ldexpf(x[i], -e)) << (4 * i);
+    return w;
+  }
 };
 
 //
-// The same pass serves the FP4 cache (Fmt = E2M1Rows, 4-byte loads; no append).
-// With kAppend (decode_step_static_fp8) the split that owns p = write_pos[b]
-// first quantises the new token's K and V rows (as kv_append_fp8 does) in the
-// lanes that later consume row p; they store codes and scales and keep both in
-// registers for that row, and p is attended whatever its mask entry says.
+// The same pass serves the FP4 cache (Fmt = E2M1Rows, 4-byte loads).  With
+// kAppend (decode_step_static_fp8 / _fp4) the split that owns p = write_pos[b]
+// first quantises the new token's K and V rows (as kv_append_fp8 / kv_append_fp4
+// do) in the lanes that later consume row p; they store codes and scales and keep
+// both in registers for that row, and p is attended whatever its mask entry says.
 // Occupancy: at one or two steps the kernel fits 7 waves per SIMD (<= 72 VGPRs);
 // left to itself the append variant takes 73 and drops to 6 (the fused batch-8
 // call measured 32.8 us at 6 waves, 31.4 us at 7).
@@ -301,7 +316,6 @@ static_decode_lowbit_kernel(const float* __restrict__ q, uint8_t* __restrict__ k
   // the rows a wave loads at once (kWaves * RPW per u) tile 64-row words, so a
   // lane group's row never leaves the word (s kStep + u kWaves RPW) / 64
   static_assert(64 % (kWaves * RPW) == 0, "row words");
-  static_assert(!kAppend || Fmt::kRowDiv == 1, "the fused append writes E4M3 codes");
   constexpr int kRowBytes = D / Fmt::kRowDiv;
   typedef typename Fmt::Word Word;
   const int split = blockIdx.x / units;
@@ -335,7 +349,7 @@ static_decode_lowbit_kernel(const float* __restrict__ q, uint8_t* __restrict__ k
   const bool report = split == 0 && h == 0 && threadIdx.x == 0;
   // the appended row's codes and scales, in the lanes that own it
   float new_ks = 0.f, new_vs = 0.f;
-  u32x2_t new_kw = {0u, 0u}, new_vw = {0u, 0u};
+  Word new_kw{}, new_vw{};
   if constexpr (kAppend) {
     if (p < 0 || p >= cap) {
       if (report) raise_flag(err_flag, 2);
@@ -356,16 +370,11 @@ static_decode_lowbit_kernel(const float* __restrict__ q, uint8_t* __restrict__ k
         }
         ka = group_max<LPR>(ka);
         va = group_max<LPR>(va);
-        const int ke = e4m3_exponent_for(ka), ve = e4m3_exponent_for(va);
-        u32x2_t kw = {0u, 0u}, vw = {0u, 0u};
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          kw[i >> 2] |= e4m3_code(ldexpf(kx[i], -ke)) << (8 * (i & 3));
-          vw[i >> 2] |= e4m3_code(ldexpf(vx[i], -ve)) << (8 * (i & 3));
-        }
-        const size_t at = ((size_t)bh * cap + p) * D + (size_t)sub * 8;
-        *reinterpret_cast<u32x2_t*>(k_codes + at) = kw;
-        *reinterpret_cast<u32x2_t*>(v_codes + at) = vw;
+        const int ke = Fmt::exponent_for(ka), ve = Fmt::exponent_for(va);
+        const Word kw = Fmt::quantise8(kx, ke), vw = Fmt::quantise8(vx, ve);
+        const size_t at = (((size_t)bh * cap + p) * D + (size_t)sub * 8) / Fmt::kRowDiv;
+        *reinterpret_cast<Word*>(k_codes + at) = kw;
+        *reinterpret_cast<Word*>(v_codes + at) = vw;
         new_kw = kw;
         new_vw = vw;
         new_ks = ldexpf(1.f, ke);
@@ -497,14 +506,12 @@ static void launch_static_fp8_k(const float* q, void* k_codes, void* v_codes, fl
   auto* vc = static_cast<uint8_t*>(v_codes);
   auto* kn = static_cast<const uint16_t*>(k_new);
   auto* vn = static_cast<const uint16_t*>(v_new);
-  if constexpr (Fmt::kRowDiv == 1) {
-    if (write_pos) {
-      hipLaunchKernelGGL((static_decode_lowbit_kernel<Fmt, D, 4, kSteps, true>), grid,
-                         dim3(kThreads), 0, stream, q, kc, vc, k_scale, v_scale, mask, valid_len,
-                         kn, vn, write_pos, H, cap, scale * kLog2e, plan.chunk, B * H, w, out,
-                         lse, err_flag);
-      return;
-    }
+  if (write_pos) {
+    hipLaunchKernelGGL((static_decode_lowbit_kernel<Fmt, D, 4, kSteps, true>), grid,
+                       dim3(kThreads), 0, stream, q, kc, vc, k_scale, v_scale, mask, valid_len,
+                       kn, vn, write_pos, H, cap, scale * kLog2e, plan.chunk, B * H, w, out,
+                       lse, err_flag);
+    return;
   }
   hipLaunchKernelGGL((static_decode_lowbit_kernel<Fmt, D, 4, kSteps, false>), grid,
                      dim3(kThreads), 0, stream, q, kc, vc, k_scale, v_scale, mask, valid_len, kn,
@@ -567,6 +574,18 @@ hipError_t launch_decode_static_fp4(const float* q, const void* k_codes, const v
       q, const_cast<void*>(k_codes), const_cast<void*>(v_codes), const_cast<float*>(k_scale),
       const_cast<float*>(v_scale), const_cast<int32_t*>(mask), valid_len, nullptr, nullptr,
       nullptr, B, H, cap, D, scale, out, lse, ws, plan, err_flag, stream);
+}
+
+hipError_t launch_decode_step_static_fp4(const float* q, void* k_codes, void* v_codes,
+                                         float* k_scale, float* v_scale, int32_t* mask,
+                                         const int32_t* valid_len, const void* k_new,
+                                         const void* v_new, const int32_t* write_pos, int B,
+                                         int H, int cap, int D, float scale, float* out,
+                                         float* lse, void* ws, const SplitPlan& plan,
+                                         int32_t* err_flag, hipStream_t stream) {
+  return launch_static_lowbit<E2M1Rows>(q, k_codes, v_codes, k_scale, v_scale, mask, valid_len,
+                                        k_new, v_new, write_pos, B, H, cap, D, scale, out, lse,
+                                        ws, plan, err_flag, stream);
 }
 
 // ---------------------------------------------------------------------------

@@ -64,6 +64,14 @@ hipError_t launch_decode_static_fp4(const float* q, const void* k_codes, const v
                                     const int32_t* mask, const int32_t* valid_len, int B, int H,
                                     int cap, int D, float scale, float* out, float* lse, void* ws,
                                     const SplitPlan& plan, int32_t* err_flag, hipStream_t stream);
+// decode_attn_static_fp4 with the quantising append of kv_append_fp4 in the same pass
+hipError_t launch_decode_step_static_fp4(const float* q, void* k_codes, void* v_codes,
+                                         float* k_scale, float* v_scale, int32_t* mask,
+                                         const int32_t* valid_len, const void* k_new,
+                                         const void* v_new, const int32_t* write_pos, int B,
+                                         int H, int cap, int D, float scale, float* out,
+                                         float* lse, void* ws, const SplitPlan& plan,
+                                         int32_t* err_flag, hipStream_t stream);
 // FP8 paged pool: codes uint8 [num_blocks, block_size, Hkv, D], scales fp32
 // [num_blocks, block_size, Hkv]; D = 128, Hkv dividing 16 (the all-heads kernel).
 hipError_t launch_paged_append_fp8(void* k_codes, void* v_codes, float* k_scale,

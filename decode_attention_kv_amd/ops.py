@@ -254,6 +254,43 @@ def decode_step_static_fp8(q, k_codes, v_codes, k_scale, v_scale, k_new, v_new, 
     return out, lse
 
 
+def decode_step_static_fp4(q, k_codes, v_codes, k_scale, v_scale, k_new, v_new, write_pos,
+                           mask=None, valid_len=None, scale=None, out=None, lse=None,
+                           workspace=None, num_splits=0, err_flag=None, want_lse=True):
+    """kv_append_fp4 followed by decode_attn_static_fp4, in one pass (codes uint8
+    [B, H, cap, D / 2]).  Returns ``(out, lse)``."""
+    _need(k_codes, "k_codes", torch.uint8)
+    B, H, cap, half = k_codes.shape
+    D = 2 * half
+    _need(v_codes, "v_codes", torch.uint8, (B, H, cap, half))
+    _need(k_scale, "k_scale", torch.float32, (B, H, cap))
+    _need(v_scale, "v_scale", torch.float32, (B, H, cap))
+    _need(q, "q", torch.float32, (B, H, D))
+    _need(k_new, "k_new", torch.bfloat16, (B, H, D))
+    _need(v_new, "v_new", torch.bfloat16, (B, H, D))
+    _need(write_pos, "write_pos", torch.int32, (B,))
+    _opt(mask, "mask", torch.int32, (B, cap))
+    _opt(valid_len, "valid_len", torch.int32, (B,))
+    if mask is None and valid_len is None:
+        raise ValueError("give a mask, a valid length, or both")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty((B, H, D), dtype=torch.float32, device=q.device)
+    _need(out, "out", torch.float32, (B, H, D))
+    if lse is None and want_lse:
+        lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
+    _opt(lse, "lse", torch.float32, (B, H))
+    _opt(err_flag, "err_flag", torch.int32, (1,))
+    nbytes = int(lib().dakv_decode_attn_static_fp8_workspace_size(B, H, cap, D))
+    ws = _workspace(nbytes, q.device, workspace)
+    check("decode_step_static_fp4", lib().dakv_decode_step_static_fp4(
+        _p(q), _p(k_codes), _p(v_codes), _p(k_scale), _p(v_scale), _p(k_new), _p(v_new),
+        _p(write_pos), _p(mask), _p(valid_len), B, H, cap, D, float(scale), _p(out), _p(lse),
+        _p(ws), ws.numel(), int(num_splits), _p(err_flag), _stream()))
+    return out, lse
+
+
 # ------------------------------------------------------ copy_kvcache / trim
 
 

@@ -324,6 +324,19 @@ int dakv_decode_attn_static_fp4(const float* q, const void* k_codes, const void*
                                 void* stream);
 
 /*
+ * decode_step_static_fp4 -- kv_append_fp4 followed by decode_attn_static_fp4, in
+ * one split pass, as decode_step_static_fp8 is for the FP8 cache (same results as
+ * the two calls).  k_codes, v_codes uint8 [B, H, cap, D / 2]; other arguments as
+ * decode_step_static_fp8.  Supported: D in {64, 128}, cap <= 65536.
+ */
+int dakv_decode_step_static_fp4(const float* q, void* k_codes, void* v_codes, float* k_scale,
+                                float* v_scale, const void* k_new, const void* v_new,
+                                const int32_t* write_pos, int32_t* mask, const int32_t* valid_len,
+                                int B, int H, int cap, int D, float scale, float* out, float* lse,
+                                void* workspace, size_t workspace_bytes, int num_splits,
+                                int32_t* err_flag, void* stream);
+
+/*
  * FP8 paged pool (the FP8 cache above in the paged layout): codes uint8
  * [num_blocks, block_size, Hkv, D] and one fp32 power-of-two scale per (block,
  * slot, KV head) [num_blocks, block_size, Hkv] for K and for V; values decode to

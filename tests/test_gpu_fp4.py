@@ -115,3 +115,82 @@ def test_quantise_on_device_then_attend_full_size_sampled():
         kq, kscale = fp4.quantize_rows(k_new[b])
         assert np.array_equal(codes[0][0, :, pos[b]], kq)
         assert np.array_equal(codes[2][0, :, pos[b]].astype(np.float64), kscale)
+
+
+# ------------------------------------------------ fused append + attend (FP4 cache)
+
+
+def run_step_fp4(q, kc, vc, ks, vs, k_new, v_new, pos, mask, valid_len, **kw):
+    dev = [torch.from_numpy(a).to(DEV) for a in (q, kc, vc, ks, vs)]
+    m = None if mask is None else torch.from_numpy(mask).to(DEV)
+    vl = None if valid_len is None else torch.tensor(valid_len, dtype=torch.int32, device=DEV)
+    out, lse = dakv.decode_step_static_fp4(
+        *dev, bf16_dev(k_new), bf16_dev(v_new), torch.tensor(pos, dtype=torch.int32, device=DEV),
+        mask=m, valid_len=vl, **kw)
+    torch.cuda.synchronize()
+    state = [npy(x) for x in dev[1:]] + [None if m is None else npy(m)]
+    return npy(out), npy(lse), state
+
+
+@pytest.mark.parametrize("D,cap,lengths,pos,use_mask,use_len", [
+    (64, 1152, [5, 103, 1152, 640], [4, 102, 1151, 700], True, True),
+    (128, 700, [1, 64, 65, 700, 300], [0, 63, 64, 699, 500], True, True),
+    (128, 4096, [4096, 1999], [4000, 1998], False, True),
+    (128, 300, [300, 300], [0, 257], True, False),
+])
+def test_decode_step_fp4_matches_append_then_attend(D, cap, lengths, pos, use_mask, use_len):
+    """Fused append + attend over the FP4 cache: the stored codes, scales and mask are
+    bit-exact with the oracle's kv_append_fp4, the output matches decode_static_fp4 on
+    that state (a position at or past the valid length is stored but not attended)."""
+    rng = np.random.default_rng(71 + D + cap)
+    B, H = len(lengths), 3
+    kc = rng.integers(0, 256, size=(B, H, cap, D // 2)).astype(np.uint8)
+    vc = rng.integers(0, 256, size=(B, H, cap, D // 2)).astype(np.uint8)
+    ks, vs = random_scales(rng, (B, H, cap)), random_scales(rng, (B, H, cap))
+    mask = (rng.uniform(size=(B, cap)) < 0.8).astype(np.int32) if use_mask else None
+    if mask is not None:
+        mask[np.arange(B), pos] = 0          # the append must set it
+    k_new = round_to_bf16_bits(rng.standard_normal((B, H, D)) * 3.0)
+    v_new = round_to_bf16_bits(rng.standard_normal((B, H, D)) * 0.5)
+    q = (rng.standard_normal((B, H, D)) * 0.2).astype(np.float32)
+    vl = lengths if use_len else None
+    out, lse, state = run_step_fp4(q, kc, vc, ks, vs, k_new, v_new, pos, mask, vl)
+    want = oracle.kv_append_fp4(kc, vc, ks, vs, k_new, v_new, pos, mask)
+    assert np.array_equal(state[0], want[0]) and np.array_equal(state[1], want[1])
+    assert np.array_equal(state[2].astype(np.float64), want[2])
+    assert np.array_equal(state[3].astype(np.float64), want[3])
+    if mask is not None:
+        assert np.array_equal(state[4], want[4])
+    ref_out, ref_lse = oracle.decode_static_fp4(q, *want[:4], mask=want[4], valid_len=vl)
+    assert_attention_close(out, ref_out)
+    assert_lse_close(lse, ref_lse)
+
+
+def test_decode_step_fp4_equals_the_two_calls_and_flags_bad_position():
+    rng = np.random.default_rng(81)
+    B, H, cap, D = 3, 4, 2048, 128
+    lengths, pos = [2048, 1000, 77], [1500, 999, 5000]
+    kc = rng.integers(0, 256, size=(B, H, cap, D // 2)).astype(np.uint8)
+    vc = rng.integers(0, 256, size=(B, H, cap, D // 2)).astype(np.uint8)
+    ks, vs = random_scales(rng, (B, H, cap)), random_scales(rng, (B, H, cap))
+    k_new = round_to_bf16_bits(rng.standard_normal((B, H, D)))
+    v_new = round_to_bf16_bits(rng.standard_normal((B, H, D)))
+    q = (rng.standard_normal((B, H, D)) * 0.2).astype(np.float32)
+    vl = torch.tensor(lengths, dtype=torch.int32, device=DEV)
+    wp = torch.tensor(pos, dtype=torch.int32, device=DEV)
+    for splits in (0, 1, 13):
+        a = [torch.from_numpy(x).to(DEV) for x in (kc, vc, ks, vs)]
+        b = [x.clone() for x in a]
+        qd = torch.from_numpy(q).to(DEV)
+        fa = torch.zeros(1, dtype=torch.int32, device=DEV)
+        fb = torch.zeros(1, dtype=torch.int32, device=DEV)
+        o1, l1 = dakv.decode_step_static_fp4(qd, *a, bf16_dev(k_new), bf16_dev(v_new), wp,
+                                             valid_len=vl, num_splits=splits, err_flag=fa)
+        dakv.kv_append_fp4(*b, bf16_dev(k_new), bf16_dev(v_new), wp, err_flag=fb)
+        o2, l2 = dakv.decode_attn_static_fp4(qd, *b, valid_len=vl, num_splits=splits)
+        torch.cuda.synchronize()
+        for x, y in zip(a, b):
+            assert torch.equal(x, y)
+        assert torch.equal(o1, o2) and torch.equal(l1, l2)
+        assert int(fa.item()) & dakv._lib.ERR_WRITE_POS
+        assert int(fb.item()) & dakv._lib.ERR_WRITE_POS
