@@ -166,6 +166,73 @@ def test_entry_points_reject_bad_arguments_before_any_launch():
                                           NULL, fake, 1 << 20, NULL, NULL) == _lib.ENOTSUP
 
 
+def test_low_bit_fused_and_sparse_entry_points_reject_bad_arguments():
+    """Host checks of the FP8/FP4, fused-step, latent-append and sparse entry points:
+    each bad argument returns its status before anything is launched."""
+    L = dakv.lib()
+    fake = ctypes.c_void_p(4096)
+    ws = L.dakv_decode_attn_static_workspace_size(1, 4, 1152, 64)
+    # kv_append_fp4: D not a multiple of 16, missing write position
+    assert L.dakv_kv_append_fp4(*([fake] * 7), NULL, 1, 1, 4, 24, NULL, NULL) == _lib.ENOTSUP
+    assert L.dakv_kv_append_fp4(*([fake] * 6), NULL, NULL, 1, 1, 4, 64, NULL, NULL) == _lib.EINVAL
+    # decode_attn_static_fp4: head dim, missing scales, short workspace
+    f4 = lambda D, ksc, wsb: (fake, fake, fake, ksc, fake, fake, NULL, 1, 4, 1152, D, 0.125,
+                              fake, NULL, fake, wsb, 0, NULL, NULL)
+    assert L.dakv_decode_attn_static_fp4(*f4(96, fake, ws)) == _lib.ENOTSUP
+    assert L.dakv_decode_attn_static_fp4(*f4(64, NULL, ws)) == _lib.EINVAL
+    assert L.dakv_decode_attn_static_fp4(*f4(64, fake, ws - 4)) == _lib.EINVAL
+    # fused steps (bf16, FP8, FP4): head dim, missing write position, neither mask nor
+    # valid length, short workspace, capacity past the largest split plan
+    low = lambda D, wp, m, vl, wsb, cap=1152: (fake, fake, fake, fake, fake, fake, fake, wp, m,
+                                               vl, 1, 4, cap, D, 0.125, fake, NULL, fake, wsb, 0,
+                                               NULL, NULL)
+    bf = lambda D, wp, m, vl, wsb, cap=1152: (fake, fake, fake, fake, fake, wp, m, vl, 1, 4, cap,
+                                              D, 0.125, fake, NULL, fake, wsb, 0, NULL, NULL)
+    for fn, args in ((L.dakv_decode_step_static_fp8, low), (L.dakv_decode_step_static_fp4, low),
+                     (L.dakv_decode_step_static, bf)):
+        assert fn(*args(96, fake, fake, NULL, ws)) == _lib.ENOTSUP
+        assert fn(*args(64, NULL, fake, NULL, ws)) == _lib.EINVAL
+        assert fn(*args(64, fake, NULL, NULL, ws)) == _lib.EINVAL
+        assert fn(*args(64, fake, fake, NULL, ws - 4)) == _lib.EINVAL
+        assert fn(*args(64, fake, fake, NULL, ws, 1 << 20)) == _lib.ENOTSUP
+    # paged FP4 append: head dim, no table columns, missing table
+    pa = lambda tab, cols, D: (fake, fake, fake, fake, fake, fake, tab, cols, fake, NULL, 2, 2, D,
+                               10, 16, NULL, NULL)
+    assert L.dakv_paged_append_fp4(*pa(fake, 4, 24)) == _lib.ENOTSUP
+    assert L.dakv_paged_append_fp4(*pa(fake, 0, 128)) == _lib.EINVAL
+    assert L.dakv_paged_append_fp4(*pa(NULL, 4, 128)) == _lib.EINVAL
+    # paged FP4 decode: heads not divisible, head dim, group of 16, block size
+    wsp = L.dakv_decode_attn_paged_workspace_size(2, 64, 128, 100, 16)
+    pd = lambda Hq, Hkv, D, bs: (fake, fake, fake, fake, fake, fake, 4, fake, NULL, 2, Hq, Hkv, D,
+                                 10, bs, 100, 0.1, fake, NULL, fake, wsp, 0, NULL, NULL)
+    assert L.dakv_decode_attn_paged_fp4(*pd(8, 3, 128, 16)) == _lib.EINVAL
+    assert L.dakv_decode_attn_paged_fp4(*pd(8, 2, 64, 16)) == _lib.ENOTSUP
+    assert L.dakv_decode_attn_paged_fp4(*pd(64, 4, 128, 16)) == _lib.ENOTSUP
+    assert L.dakv_decode_attn_paged_fp4(*pd(8, 2, 128, 12)) == _lib.ENOTSUP
+    # latent appends: rows longer than 576, odd FP4 rows, missing scales, empty batch
+    la = lambda sc, d: (fake, sc, fake, fake, 2, 64, d, NULL, NULL)
+    assert L.dakv_latent_append_fp8(*la(fake, 600)) == _lib.ENOTSUP
+    assert L.dakv_latent_append_fp4(*la(fake, 577)) == _lib.ENOTSUP
+    assert L.dakv_latent_append_fp4(*la(NULL, 576)) == _lib.EINVAL
+    assert L.dakv_latent_append_fp8(NULL, NULL, NULL, NULL, 0, 64, 576, NULL, NULL) == _lib.OK
+    # sparse over codes: missing scales, head count, latent width, a cache too long for
+    # 32-bit row offsets, too many (sequence, token) pairs; empty batch is a no-op
+    sp = lambda sc, B, s_q, Hq, s_kv, d_qk: (fake, fake, sc, fake, B, s_q, Hq, s_kv, d_qk, 512,
+                                             64, 0.04, fake, NULL, fake, 1 << 30, NULL, NULL)
+    for fn in (L.dakv_sparse_topk_attn_fp8, L.dakv_sparse_topk_attn_fp4):
+        assert fn(*sp(NULL, 1, 1, 128, 4096, 576)) == _lib.EINVAL
+        assert fn(*sp(fake, 1, 1, 24, 4096, 576)) == _lib.ENOTSUP
+        assert fn(*sp(fake, 1, 1, 128, 4096, 512)) == _lib.ENOTSUP
+        assert fn(*sp(fake, 1, 1, 128, 2_000_000, 576)) == _lib.ENOTSUP
+        assert fn(*sp(fake, 1 << 13, 1 << 12, 128, 4096, 576)) == _lib.EINVAL
+        assert fn(*sp(NULL, 0, 1, 128, 4096, 576)) == _lib.OK
+    # several q-tokens (bf16): no tokens is a no-op, a missing index table is an error
+    st = lambda s_q, idx: (fake, fake, idx, 1, s_q, 128, 4096, 576, 512, 64, 0.04, fake, NULL,
+                           fake, 1 << 30, NULL, NULL)
+    assert L.dakv_sparse_topk_attn(*st(0, NULL)) == _lib.OK
+    assert L.dakv_sparse_topk_attn(*st(2, NULL)) == _lib.EINVAL
+
+
 def test_python_binding_rejects_cpu_tensors():
     import torch
     k = torch.zeros((1, 1, 4, 8), dtype=torch.bfloat16)
