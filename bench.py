@@ -225,7 +225,7 @@ def gather_leg(torch, dakv, workloads, acc, reps=20, counter_pass=False):
             "frac_of_peak": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
 
 
-def fp8_leg(torch, dakv, acc, B=8, steps=10):
+def fp8_leg(torch, dakv, acc, B=8, steps=10, counter_pass=False):
     """The batch-B LLaMA-7B-shaped step over an FP8 cache: 32 layers x
     decode_step_static_fp8 (append + attend in one pass), same lengths as the bf16
     step, captured as a HIP graph; the two-call form (kv_append_fp8 +
@@ -281,6 +281,12 @@ def fp8_leg(torch, dakv, acc, B=8, steps=10):
         del graph
         return ms
 
+    if counter_pass:
+        fused()
+        torch.cuda.synchronize()
+        del layers
+        return (acc.decode_static_fp8_bytes(B, H, D, lengths) +
+                acc.kv_append_fp8_bytes(B, H, D))
     ms = graph_ms(fused)
     ms_two = graph_ms(two_calls)
     step_bytes = n_layers * (acc.decode_static_fp8_bytes(B, H, D, lengths) +
@@ -299,7 +305,7 @@ def fp8_leg(torch, dakv, acc, B=8, steps=10):
             "bf16_equivalent_GBps": round(bf16_bytes / (ms * 1e-3) / 1e9, 1)}
 
 
-def fp4_leg(torch, dakv, acc, B=8, steps=10):
+def fp4_leg(torch, dakv, acc, B=8, steps=10, counter_pass=False):
     """The batch-B LLaMA-7B-shaped step over an FP4 cache: 32 layers x
     decode_step_static_fp4 (append and attend in one pass), same lengths as the bf16
     step, captured as a HIP graph; also timed as kv_append_fp4 + decode_attn_static_fp4.
@@ -354,6 +360,12 @@ def fp4_leg(torch, dakv, acc, B=8, steps=10):
         del graph
         return t
 
+    if counter_pass:
+        run_fused()
+        torch.cuda.synchronize()
+        del layers
+        return (acc.decode_static_fp4_bytes(B, H, D, lengths) +
+                acc.kv_append_fp4_bytes(B, H, D))
     ms = timed(run_fused)
     ms_two = timed(run_two)
     step_bytes = n_layers * (acc.decode_static_fp4_bytes(B, H, D, lengths) +
@@ -485,7 +497,7 @@ def paged_leg(torch, dakv, workloads, acc, counter_pass=False):
             "frac_of_peak": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
 
 
-def paged_lowbit_leg(torch, dakv, workloads, acc, fmt="fp8"):
+def paged_lowbit_leg(torch, dakv, workloads, acc, fmt="fp8", counter_pass=False):
     """The paged GQA config over a low-bit pool (same lengths, table and pool size):
     random finite E4M3 codes (fmt "fp8") or random bytes of two E2M1 codes ("fp4"),
     row scales random powers of two."""
@@ -517,9 +529,13 @@ def paged_lowbit_leg(torch, dakv, workloads, acc, fmt="fp8"):
     call = lambda: fn(case.q, codes[0], codes[1], scales[0], scales[1], t, s, None,
                       max_seq_len=max_len, scale=case.scale, out=out, workspace=ws,
                       want_lse=False)
-    ms = time_cold(torch, call)
     nbytes = (acc.decode_paged_fp4_bytes if fp4 else acc.decode_paged_fp8_bytes)(
         idx.lengths, case.Hq, Hkv, D, bs)
+    if counter_pass:
+        call()
+        torch.cuda.synchronize()
+        return nbytes
+    ms = time_cold(torch, call)
     bf16_bytes = acc.decode_paged_bytes(idx.lengths, case.Hq, Hkv, D, bs)
     del case, codes, scales, out, ws
     name = "an FP4 pool (E2M1 two per byte" if fp4 else "an FP8 pool (E4M3"
@@ -588,7 +604,7 @@ def sparse_tokens_leg(torch, dakv, workloads, acc, s_q=2):
             "frac_of_bf16_mfma_peak": round(flops / (ms * 1e-3) / 2.5e15, 4)}
 
 
-def sparse_lowbit_leg(torch, dakv, workloads, acc, fmt="fp8"):
+def sparse_lowbit_leg(torch, dakv, workloads, acc, fmt="fp8", counter_pass=False):
     """The sparse MLA config over a low-bit latent cache: E4M3 (fmt "fp8") or E2M1 two
     per byte ("fp4") codes with one power-of-two scale per latent row."""
     make = workloads.sparse_fp8_case if fmt == "fp8" else workloads.sparse_fp4_case
@@ -602,8 +618,12 @@ def sparse_lowbit_leg(torch, dakv, workloads, acc, fmt="fp8"):
                      dtype=torch.uint8, device="cuda:0")
     call = lambda: fn(case.q, case.codes, case.scale, case.indices, d_v=case.d_v,
                       sm_scale=case.sm_scale, out=out, workspace=ws, want_lse=False)
-    ms = time_cold(torch, call)
     nbytes = nbytes_of(B, Hq, d_qk, case.d_v, topk)
+    if counter_pass:
+        call()
+        torch.cuda.synchronize()
+        return nbytes
+    ms = time_cold(torch, call)
     flops = acc.sparse_flops(B, Hq, d_qk, case.d_v, topk)
     del case, out, ws
     name = "FP8 (E4M3" if fmt == "fp8" else "FP4 (E2M1, two per byte"
@@ -665,8 +685,8 @@ def cpu_baseline(step, budget_s):
 def counter_pass(torch, dakv, workloads, acc, B, calls=3):
     """Launches for hardware-counter runs: a plain 1 GiB copy first (its FETCH_SIZE
     and WRITE_SIZE give the counters' scale), then `calls` eager fused steps of the
-    batch-B benchmark step and one call of each other leg.  Prints the algorithmic
-    bytes of each launch kind."""
+    batch-B benchmark step and one call (the low-bit steps: one step of 32 calls) of
+    each other leg.  Prints the algorithmic bytes per call of each launch kind."""
     a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda:0")
     b = torch.empty_like(a)
     a.fill_(1)
@@ -688,6 +708,17 @@ def counter_pass(torch, dakv, workloads, acc, B, calls=3):
         info[name + "_call_bytes"] = leg(torch, dakv, workloads, acc, counter_pass=True)
         torch.cuda.empty_cache()
     info["copy_kvcache_call_bytes"] = copy_leg(torch, dakv, acc, counter_pass=True)
+    torch.cuda.empty_cache()
+    info["static_fp8_step_call_bytes"] = fp8_leg(torch, dakv, acc, B, counter_pass=True)
+    torch.cuda.empty_cache()
+    info["static_fp4_step_call_bytes"] = fp4_leg(torch, dakv, acc, B, counter_pass=True)
+    for fmt in ("fp8", "fp4"):
+        torch.cuda.empty_cache()
+        info[f"paged_gqa_{fmt}_call_bytes"] = paged_lowbit_leg(torch, dakv, workloads, acc, fmt,
+                                                               counter_pass=True)
+        torch.cuda.empty_cache()
+        info[f"sparse_mla_{fmt}_call_bytes"] = sparse_lowbit_leg(torch, dakv, workloads, acc,
+                                                                 fmt, counter_pass=True)
     print(json.dumps(info), flush=True)
 
 
