@@ -331,20 +331,20 @@ static_decode_lowbit_kernel(const float* __restrict__ q, uint8_t* __restrict__ k
   const int32_t* mrow = mask ? mask + (size_t)b * cap : nullptr;
   const float* ksrow = k_scale + (size_t)bh * cap;
   const float* vsrow = v_scale + (size_t)bh * cap;
-  // every load before any wait: valid length, query, and per 64-row block of the
-  // split the mask entry and both scales of row r0 + 64 k + lane (clamped)
+  // before any wait: the valid length, the append position, the query and, per
+  // 64-row block of the split, the mask entry of row r0 + 64 k + lane (clamped).
+  // The row scales are first used after the codes arrive, so they go out only
+  // once the split is known to hold rows.
   const int Lraw = valid_len ? valid_len[b] : cap;
   int p = kAppend ? write_pos[b] : -1;
   const float4* qp = reinterpret_cast<const float4*>(q + (size_t)bh * D + sub * 8);
   const float4 qa = qp[0], qc = qp[1];
+  // (loaded under one uniform branch and tested at the ballots: a per-entry select
+  // would make each load wait for the one before it)
   int32_t mv[kBallots];
-  float ksv[kBallots], vsv[kBallots];
+  if (mrow) {
 #pragma unroll
-  for (int k = 0; k < kBallots; ++k) {
-    const int r = min(r0 + 64 * k + lane, cap - 1);
-    mv[k] = mrow ? mrow[r] : 1;
-    ksv[k] = ksrow[r];
-    vsv[k] = vsrow[r];
+    for (int k = 0; k < kBallots; ++k) mv[k] = mrow[min(r0 + 64 * k + lane, cap - 1)];
   }
   const bool report = split == 0 && h == 0 && threadIdx.x == 0;
   // the appended row's codes and scales, in the lanes that own it
@@ -396,6 +396,15 @@ static_decode_lowbit_kernel(const float* __restrict__ q, uint8_t* __restrict__ k
   }
   const int n = L > 0 ? (L + chunk - 1) / chunk : 1;
   if (split >= n) return;
+  // scales of the split's rows (row p's, if this split stores it, is taken from the
+  // quantiser below, not from memory)
+  float ksv[kBallots], vsv[kBallots];
+#pragma unroll
+  for (int k = 0; k < kBallots; ++k) {
+    const int r = min(r0 + 64 * k + lane, cap - 1);
+    ksv[k] = ksrow[r];
+    vsv[k] = vsrow[r];
+  }
   const int r1 = min(r0 + chunk, L);
   float qr[8];
   qr[0] = qa.x * scale_log2; qr[1] = qa.y * scale_log2;
@@ -404,7 +413,8 @@ static_decode_lowbit_kernel(const float* __restrict__ q, uint8_t* __restrict__ k
   qr[6] = qc.z * scale_log2; qr[7] = qc.w * scale_log2;
   uint64_t bits[kBallots];
 #pragma unroll
-  for (int k = 0; k < kBallots; ++k) bits[k] = __ballot(r0 + 64 * k + lane < r1 && mv[k] != 0);
+  for (int k = 0; k < kBallots; ++k)
+    bits[k] = __ballot(r0 + 64 * k + lane < r1 && (!mrow || mv[k] != 0));
   const __amdgpu_buffer_rsrc_t kr_rs = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint8_t*>(k_codes) + (size_t)bh * cap * kRowBytes, (short)0, cap * kRowBytes,
       0x00020000);
