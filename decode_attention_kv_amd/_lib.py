@@ -49,6 +49,7 @@ SIGNATURES = {
     "dakv_copy_kvcache": (_i, [_vp, _vp, _i, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp]),
     "dakv_trim_kvcache": (_i, [_vp, _vp, _i, _i, _vp, _vp]),
     "dakv_decode_attn_static_workspace_size": (_sz, [_i, _i, _i, _i]),
+    "dakv_decode_attn_static_split_rows": (_i, [_i, _i, _i, _i, _i]),
     "dakv_decode_attn_static": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _vp, _vp,
                                      _vp, _sz, _i, _vp, _vp]),
     "dakv_decode_step_static": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _f,

@@ -211,6 +211,12 @@ size_t dakv_decode_attn_static_workspace_size(int B, int H, int cap, int D) {
   return dakv::static_workspace_bytes(B, H, cap, D);
 }
 
+int dakv_decode_attn_static_split_rows(int B, int H, int cap, int D, int num_splits) {
+  if (B <= 0 || H <= 0 || num_splits < 0 || (D != 64 && D != 128)) return 0;
+  if (!dakv::static_supported(cap)) return 0;
+  return dakv::plan_static(B, H, cap, D, num_splits).chunk;
+}
+
 int dakv_decode_attn_static(const float* q, const void* k_cache, const void* v_cache,
                             const int32_t* mask, const int32_t* valid_len, int B, int H,
                             int cap, int D, float scale, float* out, float* lse,

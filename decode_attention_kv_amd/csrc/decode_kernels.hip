@@ -214,7 +214,8 @@ __device__ __forceinline__ void issue_slots(const GlobalRows& rows, int t0, int 
   for (int u = 0; u < U; ++u) {
     const int t = t0 + u * ts;
     ok[u] = t < r1;
-    rows.load(row_at(t, ok[u]), kr[u], vr[u]);
+    const size_t off = row_at(t, ok[u]);
+    rows.load(off, ok[u], kr[u], vr[u]);
   }
 }
 

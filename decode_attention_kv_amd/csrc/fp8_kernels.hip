@@ -256,6 +256,9 @@ struct E4M3Rows {                          // one byte per element
     return __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, kLoadNonTemporal);
   }
   __device__ static void unpack(const Word& w, float (&f)[8]) { unpack8_fp8(w, f); }
+  __device__ static Word select(bool ok, const Word& w) {   // w, or the +0 codes
+    return Word{ok ? w[0] : 0u, ok ? w[1] : 0u};
+  }
   // the scale exponent of a row with largest magnitude amax, and 8 values' codes
   __device__ static int exponent_for(float amax) { return e4m3_exponent_for(amax); }
   __device__ static Word quantise8(const float (&x)[8], int e) {
@@ -281,6 +284,7 @@ struct E2M1Rows {                          // half a byte per element, element 2
     f[0] = a[0]; f[1] = a[1]; f[2] = b[0]; f[3] = b[1];
     f[4] = c[0]; f[5] = c[1]; f[6] = d[0]; f[7] = d[1];
   }
+  __device__ static Word select(bool ok, const Word& w) { return ok ? w : 0u; }
   __device__ static int exponent_for(float amax) { return e2m1_exponent_for(amax); }
   __device__ static Word quantise8(const float (&x)[8], int e) {
     Word w = 0u;
@@ -462,7 +466,10 @@ static_decode_lowbit_kernel(const float* __restrict__ q, uint8_t* __restrict__ k
       const float ksh = __shfl(ksv[word], o_row - 64 * word);
       const float vsh = __shfl(vsv[word], o_row - 64 * word);
       const float ks = fresh[u] ? new_ks : ksh;
-      ws_v[u] = fresh[u] ? new_vs : vsh;
+      // a row that is not attended has zero codes (its load is past the resource)
+      // and gets weight 0; its stored V scale may be anything, an infinity or NaN
+      // included, so the scale it enters O with is 0, not the stored one
+      ws_v[u] = ok[u] ? (fresh[u] ? new_vs : vsh) : 0.f;
       sc[u] = ok[u] ? acc * ks : kNegInf;
     }
     float mnew = m;
@@ -764,9 +771,14 @@ paged_rows_lowbit_kernel(const uint16_t* __restrict__ q, const uint8_t* __restri
       const size_t row = row_at(t, ok[u]);
       const size_t c = row * Hkv * (D / Fmt::kRowDiv) + code_off;
       kw[u] = __builtin_nontemporal_load(reinterpret_cast<const Word*>(k_codes + c));
-      vw[u] = __builtin_nontemporal_load(reinterpret_cast<const Word*>(v_codes + c));
+      const Word v_in = __builtin_nontemporal_load(reinterpret_cast<const Word*>(v_codes + c));
       ksc[u] = k_scale[row * Hkv + h];
-      vsc[u] = v_scale[row * Hkv + h];
+      const float vs_in = v_scale[row * Hkv + h];
+      // an unused row re-reads pool row 0, which may hold NaN codes or scales: its V
+      // codes (0 is the +0 code) and V scale become zeros once they arrive, so it
+      // adds exactly nothing to O; its score is replaced by -inf below
+      vw[u] = Fmt::select(ok[u], v_in);
+      vsc[u] = ok[u] ? vs_in : 0.f;
     }
   };
   HeadState<G> st;

@@ -100,7 +100,9 @@ __device__ __forceinline__ void merge_groups(HeadState<G, E>& st) {
 // Where a loop step's K/V pieces come from.  Both loaders are branch-free: a row
 // that must not be used still issues its load, but the load either touches no
 // memory (buffer load past the end of the resource returns zeros) or re-reads a
-// fixed in-bounds location, and its value is never used.
+// fixed in-bounds location whose V value is then replaced by zeros.  Such a row
+// enters the update with weight 0, and 0 times a NaN or an infinity left in an
+// unused slot of the cache would still be NaN, so its V must be exactly zero.
 //
 // BufferRows: one (sequence, head) region of the static cache; `off` is a byte
 // offset inside it, and kNoRow (past num_records) stands for "no row".
@@ -118,7 +120,8 @@ struct BufferRows {
                                             0x00020000)),
         v(__builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(vbase), (short)0, (int)bytes,
                                             0x00020000)) {}
-  __device__ __forceinline__ void load(uint32_t off, uint4& kr, uint4& vr) const {
+  // (ok is not needed: the "no row" offset already returns zeros)
+  __device__ __forceinline__ void load(uint32_t off, bool, uint4& kr, uint4& vr) const {
     typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
     const u32x4 a = __builtin_amdgcn_raw_buffer_load_b128(k, (int)off, 0, kLoadNonTemporal);
     const u32x4 b = __builtin_amdgcn_raw_buffer_load_b128(v, (int)off, 0, kLoadNonTemporal);
@@ -128,16 +131,18 @@ struct BufferRows {
 };
 
 // GlobalRows: the paged pool through 64-bit addresses; `off` is an element offset
-// from the pool base (0, an in-bounds location, for rows that are not used).
+// from the pool base (0, an in-bounds location, for rows that are not used: their
+// V is zeroed by a select once it arrives; their K only feeds a score that the
+// caller replaces by -inf).
 struct GlobalRows {
   const uint16_t* k;
   const uint16_t* v;
-  __device__ __forceinline__ void load(size_t off, uint4& kr, uint4& vr) const {
+  __device__ __forceinline__ void load(size_t off, bool ok, uint4& kr, uint4& vr) const {
     typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
     const u32x4 a = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(k + off));
     const u32x4 b = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(v + off));
     kr = make_uint4(a[0], a[1], a[2], a[3]);
-    vr = make_uint4(b[0], b[1], b[2], b[3]);
+    vr = make_uint4(ok ? b[0] : 0u, ok ? b[1] : 0u, ok ? b[2] : 0u, ok ? b[3] : 0u);
   }
 };
 
@@ -153,7 +158,8 @@ __device__ __forceinline__ void issue_rows(const Rows& rows, int base, int r1, i
   for (int u = 0; u < U; ++u) {
     const int t = base + (u * kWaves + wave) * RPW + slot;
     ok[u] = t < r1;
-    rows.load(row_at(t, ok[u]), kr[u], vr[u]);
+    const auto off = row_at(t, ok[u]);
+    rows.load(off, ok[u], kr[u], vr[u]);
     patch(t, kr[u], vr[u]);
   }
 }

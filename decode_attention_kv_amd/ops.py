@@ -343,6 +343,11 @@ def decode_attn_static_workspace_size(B, H, cap, D):
     return int(lib().dakv_decode_attn_static_workspace_size(B, H, cap, D))
 
 
+def decode_attn_static_split_rows(B, H, cap, D, num_splits=0):
+    """Rows per split of a static-layout decode call of these sizes (0: unsupported)."""
+    return int(lib().dakv_decode_attn_static_split_rows(B, H, cap, D, num_splits))
+
+
 def _workspace(nbytes, device, workspace):
     """The caller's workspace, or a new one."""
     if workspace is not None:

@@ -182,6 +182,15 @@ int dakv_trim_kvcache(int32_t* mask, const int32_t* new_len, int B, int cap, int
 size_t dakv_decode_attn_static_workspace_size(int B, int H, int cap, int D);
 
 /*
+ * Rows per split that dakv_decode_attn_static, dakv_decode_step_static and their
+ * FP8 / FP4 forms use for these sizes and num_splits (0 = automatic): 64, 128 or
+ * 256.  The split pass of such a call runs chunk / (rows per step) steps, so this
+ * names the kernel instantiation a call reaches.  0 for sizes no kernel serves.
+ * Pure host computation; no device work.
+ */
+int dakv_decode_attn_static_split_rows(int B, int H, int cap, int D, int num_splits);
+
+/*
  * decode_attn_static -- one new query row per (sequence, head) attending over
  * the static buffer.  [NPU-LLM] "Attention on the NPU": decomposed SDPA
  * (Q K^T, times the scale, plus the mask, softmax, times V) and "incremental

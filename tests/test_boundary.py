@@ -238,3 +238,18 @@ def test_python_binding_rejects_cpu_tensors():
     k = torch.zeros((1, 1, 4, 8), dtype=torch.bfloat16)
     with pytest.raises(ValueError, match="GPU"):
         dakv.decode_attn_static(torch.zeros((1, 1, 8)), k, k, valid_len=torch.ones(1, dtype=torch.int32))
+
+
+def test_static_split_rows_query_names_the_instantiation():
+    """Host planning of the static split pass (rows per split) as the kernels use it:
+    a call of the LLaMA-7B-shaped layer at batch 8 takes 128-row splits, at batch 1
+    64-row ones; forced split counts and large capacities take up to 256 rows."""
+    rows = dakv.decode_attn_static_split_rows
+    assert rows(8, 32, 4096, 128) == 128
+    assert rows(1, 32, 4096, 128) == 64
+    assert rows(4, 4, 4096, 128) == 64
+    assert rows(8, 32, 4096, 128, num_splits=32) == 128
+    assert rows(1, 4, 4096, 128, num_splits=1) == 256
+    assert rows(2, 2, 65536, 64) == 256
+    assert rows(1, 1, 65537, 64) == 0
+    assert rows(1, 1, 4096, 96) == 0
