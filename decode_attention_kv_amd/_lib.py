@@ -15,6 +15,8 @@ EINVAL = -1
 ENOTSUP = -2
 ERANGE = -3
 EHIP = -4
+ESCRATCH = -5
+NOALLOC_SCRATCH_BYTES = 16 << 20
 
 ERR_BLOCK_ID = 1
 ERR_WRITE_POS = 2
@@ -50,6 +52,9 @@ SIGNATURES = {
     "dakv_trim_kvcache": (_i, [_vp, _vp, _i, _i, _vp, _vp]),
     "dakv_decode_attn_static_workspace_size": (_sz, [_i, _i, _i, _i]),
     "dakv_decode_attn_static_split_rows": (_i, [_i, _i, _i, _i, _i]),
+    "dakv_decode_attn_static_noalloc_scratch_bytes": (_sz, [_i, _i, _i, _i, _i]),
+    "dakv_decode_attn_static_noalloc": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _vp,
+                                             _vp, _i, _vp, _vp]),
     "dakv_decode_attn_static": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _vp, _vp,
                                      _vp, _sz, _i, _vp, _vp]),
     "dakv_decode_step_static": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _f,

@@ -4,6 +4,8 @@
 
 #include <stdint.h>
 
+#include <mutex>
+
 #include "../../include/dakv.h"
 #include "launch.hpp"
 
@@ -29,6 +31,8 @@ const char* dakv_strerror(int code) {
     case DAKV_ENOTSUP: return "unsupported shape (no kernel built for it)";
     case DAKV_ERANGE: return "index content outside the contract";
     case DAKV_EHIP: return "HIP runtime error at launch";
+    case DAKV_ESCRATCH:
+      return "the call needs more split-partial memory than the library's fixed scratch holds";
     default: return "unknown status";
   }
 }
@@ -237,6 +241,66 @@ int dakv_decode_attn_static(const float* q, const void* k_cache, const void* v_c
       q, const_cast<void*>(k_cache), const_cast<void*>(v_cache), const_cast<int32_t*>(mask),
       valid_len, nullptr, nullptr, nullptr, B, H, cap, D, scale, out, lse, workspace, plan,
       err_flag, as_stream(stream)));
+}
+
+// ---------------------------------- decode_attn_static without any allocation
+// The split partials of dakv_decode_attn_static_noalloc live in this fixed array
+// instead of a caller workspace.  Each GPU the library runs on holds its own copy
+// until the process ends.  In host code `scratch` only names the symbol: its
+// device address on a device comes from hipGetSymbolAddress with that device
+// current, looked up once per device and kept in g_scratch_ptr.
+static __device__ __align__(256) float scratch[DAKV_NOALLOC_SCRATCH_BYTES / sizeof(float)];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+// This device's copy of scratch, or nullptr on a HIP error.
+void* scratch_on_current_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    g_scratch_ptr[dev] = p;
+  }
+  return g_scratch_ptr[dev];
+}
+
+}  // namespace
+
+size_t dakv_decode_attn_static_noalloc_scratch_bytes(int B, int H, int cap, int D,
+                                                     int num_splits) {
+  if (B <= 0 || H <= 0 || num_splits < 0 || (D != 64 && D != 128)) return 0;
+  if (!dakv::static_supported(cap)) return 0;
+  const dakv::SplitPlan plan = dakv::plan_static(B, H, cap, D, num_splits);
+  return dakv::static_plan_workspace_bytes(B, H, D, plan);
+}
+
+int dakv_decode_attn_static_noalloc(const float* q, const void* k_cache, const void* v_cache,
+                                    const int32_t* mask, const int32_t* valid_len, int B, int H,
+                                    int cap, int D, float scale, float* out, float* lse,
+                                    int num_splits, int32_t* err_flag, void* stream) {
+  if (B < 0 || H < 0 || cap <= 0 || D <= 0 || num_splits < 0) return DAKV_EINVAL;
+  if (B == 0 || H == 0) return DAKV_OK;
+  if (D != 64 && D != 128) return DAKV_ENOTSUP;
+  if (!dakv::static_supported(cap)) return DAKV_ENOTSUP;
+  if (!q || !k_cache || !v_cache || !out) return DAKV_EINVAL;
+  if (!mask && !valid_len) return DAKV_EINVAL;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out))
+    return DAKV_EINVAL;
+  const dakv::SplitPlan plan = dakv::plan_static(B, H, cap, D, num_splits);
+  if (dakv::static_plan_workspace_bytes(B, H, D, plan) > DAKV_NOALLOC_SCRATCH_BYTES)
+    return DAKV_ESCRATCH;
+  void* ws = scratch_on_current_device();
+  if (!ws) return DAKV_EHIP;
+  return from_hip(dakv::launch_decode_static(
+      q, const_cast<void*>(k_cache), const_cast<void*>(v_cache), const_cast<int32_t*>(mask),
+      valid_len, nullptr, nullptr, nullptr, B, H, cap, D, scale, out, lse, ws, plan, err_flag,
+      as_stream(stream)));
 }
 
 int dakv_decode_step_static(const float* q, void* k_cache, void* v_cache, const void* k_new,

@@ -387,6 +387,10 @@ size_t static_workspace_bytes(int B, int H, int cap, int D) {
   return ws_floats((size_t)B * H, splits, D) * sizeof(float);
 }
 
+size_t static_plan_workspace_bytes(int B, int H, int D, const SplitPlan& plan) {
+  return plan.max_splits > 1 ? ws_floats((size_t)B * H, plan.max_splits, D) * sizeof(float) : 0;
+}
+
 
 template <int D, int kSteps, bool kAppend>
 static void launch_static_k(const float* q, void* k_cache, void* v_cache, int32_t* mask,

@@ -35,6 +35,8 @@ SplitPlan plan_static(int B, int H, int cap, int D, int forced_splits);
 // Whether a capacity fits the split limits of the static kernel (<= 65536 rows).
 bool static_supported(int cap);
 size_t static_workspace_bytes(int B, int H, int cap, int D);
+// Workspace bytes a call with this plan actually writes (<= static_workspace_bytes).
+size_t static_plan_workspace_bytes(int B, int H, int D, const SplitPlan& plan);
 // write_pos != NULL: append k_new / v_new (bf16 [B, H, D]) first (decode_step_static_fp8)
 hipError_t launch_decode_static_fp8(const float* q, void* k_codes, void* v_codes, float* k_scale,
                                     float* v_scale, int32_t* mask, const int32_t* valid_len,

@@ -391,6 +391,34 @@ def decode_attn_static(q, k_cache, v_cache, mask=None, valid_len=None, scale=Non
     return out, lse
 
 
+def decode_attn_static_noalloc(q, k_cache, v_cache, mask=None, valid_len=None, scale=None,
+                               out=None, lse=None, num_splits=0, err_flag=None, want_lse=True):
+    """decode_attn_static with its split partials in the library's fixed device scratch
+    (no workspace argument; the C call allocates nothing).  Returns ``(out, lse)``.
+    Calls that overlap on one GPU share that scratch and must not run concurrently."""
+    _need(k_cache, "k_cache", torch.bfloat16)
+    B, H, cap, D = k_cache.shape
+    _need(v_cache, "v_cache", torch.bfloat16, (B, H, cap, D))
+    _need(q, "q", torch.float32, (B, H, D))
+    _opt(mask, "mask", torch.int32, (B, cap))
+    _opt(valid_len, "valid_len", torch.int32, (B,))
+    if mask is None and valid_len is None:
+        raise ValueError("give a mask, a valid length, or both")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty((B, H, D), dtype=torch.float32, device=q.device)
+    _need(out, "out", torch.float32, (B, H, D))
+    if lse is None and want_lse:
+        lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
+    _opt(lse, "lse", torch.float32, (B, H))
+    _opt(err_flag, "err_flag", torch.int32, (1,))
+    check("decode_attn_static_noalloc", lib().dakv_decode_attn_static_noalloc(
+        _p(q), _p(k_cache), _p(v_cache), _p(mask), _p(valid_len), B, H, cap, D, float(scale),
+        _p(out), _p(lse), int(num_splits), _p(err_flag), _stream()))
+    return out, lse
+
+
 def decode_step_static(q, k_cache, v_cache, k_new, v_new, write_pos, mask=None, valid_len=None,
                        scale=None, out=None, lse=None, workspace=None, num_splits=0,
                        err_flag=None, want_lse=True):

@@ -40,6 +40,7 @@ extern "C" {
 #define DAKV_ENOTSUP (-2) /* a shape no kernel is built for (head_dim, block size, ...) */
 #define DAKV_ERANGE (-3)  /* a host validator found index content outside the contract */
 #define DAKV_EHIP (-4)    /* the HIP runtime reported an error at launch */
+#define DAKV_ESCRATCH (-5) /* a call needs more than the fixed scratch of the no-alloc entry */
 
 /* ---- device error-flag bits (OR-ed into *err_flag) ---------------------- */
 #define DAKV_ERR_BLOCK_ID 1     /* a used block-table entry is outside [0, num_blocks) */
@@ -241,6 +242,34 @@ int dakv_decode_step_static(const float* q, void* k_cache, void* v_cache, const 
                             const int32_t* valid_len, int B, int H, int cap, int D, float scale,
                             float* out, float* lse, void* workspace, size_t workspace_bytes,
                             int num_splits, int32_t* err_flag, void* stream);
+
+/*
+ * decode_attn_static_noalloc -- dakv_decode_attn_static for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation): the same arguments without the workspace,
+ * the same kernels and the same results bit for bit.  The split partials go to a
+ * fixed device array of DAKV_NOALLOC_SCRATCH_BYTES bytes inside the library (one
+ * per GPU, held from the first call on that GPU until the process ends; its
+ * address is looked up on that first call, with the device current).  The call
+ * itself allocates and frees nothing.
+ *   Limit: a call whose partials exceed the array
+ *   (dakv_decode_attn_static_noalloc_scratch_bytes(...) > DAKV_NOALLOC_SCRATCH_BYTES)
+ *   returns DAKV_ESCRATCH before anything is enqueued.  16 MiB holds every call
+ *   of B * H <= 256 heads at D = 128 and cap <= 4096 (the 7B-shaped layer at
+ *   batch 8).
+ *   Sharing: every call on one GPU uses that GPU's one array, which keeps the
+ *   last call's contents; calls that overlap in time on one GPU (other streams,
+ *   other threads) race on it and must be serialised by the caller.  Nothing in
+ *   it needs to start at zero: each split writes its partial before the merge
+ *   reads it.
+ */
+#define DAKV_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+size_t dakv_decode_attn_static_noalloc_scratch_bytes(int B, int H, int cap, int D,
+                                                     int num_splits);
+int dakv_decode_attn_static_noalloc(const float* q, const void* k_cache, const void* v_cache,
+                                    const int32_t* mask, const int32_t* valid_len, int B, int H,
+                                    int cap, int D, float scale, float* out, float* lse,
+                                    int num_splits, int32_t* err_flag, void* stream);
 
 /* ========================================================================
  * Paged KV cache   ([PyPTO] section 3, tensor contract and gather semantics)

@@ -253,3 +253,22 @@ def test_static_split_rows_query_names_the_instantiation():
     assert rows(2, 2, 65536, 64) == 256
     assert rows(1, 1, 65537, 64) == 0
     assert rows(1, 1, 4096, 96) == 0
+
+
+def test_noalloc_entry_checks_its_scratch_limit_on_the_host():
+    """The allocation-free decode_attn_static form reports the partial bytes a call
+    needs and refuses, before any device work, calls beyond its fixed scratch."""
+    L = dakv.lib()
+    need = L.dakv_decode_attn_static_noalloc_scratch_bytes
+    assert need(8, 32, 4096, 128, 0) == 8 * 32 * 32 * 129 * 4   # 128-row splits
+    assert need(1, 4, 256, 128, 1) == 0                          # one split: no partials
+    assert need(1, 1, 4096, 96, 0) == 0                          # unsupported head_dim
+    fake = ctypes.c_void_p(4096)
+    args = lambda B, H, cap: (fake, fake, fake, NULL, fake, B, H, cap, 128, 0.1, fake, NULL, 0,
+                              NULL, NULL)
+    assert need(64, 32, 4096, 128, 0) > _lib.NOALLOC_SCRATCH_BYTES
+    assert L.dakv_decode_attn_static_noalloc(*args(64, 32, 4096)) == _lib.ESCRATCH
+    assert L.dakv_decode_attn_static_noalloc(*args(0, 32, 4096)) == _lib.OK
+    assert L.dakv_decode_attn_static_noalloc(NULL, fake, fake, NULL, fake, 1, 1, 64, 128, 0.1,
+                                             fake, NULL, 0, NULL, NULL) == _lib.EINVAL
+    assert "scratch" in dakv.strerror(_lib.ESCRATCH)
