@@ -30,6 +30,8 @@ if ROOT not in sys.path:
 
 METRIC = "decode-attn µs/step and achieved HBM GB/s (% of peak); gather GB/s"
 HBM_PEAK_GBS = 8000.0
+REPS = 50      # timed repetitions of every per-call leg and step distribution
+WARM = 5       # untimed repetitions before them (cold caches, first-launch costs)
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "static_decode_step_b8_traffic.md")
@@ -90,9 +92,10 @@ def event_pair(torch):
 class StaticStep:
     """32 layers x (kv_append + decode_attn_static) with preallocated outputs."""
 
-    def __init__(self, B, torch, dakv, workloads, acc, seed=2):
+    def __init__(self, B, torch, dakv, workloads, acc, seed=2, lengths=None):
         self.torch, self.dakv = torch, dakv
-        self.model = workloads.static_llama_layers(B, device="cuda:0", seed=seed)
+        self.model = workloads.static_llama_layers(B, device="cuda:0", seed=seed,
+                                                   lengths=lengths)
         m = self.model
         self.outs = [torch.empty((B, m.H, m.D), dtype=torch.float32, device="cuda:0")
                      for _ in m.layers]
@@ -194,7 +197,80 @@ def time_steps(torch, fn, steps, warmup):
     return s.elapsed_time(e) / steps, wall
 
 
-def gather_leg(torch, dakv, workloads, acc, reps=20, counter_pass=False):
+def step_stats(torch, fn, reps=REPS, warm=WARM):
+    """Duration statistics of individual runs of fn (one HIP event pair each, back to
+    back on the current stream)."""
+    for _ in range(warm):
+        fn()
+    torch.cuda.synchronize()
+    pairs = []
+    for _ in range(reps):
+        a, b = event_pair(torch)
+        a.record()
+        fn()
+        b.record()
+        pairs.append((a, b))
+    torch.cuda.synchronize()
+    return stats_ms([x.elapsed_time(y) for x, y in pairs])
+
+
+def tiny_leg(torch, dakv, workloads, acc):
+    """The tiny static config (batch 1, 4 heads, head_dim 64, capacity 1152, N(0, 10^2)
+    garbage past L): one decode_attn_static call per L, cold last-level cache.  Its
+    bytes are far below what launch latency hides, so it is reported, not graded."""
+    res = {}
+    for L in (4, 5, 103, 1152):
+        case = workloads.static_tiny(L, device="cuda:0")
+        out = torch.empty((1, 4, 64), dtype=torch.float32, device="cuda:0")
+        ws = torch.zeros(dakv.decode_attn_static_workspace_size(1, 4, 1152, 64),
+                         dtype=torch.uint8, device="cuda:0")
+        call = lambda: dakv.decode_attn_static(case.q, case.k_cache, case.v_cache,
+                                               mask=case.mask, valid_len=case.valid_len,
+                                               scale=case.scale, out=out, workspace=ws,
+                                               want_lse=False)
+        st = time_cold(torch, call)
+        nbytes = acc.decode_static_bytes(1, 4, 64, [L], q_elem=acc.FP32, with_mask=True,
+                                         with_lse=False)
+        res[f"L{L}"] = {**us(st), "algorithmic_bytes": nbytes}
+        del case, out, ws
+    return {"workload": "static-buffer decode, tiny: batch 1, 4 heads, head_dim 64, "
+                        "capacity 1152 (1024 + 128), one decode_attn_static call", **res}
+
+
+def batch1_legs(torch, dakv, workloads, acc, seeds=range(11, 19)):
+    """The LLaMA-7B-shaped step at batch 1: the pinned full-context case (L = 4096, the
+    pages' 64 MiB-per-layer / 2 GiB-per-token LLaMA-7B example) and eight drawn lengths
+    (seeds 11..18), each a 32-layer fused step replayed as a HIP graph; the draws are
+    reported bytes-weighted (total bytes / total time)."""
+    def one(lengths=None, seed=12):
+        s1 = StaticStep(1, torch, dakv, workloads, acc, seed=seed, lengths=lengths)
+        g1 = s1.capture(s1.run)
+        st = step_stats(torch, g1.replay)
+        f1, a1, ap1 = s1.per_launch_ms()
+        r = {**us(st, "us_per_step"), "valid_length": s1.model.lengths[0],
+             "algorithmic_bytes_per_step": s1.step_bytes,
+             "GBps": round(s1.step_bytes / (st["median"] * 1e-3) / 1e9, 1),
+             "step_us_per_call": round(f1 * 1e3, 2), "attn_us_per_call": round(a1 * 1e3, 2),
+             "kv_append_us_per_call": round(ap1 * 1e3, 2)}
+        del g1, s1
+        torch.cuda.empty_cache()
+        return r
+    pinned = one(lengths=[4096])
+    draws, tb, tt = [], 0, 0.0
+    for seed in seeds:
+        r = one(seed=seed)
+        draws.append({"seed": seed, "valid_length": r["valid_length"],
+                      "us_per_step": r["us_per_step"], "GBps": r["GBps"]})
+        tb += r["algorithmic_bytes_per_step"]
+        tt += r["us_per_step"] * 1e-6
+    pinned["frac_of_peak"] = round(pinned["GBps"] / HBM_PEAK_GBS, 4)
+    return {"pinned_L4096": pinned,
+            "seeds_11_18": {"draws": draws, "bytes_weighted_GBps": round(tb / tt / 1e9, 1),
+                            "bytes_weighted_frac_of_peak": round(tb / tt / 1e9 / HBM_PEAK_GBS, 4),
+                            "mean_us_per_step": round(tt / len(draws) * 1e6, 1)}}
+
+
+def gather_leg(torch, dakv, workloads, acc, counter_pass=False):
     case = workloads.gather_nd(device="cuda:0", seed=3)
     idx = case.index
     t = torch.from_numpy(idx.block_tables).to("cuda:0")
@@ -213,14 +289,15 @@ def gather_leg(torch, dakv, workloads, acc, reps=20, counter_pass=False):
         return acc.gather_bytes(idx.lengths, 8, 128, 8, 128, 128, with_offset=True)
     # the 247 MB read and 247 MB written fit the 256 MB last-level cache together
     # only in part; flush it between calls so that every call reads from HBM
-    ms = time_cold(torch, call, reps)
-    warm_ms = time_call(torch, call)
+    st = time_cold(torch, call)
+    warm = time_call(torch, call)
+    ms = st["median"]
     nbytes = acc.gather_bytes(idx.lengths, 8, 128, 8, 128, 128, with_offset=True)
     del case, ko, vo
     return {"workload": "gather_pa_kv_cache ND: cache [8192,128,8,128] bf16, 32 sequences "
                         "of U{1..4096} tokens, block_tables [32,64], random offsets",
-            "total_tokens": T, "us_per_call": round(ms * 1e3, 2),
-            "us_per_call_back_to_back": round(warm_ms * 1e3, 2),
+            "total_tokens": T, **us(st),
+            "us_per_call_back_to_back": round(warm["median"] * 1e3, 2),
             "algorithmic_bytes": nbytes, "GBps": round(nbytes / (ms * 1e-3) / 1e9, 1),
             "frac_of_peak": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
 
@@ -277,9 +354,9 @@ def fp8_leg(torch, dakv, acc, B=8, steps=10, counter_pass=False):
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):
             run()
-        ms, _ = time_steps(torch, graph.replay, steps, 3)
+        st = step_stats(torch, graph.replay)
         del graph
-        return ms
+        return st["median"]
 
     if counter_pass:
         fused()
@@ -356,9 +433,9 @@ def fp4_leg(torch, dakv, acc, B=8, steps=10, counter_pass=False):
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):
             run()
-        t, _ = time_steps(torch, graph.replay, steps, 3)
+        st = step_stats(torch, graph.replay)
         del graph
-        return t
+        return st["median"]
 
     if counter_pass:
         run_fused()
@@ -402,11 +479,12 @@ def copy_leg(torch, dakv, acc, counter_pass=False):
         torch.cuda.synchronize()
         del src, dst
         return nbytes
-    ms = time_cold(torch, call, graph=True)
+    st = time_cold(torch, call, graph=True)
+    ms = st["median"]
     del src, dst
     return {"workload": "copy_kvcache: 64 tensors [1, 32, 1024 -> 1152, 128] bf16, 1024 rows "
                         "(512 MiB read, 512 MiB written) + mask",
-            "us_per_call": round(ms * 1e3, 2), "algorithmic_bytes": nbytes,
+            **us(st), "algorithmic_bytes": nbytes,
             "GBps": round(nbytes / (ms * 1e-3) / 1e9, 1),
             "frac_of_peak": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
 
@@ -429,13 +507,29 @@ def as_graph(torch, call):
     return graph
 
 
-def time_cold(torch, call, reps=20, warm=3, graph=False):
-    """Average duration of one call with the last-level cache flushed before each:
+def stats_ms(samples):
+    """median / p10 / p90 / mean of per-rep durations (ms), and the rep count."""
+    import numpy as np
+    a = np.asarray(samples, dtype=np.float64)
+    return {"median": float(np.median(a)), "p10": float(np.percentile(a, 10)),
+            "p90": float(np.percentile(a, 90)), "mean": float(a.mean()), "reps": int(a.size)}
+
+
+def us(st, prefix="us_per_call"):
+    """A stats_ms dict as JSON fields in microseconds (the median is the headline)."""
+    return {prefix: round(st["median"] * 1e3, 2), prefix + "_p10": round(st["p10"] * 1e3, 2),
+            prefix + "_p90": round(st["p90"] * 1e3, 2), prefix + "_mean": round(st["mean"] * 1e3, 2),
+            "reps": st["reps"]}
+
+
+def time_cold(torch, call, reps=REPS, warm=WARM, graph=False):
+    """Duration statistics of one call with the last-level cache flushed before each:
     a 1 GiB buffer is read (summed) in between, which leaves only clean lines of
     that buffer in the cache, so the call neither hits its own data nor pays for
-    writing back someone else's (HIP events on the current stream).  The flush gives
-    the host a head start of its duration to prepare the call; a call whose argument
-    marshalling takes longer (``graph=True``) is timed as a replay of its graph."""
+    writing back someone else's (one HIP event pair per rep on the current stream).
+    The flush gives the host a head start of its duration to prepare the call; a
+    call whose argument marshalling takes longer (``graph=True``) is timed as a
+    replay of its graph."""
     g = as_graph(torch, call) if graph else None
     run = g.replay if graph else call
     flush = torch.zeros(1 << 28, dtype=torch.float32, device="cuda:0")
@@ -451,11 +545,12 @@ def time_cold(torch, call, reps=20, warm=3, graph=False):
             pairs.append((a, b))
     torch.cuda.synchronize()
     del flush, sink, g
-    return sum(x.elapsed_time(y) for x, y in pairs) / len(pairs)
+    return stats_ms([x.elapsed_time(y) for x, y in pairs])
 
 
-def time_call(torch, call, reps=20, warm=3):
-    """Average duration of one call from back-to-back HIP event pairs on the current stream."""
+def time_call(torch, call, reps=REPS, warm=WARM):
+    """Duration statistics of one call from back-to-back HIP event pairs on the
+    current stream (caches warm)."""
     for _ in range(warm):
         call()
     torch.cuda.synchronize()
@@ -467,7 +562,32 @@ def time_call(torch, call, reps=20, warm=3):
         b.record()
         pairs.append((a, b))
     torch.cuda.synchronize()
-    return sum(x.elapsed_time(y) for x, y in pairs) / len(pairs)
+    return stats_ms([x.elapsed_time(y) for x, y in pairs])
+
+
+def ceilings(torch):
+    """What the HBM delivers to plain copies on this device, for context (the bar
+    stays against the 8 TB/s peak): a 1 GiB device-to-device hipMemcpyAsync (bytes
+    read + written per second) and a 1 GiB fp32 sum (torch's reduction kernel; bytes
+    read per second), medians of 20 event-timed runs each."""
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda:0")
+    b = torch.empty_like(a)
+    a.fill_(1)
+    copy = time_call(torch, lambda: b.copy_(a), reps=20, warm=3)
+    del b
+    f = a.view(torch.float32)
+    f.fill_(1.0)
+    sink = torch.zeros((), dtype=torch.float32, device="cuda:0")
+    read = time_call(torch, lambda: torch.sum(f, dim=0, out=sink), reps=20, warm=3)
+    del a, f, sink
+    torch.cuda.empty_cache()
+    props = torch.cuda.get_device_properties(0)
+    return {"d2d_copy_GBps": round(2 * n / (copy["median"] * 1e-3) / 1e9, 1),
+            "read_sum_GBps": round(n / (read["median"] * 1e-3) / 1e9, 1),
+            "device": getattr(props, "name", ""), "arch": getattr(props, "gcnArchName", ""),
+            "compute_units": getattr(props, "multi_processor_count", None),
+            "hbm_bytes": getattr(props, "total_memory", None)}
 
 
 def paged_leg(torch, dakv, workloads, acc, counter_pass=False):
@@ -487,12 +607,13 @@ def paged_leg(torch, dakv, workloads, acc, counter_pass=False):
         call()
         torch.cuda.synchronize()
         return acc.decode_paged_bytes(idx.lengths, case.Hq, case.Hkv, case.D, 16)
-    ms = time_cold(torch, call)
+    st = time_cold(torch, call)
+    ms = st["median"]
     nbytes = acc.decode_paged_bytes(idx.lengths, case.Hq, case.Hkv, case.D, 16)
     del case, out, ws
     return {"workload": "paged GQA decode: batch 64, 32 query / 8 KV heads, head_dim 128, "
                         "block 16, contexts log-uniform [512, 16384]",
-            "total_tokens": int(sum(idx.lengths)), "us_per_call": round(ms * 1e3, 2),
+            "total_tokens": int(sum(idx.lengths)), **us(st),
             "algorithmic_bytes": nbytes, "GBps": round(nbytes / (ms * 1e-3) / 1e9, 1),
             "frac_of_peak": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
 
@@ -535,14 +656,15 @@ def paged_lowbit_leg(torch, dakv, workloads, acc, fmt="fp8", counter_pass=False)
         call()
         torch.cuda.synchronize()
         return nbytes
-    ms = time_cold(torch, call)
+    st = time_cold(torch, call)
+    ms = st["median"]
     bf16_bytes = acc.decode_paged_bytes(idx.lengths, case.Hq, Hkv, D, bs)
     del case, codes, scales, out, ws
     name = "an FP4 pool (E2M1 two per byte" if fp4 else "an FP8 pool (E4M3"
     return {"workload": f"paged GQA decode over {name} + row scale): batch 64, "
                         "32 query / 8 KV heads, head_dim 128, block 16, contexts log-uniform "
                         "[512, 16384]",
-            "us_per_call": round(ms * 1e3, 2), "algorithmic_bytes": nbytes,
+            **us(st), "algorithmic_bytes": nbytes,
             "GBps": round(nbytes / (ms * 1e-3) / 1e9, 1),
             "frac_of_peak": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
             "bf16_equivalent_GBps": round(bf16_bytes / (ms * 1e-3) / 1e9, 1)}
@@ -564,14 +686,15 @@ def sparse_leg(torch, dakv, workloads, acc, counter_pass=False):
         return acc.sparse_bytes(B, Hq, d_qk, case.d_v, topk)
     # the 604 MB cache exceeds the 256 MB last-level cache, but the 44 MB actually
     # touched fits: flush it between calls
-    ms = time_cold(torch, call)
-    warm_ms = time_call(torch, call)
+    st = time_cold(torch, call)
+    warm = time_call(torch, call)
+    ms = st["median"]
     nbytes = acc.sparse_bytes(B, Hq, d_qk, case.d_v, topk)
     flops = acc.sparse_flops(B, Hq, d_qk, case.d_v, topk)
     del case, out, ws
     return {"workload": "top-k sparse MLA decode: batch 16, 128 heads on one latent KV, "
                         "d_qk 576 / d_v 512, context 32768, top-2048",
-            "us_per_call": round(ms * 1e3, 2), "us_per_call_warm_cache": round(warm_ms * 1e3, 2),
+            **us(st), "us_per_call_warm_cache": round(warm["median"] * 1e3, 2),
             "algorithmic_bytes": nbytes, "GBps": round(nbytes / (ms * 1e-3) / 1e9, 1),
             "frac_of_hbm_peak": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
             "TFLOPs": round(flops / (ms * 1e-3) / 1e12, 1),
@@ -592,13 +715,14 @@ def sparse_tokens_leg(torch, dakv, workloads, acc, s_q=2):
     call = lambda: dakv.sparse_topk_attn(case.q, case.kv, case.indices, d_v=case.d_v,
                                          sm_scale=case.sm_scale, out=out, workspace=ws,
                                          want_lse=False)
-    ms = time_cold(torch, call)
+    st = time_cold(torch, call)
+    ms = st["median"]
     nbytes = acc.sparse_bytes(B * s_q, Hq, d_qk, case.d_v, topk)
     flops = acc.sparse_flops(B * s_q, Hq, d_qk, case.d_v, topk)
     del case, out, ws
     return {"workload": f"top-k sparse MLA, {s_q} q-tokens per sequence: batch 16, 128 heads, "
                         f"d_qk 576 / d_v 512, context 32768, top-2048 per token",
-            "us_per_call": round(ms * 1e3, 2), "algorithmic_bytes": nbytes,
+            **us(st), "algorithmic_bytes": nbytes,
             "GBps": round(nbytes / (ms * 1e-3) / 1e9, 1),
             "TFLOPs": round(flops / (ms * 1e-3) / 1e12, 1),
             "frac_of_bf16_mfma_peak": round(flops / (ms * 1e-3) / 2.5e15, 4)}
@@ -623,13 +747,14 @@ def sparse_lowbit_leg(torch, dakv, workloads, acc, fmt="fp8", counter_pass=False
         call()
         torch.cuda.synchronize()
         return nbytes
-    ms = time_cold(torch, call)
+    st = time_cold(torch, call)
+    ms = st["median"]
     flops = acc.sparse_flops(B, Hq, d_qk, case.d_v, topk)
     del case, out, ws
     name = "FP8 (E4M3" if fmt == "fp8" else "FP4 (E2M1, two per byte"
     return {"workload": f"top-k sparse MLA decode over an {name} + row scale) latent cache: "
                         "batch 16, 128 heads, d_qk 576 / d_v 512, context 32768, top-2048",
-            "us_per_call": round(ms * 1e3, 2), "algorithmic_bytes": nbytes,
+            **us(st), "algorithmic_bytes": nbytes,
             "GBps": round(nbytes / (ms * 1e-3) / 1e9, 1),
             "frac_of_hbm_peak": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
             "TFLOPs": round(flops / (ms * 1e-3) / 1e12, 1),
@@ -680,6 +805,70 @@ def cpu_baseline(step, budget_s):
             "kind": "oracle",
             "sample": f"{pairs} (layer, sequence) pairs of the batch-{m.B} step "
                       f"(append + attend, fp64 NumPy), {spent:.1f} s"}
+
+
+def cpu_single_thread(torch, workloads, acc):
+    """The oracle with one BLAS/OpenMP thread on bounded samples of the tiny static
+    config (all four L), the gather (two sequences, their blocks copied out of the
+    pool) and the sparse MLA config (one sequence); GB/s of algorithmic bytes."""
+    import numpy as np
+    import oracle
+    from threadpoolctl import threadpool_limits
+
+    def bits(t):
+        return t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+
+    res = {}
+    with threadpool_limits(limits=1):
+        nbytes, spent = 0, 0.0
+        for L in (4, 5, 103, 1152):
+            case = workloads.static_tiny(L, device="cuda:0")
+            args = (case.q.cpu().numpy(), bits(case.k_cache), bits(case.v_cache),
+                    case.mask.cpu().numpy(), [L], case.scale)
+            t0 = time.perf_counter()
+            oracle.decode_static(*args)
+            spent += time.perf_counter() - t0
+            nbytes += acc.decode_static_bytes(1, 4, 64, [L], q_elem=acc.FP32, with_mask=True,
+                                              with_lse=False)
+        res["static_tiny"] = {"seconds": round(spent, 4), "GBps": round(nbytes / spent / 1e9, 4),
+                              "sample": "one call at each L in {4, 5, 103, 1152}"}
+        g = workloads.gather_nd(device="cuda:0", seed=3)
+        idx = g.index
+        pick = [0, 1]
+        lens = [idx.lengths[q] for q in pick]
+        cols = [-(-L // 128) for L in lens]
+        ids = np.concatenate([idx.block_tables[q, idx.seq_offset[q] // 128:
+                                               idx.seq_offset[q] // 128 + c]
+                              for q, c in zip(pick, cols)])
+        sel = torch.from_numpy(ids.astype(np.int64)).to("cuda:0")
+        kc, vc = bits(g.key_cache.index_select(0, sel)), bits(g.value_cache.index_select(0, sel))
+        del g
+        tables = np.full((len(pick), max(cols)), 0, dtype=np.int32)
+        at = 0
+        for i, c in enumerate(cols):
+            tables[i, :c] = np.arange(at, at + c)
+            at += c
+        seq_lens = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+        t0 = time.perf_counter()
+        oracle.gather_pa_kv_cache(kc, vc, tables, seq_lens, None)
+        spent = time.perf_counter() - t0
+        nbytes = acc.gather_bytes(lens, 8, 128, 8, 128, 128, with_offset=False)
+        res["gather_nd"] = {"seconds": round(spent, 4), "GBps": round(nbytes / spent / 1e9, 4),
+                            "sample": f"2 of 32 sequences ({sum(lens)} tokens)"}
+        sp = workloads.sparse_mla(device="cuda:0", seed=5)
+        q, kv, ind = bits(sp.q[:1]), bits(sp.kv[:1]), sp.indices[:1].cpu().numpy()
+        d_v, sm = sp.d_v, sp.sm_scale
+        del sp
+        t0 = time.perf_counter()
+        oracle.sparse_topk_decode(q, kv, ind, d_v, sm)
+        spent = time.perf_counter() - t0
+        nbytes = acc.sparse_bytes(1, 128, 576, 512, 2048)
+        res["sparse_mla"] = {"seconds": round(spent, 4), "GBps": round(nbytes / spent / 1e9, 4),
+                             "TFLOPs": round(acc.sparse_flops(1, 128, 576, 512, 2048) / spent
+                                             / 1e12, 6),
+                             "sample": "1 of 16 sequences (128 heads, top-2048)"}
+    torch.cuda.empty_cache()
+    return {"threads": 1, **res}
 
 
 def counter_pass(torch, dakv, workloads, acc, B, calls=3):
@@ -744,9 +933,11 @@ def main():
     if args.counter_pass:
         counter_pass(torch, dakv, workloads, acc, B)
         return
+    ceil = ceilings(torch)
     step = StaticStep(B, torch, dakv, workloads, acc)
     graph = step.capture(step.run)
     ms, wall = time_steps(torch, graph.replay, args.steps, args.warmup)
+    dist = step_stats(torch, graph.replay)
     eager_ms, _ = time_steps(torch, step.run, max(3, args.steps // 4), 1)
     g_unf = step.capture(step.run_unfused)
     unfused_ms, _ = time_steps(torch, g_unf.replay, max(5, args.steps // 2), 2)
@@ -767,6 +958,8 @@ def main():
         "us_per_step": round(ms * 1e3, 1),
         "us_per_step_eager_launches": round(eager_ms * 1e3, 1),
         "us_per_step_unfused": round(unfused_ms * 1e3, 1),
+        "step_distribution": {**us(dist, "us_per_step"),
+                              "note": "separately event-timed graph replays"},
         "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
         "higher_is_better": True,
         "scaling": "weak",
@@ -796,25 +989,16 @@ def main():
             "kv_append_us_per_call": round(app_ms * 1e3, 2),
         },
         "wall_s_timed": round(wall, 3),
+        "ceilings": ceil,
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(step, args.cpu_seconds)
     del graph, step
     torch.cuda.empty_cache()
     if not args.no_extras:
-        s1 = StaticStep(1, torch, dakv, workloads, acc, seed=12)
-        g1 = s1.capture(s1.run)
-        ms1, _ = time_steps(torch, g1.replay, max(args.steps, 20), args.warmup)
-        f1, a1, ap1 = s1.per_launch_ms()
-        line["batch1"] = {
-            "us_per_step": round(ms1 * 1e3, 1),
-            "GBps": round(s1.step_bytes / (ms1 * 1e-3) / 1e9, 1),
-            "valid_lengths": s1.model.lengths,
-            "step_us_per_call": round(f1 * 1e3, 2),
-            "attn_us_per_call": round(a1 * 1e3, 2),
-            "kv_append_us_per_call": round(ap1 * 1e3, 2),
-        }
-        del g1, s1
+        line["batch1"] = batch1_legs(torch, dakv, workloads, acc)
+        torch.cuda.empty_cache()
+        line["static_tiny"] = tiny_leg(torch, dakv, workloads, acc)
         torch.cuda.empty_cache()
         line["gather"] = gather_leg(torch, dakv, workloads, acc)
         torch.cuda.empty_cache()
@@ -836,6 +1020,9 @@ def main():
         line["static_fp8"] = fp8_leg(torch, dakv, acc)
         torch.cuda.empty_cache()
         line["static_fp4"] = fp4_leg(torch, dakv, acc)
+        if not args.no_cpu_baseline:
+            torch.cuda.empty_cache()
+            line["cpu_baseline"]["single_thread"] = cpu_single_thread(torch, workloads, acc)
     print(json.dumps(line), flush=True)
 
 
