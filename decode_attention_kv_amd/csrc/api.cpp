@@ -383,6 +383,14 @@ int dakv_decode_attn_paged(const void* q, const void* key_cache, const void* val
     return DAKV_EINVAL;
   if (workspace_bytes < dakv::paged_workspace_bytes(B, Hq, D, max_seq_len, block_size))
     return DAKV_EINVAL;
+  if (dakv::paged_mfma_shape(B, Hq, Hkv, D, block_size)) {
+    const dakv::SplitPlan mplan =
+        dakv::plan_paged_mfma(B, Hkv, max_seq_len, block_size, num_splits);
+    return from_hip(dakv::launch_decode_paged_mfma(
+        q, key_cache, value_cache, block_tables, table_cols, seq_lens, seq_offset, B, Hq, Hkv,
+        num_blocks, block_size, max_seq_len, scale, out, lse, workspace, mplan, err_flag,
+        as_stream(stream)));
+  }
   const dakv::SplitPlan plan = dakv::plan_paged(B, Hkv, G, max_seq_len, block_size, num_splits);
   return from_hip(dakv::launch_decode_paged(q, key_cache, value_cache, block_tables, table_cols,
                                             seq_lens, seq_offset, B, Hq, Hkv, D, num_blocks,

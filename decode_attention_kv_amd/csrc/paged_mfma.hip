@@ -1,0 +1,602 @@
+// Paged GQA decode on the matrix cores, for 2, 4 or a multiple of 8 KV heads.
+//
+// Work split: one workgroup (8 waves) per (sequence, split, group of GH = min(Hkv,
+// 8) KV heads); wave w serves KV head w % GH of the group and 16 GH of the 128
+// output dims (part w / GH) of its G query heads.  The group's GH x 256 bytes of
+// each token row (K, and likewise V) are contiguous in the pool -- a whole token
+// row at Hkv <= 8, read at once, which keeps the HBM accesses of a row together
+// (the same rows split over four workgroups of two heads each streamed at 3 TB/s).
+// The workgroup streams 16-token tiles with coalesced 16-byte non-temporal loads
+// into registers, PmShape::Ahead tiles ahead, and writes each arriving tile into one of
+// two LDS tiles for the matrix cores.  The
+// loads go through a buffer resource that spans exactly the tile's pool block:
+// tokens past the split's end read past the resource and load zeros, and a block
+// id outside the pool gives an empty resource, so no unused slot of the pool is
+// ever read.
+//
+// Per tile and KV head (the grouped-query sharing of one K/V tile by several
+// query heads, NPU article's closing section; online softmax as in its Flash SDPA
+// passage):
+//   * S^T[token, head] = K Q^T with v_mfma_f32_16x16x32_bf16: A = the 16 tokens'
+//     K rows from LDS (lane: token lane % 16, dims 32 s + 8 (lane / 16)), B = Q^T
+//     of the G query heads held in registers (columns G..15 zero), 4 k-steps.
+//   * The C layout of S^T (lane: head lane % 16, tokens 4 (lane / 16) + i) is the
+//     A layout of P for O = P V with v_mfma_f32_16x16x16_bf16, so each lane forms
+//     its P operand from its own scores; P enters as bf16 hi + lo parts.
+//   * V (the B operand: 4 tokens of one dim per lane) comes from LDS with the
+//     transposing read ds_read_b64_tr_b16.
+// LDS rows are 512 bytes; piece p (16 bytes) of token row t is stored at p XOR
+// ((t % 16) << 1), which puts the 32 pieces of each half-wave operand read, and
+// the 64 8-byte pieces of each transposing read, in distinct banks.
+// The grid is persistent: as many workgroups as the device holds at once, each
+// taking every gridDim-th split of the compact list of splits with rows (built in
+// LDS from the lengths), so no workgroup slot is spent on the splits past a
+// sequence's end; the next split's table entries and query are loaded while the
+// current split streams.  Splits end as in the other paged kernels: the output
+// directly (one split) or a partial for merge_kernel.
+#include "split_common.hpp"
+
+namespace dakv {
+
+namespace {
+
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4;
+
+constexpr int kPmTile = 16;                           // tokens per tile
+constexpr int kPmWaves = 8;
+constexpr int kPmThreads = 64 * kPmWaves;
+constexpr uint32_t kPmNoRow = 0x80000000u;            // a buffer offset past any block
+constexpr int kPmMaxSeqs = 512;                       // sequences the split map holds
+constexpr int kPmSplitsTarget = 2048;                 // splits of a call at full lengths
+
+// Tile geometry for a group of GH KV heads: token rows of RB bytes, K then V.
+template <int GH>
+struct PmShape {
+  static constexpr int RB = 256 * GH;                   // a token's K (or V) for the group
+  static constexpr int Half = kPmTile * RB;             // a tile's K (or V)
+  static constexpr int Buf = 2 * Half;
+  static constexpr int HalfLoads = Half / 1024 / kPmWaves;   // wave loads of K (and V)
+  static constexpr int Loads = 2 * HalfLoads;                // per wave and tile
+  static constexpr int Ahead = GH == 8 ? 2 : 4;               // tiles loaded ahead
+  static constexpr int Blocks = 128 / 16 / (kPmWaves / GH);   // dim blocks of a wave
+  static_assert(Half % (1024 * kPmWaves) == 0, "whole wave loads per half tile");
+};
+
+// s_waitcnt immediate waiting until at most n vector memory operations are
+// outstanding (vmcnt in bits 3:0 and 15:14; expcnt and lgkmcnt left at their maximum)
+constexpr int wait_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
+constexpr int kWaitLgkm0Pm = 15 | (7 << 4) | (0 << 8) | (3 << 14);  // lgkmcnt(0) only
+
+__device__ __forceinline__ int pm_slot(int p, int t) { return p ^ ((t & 15) << 1); }
+
+__device__ __forceinline__ float pm_group4_max(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+__device__ __forceinline__ float pm_group4_sum(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+__device__ __forceinline__ short bf16_bits(__bf16 x) { return __builtin_bit_cast(short, x); }
+
+}  // namespace
+
+template <int G, int GH>
+__global__ void __launch_bounds__(kPmThreads)
+paged_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ key_cache,
+                  const uint16_t* __restrict__ value_cache,
+                  const int32_t* __restrict__ block_tables, int table_cols,
+                  const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ seq_offset,
+                  int B, int Hkv, int num_blocks, int block_size, int bs_log2, int max_len,
+                  float scale_log2, int chunk, int max_splits, Workspace ws,
+                  float* __restrict__ out, float* __restrict__ lse, int32_t* err_flag) {
+  constexpr int D = 128;
+  using S = PmShape<GH>;
+  constexpr int NB = S::Blocks;
+  constexpr int A = S::Ahead;
+  constexpr int QB = GH * G * D * 2;             // a split's query: GH x G heads
+  constexpr int QPieces = QB / 16;
+  constexpr int QLoads = (QPieces + kPmThreads - 1) / kPmThreads;
+  static_assert(G >= 1 && G <= 16, "query heads per KV head fit the 16 MFMA columns");
+  __shared__ __attribute__((aligned(1024))) uint8_t tile0[S::Buf];
+  __shared__ __attribute__((aligned(1024))) uint8_t tile1[S::Buf];
+  __shared__ __attribute__((aligned(16))) uint8_t qbuf[2][QB];
+  __shared__ int tbl[2][kMaxTableSpan];
+  __shared__ int pref[kPmMaxSeqs + 1];   // splits (x head groups) before sequence b
+  __shared__ int slen[kPmMaxSeqs];       // effective length of sequence b
+  __shared__ int soff[kPmMaxSeqs];       // its table offset in blocks
+  const int ngroups = Hkv / GH;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int hw = wave % GH;     // KV head of the group this wave computes
+  const int part = wave / GH;   // its part of the 128 output dims (NB blocks of 16)
+  const int grp = lane >> 4;
+  const int col16 = lane & 15;
+  const int Hq = Hkv * G;
+  const int bs_mask = block_size - 1;
+  const uint32_t block_bytes = (uint32_t)block_size * Hkv * D * 2;
+  const size_t block_elems = (size_t)block_size * Hkv * D;
+  const int W = (int)gridDim.x;
+
+  // The splits with rows, numbered sequence-major (then head group, then split):
+  // lengths, table offsets and split counts of every sequence, and their prefix sum.
+  for (int b = threadIdx.x; b < B; b += kPmThreads) {
+    int toff = 0;
+    const int L = paged_len(seq_lens, seq_offset, b, block_size, table_cols, max_len, &toff,
+                            err_flag, blockIdx.x == 0);
+    slen[b] = L;
+    soff[b] = toff;
+    pref[b + 1] = ngroups * (L > 0 ? (L + chunk - 1) / chunk : 1);  // split 0 of an empty
+  }                                                                  // sequence writes zeros
+  __syncthreads();
+  if (wave == 0) {
+    int carry = 0;
+    for (int b0 = 0; b0 < B; b0 += 64) {
+      int v = b0 + lane < B ? pref[b0 + lane + 1] : 0;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int u = __shfl_up(v, off);
+        if (lane >= off) v += u;
+      }
+      if (b0 + lane < B) pref[b0 + lane + 1] = carry + v;
+      carry += __shfl(v, 63);
+    }
+    if (lane == 0) pref[0] = 0;
+  }
+  __syncthreads();
+  const int total = pref[B];
+  if ((int)blockIdx.x >= total) return;
+
+  // One split ("item"): sequence b, head group hg, rows [r0, r1); this workgroup
+  // takes items blockIdx.x, blockIdx.x + W, ...  Each item takes max(A, ntiles)
+  // steps (the extra ones over empty tiles), so the loads run at most one item
+  // ahead of the arithmetic.
+  struct Item {
+    int idx, b, hg, split, n, r0, r1, ntiles, blk0, nblk, steps;
+  };
+  auto item_of = [&](int i) {
+    Item it;
+    it.idx = i;
+    if (i >= total) {  // past the last item: no rows
+      it.b = 0; it.hg = 0; it.split = 0; it.n = 1; it.r0 = 0; it.r1 = 0;
+      it.ntiles = 0; it.blk0 = 0; it.nblk = 0; it.steps = A;
+      return it;
+    }
+    int lo = 0, hi = B - 1;  // the sequence b with pref[b] <= i < pref[b + 1]
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (pref[mid] <= i) lo = mid;
+      else hi = mid - 1;
+    }
+    it.b = lo;
+    const int L = slen[lo];
+    it.n = L > 0 ? (L + chunk - 1) / chunk : 1;
+    const int r = i - pref[lo];
+    it.hg = r / it.n;
+    it.split = r - it.hg * it.n;
+    it.r0 = it.split * chunk;
+    it.r1 = min(it.r0 + chunk, L);
+    it.ntiles = it.r1 > it.r0 ? (it.r1 - it.r0 + kPmTile - 1) / kPmTile : 0;
+    it.blk0 = it.r0 >> bs_log2;
+    it.nblk = it.r1 > it.r0 ? ((it.r1 - 1) >> bs_log2) - it.blk0 + 1 : 0;
+    it.steps = it.ntiles > A ? it.ntiles : A;
+    return it;
+  };
+  int total_steps = 0;
+  for (int i = blockIdx.x; i < total; i += W) total_steps += item_of(i).steps;
+
+  // Per-item metadata travels through registers into LDS: the load side reads an
+  // item's query (and the next item's table entries) when it reaches the item, and
+  // stores them to LDS one step later, after the step's wait has covered them.
+  u32x4_t qstage[QLoads];
+  int tstage = -1;
+  auto meta_load = [&](const Item& it, const Item& nx) {
+    const __amdgpu_buffer_rsrc_t qr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(q) + ((size_t)it.b * Hq + (size_t)GH * it.hg * G) * D,
+        (short)0, it.idx < total ? QB : 0, 0x00020000);
+#pragma unroll
+    for (int k = 0; k < QLoads; ++k) {
+      const int c = (int)threadIdx.x + kPmThreads * k;
+      qstage[k] = __builtin_amdgcn_raw_buffer_load_b128(qr, c < QPieces ? c * 16 : (int)kPmNoRow,
+                                                        0, 0);
+    }
+    tstage = -1;
+    if ((int)threadIdx.x < nx.nblk)
+      tstage = block_tables[(size_t)nx.b * table_cols + soff[nx.b] + nx.blk0 + threadIdx.x];
+  };
+  auto meta_store = [&](int parity_q, int parity_t) {
+#pragma unroll
+    for (int k = 0; k < QLoads; ++k) {
+      const int c = (int)threadIdx.x + kPmThreads * k;
+      if (c < QPieces) *reinterpret_cast<u32x4_t*>(&qbuf[parity_q][c * 16]) = qstage[k];
+    }
+    if ((int)threadIdx.x < kMaxTableSpan) tbl[parity_t][threadIdx.x] = tstage;
+  };
+
+  // The first item's table, synchronously.
+  Item ld = item_of(blockIdx.x);   // the item the loads are in
+  if ((int)threadIdx.x < ld.nblk)
+    tbl[0][threadIdx.x] =
+        block_tables[(size_t)ld.b * table_cols + soff[ld.b] + ld.blk0 + threadIdx.x];
+  __builtin_amdgcn_s_waitcnt(wait_vm(0));
+  __syncthreads();
+  int ld_t = 0, ld_j = 0;          // tile of the item, ordinal of the item (LDS parity)
+  bool meta_pending = false;       // the loaded metadata waits to be stored
+  int mq = 0, mt = 0;              // where it goes
+
+  typedef u32x4_t TileRegs[S::Loads];
+  // Loads of the next tile on the load side: wave load I = HalfLoads wave + k of the
+  // K half (and of the V half) covers bytes [1024 I, 1024 I + 1024) of it; lane L
+  // takes byte 16 L: row (1024 I + 16 L) / RB, piece ((1024 I + 16 L) % RB) / 16.  A
+  // tile past the item's rows gets an empty resource (zeros, no memory traffic), so
+  // every step issues the same tile loads.  Returns the tile's block id (-1: none).
+  auto issue = [&](TileRegs& r) -> int {
+    if (ld_t == 0) {  // a new item: its query, and the next item's table
+      const Item nx = item_of(ld.idx + W);
+      meta_load(ld, nx);
+      meta_pending = true;
+      mq = ld_j & 1;
+      mt = (ld_j + 1) & 1;
+    }
+    int phys = -1;
+    if (ld_t < ld.ntiles) {
+      phys = __builtin_amdgcn_readfirstlane(
+          tbl[ld_j & 1][((ld.r0 + ld_t * kPmTile) >> bs_log2) - ld.blk0]);
+      if (phys < 0 || phys >= num_blocks) {
+        if (threadIdx.x == 0) raise_flag(err_flag, 1);
+        phys = -1;
+      }
+    }
+    const size_t base = phys >= 0 ? (size_t)phys * block_elems : 0;
+    const int records = phys >= 0 ? (int)block_bytes : 0;
+    const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(key_cache) + base, (short)0, records, 0x00020000);
+    const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(value_cache) + base, (short)0, records, 0x00020000);
+    const int tok0 = ld.r0 + ld_t * kPmTile;
+#pragma unroll
+    for (int k = 0; k < S::HalfLoads; ++k) {
+      const int byte = 1024 * (wave * S::HalfLoads + k) + 16 * lane;
+      const int row = byte / S::RB;
+      const int tok = tok0 + row;
+      const uint32_t off =
+          tok < ld.r1 ? (uint32_t)(((tok & bs_mask) * Hkv + GH * ld.hg) * (D * 2) +
+                                   byte % S::RB)
+                      : kPmNoRow;
+      r[k] = __builtin_amdgcn_raw_buffer_load_b128(kr, (int)off, 0, kLoadNonTemporal);
+      r[S::HalfLoads + k] = __builtin_amdgcn_raw_buffer_load_b128(vr, (int)off, 0,
+                                                                  kLoadNonTemporal);
+    }
+    if (++ld_t == ld.steps) {
+      ld = item_of(ld.idx + W);
+      ld_t = 0;
+      ++ld_j;
+    }
+    return phys;
+  };
+  // the arrived registers of a tile into an LDS tile, pieces permuted
+  auto put = [&](const TileRegs& r, uint8_t* dst) {
+#pragma unroll
+    for (int k = 0; k < S::HalfLoads; ++k) {
+      const int byte = 1024 * (wave * S::HalfLoads + k) + 16 * lane;
+      const int row = byte / S::RB;
+      const int at = row * S::RB + pm_slot((byte % S::RB) / 16, row) * 16;
+      *reinterpret_cast<u32x4_t*>(dst + at) = r[k];
+      *reinterpret_cast<u32x4_t*>(dst + S::Half + at) = r[S::HalfLoads + k];
+    }
+  };
+
+  // operand addresses inside a tile: A = row col16, pieces 16 hw + 4 s + grp;
+  // V = row 4 grp + col16 / 4, dims 16 (NB part + jb) + 4 (col16 % 4) .. +3: piece
+  // 16 hw + 2 (NB part + jb) + (col16 % 4) / 2, byte 8 (col16 % 2) of it; the
+  // query operand (B: head col16 of the wave's KV head, dims 32 s + 8 grp) from
+  // the item's query in LDS, zero for col16 >= G
+  const int a_row = col16 * S::RB;
+  int a_off[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) a_off[s] = a_row + pm_slot(16 * hw + 4 * s + grp, col16) * 16;
+  const int v_row_i = 4 * grp + (col16 >> 2);
+  const int v_row = S::Half + v_row_i * S::RB;
+  int v_off[NB];
+#pragma unroll
+  for (int jb = 0; jb < NB; ++jb)
+    v_off[jb] = v_row +
+                pm_slot(16 * hw + 2 * (NB * part + jb) + ((col16 & 3) >> 1), v_row_i) * 16 +
+                (col16 & 1) * 8;
+  const int q_off = ((hw * G + (col16 < G ? col16 : 0)) * D + 8 * grp) * 2;
+
+  // The arithmetic side: the item it works on, its tile, and the running state --
+  // O of the G query heads over this wave's NB dim blocks (C layout: lane -> dim
+  // 16 (NB part + jb) + col16, heads 4 grp + i; rows G..15 stay zero), the running
+  // max (head col16, the same in the four lane groups) and this lane's share of
+  // the sum of exponentials.
+  Item ci = item_of(blockIdx.x);
+  int ct = 0, cj = 0;
+  f32x4_t oacc[NB];
+#pragma unroll
+  for (int jb = 0; jb < NB; ++jb) oacc[jb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float m = kNegInf, lsum = 0.f;
+
+  auto compute = [&](const uint8_t* T, int phys) {
+    const int tok0 = ci.r0 + ct * kPmTile;
+    const bool block_ok = phys >= 0;
+    const uint8_t* qp = qbuf[cj & 1] + q_off;
+    u32x4_t qr[4], a[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      qr[s] = *reinterpret_cast<const u32x4_t*>(qp + 64 * s);
+      if (col16 >= G) qr[s] = u32x4_t{0u, 0u, 0u, 0u};
+      a[s] = *reinterpret_cast<const u32x4_t*>(T + a_off[s]);
+    }
+    i16x4_t vb[NB];
+#pragma unroll
+    for (int jb = 0; jb < NB; ++jb)
+      vb[jb] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(T + v_off[jb]));
+    f32x4_t st0 = f32x4_t{0.f, 0.f, 0.f, 0.f}, st1 = st0;
+    st0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a[0]),
+                                                  __builtin_bit_cast(bf16x8_t, qr[0]), st0, 0,
+                                                  0, 0);
+    st1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a[1]),
+                                                  __builtin_bit_cast(bf16x8_t, qr[1]), st1, 0,
+                                                  0, 0);
+    st0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a[2]),
+                                                  __builtin_bit_cast(bf16x8_t, qr[2]), st0, 0,
+                                                  0, 0);
+    st1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a[3]),
+                                                  __builtin_bit_cast(bf16x8_t, qr[3]), st1, 0,
+                                                  0, 0);
+    float sc[4];
+    float tmax = kNegInf;
+#pragma unroll
+    for (int i2 = 0; i2 < 4; ++i2) {
+      const bool ok = block_ok && tok0 + 4 * grp + i2 < ci.r1;
+      sc[i2] = ok ? (st0[i2] + st1[i2]) * scale_log2 : kNegInf;
+      tmax = fmaxf(tmax, sc[i2]);
+    }
+    tmax = pm_group4_max(tmax);
+    const float mnew = fmaxf(m, tmax);
+    const float ms = mnew == kNegInf ? 0.f : mnew;
+    const float alpha = exp2_fast(m - ms);
+    m = mnew;
+    i16x4_t pa, pl;
+    float psum = 0.f;
+#pragma unroll
+    for (int i2 = 0; i2 < 4; ++i2) {
+      const float p = exp2_fast(sc[i2] - ms);
+      psum += p;
+      const __bf16 hi = (__bf16)p;
+      pa[i2] = bf16_bits(hi);
+      pl[i2] = bf16_bits((__bf16)(p - (float)hi));
+    }
+    lsum = lsum * alpha + psum;
+    float a4[4];
+#pragma unroll
+    for (int i2 = 0; i2 < 4; ++i2) a4[i2] = __shfl(alpha, 4 * grp + i2);
+#pragma unroll
+    for (int jb = 0; jb < NB; ++jb) {
+#pragma unroll
+      for (int i2 = 0; i2 < 4; ++i2) oacc[jb][i2] *= a4[i2];
+      oacc[jb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, vb[jb], oacc[jb], 0, 0, 0);
+      oacc[jb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pl, vb[jb], oacc[jb], 0, 0, 0);
+    }
+  };
+
+  // End of an item: per head (lane col16) the running max and the sum of
+  // exponentials, moved to the lanes that hold the head's row of O; the output
+  // (an item that is its sequence's only split) or the split's partial.
+  auto finish = [&]() {
+    const float lhead = pm_group4_sum(lsum);
+    const size_t head0 = (size_t)ci.b * Hq + (size_t)(GH * ci.hg + hw) * G;
+#pragma unroll
+    for (int i2 = 0; i2 < 4; ++i2) {
+      const int j = 4 * grp + i2;
+      const float M = __shfl(m, j);
+      const float den = __shfl(lhead, j);
+      if (j < G) {
+        const bool any = M != kNegInf;
+        const float inv = any ? 1.f / den : 0.f;
+        const float lse2 = any ? M + __log2f(den) : kNegInf;
+        float* dst = ci.n == 1 ? out + (head0 + j) * D
+                               : ws.o + ((head0 + j) * max_splits + ci.split) * D;
+        dst += 16 * NB * part + col16;
+#pragma unroll
+        for (int jb = 0; jb < NB; ++jb) dst[16 * jb] = oacc[jb][i2] * inv;
+        if (part == 0 && col16 == 0) {
+          if (ci.n == 1) {
+            if (lse) lse[head0 + j] = lse2 * kLn2;
+          } else {
+            ws.lse[(head0 + j) * max_splits + ci.split] = lse2;
+          }
+        }
+      }
+    }
+  };
+
+  // One step s: wait for this wave's loads of tile s (the loads of the A - 1 tiles
+  // issued after it may stay outstanding; anything issued before it is complete
+  // too), store the item metadata loaded one step earlier and write tile s to LDS
+  // tile T, refill the registers with tile s + A; the barrier then makes every
+  // wave's stores visible (one step earlier it ended every wave's reads of T's
+  // previous tile, s - 2); arithmetic on tile s.  Every step issues the same tile
+  // loads (the ones past the last item are empty), so one wait count fits all.
+  constexpr int kUnroll = A % 2 == 0 ? A : 2 * A;
+  TileRegs regs[A];
+  int phys_ring[A];
+#pragma unroll
+  for (int k = 0; k < A; ++k) phys_ring[k] = issue(regs[k]);
+  auto step = [&](int s, TileRegs& r, int& phys_slot, uint8_t* T) {
+    __builtin_amdgcn_s_waitcnt(wait_vm((A - 1) * S::Loads));
+    if (meta_pending) {
+      meta_store(mq, mt);
+      meta_pending = false;
+    }
+    put(r, T);
+    const int phys = phys_slot;
+    phys_slot = issue(r);
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0Pm);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (s < total_steps) {
+      if (ct < ci.ntiles) compute(T, phys);
+      if (++ct == ci.steps) {
+        finish();
+        ci = item_of(ci.idx + W);
+        ct = 0;
+        ++cj;
+#pragma unroll
+        for (int jb = 0; jb < NB; ++jb) oacc[jb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        m = kNegInf;
+        lsum = 0.f;
+      }
+    }
+  };
+  for (int s = 0; s < total_steps; s += kUnroll) {
+#pragma unroll
+    for (int k = 0; k < kUnroll; ++k)
+      step(s + k, regs[k % A], phys_ring[k % A], (k & 1) ? tile1 : tile0);
+  }
+  // the empty tiles' loads are still in flight: let them land
+  __builtin_amdgcn_s_waitcnt(wait_vm(0));
+}
+
+// ------------------------------------------------------------------- planning
+static int round_up_pm(int x, int m) { return (x + m - 1) / m * m; }
+
+bool paged_mfma_shape(int B, int Hq, int Hkv, int D, int block_size) {
+  if (B > kPmMaxSeqs) return false;
+  if (!(Hkv == 2 || Hkv == 4 || Hkv % 8 == 0) || Hq % Hkv != 0 || D != 128) return false;
+  const int G = Hq / Hkv;
+  return (G == 1 || G == 2 || G == 4 || G == 8) && block_size >= kPmTile &&
+         (block_size == 16 || block_size == 32 || block_size == 64 || block_size == 128);
+}
+
+SplitPlan plan_paged_mfma(int B, int Hkv, int max_seq_len, int block_size, int forced_splits) {
+  SplitPlan p;
+  const int unit = block_size > kMinChunk ? block_size : kMinChunk;
+  // one split may touch at most kMaxTableSpan - 2 blocks; the merge takes <= 256
+  const int most = ((kMaxTableSpan - 2) * block_size) / unit * unit;
+  const int least = round_up_pm((max_seq_len + kMaxSplits - 1) / kMaxSplits, unit);
+  int c;
+  if (forced_splits > 0) {
+    c = round_up_pm((max_seq_len + forced_splits - 1) / forced_splits, unit);
+  } else {
+    // about kPmSplitsTarget splits if every sequence had max_seq_len tokens.  Each
+    // split adds a partial output that is written, read back and merged, and the
+    // persistent workgroups take whole splits: 512-token splits (the batch-64,
+    // 16384-token paged config) measured 263 us, 256-token ones 287 us, 128-token
+    // ones 314 us.
+    const int gh = Hkv < 8 ? Hkv : 8;
+    const int groups = Hkv / gh;
+    const long long want = ((long long)B * groups * max_seq_len + kPmSplitsTarget - 1) /
+                           kPmSplitsTarget;
+    c = round_up_pm(want < 1 ? 1 : (int)(want > 1024 ? 1024 : want), unit);
+  }
+  if (c < unit) c = unit;
+  if (c > most) c = most;
+  if (c < least) c = least;
+  p.chunk = c;
+  p.max_splits = max_seq_len > 0 ? (max_seq_len + c - 1) / c : 1;
+  return p;
+}
+
+// Workgroups of a persistent launch: as many as the device keeps resident at once
+// (occupancy per CU times the CU count, both queried once per device and kernel).
+template <int G, int GH>
+static int resident_workgroups() {
+  constexpr int kMaxDev = 64;
+  static int cached[kMaxDev];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) return 0;
+  if (cached[dev] > 0) return cached[dev];
+  int cus = 0, per_cu = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, paged_mfma_kernel<G, GH>,
+                                                   kPmThreads, 0) != hipSuccess)
+    return 0;
+  const int n = cus * (per_cu > 0 ? per_cu : 1);
+  cached[dev] = n;  // the same value whichever thread stores it
+  return n;
+}
+
+template <int G, int GH>
+static hipError_t launch_pm(const uint16_t* qb, const uint16_t* kc, const uint16_t* vc,
+                            const int32_t* block_tables, int table_cols,
+                            const int32_t* seq_lens, const int32_t* seq_offset, int B, int Hkv,
+                            int num_blocks, int block_size, int bs_log2, int max_seq_len,
+                            float scale, const SplitPlan& plan, const Workspace& w, float* out,
+                            float* lse, int32_t* err_flag, hipStream_t stream) {
+  const int resident = resident_workgroups<G, GH>();
+  if (resident <= 0) return hipErrorInvalidValue;
+  const long long items = (long long)B * (Hkv / GH) * plan.max_splits;  // at most
+  const unsigned grid = (unsigned)(items < resident ? items : resident);
+  hipLaunchKernelGGL((paged_mfma_kernel<G, GH>), dim3(grid), dim3(kPmThreads), 0, stream, qb,
+                     kc, vc, block_tables, table_cols, seq_lens, seq_offset, B, Hkv,
+                     num_blocks, block_size, bs_log2, max_seq_len, scale * kLog2e, plan.chunk,
+                     plan.max_splits, w, out, lse, err_flag);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_paged_mfma(const void* q, const void* key_cache,
+                                    const void* value_cache, const int32_t* block_tables,
+                                    int table_cols, const int32_t* seq_lens,
+                                    const int32_t* seq_offset, int B, int Hq, int Hkv,
+                                    int num_blocks, int block_size, int max_seq_len,
+                                    float scale, float* out, float* lse, void* ws,
+                                    const SplitPlan& plan, int32_t* err_flag,
+                                    hipStream_t stream) {
+  const Workspace w = carve(ws, (size_t)B * Hq, plan.max_splits, 128);
+  int bs_log2 = 0;
+  while ((1 << bs_log2) < block_size) ++bs_log2;
+  const auto* qb = static_cast<const uint16_t*>(q);
+  const auto* kc = static_cast<const uint16_t*>(key_cache);
+  const auto* vc = static_cast<const uint16_t*>(value_cache);
+  // KV heads per workgroup: up to 8 (whole token rows at Hkv = 8); 4 at G = 8, whose
+  // query buffers would not fit the LDS next to 8-head tiles
+  const int gh_max = Hq / Hkv == 8 ? 4 : 8;
+  const int GH = Hkv < gh_max ? Hkv : gh_max;
+  hipError_t err = hipErrorInvalidValue;
+#define DAKV_PM(GG, HH)                                                                      \
+  err = launch_pm<GG, HH>(qb, kc, vc, block_tables, table_cols, seq_lens, seq_offset, B, Hkv, \
+                          num_blocks, block_size, bs_log2, max_seq_len, scale, plan, w, out, \
+                          lse, err_flag, stream)
+#define DAKV_PM_H(GG)                  \
+  switch (GH) {                        \
+    case 2: DAKV_PM(GG, 2); break;     \
+    case 4: DAKV_PM(GG, 4); break;     \
+    default: DAKV_PM(GG, 8); break;    \
+  }
+  switch (Hq / Hkv) {
+    case 1: DAKV_PM_H(1); break;
+    case 2: DAKV_PM_H(2); break;
+    case 4: DAKV_PM_H(4); break;
+    case 8:
+      if (GH == 2) DAKV_PM(8, 2);
+      else DAKV_PM(8, 4);
+      break;
+    default: return hipErrorInvalidValue;
+  }
+#undef DAKV_PM_H
+#undef DAKV_PM
+  if (err != hipSuccess || plan.max_splits <= 1) return err;
+  return launch_paged_merge(w, B, Hq, plan.chunk, plan.max_splits, seq_lens, seq_offset,
+                            block_size, table_cols, max_seq_len, out, lse, stream);
+}
+
+}  // namespace dakv
