@@ -449,6 +449,14 @@ static int decode_paged_lowbit(bool fp4, const void* q, const void* k_codes,
     return DAKV_EINVAL;
   if (workspace_bytes < dakv::paged_workspace_bytes(B, Hq, D, max_seq_len, block_size))
     return DAKV_EINVAL;
+  if (dakv::paged_mfma_shape(B, Hq, Hkv, D, block_size)) {
+    const dakv::SplitPlan mplan =
+        dakv::plan_paged_mfma(B, Hkv, max_seq_len, block_size, num_splits);
+    return from_hip(dakv::launch_decode_paged_mfma_lowbit(
+        fp4, q, k_codes, v_codes, k_scale, v_scale, block_tables, table_cols, seq_lens,
+        seq_offset, B, Hq, Hkv, num_blocks, block_size, max_seq_len, scale, out, lse, workspace,
+        mplan, err_flag, as_stream(stream)));
+  }
   const dakv::SplitPlan plan =
       dakv::plan_paged(B, Hkv, Hq / Hkv, max_seq_len, block_size, num_splits);
   const auto launch = fp4 ? dakv::launch_decode_paged_fp4 : dakv::launch_decode_paged_fp8;

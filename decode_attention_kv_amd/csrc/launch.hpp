@@ -109,7 +109,9 @@ hipError_t launch_decode_paged_fp4(const void* q, const void* k_codes, const voi
 SplitPlan plan_paged(int B, int Hkv, int G, int max_seq_len, int block_size,
                      int forced_splits);
 // Paged decode on the matrix cores (paged_mfma.hip): Hkv in {2, 4, 8k}, G in {1, 2, 4,
-// 8}, D = 128, block_size in {16, 32, 64, 128}, B <= 1024; its own split plan.
+// 8}, D = 128, block_size in {16, 32, 64, 128}, B <= 512; its own split plan.  The
+// same kernel serves the bf16 pool and the FP8 / FP4 pools (codes dequantised with
+// their row scales on the way into LDS).
 bool paged_mfma_shape(int B, int Hq, int Hkv, int D, int block_size);
 SplitPlan plan_paged_mfma(int B, int Hkv, int max_seq_len, int block_size, int forced_splits);
 hipError_t launch_decode_paged_mfma(const void* q, const void* key_cache,
@@ -120,6 +122,15 @@ hipError_t launch_decode_paged_mfma(const void* q, const void* key_cache,
                                     float scale, float* out, float* lse, void* ws,
                                     const SplitPlan& plan, int32_t* err_flag,
                                     hipStream_t stream);
+hipError_t launch_decode_paged_mfma_lowbit(bool fp4, const void* q, const void* k_codes,
+                                           const void* v_codes, const float* k_scale,
+                                           const float* v_scale, const int32_t* block_tables,
+                                           int table_cols, const int32_t* seq_lens,
+                                           const int32_t* seq_offset, int B, int Hq, int Hkv,
+                                           int num_blocks, int block_size, int max_seq_len,
+                                           float scale, float* out, float* lse, void* ws,
+                                           const SplitPlan& plan, int32_t* err_flag,
+                                           hipStream_t stream);
 // Whether a sequence of max_seq_len tokens fits the split limits of the paged kernel.
 bool paged_supported(int max_seq_len, int block_size);
 size_t paged_workspace_bytes(int B, int Hq, int D, int max_seq_len, int block_size);

@@ -53,19 +53,76 @@ constexpr int kPmThreads = 64 * kPmWaves;
 constexpr uint32_t kPmNoRow = 0x80000000u;            // a buffer offset past any block
 constexpr int kPmMaxSeqs = 512;                       // sequences the split map holds
 constexpr int kPmSplitsTarget = 2048;                 // splits of a call at full lengths
+// The running max of a head moves only when a tile raises it by more than this
+// (log2 units): the skip-scale of the FlashMLA article, so that most tiles neither
+// rescale the output nor move the reference of the exponentials (which stay below
+// 2^kPmRescale).
+constexpr float kPmRescale = 8.0f;
 
-// Tile geometry for a group of GH KV heads: token rows of RB bytes, K then V.
-template <int GH>
+// Tile geometry for a group of GH KV heads over a pool of Bits-bit elements (16:
+// bf16; 8: E4M3 codes; 4: E2M1 codes, two per byte, each with a per-row scale).
+// In LDS a tile is always bf16: token rows of RB bytes, K then V.  In the pool a
+// token's row for the group is CRB bytes, a tile's K (or V) CH bytes, read by lane
+// loads of LW bytes.
+template <int GH, int Bits>
 struct PmShape {
+  static constexpr bool Coded = Bits < 16;
   static constexpr int RB = 256 * GH;                   // a token's K (or V) for the group
   static constexpr int Half = kPmTile * RB;             // a tile's K (or V)
   static constexpr int Buf = 2 * Half;
-  static constexpr int HalfLoads = Half / 1024 / kPmWaves;   // wave loads of K (and V)
-  static constexpr int Loads = 2 * HalfLoads;                // per wave and tile
-  static constexpr int Ahead = GH == 8 ? 2 : 4;               // tiles loaded ahead
+  static constexpr int CB = 128 * Bits / 8;             // pool bytes of one head's row
+  static constexpr int CRB = GH * CB;
+  static constexpr int CH = kPmTile * CRB;
+  static constexpr int LW = CH / 512 >= 16 ? 16 : CH / 512;
+  static constexpr int HalfLoads = CH / (512 * LW);     // lane loads of K (and V) codes
+  static constexpr int Elems = LW * 8 / Bits;           // elements of one lane load
+  static constexpr int Loads = 2 * HalfLoads * (Coded ? 2 : 1);  // per wave and tile
+  static constexpr int Ahead =                                  // tiles loaded ahead
+      Coded ? (GH == 8 ? (Bits == 8 ? 3 : 6) : 4) : (GH == 8 ? 2 : 4);
   static constexpr int Blocks = 128 / 16 / (kPmWaves / GH);   // dim blocks of a wave
-  static_assert(Half % (1024 * kPmWaves) == 0, "whole wave loads per half tile");
+  static_assert(LW >= 4 && CH % (512 * LW) == 0, "whole lane loads per half tile");
+  static_assert(CB % LW == 0, "a lane load stays inside one head's row");
 };
+
+typedef uint32_t pm_u32x2_t __attribute__((ext_vector_type(2)));
+
+// one lane load of LW bytes (LW = 4, 8 or 16) into the low words of a u32x4
+template <int LW>
+__device__ __forceinline__ u32x4_t pm_load(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  if constexpr (LW == 16) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, kLoadNonTemporal);
+  } else if constexpr (LW == 8) {
+    const pm_u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, kLoadNonTemporal);
+    return u32x4_t{v[0], v[1], 0u, 0u};
+  } else {
+    return u32x4_t{__builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, kLoadNonTemporal), 0u,
+                   0u, 0u};
+  }
+}
+
+// LW bytes of codes times the row's power-of-two scale -> bf16 pairs (exact: an
+// E4M3 or E2M1 value times 2^e is a bf16 number); word i holds elements 2i, 2i + 1
+template <int Bits, int LW>
+__device__ __forceinline__ void pm_dequant(const u32x4_t& c, float sc,
+                                           uint32_t (&w)[LW * 8 / Bits / 2]) {
+#pragma unroll
+  for (int i = 0; i < LW / 4; ++i) {
+    if constexpr (Bits == 8) {
+      w[2 * i] = __builtin_bit_cast(uint32_t,
+                                    __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[i], sc, false));
+      w[2 * i + 1] = __builtin_bit_cast(uint32_t,
+                                        __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[i], sc, true));
+    } else {
+      w[4 * i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c[i], sc, 0));
+      w[4 * i + 1] =
+          __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c[i], sc, 1));
+      w[4 * i + 2] =
+          __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c[i], sc, 2));
+      w[4 * i + 3] =
+          __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c[i], sc, 3));
+    }
+  }
+}
 
 // s_waitcnt immediate waiting until at most n vector memory operations are
 // outstanding (vmcnt in bits 3:0 and 15:14; expcnt and lgkmcnt left at their maximum)
@@ -97,17 +154,18 @@ __device__ __forceinline__ short bf16_bits(__bf16 x) { return __builtin_bit_cast
 
 }  // namespace
 
-template <int G, int GH>
+template <int Bits, int G, int GH>
 __global__ void __launch_bounds__(kPmThreads)
-paged_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ key_cache,
-                  const uint16_t* __restrict__ value_cache,
+paged_mfma_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ key_cache,
+                  const uint8_t* __restrict__ value_cache, const float* __restrict__ k_scale,
+                  const float* __restrict__ v_scale,
                   const int32_t* __restrict__ block_tables, int table_cols,
                   const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ seq_offset,
                   int B, int Hkv, int num_blocks, int block_size, int bs_log2, int max_len,
                   float scale_log2, int chunk, int max_splits, Workspace ws,
                   float* __restrict__ out, float* __restrict__ lse, int32_t* err_flag) {
   constexpr int D = 128;
-  using S = PmShape<GH>;
+  using S = PmShape<GH, Bits>;
   constexpr int NB = S::Blocks;
   constexpr int A = S::Ahead;
   constexpr int QB = GH * G * D * 2;             // a split's query: GH x G heads
@@ -117,7 +175,6 @@ paged_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k
   __shared__ __attribute__((aligned(1024))) uint8_t tile0[S::Buf];
   __shared__ __attribute__((aligned(1024))) uint8_t tile1[S::Buf];
   __shared__ __attribute__((aligned(16))) uint8_t qbuf[2][QB];
-  __shared__ int tbl[2][kMaxTableSpan];
   __shared__ int pref[kPmMaxSeqs + 1];   // splits (x head groups) before sequence b
   __shared__ int slen[kPmMaxSeqs];       // effective length of sequence b
   __shared__ int soff[kPmMaxSeqs];       // its table offset in blocks
@@ -130,8 +187,8 @@ paged_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k
   const int col16 = lane & 15;
   const int Hq = Hkv * G;
   const int bs_mask = block_size - 1;
-  const uint32_t block_bytes = (uint32_t)block_size * Hkv * D * 2;
-  const size_t block_elems = (size_t)block_size * Hkv * D;
+  const uint32_t block_bytes = (uint32_t)block_size * Hkv * S::CB;   // pool bytes of a block
+  const int block_rows = block_size * Hkv;                             // its (slot, head) rows
   const int W = (int)gridDim.x;
 
   // The splits with rows, numbered sequence-major (then head group, then split):
@@ -201,104 +258,151 @@ paged_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k
   int total_steps = 0;
   for (int i = blockIdx.x; i < total; i += W) total_steps += item_of(i).steps;
 
-  // Per-item metadata travels through registers into LDS: the load side reads an
-  // item's query (and the next item's table entries) when it reaches the item, and
-  // stores them to LDS one step later, after the step's wait has covered them.
+  // Per-item metadata: the load side reads an item's query when it reaches the item
+  // and stores it to LDS one step later, after the step's wait has covered it.  The
+  // block-table entries of the item the loads are in stay in registers of every
+  // wave (lane l: entries l and 64 + l), and the next item's are loaded alongside
+  // the query, so a tile's block id is a lane read, not an LDS round trip.
+  static_assert(kMaxTableSpan <= 128, "two table registers per lane");
   u32x4_t qstage[QLoads];
-  int tstage = -1;
+  int tcur0 = -1, tcur1 = -1, tnx0 = -1, tnx1 = -1;
+  auto table_load = [&](const Item& it, int& t0, int& t1) {
+    const int32_t* row = block_tables + (size_t)it.b * table_cols + soff[it.b] + it.blk0;
+    t0 = lane < it.nblk ? row[lane] : -1;
+    t1 = 64 + lane < it.nblk ? row[64 + lane] : -1;
+  };
   auto meta_load = [&](const Item& it, const Item& nx) {
+    const int qhead = __builtin_amdgcn_readfirstlane(it.b * Hq + GH * it.hg * G);
+    const int qrec = __builtin_amdgcn_readfirstlane(it.idx < total ? QB : 0);
     const __amdgpu_buffer_rsrc_t qr = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t*>(q) + ((size_t)it.b * Hq + (size_t)GH * it.hg * G) * D,
-        (short)0, it.idx < total ? QB : 0, 0x00020000);
+        const_cast<uint16_t*>(q) + (size_t)qhead * D, (short)0, qrec, 0x00020000);
 #pragma unroll
     for (int k = 0; k < QLoads; ++k) {
       const int c = (int)threadIdx.x + kPmThreads * k;
       qstage[k] = __builtin_amdgcn_raw_buffer_load_b128(qr, c < QPieces ? c * 16 : (int)kPmNoRow,
                                                         0, 0);
     }
-    tstage = -1;
-    if ((int)threadIdx.x < nx.nblk)
-      tstage = block_tables[(size_t)nx.b * table_cols + soff[nx.b] + nx.blk0 + threadIdx.x];
+    table_load(nx, tnx0, tnx1);
   };
-  auto meta_store = [&](int parity_q, int parity_t) {
+  auto meta_store = [&](int parity_q) {
 #pragma unroll
     for (int k = 0; k < QLoads; ++k) {
       const int c = (int)threadIdx.x + kPmThreads * k;
       if (c < QPieces) *reinterpret_cast<u32x4_t*>(&qbuf[parity_q][c * 16]) = qstage[k];
     }
-    if ((int)threadIdx.x < kMaxTableSpan) tbl[parity_t][threadIdx.x] = tstage;
   };
 
-  // The first item's table, synchronously.
   Item ld = item_of(blockIdx.x);   // the item the loads are in
-  if ((int)threadIdx.x < ld.nblk)
-    tbl[0][threadIdx.x] =
-        block_tables[(size_t)ld.b * table_cols + soff[ld.b] + ld.blk0 + threadIdx.x];
-  __builtin_amdgcn_s_waitcnt(wait_vm(0));
-  __syncthreads();
+  table_load(ld, tcur0, tcur1);
   int ld_t = 0, ld_j = 0;          // tile of the item, ordinal of the item (LDS parity)
-  bool meta_pending = false;       // the loaded metadata waits to be stored
-  int mq = 0, mt = 0;              // where it goes
+  bool meta_pending = false;       // the loaded query waits to be stored
+  int mq = 0;                      // where it goes
 
-  typedef u32x4_t TileRegs[S::Loads];
+  // a tile in registers: K codes, V codes (lane load k of each), and for a coded
+  // pool the scales of the rows those loads hit
+  struct TileRegs {
+    u32x4_t c[2 * S::HalfLoads];
+    float s[2 * S::HalfLoads];
+  };
   // Loads of the next tile on the load side: wave load I = HalfLoads wave + k of the
-  // K half (and of the V half) covers bytes [1024 I, 1024 I + 1024) of it; lane L
-  // takes byte 16 L: row (1024 I + 16 L) / RB, piece ((1024 I + 16 L) % RB) / 16.  A
-  // tile past the item's rows gets an empty resource (zeros, no memory traffic), so
-  // every step issues the same tile loads.  Returns the tile's block id (-1: none).
+  // K half (and of the V half) covers pool bytes [64 LW I, 64 LW (I + 1)) of the
+  // tile's group rows; lane L takes LW bytes at cb = LW (64 I + L): token row cb /
+  // CRB, byte cb % CRB of it (head (cb % CRB) / CB).  A tile past the item's rows
+  // gets an empty resource (zeros, no memory traffic), so every step issues the same
+  // tile loads.  Returns the tile's block id (-1: none).
   auto issue = [&](TileRegs& r) -> int {
     if (ld_t == 0) {  // a new item: its query, and the next item's table
       const Item nx = item_of(ld.idx + W);
       meta_load(ld, nx);
       meta_pending = true;
       mq = ld_j & 1;
-      mt = (ld_j + 1) & 1;
     }
+    // (the block id is made wave-uniform explicitly: a resource built from a value the
+    // compiler cannot prove uniform turns every load into a loop over distinct values)
     int phys = -1;
     if (ld_t < ld.ntiles) {
-      phys = __builtin_amdgcn_readfirstlane(
-          tbl[ld_j & 1][((ld.r0 + ld_t * kPmTile) >> bs_log2) - ld.blk0]);
-      if (phys < 0 || phys >= num_blocks) {
-        if (threadIdx.x == 0) raise_flag(err_flag, 1);
-        phys = -1;
-      }
+      const int e = __builtin_amdgcn_readfirstlane(((ld.r0 + ld_t * kPmTile) >> bs_log2) -
+                                                   ld.blk0);
+      phys = e < 64 ? __builtin_amdgcn_readlane(tcur0, e) : __builtin_amdgcn_readlane(tcur1, e - 64);
     }
-    const size_t base = phys >= 0 ? (size_t)phys * block_elems : 0;
+    const bool bad = ld_t < ld.ntiles && (phys < 0 || phys >= num_blocks);
+    if (bad && threadIdx.x == 0) raise_flag(err_flag, 1);
+    phys = __builtin_amdgcn_readfirstlane(bad ? -1 : phys);
+    const size_t base = phys >= 0 ? (size_t)phys * block_bytes : 0;
     const int records = phys >= 0 ? (int)block_bytes : 0;
     const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t*>(key_cache) + base, (short)0, records, 0x00020000);
+        const_cast<uint8_t*>(key_cache) + base, (short)0, records, 0x00020000);
     const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t*>(value_cache) + base, (short)0, records, 0x00020000);
+        const_cast<uint8_t*>(value_cache) + base, (short)0, records, 0x00020000);
+    __amdgpu_buffer_rsrc_t ksr = kr, vsr = vr;
+    if constexpr (S::Coded) {
+      const size_t sbase = phys >= 0 ? (size_t)phys * block_rows : 0;
+      const int srecords = phys >= 0 ? block_rows * 4 : 0;
+      ksr = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(k_scale) + sbase, (short)0,
+                                              srecords, 0x00020000);
+      vsr = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(v_scale) + sbase, (short)0,
+                                              srecords, 0x00020000);
+    }
     const int tok0 = ld.r0 + ld_t * kPmTile;
 #pragma unroll
     for (int k = 0; k < S::HalfLoads; ++k) {
-      const int byte = 1024 * (wave * S::HalfLoads + k) + 16 * lane;
-      const int row = byte / S::RB;
+      const int cb = S::LW * (lane + 64 * (wave * S::HalfLoads + k));
+      const int row = cb / S::CRB;
+      const int cbr = cb % S::CRB;
       const int tok = tok0 + row;
-      const uint32_t off =
-          tok < ld.r1 ? (uint32_t)(((tok & bs_mask) * Hkv + GH * ld.hg) * (D * 2) +
-                                   byte % S::RB)
-                      : kPmNoRow;
-      r[k] = __builtin_amdgcn_raw_buffer_load_b128(kr, (int)off, 0, kLoadNonTemporal);
-      r[S::HalfLoads + k] = __builtin_amdgcn_raw_buffer_load_b128(vr, (int)off, 0,
-                                                                  kLoadNonTemporal);
+      const int srow = (tok & bs_mask) * Hkv + GH * ld.hg;   // the group's first (slot, head)
+      const bool in = tok < ld.r1;
+      const uint32_t off = in ? (uint32_t)(srow * S::CB + cbr) : kPmNoRow;
+      r.c[k] = pm_load<S::LW>(kr, off);
+      r.c[S::HalfLoads + k] = pm_load<S::LW>(vr, off);
+      if constexpr (S::Coded) {
+        const uint32_t so = in ? (uint32_t)((srow + cbr / S::CB) * 4) : kPmNoRow;
+        r.s[k] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(ksr, (int)so, 0,
+                                                                      kLoadNonTemporal));
+        r.s[S::HalfLoads + k] = __uint_as_float(
+            __builtin_amdgcn_raw_buffer_load_b32(vsr, (int)so, 0, kLoadNonTemporal));
+      }
     }
     if (++ld_t == ld.steps) {
       ld = item_of(ld.idx + W);
       ld_t = 0;
       ++ld_j;
+      tcur0 = tnx0;
+      tcur1 = tnx1;
     }
     return phys;
   };
-  // the arrived registers of a tile into an LDS tile, pieces permuted
+  // the arrived registers of a tile into an LDS tile as bf16 (codes dequantised
+  // with their row's scale), pieces permuted
   auto put = [&](const TileRegs& r, uint8_t* dst) {
 #pragma unroll
     for (int k = 0; k < S::HalfLoads; ++k) {
-      const int byte = 1024 * (wave * S::HalfLoads + k) + 16 * lane;
-      const int row = byte / S::RB;
-      const int at = row * S::RB + pm_slot((byte % S::RB) / 16, row) * 16;
-      *reinterpret_cast<u32x4_t*>(dst + at) = r[k];
-      *reinterpret_cast<u32x4_t*>(dst + S::Half + at) = r[S::HalfLoads + k];
+      const int cb = S::LW * (lane + 64 * (wave * S::HalfLoads + k));
+      const int row = cb / S::CRB;
+      const int cbr = cb % S::CRB;
+      if constexpr (!S::Coded) {
+        const int at = row * S::RB + pm_slot(cbr / 16, row) * 16;
+        *reinterpret_cast<u32x4_t*>(dst + at) = r.c[k];
+        *reinterpret_cast<u32x4_t*>(dst + S::Half + at) = r.c[S::HalfLoads + k];
+      } else {
+        // the load's first element as a byte offset into the bf16 row
+        const int at = (cbr / S::CB) * 256 + (cbr % S::CB) * (16 / Bits);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          uint32_t w[S::Elems / 2];
+          pm_dequant<Bits, S::LW>(r.c[h * S::HalfLoads + k], r.s[h * S::HalfLoads + k], w);
+          uint8_t* rowp = dst + h * S::Half + row * S::RB;
+          if constexpr (S::Elems >= 8) {
+#pragma unroll
+            for (int p = 0; p < S::Elems / 8; ++p)
+              *reinterpret_cast<u32x4_t*>(rowp + pm_slot(at / 16 + p, row) * 16) =
+                  u32x4_t{w[4 * p], w[4 * p + 1], w[4 * p + 2], w[4 * p + 3]};
+          } else {
+            *reinterpret_cast<pm_u32x2_t*>(rowp + pm_slot(at / 16, row) * 16 + at % 16) =
+                pm_u32x2_t{w[0], w[1]};
+          }
+        }
+      }
     }
   };
 
@@ -333,17 +437,22 @@ paged_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k
   for (int jb = 0; jb < NB; ++jb) oacc[jb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   float m = kNegInf, lsum = 0.f;
 
+  // the item's query as B operands, read from LDS at its first tile
+  u32x4_t qr[4];
   auto compute = [&](const uint8_t* T, int phys) {
     const int tok0 = ci.r0 + ct * kPmTile;
     const bool block_ok = phys >= 0;
-    const uint8_t* qp = qbuf[cj & 1] + q_off;
-    u32x4_t qr[4], a[4];
+    if (ct == 0) {
+      const uint8_t* qp = qbuf[cj & 1] + q_off;
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      qr[s] = *reinterpret_cast<const u32x4_t*>(qp + 64 * s);
-      if (col16 >= G) qr[s] = u32x4_t{0u, 0u, 0u, 0u};
-      a[s] = *reinterpret_cast<const u32x4_t*>(T + a_off[s]);
+      for (int s = 0; s < 4; ++s) {
+        qr[s] = *reinterpret_cast<const u32x4_t*>(qp + 64 * s);
+        if (col16 >= G) qr[s] = u32x4_t{0u, 0u, 0u, 0u};
+      }
     }
+    u32x4_t a[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) a[s] = *reinterpret_cast<const u32x4_t*>(T + a_off[s]);
     i16x4_t vb[NB];
 #pragma unroll
     for (int jb = 0; jb < NB; ++jb)
@@ -370,10 +479,33 @@ paged_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k
       tmax = fmaxf(tmax, sc[i2]);
     }
     tmax = pm_group4_max(tmax);
-    const float mnew = fmaxf(m, tmax);
-    const float ms = mnew == kNegInf ? 0.f : mnew;
-    const float alpha = exp2_fast(m - ms);
-    m = mnew;
+    // skip-scale: a wave-uniform decision; a head whose max did not move gets alpha 1
+    if (__any(tmax > m + kPmRescale)) {
+      const float mnew = fmaxf(m, tmax);
+      const float alpha = mnew == kNegInf ? 1.f : exp2_fast(m - mnew);
+      m = mnew;
+      lsum *= alpha;
+      // alpha of head 4 grp + i for the output rows this lane holds: heads live in
+      // lanes 0..G-1 (rows G..15 belong to no head and take any finite factor)
+      float a4[4];
+#pragma unroll
+      for (int i2 = 0; i2 < 4; ++i2) {
+        const float lo = __int_as_float(
+            __builtin_amdgcn_readlane(__float_as_int(alpha), i2 < G ? i2 : 0));
+        if constexpr (G > 4) {
+          const float hi = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), 4 + i2));
+          a4[i2] = grp == 1 ? hi : lo;
+        } else {
+          a4[i2] = lo;
+        }
+      }
+#pragma unroll
+      for (int jb = 0; jb < NB; ++jb) {
+#pragma unroll
+        for (int i2 = 0; i2 < 4; ++i2) oacc[jb][i2] *= a4[i2];
+      }
+    }
+    const float ms = m == kNegInf ? 0.f : m;
     i16x4_t pa, pl;
     float psum = 0.f;
 #pragma unroll
@@ -384,14 +516,9 @@ paged_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k
       pa[i2] = bf16_bits(hi);
       pl[i2] = bf16_bits((__bf16)(p - (float)hi));
     }
-    lsum = lsum * alpha + psum;
-    float a4[4];
-#pragma unroll
-    for (int i2 = 0; i2 < 4; ++i2) a4[i2] = __shfl(alpha, 4 * grp + i2);
+    lsum += psum;
 #pragma unroll
     for (int jb = 0; jb < NB; ++jb) {
-#pragma unroll
-      for (int i2 = 0; i2 < 4; ++i2) oacc[jb][i2] *= a4[i2];
       oacc[jb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, vb[jb], oacc[jb], 0, 0, 0);
       oacc[jb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pl, vb[jb], oacc[jb], 0, 0, 0);
     }
@@ -431,10 +558,12 @@ paged_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k
   // One step s: wait for this wave's loads of tile s (the loads of the A - 1 tiles
   // issued after it may stay outstanding; anything issued before it is complete
   // too), store the item metadata loaded one step earlier and write tile s to LDS
-  // tile T, refill the registers with tile s + A; the barrier then makes every
-  // wave's stores visible (one step earlier it ended every wave's reads of T's
-  // previous tile, s - 2); arithmetic on tile s.  Every step issues the same tile
-  // loads (the ones past the last item are empty), so one wait count fits all.
+  // tile T; the barrier then makes every wave's stores visible (one step earlier it
+  // ended every wave's reads of T's previous tile, s - 2); refill the registers with
+  // tile s + A (after the barrier, so that the waves' loads enter the memory
+  // pipeline while other waves compute); arithmetic on tile s.  Every step issues
+  // the same tile loads (the ones past the last item are empty), so one wait count
+  // fits all.
   constexpr int kUnroll = A % 2 == 0 ? A : 2 * A;
   TileRegs regs[A];
   int phys_ring[A];
@@ -443,16 +572,16 @@ paged_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k
   auto step = [&](int s, TileRegs& r, int& phys_slot, uint8_t* T) {
     __builtin_amdgcn_s_waitcnt(wait_vm((A - 1) * S::Loads));
     if (meta_pending) {
-      meta_store(mq, mt);
+      meta_store(mq);
       meta_pending = false;
     }
     put(r, T);
-    const int phys = phys_slot;
-    phys_slot = issue(r);
     __builtin_amdgcn_s_waitcnt(kWaitLgkm0Pm);
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
+    const int phys = phys_slot;
+    phys_slot = issue(r);
     if (s < total_steps) {
       if (ct < ci.ntiles) compute(T, phys);
       if (++ct == ci.steps) {
@@ -518,7 +647,7 @@ SplitPlan plan_paged_mfma(int B, int Hkv, int max_seq_len, int block_size, int f
 
 // Workgroups of a persistent launch: as many as the device keeps resident at once
 // (occupancy per CU times the CU count, both queried once per device and kernel).
-template <int G, int GH>
+template <int Bits, int G, int GH>
 static int resident_workgroups() {
   constexpr int kMaxDev = 64;
   static int cached[kMaxDev];
@@ -527,7 +656,7 @@ static int resident_workgroups() {
   if (cached[dev] > 0) return cached[dev];
   int cus = 0, per_cu = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, paged_mfma_kernel<G, GH>,
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, paged_mfma_kernel<Bits, G, GH>,
                                                    kPmThreads, 0) != hipSuccess)
     return 0;
   const int n = cus * (per_cu > 0 ? per_cu : 1);
@@ -535,47 +664,53 @@ static int resident_workgroups() {
   return n;
 }
 
-template <int G, int GH>
-static hipError_t launch_pm(const uint16_t* qb, const uint16_t* kc, const uint16_t* vc,
-                            const int32_t* block_tables, int table_cols,
+template <int Bits, int G, int GH>
+static hipError_t launch_pm(const uint16_t* qb, const uint8_t* kc, const uint8_t* vc,
+                            const float* ks, const float* vs, const int32_t* block_tables,
+                            int table_cols,
                             const int32_t* seq_lens, const int32_t* seq_offset, int B, int Hkv,
                             int num_blocks, int block_size, int bs_log2, int max_seq_len,
                             float scale, const SplitPlan& plan, const Workspace& w, float* out,
                             float* lse, int32_t* err_flag, hipStream_t stream) {
-  const int resident = resident_workgroups<G, GH>();
+  const int resident = resident_workgroups<Bits, G, GH>();
   if (resident <= 0) return hipErrorInvalidValue;
   const long long items = (long long)B * (Hkv / GH) * plan.max_splits;  // at most
   const unsigned grid = (unsigned)(items < resident ? items : resident);
-  hipLaunchKernelGGL((paged_mfma_kernel<G, GH>), dim3(grid), dim3(kPmThreads), 0, stream, qb,
-                     kc, vc, block_tables, table_cols, seq_lens, seq_offset, B, Hkv,
+  hipLaunchKernelGGL((paged_mfma_kernel<Bits, G, GH>), dim3(grid), dim3(kPmThreads), 0, stream,
+                     qb, kc, vc, ks, vs, block_tables, table_cols, seq_lens, seq_offset, B, Hkv,
                      num_blocks, block_size, bs_log2, max_seq_len, scale * kLog2e, plan.chunk,
                      plan.max_splits, w, out, lse, err_flag);
   return hipGetLastError();
 }
 
-hipError_t launch_decode_paged_mfma(const void* q, const void* key_cache,
-                                    const void* value_cache, const int32_t* block_tables,
-                                    int table_cols, const int32_t* seq_lens,
-                                    const int32_t* seq_offset, int B, int Hq, int Hkv,
-                                    int num_blocks, int block_size, int max_seq_len,
-                                    float scale, float* out, float* lse, void* ws,
-                                    const SplitPlan& plan, int32_t* err_flag,
-                                    hipStream_t stream) {
+template <int Bits>
+static hipError_t launch_paged_mfma_fmt(const void* q, const void* key_cache,
+                                        const void* value_cache, const float* k_scale,
+                                        const float* v_scale, const int32_t* block_tables,
+                                        int table_cols, const int32_t* seq_lens,
+                                        const int32_t* seq_offset, int B, int Hq, int Hkv,
+                                        int num_blocks, int block_size, int max_seq_len,
+                                        float scale, float* out, float* lse, void* ws,
+                                        const SplitPlan& plan, int32_t* err_flag,
+                                        hipStream_t stream) {
   const Workspace w = carve(ws, (size_t)B * Hq, plan.max_splits, 128);
   int bs_log2 = 0;
   while ((1 << bs_log2) < block_size) ++bs_log2;
   const auto* qb = static_cast<const uint16_t*>(q);
-  const auto* kc = static_cast<const uint16_t*>(key_cache);
-  const auto* vc = static_cast<const uint16_t*>(value_cache);
+  const auto* kc = static_cast<const uint8_t*>(key_cache);
+  const auto* vc = static_cast<const uint8_t*>(value_cache);
   // KV heads per workgroup: up to 8 (whole token rows at Hkv = 8); 4 at G = 8, whose
-  // query buffers would not fit the LDS next to 8-head tiles
-  const int gh_max = Hq / Hkv == 8 ? 4 : 8;
+  // query buffers would not fit the LDS next to 8-head tiles, and over the FP4 pool,
+  // where half-size tiles let two workgroups share a CU (measured at the batch-64
+  // paged config: 168 us with 4 heads, 191 us with 8; the FP8 pool is faster with 8:
+  // 183 us against 228 us)
+  const int gh_max = (Hq / Hkv == 8 || Bits == 4) ? 4 : 8;
   const int GH = Hkv < gh_max ? Hkv : gh_max;
   hipError_t err = hipErrorInvalidValue;
-#define DAKV_PM(GG, HH)                                                                      \
-  err = launch_pm<GG, HH>(qb, kc, vc, block_tables, table_cols, seq_lens, seq_offset, B, Hkv, \
-                          num_blocks, block_size, bs_log2, max_seq_len, scale, plan, w, out, \
-                          lse, err_flag, stream)
+#define DAKV_PM(GG, HH)                                                                       \
+  err = launch_pm<Bits, GG, HH>(qb, kc, vc, k_scale, v_scale, block_tables, table_cols,       \
+                                seq_lens, seq_offset, B, Hkv, num_blocks, block_size, bs_log2, \
+                                max_seq_len, scale, plan, w, out, lse, err_flag, stream)
 #define DAKV_PM_H(GG)                  \
   switch (GH) {                        \
     case 2: DAKV_PM(GG, 2); break;     \
@@ -597,6 +732,35 @@ hipError_t launch_decode_paged_mfma(const void* q, const void* key_cache,
   if (err != hipSuccess || plan.max_splits <= 1) return err;
   return launch_paged_merge(w, B, Hq, plan.chunk, plan.max_splits, seq_lens, seq_offset,
                             block_size, table_cols, max_seq_len, out, lse, stream);
+}
+
+hipError_t launch_decode_paged_mfma(const void* q, const void* key_cache,
+                                    const void* value_cache, const int32_t* block_tables,
+                                    int table_cols, const int32_t* seq_lens,
+                                    const int32_t* seq_offset, int B, int Hq, int Hkv,
+                                    int num_blocks, int block_size, int max_seq_len,
+                                    float scale, float* out, float* lse, void* ws,
+                                    const SplitPlan& plan, int32_t* err_flag,
+                                    hipStream_t stream) {
+  return launch_paged_mfma_fmt<16>(q, key_cache, value_cache, nullptr, nullptr, block_tables,
+                                   table_cols, seq_lens, seq_offset, B, Hq, Hkv, num_blocks,
+                                   block_size, max_seq_len, scale, out, lse, ws, plan, err_flag,
+                                   stream);
+}
+
+hipError_t launch_decode_paged_mfma_lowbit(bool fp4, const void* q, const void* k_codes,
+                                           const void* v_codes, const float* k_scale,
+                                           const float* v_scale, const int32_t* block_tables,
+                                           int table_cols, const int32_t* seq_lens,
+                                           const int32_t* seq_offset, int B, int Hq, int Hkv,
+                                           int num_blocks, int block_size, int max_seq_len,
+                                           float scale, float* out, float* lse, void* ws,
+                                           const SplitPlan& plan, int32_t* err_flag,
+                                           hipStream_t stream) {
+  const auto launch = fp4 ? launch_paged_mfma_fmt<4> : launch_paged_mfma_fmt<8>;
+  return launch(q, k_codes, v_codes, k_scale, v_scale, block_tables, table_cols, seq_lens,
+                seq_offset, B, Hq, Hkv, num_blocks, block_size, max_seq_len, scale, out, lse,
+                ws, plan, err_flag, stream);
 }
 
 }  // namespace dakv
