@@ -36,36 +36,62 @@ WARM = 5       # untimed repetitions before them (cold caches, first-launch cost
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "static_decode_step_b8_traffic.md")
 STATIC_SOURCES = ("decode_kernels.hip", "split_common.hpp", "device.hpp")
+SPARSE_COUNTER_FILE = os.path.join(ROOT, "profiles", "sparse_mla_b16_kernel_trace_and_traffic.md")
+SPARSE_SOURCES = ("sparse_kernels.hip", "device.hpp")
 
 
-def static_sources_sha256():
+def sources_sha256(names):
     import hashlib
     h = hashlib.sha256()
-    for name in STATIC_SOURCES:
+    for name in names:
         with open(os.path.join(ROOT, "decode_attention_kv_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
 
 
-def recorded_traffic():
-    """HBM bytes per fused step call from the committed counter summary, or None
-    when it is missing or was taken on other kernel sources than these."""
+def static_sources_sha256():
+    return sources_sha256(STATIC_SOURCES)
+
+
+def sparse_sources_sha256():
+    return sources_sha256(SPARSE_SOURCES)
+
+
+def recorded_value(path, sha_key, sha, key, kind=int):
+    """A `key: value` line of a committed counter summary, or None when the file is
+    missing or its `sha_key` line names other kernel sources than `sha`."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(path) as f:
             text = f.read()
     except OSError:
         return None
     fields = {}
     for raw in text.splitlines():
-        if ":" in raw and raw.strip().startswith(("kernel_sources_sha256", "traffic_bytes_per_call")):
-            k, v = raw.strip().strip("`").split(":", 1)
+        line = raw.strip().strip("`")
+        if ":" in line and line.startswith((sha_key, key)):
+            k, v = line.split(":", 1)
             fields[k.strip()] = v.strip().strip("`")
-    if fields.get("kernel_sources_sha256") != static_sources_sha256():
+    if fields.get(sha_key) != sha:
         return None
     try:
-        return int(fields["traffic_bytes_per_call"])
+        return kind(fields[key])
     except (KeyError, ValueError):
         return None
+
+
+def recorded_traffic():
+    """HBM bytes per fused step call from the committed counter summary, or None
+    when it is missing or was taken on other kernel sources than these."""
+    return recorded_value(TRAFFIC_FILE, "kernel_sources_sha256", static_sources_sha256(),
+                          "traffic_bytes_per_call")
+
+
+def recorded_sparse_mfma_busy():
+    """The sparse split kernel's MFMA-busy fraction (SQ_VALU_MFMA_BUSY_CYCLES over the
+    active cycles of all SIMDs) from the committed counter summary, or None when it
+    was taken on other kernel sources than these."""
+    return recorded_value(SPARSE_COUNTER_FILE, "sparse_sources_sha256", sparse_sources_sha256(),
+                          "sparse_split_mfma_busy", float)
 
 
 def parse():
@@ -698,7 +724,11 @@ def sparse_leg(torch, dakv, workloads, acc, counter_pass=False):
             "algorithmic_bytes": nbytes, "GBps": round(nbytes / (ms * 1e-3) / 1e9, 1),
             "frac_of_hbm_peak": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
             "TFLOPs": round(flops / (ms * 1e-3) / 1e12, 1),
-            "frac_of_bf16_mfma_peak": round(flops / (ms * 1e-3) / 2.5e15, 4)}
+            "frac_of_bf16_mfma_peak": round(flops / (ms * 1e-3) / 2.5e15, 4),
+            "split_kernel_mfma_busy_counter": recorded_sparse_mfma_busy(),
+            "mfma_busy_source": "profiles/sparse_mla_b16_kernel_trace_and_traffic.md "
+                                "(SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE x SIMDs), split "
+                                "kernel only; null when taken on other kernel sources)"}
 
 
 def sparse_tokens_leg(torch, dakv, workloads, acc, s_q=2):

@@ -258,7 +258,7 @@ __host__ __device__ inline size_t ws_floats(size_t heads, int max_splits, int D)
 // (thread j holds split j) together with its first kMergePre partial loads (the
 // D/4 float4 columns are shared among kThreads / (D/4) split groups); the max and
 // the weights 2^(lse_j - max) go through LDS, and the groups are summed there.
-constexpr int kMergePre = 4;
+constexpr int kMergePre = 8;
 
 template <int D>
 __device__ __forceinline__ void merge_head(const float* __restrict__ lp,
@@ -301,10 +301,22 @@ __device__ __forceinline__ void merge_head(const float* __restrict__ lp,
     const float wj = j < n ? sm_w[j] : 0.f;
     acc.x += wj * pre[k].x; acc.y += wj * pre[k].y; acc.z += wj * pre[k].z; acc.w += wj * pre[k].w;
   }
-  for (int j = grp + kMergePre * kGroups; j < n; j += kGroups) {
-    const float wj = sm_w[j];
-    const float4 y = *reinterpret_cast<const float4*>(cp + (size_t)j * D);
-    acc.x += wj * y.x; acc.y += wj * y.y; acc.z += wj * y.z; acc.w += wj * y.w;
+  // more splits than the prefetch covers: kMergePre partials per thread at a time,
+  // all loads of a batch issued before its first use
+  for (int j0 = grp + kMergePre * kGroups; j0 < n; j0 += kMergePre * kGroups) {
+    float4 y[kMergePre];
+#pragma unroll
+    for (int k = 0; k < kMergePre; ++k) {
+      const int j = j0 + k * kGroups;
+      y[k] = j < n ? *reinterpret_cast<const float4*>(cp + (size_t)j * D)
+                   : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int k = 0; k < kMergePre; ++k) {
+      const int j = j0 + k * kGroups;
+      const float wj = j < n ? sm_w[j] : 0.f;
+      acc.x += wj * y[k].x; acc.y += wj * y[k].y; acc.z += wj * y[k].z; acc.w += wj * y[k].w;
+    }
   }
   sm_red[tid] = acc;
   __syncthreads();
