@@ -24,14 +24,16 @@
 //     rows x 32 dims from LDS (read a batch of k-steps ahead), B = Q^T of the
 //     wave's 16 heads, held in registers for the whole split (18 k-steps x 16
 //     bytes per lane); three accumulation chains.
-//   * Each wave publishes its scores through LDS (one barrier per tile); every
-//     wave of the head block then reads all 64 rows' scores, so the four keep
-//     the same running max and sums and take the same rescale decisions.
+//   * Each wave exponentiates its own 16 rows against the running max the four
+//     waves of a head block share, and publishes P (as bf16 hi + lo parts) with
+//     its rows' max through LDS (one barrier per tile).  Only when a tile raises
+//     a max by more than the skip-scale threshold (the first tile always does)
+//     does the whole workgroup move the max, rescale and publish again.
 //   * The C layout of S^T (lane: head lane % 16, tokens 4 (lane / 16) + i of a
 //     row block) is the A layout of P for O = P V when the 8 tokens of a lane
 //     group in k-step kk are tokens {4g..4g+3} of row blocks 2 kk and 2 kk + 1,
-//     so each lane forms its P operands from the scores it read.  P enters the
-//     matrix core as bf16 hi + lo parts (two MFMAs per block).
+//     so each lane reads its P operands as published.  P enters the matrix core
+//     as bf16 hi + lo parts (two MFMAs per block).
 //   * The B operand of P V (8 rows of one dim per lane) comes straight from LDS
 //     with two transposing reads ds_read_b64_tr_b16: lane j of a 16-lane group
 //     points at row 4 (group) + j / 4 (+16), dims 4 (j % 4) .. +3 of a 16-dim
@@ -153,7 +155,13 @@ sparse_split_kernel(const uint16_t* __restrict__ q, const void* __restrict__ kv,
   __shared__ __attribute__((aligned(1024))) uint8_t buf1[kTileBytes];
   __shared__ uint32_t rows[kSplit];  // byte offset of each index's row in kv[b], or kNoRow
   __shared__ float row_scale[kCodes ? kSplit : 1];       // codes: each index's row scale
-  __shared__ f32x4_t sm_s[2][kRowBlocks][64];            // scores of each row block
+  // P of each row block (bf16 hi parts in .xy, lo parts in .zw; lane layout of the
+  // block's scores), each row block's score max per head, the waves' rescale flags
+  // and, at the end, each row block's sum of exponentials per head
+  __shared__ u32x4_t sm_p[2][kRowBlocks][64];
+  __shared__ float sm_mx[2][kRowBlocks][16];
+  __shared__ int sm_flag[kSpWaves];
+  __shared__ float sm_l[2][kRowBlocks][16];
   const int hg = blockIdx.x / per_hg;
   const int u = blockIdx.x - hg * per_hg;
   if (u >= B * n_splits) return;
@@ -403,31 +411,48 @@ sparse_split_kernel(const uint16_t* __restrict__ q, const void* __restrict__ kv,
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-    // scores of tile rows 16 rb + 4 grp + i for head col16 (-inf for rows past
-    // the index list), published to the head block's other three waves
-    {
-      f32x4_t sc;
+    // scores of this wave's tile rows 16 rb + 4 grp + i for head col16 (-inf for
+    // rows past the index list), and their max per head
+    float sc[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int tok = it * kTile + rb * kRowBlock + 4 * grp + i;
-        sc[i] = rows[tok] != kNoRow ? (st[0][i] + st[1][i] + st[2][i]) * scale_log2 : kNegInf;
-      }
-      sm_s[hb][rb][lane] = sc;
+    for (int i = 0; i < 4; ++i) {
+      const int tok = it * kTile + rb * kRowBlock + 4 * grp + i;
+      sc[i] = rows[tok] != kNoRow ? (st[0][i] + st[1][i] + st[2][i]) * scale_log2 : kNegInf;
     }
+    const float bmax = group4_max(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])));
+    // skip-scale: the exponentials of this wave's rows are taken against the running
+    // max m_ref as it stands; a tile that raises it by more than the threshold in
+    // any row block (the first tile always does) is redone below for the whole
+    // workgroup, so that every wave passes the same barriers
+    auto publish = [&](float mu) {
+      u32x4_t pk;
+      float ps = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; i += 2) {
+        const float p0 = exp2_fast(sc[i] - mu), p1 = exp2_fast(sc[i + 1] - mu);
+        ps += p0 + p1;
+        const __bf16 h0 = (__bf16)p0, h1 = (__bf16)p1;
+        const bf16x2_t hh = {h0, h1};
+        const bf16x2_t ll = {(__bf16)(p0 - (float)h0), (__bf16)(p1 - (float)h1)};
+        pk[i >> 1] = __builtin_bit_cast(uint32_t, hh);
+        pk[2 + (i >> 1)] = __builtin_bit_cast(uint32_t, ll);
+      }
+      sm_p[hb][rb][lane] = pk;
+      return ps;
+    };
+    const bool raise = __any(bmax > m_ref + kRescale);
+    float psum = publish(m_ref == kNegInf ? 0.f : m_ref);
+    if (grp == 0) sm_mx[hb][rb][col16] = bmax;
+    if (lane == 0) sm_flag[wave] = raise;
     lds_barrier();
-    // every wave of the head block now holds all 64 rows' scores in the same
-    // layout (row block b: tokens 16 b + 4 grp + i) and takes the same decisions
-    f32x4_t y[kRowBlocks];
+    bool redo = false;
 #pragma unroll
-    for (int b4 = 0; b4 < kRowBlocks; ++b4) y[b4] = sm_s[hb][b4][lane];
-    float tmax = kNegInf;
+    for (int w = 0; w < kSpWaves; ++w) redo |= sm_flag[w] != 0;
+    if (redo) {  // rare: the running max moves (the same decision in every wave)
+      float tmax = kNegInf;
 #pragma unroll
-    for (int b4 = 0; b4 < kRowBlocks; ++b4)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) tmax = fmaxf(tmax, y[b4][i]);
-    tmax = group4_max(tmax);
-    const float mnew = fmaxf(m_ref, tmax);
-    if (__any(mnew > m_ref + kRescale)) {
+      for (int b4 = 0; b4 < kRowBlocks; ++b4) tmax = fmaxf(tmax, sm_mx[hb][b4][col16]);
+      const float mnew = fmaxf(m_ref, tmax);
       const float alpha = mnew == kNegInf ? 1.f : exp2_fast(m_ref - mnew);
       lsum *= alpha;
       m_ref = mnew;
@@ -439,26 +464,24 @@ sparse_split_kernel(const uint16_t* __restrict__ q, const void* __restrict__ kv,
 #pragma unroll
         for (int i = 0; i < 4; ++i) oacc[j][i] *= a4[i];
       }
+      // (no wave reads P before the barrier below, so it can be rewritten now)
+      psum = publish(m_ref == kNegInf ? 0.f : m_ref);
+      lds_barrier();
     }
-    const float mu = m_ref == kNegInf ? 0.f : m_ref;
+    lsum += psum;
 
     // O += P V over the tile's 64 rows for dim blocks 8 rb .. 8 rb + 7.  k-step
     // kk: lane group g holds tokens {4g..4g+3} of row blocks 2 kk and 2 kk + 1
-    // (the C layout of those blocks' scores), and the transposing reads return V
-    // rows in the same order.  P as two bf16 parts (p = hi + lo to about 16
-    // significant bits): rounding P to one bf16 alone can put the output off by
-    // more than 2e-3 when a few rows dominate the softmax.
+    // (the published P of those blocks, in their scores' lane layout), and the
+    // transposing reads return V rows in the same order.  P enters as two bf16
+    // parts (p = hi + lo to about 16 significant bits): rounding P to one bf16
+    // alone can put the output off by more than 2e-3 when a few rows dominate the
+    // softmax.
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
-      bf16x8_t pa, pl;
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const float p = exp2_fast(y[2 * kk + (k >> 2)][k & 3] - mu);
-        lsum += p;
-        const __bf16 hi = (__bf16)p;
-        pa[k] = hi;
-        pl[k] = (__bf16)(p - (float)hi);
-      }
+      const u32x4_t q0 = sm_p[hb][2 * kk][lane], q1 = sm_p[hb][2 * kk + 1][lane];
+      const bf16x8_t pa = __builtin_bit_cast(bf16x8_t, u32x4_t{q0[0], q0[1], q1[0], q1[1]});
+      const bf16x8_t pl = __builtin_bit_cast(bf16x8_t, u32x4_t{q0[2], q0[3], q1[2], q1[3]});
       const uint8_t* vp0 = T + vbase[kk][0];
       const uint8_t* vp1 = T + vbase[kk][1];
       i16x4_t vb[kWaveDimBlocks][2];
@@ -488,9 +511,12 @@ sparse_split_kernel(const uint16_t* __restrict__ q, const void* __restrict__ kv,
     if (it + 1 < ntiles) tile(it + 1, buf1, buf0);
   }
 
-  // Epilogue.  The sum of exponentials per head (the four waves of a head block
-  // hold the same sums and the same running max).
+  // Epilogue.  The sum of exponentials per head: each wave summed its own row
+  // block's, against the running max that the four waves of a head block share.
   lsum = group4_sum(lsum);
+  if (grp == 0) sm_l[hb][rb][col16] = lsum;
+  lds_barrier();
+  lsum = sm_l[hb][0][col16] + sm_l[hb][1][col16] + sm_l[hb][2][col16] + sm_l[hb][3][col16];
   float inv[4], lse2[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
