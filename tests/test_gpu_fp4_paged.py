@@ -45,6 +45,7 @@ def run_decode(q_bits, pool, index, **kw):
     ([5, 64, 65, 1000], 4, 4, 32),        # G = 1
     ([300, 1], 16, 2, 64),                # G = 8
     ([129, 0, 77], 8, 4, 128),            # an empty sequence, block 128
+    ([700, 33], 32, 16, 16),              # 16 KV heads: several head groups
     ([40, 300], 4, 1, 16),                # one KV head: the VALU kernel
 ])
 def test_paged_fp4_decode_matches_oracle(lengths, Hq, Hkv, bs):

@@ -256,3 +256,61 @@ def test_paged_longest_supported_sequence():
     with pytest.raises(ValueError):
         dakv.decode_attn_paged(case.q, case.key_cache, case.value_cache, t, s, o,
                                max_seq_len=262145)
+
+
+# ---------------------------------------------- the matrix-core kernel's own edges
+# (Hkv in {2, 4, 8k} with D = 128 and at most 512 sequences take paged_mfma_kernel;
+# the tests above with one or three KV heads reach the other kernels)
+
+def test_paged_mfma_single_token_bit_exact_and_empty_sequence():
+    case = workloads.paged_case([1, 0, 1], Hq=8, Hkv=2, D=128, block_size=16, device=DEV,
+                                seed=170)
+    out, lse = run_paged(case)
+    vc = bits(case.value_cache)
+    for b in (0, 2):
+        blk = case.index.block_tables[b, 0]
+        for h in range(8):
+            expect = (vc[blk, 0, h // 4].astype(np.uint32) << 16).view(np.float32)
+            assert np.array_equal(out[b, h], expect), (b, h)
+    assert np.all(out[1] == 0) and np.all(np.isneginf(lse[1]))
+
+
+def test_paged_mfma_bad_block_id_is_flagged_and_others_unaffected():
+    case = workloads.paged_case([40, 40, 300], Hq=32, Hkv=8, D=128, block_size=16, device=DEV,
+                                seed=174)
+    good = case.index.block_tables.copy()
+    case.index.block_tables[1, 1] = 10 ** 6
+    flag = torch.zeros(1, dtype=torch.int32, device=DEV)
+    out, _ = run_paged(case, err_flag=flag)
+    assert int(flag.item()) & dakv._lib.ERR_BLOCK_ID
+    case.index.block_tables = good
+    ref, _ = oracle_paged(case)
+    assert_attention_close(out[0], ref[0])
+    assert_attention_close(out[2], ref[2])
+
+
+@pytest.mark.parametrize("B", [512, 513])
+def test_paged_sequence_count_at_the_split_map_limit(B):
+    """512 sequences are the most the matrix-core kernel's split map holds (one more
+    takes the all-heads kernel); both against the oracle."""
+    print(f"paged B={B}", flush=True)
+    rng = np.random.default_rng(180 + B)
+    lengths = rng.integers(0, 40, size=B).tolist()
+    case = workloads.paged_case(lengths, Hq=32, Hkv=8, D=128, block_size=16, device=DEV,
+                                seed=181 + B)
+    out, lse = run_paged(case)
+    ref_out, ref_lse = oracle_paged(case)
+    assert_attention_close(out, ref_out)
+    assert_lse_close(lse, ref_lse)
+
+
+def test_paged_mfma_longest_supported_sequence():
+    """Block 16, 2 KV heads: 262144 tokens (256 splits of 1024) through the matrix-core
+    kernel, with a 3-token sequence beside it."""
+    print("paged mfma 262144 tokens", flush=True)
+    case = workloads.paged_case([262144, 3], Hq=2, Hkv=2, D=128, block_size=16, device=DEV,
+                                seed=177)
+    out, lse = run_paged(case)
+    ref_out, ref_lse = oracle_paged(case)
+    assert_attention_close(out, ref_out)
+    assert_lse_close(lse, ref_lse)
