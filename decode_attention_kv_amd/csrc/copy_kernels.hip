@@ -61,8 +61,11 @@ hipError_t launch_kv_append(void* k_cache, void* v_cache, const void* k_new, con
 // all of its loads issued before the first store (non-temporal both ways).
 // Grid: n * B * H * chunks, chunk fastest; chunks past the copied length exit.
 // ---------------------------------------------------------------------------
-constexpr int kCopyLoads = 8;                        // 16-byte loads per thread
-constexpr int kCopyBytes = 256 * kCopyLoads * 16;    // 32 KiB per workgroup
+// 4 loads of 16 bytes per thread (16 KiB per workgroup): the 64-tensor, 1 GiB
+// hand-over measured 187.8 us per call, against 190.9 / 189.9 / 190.1 / 192.9 us
+// with 2 / 3 / 6 / 8 loads per thread.
+constexpr int kCopyLoads = 4;                        // 16-byte loads per thread
+constexpr int kCopyBytes = 256 * kCopyLoads * 16;    // 16 KiB per workgroup
 
 struct CopyTable {
   const uint8_t* src[kCopyMaxTensors];
@@ -173,11 +176,15 @@ hipError_t launch_trim_kvcache(int32_t* mask, const int32_t* new_len, int B, int
 // bad block id are written as zeros).  Loads and stores are non-temporal: each
 // byte moves once.
 // ---------------------------------------------------------------------------
-constexpr int kGatherTok = 32;
-// At 4 KiB per token (K + V) a workgroup's 32 rows are one round of 32 loads per
-// thread: all of its loads are in flight before the first store (measured 6%
-// faster than two rounds of 16 at batch 32 x U{1..4096}, at 2 waves per SIMD).
-constexpr int kGatherSlots = 32;
+// A workgroup takes 3 tokens: at 4 KiB per token (K + V, 8 heads x 128 dims) that
+// is 3 loads per thread, all in flight before the first store, in a small kernel
+// (30-odd VGPRs) that keeps 8 workgroups on every CU, so that the two dependent
+// reads each workgroup starts with (the lengths, then the block table) overlap
+// other workgroups' copies.  Measured at batch 32 x U{1..4096} (494 MB): 3 tokens
+// 87.0 us per call; 2: 90.0; 4: 90.6; 5: 89.6; 8: 92.9; 16: 96.7; 32 tokens (one
+// round of 32 loads per thread, 294 VGPRs, one wave per SIMD): 95.1.
+constexpr int kGatherTok = 3;
+constexpr int kGatherSlots = 3;
 constexpr int kGatherLensLds = 4096;
 
 
@@ -259,8 +266,11 @@ gather_kernel(const uint8_t* __restrict__ key_cache, const uint8_t* __restrict__
 }
 
 // Longest token row (K plus V, in 16-byte pieces) the kernel takes: the
-// reciprocal multiply that splits piece indices is exact up to here.
+// reciprocal multiply that splits piece indices is exact for i < kGatherTok * P
+// while kGatherTok * P^2 < 2^32.
 constexpr int kGatherMaxPieces = 11584;
+static_assert((unsigned long long)kGatherTok * kGatherMaxPieces * kGatherMaxPieces < (1ull << 32),
+              "piece split exact");
 
 hipError_t launch_gather(const void* key_cache, const void* value_cache, int num_blocks,
                          int block_size, int k_row_bytes, int v_row_bytes,
@@ -271,7 +281,7 @@ hipError_t launch_gather(const void* key_cache, const void* value_cache, int num
   const int kp = k_row_bytes / 16, vp = v_row_bytes / 16;
   const int P = kp + vp;
   if (P > kGatherMaxPieces) return hipErrorNotSupported;
-  // ceil(2^32 / P): exact i / P for every i < kGatherTok * P when P <= 11584
+  // ceil(2^32 / P): exact i / P for every i < kGatherTok * P when P <= kGatherMaxPieces
   const uint32_t magic = (uint32_t)(((1ull << 32) + (uint64_t)P - 1) / (uint64_t)P);
   const int grid = (total_tokens + kGatherTok - 1) / kGatherTok;
   hipLaunchKernelGGL(gather_kernel, dim3(grid), dim3(256), 0, stream,
