@@ -297,9 +297,10 @@ struct E2M1Rows {                          // half a byte per element, element 2
 //
 // The same pass serves the FP4 cache (Fmt = E2M1Rows, 4-byte loads).  With
 // kAppend (decode_step_static_fp8 / _fp4) the split that owns p = write_pos[b]
-// first quantises the new token's K and V rows (as kv_append_fp8 / kv_append_fp4
-// do) in the lanes that later consume row p; they store codes and scales and keep
-// both in registers for that row, and p is attended whatever its mask entry says.
+// quantises the new token's K and V rows (as kv_append_fp8 / kv_append_fp4 do) in
+// the lanes that later consume row p, once their first loads are issued; they
+// store codes and scales and keep both in registers for that row, and p is
+// attended whatever its mask entry says.
 // Occupancy: at one or two steps the kernel fits 7 waves per SIMD (<= 72 VGPRs);
 // left to itself the append variant takes 73 and drops to 6 (the fused batch-8
 // call measured 32.8 us at 6 waves, 31.4 us at 7).
@@ -351,42 +352,55 @@ static_decode_lowbit_kernel(const float* __restrict__ q, uint8_t* __restrict__ k
     for (int k = 0; k < kBallots; ++k) mv[k] = mrow[min(r0 + 64 * k + lane, cap - 1)];
   }
   const bool report = split == 0 && h == 0 && threadIdx.x == 0;
-  // the appended row's codes and scales, in the lanes that own it
+  // the appended row's codes and scales, in the lanes that own it.  E4M3: its bf16
+  // rows are loaded here but quantised and stored only once this wave's first
+  // code loads are in flight (the row enters the attention from registers, so
+  // nothing waits for those stores): the owning splits are the last ones of their
+  // heads, dispatched late, and the quantiser ahead of their loads cost the fused
+  // batch-8 step 2% (977 against 958 us per step).  E2M1 quantises at once (late,
+  // its step measured 1% slower).
+  constexpr bool kLate = Fmt::kRowDiv == 1;
   float new_ks = 0.f, new_vs = 0.f;
   Word new_kw{}, new_vw{};
+  bool owner = false;
+  uint4 kn{}, vn{};
+  auto append = [&]() {
+    float kx[8], vx[8];
+    unpack8(kn, kx);
+    unpack8(vn, vx);
+    float ka = 0.f, va = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      ka = fmaxf(ka, fabsf(kx[i]));
+      va = fmaxf(va, fabsf(vx[i]));
+    }
+    ka = group_max<LPR>(ka);
+    va = group_max<LPR>(va);
+    const int ke = Fmt::exponent_for(ka), ve = Fmt::exponent_for(va);
+    const Word kw = Fmt::quantise8(kx, ke), vw = Fmt::quantise8(vx, ve);
+    const size_t at = (((size_t)bh * cap + p) * D + (size_t)sub * 8) / Fmt::kRowDiv;
+    *reinterpret_cast<Word*>(k_codes + at) = kw;
+    *reinterpret_cast<Word*>(v_codes + at) = vw;
+    new_kw = kw;
+    new_vw = vw;
+    new_ks = ldexpf(1.f, ke);
+    new_vs = ldexpf(1.f, ve);
+    if (sub == 0) {
+      k_scale[(size_t)bh * cap + p] = new_ks;
+      v_scale[(size_t)bh * cap + p] = new_vs;
+    }
+  };
   if constexpr (kAppend) {
     if (p < 0 || p >= cap) {
       if (report) raise_flag(err_flag, 2);
       p = -1;
     } else if (p / chunk == split) {
       const int o = p - r0;
-      if (wave == (o / RPW) % kWaves && slot == o % RPW) {
-        const uint4 kn = load16(k_new + (size_t)bh * D + sub * 8);
-        const uint4 vn = load16(v_new + (size_t)bh * D + sub * 8);
-        float kx[8], vx[8];
-        unpack8(kn, kx);
-        unpack8(vn, vx);
-        float ka = 0.f, va = 0.f;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          ka = fmaxf(ka, fabsf(kx[i]));
-          va = fmaxf(va, fabsf(vx[i]));
-        }
-        ka = group_max<LPR>(ka);
-        va = group_max<LPR>(va);
-        const int ke = Fmt::exponent_for(ka), ve = Fmt::exponent_for(va);
-        const Word kw = Fmt::quantise8(kx, ke), vw = Fmt::quantise8(vx, ve);
-        const size_t at = (((size_t)bh * cap + p) * D + (size_t)sub * 8) / Fmt::kRowDiv;
-        *reinterpret_cast<Word*>(k_codes + at) = kw;
-        *reinterpret_cast<Word*>(v_codes + at) = vw;
-        new_kw = kw;
-        new_vw = vw;
-        new_ks = ldexpf(1.f, ke);
-        new_vs = ldexpf(1.f, ve);
-        if (sub == 0) {
-          k_scale[(size_t)bh * cap + p] = new_ks;
-          v_scale[(size_t)bh * cap + p] = new_vs;
-        }
+      owner = wave == (o / RPW) % kWaves && slot == o % RPW;
+      if (owner) {
+        kn = load16(k_new + (size_t)bh * D + sub * 8);
+        vn = load16(v_new + (size_t)bh * D + sub * 8);
+        if constexpr (!kLate) append();
       }
       if (mask && h == 0 && threadIdx.x == 0) mask[(size_t)b * cap + p] = 1;
     } else {
@@ -399,7 +413,10 @@ static_decode_lowbit_kernel(const float* __restrict__ q, uint8_t* __restrict__ k
     L = L < 0 ? 0 : cap;
   }
   const int n = L > 0 ? (L + chunk - 1) / chunk : 1;
-  if (split >= n) return;
+  if (split >= n) {
+    if (kAppend && kLate && owner) append();  // a row past the attended ones is still stored
+    return;
+  }
   // scales of the split's rows (row p's, if this split stores it, is taken from the
   // quantiser below, not from memory)
   float ksv[kBallots], vsv[kBallots];
@@ -497,6 +514,9 @@ static_decode_lowbit_kernel(const float* __restrict__ q, uint8_t* __restrict__ k
   Word kw[2][U], vw[2][U];
   bool ok[2][U];
   issue(0, kw[0], vw[0], ok[0]);
+  if constexpr (kAppend && kLate) {
+    if (owner) append();  // the first step's loads are in flight
+  }
 #pragma unroll
   for (int s = 0; s < kSteps; ++s) {
     if (s + 1 < kSteps) issue(s + 1, kw[(s + 1) & 1], vw[(s + 1) & 1], ok[(s + 1) & 1]);
