@@ -29,11 +29,13 @@ namespace dakv {
 // A split is kSteps steps of U rows per lane group (chunk rows).  Workgroups are
 // numbered split-major (all units' first splits, then all second splits, ...).
 //
-// Appending: the split that owns position p = write_pos[b] stores the new K/V row
-// with exactly the lanes that later load that row's pieces, so the ordinary load
-// returns the stored values (a lane's load after its own store to the same
-// address); p is attended whatever its mask entry says (the append sets it), and
-// the mask bit is written once per sequence.
+// Appending: in the split that owns position p = write_pos[b], the lanes that
+// later load that row's pieces load the new K/V row at the start and use it in
+// place of what their load of row p returns (the old contents); they store it to
+// the cache after the row loop, so the owning split (the last of its head,
+// dispatched late) issues its row loads without waiting for the new row.  p is
+// attended whatever its mask entry says (the append sets it), and the mask bit is
+// written once per sequence.
 template <int D, int U, int kSteps, bool kAppend>
 __global__ void __launch_bounds__(kThreads)
 static_decode_kernel(const float* __restrict__ q, uint16_t* __restrict__ k_cache,
@@ -70,29 +72,39 @@ static_decode_kernel(const float* __restrict__ q, uint16_t* __restrict__ k_cache
     for (int k = 0; k < kBallots; ++k) mv[k] = mrow[min(r0 + 64 * k + lane, cap - 1)];
   }
   const bool report = split == 0 && h == 0 && threadIdx.x == 0;
+  bool owner = false;  // this lane loads a piece of row p in the loop below
+  uint4 kn{}, vn{};
   if constexpr (kAppend) {
     if (p < 0 || p >= cap) {
       if (report) raise_flag(err_flag, 2);
       p = -1;
     } else if (p / chunk == split) {
       const int o = p - r0;  // the lanes of (wave, slot) below load row p in the loop
-      if (wave == (o / RPW) % kWaves && slot == o % RPW) {
-        const size_t at = ((size_t)bh * cap + p) * D + (size_t)sub * 8;
-        store16(k_cache + at, load16(k_new + (size_t)bh * D + sub * 8));
-        store16(v_cache + at, load16(v_new + (size_t)bh * D + sub * 8));
+      owner = wave == (o / RPW) % kWaves && slot == o % RPW;
+      if (owner) {
+        kn = load16(k_new + (size_t)bh * D + sub * 8);
+        vn = load16(v_new + (size_t)bh * D + sub * 8);
       }
       if (mrow && h == 0 && threadIdx.x == 0) mask[(size_t)b * cap + p] = 1;
     } else {
       p = -1;  // another split holds the new row
     }
   }
+  auto store_new = [&]() {
+    const size_t at = ((size_t)bh * cap + p) * D + (size_t)sub * 8;
+    store16(k_cache + at, kn);
+    store16(v_cache + at, vn);
+  };
   int L = Lraw;
   if (L < 0 || L > cap) {
     if (report) raise_flag(err_flag, 16);
     L = L < 0 ? 0 : cap;
   }
   const int n = L > 0 ? (L + chunk - 1) / chunk : 1;
-  if (split >= n) return;
+  if (split >= n) {
+    if (kAppend && owner) store_new();  // a row past the attended ones is still stored
+    return;
+  }
   const int r1 = min(r0 + chunk, L);
   float qr[1][8];
   qr[0][0] = qa.x * scale_log2; qr[0][1] = qa.y * scale_log2;
@@ -112,9 +124,16 @@ static_decode_kernel(const float* __restrict__ q, uint16_t* __restrict__ k_cache
     ok = ok && (((bits[o >> 6] >> (o & 63)) & 1ull) || t == p);
     return ok ? (uint32_t)t * (D * 2) + lane_off : BufferRows::kNoRow;
   };
+  auto patch = [&](int t, uint4& kr, uint4& vr) {
+    if (kAppend && t == p) {  // only the owning lanes meet row p
+      kr = kn;
+      vr = vn;
+    }
+  };
   HeadState<1> st;
   init_state(st);
-  attend_rows_fixed<D, 1, U, kSteps>(rows, qr, r0, r1, wave, slot, row_at, NoPatch{}, st);
+  attend_rows_fixed<D, 1, U, kSteps>(rows, qr, r0, r1, wave, slot, row_at, patch, st);
+  if (kAppend && owner) store_new();
   merge_groups<LPR, 1>(st);
   finish_split<D, 1>(st, lane, wave, ws, (size_t)bh, split, n, max_splits, out, lse);
 }

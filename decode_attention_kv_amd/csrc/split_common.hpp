@@ -2,7 +2,9 @@
 // launch shape, online-softmax state and its in-wave merge, the branch-free row
 // loaders, the workspace of split partials, the log-sum-exp merge of one head,
 // and the end of a split (waves combined through LDS, then the output or the
-// split's partial written).
+// split's partial written).  Every multiply-add here is an explicit fmaf, so that
+// each kernel instantiation rounds alike whatever the compiler would contract
+// (the fused append + attend step is bit-identical to the two separate calls).
 #pragma once
 
 #include "device.hpp"
@@ -86,11 +88,11 @@ __device__ __forceinline__ void merge_groups(HeadState<G, E>& st) {
       const float Ms = M == kNegInf ? 0.f : M;
       const float ws = exp2_fast(st.m[j] - Ms);
       const float wo = exp2_fast(mo - Ms);
-      st.l[j] = st.l[j] * ws + lo * wo;
+      st.l[j] = fmaf(st.l[j], ws, lo * wo);
 #pragma unroll
       for (int i = 0; i < E; ++i) {
         const float oo = __shfl_xor(st.o[j][i], off);
-        st.o[j][i] = st.o[j][i] * ws + oo * wo;
+        st.o[j][i] = fmaf(st.o[j][i], ws, oo * wo);
       }
       st.m[j] = M;
     }
@@ -148,11 +150,11 @@ struct GlobalRows {
 
 // One loop step's loads: U rows per lane group, K and V.  RowAt(t, ok) returns
 // the loader offset of row t (or the loader's "no row" value) and clears ok for
-// rows that must not be used; Patch(t, kr, vr) may then replace a row's values.
-template <int D, int U, typename Rows, typename RowAt, typename Patch>
+// rows that must not be used.
+template <int D, int U, typename Rows, typename RowAt>
 __device__ __forceinline__ void issue_rows(const Rows& rows, int base, int r1, int wave,
-                                           int slot, RowAt& row_at, Patch& patch,
-                                           uint4 (&kr)[U], uint4 (&vr)[U], bool (&ok)[U]) {
+                                           int slot, RowAt& row_at, uint4 (&kr)[U],
+                                           uint4 (&vr)[U], bool (&ok)[U]) {
   constexpr int RPW = 64 / (D / 8);
 #pragma unroll
   for (int u = 0; u < U; ++u) {
@@ -160,7 +162,6 @@ __device__ __forceinline__ void issue_rows(const Rows& rows, int base, int r1, i
     ok[u] = t < r1;
     const auto off = row_at(t, ok[u]);
     rows.load(off, ok[u], kr[u], vr[u]);
-    patch(t, kr[u], vr[u]);
   }
 }
 
@@ -203,7 +204,7 @@ __device__ __forceinline__ void consume_rows(const float (&q)[G][8], const uint4
       p[u] = exp2_fast(s[j][u] - ms);
       psum += p[u];
     }
-    st.l[j] = st.l[j] * alpha + psum;
+    st.l[j] = fmaf(st.l[j], alpha, psum);
 #pragma unroll
     for (int i = 0; i < 8; ++i) st.o[j][i] *= alpha;
     st.m[j] = mnew;
@@ -222,7 +223,9 @@ __device__ __forceinline__ void consume_rows(const float (&q)[G][8], const uint4
 // (U rows per lane group, K and V) before using any; the steps are fully unrolled
 // with two register sets used in turn, so the loads of step s+1 are in flight
 // while step s is computed and, with no loop, the compiler waits on exactly the
-// loads each step needs.  q is pre-scaled by scale * log2(e).
+// loads each step needs.  q is pre-scaled by scale * log2(e).  Patch(t, kr, vr)
+// may replace row t's values when its step is computed (after its loads have
+// arrived, so a replacement never makes the issue wait).
 template <int D, int G, int U, int kSteps, typename Rows, typename RowAt, typename Patch>
 __device__ __forceinline__ void attend_rows_fixed(const Rows& rows, const float (&q)[G][8],
                                                   int r0, int r1, int wave, int slot,
@@ -231,12 +234,15 @@ __device__ __forceinline__ void attend_rows_fixed(const Rows& rows, const float 
   constexpr int kStep = kWaves * RPW * U;
   uint4 kr[2][U], vr[2][U];
   bool ok[2][U];
-  issue_rows<D, U>(rows, r0, r1, wave, slot, row_at, patch, kr[0], vr[0], ok[0]);
+  issue_rows<D, U>(rows, r0, r1, wave, slot, row_at, kr[0], vr[0], ok[0]);
 #pragma unroll
   for (int s = 0; s < kSteps; ++s) {
     if (s + 1 < kSteps)
-      issue_rows<D, U>(rows, r0 + (s + 1) * kStep, r1, wave, slot, row_at, patch,
+      issue_rows<D, U>(rows, r0 + (s + 1) * kStep, r1, wave, slot, row_at,
                        kr[(s + 1) & 1], vr[(s + 1) & 1], ok[(s + 1) & 1]);
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      patch(r0 + s * kStep + (u * kWaves + wave) * RPW + slot, kr[s & 1][u], vr[s & 1][u]);
     consume_rows<D, G, U>(q, kr[s & 1], vr[s & 1], ok[s & 1], st);
   }
 }
@@ -299,7 +305,8 @@ __device__ __forceinline__ void merge_head(const float* __restrict__ lp,
   for (int k = 0; k < kMergePre; ++k) {
     const int j = grp + k * kGroups;
     const float wj = j < n ? sm_w[j] : 0.f;
-    acc.x += wj * pre[k].x; acc.y += wj * pre[k].y; acc.z += wj * pre[k].z; acc.w += wj * pre[k].w;
+    acc.x = fmaf(wj, pre[k].x, acc.x); acc.y = fmaf(wj, pre[k].y, acc.y);
+    acc.z = fmaf(wj, pre[k].z, acc.z); acc.w = fmaf(wj, pre[k].w, acc.w);
   }
   // more splits than the prefetch covers: kMergePre partials per thread at a time,
   // all loads of a batch issued before its first use
@@ -315,7 +322,8 @@ __device__ __forceinline__ void merge_head(const float* __restrict__ lp,
     for (int k = 0; k < kMergePre; ++k) {
       const int j = j0 + k * kGroups;
       const float wj = j < n ? sm_w[j] : 0.f;
-      acc.x += wj * y[k].x; acc.y += wj * y[k].y; acc.z += wj * y[k].z; acc.w += wj * y[k].w;
+      acc.x = fmaf(wj, y[k].x, acc.x); acc.y = fmaf(wj, y[k].y, acc.y);
+      acc.z = fmaf(wj, y[k].z, acc.z); acc.w = fmaf(wj, y[k].w, acc.w);
     }
   }
   sm_red[tid] = acc;
@@ -375,8 +383,8 @@ __device__ __forceinline__ void finish_split(const HeadState<G, E>& st, int lane
 #pragma unroll
       for (int w = 0; w < kWaves; ++w) {
         const float wt = exp2_fast(sm_m[w][j] - M);
-        num += wt * sm_o[w][j][d];
-        den += wt * sm_l[w][j];
+        num = fmaf(wt, sm_o[w][j][d], num);
+        den = fmaf(wt, sm_l[w][j], den);
       }
       val = num / den;
       lse2 = M + __log2f(den);
@@ -444,8 +452,8 @@ __device__ __forceinline__ void finish_split_rows(const HeadState<G>& st, int gi
       for (int s = 0; s < ts; ++s) {
         const int g2 = h + s * Hkv;
         const float wt = exp2_fast(sm_m[g2][j] - M);
-        num += wt * sm_o[g2][j][d];
-        den += wt * sm_l[g2][j];
+        num = fmaf(wt, sm_o[g2][j][d], num);
+        den = fmaf(wt, sm_l[g2][j], den);
       }
       val = num / den;
       lse2 = M + __log2f(den);
