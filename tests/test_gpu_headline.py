@@ -11,8 +11,9 @@ and its Part 4 (the same command list replayed every token).
 
 Checked: every replay bit-identical to the eager fused step; the fused step
 bit-identical to the two calls kv_append + decode_attn_static on the same state;
-sampled (layer, sequence) pairs against oracle.kv_append followed by
-oracle.decode_static on the pre-step state; rows other than L - 1 untouched.  The FP8
+every sequence of the first and last layers (and two more pairs) against
+oracle.kv_append followed by oracle.decode_static on the pre-step state; rows other
+than L - 1 untouched.  The FP8
 and FP4 caches run the same check with their fused step at the same shape (4 layers).
 """
 
@@ -45,10 +46,12 @@ def capture(fn):
 
 
 def sampled_pairs(n_layers, lengths, seed):
+    """Every sequence of the first and the last layer, the longest one in the middle
+    layer, and one more drawn pair."""
     rng = np.random.default_rng(seed)
     longest = int(np.argmax(lengths))
-    pairs = {(0, 0), (n_layers - 1, B - 1), (n_layers // 2, longest),
-             (int(rng.integers(0, n_layers)), int(rng.integers(0, B)))}
+    pairs = {(0, b) for b in range(B)} | {(n_layers - 1, b) for b in range(B)}
+    pairs |= {(n_layers // 2, longest), (int(rng.integers(0, n_layers)), int(rng.integers(0, B)))}
     return sorted(pairs)
 
 

@@ -223,17 +223,15 @@ def test_paged_bad_block_id_is_flagged():
     assert_attention_close(out[0], ref[0])
 
 
-def test_paged_gqa_full_size_sampled():
+def test_paged_gqa_full_size_every_sequence():
     """Batch 64, 32/8 heads, block 16, contexts log-uniform on [512, 16384]; every
-    output of 6 sampled sequences against the oracle."""
+    output of every sequence against the oracle."""
     print("paged full size", flush=True)
     case = workloads.paged_gqa(device=DEV, seed=4)
     out, lse = run_paged(case)
     kc, vc, qb = bits(case.key_cache), bits(case.value_cache), bits(case.q)
     idx = case.index
-    rng = np.random.default_rng(75)
-    longest = int(np.argmax(idx.lengths))
-    for b in sorted({0, 63, longest, *rng.integers(1, 63, size=3).tolist()}):
+    for b in range(64):
         L = idx.lengths[b]
         ref_out, ref_lse = oracle.decode_paged(qb[b:b + 1], kc, vc, idx.block_tables[b:b + 1],
                                                np.array([0, L], dtype=np.int32), None,

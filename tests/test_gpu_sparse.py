@@ -87,13 +87,13 @@ def test_sparse_out_of_range_index_is_flagged_and_skipped():
         dakv.validate_sparse(idx, 200)
 
 
-def test_sparse_mla_full_size_sampled():
+def test_sparse_mla_full_size_every_sequence():
     """Batch 16, 128 heads, d_qk 576 / d_v 512, context 32768, top-2048: every output of
-    three sequences against the oracle."""
+    every sequence against the oracle."""
     print("sparse full size", flush=True)
     case = workloads.sparse_mla(device=DEV, seed=5)
     out, lse = run(case)
-    for b in (0, 7, 15):
+    for b in range(16):
         r_out, r_lse = ref(case, rows=slice(b, b + 1))
         assert_attention_close(out[b:b + 1], r_out)
         assert_lse_close(lse[b:b + 1], r_lse)
