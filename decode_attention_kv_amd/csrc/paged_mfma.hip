@@ -76,12 +76,21 @@ struct PmShape {
   static constexpr int LW = CH / 512 >= 16 ? 16 : CH / 512;
   static constexpr int HalfLoads = CH / (512 * LW);     // lane loads of K (and V) codes
   static constexpr int Elems = LW * 8 / Bits;           // elements of one lane load
-  static constexpr int Loads = 2 * HalfLoads * (Coded ? 2 : 1);  // per wave and tile
+  // Scales of a coded pool: with two or more code loads per half (FP8 at 8 heads), one
+  // load per half fetches the ScaleEntries (token row, head) entries the wave's code
+  // loads touch and each lane takes its own with a cross-lane read; otherwise (E2M1:
+  // one code load per half, where that saves no load but costs registers) every code
+  // load has its own scale load.  Lane loads of a tile, per wave:
+  static constexpr int ScaleEntries = HalfLoads * 64 * LW / CB;
+  static constexpr bool SharedScales = Coded && HalfLoads >= 2;
+  static constexpr int ScaleRegs = !Coded ? 1 : (SharedScales ? 2 : 2 * HalfLoads);
+  static constexpr int Loads = 2 * HalfLoads + (!Coded ? 0 : (SharedScales ? 2 : 2 * HalfLoads));
   static constexpr int Ahead =                                  // tiles loaded ahead
       Coded ? (GH == 8 ? (Bits == 8 ? 3 : 6) : 4) : (GH == 8 ? 2 : 4);
   static constexpr int Blocks = 128 / 16 / (kPmWaves / GH);   // dim blocks of a wave
   static_assert(LW >= 4 && CH % (512 * LW) == 0, "whole lane loads per half tile");
   static_assert(CB % LW == 0, "a lane load stays inside one head's row");
+  static_assert(!SharedScales || ScaleEntries <= 64, "one scale per lane");
 };
 
 typedef uint32_t pm_u32x2_t __attribute__((ext_vector_type(2)));
@@ -299,10 +308,11 @@ paged_mfma_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ ke
   int mq = 0;                      // where it goes
 
   // a tile in registers: K codes, V codes (lane load k of each), and for a coded
-  // pool the scales of the rows those loads hit
+  // pool the scales: shared, lane j holding entry j of the wave's ScaleEntries (s[0]
+  // for K, s[1] for V); else the scale of each code load (s[k], s[HalfLoads + k])
   struct TileRegs {
     u32x4_t c[2 * S::HalfLoads];
-    float s[2 * S::HalfLoads];
+    float s[S::ScaleRegs];
   };
   // Loads of the next tile on the load side: wave load I = HalfLoads wave + k of the
   // K half (and of the V half) covers pool bytes [64 LW I, 64 LW (I + 1)) of the
@@ -355,13 +365,28 @@ paged_mfma_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ ke
       const uint32_t off = in ? (uint32_t)(srow * S::CB + cbr) : kPmNoRow;
       r.c[k] = pm_load<S::LW>(kr, off);
       r.c[S::HalfLoads + k] = pm_load<S::LW>(vr, off);
-      if constexpr (S::Coded) {
+      if constexpr (S::Coded && !S::SharedScales) {
         const uint32_t so = in ? (uint32_t)((srow + cbr / S::CB) * 4) : kPmNoRow;
         r.s[k] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(ksr, (int)so, 0,
                                                                       kLoadNonTemporal));
         r.s[S::HalfLoads + k] = __uint_as_float(
             __builtin_amdgcn_raw_buffer_load_b32(vsr, (int)so, 0, kLoadNonTemporal));
       }
+    }
+    if constexpr (S::SharedScales) {
+      // the scales: one load per half, lane j taking entry e0 + j (token row e / GH,
+      // head e % GH of the group); the loads above hit ScaleEntries entries in all,
+      // each shared by CB / LW lanes, so this replaces a scale load per code load
+      // (measured: the per-load scale loads cost as much as the code loads)
+      const int e = 64 * S::LW * wave * S::HalfLoads / S::CB + lane;
+      const int tok = tok0 + e / GH;
+      const bool in = lane < S::ScaleEntries && tok < ld.r1;
+      const uint32_t so =
+          in ? (uint32_t)((((tok & bs_mask) * Hkv + GH * ld.hg + e % GH)) * 4) : kPmNoRow;
+      r.s[0] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(ksr, (int)so, 0,
+                                                                    kLoadNonTemporal));
+      r.s[1] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(vsr, (int)so, 0,
+                                                                    kLoadNonTemporal));
     }
     if (++ld_t == ld.steps) {
       ld = item_of(ld.idx + W);
@@ -385,12 +410,20 @@ paged_mfma_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ ke
         *reinterpret_cast<u32x4_t*>(dst + at) = r.c[k];
         *reinterpret_cast<u32x4_t*>(dst + S::Half + at) = r.c[S::HalfLoads + k];
       } else {
-        // the load's first element as a byte offset into the bf16 row
+        // the load's first element as a byte offset into the bf16 row; with shared
+        // scales its scale is entry (LW (lane + 64 k)) / CB of the wave's, held by
+        // that lane
         const int at = (cbr / S::CB) * 256 + (cbr % S::CB) * (16 / Bits);
+        const int src = (S::LW * (lane + 64 * k)) / S::CB;
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
           uint32_t w[S::Elems / 2];
-          pm_dequant<Bits, S::LW>(r.c[h * S::HalfLoads + k], r.s[h * S::HalfLoads + k], w);
+          float sc;
+          if constexpr (S::SharedScales)
+            sc = __int_as_float(__builtin_amdgcn_ds_bpermute(src * 4, __float_as_int(r.s[h])));
+          else
+            sc = r.s[h * S::HalfLoads + k];
+          pm_dequant<Bits, S::LW>(r.c[h * S::HalfLoads + k], sc, w);
           uint8_t* rowp = dst + h * S::Half + row * S::RB;
           if constexpr (S::Elems >= 8) {
 #pragma unroll
