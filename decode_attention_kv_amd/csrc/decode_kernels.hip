@@ -12,7 +12,9 @@
 // set are never loaded.  For grouped-query attention each loaded K/V row serves
 // all G query heads of its KV head.
 //
-// End of a split: the groups of a wave merge through cross-lane shuffles, the 4
+// End of a split: in the static kernel every lane group's state goes to LDS and
+// each output element combines all 16 of them after one barrier; in the paged
+// kernels the groups of a wave merge through cross-lane shuffles first, the 4
 // waves through LDS.  A sequence that fits one split writes out = o / l directly.
 // Otherwise each split stores its normalised partial o / l and log2-sum-exp in the
 // workspace and merge_kernel combines them (weights 2^(lse_j - max)).  (Merging in
@@ -134,8 +136,7 @@ static_decode_kernel(const float* __restrict__ q, uint16_t* __restrict__ k_cache
   init_state(st);
   attend_rows_fixed<D, 1, U, kSteps>(rows, qr, r0, r1, wave, slot, row_at, patch, st);
   if (kAppend && owner) store_new();
-  merge_groups<LPR, 1>(st);
-  finish_split<D, 1>(st, lane, wave, ws, (size_t)bh, split, n, max_splits, out, lse);
+  finish_split_flat<D>(st, lane, wave, ws, (size_t)bh, split, n, max_splits, out, lse);
 }
 
 // ------------------------------------------------------------------ paged layout

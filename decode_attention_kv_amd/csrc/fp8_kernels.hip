@@ -527,8 +527,7 @@ static_decode_lowbit_kernel(const float* __restrict__ q, uint8_t* __restrict__ k
   st.l[0] = l;
 #pragma unroll
   for (int i = 0; i < 8; ++i) st.o[0][i] = o[i];
-  merge_groups<LPR, 1>(st);
-  finish_split<D, 1>(st, lane, wave, ws, (size_t)bh, split, n, max_splits, out, lse);
+  finish_split_flat<D>(st, lane, wave, ws, (size_t)bh, split, n, max_splits, out, lse);
 }
 
 template <typename Fmt, int D, int kSteps>

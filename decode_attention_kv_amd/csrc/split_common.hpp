@@ -345,6 +345,57 @@ __device__ __forceinline__ void merge_head(const float* __restrict__ lp,
   __syncthreads();
 }
 
+// End of a split without the in-wave merge: every lane group's state (kWaves x RPW
+// of them, RPW = 64 / (D / E) per wave) goes to LDS at once and each output element
+// combines all of them after one barrier.  (The in-wave merge first took two rounds of
+// cross-lane exchanges, each waiting on the previous.)
+template <int D, int E>
+__device__ __forceinline__ void finish_split_flat(const HeadState<1, E>& st, int lane, int wave,
+                                                  const Workspace& ws, size_t head0, int split,
+                                                  int n, int max_splits, float* __restrict__ out,
+                                                  float* __restrict__ lse) {
+  constexpr int LPR = D / E;
+  constexpr int RPW = 64 / LPR;
+  constexpr int NS = kWaves * RPW;  // lane groups of the workgroup
+  __shared__ float sm_o[NS][D];
+  __shared__ float sm_m[NS];
+  __shared__ float sm_l[NS];
+  const int g = wave * RPW + lane / LPR;
+  const int sub = lane % LPR;
+#pragma unroll
+  for (int i = 0; i < E; ++i) sm_o[g][sub * E + i] = st.o[0][i];
+  if (sub == 0) {
+    sm_m[g] = st.m[0];
+    sm_l[g] = st.l[0];
+  }
+  __syncthreads();
+  for (int d = threadIdx.x; d < D; d += kThreads) {
+    float M = kNegInf;
+#pragma unroll
+    for (int k = 0; k < NS; ++k) M = fmaxf(M, sm_m[k]);
+    float val = 0.f, lse2 = kNegInf;
+    if (M != kNegInf) {
+      float num = 0.f, den = 0.f;
+#pragma unroll
+      for (int k = 0; k < NS; ++k) {
+        const float wt = exp2_fast(sm_m[k] - M);
+        num = fmaf(wt, sm_o[k][d], num);
+        den = fmaf(wt, sm_l[k], den);
+      }
+      val = num / den;
+      lse2 = M + __log2f(den);
+    }
+    if (n == 1) {
+      out[head0 * D + d] = val;
+      if (lse && d == 0) lse[head0] = lse2 * kLn2;
+    } else {
+      const size_t row = head0 * max_splits + split;
+      ws.o[row * D + d] = val;
+      if (d == 0) ws.lse[row] = lse2;
+    }
+  }
+}
+
 // End of a split: combine the waves through LDS, then write the output directly
 // (a sequence that fits one split) or this split's partial for merge_kernel.
 // (The splits are not merged in the last one to finish: publishing the partials
