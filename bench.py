@@ -609,11 +609,30 @@ def ceilings(torch):
     del a, f, sink
     torch.cuda.empty_cache()
     props = torch.cuda.get_device_properties(0)
+    clocks = device_clocks()
     return {"d2d_copy_GBps": round(2 * n / (copy["median"] * 1e-3) / 1e9, 1),
             "read_sum_GBps": round(n / (read["median"] * 1e-3) / 1e9, 1),
             "device": getattr(props, "name", ""), "arch": getattr(props, "gcnArchName", ""),
             "compute_units": getattr(props, "multi_processor_count", None),
-            "hbm_bytes": getattr(props, "total_memory", None)}
+            "hbm_bytes": getattr(props, "total_memory", None), **clocks}
+
+
+def device_clocks():
+    """Peak engine and memory clocks (MHz) and the memory bus width of device 0, as the
+    HIP runtime reports them (hipDeviceGetAttribute), for the record; None where the
+    runtime library cannot be opened."""
+    import ctypes
+    attrs = {"sclk_peak_MHz": 5, "mclk_peak_MHz": 60, "memory_bus_bits": 59}
+    try:
+        hip = ctypes.CDLL("libamdhip64.so")
+    except OSError:
+        return {k: None for k in attrs}
+    out = {}
+    for key, attr in attrs.items():
+        v = ctypes.c_int(0)
+        ok = hip.hipDeviceGetAttribute(ctypes.byref(v), ctypes.c_int(attr), ctypes.c_int(0)) == 0
+        out[key] = (v.value // 1000 if key.endswith("MHz") else v.value) if ok else None
+    return out
 
 
 def paged_leg(torch, dakv, workloads, acc, counter_pass=False):
