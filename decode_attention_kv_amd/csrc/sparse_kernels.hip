@@ -14,12 +14,12 @@
 // are 16 heads x 128 dims and two waves fit each SIMD.
 //   * Rows are gathered by direct-to-LDS buffer loads (16 bytes per lane, no
 //     registers) into two tile buffers: tile it + 1 is in flight while tile it is
-//     computed.  A tile is 64 unpadded 1152-byte rows; the 16-byte pieces of row
-//     r are stored in a permuted order (the piece's low 3 bits XOR (r / 2) % 8).
-//     On this chip's LDS, which serves 32 lanes of a 16-byte read per pass from
-//     512-byte bank rows (measured), that puts the 32 pieces each pass reads
-//     (16 rows x an aligned pair of pieces, for both read patterns below) in
-//     distinct banks.
+//     computed, its loads issued in three parts over tile it.  A tile is 64 unpadded
+//     1152-byte rows; the 16-byte pieces of row r are stored in a permuted order
+//     (the piece's low 3 bits XOR (r / 2) % 8). On this chip's LDS, which serves 32
+//     lanes of a 16-byte read per pass from 512-byte bank rows (measured), that puts
+//     the 32 pieces each pass reads (16 rows x an aligned pair of pieces, for both
+//     read patterns below) in distinct banks.
 //   * S^T[token, head] = G Q^T with v_mfma_f32_16x16x32_bf16: A = the wave's 16
 //     rows x 32 dims from LDS (read a batch of k-steps ahead), B = Q^T of the
 //     wave's 16 heads, held in registers for the whole split (18 k-steps x 16
@@ -68,6 +68,13 @@ constexpr int kHeadsPerWG = 32;
 constexpr int kRowBlock = 16;                           // tile rows one wave scores
 constexpr int kRowBlocks = kTile / kRowBlock;           // 4 waves per head block
 constexpr int kDmaPerWave = kTileBytes / 1024 / kSpWaves;  // 9 wave loads of 1 KiB per tile
+// The next tile's gather is spread over the tile (a wave's loads [0, kGatherTop) at its
+// top, [kGatherTop, kGatherMid) once the scores are in, the rest after the P
+// exchange), so that the rows landing in LDS compete less with the scores' operand
+// reads.  Measured per call (bf16 rows): all at the top 36.5 us; 3 / 6 35.0; 2 / 4 / 3
+// 34.2 (1 / 3 / 5 and 1 / 4 / 4 34.7; 2 / 3 / 4 34.8).
+constexpr int kGatherTop = 2;
+constexpr int kGatherMid = 6;
 constexpr int kKSteps = kDqk / 32;                      // 18
 constexpr int kDimsPerWave = kDv / kRowBlocks;          // 128 output dims per wave
 constexpr int kWaveDimBlocks = kDimsPerWave / 16;       // 8 blocks of 16 dims
@@ -235,10 +242,11 @@ sparse_split_kernel(const uint16_t* __restrict__ q, const void* __restrict__ kv,
   // [1024 I, 1024 I + 1024) of the tile, lane L the 16 bytes at 1024 I + 16 L,
   // i.e. position c = 64 I + L = 72 r + s of row r, which holds piece
   // piece_slot(s, r).  Rows past the split's end load kNoRow offsets (zeros).
-  auto fetch_tile = [&](int ti, uint8_t* dst) {
+  auto fetch_tile = [&](int ti, uint8_t* dst, int k0, int k1) {  // this wave's loads [k0, k1)
     uint32_t off[kDmaPerWave];
 #pragma unroll
     for (int k = 0; k < kDmaPerWave; ++k) {
+      if (k < k0 || k >= k1) continue;
       const int I = wave * kDmaPerWave + k;
       const int c = I * 64 + lane;
       const int r = c / kPieces;
@@ -249,6 +257,7 @@ sparse_split_kernel(const uint16_t* __restrict__ q, const void* __restrict__ kv,
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int k = 0; k < kDmaPerWave; ++k) {
+      if (k < k0 || k >= k1) continue;
       const int I = wave * kDmaPerWave + k;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(kvr, (lds_void*)(dst + I * 1024), 16, (int)off[k],
                                                0, 0, 0);
@@ -321,7 +330,7 @@ sparse_split_kernel(const uint16_t* __restrict__ q, const void* __restrict__ kv,
     }
   };
   if constexpr (kCodes) load_codes(0);
-  else fetch_tile(0, buf0);
+  else fetch_tile(0, buf0, 0, kDmaPerWave);
   // Q^T of the wave's heads as B operands, read from buf1 once its gather is
   // complete: lane -> head head0 + col16 (row hb * 16 + col16 of buf1), dims
   // 32 s + 8 grp .. +8.  All reads are done before tile 1's gather refills buf1.
@@ -391,7 +400,7 @@ sparse_split_kernel(const uint16_t* __restrict__ q, const void* __restrict__ kv,
     asm volatile("" ::: "memory");
     if (it + 1 < ntiles) {
       if constexpr (kCodes) load_codes(it + 1);
-      else fetch_tile(it + 1, N);
+      else fetch_tile(it + 1, N, 0, kGatherTop);
     }
 
     // S^T = G Q^T for the wave's 16 rows over 18 k-steps in three chains; A
@@ -422,6 +431,9 @@ sparse_split_kernel(const uint16_t* __restrict__ q, const void* __restrict__ kv,
                                                           as_bf16x8(qreg[s0 + k]), st[k], 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
       }
+    }
+    if constexpr (!kCodes) {
+      if (it + 1 < ntiles) fetch_tile(it + 1, N, kGatherTop, kGatherMid);
     }
     // scores of this wave's tile rows 16 rb + 4 grp + i for head col16 (-inf for
     // rows past the index list), and their max per head
@@ -496,6 +508,9 @@ sparse_split_kernel(const uint16_t* __restrict__ q, const void* __restrict__ kv,
       lds_barrier();
     }
     lsum += psum;
+    if constexpr (!kCodes) {
+      if (it + 1 < ntiles) fetch_tile(it + 1, N, kGatherMid, kDmaPerWave);
+    }
 
     // O += P V over the tile's 64 rows for dim blocks 8 rb .. 8 rb + 7.  k-step
     // kk: lane group g holds tokens {4g..4g+3} of row blocks 2 kk and 2 kk + 1
