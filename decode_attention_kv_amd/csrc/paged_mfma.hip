@@ -575,13 +575,18 @@ paged_mfma_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ ke
         float* dst = ci.n == 1 ? out + (head0 + j) * D
                                : ws.o + ((head0 + j) * max_splits + ci.split) * D;
         dst += 16 * NB * part + col16;
+        if (ci.n == 1) {
 #pragma unroll
-        for (int jb = 0; jb < NB; ++jb) dst[16 * jb] = oacc[jb][i2] * inv;
+          for (int jb = 0; jb < NB; ++jb) dst[16 * jb] = oacc[jb][i2] * inv;
+        } else {
+#pragma unroll
+          for (int jb = 0; jb < NB; ++jb) store_through(&dst[16 * jb], oacc[jb][i2] * inv);
+        }
         if (part == 0 && col16 == 0) {
           if (ci.n == 1) {
             if (lse) lse[head0 + j] = lse2 * kLn2;
           } else {
-            ws.lse[(head0 + j) * max_splits + ci.split] = lse2;
+            store_through(&ws.lse[(head0 + j) * max_splits + ci.split], lse2);
           }
         }
       }
