@@ -58,7 +58,8 @@ hipError_t launch_kv_append(void* k_cache, void* v_cache, const void* k_new, con
 // (tensor, sequence, head) those rows are len_b * row_bytes contiguous bytes in
 // both buffers (only the capacity strides differ), so the work is a batch of
 // contiguous copies; a workgroup moves one kCopyBytes chunk of one of them with
-// all of its loads issued before the first store (non-temporal both ways).
+// all of its loads issued before the first store (non-temporal loads; stores written
+// through, kStoreThrough).
 // Grid: n * B * H * chunks, chunk fastest; chunks past the copied length exit.
 // ---------------------------------------------------------------------------
 // 4 loads of 16 bytes per thread (16 KiB per workgroup): the 64-tensor, 1 GiB
@@ -99,6 +100,8 @@ copy_kvcache_kernel(CopyTable t, int BH, int H, int src_cap, int dst_cap, int ro
   const int n16 = (int)(min((size_t)kCopyBytes, bytes - start) / 16);
   const uint8_t* src = t.src[i] + (size_t)bh * src_cap * row_bytes + start;
   uint8_t* dst = t.dst[i] + (size_t)bh * dst_cap * row_bytes + start;
+  const __amdgpu_buffer_rsrc_t dr = __builtin_amdgcn_make_buffer_rsrc(dst, (short)0, n16 * 16,
+                                                                      0x00020000);
   gx_u32x4 v[kCopyLoads];
 #pragma unroll
   for (int k = 0; k < kCopyLoads; ++k) {
@@ -108,7 +111,7 @@ copy_kvcache_kernel(CopyTable t, int BH, int H, int src_cap, int dst_cap, int ro
 #pragma unroll
   for (int k = 0; k < kCopyLoads; ++k) {
     const int j = (int)threadIdx.x + 256 * k;
-    if (j < n16) __builtin_nontemporal_store(v[k], reinterpret_cast<gx_u32x4*>(dst) + j);
+    if (j < n16) store16_through(dr, j * 16, make_uint4(v[k][0], v[k][1], v[k][2], v[k][3]));
   }
 }
 
@@ -173,8 +176,9 @@ hipError_t launch_trim_kvcache(int32_t* mask, const int32_t* new_len, int B, int
 // every thread issues kGatherSlots loads before its first store, consecutive
 // threads touch consecutive pieces of a row, and there is no branch per load
 // (pieces past the end re-read the last piece and are not stored; rows with a
-// bad block id are written as zeros).  Loads and stores are non-temporal: each
-// byte moves once.
+// bad block id are written as zeros).  Loads are non-temporal (each byte moves
+// once); stores are written through (kStoreThrough), so the output leaves no dirty
+// lines in the L2s.
 // ---------------------------------------------------------------------------
 // A workgroup takes 3 tokens: at 4 KiB per token (K + V, 8 heads x 128 dims) that
 // is 3 loads per thread, all in flight before the first store, in a small kernel
@@ -239,9 +243,15 @@ gather_kernel(const uint8_t* __restrict__ key_cache, const uint8_t* __restrict__
   const int P = k_pieces + v_pieces;
   const int N = ntok * P;
   const size_t kb = (size_t)k_pieces * 16, vb = (size_t)v_pieces * 16;
+  // the workgroup's output rows of each output, stored through (sc1)
+  const __amdgpu_buffer_rsrc_t rko = __builtin_amdgcn_make_buffer_rsrc(
+      key_out + (size_t)tok0 * kb, (short)0, (int)(ntok * kb), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rvo = __builtin_amdgcn_make_buffer_rsrc(
+      value_out + (size_t)tok0 * vb, (short)0, (int)(ntok * vb), 0x00020000);
   for (int base = 0; base < N; base += 256 * kGatherSlots) {
     gx_u32x4 r[kGatherSlots];
-    uint8_t* dst[kGatherSlots];
+    int doff[kGatherSlots];
+    bool dk[kGatherSlots];
 #pragma unroll
     for (int s = 0; s < kGatherSlots; ++s) {
       const int i = min(base + s * 256 + tid, N - 1);
@@ -249,19 +259,21 @@ gather_kernel(const uint8_t* __restrict__ key_cache, const uint8_t* __restrict__
       const int pc = i - j * P;
       const long long sr = src_row[j];
       const size_t row = sr >= 0 ? (size_t)sr : 0;
-      const size_t o = (size_t)(tok0 + j);
       const bool is_k = pc < k_pieces;
       const uint8_t* src = is_k ? key_cache + row * kb + (size_t)pc * 16
                                 : value_cache + row * vb + (size_t)(pc - k_pieces) * 16;
-      dst[s] = is_k ? key_out + o * kb + (size_t)pc * 16
-                    : value_out + o * vb + (size_t)(pc - k_pieces) * 16;
+      dk[s] = is_k;
+      doff[s] = is_k ? (int)(j * kb) + pc * 16 : (int)(j * vb) + (pc - k_pieces) * 16;
       const gx_u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const gx_u32x4*>(src));
       r[s] = sr >= 0 ? v : gx_u32x4{0u, 0u, 0u, 0u};
     }
 #pragma unroll
     for (int s = 0; s < kGatherSlots; ++s)
-      if (base + s * 256 + tid < N)
-        __builtin_nontemporal_store(r[s], reinterpret_cast<gx_u32x4*>(dst[s]));
+      if (base + s * 256 + tid < N) {
+        const uint4 w = make_uint4(r[s][0], r[s][1], r[s][2], r[s][3]);
+        if (dk[s]) store16_through(rko, doff[s], w);
+        else store16_through(rvo, doff[s], w);
+      }
   }
 }
 

@@ -82,6 +82,18 @@ __device__ __forceinline__ void store_through(float* p, float v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Cache-policy operand of a buffer store written through to the point of coherence
+// (sc1).  A streaming copy that stores this way leaves no dirty lines in the XCD's L2
+// (the paged gather: 87.5 -> 78.6 us per call, 494 MB moved; non-temporal stores, with
+// or without sc1, measured the same as plain ones).
+constexpr int kStoreThrough = 16;
+
+// 16 bytes through a buffer resource with kStoreThrough
+__device__ __forceinline__ void store16_through(__amdgpu_buffer_rsrc_t r, int off, const uint4& v) {
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  __builtin_amdgcn_raw_buffer_store_b128(u32x4{v.x, v.y, v.z, v.w}, r, off, 0, kStoreThrough);
+}
+
 __device__ __forceinline__ uint4 load16(const void* p) {
   return *reinterpret_cast<const uint4*>(p);
 }
