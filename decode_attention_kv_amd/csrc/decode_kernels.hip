@@ -538,7 +538,10 @@ size_t paged_workspace_bytes(int B, int Hq, int D, int max_seq_len, int block_si
   const int least = round_up((max_seq_len + kMaxSplits - 1) / kMaxSplits, unit);
   const int c = least > unit ? least : unit;
   const int splits = max_seq_len > 0 ? (max_seq_len + c - 1) / c : 1;
-  return ws_floats((size_t)B * Hq, splits, D) * sizeof(float);
+  // the matrix-core kernel's pieces: up to one more per head, and a count per
+  // (sequence, head group)
+  return ws_floats((size_t)B * Hq, splits + 1, D) * sizeof(float) +
+         (size_t)B * Hq * sizeof(int32_t);
 }
 
 hipError_t launch_decode_paged(const void* q, const void* key_cache, const void* value_cache,

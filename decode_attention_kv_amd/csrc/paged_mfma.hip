@@ -1,7 +1,7 @@
 // Paged GQA decode on the matrix cores, for 2, 4 or a multiple of 8 KV heads.
 //
-// Work split: one workgroup (8 waves) per (sequence, split, group of GH = min(Hkv,
-// 8) KV heads); wave w serves KV head w % GH of the group and 16 GH of the 128
+// Work split: a workgroup (8 waves) works on a group of GH = min(Hkv, 8) KV heads
+// of one sequence at a time; wave w serves KV head w % GH of the group and 16 GH of the 128
 // output dims (part w / GH) of its G query heads.  The group's GH x 256 bytes of
 // each token row (K, and likewise V) are contiguous in the pool -- a whole token
 // row at Hkv <= 8, read at once, which keeps the HBM accesses of a row together
@@ -28,12 +28,17 @@
 // LDS rows are 512 bytes; piece p (16 bytes) of token row t is stored at p XOR
 // ((t % 16) << 1), which puts the 32 pieces of each half-wave operand read, and
 // the 64 8-byte pieces of each transposing read, in distinct banks.
-// The grid is persistent: as many workgroups as the device holds at once, each
-// taking every gridDim-th split of the compact list of splits with rows (built in
-// LDS from the lengths), so no workgroup slot is spent on the splits past a
-// sequence's end; the next split's table entries and query are loaded while the
-// current split streams.  Splits end as in the other paged kernels: the output
-// directly (one split) or a partial for merge_kernel.
+// The grid is persistent: as many workgroups as the device holds at once.  The
+// 16-token tiles of all (sequence, head group) pairs, numbered sequence-major in
+// LDS from the lengths, are cut into equal ranges, one per workgroup (a few per
+// workgroup when the ranges would exceed a table span), so every workgroup streams
+// about the same number of tiles and none is spent past a sequence's end.  The part
+// of a range inside one (sequence, head group) is an item; the next item's table
+// entries and query are loaded while the current one streams.  An item ends with
+// the output (the whole of its sequence's group) or a partial, and
+// piece_merge_kernel combines the partials of each query head.  A call whose
+// sequences all fit one split of the plan takes whole (sequence, head group) pairs
+// instead, and needs no merge.
 #include "split_common.hpp"
 
 namespace dakv {
@@ -172,7 +177,8 @@ paged_mfma_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ ke
                   const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ seq_offset,
                   int B, int Hkv, int num_blocks, int block_size, int bs_log2, int max_len,
                   float scale_log2, int chunk, int max_splits, Workspace ws,
-                  float* __restrict__ out, float* __restrict__ lse, int32_t* err_flag) {
+                  int32_t* __restrict__ nseg, float* __restrict__ out, float* __restrict__ lse,
+                  int32_t* err_flag) {
   constexpr int D = 128;
   using S = PmShape<GH, Bits>;
   constexpr int NB = S::Blocks;
@@ -184,7 +190,7 @@ paged_mfma_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ ke
   __shared__ __attribute__((aligned(1024))) uint8_t tile0[S::Buf];
   __shared__ __attribute__((aligned(1024))) uint8_t tile1[S::Buf];
   __shared__ __attribute__((aligned(16))) uint8_t qbuf[2][QB];
-  __shared__ int pref[kPmMaxSeqs + 1];   // splits (x head groups) before sequence b
+  __shared__ int pref[kPmMaxSeqs + 1];   // work units (x head groups) before sequence b
   __shared__ int slen[kPmMaxSeqs];       // effective length of sequence b
   __shared__ int soff[kPmMaxSeqs];       // its table offset in blocks
   const int ngroups = Hkv / GH;
@@ -200,16 +206,19 @@ paged_mfma_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ ke
   const int block_rows = block_size * Hkv;                             // its (slot, head) rows
   const int W = (int)gridDim.x;
 
-  // The splits with rows, numbered sequence-major (then head group, then split):
-  // lengths, table offsets and split counts of every sequence, and their prefix sum.
+  // Work units numbered sequence-major, then head group: with ranges, the 16-token
+  // tiles of every (sequence, head group) (an empty sequence counts one, so that a
+  // workgroup writes its zeros); without, whole (sequence, head group) pairs.
+  // Lengths, table offsets, and the prefix sum of the units.
+  const bool ranged = chunk > 0;
   for (int b = threadIdx.x; b < B; b += kPmThreads) {
     int toff = 0;
     const int L = paged_len(seq_lens, seq_offset, b, block_size, table_cols, max_len, &toff,
                             err_flag, blockIdx.x == 0);
     slen[b] = L;
     soff[b] = toff;
-    pref[b + 1] = ngroups * (L > 0 ? (L + chunk - 1) / chunk : 1);  // split 0 of an empty
-  }                                                                  // sequence writes zeros
+    pref[b + 1] = ngroups * (!ranged ? 1 : (L > 0 ? (L + kPmTile - 1) / kPmTile : 1));
+  }
   __syncthreads();
   if (wave == 0) {
     int carry = 0;
@@ -227,45 +236,93 @@ paged_mfma_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ ke
   }
   __syncthreads();
   const int total = pref[B];
-  if ((int)blockIdx.x >= total) return;
+  // Ranges: workgroup w takes the tiles [R k, R (k + 1)) for k = w, w + W, ..., with
+  // R = the tiles of the call over the workgroups, so that every workgroup streams
+  // about the same number of tiles whatever the mix of lengths (whole splits of a
+  // fixed size left up to a split more on some workgroups: 96 against 90.4 tiles of
+  // the mean at the batch-64 config).  R is at least chunk / 16 tiles, which bounds
+  // the pieces of one (sequence, head group) by the splits of a chunk-sized plan
+  // plus one, and at most 126 blocks, which keeps a piece's table entries within
+  // two registers a lane.
+  int R = 1;
+  if (ranged) {
+    R = (total + W - 1) / W;
+    const int least = chunk / kPmTile;
+    const int span = 126 * block_size / kPmTile;
+    if (R < least) R = least;
+    if (R > span) R = span;
+  }
+  if ((int)blockIdx.x * R >= total) return;
 
-  // One split ("item"): sequence b, head group hg, rows [r0, r1); this workgroup
-  // takes items blockIdx.x, blockIdx.x + W, ...  Each item takes max(A, ntiles)
-  // steps (the extra ones over empty tiles), so the loads run at most one item
-  // ahead of the arithmetic.
+  // One item: sequence b, head group hg, rows [r0, r1), piece `split` of the n of
+  // its (sequence, head group) -- with ranges the part of a range inside one
+  // (sequence, head group), else a whole one (n = 1).  `next` is this workgroup's
+  // next item.  Each item takes max(A, ntiles) steps (the extra ones over empty
+  // tiles), so the loads run at most one item ahead of the arithmetic.
   struct Item {
-    int idx, b, hg, split, n, r0, r1, ntiles, blk0, nblk, steps;
+    int idx, next, b, hg, split, n, r0, r1, ntiles, blk0, nblk, steps;
   };
-  auto item_of = [&](int i) {
+  auto item_of = [&](int g) {
     Item it;
-    it.idx = i;
-    if (i >= total) {  // past the last item: no rows
-      it.b = 0; it.hg = 0; it.split = 0; it.n = 1; it.r0 = 0; it.r1 = 0;
+    it.idx = g;
+    if (g >= total) {  // past the last item: no rows
+      it.next = g; it.b = 0; it.hg = 0; it.split = 0; it.n = 1; it.r0 = 0; it.r1 = 0;
       it.ntiles = 0; it.blk0 = 0; it.nblk = 0; it.steps = A;
       return it;
     }
-    int lo = 0, hi = B - 1;  // the sequence b with pref[b] <= i < pref[b + 1]
+    int lo = 0, hi = B - 1;  // the sequence b with pref[b] <= g < pref[b + 1]
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
-      if (pref[mid] <= i) lo = mid;
+      if (pref[mid] <= g) lo = mid;
       else hi = mid - 1;
     }
     it.b = lo;
     const int L = slen[lo];
-    it.n = L > 0 ? (L + chunk - 1) / chunk : 1;
-    const int r = i - pref[lo];
-    it.hg = r / it.n;
-    it.split = r - it.hg * it.n;
-    it.r0 = it.split * chunk;
-    it.r1 = min(it.r0 + chunk, L);
+    if (ranged) {
+      const int u = L > 0 ? (L + kPmTile - 1) / kPmTile : 1;  // units of a head group
+      const int rel = g - pref[lo];
+      it.hg = rel / u;
+      const int t0 = rel - it.hg * u;
+      const int first = pref[lo] + it.hg * u;                // its first unit
+      const int k = g / R;
+      const int rend = min((k + 1) * R, total);
+      const int t1 = min(u, t0 + (rend - g));
+      it.split = k - first / R;                                // range starts in (first, g]
+      it.n = (first + u - 1) / R - first / R + 1;
+      it.r0 = min(t0 * kPmTile, L);
+      it.r1 = min(t1 * kPmTile, L);
+      const int gend = g + (t1 - t0);
+      it.next = gend < rend ? gend : (k + W) * R;
+    } else {
+      it.hg = g - pref[lo];
+      it.split = 0;
+      it.n = 1;
+      it.r0 = 0;
+      it.r1 = L;
+      it.next = g + W;
+    }
     it.ntiles = it.r1 > it.r0 ? (it.r1 - it.r0 + kPmTile - 1) / kPmTile : 0;
     it.blk0 = it.r0 >> bs_log2;
     it.nblk = it.r1 > it.r0 ? ((it.r1 - 1) >> bs_log2) - it.blk0 + 1 : 0;
     it.steps = it.ntiles > A ? it.ntiles : A;
+    // the same in every lane (from LDS and uniform values): scalar registers
+    it.next = __builtin_amdgcn_readfirstlane(it.next);
+    it.b = __builtin_amdgcn_readfirstlane(it.b);
+    it.hg = __builtin_amdgcn_readfirstlane(it.hg);
+    it.split = __builtin_amdgcn_readfirstlane(it.split);
+    it.n = __builtin_amdgcn_readfirstlane(it.n);
+    it.r0 = __builtin_amdgcn_readfirstlane(it.r0);
+    it.r1 = __builtin_amdgcn_readfirstlane(it.r1);
+    it.ntiles = __builtin_amdgcn_readfirstlane(it.ntiles);
+    it.blk0 = __builtin_amdgcn_readfirstlane(it.blk0);
+    it.nblk = __builtin_amdgcn_readfirstlane(it.nblk);
+    it.steps = __builtin_amdgcn_readfirstlane(it.steps);
     return it;
   };
+  const int first_item = (int)blockIdx.x * R;
   int total_steps = 0;
-  for (int i = blockIdx.x; i < total; i += W) total_steps += item_of(i).steps;
+  for (Item it = item_of(first_item); it.idx < total; it = item_of(it.next))
+    total_steps += it.steps;
 
   // Per-item metadata: the load side reads an item's query when it reaches the item
   // and stores it to LDS one step later, after the step's wait has covered it.  The
@@ -301,7 +358,7 @@ paged_mfma_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ ke
     }
   };
 
-  Item ld = item_of(blockIdx.x);   // the item the loads are in
+  Item ld = item_of(first_item);   // the item the loads are in
   table_load(ld, tcur0, tcur1);
   int ld_t = 0, ld_j = 0;          // tile of the item, ordinal of the item (LDS parity)
   bool meta_pending = false;       // the loaded query waits to be stored
@@ -322,7 +379,7 @@ paged_mfma_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ ke
   // tile loads.  Returns the tile's block id (-1: none).
   auto issue = [&](TileRegs& r) -> int {
     if (ld_t == 0) {  // a new item: its query, and the next item's table
-      const Item nx = item_of(ld.idx + W);
+      const Item nx = item_of(ld.next);
       meta_load(ld, nx);
       meta_pending = true;
       mq = ld_j & 1;
@@ -389,7 +446,7 @@ paged_mfma_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ ke
                                                                     kLoadNonTemporal));
     }
     if (++ld_t == ld.steps) {
-      ld = item_of(ld.idx + W);
+      ld = item_of(ld.next);
       ld_t = 0;
       ++ld_j;
       tcur0 = tnx0;
@@ -463,7 +520,7 @@ paged_mfma_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ ke
   // 16 (NB part + jb) + col16, heads 4 grp + i; rows G..15 stay zero), the running
   // max (head col16, the same in the four lane groups) and this lane's share of
   // the sum of exponentials.
-  Item ci = item_of(blockIdx.x);
+  Item ci = item_of(first_item);
   int ct = 0, cj = 0;
   f32x4_t oacc[NB];
 #pragma unroll
@@ -563,6 +620,8 @@ paged_mfma_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ ke
   auto finish = [&]() {
     const float lhead = pm_group4_sum(lsum);
     const size_t head0 = (size_t)ci.b * Hq + (size_t)(GH * ci.hg + hw) * G;
+    // the merge reads how many pieces the (sequence, head group) has
+    if (ranged && ci.split == 0 && threadIdx.x == 0) nseg[ci.b * ngroups + ci.hg] = ci.n;
 #pragma unroll
     for (int i2 = 0; i2 < 4; ++i2) {
       const int j = 4 * grp + i2;
@@ -624,7 +683,7 @@ paged_mfma_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ ke
       if (ct < ci.ntiles) compute(T, phys);
       if (++ct == ci.steps) {
         finish();
-        ci = item_of(ci.idx + W);
+        ci = item_of(ci.next);
         ct = 0;
         ++cj;
 #pragma unroll
@@ -643,6 +702,31 @@ paged_mfma_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ ke
   __builtin_amdgcn_s_waitcnt(wait_vm(0));
 }
 
+// ------------------------------------------------------------------- merge
+// One workgroup per (sequence, query head): the pieces of its (sequence, head
+// group), as many as the split kernel recorded; a head of one piece has its output.
+__global__ void __launch_bounds__(kThreads)
+piece_merge_kernel(Workspace ws, const int32_t* __restrict__ nseg, int heads,
+                   int heads_per_group, int stride, float* __restrict__ out,
+                   float* __restrict__ lse) {
+  const int bh = blockIdx.x;
+  const int b = bh / heads;
+  const int h = bh - b * heads;
+  int n = nseg[b * (heads / heads_per_group) + h / heads_per_group];
+  if (n <= 1) return;
+  if (n > stride) n = stride;
+  merge_head<128>(ws.lse + (size_t)bh * stride, ws.o + (size_t)bh * stride * 128, n,
+                  out + (size_t)bh * 128, lse ? lse + bh : nullptr);
+}
+
+static hipError_t launch_paged_piece_merge(const Workspace& w, const int32_t* nseg, int B,
+                                           int Hq, int heads_per_group, int stride, float* out,
+                                           float* lse, hipStream_t stream) {
+  hipLaunchKernelGGL(piece_merge_kernel, dim3(B * Hq), dim3(kThreads), 0, stream, w, nseg, Hq,
+                     heads_per_group, stride, out, lse);
+  return hipGetLastError();
+}
+
 // ------------------------------------------------------------------- planning
 static int round_up_pm(int x, int m) { return (x + m - 1) / m * m; }
 
@@ -658,17 +742,19 @@ SplitPlan plan_paged_mfma(int B, int Hkv, int max_seq_len, int block_size, int f
   SplitPlan p;
   const int unit = block_size > kMinChunk ? block_size : kMinChunk;
   // one split may touch at most kMaxTableSpan - 2 blocks; the merge takes <= 256
+  // pieces, and a (sequence, head group) has at most the plan's splits plus one
   const int most = ((kMaxTableSpan - 2) * block_size) / unit * unit;
-  const int least = round_up_pm((max_seq_len + kMaxSplits - 1) / kMaxSplits, unit);
+  const int least = round_up_pm((max_seq_len + kMaxSplits - 2) / (kMaxSplits - 1), unit);
   int c;
   if (forced_splits > 0) {
     c = round_up_pm((max_seq_len + forced_splits - 1) / forced_splits, unit);
   } else {
-    // about kPmSplitsTarget splits if every sequence had max_seq_len tokens.  Each
-    // split adds a partial output that is written, read back and merged, and the
-    // persistent workgroups take whole splits: 512-token splits (the batch-64,
-    // 16384-token paged config) measured 263 us, 256-token ones 287 us, 128-token
-    // ones 314 us.
+    // about kPmSplitsTarget splits if every sequence had max_seq_len tokens.  The
+    // chunk is the shortest range a workgroup takes (and bounds the pieces of a
+    // sequence); each piece adds a partial output that is written, read back and
+    // merged.  When the persistent workgroups took whole splits, 512-token splits
+    // (the batch-64, 16384-token paged config) measured 263 us, 256-token ones
+    // 287 us, 128-token ones 314 us.
     const int gh = Hkv < 8 ? Hkv : 8;
     const int groups = Hkv / gh;
     const long long want = ((long long)B * groups * max_seq_len + kPmSplitsTarget - 1) /
@@ -708,16 +794,21 @@ static hipError_t launch_pm(const uint16_t* qb, const uint8_t* kc, const uint8_t
                             int table_cols,
                             const int32_t* seq_lens, const int32_t* seq_offset, int B, int Hkv,
                             int num_blocks, int block_size, int bs_log2, int max_seq_len,
-                            float scale, const SplitPlan& plan, const Workspace& w, float* out,
-                            float* lse, int32_t* err_flag, hipStream_t stream) {
+                            float scale, const SplitPlan& plan, const Workspace& w,
+                            int32_t* nseg, float* out, float* lse, int32_t* err_flag,
+                            hipStream_t stream) {
   const int resident = resident_workgroups<Bits, G, GH>();
   if (resident <= 0) return hipErrorInvalidValue;
-  const long long items = (long long)B * (Hkv / GH) * plan.max_splits;  // at most
+  // at most: a range per workgroup, or (one split) every (sequence, head group)
+  const long long items = (long long)B * (Hkv / GH) * (plan.max_splits + 1);
   const unsigned grid = (unsigned)(items < resident ? items : resident);
+  // ranges when a sequence may need more than one split; the piece stride of the
+  // workspace is the plan's splits plus one
+  const int chunk = plan.max_splits > 1 ? plan.chunk : 0;
   hipLaunchKernelGGL((paged_mfma_kernel<Bits, G, GH>), dim3(grid), dim3(kPmThreads), 0, stream,
                      qb, kc, vc, ks, vs, block_tables, table_cols, seq_lens, seq_offset, B, Hkv,
-                     num_blocks, block_size, bs_log2, max_seq_len, scale * kLog2e, plan.chunk,
-                     plan.max_splits, w, out, lse, err_flag);
+                     num_blocks, block_size, bs_log2, max_seq_len, scale * kLog2e, chunk,
+                     plan.max_splits + 1, w, nseg, out, lse, err_flag);
   return hipGetLastError();
 }
 
@@ -731,7 +822,9 @@ static hipError_t launch_paged_mfma_fmt(const void* q, const void* key_cache,
                                         float scale, float* out, float* lse, void* ws,
                                         const SplitPlan& plan, int32_t* err_flag,
                                         hipStream_t stream) {
-  const Workspace w = carve(ws, (size_t)B * Hq, plan.max_splits, 128);
+  const int stride = plan.max_splits + 1;  // pieces of a (sequence, head group), at most
+  const Workspace w = carve(ws, (size_t)B * Hq, stride, 128);
+  int32_t* nseg = reinterpret_cast<int32_t*>(w.lse + (size_t)B * Hq * stride);
   int bs_log2 = 0;
   while ((1 << bs_log2) < block_size) ++bs_log2;
   const auto* qb = static_cast<const uint16_t*>(q);
@@ -748,7 +841,7 @@ static hipError_t launch_paged_mfma_fmt(const void* q, const void* key_cache,
 #define DAKV_PM(GG, HH)                                                                       \
   err = launch_pm<Bits, GG, HH>(qb, kc, vc, k_scale, v_scale, block_tables, table_cols,       \
                                 seq_lens, seq_offset, B, Hkv, num_blocks, block_size, bs_log2, \
-                                max_seq_len, scale, plan, w, out, lse, err_flag, stream)
+                                max_seq_len, scale, plan, w, nseg, out, lse, err_flag, stream)
 #define DAKV_PM_H(GG)                  \
   switch (GH) {                        \
     case 2: DAKV_PM(GG, 2); break;     \
@@ -768,8 +861,7 @@ static hipError_t launch_paged_mfma_fmt(const void* q, const void* key_cache,
 #undef DAKV_PM_H
 #undef DAKV_PM
   if (err != hipSuccess || plan.max_splits <= 1) return err;
-  return launch_paged_merge(w, B, Hq, plan.chunk, plan.max_splits, seq_lens, seq_offset,
-                            block_size, table_cols, max_seq_len, out, lse, stream);
+  return launch_paged_piece_merge(w, nseg, B, Hq, Hq / Hkv * GH, stride, out, lse, stream);
 }
 
 hipError_t launch_decode_paged_mfma(const void* q, const void* key_cache,
