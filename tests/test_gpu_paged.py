@@ -260,6 +260,25 @@ def test_paged_longest_supported_sequence():
 # (Hkv in {2, 4, 8k} with D = 128 and at most 512 sequences take paged_mfma_kernel;
 # the tests above with one or three KV heads reach the other kernels)
 
+def test_paged_mfma_ranges_cut_groups_and_workspace_reuse():
+    """The matrix-core kernel gives every workgroup an equal range of 16-token tiles, so
+    ranges cut through (sequence, head group) pairs: mixed lengths (empty and one-token
+    sequences among them) with many pieces per group; then the same workspace for a call
+    with other piece counts, and for one whose sequences all fit a single split (no
+    merge, the recorded piece counts of the earlier calls left in the workspace)."""
+    calls = ([5000, 0, 1, 3000, 17, 12000, 640], [40000, 33, 2048], [300, 0, 511])
+    need = max(dakv.decode_attn_paged_workspace_size(len(c), 32, 128, max(c), 16) for c in calls)
+    ws = torch.empty(need, dtype=torch.uint8, device=DEV)
+    for i, lengths in enumerate(calls):
+        print(f"paged ranges call {i}: {lengths}", flush=True)
+        case = workloads.paged_case(lengths, Hq=32, Hkv=8, D=128, block_size=16, device=DEV,
+                                    seed=180 + i)
+        out, lse = run_paged(case, workspace=ws)
+        ref_out, ref_lse = oracle_paged(case)
+        assert_attention_close(out, ref_out)
+        assert_lse_close(lse, ref_lse)
+
+
 def test_paged_mfma_single_token_bit_exact_and_empty_sequence():
     case = workloads.paged_case([1, 0, 1], Hq=8, Hkv=2, D=128, block_size=16, device=DEV,
                                 seed=170)
