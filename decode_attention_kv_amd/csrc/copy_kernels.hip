@@ -62,11 +62,12 @@ hipError_t launch_kv_append(void* k_cache, void* v_cache, const void* k_new, con
 // through, kStoreThrough).
 // Grid: n * B * H * chunks, chunk fastest; chunks past the copied length exit.
 // ---------------------------------------------------------------------------
-// 4 loads of 16 bytes per thread (16 KiB per workgroup): the 64-tensor, 1 GiB
-// hand-over measured 187.8 us per call, against 190.9 / 189.9 / 190.1 / 192.9 us
-// with 2 / 3 / 6 / 8 loads per thread.
-constexpr int kCopyLoads = 4;                        // 16-byte loads per thread
-constexpr int kCopyBytes = 256 * kCopyLoads * 16;    // 16 KiB per workgroup
+// 2 loads of 16 bytes per thread (8 KiB per workgroup): the 64-tensor, 1 GiB
+// hand-over measured 163.9 us per call, against 163.8 / 165.4 / 170.7 us with 1 / 4 /
+// 8 loads per thread (with non-temporal stores 4 loads were best: 187.8 against 190.9 /
+// 189.9 / 190.1 / 192.9 us with 2 / 3 / 6 / 8).
+constexpr int kCopyLoads = 2;                        // 16-byte loads per thread
+constexpr int kCopyBytes = 256 * kCopyLoads * 16;    // 8 KiB per workgroup
 
 struct CopyTable {
   const uint8_t* src[kCopyMaxTensors];
@@ -180,15 +181,17 @@ hipError_t launch_trim_kvcache(int32_t* mask, const int32_t* new_len, int B, int
 // once); stores are written through (kStoreThrough), so the output leaves no dirty
 // lines in the L2s.
 // ---------------------------------------------------------------------------
-// A workgroup takes 3 tokens: at 4 KiB per token (K + V, 8 heads x 128 dims) that
-// is 3 loads per thread, all in flight before the first store, in a small kernel
-// (30-odd VGPRs) that keeps 8 workgroups on every CU, so that the two dependent
-// reads each workgroup starts with (the lengths, then the block table) overlap
-// other workgroups' copies.  Measured at batch 32 x U{1..4096} (494 MB): 3 tokens
-// 87.0 us per call; 2: 90.0; 4: 90.6; 5: 89.6; 8: 92.9; 16: 96.7; 32 tokens (one
-// round of 32 loads per thread, 294 VGPRs, one wave per SIMD): 95.1.
-constexpr int kGatherTok = 3;
-constexpr int kGatherSlots = 3;
+// A workgroup takes 6 tokens: at 4 KiB per token (K + V, 8 heads x 128 dims) that
+// is 6 loads per thread, all in flight before the first store, in a small kernel
+// that keeps several workgroups on every CU, so that the two dependent reads each
+// workgroup starts with (the lengths, then the block table) overlap other
+// workgroups' copies.  Measured at batch 32 x U{1..4096} (494 MB), stores written
+// through: 6 tokens 76.1 us per call; 2: 84.9; 3: 77.6; 4: 77.4; 5: 76.8; 8: 77.5;
+// 12: 76.9.  (With non-temporal stores 3 tokens were best: 87.0 us; 2: 90.0; 4:
+// 90.6; 5: 89.6; 8: 92.9; 16: 96.7; 32 tokens, one round of 32 loads per thread,
+// 294 VGPRs, one wave per SIMD: 95.1.)
+constexpr int kGatherTok = 6;
+constexpr int kGatherSlots = 6;
 constexpr int kGatherLensLds = 4096;
 
 
