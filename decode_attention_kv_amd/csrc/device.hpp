@@ -77,7 +77,8 @@ __device__ __forceinline__ void raise_flag(int32_t* err_flag, int32_t bit) {
 // K/V lines until the end-of-kernel write-back (paged GQA call 262 -> 251 us).  Measured
 // and not used elsewhere: the sparse pass, whose partials are all written at its end, is
 // unchanged, and the static pass, whose short workgroups then end later, is slower (batch-8
-// step 1294 -> 1382 us).
+// step 1294 -> 1382 us); so are the merge kernels' outputs (sparse call 34.0 -> 36.2 us,
+// batch-8 step 1299 -> 1303 us).
 __device__ __forceinline__ void store_through(float* p, float v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
